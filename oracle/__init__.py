@@ -1,0 +1,222 @@
+"""CPU oracle for the fused MoE layer (ctypes wrapper over ``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
+and by the benchmark's ``cpu_baseline`` leg, never by the product package.  It
+shares no code with the HIP library.  All floating-point results are float64.
+
+Parity pins (what fixes each function independently of itself) live in
+``tests/test_oracle_*.py``.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+SOFTMAX, SIGMOID = 0, 1
+W_BF16, W_MXFP4 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) into ``liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _W(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        vp, i64, i32, dbl, u8 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_double, ctypes.c_uint8)
+        Wp = ctypes.POINTER(_W)
+        L.oracle_e8m0_scale.restype = dbl
+        L.oracle_e8m0_scale.argtypes = [u8]
+        L.oracle_mxfp4_value.restype = dbl
+        L.oracle_mxfp4_value.argtypes = [vp, vp, i64, i64, i64]
+        L.oracle_route.restype = None
+        L.oracle_route.argtypes = [vp, i64, i32, i32, i32, i32, dbl, vp, vp]
+        L.oracle_permute.restype = ctypes.c_int
+        L.oracle_permute.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
+        L.oracle_hidden_rows.restype = None
+        L.oracle_hidden_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
+        L.oracle_out_rows.restype = None
+        L.oracle_out_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
+        L.oracle_finalize.restype = None
+        L.oracle_finalize.argtypes = [vp, vp, vp, i64, i32, i64, dbl, vp, vp]
+        L.oracle_moe_tokens.restype = None
+        L.oracle_moe_tokens.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dbl, vp, Wp, Wp,
+                                        i64, vp, vp, dbl, vp, i64, vp, vp, vp, vp]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _c(a: Optional[np.ndarray], dtype) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+class Weights:
+    """Expert weights in bf16 bits ([rows, K] uint16) or MXFP4 (packed uint8
+    [rows, K/2] + E8M0 uint8 [rows, K/32]).  Keeps the arrays alive."""
+
+    def __init__(self, data: np.ndarray, scales: Optional[np.ndarray] = None):
+        if scales is None:
+            self.data = _c(data, np.uint16)
+            self.scales = None
+            self.fmt = W_BF16
+        else:
+            self.data = _c(data, np.uint8)
+            self.scales = _c(scales, np.uint8)
+            self.fmt = W_MXFP4
+        self._s = _W(self.fmt, _p(self.data), _p(self.scales))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def e8m0_scale(s: int) -> float:
+    return float(_load().oracle_e8m0_scale(s))
+
+
+def mxfp4_value(packed: np.ndarray, scales: np.ndarray, row: int, K: int, kk: int) -> float:
+    packed, scales = _c(packed, np.uint8), _c(scales, np.uint8)
+    return float(_load().oracle_mxfp4_value(_p(packed), _p(scales), row, K, kk))
+
+
+def mxfp4_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Element-by-element decode of [rows, K/2] + [rows, K/32] -> float64 [rows, K]
+    (small inputs only: one C call per element)."""
+    packed, scales = _c(packed, np.uint8), _c(scales, np.uint8)
+    rows, K = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((rows, K), dtype=np.float64)
+    f = _load().oracle_mxfp4_value
+    for r in range(rows):
+        for kk in range(K):
+            out[r, kk] = f(_p(packed), _p(scales), r, K, kk)
+    return out
+
+
+def route(logits: np.ndarray, k: int, score: int, renormalize: bool, rsf: float):
+    """-> (ids int32 [T, k], weights float64 [T, k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    _load().oracle_route(_p(logits), T, E, k, score, int(bool(renormalize)), rsf, _p(ids), _p(w))
+    return ids, w
+
+
+def permute(ids: np.ndarray, E: int, E_l: int, expert_map: Optional[np.ndarray] = None):
+    """-> (map int32 [T, k], offsets int32 [E_l+1], counts int32 [E_l]).
+    Raises ValueError on ids outside [0, E) or map entries outside [-1, E_l)."""
+    ids = _c(ids, np.int32)
+    expert_map = _c(expert_map, np.int32)
+    T, k = ids.shape
+    m = np.empty((T, k), dtype=np.int32)
+    offsets = np.empty(E_l + 1, dtype=np.int32)
+    counts = np.empty(max(E_l, 1), dtype=np.int32)
+    rc = _load().oracle_permute(_p(ids), _p(expert_map), T, k, E, E_l, _p(m), _p(offsets),
+                                _p(counts))
+    if rc != 0:
+        raise ValueError("expert id out of range")
+    return m, offsets, counts[:E_l]
+
+
+def hidden_rows(a_bf16: np.ndarray, w1: Weights, expert_of_row: np.ndarray, I: int) -> np.ndarray:
+    """h[r] = silu(W1g[e_r] a_r) * (W1u[e_r] a_r), float64 [rows, I]."""
+    a = _c(a_bf16, np.uint16)
+    eor = _c(expert_of_row.astype(np.int32), np.int32)
+    rows, H = a.shape
+    h = np.empty((rows, I), dtype=np.float64)
+    _load().oracle_hidden_rows(_p(a), rows, H, I, w1.ref, _p(eor), _p(h))
+    return h
+
+
+def out_rows(h_bf16: np.ndarray, w2: Weights, expert_of_row: np.ndarray, H: int) -> np.ndarray:
+    """y[r] = W2[e_r] h_r, float64 [rows, H]."""
+    hb = _c(h_bf16, np.uint16)
+    eor = _c(expert_of_row.astype(np.int32), np.int32)
+    rows, I = hb.shape
+    y = np.empty((rows, H), dtype=np.float64)
+    _load().oracle_out_rows(_p(hb), rows, I, H, w2.ref, _p(eor), _p(y))
+    return y
+
+
+def finalize(y_perm_bf16: np.ndarray, weights: np.ndarray, pmap: np.ndarray, rsf_fin: float = 1.0,
+             shared_bf16: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = rsf_fin * sum_{map>=0} w * Y[map] + shared[t], float64 [T, H]."""
+    y = _c(y_perm_bf16, np.uint16)
+    w = _c(np.asarray(weights, dtype=np.float64), np.float64)
+    pmap = _c(pmap, np.int32)
+    shared = _c(shared_bf16, np.uint16)
+    T, k = pmap.shape
+    H = y.shape[1]
+    out = np.empty((T, H), dtype=np.float64)
+    _load().oracle_finalize(_p(y), _p(w), _p(pmap), T, k, H, rsf_fin, _p(shared), _p(out))
+    return out
+
+
+def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights, I: int, k: int,
+               score: int, renormalize: bool, rsf: float,
+               expert_map: Optional[np.ndarray] = None, shared_I: int = 0,
+               ws1: Optional[np.ndarray] = None, ws2: Optional[np.ndarray] = None,
+               rsf_fin: float = 1.0, tokens: Optional[Sequence[int]] = None):
+    """The whole layer for the listed tokens (all when None).
+
+    Returns dict: out float64 [n, H], y_routes float64 [n, k, H] (unweighted
+    per-route expert outputs, zero when not local), ids int32 [n, k],
+    weights float64 [n, k], tokens int64 [n]."""
+    x = _c(x_bf16, np.uint16)
+    logits = _c(logits, np.float32)
+    T, H = x.shape
+    E = logits.shape[1]
+    tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    tok = np.ascontiguousarray(tok)
+    n = tok.shape[0]
+    out = np.empty((n, H), dtype=np.float64)
+    y = np.empty((n, k, H), dtype=np.float64)
+    ids = np.empty((n, k), dtype=np.int32)
+    w = np.empty((n, k), dtype=np.float64)
+    expert_map = _c(expert_map, np.int32)
+    ws1 = _c(ws1, np.uint16)
+    ws2 = _c(ws2, np.uint16)
+    _load().oracle_moe_tokens(_p(x), H, I, _p(logits), E, k, score, int(bool(renormalize)), rsf,
+                              _p(expert_map), w1.ref, w2.ref, shared_I, _p(ws1), _p(ws2),
+                              rsf_fin, _p(tok), n, _p(out), _p(y), _p(ids), _p(w))
+    return {"out": out, "y_routes": y, "ids": ids, "weights": w, "tokens": tok}

@@ -1,0 +1,318 @@
+/*
+ * CPU oracle for the fused MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code with the HIP library.
+ *
+ * Plain, slow, obviously correct: per token, per routed expert, a dense
+ * SiLU-gated MLP, all in double precision.  Every function names the passage
+ * of the pages it follows.  Pages:
+ *   [OUT]  vLLM "moe_output.py" (output contract between a MoE layer and a
+ *          consumer that fuses its tail): UnfinalizedMoEOutput, MoEOutput.
+ *   [MOD]  vLLM "modular_kernel.py" (modular fused-MoE kernel): the stage
+ *          comment [Router] -> [Quantize-Dispatch] -> [Permute-Experts-
+ *          Unpermute] -> [Combine]; _moe_problem_size; prepare / finalize /
+ *          apply / activation; FusedMoEModularKernel.forward.
+ *   [EP]   vLLM "flashinfer_moe_ep.py": _E2M1_LUT, _dequant_fp4_ue8m0_gran32.
+ *
+ * Readings where the pages are silent (each is listed in the design doc):
+ *   - w1 is [E, 2I, H]: rows [0, I) are the gate (SiLU'd), rows [I, 2I) the
+ *     up projection; w2 is [E, H, I]; both contiguous along the reduction dim.
+ *   - top-k is taken on the fp32 logits, ordered by logit descending, ties to
+ *     the smaller expert id.
+ *   - Routes of one local expert are placed in ascending expanded index
+ *     t*k+j; experts in ascending local id; offsets are not padded.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
+enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1 };
+
+typedef struct {
+  int32_t fmt;            /* OR_W_BF16 or OR_W_MXFP4 */
+  const void* data;       /* bf16 [rows, K] or packed e2m1 [rows, K/2] */
+  const uint8_t* scales;  /* E8M0 [rows, K/32] (MXFP4 only) */
+} oracle_weights;
+
+static double bf16_val(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ---- MXFP4 decode ([EP] _E2M1_LUT and _dequant_fp4_ue8m0_gran32) ----------
+ * e2m1 code -> value table as the page prints it (code 8 is -0.0).  The scale
+ * byte s is read as the float whose bit pattern is s<<23: 2^(s-127) for
+ * 1 <= s <= 254, +0.0 for s = 0 and +inf for s = 255. */
+static const double kE2M1[16] = {0.0,  0.5,  1.0,  1.5,  2.0,  3.0,  4.0,  6.0,
+                                 -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0};
+
+double oracle_e8m0_scale(uint8_t s) {
+  if (s == 0) return 0.0;
+  if (s == 255) return INFINITY;
+  return ldexp(1.0, (int)s - 127);
+}
+
+/* Element kk of packed row `row` (K elements per row): low nibble = even kk. */
+double oracle_mxfp4_value(const uint8_t* packed, const uint8_t* scales, int64_t row, int64_t K,
+                          int64_t kk) {
+  uint8_t b = packed[row * (K / 2) + kk / 2];
+  uint8_t code = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+  return kE2M1[code] * oracle_e8m0_scale(scales[row * (K / 32) + kk / 32]);
+}
+
+/* Weight element (row, kk) of a [rows, K] matrix in either storage format. */
+double oracle_weight_at(const oracle_weights* w, int64_t row, int64_t K, int64_t kk) {
+  if (w->fmt == OR_W_MXFP4)
+    return oracle_mxfp4_value((const uint8_t*)w->data, w->scales, row, K, kk);
+  return bf16_val(((const uint16_t*)w->data)[row * K + kk]);
+}
+
+/* sum_kk W[row, kk] * v[kk], ascending kk, in double. */
+static double dot_row(const oracle_weights* w, int64_t row, int64_t K, const double* v) {
+  double acc = 0.0;
+  if (w->fmt == OR_W_MXFP4) {
+    const uint8_t* p = (const uint8_t*)w->data + row * (K / 2);
+    const uint8_t* s = w->scales + row * (K / 32);
+    for (int64_t kk = 0; kk < K; ++kk) {
+      uint8_t b = p[kk / 2];
+      uint8_t code = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+      acc += kE2M1[code] * oracle_e8m0_scale(s[kk / 32]) * v[kk];
+    }
+  } else {
+    const uint16_t* p = (const uint16_t*)w->data + row * K;
+    for (int64_t kk = 0; kk < K; ++kk) acc += bf16_val(p[kk]) * v[kk];
+  }
+  return acc;
+}
+
+/* ---- [Router] ([MOD] stage comment; [OUT] expert_weights carry the routed
+ * scaling factor when the routing method folds it in) ------------------------
+ * For token t: pick k experts by repeatedly taking the largest remaining
+ * logit (scan in ascending id, strict '>' so ties keep the smaller id).
+ * Scores: softmax over all E experts, or the logistic sigmoid of each logit.
+ * With renormalize the k selected scores are divided by their sum.  The
+ * result is multiplied by rsf. */
+void oracle_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score_fn,
+                  int32_t renormalize, double rsf, int32_t* ids, double* weights) {
+  char* taken = (char*)malloc((size_t)E);
+  double* score = (double*)malloc(sizeof(double) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+      taken[best] = 1;
+      ids[t * k + j] = best;
+    }
+    if (score_fn == OR_SOFTMAX) {
+      double m = l[0];
+      for (int e = 1; e < E; ++e)
+        if (l[e] > m) m = l[e];
+      double z = 0.0;
+      for (int e = 0; e < E; ++e) z += exp((double)l[e] - m);
+      for (int e = 0; e < E; ++e) score[e] = exp((double)l[e] - m) / z;
+    } else {
+      for (int e = 0; e < E; ++e) score[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+    }
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j) sel += score[ids[t * k + j]];
+    for (int j = 0; j < k; ++j) {
+      double w = score[ids[t * k + j]];
+      if (renormalize) w /= sel;
+      weights[t * k + j] = w * rsf;
+    }
+  }
+  free(taken);
+  free(score);
+}
+
+/* ---- Permute ([MOD] prepare: expert_map maps global to local expert ids and
+ * the per-local-expert token counts; [OUT] expanded_idx_to_permuted_idx is
+ * int32 [num_tokens, top_k] with -1 for an expert that is not local) --------
+ * L = expert_map[id] (or id when there is no map).  counts[L] = routes to L;
+ * offsets = exclusive prefix sum of counts (E_l + 1 entries).  Walking the
+ * expanded index x = t*k + j upward, map[x] = offsets[L] + (routes to L seen
+ * so far), or -1 when L < 0.  Returns 0, or -1 on an id outside [0, E) or a
+ * local id outside [-1, E_l). */
+int oracle_permute(const int32_t* ids, const int32_t* expert_map, int64_t T, int32_t k,
+                   int32_t E, int32_t E_l, int32_t* map, int32_t* offsets, int32_t* counts) {
+  int64_t R = T * k;
+  for (int e = 0; e < E_l; ++e) counts[e] = 0;
+  for (int64_t x = 0; x < R; ++x) {
+    int32_t id = ids[x];
+    if (id < 0 || id >= E) return -1;
+    int32_t L = expert_map ? expert_map[id] : id;
+    if (L < -1 || L >= E_l) return -1;
+    if (L >= 0) counts[L] += 1;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E_l; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* seen = (int32_t*)calloc((size_t)(E_l > 0 ? E_l : 1), sizeof(int32_t));
+  for (int64_t x = 0; x < R; ++x) {
+    int32_t L = expert_map ? expert_map[ids[x]] : ids[x];
+    if (L < 0) {
+      map[x] = -1;
+    } else {
+      map[x] = offsets[L] + seen[L];
+      seen[L] += 1;
+    }
+  }
+  free(seen);
+  return 0;
+}
+
+/* ---- Experts ([MOD] apply: GEMM1, activation, GEMM2, unweighted; activation:
+ * the output is half the width of the input and "silu" gives
+ * silu(first half) * second half; _moe_problem_size: w1 is [E, N, .], w2 is
+ * [E, K, .] with K the hidden size) ------------------------------------------
+ * h[i] = silu(g_i) * u_i with g_i = W1[e, i, :] . x, u_i = W1[e, I + i, :] . x,
+ * silu(g) = g / (1 + exp(-g)). */
+void oracle_expert_hidden(const double* x, int64_t H, int64_t I, const oracle_weights* w1,
+                          int64_t e, double* h) {
+  for (int64_t i = 0; i < I; ++i) {
+    double g = dot_row(w1, e * 2 * I + i, H, x);
+    double u = dot_row(w1, e * 2 * I + I + i, H, x);
+    h[i] = g / (1.0 + exp(-g)) * u;
+  }
+}
+
+/* y[n] = W2[e, n, :] . h */
+void oracle_expert_out(const double* h, int64_t H, int64_t I, const oracle_weights* w2,
+                       int64_t e, double* y) {
+  for (int64_t n = 0; n < H; ++n) y[n] = dot_row(w2, e * H + n, I, h);
+}
+
+/* Batched helpers over bf16 rows (parallel over rows; each row is the plain
+ * per-row function above).  Used to check the two grouped GEMMs on their own:
+ *   hidden: rows[r] -> h[r] with expert expert_of_row[r];
+ *   out:    h rows (bf16) -> y[r]. */
+void oracle_hidden_rows(const uint16_t* a, int64_t rows, int64_t H, int64_t I,
+                        const oracle_weights* w1, const int32_t* expert_of_row, double* h) {
+#pragma omp parallel
+  {
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < H; ++c) xv[c] = bf16_val(a[r * H + c]);
+      oracle_expert_hidden(xv, H, I, w1, expert_of_row[r], h + r * I);
+    }
+    free(xv);
+  }
+}
+
+void oracle_out_rows(const uint16_t* hb, int64_t rows, int64_t I, int64_t H,
+                     const oracle_weights* w2, const int32_t* expert_of_row, double* y) {
+#pragma omp parallel
+  {
+    double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < I; ++c) hv[c] = bf16_val(hb[r * I + c]);
+      oracle_expert_out(hv, H, I, w2, expert_of_row[r], y + r * H);
+    }
+    free(hv);
+  }
+}
+
+/* ---- [Combine] ([MOD] finalize: apply the weights to the unweighted expert
+ * output and reduce over top-k, written into an output that starts at zero
+ * (forward allocates zeros_like); [OUT] MoEOutput: the routed scaling factor
+ * multiplies the routed sum before the shared-expert add; -1 entries of the
+ * map name no row) -----------------------------------------------------------
+ * out[t] = rsf_fin * sum_{j : map[t,j] >= 0} w[t,j] * Y[map[t,j]] + shared[t]. */
+void oracle_finalize(const uint16_t* y_perm, const double* w, const int32_t* map, int64_t T,
+                     int32_t k, int64_t H, double rsf_fin, const uint16_t* shared, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int32_t r = map[t * k + j];
+      if (r < 0) continue;
+      for (int64_t n = 0; n < H; ++n) o[n] += w[t * k + j] * bf16_val(y_perm[(int64_t)r * H + n]);
+    }
+    for (int64_t n = 0; n < H; ++n) {
+      o[n] *= rsf_fin;
+      if (shared) o[n] += bf16_val(shared[t * H + n]);
+    }
+  }
+}
+
+/* ---- The whole layer on selected tokens ([MOD] forward: prepare, apply,
+ * finalize; [OUT] MoEOutput for the shared add) -------------------------------
+ * For each listed token t: route it, localize each route through the expert
+ * map, run the expert MLP of every local route, and combine:
+ *   out[t] = rsf_fin * sum_j w_j * MLP_{L_j}(x_t) + MLP_shared(x_t).
+ * Optional outputs: y_routes [n, k, H] (the unweighted per-route expert output,
+ * zero for non-local routes), ids [n, k], weights [n, k].
+ * shared_I = 0 disables the shared expert. */
+void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* logits, int32_t E,
+                       int32_t k, int32_t score_fn, int32_t renormalize, double rsf,
+                       const int32_t* expert_map, const oracle_weights* w1,
+                       const oracle_weights* w2, int64_t shared_I, const uint16_t* ws1,
+                       const uint16_t* ws2, double rsf_fin, const int64_t* tokens,
+                       int64_t n_tokens, double* out, double* y_routes, int32_t* ids_out,
+                       double* w_out) {
+  oracle_weights s1 = {OR_W_BF16, ws1, NULL};
+  oracle_weights s2 = {OR_W_BF16, ws2, NULL};
+#pragma omp parallel
+  {
+    int64_t Imax = I > shared_I ? I : shared_I;
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+    double* hv = (double*)malloc(sizeof(double) * (size_t)Imax);
+    double* yv = (double*)malloc(sizeof(double) * (size_t)H);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* wts = (double*)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t s = 0; s < n_tokens; ++s) {
+      int64_t t = tokens[s];
+      for (int64_t c = 0; c < H; ++c) xv[c] = bf16_val(x[t * H + c]);
+      oracle_route(logits + t * E, 1, E, k, score_fn, renormalize, rsf, ids, wts);
+      double* o = out + s * H;
+      for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        int32_t L = expert_map ? expert_map[ids[j]] : ids[j];
+        if (ids_out) ids_out[s * k + j] = ids[j];
+        if (w_out) w_out[s * k + j] = wts[j];
+        double* yr = y_routes ? y_routes + (s * k + j) * H : yv;
+        if (L < 0) {
+          for (int64_t n = 0; n < H; ++n) yr[n] = 0.0;
+          continue;
+        }
+        oracle_expert_hidden(xv, H, I, w1, L, hv);
+        oracle_expert_out(hv, H, I, w2, L, yr);
+        for (int64_t n = 0; n < H; ++n) o[n] += wts[j] * yr[n];
+      }
+      for (int64_t n = 0; n < H; ++n) o[n] *= rsf_fin;
+      if (shared_I > 0) {
+        oracle_expert_hidden(xv, H, shared_I, &s1, 0, hv);
+        oracle_expert_out(hv, H, shared_I, &s2, 0, yv);
+        for (int64_t n = 0; n < H; ++n) o[n] += yv[n];
+      }
+    }
+    free(xv);
+    free(hv);
+    free(yv);
+    free(ids);
+    free(wts);
+  }
+}
+
+int oracle_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}
