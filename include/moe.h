@@ -1,0 +1,247 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts layer for AMD Instinct MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The layer follows the stage decomposition of vLLM's modular fused-MoE kernel
+ * (page "modular_kernel.py", the module comment: Router -> Quantize-Dispatch
+ * -> Permute-Experts-Unpermute -> Combine):
+ *
+ *   moe_route_topk         Router: top-k experts per token and their weights
+ *   moe_permute            Quantize-Dispatch (single-GPU part): the permute map
+ *                          and per-local-expert row offsets, and the gather of
+ *                          token rows into expert-contiguous order
+ *   moe_grouped_gemm1_act  Experts, GEMM1 with the SiLU(gate) * up activation
+ *   moe_grouped_gemm2      Experts, GEMM2 (unweighted, unreduced output)
+ *   moe_finalize           Unpermute + Combine: weights, top-k reduction,
+ *                          optional shared-expert add
+ *   moe_fused_experts_unfinalized
+ *                          all but the last step; returns the three buffers of
+ *                          the deferred-finalize contract (page "moe_output.py",
+ *                          UnfinalizedMoEOutput)
+ *   moe_fused_experts      the whole layer, finalized
+ *
+ * Conventions for every call
+ *   - Memory: the caller owns every buffer.  Pointers marked (device) must be
+ *     device memory of the current HIP device; nothing is allocated, freed or
+ *     copied between host and device by these calls, and the host never waits
+ *     for the device.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream), so every call can be captured into a HIP graph.
+ *   - Layout: arrays are dense and row-major with the shapes given, with no
+ *     padding between rows; bf16 arrays hold IEEE bfloat16 bit patterns.
+ *     Device pointers must be 16-byte aligned.
+ *   - Sizes are explicit arguments.  Nothing is inferred from a trailing
+ *     dimension, since packed 4-bit weights halve it (page "modular_kernel.py",
+ *     _moe_problem_size).
+ *   - Names: T tokens, H hidden size, I expert intermediate size, E global
+ *     experts, E_l local experts, k top_k, R = T*k routes, R_l routes to local
+ *     experts, R_pad >= R the row count of permuted buffers.
+ *   - Errors: each call returns MOE_OK (0) or a negative moe_status and
+ *     enqueues nothing when it fails; moe_last_error() gives a thread-local
+ *     message.  T = 0 is valid and enqueues nothing.
+ *   - Calls on one stream run in order; two calls that write the same buffer
+ *     on different streams race.
+ */
+#ifndef MOE_MI355X_MOE_H_
+#define MOE_MI355X_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  They mirror the checks of the output-contract page
+ * (convert_flashinfer_moe_output raises ValueError on: negative num_tokens,
+ * non-positive top_k, a deferred output given a destination, a non-int32 map,
+ * element counts other than num_tokens * top_k, mixed devices, non-contiguous
+ * buffers). */
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1,     /* T < 0, k <= 0, k > E, E_l > E, bad size  */
+  MOE_ERR_UNSUPPORTED = -2,          /* dtype, score function or activation tag  */
+  MOE_ERR_SIZE_MISMATCH = -3,        /* R_pad < T*k, workspace too small         */
+  MOE_ERR_MISALIGNED = -4,           /* a device pointer not 16-byte aligned     */
+  MOE_ERR_DEVICE = -5,               /* a pointer that is not device memory      */
+  MOE_ERR_DESTINATION_CONFLICT = -6, /* buffers that must not overlap do         */
+  MOE_ERR_HIP = -7                   /* the HIP runtime reported an error        */
+} moe_status;
+
+/* Router score functions. */
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+
+/* Element types. */
+enum {
+  MOE_DTYPE_BF16 = 0,  /* bfloat16                                              */
+  MOE_DTYPE_F32 = 1,   /* float32                                               */
+  MOE_DTYPE_MXFP4 = 2  /* e2m1 pairs (low nibble = even element) + one E8M0 scale
+                          byte per 32 elements along the reduction dimension    */
+};
+
+/* Activations of GEMM1 (page "modular_kernel.py", activation(): the output is
+ * half as wide as GEMM1's; "silu" gives silu(first half) * second half). */
+enum { MOE_ACT_SILU = 0 };
+
+/* Expert weights of one GEMM, all local experts, reduction dimension last:
+ *   BF16:  data = bf16 [E_l, N, K],   scales = NULL
+ *   MXFP4: data = u8 [E_l, N, K/2],   scales = u8 [E_l, N, K/32]
+ * (GEMM1: N = 2I, K = H, rows [0, I) gate and [I, 2I) up; GEMM2: N = H, K = I.)
+ * The tag matters: a buffer read as a wider type than it holds is garbage
+ * (page "moe_output.py", the comment on expert_weights). */
+typedef struct moe_weights {
+  int32_t dtype;
+  const void* data;      /* (device) */
+  const uint8_t* scales; /* (device) MXFP4 only */
+} moe_weights;
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Padded permuted row count this library uses for T tokens and top_k k:
+ * T*k rounded up to a multiple of 128 (0 for T = 0).  Any R_pad >= T*k is
+ * accepted; rows at or past the local route count are never read
+ * (page "moe_output.py": the padded row count is never referenced). */
+int64_t moe_permuted_rows(int64_t T, int32_t k);
+
+/* Workspace bytes moe_fused_experts and moe_fused_experts_unfinalized need
+ * for this problem; the workspace of moe_permute needs no more.  Host-only
+ * arithmetic.  Returns MOE_ERR_INVALID_ARGUMENT on bad sizes.  Mirrors
+ * FusedMoEPermuteExpertsUnpermute.workspace_shapes (page "modular_kernel.py"):
+ * the caller allocates, the library reuses. */
+int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, int32_t I,
+                       int32_t w_dtype, size_t* bytes);
+
+/* Router ([Router] stage).  For each token t the k experts with the largest
+ * logits, ordered by logit descending, ties to the smaller expert id, and
+ * their weights:
+ *   SOFTMAX: p = softmax over all E logits;   SIGMOID: p_e = 1/(1+exp(-l_e));
+ *   renormalize != 0: w_j = p_j / sum over the k selected p;  else w_j = p_j;
+ *   then w_j *= rsf (the routed scaling factor, folded into the weights as the
+ *   expert_weights comment of page "moe_output.py" describes).
+ *   logits       (device) fp32 [T, E]
+ *   topk_ids     (device) int32 [T, k]  out
+ *   topk_weights (device) fp32 [T, k]   out
+ * Limits: 1 <= k <= min(E, 32), E <= 1024. */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score_fn,
+                   int32_t renormalize, float rsf, int32_t* topk_ids, float* topk_weights,
+                   void* stream);
+
+/* Permute (single-GPU part of [Quantize-Dispatch]; prepare() of page
+ * "modular_kernel.py" with its expert_map and per-local-expert counts).
+ *   L(t,j) = expert_map[topk_ids[t,j]] (or topk_ids[t,j] when expert_map is
+ *   NULL); L = -1 marks an expert that is not local.
+ *   offsets[e] = number of local routes to local experts < e, e in [0, E_l];
+ *   offsets[E_l] = R_l.
+ *   map[t,j] = offsets[L] + (number of routes (t',j') to L with t'*k+j' <
+ *   t*k+j), or -1 when L = -1 (page "moe_output.py",
+ *   expanded_idx_to_permuted_idx).  The order is stable and deterministic.
+ *   inv[r] = t*k+j of the route placed in row r, for r < R_l; -1 for
+ *   R_l <= r < R_pad.
+ *   x_perm[r, :] = x[inv[r] / k, :] for r < R_l; rows >= R_l are not written.
+ *   topk_ids   (device) int32 [T, k]; an id outside [0, E) is a caller error
+ *              and is treated as a non-local route
+ *   expert_map (device) int32 [E] with entries in [-1, E_l), or NULL (E_l = E)
+ *   x          (device) bf16 [T, H]
+ *   map        (device) int32 [T, k]      out
+ *   offsets    (device) int32 [E_l + 1]   out
+ *   inv        (device) int32 [R_pad]     out, may be NULL
+ *   x_perm     (device) bf16 [R_pad, H]   out, may be NULL (no gather)
+ *   workspace  (device) scratch of moe_workspace_size() bytes, may be NULL
+ *              when workspace_bytes is 0 (this version needs none)
+ * Limits: E_l <= 1024, H a multiple of 8. */
+int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                int32_t E, int32_t E_l, const void* x, int32_t H, int64_t R_pad, int32_t* map,
+                int32_t* offsets, int32_t* inv, void* x_perm, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Grouped GEMM1 + activation (apply() and activation() of page
+ * "modular_kernel.py").  For every local expert e and row r in
+ * [offsets[e], offsets[e+1]):
+ *   g = a_perm[r, :] . W1[e, n, :],  u = a_perm[r, :] . W1[e, I + n, :]
+ *   h[r, n] = silu(g) * u   (fp32 accumulation, one rounding to bf16)
+ *   a_perm  (device) bf16 [R_pad, H]
+ *   offsets (device) int32 [E_l + 1] as written by moe_permute
+ *   w1      GEMM1 weights, N = 2I, K = H (BF16; MXFP4 returns UNSUPPORTED in
+ *           this version)
+ *   h       (device) bf16 [R_pad, I] out; rows >= offsets[E_l] not written
+ * Limits: H and I multiples of 64; R_pad >= offsets[E_l]. */
+int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                          int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
+                          void* h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped GEMM2 (apply() of page "modular_kernel.py"; its output is the
+ * unweighted, unreduced gemm2_permuted of page "moe_output.py": densely
+ * packed at H).  For every local expert e and row r in [offsets[e],
+ * offsets[e+1]):  y[r, n] = h[r, :] . W2[e, n, :]  (fp32 accumulation, bf16).
+ *   h       (device) bf16 [R_pad, I]
+ *   w2      GEMM2 weights, N = H, K = I
+ *   y       (device) bf16 [R_pad, H] out; rows >= offsets[E_l] not written
+ * Limits: H and I multiples of 64. */
+int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                      int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Finalize (finalize() of page "modular_kernel.py"; MoEOutput of page
+ * "moe_output.py": the routed scaling factor multiplies the routed sum before
+ * the shared-expert add).
+ *   out[t, :] = rsf_fin * sum_{j ascending, map[t,j] >= 0} w[t,j] * y[map[t,j], :]
+ *               + shared[t, :]
+ * fp32 accumulation, one rounding to bf16.  -1 entries are skipped, so rows
+ * the map never names are never read.  Every row of out is written (a token
+ * with no local route gets 0, or its shared row).
+ *   y_perm   (device) bf16 [>= R_l, H]
+ *   weights  (device) [T, k] of weights_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16)
+ *   map      (device) int32 [T, k]
+ *   shared   (device) bf16 [T, H] or NULL
+ *   out      (device) bf16 [T, H] out; may alias shared exactly (in place),
+ *            must not overlap y_perm
+ * Limits: H a multiple of 8, k <= 32. */
+int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
+                 const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
+                 const void* shared, void* out, void* stream);
+
+/* Deferred-finalize form (UnfinalizedMoEOutput of page "moe_output.py"): the
+ * router, permute and both GEMMs, stopping before the top-k reduction.
+ *   logits          (device) fp32 [T, E];  x (device) bf16 [T, H]
+ *   expert_map      (device) int32 [E] or NULL
+ *   gemm2_permuted  (device) bf16 [R_pad, H] out (unweighted GEMM2 rows)
+ *   expert_weights  (device) bf16 [T, k] out (the activation dtype, since this
+ *                   call routes itself), rsf already applied
+ *   map             (device) int32 [T, k] out (-1 = expert not local)
+ *   workspace       (device) >= moe_workspace_size() bytes, 256-byte aligned
+ * A deferred call takes no destination for the finalized output; pass the
+ * three buffers to moe_finalize (weights_dtype MOE_DTYPE_BF16) later. */
+int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
+                                  int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                                  int32_t renormalize, float rsf, const int32_t* expert_map,
+                                  const moe_weights* w1, const moe_weights* w2, int64_t R_pad,
+                                  void* gemm2_permuted, void* expert_weights, int32_t* map,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer, finalized:
+ *   out = rsf_fin * sum_j w_j * MLP_{L_j}(x) + shared MLP(x)
+ * with the shared expert (one dense SiLU MLP, intermediate shared_I, weights
+ * ws1 bf16 [2*shared_I, H] and ws2 bf16 [H, shared_I]) present when
+ * shared_I > 0.
+ *   out       (device) bf16 [T, H]; must not overlap x
+ *   workspace (device) >= moe_workspace_size() bytes (with the shared expert:
+ *             moe_workspace_size() + moe_shared_workspace_size()) */
+int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
+                      float rsf, const int32_t* expert_map, const moe_weights* w1,
+                      const moe_weights* w2, int32_t shared_I, const void* ws1, const void* ws2,
+                      float rsf_fin, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Extra workspace bytes moe_fused_experts needs for a shared expert of
+ * intermediate size shared_I (0 when shared_I = 0). */
+int moe_shared_workspace_size(int64_t T, int32_t H, int32_t shared_I, size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_MOE_H_ */

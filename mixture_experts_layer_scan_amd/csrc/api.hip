@@ -1,0 +1,488 @@
+// C ABI of the fused MoE layer: argument checks, workspace layout and the
+// call sequences of the fused entry points.  Every check runs on the host
+// before anything is enqueued; a failing call enqueues nothing.  The checks
+// follow convert_flashinfer_moe_output of vLLM's MoE output contract
+// (num_tokens >= 0, top_k > 0, int32 map, T * k elements, one device,
+// contiguous buffers, no destination for a deferred output).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool validate_pointers() {
+  static int mode = -1;
+  if (mode < 0) {
+    const char* v = getenv("MOE_VALIDATE");
+    mode = (v && v[0] && v[0] != '0') ? 1 : 0;
+  }
+  return mode == 1;
+}
+
+// Under MOE_VALIDATE=1: the pointer must be device memory (or managed).
+int check_device_ptr(const void* p, const char* name) {
+  if (!p || !validate_pointers()) return MOE_OK;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "%s is not a HIP allocation", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(MOE_ERR_DEVICE, "%s is not device memory", name);
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)            \
+  do {                             \
+    int _s = (expr);               \
+    if (_s != MOE_OK) return _s;   \
+  } while (0)
+
+int need_ptr(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_MISALIGNED, "%s must be 16-byte aligned", name);
+  return check_device_ptr(p, name);
+}
+
+int opt_ptr(const void* p, const char* name) {
+  if (!p) return MOE_OK;
+  if (!aligned16(p)) return fail(MOE_ERR_MISALIGNED, "%s must be 16-byte aligned", name);
+  return check_device_ptr(p, name);
+}
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return a && b && an && bn && x < y + bn && y < x + an;
+}
+
+int check_route_sizes(int64_t T, int32_t E, int32_t k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens must be non-negative (T=%lld)", (long long)T);
+  if (k <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be positive (k=%d)", k);
+  if (E <= 0 || E > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "E must be in [1, 1024] (E=%d)", E);
+  if (k > E || k > 32) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be <= min(E, 32) (k=%d, E=%d)", k, E);
+  if (T > (int64_t(1) << 31) / k) return fail(MOE_ERR_INVALID_ARGUMENT, "T * k must fit in int32");
+  return MOE_OK;
+}
+
+int check_local(int32_t E, int32_t E_l) {
+  if (E_l <= 0 || E_l > E || E_l > 1024)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "E_l must be in [1, min(E, 1024)] (E_l=%d, E=%d)", E_l, E);
+  return MOE_OK;
+}
+
+int check_gemm_dims(int32_t H, int32_t I) {
+  if (H <= 0 || H % 64) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 64 (H=%d)", H);
+  if (I <= 0 || I % 64) return fail(MOE_ERR_INVALID_ARGUMENT, "I must be a positive multiple of 64 (I=%d)", I);
+  return MOE_OK;
+}
+
+int check_weights(const moe_weights* w, const char* name) {
+  if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
+  if (w->dtype == MOE_DTYPE_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: MXFP4 weights are not supported by this build", name);
+  if (w->dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight dtype %d", name, w->dtype);
+  return need_ptr(w->data, name);
+}
+
+// The GEMMs address each operand through a buffer descriptor with a 32-bit
+// byte range: one expert's weights and the permuted rows must each span
+// less than 4 GiB.
+int check_gemm_extent(int64_t rows, int32_t K, int64_t N_total) {
+  const int64_t lim = int64_t(0xFFFFFFFF);
+  if (rows * K * 2 > lim) return fail(MOE_ERR_INVALID_ARGUMENT, "permuted rows span more than 4 GiB");
+  if (N_total * K * 2 > lim) return fail(MOE_ERR_INVALID_ARGUMENT, "one expert's weights span more than 4 GiB");
+  return MOE_OK;
+}
+
+int check_rpad(int64_t T, int32_t k, int64_t R_pad) {
+  if (R_pad < T * k) return fail(MOE_ERR_SIZE_MISMATCH, "R_pad (%lld) < T * k (%lld)", (long long)R_pad, (long long)(T * k));
+  if (R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "R_pad must fit in int32");
+  return MOE_OK;
+}
+
+struct Carve {
+  char* p;
+  size_t used = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* r = reinterpret_cast<T*>(p + used);
+    used += align_up(count * sizeof(T));
+    return r;
+  }
+};
+
+size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) {
+  const int64_t R_pad = moe_permuted_rows(T, k);
+  size_t b = 0;
+  b += align_up(sizeof(int32_t) * T * k);               // topk ids
+  b += align_up(sizeof(float) * T * k);                 // topk weights
+  b += align_up(sizeof(int32_t) * T * k);               // permute map (finalized form)
+  b += align_up(sizeof(int32_t) * (E_l + 1));           // offsets
+  b += align_up(sizeof(uint16_t) * R_pad * H);          // x_perm, then GEMM2 output
+  b += align_up(sizeof(uint16_t) * R_pad * I);          // h
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, score function or activation";
+    case MOE_ERR_SIZE_MISMATCH: return "size mismatch";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_DEVICE: return "pointer is not device memory";
+    case MOE_ERR_DESTINATION_CONFLICT: return "destination conflict";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_permuted_rows(int64_t T, int32_t k) {
+  if (T <= 0 || k <= 0) return 0;
+  return (T * k + 127) / 128 * 128;
+}
+
+int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, int32_t I,
+                       int32_t w_dtype, size_t* bytes) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  MOE_CHECK(check_gemm_dims(H, I));
+  if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown weight dtype %d", w_dtype);
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  *bytes = routed_ws_bytes(T, k, E_l, H, I);
+  return MOE_OK;
+}
+
+int moe_shared_workspace_size(int64_t T, int32_t H, int32_t shared_I, size_t* bytes) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens must be non-negative");
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  if (shared_I < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "shared_I must be >= 0");
+  if (shared_I == 0) {
+    *bytes = 0;
+    return MOE_OK;
+  }
+  MOE_CHECK(check_gemm_dims(H, shared_I));
+  *bytes = align_up(sizeof(int32_t) * 2) + align_up(sizeof(uint16_t) * T * shared_I) +
+           align_up(sizeof(uint16_t) * T * H);
+  return MOE_OK;
+}
+
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score_fn,
+                   int32_t renormalize, float rsf, int32_t* topk_ids, float* topk_weights,
+                   void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown score function %d", score_fn);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(logits, "logits"));
+  MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+  MOE_CHECK(need_ptr(topk_weights, "topk_weights"));
+  hipError_t e = moe::launch_route_topk(logits, T, E, k, score_fn, renormalize, rsf, topk_ids,
+                                        topk_weights, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_topk");
+}
+
+int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                int32_t E, int32_t E_l, const void* x, int32_t H, int64_t R_pad, int32_t* map,
+                int32_t* offsets, int32_t* inv, void* x_perm, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  if (x_perm && (H <= 0 || H % 8)) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8 (H=%d)", H);
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(opt_ptr(inv, "inv"));
+  MOE_CHECK(opt_ptr(x_perm, "x_perm"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(map, "map"));
+    if (x_perm) MOE_CHECK(need_ptr(x, "x"));
+  }
+  if (x_perm && overlap(x, sizeof(uint16_t) * T * H, x_perm, sizeof(uint16_t) * R_pad * H))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "x_perm must not overlap x");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Offsets (and the inverse map's padding) are written even for T = 0.
+  hipError_t e = moe::launch_permute(topk_ids, expert_map, T, k, E, E_l, map, offsets, inv, R_pad, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute");
+  if (x_perm && T > 0) {
+    e = moe::launch_gather_rows(x, map, T, k, H, x_perm, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute gather");
+  }
+  return MOE_OK;
+}
+
+static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                       int32_t K, int32_t N_out, int gated, const moe_weights* w, void* c,
+                       void* stream, const char* name) {
+  if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
+  if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
+  MOE_CHECK(check_weights(w, name));
+  MOE_CHECK(check_gemm_extent(R_pad, K, gated ? 2 * int64_t(N_out) : N_out));
+  if (R_pad == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(a, "input rows"));
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(need_ptr(c, "output rows"));
+  if (overlap(a, sizeof(uint16_t) * R_pad * K, c, sizeof(uint16_t) * R_pad * N_out))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
+  moe::GemmArgs g{a, w->data, offsets, E_l, K, N_out, gated, R_pad, c};
+  hipError_t e = moe::launch_grouped_gemm(g, R_pad, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, name);
+}
+
+int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                          int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
+                          void* h, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  MOE_CHECK(check_gemm_dims(H, I));
+  if (activation != MOE_ACT_SILU) return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, w1, h, stream, "moe_grouped_gemm1_act");
+}
+
+int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                      int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  MOE_CHECK(check_gemm_dims(H, I));
+  return gemm_common(h, offsets, E_l, R_pad, I, H, 0, w2, y, stream, "moe_grouped_gemm2");
+}
+
+int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
+                 const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
+                 const void* shared, void* out, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens must be non-negative (T=%lld)", (long long)T);
+  if (k <= 0 || k > 32) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be in [1, 32] (k=%d)", k);
+  if (H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8 (H=%d)", H);
+  if (weights_dtype != MOE_DTYPE_F32 && weights_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
+  MOE_CHECK(need_ptr(weights, "expert_weights"));
+  MOE_CHECK(need_ptr(map, "map"));
+  MOE_CHECK(opt_ptr(shared, "shared"));
+  MOE_CHECK(need_ptr(out, "out"));
+  const size_t out_bytes = sizeof(uint16_t) * T * H;
+  if (shared && shared != out && overlap(shared, out_bytes, out, out_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out must alias shared exactly or not overlap it");
+  if (overlap(y_perm, sizeof(uint16_t) * T * k * H, out, out_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap gemm2_permuted");
+  hipError_t e = moe::launch_finalize(y_perm, weights, weights_dtype == MOE_DTYPE_BF16, map, T, k, H,
+                                      rsf_fin, shared, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_finalize");
+}
+
+// Workspace of the routed part of the fused entry points (rows sized for
+// moe_permuted_rows(T, k); the GEMMs never touch rows past the local routes).
+struct RoutedWs {
+  int32_t* ids;
+  float* wts;
+  int32_t* map;
+  int32_t* offsets;
+  uint16_t* x_perm;  // gathered rows, later reused for the GEMM2 output
+  uint16_t* h;
+  int64_t rows;
+};
+
+static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) {
+  RoutedWs b;
+  b.rows = moe_permuted_rows(T, k);
+  b.ids = c.take<int32_t>(T * k);
+  b.wts = c.take<float>(T * k);
+  b.map = c.take<int32_t>(T * k);
+  b.offsets = c.take<int32_t>(E_l + 1);
+  b.x_perm = c.take<uint16_t>(b.rows * H);
+  b.h = c.take<uint16_t>(b.rows * I);
+  return b;
+}
+
+// Route, permute, GEMM1, GEMM2 on one stream.  map_out / y_out default to the
+// workspace copies; w_bf16_out, when given, receives bf16 routing weights.
+static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
+                      float rsf, const int32_t* expert_map, const moe_weights* w1,
+                      const moe_weights* w2, const RoutedWs& b, int32_t* map_out, void* y_out,
+                      uint16_t* w_bf16_out, hipStream_t s) {
+  int32_t* map = map_out ? map_out : b.map;
+  void* y = y_out ? y_out : b.x_perm;
+  hipError_t e = moe::launch_route_topk(logits, T, E, k, score_fn, renormalize, rsf, b.ids, b.wts,
+                                        w_bf16_out, s);
+  if (e != hipSuccess) return hip_fail(e, "route");
+  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s);
+  if (e != hipSuccess) return hip_fail(e, "permute");
+  e = moe::launch_gather_rows(x, map, T, k, H, b.x_perm, s);
+  if (e != hipSuccess) return hip_fail(e, "gather");
+  moe::GemmArgs g1{b.x_perm, w1->data, b.offsets, E_l, H, I, 1, b.rows, b.h};
+  e = moe::launch_grouped_gemm(g1, b.rows, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm1");
+  moe::GemmArgs g2{b.h, w2->data, b.offsets, E_l, I, H, 0, b.rows, y};
+  e = moe::launch_grouped_gemm(g2, b.rows, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm2");
+  return MOE_OK;
+}
+
+static int check_fused_args(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                            int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                            const int32_t* expert_map, const moe_weights* w1,
+                            const moe_weights* w2) {
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  MOE_CHECK(check_gemm_dims(H, I));
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown score function %d", score_fn);
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_weights(w1, "w1"));
+  MOE_CHECK(check_weights(w2, "w2"));
+  const int64_t rows = moe_permuted_rows(T, k);
+  MOE_CHECK(check_gemm_extent(rows, H, 2 * int64_t(I)));
+  MOE_CHECK(check_gemm_extent(rows, I, H));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(logits, "logits"));
+    MOE_CHECK(need_ptr(x, "x"));
+  }
+  return MOE_OK;
+}
+
+static int check_workspace(void* workspace, size_t have, size_t need) {
+  MOE_CHECK(need_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_ERR_SIZE_MISMATCH, "workspace too small (%zu < %zu bytes)", have, need);
+  return MOE_OK;
+}
+
+int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
+                                  int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                                  int32_t renormalize, float rsf, const int32_t* expert_map,
+                                  const moe_weights* w1, const moe_weights* w2, int64_t R_pad,
+                                  void* gemm2_permuted, void* expert_weights, int32_t* map,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2));
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
+  MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
+  MOE_CHECK(need_ptr(map, "map"));
+  MOE_CHECK(check_workspace(workspace, workspace_bytes, routed_ws_bytes(T, k, E_l, H, I)));
+  Carve c{static_cast<char*>(workspace)};
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I);
+  return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
+                    b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
+                    static_cast<hipStream_t>(stream));
+}
+
+int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
+                      float rsf, const int32_t* expert_map, const moe_weights* w1,
+                      const moe_weights* w2, int32_t shared_I, const void* ws1, const void* ws2,
+                      float rsf_fin, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2));
+  if (shared_I < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "shared_I must be >= 0");
+  if (shared_I > 0) {
+    MOE_CHECK(check_gemm_dims(H, shared_I));
+    MOE_CHECK(check_gemm_extent(T, H, 2 * int64_t(shared_I)));
+    MOE_CHECK(check_gemm_extent(T, shared_I, H));
+  }
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(out, "out"));
+  if (shared_I > 0) {
+    MOE_CHECK(need_ptr(ws1, "ws1"));
+    MOE_CHECK(need_ptr(ws2, "ws2"));
+  }
+  size_t shared_bytes = 0;
+  MOE_CHECK(moe_shared_workspace_size(T, H, shared_I, &shared_bytes));
+  MOE_CHECK(check_workspace(workspace, workspace_bytes,
+                            routed_ws_bytes(T, k, E_l, H, I) + shared_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carve c{static_cast<char*>(workspace)};
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I);
+  MOE_CHECK(run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1,
+                       w2, b, nullptr, nullptr, nullptr, s));
+  const uint16_t* shared_out = nullptr;
+  if (shared_I > 0) {
+    // the shared expert is one dense SiLU MLP: a single-expert grouped GEMM
+    // pair over all T rows of x
+    int32_t* s_off = c.take<int32_t>(2);
+    uint16_t* s_h = c.take<uint16_t>(T * shared_I);
+    uint16_t* s_y = c.take<uint16_t>(T * H);
+    hipError_t e = moe::launch_fill_i32(s_off, 2, 0, static_cast<int32_t>(T), s);
+    if (e != hipSuccess) return hip_fail(e, "shared offsets");
+    moe::GemmArgs g1{x, ws1, s_off, 1, H, shared_I, 1, T, s_h};
+    e = moe::launch_grouped_gemm(g1, T, s);
+    if (e != hipSuccess) return hip_fail(e, "shared gemm1");
+    moe::GemmArgs g2{s_h, ws2, s_off, 1, shared_I, H, 0, T, s_y};
+    e = moe::launch_grouped_gemm(g2, T, s);
+    if (e != hipSuccess) return hip_fail(e, "shared gemm2");
+    shared_out = s_y;
+  }
+  hipError_t e = moe::launch_finalize(b.x_perm, b.wts, 0, b.map, T, k, H, rsf_fin, shared_out,
+                                      out, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "finalize");
+}
+
+}  // extern "C"
+
+namespace moe {
+
+int device_cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+// Shared device helpers and host launch declarations of the MoE HIP library.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 (bit patterns in uint16_t) ------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & (kWave - 1)); }
+
+// Mask of lanes of this wave whose `key` equals this lane's, among lanes with
+// `active` set (0 for an inactive lane).  key must lie in [0, 2^nbits).
+__device__ __forceinline__ uint64_t wave_match(uint32_t key, bool active, int nbits) {
+  uint64_t peers = __ballot(active);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return active ? peers : 0ull;
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of one int per thread over a whole block of
+// blockDim.x <= 1024 threads.  `scratch` holds >= 16 ints of LDS.  Returns the
+// exclusive prefix; *total receives the block sum.  Contains __syncthreads().
+__device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  const int inc = wave_inclusive_sum(v);
+  if (lane == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int s = scratch[i];
+    if (i < w) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+}  // namespace moe
+
+// ---- host launchers (one per .hip file); each returns a hipError_t ----------
+namespace moe {
+
+struct GemmArgs {
+  const void* a;          // bf16 [R_pad, K]
+  const void* w;          // bf16 [E_l, N_total, K]
+  const int32_t* offsets; // [E_l + 1]
+  int E_l;
+  int K;
+  int N_out;              // output columns (I when gated, else N)
+  int gated;              // 1: GEMM1 with silu(gate) * up, N_total = 2 * N_out
+  int64_t R_pad;
+  void* c;                // bf16 [R_pad, N_out]
+};
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score_fn,
+                             int renormalize, float rsf, int32_t* ids, float* w,
+                             uint16_t* w_bf16, hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
+                          int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
+                          hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
+                              void* x_perm, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s);
+hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
+                           int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,
+                           hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,169 @@
+// Permute: the single-GPU part of [Quantize-Dispatch] of vLLM's modular
+// fused-MoE kernel (prepare() with its expert_map and per-local-expert counts)
+// producing the expanded_idx_to_permuted_idx map of vLLM's MoE output contract
+// (int32, -1 for an expert that is not local).
+//
+// Deterministic stable counting sort in one workgroup of 16 waves:
+//   - wave w owns a contiguous run of the expanded index x = t*k + j and walks
+//     it 64 routes at a time;
+//   - inside a step, lanes with equal local expert find each other with a
+//     ballot per key bit (wave_match); the lowest such lane adds the group
+//     size to the wave's LDS histogram row, so no atomics are needed;
+//   - a column scan over the 16 wave rows and a block scan over experts give
+//     every (wave, expert) pair its first output row;
+//   - the second walk ranks each lane among its peers with a popcount of the
+//     lower-lane mask, so the order within an expert is ascending x.
+// Rows are then gathered token-major: each token row is read once and written
+// to each of its (up to k) local slots with 16-byte accesses.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPermuteThreads = 1024;
+constexpr int kPermuteWaves = kPermuteThreads / kWave;
+
+__device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids,
+                                            const int32_t* __restrict__ emap, int64_t x, int E,
+                                            int E_l) {
+  const int id = ids[x];
+  if (id < 0 || id >= E) return -1;
+  const int L = emap ? emap[id] : id;
+  return (L >= 0 && L < E_l) ? L : -1;
+}
+
+__global__ __launch_bounds__(kPermuteThreads) void permute_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ emap, int64_t R, int E, int E_l,
+    int32_t* __restrict__ map, int32_t* __restrict__ offsets, int32_t* __restrict__ inv,
+    int64_t R_pad) {
+  extern __shared__ int32_t smem[];
+  int32_t* hist = smem;                                // [waves][E_l]
+  int32_t* scratch = smem + kPermuteWaves * E_l;       // 16 ints
+  __shared__ int32_t s_total;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  for (int i = threadIdx.x; i < kPermuteWaves * E_l; i += kPermuteThreads) hist[i] = 0;
+  __syncthreads();
+
+  const int64_t per_wave = ((R + kPermuteWaves * kWave - 1) / (kPermuteWaves * kWave)) * kWave;
+  const int64_t beg = w * per_wave;
+  const int64_t end = (beg + per_wave < R) ? beg + per_wave : R;
+  const int nbits = 32 - __clz(E_l);  // keys L + 1 lie in [0, E_l]
+  int32_t* my_hist = hist + w * E_l;
+
+  // Walk 1: per-wave histogram.
+  for (int64_t base = beg; base < end; base += kWave) {
+    const int64_t x = base + lane;
+    const bool valid = x < end;
+    const int L = valid ? local_expert(ids, emap, x, E, E_l) : -1;
+    const uint64_t peers = wave_match(static_cast<uint32_t>(L + 1), valid, nbits);
+    if (valid && L >= 0 && (peers & lt_mask) == 0ull) my_hist[L] += __popcll(peers);
+  }
+  __syncthreads();
+
+  // Column scan over waves: hist[w][e] becomes the count of routes to e in
+  // waves before w; the per-expert totals go through a block scan.
+  int cnt_total = 0;
+  const int e = threadIdx.x;  // E_l <= kPermuteThreads
+  if (e < E_l) {
+    for (int ww = 0; ww < kPermuteWaves; ++ww) {
+      const int c = hist[ww * E_l + e];
+      hist[ww * E_l + e] = cnt_total;
+      cnt_total += c;
+    }
+  }
+  int total = 0;
+  const int start = block_exclusive_sum(e < E_l ? cnt_total : 0, scratch, &total);
+  if (e < E_l) {
+    offsets[e] = start;
+    for (int ww = 0; ww < kPermuteWaves; ++ww) hist[ww * E_l + e] += start;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E_l] = total;
+    s_total = total;
+  }
+  __syncthreads();
+
+  // Walk 2: ranks, map and inverse map.
+  for (int64_t base = beg; base < end; base += kWave) {
+    const int64_t x = base + lane;
+    const bool valid = x < end;
+    const int L = valid ? local_expert(ids, emap, x, E, E_l) : -1;
+    const uint64_t peers = wave_match(static_cast<uint32_t>(L + 1), valid, nbits);
+    if (valid) {
+      if (L >= 0) {
+        const int slot = my_hist[L] + __popcll(peers & lt_mask);
+        map[x] = slot;
+        if (inv) inv[slot] = static_cast<int32_t>(x);
+      } else {
+        map[x] = -1;
+      }
+    }
+    // every lane has read its row of my_hist above before the leader adds
+    if (valid && L >= 0 && (peers & lt_mask) == 0ull) my_hist[L] += __popcll(peers);
+  }
+  if (inv) {
+    for (int64_t r = s_total + threadIdx.x; r < R_pad; r += kPermuteThreads) inv[r] = -1;
+  }
+}
+
+// x_perm[map[t, j], :] = x[t, :] for every local route of token t.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ map,
+                                                          int64_t T, int k, int H8,
+                                                          uint4* __restrict__ x_perm) {
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const int32_t* m = map + t * k;
+    const uint4* src = x + t * H8;
+    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
+      const uint4 v = src[c];
+      for (int j = 0; j < k; ++j) {
+        const int32_t r = m[j];
+        if (r >= 0) x_perm[static_cast<int64_t>(r) * H8 + c] = v;
+      }
+    }
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v0, int32_t step) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v0 + static_cast<int32_t>(i) * step;
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
+                          int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
+                          hipStream_t s) {
+  const size_t lds = sizeof(int32_t) * (static_cast<size_t>(kPermuteWaves) * E_l + 16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermuteThreads), lds, s, ids, emap, T * k, E,
+                     E_l, map, offsets, inv, R_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
+                              void* x_perm, hipStream_t s) {
+  const int64_t blocks = T < 8192 ? T : 8192;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), map, T, k, H / 8, static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s) {
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks > 0 ? blocks : 1)),
+                     dim3(256), 0, s, p, n, v0, step);
+  return hipGetLastError();
+}
+
+}  // namespace moe

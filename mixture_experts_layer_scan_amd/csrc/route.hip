@@ -1,0 +1,129 @@
+// Router: top-k experts per token and their weights (the [Router] stage of
+// vLLM's modular fused-MoE kernel; the weights carry the routed scaling factor
+// as the expert_weights comment of vLLM's MoE output contract describes).
+//
+// One wave per token.  Lane l holds logits l, l+64, l+128, ... in registers.
+// Each of the k rounds takes a wave-wide argmax under the order
+// (logit descending, expert id ascending) with an xor butterfly, so every lane
+// ends the round with the same winner; the winning element is marked taken.
+// Lane j keeps the j-th winner, so the k results end up in lanes 0..k-1 and
+// are stored with one coalesced write.  Selection compares fp32 logits only
+// (no arithmetic), so the chosen ids are exact.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t T, int E, int k, int score_fn,
+                                                         int renormalize, float rsf,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w,
+                                                         uint16_t* __restrict__ w_bf16) {
+  const int lane = lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // whole wave leaves together
+  const float* row = logits + t * E;
+
+  float v[EPL];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = i * kWave + lane;
+    v[i] = (e < E) ? row[e] : -INFINITY;
+    if (e >= E) taken |= 1u << i;
+  }
+
+  float my_v = -INFINITY;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = i * kWave + lane;
+      if (!((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oi = __shfl_xor(bi, off, kWave);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == j) {
+      my_v = bv;
+      my_id = bi;
+    }
+  }
+
+  // Scores of the selected experts (lanes < k) and the normaliser.
+  const bool sel = lane < k;
+  const float vmax = __shfl(my_v, 0, kWave);  // the first pick is the largest logit
+  float p = 0.0f;
+  if (score_fn == 0) {
+    p = sel ? expf(my_v - vmax) : 0.0f;
+  } else {
+    p = sel ? 1.0f / (1.0f + expf(-my_v)) : 0.0f;
+  }
+  float denom = 1.0f;
+  if (renormalize) {
+    float s = p;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    denom = s;
+  } else if (score_fn == 0) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = i * kWave + lane;
+      if (e < E) s += expf(v[i] - vmax);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    denom = s;
+  }
+  if (sel) {
+    const float wt = p / denom * rsf;
+    ids[t * k + lane] = my_id;
+    w[t * k + lane] = wt;
+    if (w_bf16) w_bf16[t * k + lane] = f32_to_bf16(wt);
+  }
+}
+
+template <int EPL>
+hipError_t launch_epl(const float* logits, int64_t T, int E, int k, int score_fn, int renorm,
+                      float rsf, int32_t* ids, float* w, uint16_t* w_bf16, hipStream_t s) {
+  const int per_block = 4;
+  const int64_t blocks = (T + per_block - 1) / per_block;
+  hipLaunchKernelGGL(route_topk_kernel<EPL>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(per_block * kWave), 0, s, logits, T, E, k, score_fn, renorm, rsf, ids,
+                     w, w_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score_fn,
+                             int renormalize, float rsf, int32_t* ids, float* w,
+                             uint16_t* w_bf16, hipStream_t s) {
+  const int epl = (E + kWave - 1) / kWave;
+  if (epl <= 1) return launch_epl<1>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+  if (epl <= 2) return launch_epl<2>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+  if (epl <= 4) return launch_epl<4>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+  if (epl <= 8) return launch_epl<8>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+  return launch_epl<16>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+}
+
+}  // namespace moe

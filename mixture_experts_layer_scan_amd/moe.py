@@ -1,0 +1,323 @@
+"""Python binding of the C ABI in include/moe.h (argument marshalling only).
+
+Every function has the name of the C call it wraps.  It checks what the MoE
+output contract checks of its buffers (shape, dtype, device, contiguity),
+allocates missing outputs with torch on the input's device, passes raw
+pointers and the current HIP stream (or the given one) to the library and
+raises ``MoeError`` on a non-zero status.  All arithmetic happens in the HIP
+kernels; nothing here computes on the data.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import MoeWeightsC, lib
+
+SOFTMAX, SIGMOID = 0, 1
+DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4 = 0, 1, 2
+ACT_SILU = 0
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        L = lib()
+        raise MoeError(status, f"{name}: {L.moe_status_string(status).decode()}: "
+                               f"{L.moe_last_error().decode()}")
+
+
+def _stream(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+class Weights:
+    """Expert weights of one GEMM: bf16 [E_l, N, K], or MXFP4 packed uint8
+    [E_l, N, K/2] with uint8 E8M0 scales [E_l, N, K/32]."""
+
+    def __init__(self, data: torch.Tensor, scales: Optional[torch.Tensor] = None):
+        if scales is None:
+            _need(data, "weights", torch.bfloat16)
+            self.dtype = DTYPE_BF16
+        else:
+            _need(data, "weights", torch.uint8)
+            _need(scales, "scales", torch.uint8, device=data.device)
+            self.dtype = DTYPE_MXFP4
+        if data.dim() != 3:
+            raise ValueError("weights must be rank-3 [E_l, N, K(/2)]")
+        self.data, self.scales = data, scales
+        self.c = MoeWeightsC(self.dtype, data.data_ptr(), _ptr(scales))
+
+    @property
+    def E_l(self) -> int:
+        return self.data.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.data.shape[1]
+
+    @property
+    def K(self) -> int:
+        k = self.data.shape[2]
+        return k * 2 if self.dtype == DTYPE_MXFP4 else k
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def moe_permuted_rows(T: int, k: int) -> int:
+    return int(lib().moe_permuted_rows(T, k))
+
+
+def moe_workspace_size(T: int, k: int, E: int, E_l: int, H: int, I: int,
+                       w_dtype: int = DTYPE_BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(T, k, E, E_l, H, I, w_dtype, ctypes.byref(n)),
+           "moe_workspace_size")
+    return int(n.value)
+
+
+def moe_shared_workspace_size(T: int, H: int, shared_I: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_shared_workspace_size(T, H, shared_I, ctypes.byref(n)),
+           "moe_shared_workspace_size")
+    return int(n.value)
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, score_fn: int = SOFTMAX, renormalize: bool = True,
+                   rsf: float = 1.0, topk_ids: Optional[torch.Tensor] = None,
+                   topk_weights: Optional[torch.Tensor] = None, stream=None):
+    """-> (topk_ids int32 [T, k], topk_weights float32 [T, k])."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be rank-2 [T, E]")
+    T, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, (T, k), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, k), dev)
+    _check(lib().moe_route_topk(logits.data_ptr(), T, E, k, score_fn, int(bool(renormalize)),
+                                float(rsf), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                                _stream(stream)), "moe_route_topk")
+    return topk_ids, topk_weights
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
+                expert_map: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+                R_pad: Optional[int] = None, map: Optional[torch.Tensor] = None,
+                offsets: Optional[torch.Tensor] = None, inv: Optional[torch.Tensor] = None,
+                x_perm: Optional[torch.Tensor] = None, want_inv: bool = True, stream=None):
+    """-> dict(map [T,k] int32, offsets [E_l+1] int32, inv [R_pad] int32 or None,
+    x_perm [R_pad, H] bf16 or None, R_pad)."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    E_l = E if E_l is None else E_l
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    H = 0
+    if x is not None:
+        _need(x, "x", torch.bfloat16, device=dev)
+        if x.dim() != 2 or x.shape[0] != T:
+            raise ValueError("x must be [T, H]")
+        H = x.shape[1]
+        if x_perm is None:
+            x_perm = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+        _need(x_perm, "x_perm", torch.bfloat16, (R_pad, H), dev)
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty((E_l + 1,), dtype=torch.int32, device=dev)
+    if inv is None and want_inv and R_pad > 0:
+        inv = torch.empty((R_pad,), dtype=torch.int32, device=dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    _need(offsets, "offsets", torch.int32, (E_l + 1,), dev)
+    if inv is not None:
+        _need(inv, "inv", torch.int32, (R_pad,), dev)
+    _check(lib().moe_permute(topk_ids.data_ptr(), _ptr(expert_map), T, k, E, E_l, _ptr(x), H,
+                             R_pad, map.data_ptr(), offsets.data_ptr(), _ptr(inv), _ptr(x_perm),
+                             None, 0, _stream(stream)), "moe_permute")
+    return {"map": map, "offsets": offsets, "inv": inv, "x_perm": x_perm, "R_pad": R_pad}
+
+
+def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weights, I: int,
+                          h: Optional[torch.Tensor] = None, activation: int = ACT_SILU,
+                          stream=None) -> torch.Tensor:
+    """h[r] = silu(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I]."""
+    _need(a_perm, "a_perm", torch.bfloat16)
+    R_pad, H = a_perm.shape
+    dev = a_perm.device
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    _check(lib().moe_grouped_gemm1_act(a_perm.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I,
+                                       w1.ref(), activation, h.data_ptr(), None, 0,
+                                       _stream(stream)), "moe_grouped_gemm1_act")
+    return h
+
+
+def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: int,
+                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[r] = h[r] W2[e]^T -> bf16 [R_pad, H] (unweighted gemm2_permuted)."""
+    _need(h, "h", torch.bfloat16)
+    R_pad, I = h.shape
+    dev = h.device
+    _need(offsets, "offsets", torch.int32, (w2.E_l + 1,), dev)
+    if w2.N != H or w2.K != I:
+        raise ValueError(f"w2 must be [E_l, H={H}, I={I}]")
+    if y is None:
+        y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (R_pad, H), dev)
+    _check(lib().moe_grouped_gemm2(h.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
+                                   y.data_ptr(), None, 0, _stream(stream)), "moe_grouped_gemm2")
+    return y
+
+
+def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor, map: torch.Tensor,
+                 rsf_fin: float = 1.0, shared: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = rsf_fin * sum_{map>=0} w * Y[map] + shared[t] -> bf16 [T, H]."""
+    _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16)
+    if gemm2_permuted.dim() != 2:
+        raise ValueError("gemm2_permuted must be rank-2")
+    H = gemm2_permuted.shape[1]
+    dev = gemm2_permuted.device
+    _need(map, "map", torch.int32, device=dev)
+    if map.dim() != 2:
+        raise ValueError("map must be [T, k]")
+    T, k = map.shape
+    if expert_weights.dtype == torch.float32:
+        wdt = DTYPE_F32
+    elif expert_weights.dtype == torch.bfloat16:
+        wdt = DTYPE_BF16
+    else:
+        raise ValueError("expert_weights must be float32 or bfloat16")
+    _need(expert_weights, "expert_weights", expert_weights.dtype, device=dev)
+    if expert_weights.numel() != T * k:
+        raise ValueError(f"expert_weights must have T * k = {T * k} elements")
+    if shared is not None:
+        _need(shared, "shared", torch.bfloat16, (T, H), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _check(lib().moe_finalize(gemm2_permuted.data_ptr(), expert_weights.data_ptr(), wdt,
+                              map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
+                              out.data_ptr(), _stream(stream)), "moe_finalize")
+    return out
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: Weights,
+                                  k: int, score_fn: int = SOFTMAX, renormalize: bool = True,
+                                  rsf: float = 1.0, expert_map: Optional[torch.Tensor] = None,
+                                  R_pad: Optional[int] = None,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  gemm2_permuted: Optional[torch.Tensor] = None,
+                                  expert_weights: Optional[torch.Tensor] = None,
+                                  map: Optional[torch.Tensor] = None, stream=None):
+    """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k])."""
+    _need(logits, "logits", torch.float32)
+    _need(x, "x", torch.bfloat16, device=logits.device)
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w2.K
+    dev = x.device
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    if gemm2_permuted is None:
+        gemm2_permuted = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    if expert_weights is None:
+        expert_weights = torch.empty((T, k), dtype=torch.bfloat16, device=dev)
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16, (R_pad, H), dev)
+    _need(expert_weights, "expert_weights", torch.bfloat16, (T, k), dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    nbytes = moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) if T > 0 else 0
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().moe_fused_experts_unfinalized(
+        logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
+        float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), R_pad, gemm2_permuted.data_ptr(),
+        expert_weights.data_ptr(), map.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
+        "moe_fused_experts_unfinalized")
+    return gemm2_permuted, expert_weights, map
+
+
+def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: Weights, k: int,
+                      score_fn: int = SOFTMAX, renormalize: bool = True, rsf: float = 1.0,
+                      expert_map: Optional[torch.Tensor] = None,
+                      ws1: Optional[torch.Tensor] = None, ws2: Optional[torch.Tensor] = None,
+                      rsf_fin: float = 1.0, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is])."""
+    _need(logits, "logits", torch.float32)
+    _need(x, "x", torch.bfloat16, device=logits.device)
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w2.K
+    dev = x.device
+    shared_I = 0
+    if ws1 is not None or ws2 is not None:
+        _need(ws1, "ws1", torch.bfloat16, device=dev)
+        _need(ws2, "ws2", torch.bfloat16, device=dev)
+        shared_I = ws2.shape[1]
+        if tuple(ws1.shape) != (2 * shared_I, H) or tuple(ws2.shape) != (H, shared_I):
+            raise ValueError("shared weights must be ws1 [2*Is, H] and ws2 [H, Is]")
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    nbytes = 0
+    if T > 0:
+        nbytes = (moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) +
+                  moe_shared_workspace_size(T, H, shared_I))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().moe_fused_experts(
+        logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
+        float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), shared_I, _ptr(ws1), _ptr(ws2),
+        float(rsf_fin), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
+        "moe_fused_experts")
+    return out

@@ -11,8 +11,8 @@
  *   - SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast splittable pseudorandom
  *     number generators", OOPSLA 2014; constants as published by S. Vigna)
  *     hashes the counter into 64 random bits.
- *   - Box-Muller (G. Box, M. Muller, 1958) turns two uniforms into one normal
- *     (the cosine branch only).
+ *   - Box-Muller (G. Box, M. Muller, 1958) turns the uniforms of counters 2p
+ *     and 2p+1 into the normals of elements 2p (cosine) and 2p+1 (sine).
  *
  * MXFP4 encoder (input construction only; the format is the OCP Microscaling
  * v1.0 one: e2m1 elements, one E8M0 scale per 32 elements along K):
@@ -37,13 +37,25 @@ static inline uint64_t stream_key(uint64_t seed, uint64_t tensor_id) {
   return sm64(sm64(seed) ^ (tensor_id * 0xD1B54A32D192ED03ull + 0x8CB92BA72F3D8DD7ull));
 }
 
+/* Standard normals 2p and 2p+1 of the stream with the given key: one
+ * Box-Muller pair (cosine branch for the even index, sine for the odd). */
+static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+  uint64_t r1 = sm64(key + 2 * p);
+  uint64_t r2 = sm64(key + 2 * p + 1);
+  /* single precision is plenty for test data: u1 in (0, 1] on a 2^-24 grid */
+  float u1 = (float)((r1 >> 40) + 1) * (1.0f / 16777216.0f);
+  float u2 = (float)(r2 >> 40) * (1.0f / 16777216.0f);
+  float r = sqrtf(-2.0f * logf(u1));
+  float th = 6.2831853071795864769f * u2;
+  *z0 = (double)(r * cosf(th));
+  *z1 = (double)(r * sinf(th));
+}
+
 /* Standard normal number i of the stream with the given key. */
 static inline double normal_at(uint64_t key, uint64_t i) {
-  uint64_t r1 = sm64(key + 2 * i);
-  uint64_t r2 = sm64(key + 2 * i + 1);
-  double u1 = (double)((r1 >> 11) + 1) * (1.0 / 9007199254740992.0); /* (0, 1] */
-  double u2 = (double)(r2 >> 11) * (1.0 / 9007199254740992.0);       /* [0, 1) */
-  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925 * u2);
+  double z0, z1;
+  normal_pair(key, i >> 1, &z0, &z1);
+  return (i & 1) ? z1 : z0;
 }
 
 static inline uint16_t f32_to_bf16(float f) {
@@ -77,7 +89,12 @@ void synth_normal_f32(uint64_t seed, uint64_t tensor_id, int64_t n, double mean,
                       float* out) {
   const uint64_t key = stream_key(seed, tensor_id);
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) out[i] = (float)(mean + std * normal_at(key, (uint64_t)i));
+  for (int64_t p = 0; p < (n + 1) / 2; ++p) {
+    double z0, z1;
+    normal_pair(key, (uint64_t)p, &z0, &z1);
+    out[2 * p] = (float)(mean + std * z0);
+    if (2 * p + 1 < n) out[2 * p + 1] = (float)(mean + std * z1);
+  }
 }
 
 /* Same draw as synth_normal_f32, then rounded to bf16 (nearest, ties to even). */
@@ -85,8 +102,12 @@ void synth_normal_bf16(uint64_t seed, uint64_t tensor_id, int64_t n, double mean
                        uint16_t* out) {
   const uint64_t key = stream_key(seed, tensor_id);
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i)
-    out[i] = f32_to_bf16((float)(mean + std * normal_at(key, (uint64_t)i)));
+  for (int64_t p = 0; p < (n + 1) / 2; ++p) {
+    double z0, z1;
+    normal_pair(key, (uint64_t)p, &z0, &z1);
+    out[2 * p] = f32_to_bf16((float)(mean + std * z0));
+    if (2 * p + 1 < n) out[2 * p + 1] = f32_to_bf16((float)(mean + std * z1));
+  }
 }
 
 /* Row-biased fp32 logits: out[t*E+e] = (float)(N_{t*E+e} + bias[e]). */

@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (so these run on a machine with no GPU).  The error cases follow the
+checks of convert_flashinfer_moe_output in vLLM's MoE output contract."""
+import ctypes
+
+import pytest
+
+from mixture_experts_layer_scan_amd import _lib
+
+OK, INVALID, UNSUPPORTED, SIZE, MISALIGNED, DEVICE, CONFLICT, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+P = 0x10000  # a fake, 16-byte aligned "device" pointer: never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(L):
+    declared = _lib.header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(_lib.PROTOTYPES) == set(declared)
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, UNSUPPORTED, SIZE, MISALIGNED, DEVICE, CONFLICT, HIP):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(-99) == b"unknown status"
+
+
+def test_permuted_rows(L):
+    assert L.moe_permuted_rows(0, 8) == 0
+    assert L.moe_permuted_rows(1, 8) == 128
+    assert L.moe_permuted_rows(16, 8) == 128
+    assert L.moe_permuted_rows(17, 8) == 256
+    assert L.moe_permuted_rows(4096, 2) == 8192
+
+
+def _ws(L, T, k, E, El, H, I, dt=0):
+    n = ctypes.c_size_t(0)
+    s = L.moe_workspace_size(T, k, E, El, H, I, dt, ctypes.byref(n))
+    return s, n.value
+
+
+def test_workspace_size(L):
+    s, n = _ws(L, 2048, 8, 256, 256, 7168, 2048)
+    assert s == OK
+    R = 2048 * 8
+    assert n >= R * (7168 + 2048) * 2 + 3 * R * 4
+    assert _ws(L, -1, 8, 256, 256, 7168, 2048)[0] == INVALID
+    assert _ws(L, 16, 0, 8, 8, 128, 256)[0] == INVALID
+    assert _ws(L, 16, 2, 8, 8, 100, 256)[0] == INVALID      # H not a multiple of 64
+    assert _ws(L, 16, 2, 8, 9, 128, 256)[0] == INVALID      # E_l > E
+    assert _ws(L, 16, 2, 8, 8, 128, 256, 7)[0] == UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert L.moe_shared_workspace_size(2048, 7168, 0, ctypes.byref(n)) == OK and n.value == 0
+    assert L.moe_shared_workspace_size(2048, 7168, 2048, ctypes.byref(n)) == OK
+    assert n.value >= 2048 * (7168 + 2048) * 2
+
+
+def test_route_errors(L):
+    r = L.moe_route_topk
+    assert r(P, -1, 8, 2, 0, 1, 1.0, P, P, None) == INVALID
+    assert b"non-negative" in L.moe_last_error()
+    assert r(P, 4, 8, 0, 0, 1, 1.0, P, P, None) == INVALID
+    assert b"positive" in L.moe_last_error()
+    assert r(P, 4, 8, 9, 0, 1, 1.0, P, P, None) == INVALID   # k > E
+    assert r(P, 4, 2048, 2, 0, 1, 1.0, P, P, None) == INVALID  # E > 1024
+    assert r(P, 4, 8, 2, 5, 1, 1.0, P, P, None) == UNSUPPORTED
+    assert r(P + 4, 4, 8, 2, 0, 1, 1.0, P, P, None) == MISALIGNED
+    assert r(None, 4, 8, 2, 0, 1, 1.0, P, P, None) == INVALID
+    assert r(None, 0, 8, 2, 0, 1, 1.0, None, None, None) == OK  # T = 0: nothing to do
+
+
+def test_permute_errors(L):
+    f = L.moe_permute
+    # R_pad < T * k
+    assert f(P, None, 16, 2, 8, 8, P, 128, 31, P, P, P, P, None, 0, None) == SIZE
+    # no expert map but E_l != E
+    assert f(P, None, 16, 2, 8, 4, P, 128, 32, P, P, P, P, None, 0, None) == INVALID
+    # H not a multiple of 8 with a gather
+    assert f(P, None, 16, 2, 8, 8, P, 100, 32, P, P, P, P, None, 0, None) == INVALID
+    # x_perm overlapping x
+    assert f(P, None, 16, 2, 8, 8, P, 128, 32, P, P, P, P + 64, None, 0, None) == CONFLICT
+
+
+def _w(dtype=0, data=P, scales=None):
+    return ctypes.byref(_lib.MoeWeightsC(dtype, data, scales))
+
+
+def test_gemm_errors(L):
+    g1 = L.moe_grouped_gemm1_act
+    assert g1(P, P, 8, 128, 100, 256, _w(), 0, P * 64, None, 0, None) == INVALID  # H % 64
+    assert g1(P, P, 8, 128, 128, 256, _w(), 3, P * 64, None, 0, None) == UNSUPPORTED
+    assert g1(P, P, 8, 128, 128, 256, _w(9), 0, P * 64, None, 0, None) == UNSUPPORTED
+    assert g1(P, P, 8, 128, 128, 256, None, 0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, 8, 128, 128, 256, _w(), 0, P, None, 0, None) == CONFLICT  # h == a_perm
+    assert g1(P, P, 0, 128, 128, 256, _w(), 0, P * 64, None, 0, None) == INVALID  # E_l = 0
+    g2 = L.moe_grouped_gemm2
+    assert g2(P, P, 8, 128, 256, 130, _w(), P * 64, None, 0, None) == INVALID
+    # one expert's weights over 4 GiB cannot be addressed
+    assert g2(P, P, 8, 128, 65536, 65536, _w(), P * 64, None, 0, None) == INVALID
+
+
+def test_finalize_errors(L):
+    f = L.moe_finalize
+    assert f(P, P, 1, P, -1, 2, 128, 1.0, None, P * 8, None) == INVALID
+    assert f(P, P, 1, P, 16, 0, 128, 1.0, None, P * 8, None) == INVALID
+    assert f(P, P, 3, P, 16, 2, 128, 1.0, None, P * 8, None) == UNSUPPORTED  # int32 weights
+    assert f(P, P, 1, P, 16, 2, 130, 1.0, None, P * 8, None) == INVALID
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, P + 256, None) == CONFLICT  # out inside y
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, P * 4 + 16, P * 4, None) == CONFLICT  # partial alias
+    assert f(P, P, 1, P, 0, 2, 128, 1.0, None, None, None) == OK  # T = 0
+
+
+def test_fused_errors(L):
+    u = L.moe_fused_experts_unfinalized
+    args = dict(logits=P, x=P, T=16, H=128, I=256, E=8, El=8, k=2, score=0, renorm=1, rsf=1.0,
+                emap=None, w1=_w(), w2=_w(), R_pad=32, y=P, w=P, m=P, ws=P, wsb=1 << 30, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return u(*a.values())
+    assert call(T=-1) == INVALID
+    assert call(k=0) == INVALID
+    assert call(R_pad=31) == SIZE
+    assert call(wsb=1024) == SIZE
+    assert call(ws=P + 16) == MISALIGNED
+    assert call(w1=_w(7, P, P)) == UNSUPPORTED
+    assert call(El=4) == INVALID  # no map, E_l != E
+    assert call(T=0) == OK

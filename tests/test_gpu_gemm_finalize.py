@@ -1,0 +1,148 @@
+"""GPU parity of the grouped GEMMs and of finalize against the oracle, each on
+its own, at sizes that span several tiles with ragged tails, for every tile
+shape the library picks (the shape follows the mean rows per local expert:
+>= 512, >= 128, >= 48, below).
+
+Bar: relative Frobenius error <= 1e-2 for bf16 outputs against the float64
+oracle (the GPU accumulates in fp32 and rounds once to bf16: expected ~3e-3).
+Rows the kernels must not touch are checked untouched, and NaN planted in
+rows they must not read must not reach the outputs."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_scan_amd as moe
+import oracle
+import synth
+from synth import configs
+
+from gpu_util import dev, dev_bf16, host_bf16_bits, host_f64, need_gpu, rel_fro, segments_of
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+NAN_BITS = 0x7FC0
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+GEMM_CASES = [
+    # name, counts per local expert, H, I
+    ("thin_tiles", [0, 1, 5, 33, 2, 0, 17, 40], 256, 192),
+    ("slim_tiles", [70, 0, 130, 55], 384, 320),
+    ("mid_tiles", [300, 1, 420], 256, 448),
+    ("big_tiles", [700, 613], 512, 384),
+    ("one_expert_many_rows", [1100], 256, 256),
+]
+
+
+def _setup(counts, H, I, seed):
+    E_l = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R_l = int(offsets[-1])
+    R_pad = ((R_l + 127) // 128) * 128
+    a = synth.normal_bf16(seed, 0, (R_pad, H))
+    a[R_l:] = NAN_BITS  # never read
+    w1 = synth.normal_bf16(seed, 2, (E_l, 2 * I, H), std=1 / np.sqrt(H))
+    w2 = synth.normal_bf16(seed, 3, (E_l, H, I), std=1 / np.sqrt(I))
+    return E_l, offsets, R_l, R_pad, a, w1, w2
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_gemm1_act(case):
+    name, counts, H, I = case
+    E_l, offsets, R_l, R_pad, a, w1, w2 = _setup(counts, H, I, seed=sum(counts))
+    h = torch.full((R_pad, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm1_act(dev_bf16(a), dev(offsets), moe.Weights(dev_bf16(w1)), I, h=h)
+    torch.cuda.synchronize()
+    eor = segments_of(offsets, R_l)
+    ref = oracle.hidden_rows(a[:R_l], oracle.Weights(w1), eor, I)
+    got = host_f64(h)
+    assert rel_fro(got[:R_l], ref) < TOL
+    assert np.all(host_bf16_bits(h)[R_l:] == NAN_BITS)
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_gemm2(case):
+    name, counts, H, I = case
+    E_l, offsets, R_l, R_pad, a, w1, w2 = _setup(counts, H, I, seed=sum(counts) + 1)
+    hb = synth.normal_bf16(sum(counts), 7, (R_pad, I))
+    hb[R_l:] = NAN_BITS
+    y = torch.full((R_pad, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm2(dev_bf16(hb), dev(offsets), moe.Weights(dev_bf16(w2)), H, y=y)
+    torch.cuda.synchronize()
+    eor = segments_of(offsets, R_l)
+    ref = oracle.out_rows(hb[:R_l], oracle.Weights(w2), eor, H)
+    assert rel_fro(host_f64(y)[:R_l], ref) < TOL
+    assert np.all(host_bf16_bits(y)[R_l:] == NAN_BITS)
+
+
+def test_gemm_deterministic():
+    E_l, offsets, R_l, R_pad, a, w1, w2 = _setup([300, 1, 420], 256, 448, seed=99)
+    outs = []
+    for _ in range(2):
+        h = moe.moe_grouped_gemm1_act(dev_bf16(a), dev(offsets), moe.Weights(dev_bf16(w1)), 448)
+        outs.append(host_bf16_bits(h)[:R_l])
+    assert np.array_equal(outs[0], outs[1])
+
+
+FIN_CASES = [
+    # name, T, E, E_l (None: all local), k, H, weights dtype, shared
+    ("tiny_f32", 16, 8, None, 2, 128, torch.float32, False),
+    ("deepseek_shared_f32", 64, 256, None, 8, 7168, torch.float32, True),
+    ("ep_rank_bf16", 64, 256, 32, 8, 7168, torch.bfloat16, False),
+    ("ep_rank_single_token", 1, 256, 32, 8, 7168, torch.bfloat16, False),
+    ("mixtral_f32", 512, 8, None, 2, 4096, torch.float32, False),
+]
+
+
+@pytest.mark.parametrize("case", FIN_CASES, ids=[c[0] for c in FIN_CASES])
+def test_finalize(case):
+    name, T, E, E_l, k, H, wdt, with_shared = case
+    seed = T + H
+    logits = synth.normal_f32(seed, 1, (T, E))
+    ids, w = oracle.route(logits, k, 1, True, 2.5)
+    emap = None
+    if E_l is not None:
+        emap = configs.expert_map(configs.EP_DECODE)
+    m, off, _ = oracle.permute(ids, E, E_l or E, emap)
+    R_l = int(off[-1])
+    R_pad = configs.permuted_rows(T, k)
+    y = synth.normal_bf16(seed, 2, (R_pad, H))
+    y[R_l:] = NAN_BITS
+    shared = synth.normal_bf16(seed, 5, (T, H)) if with_shared else None
+    w_dev = dev(w.astype(np.float32))
+    if wdt == torch.bfloat16:
+        w_dev = w_dev.to(torch.bfloat16)
+    w_used = host_f64(w_dev)  # the oracle gets the weights the kernel reads
+    out = moe.moe_finalize(dev_bf16(y), w_dev, dev(m), 1.0,
+                           None if shared is None else dev_bf16(shared))
+    torch.cuda.synchronize()
+    ref = oracle.finalize(y, w_used, m, 1.0, shared)
+    got = host_f64(out)
+    assert np.all(np.isfinite(got))
+    assert rel_fro(got, ref) < TOL
+    # tokens with no local route get exactly 0 (or exactly their shared row)
+    none = np.all(m < 0, axis=1)
+    if none.any():
+        want = synth.bf16_bits_to_f32(shared[none]) if with_shared else 0.0
+        assert np.all(got[none] == want)
+
+
+def test_finalize_in_place_over_shared_and_rsf():
+    T, k, H = 32, 2, 256
+    logits = synth.normal_f32(5, 1, (T, 8))
+    ids, w = oracle.route(logits, k, 0, True, 1.0)
+    m, off, _ = oracle.permute(ids, 8, 8)
+    y = synth.normal_bf16(5, 2, (configs.permuted_rows(T, k), H))
+    shared = synth.normal_bf16(5, 5, (T, H))
+    s_dev = dev_bf16(shared)
+    w_dev = dev(w.astype(np.float32))
+    out = moe.moe_finalize(dev_bf16(y), w_dev, dev(m), 0.5, s_dev, out=s_dev)
+    torch.cuda.synchronize()
+    ref = oracle.finalize(y, host_f64(w_dev), m, 0.5, shared)
+    assert out.data_ptr() == s_dev.data_ptr()
+    assert rel_fro(host_f64(out), ref) < TOL

@@ -137,7 +137,7 @@ def test_finalize_matches_definition_and_is_linear():
         ref = sum(w[t, j] * yf[m[t, j]] for j in range(k) if m[t, j] >= 0)
         np.testing.assert_allclose(out[t], ref if np.ndim(ref) else np.zeros(y.shape[1]),
                                    rtol=1e-15, atol=0)
-    np.testing.assert_allclose(oracle.finalize(y, 3.0 * w, m), 3.0 * out, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(oracle.finalize(y, 3.0 * w, m), 3.0 * out, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(oracle.finalize(y, w, m, rsf_fin=2.5), 2.5 * out, rtol=1e-14,
                                atol=0)
 
