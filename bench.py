@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="before the warm-up, run one device-to-device copy of this many MiB "
+                        "(a plain copy kernel of known size, to scale HBM byte counters)")
     return p.parse_args()
 
 
@@ -169,6 +172,14 @@ def main():
         moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=stream)
         mark(6)
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

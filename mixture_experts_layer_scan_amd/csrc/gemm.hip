@@ -21,12 +21,20 @@
 //     and to the expert's weights: rows of a ragged m-tile past the segment
 //     read as zero (never another expert's rows) and are masked on store.
 //
-// Tile pipeline: BK = 64 (one 128-byte row per operand row), two LDS stages.
-// Each thread moves 16-byte chunks; chunk c of tile row r lives at chunk
-// c ^ (r & 7) of that row, which spreads the MFMA operand reads (32 rows, same
-// chunk) over the LDS banks.  The next stage's global loads are issued before
-// the current stage's MFMAs and stored to the other LDS buffer after them:
-// one barrier per k-step.
+// Tile pipeline (per k-step of BK, STAGES LDS stages)
+//   - Operands move global -> LDS with buffer_load ... lds (16 bytes a lane,
+//     straight into LDS, no registers): one wave instruction fills 1 KiB of a
+//     stage.  Rows are stored XOR-swizzled in 16-byte chunks (swz below), the
+//     lane choosing the global chunk the swizzle puts at its LDS position, so
+//     MFMA operand reads are free of bank conflicts.
+//   - k-step kt computes from stage kt % STAGES while the loads of k-step
+//     kt + STAGES - 1 stream into the stage computed one k-step earlier.  A
+//     k-step ends by waiting until this wave's loads of k-step kt + 1 landed
+//     (a partial vmcnt: later k-steps stay in flight) and a barrier, so global
+//     latency is hidden behind STAGES - 1 k-steps of MFMAs.
+//   - Inside a k-step, fenced so the compiler keeps the order: the operand
+//     reads of sub-step ks + 1 and a slice of the loads are issued before the
+//     MFMAs of sub-step ks.
 //
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
@@ -40,38 +48,101 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;
 constexpr int GROUP_M = 8;
 
 // Descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-family
 // parts: 32-bit data format, out-of-range offsets read as zero.
 constexpr int kBufferFlags = 0x00020000;
 
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
-  return uint4{v[0], v[1], v[2], v[3]};
+// Swizzle of 16-byte chunk positions within a tile row of BK bf16:
+//   BK = 64 (8 chunks, 128-byte rows): chunk c of row r sits at
+//           c ^ (r & 7) ^ ((r >> 3) & 1);
+//   BK = 32 (4 chunks, 64-byte rows):  c ^ ((r >> 2) & 3).
+// Either way 16 consecutive rows read at one logical chunk (a 16-lane group
+// of an MFMA operand read) hit 16 distinct 16-byte bank groups of the 64-bank
+// LDS.
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
 }
 
+template <int BK>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ swz_key<BK>(row)) << 3);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool GATED_>
+// Device-only instructions sit in helpers whose bodies exist only in the
+// device pass: the host pass would reject them and silently drop the kernel
+// instantiations that use them.
+
+// 16 bytes per lane from buffer `r` at byte offset voff + soff, written
+// straight into LDS at dst + 16 * lane (dst is uniform over the wave).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff,
+                                          int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, static_cast<int>(voff), soff, 0,
+                                           0);
+#endif
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
+// left open).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+#endif
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every outstanding load of the wave (vmcnt(0)),
+// including the direct-to-LDS loads of later k-steps.  Each wave instead
+// waits for its own loads of the next stage with wait_vmem before arriving;
+// the empty asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#endif
+}
+
+// The value unchanged, but opaque to the optimizer (nothing derived from it
+// is hoisted out of the enclosing loop).
+__device__ __forceinline__ int opaque(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+  return v;
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr bool GATED = GATED_;
-  static constexpr int kThreads = WM * WN * kWave;
+  static constexpr int NWAVES = WM * WN;
+  static constexpr int kThreads = NWAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int ROWS_PER_PASS = kThreads / 8;  // tile rows loaded per chunk pass
-  static constexpr int A_CH = BM / ROWS_PER_PASS;
-  static constexpr int B_CH = BN / ROWS_PER_PASS;
+  static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per tile row
+  static constexpr int ROWS_PER_LD = kWave / CHUNKS;  // tile rows per 1 KiB load
+  static constexpr int A_LD = BM / ROWS_PER_LD / NWAVES;  // loads per wave per k-step
+  static constexpr int B_LD = BN / ROWS_PER_LD / NWAVES;
+  static constexpr int LOADS = A_LD + B_LD;
+  static constexpr int SUBSTEPS = BK / 16;
   static constexpr int OUT_N = GATED ? BN / 2 : BN;
   static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(uint16_t);
+  static_assert(BK == 32 || BK == 64, "k-step");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert((STAGES - 2) * LOADS < 64, "in-flight loads must fit vmcnt");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
-  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "load passes");
+  static_assert(BM % (ROWS_PER_LD * NWAVES) == 0 && BN % (ROWS_PER_LD * NWAVES) == 0,
+                "whole load instructions");
 };
 
 template <class Cfg>
@@ -79,9 +150,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int64_t R_pad,
     uint16_t* __restrict__ C, int n_tiles) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int NT = Cfg::kThreads;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
+  constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
+  // LDS stages as distinct objects, so the compiler knows that loads into one
+  // never alias operand reads from another (unused ones are tiny)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s2[ST > 2 ? Cfg::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s3[ST > 3 ? Cfg::STAGE : 8];
   __shared__ int32_t s_mt[1025];
   __shared__ int32_t s_scratch[16];
 
@@ -118,9 +194,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int N_total = Cfg::GATED ? 2 * N_out : N_out;
   const int nk = K / BK;
 
-  const int ld_row = tid >> 3;  // tile row of this thread's first chunk
-  const int ld_chunk = tid & 7;
-  const int ld_lds = swz(ld_row, ld_chunk);  // + i * ROWS_PER_PASS * BK for pass i
+  // Load j of this wave fills tile rows [R rb, R rb + R) (R = ROWS_PER_LD,
+  // rb = j * NWAVES + wave); lane L writes the 16 bytes at LDS row
+  // R rb + L / CHUNKS, position L % CHUNKS, so it fetches the logical chunk
+  // the swizzle puts there.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int ld_sub = lane / Cfg::CHUNKS;
+  const int ld_pos = lane % Cfg::CHUNKS;
 
   for (int tile = slot; tile < total_tiles; tile += G) {
     // grouped order: GROUP_M m-tiles share each n-tile column
@@ -144,29 +224,32 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     if (rows <= 0) continue;
     const int n0 = n_tile * Cfg::OUT_N;
 
-    // Global sources through buffer descriptors: the A descriptor covers the
-    // rows [row0, seg_end) of this expert and the W descriptor this expert's
-    // weights, so a load past either range returns zero and never touches
-    // other memory.  Per-thread byte offsets stay fixed over the k loop; the
-    // k-step goes into the scalar offset.
+    // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
+    // this expert's weights; loads past either range return zero.
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(A + static_cast<int64_t>(row0) * K), 0,
-        static_cast<int>(static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * 2u), kBufferFlags);
+        static_cast<int>(static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * 2u),
+        kBufferFlags);
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(W + static_cast<int64_t>(e) * N_total * K), 0,
-        static_cast<int>(static_cast<uint32_t>(N_total) * static_cast<uint32_t>(K) * 2u), kBufferFlags);
-    uint32_t a_off[Cfg::A_CH];
+        static_cast<int>(static_cast<uint32_t>(N_total) * static_cast<uint32_t>(K) * 2u),
+        kBufferFlags);
+    uint32_t a_off[Cfg::A_LD];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_CH; ++i)
-      a_off[i] = (static_cast<uint32_t>(ld_row + i * Cfg::ROWS_PER_PASS) * K + ld_chunk * 8) * 2u;
-    uint32_t b_off[Cfg::B_CH];
+    for (int j = 0; j < Cfg::A_LD; ++j) {
+      const int r = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
+      const int c = ld_pos ^ swz_key<BK>(r);
+      a_off[j] = (static_cast<uint32_t>(r) * K + c * 8) * 2u;
+    }
+    uint32_t b_off[Cfg::B_LD];
 #pragma unroll
-    for (int i = 0; i < Cfg::B_CH; ++i) {
-      const int v = ld_row + i * Cfg::ROWS_PER_PASS;
+    for (int j = 0; j < Cfg::B_LD; ++j) {
+      const int v = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
+      const int c = ld_pos ^ swz_key<BK>(v);
       // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
       // I + n0 + v - BN/2; columns past N_out are loaded but never stored
       const int wrow = Cfg::GATED ? (v < BN / 2 ? n0 + v : N_out + n0 + v - BN / 2) : n0 + v;
-      b_off[i] = (static_cast<uint32_t>(wrow) * K + ld_chunk * 8) * 2u;
+      b_off[j] = (static_cast<uint32_t>(wrow) * K + c * 8) * 2u;
     }
 
     f32x16 acc[FM][FN];
@@ -175,64 +258,117 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    uint4 ra[Cfg::A_CH], rb[Cfg::B_CH];
-    auto gload = [&](int kt) {
+    // Slice `part` (of SUB) of k-step kt of A and W into LDS stage `st`: the
+    // loads of one k-step are spread over its sub-steps.
+    auto gload = [&](uint16_t* st, int kt, int part) {
+      const int soff = kt * BK * 2;
 #pragma unroll
-      for (int i = 0; i < Cfg::A_CH; ++i) ra[i] = bload(a_rsrc, a_off[i], kt * BK * 2);
+      for (int j = 0; j < Cfg::A_LD; ++j)
+        if (j % SUB == part)
+          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD * BK, a_off[j],
+                    soff);
 #pragma unroll
-      for (int i = 0; i < Cfg::B_CH; ++i) rb[i] = bload(b_rsrc, b_off[i], kt * BK * 2);
+      for (int j = 0; j < Cfg::B_LD; ++j)
+        if ((j + Cfg::A_LD) % SUB == part)
+          lds_dma16(b_rsrc, st + BM * BK + (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD * BK,
+                    b_off[j], soff);
     };
-    auto sstore = [&](int stage) {
-      uint16_t* as = lds + stage * Cfg::STAGE;
-      uint16_t* bs = as + BM * BK;
+    auto gload_all = [&](uint16_t* st, int kt) {
 #pragma unroll
-      for (int i = 0; i < Cfg::A_CH; ++i)
-        *reinterpret_cast<uint4*>(as + ld_lds + i * Cfg::ROWS_PER_PASS * BK) = ra[i];
-#pragma unroll
-      for (int i = 0; i < Cfg::B_CH; ++i)
-        *reinterpret_cast<uint4*>(bs + ld_lds + i * Cfg::ROWS_PER_PASS * BK) = rb[i];
+      for (int p = 0; p < SUB; ++p) gload(st, kt, p);
     };
 
-    const int frag_row = lane & 31;
-    const int frag_half = lane >> 5;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const uint16_t* as = lds + cur * Cfg::STAGE;
+    // operand fragments of k sub-step ks (16 k) from stage `as`; `ln` is the
+    // lane id made opaque per k-step so the (swizzled) addresses are rebuilt
+    // there instead of all being kept live
+    auto load_frags = [&](const uint16_t* as, int ln, int ks, bf16x8* af, bf16x8* bfr) {
       const uint16_t* bs = as + BM * BK;
+      const int frag_row = ln & 31;
+      const int chunk = ks * 2 + (ln >> 5);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int chunk = ks * 2 + frag_half;
-        bf16x8 af[FM], bfr[FN];
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * Cfg::WTM + fm * 32 + frag_row;
+        af[fm] = *reinterpret_cast<const bf16x8*>(as + swz<BK>(r, chunk));
+      }
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int r = wm * Cfg::WTM + fm * 32 + frag_row;
-          af[fm] = *reinterpret_cast<const bf16x8*>(as + swz(r, chunk));
+      for (int fn = 0; fn < FN; ++fn) {
+        int v;
+        if (Cfg::GATED) {
+          v = (fn < FN / 2) ? wn * (Cfg::WTN / 2) + fn * 32
+                            : BN / 2 + wn * (Cfg::WTN / 2) + (fn - FN / 2) * 32;
+        } else {
+          v = wn * Cfg::WTN + fn * 32;
         }
+        bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz<BK>(v + frag_row, chunk));
+      }
+    };
+
+    // k-step kt from stage `cur` while k-step kt + ST - 1 streams into `ld`
+    // (the stage computed in the previous k-step, which the barrier closed);
+    // the last k-steps reload the final one into stages nobody reads again.
+    auto kstep = [&](const uint16_t* cur, uint16_t* ld, int kt) {
+      const int kn = min(kt + ST - 1, nk - 1);
+      const int ln = opaque(lane);
+      bf16x8 fa[2][FM], fb[2][FN];
+      load_frags(cur, ln, 0, fa[0], fb[0]);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          int v;
-          if (Cfg::GATED) {
-            v = (fn < FN / 2) ? wn * (Cfg::WTN / 2) + fn * 32
-                              : BN / 2 + wn * (Cfg::WTN / 2) + (fn - FN / 2) * 32;
-          } else {
-            v = wn * Cfg::WTN + fn * 32;
-          }
-          bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz(v + frag_row, chunk));
-        }
+      for (int ks = 0; ks < SUB; ++ks) {
+        if (ks + 1 < SUB) load_frags(cur, ln, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        gload(ld, kn, ks);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][fm], fb[ks & 1][fn],
+                                                                  acc[fm][fn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
-    }
+      wait_vmem<(ST - 2) * Cfg::LOADS>();  // this wave's loads of k-step kt + 1 landed
+      stage_barrier();
+    };
 
+    // prologue: k-steps 0 .. ST-2 in flight, then k-step 0 complete
+    gload_all(lds_s0, 0);
+    if constexpr (ST > 2) gload_all(lds_s1, min(1, nk - 1));
+    if constexpr (ST > 3) gload_all(lds_s2, min(2, nk - 1));
+    wait_vmem<(ST - 2) * Cfg::LOADS>();
+    stage_barrier();
+
+    // main loop unrolled by ST, so every stage is a compile-time object:
+    // k-step kt reads stage kt % ST and loads into stage (kt - 1) % ST
+    int kt = 0;
+    if constexpr (ST == 2) {
+      for (; kt + 1 < nk; kt += 2) {
+        kstep(lds_s0, lds_s1, kt);
+        kstep(lds_s1, lds_s0, kt + 1);
+      }
+      if (kt < nk) kstep(lds_s0, lds_s1, kt);
+    } else if constexpr (ST == 3) {
+      for (; kt + 2 < nk; kt += 3) {
+        kstep(lds_s0, lds_s2, kt);
+        kstep(lds_s1, lds_s0, kt + 1);
+        kstep(lds_s2, lds_s1, kt + 2);
+      }
+      if (kt < nk) kstep(lds_s0, lds_s2, kt);
+      if (kt + 1 < nk) kstep(lds_s1, lds_s0, kt + 1);
+    } else {
+      for (; kt + 3 < nk; kt += 4) {
+        kstep(lds_s0, lds_s3, kt);
+        kstep(lds_s1, lds_s0, kt + 1);
+        kstep(lds_s2, lds_s1, kt + 2);
+        kstep(lds_s3, lds_s2, kt + 3);
+      }
+      if (kt < nk) kstep(lds_s0, lds_s3, kt);
+      if (kt + 1 < nk) kstep(lds_s1, lds_s0, kt + 1);
+      if (kt + 2 < nk) kstep(lds_s2, lds_s1, kt + 2);
+    }
+    // No load of this tile may land in a stage after the next tile refills
+    // it (each wave refills only the rows it loads itself).
+    wait_vmem<0>();
+
+    const int frag_row = lane & 31;
+    const int frag_half = lane >> 5;
     // epilogue: lane holds column (lane & 31) and rows 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -266,13 +402,9 @@ template <class Cfg>
 hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   static int occupancy = 0;
   if (occupancy == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_kernel<Cfg>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(Cfg::LDS_BYTES));
-    if (e != hipSuccess) return e;
     int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_gemm_kernel<Cfg>,
-                                                     Cfg::kThreads, Cfg::LDS_BYTES);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_gemm_kernel<Cfg>,
+                                                                Cfg::kThreads, 0);
     if (e != hipSuccess) return e;
     occupancy = occ > 0 ? occ : 1;
   }
@@ -284,21 +416,22 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
-                     dim3(Cfg::kThreads), Cfg::LDS_BYTES, s,
+                     dim3(Cfg::kThreads), 0, s,
                      static_cast<const uint16_t*>(g.a), static_cast<const uint16_t*>(g.w),
                      g.offsets, g.E_l, g.K, g.N_out, g.R_pad, static_cast<uint16_t*>(g.c),
                      n_tiles);
   return hipGetLastError();
 }
 
-using Big = TileCfg<256, 256, 2, 2, false>;
-using BigG = TileCfg<256, 256, 2, 2, true>;
-using Mid = TileCfg<128, 128, 2, 2, false>;
-using MidG = TileCfg<128, 128, 2, 2, true>;
-using Slim = TileCfg<64, 256, 1, 4, false>;
-using SlimG = TileCfg<64, 256, 1, 4, true>;
-using Thin = TileCfg<32, 256, 1, 4, false>;
-using ThinG = TileCfg<32, 256, 1, 4, true>;
+//                      BM   BN  WM WN  BK ST  gated
+using Big   = TileCfg<256, 256, 2, 2, 32, 4, false>;
+using BigG  = TileCfg<256, 256, 2, 2, 32, 4, true>;
+using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false>;
+using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true>;
+using Slim  = TileCfg<64, 256, 1, 4, 64, 3, false>;
+using SlimG = TileCfg<64, 256, 1, 4, 64, 3, true>;
+using Thin  = TileCfg<32, 256, 1, 4, 64, 4, false>;
+using ThinG = TileCfg<32, 256, 1, 4, 64, 4, true>;
 
 }  // namespace
 
