@@ -424,8 +424,8 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 }
 
 //                      BM   BN  WM WN  BK ST  gated
-using Big   = TileCfg<256, 256, 2, 2, 32, 4, false>;
-using BigG  = TileCfg<256, 256, 2, 2, 32, 4, true>;
+using Big   = TileCfg<128, 256, 2, 2, 64, 3, false>;
+using BigG  = TileCfg<128, 256, 2, 2, 64, 3, true>;
 using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false>;
 using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true>;
 using Slim  = TileCfg<64, 256, 1, 4, 64, 3, false>;
