@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused-MoE layer tokens/s and TFLOP/s (% MFMA or HBM peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -56,19 +56,20 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_units: dict):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different gemm.hip."""
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel), or None when it is
+    missing or was taken on a different gemm.hip."""
+    path = os.path.join(TRAFFIC_DIR, f"gemm_hbm_traffic_{workload}.txt")
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+        with open(path) as f:
+            kv = dict(l.strip().split("=", 1) for l in f
+                      if "=" in l and not l.lstrip().startswith("#"))
+    except OSError:
         return None
-    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash() or kv.get("workload") != workload:
         return None
-    if t.get("workload") != launch_units.get("workload"):
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return float(kv["gemm1_hbm_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, x, logits, w, target_s: float):
@@ -205,7 +206,7 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     gemm1_s = stage_ms["gemm1"] * 1e-3
     achieved = flops_gemm1 / gemm1_s / 1e12
-    traffic = measured_traffic({"workload": cfg.name})
+    traffic = measured_traffic(cfg.name)
 
     result = {
         "metric": METRIC,
