@@ -164,10 +164,11 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
  *   h[r, n] = silu(g) * u   (fp32 accumulation, one rounding to bf16)
  *   a_perm  (device) bf16 [R_pad, H]
  *   offsets (device) int32 [E_l + 1] as written by moe_permute
- *   w1      GEMM1 weights, N = 2I, K = H (BF16; MXFP4 returns UNSUPPORTED in
- *           this version)
+ *   w1      GEMM1 weights, N = 2I, K = H (BF16, or MXFP4: the decoded values
+ *           are exact in bf16, so the MFMAs run in bf16 either way)
  *   h       (device) bf16 [R_pad, I] out; rows >= offsets[E_l] not written
- * Limits: H and I multiples of 64; R_pad >= offsets[E_l]. */
+ * Limits: H and I multiples of 64; R_pad >= offsets[E_l].  MXFP4 weights
+ * without scales, or bf16 weights with scales, are MOE_ERR_INVALID_ARGUMENT. */
 int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                           int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
                           void* h, void* workspace, size_t workspace_bytes, void* stream);

@@ -102,10 +102,18 @@ int check_gemm_dims(int32_t H, int32_t I) {
 
 int check_weights(const moe_weights* w, const char* name) {
   if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
-  if (w->dtype == MOE_DTYPE_MXFP4)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: MXFP4 weights are not supported by this build", name);
+  if (w->dtype == MOE_DTYPE_MXFP4) {
+    MOE_CHECK(need_ptr(w->data, name));
+    if (!w->scales) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: MXFP4 weights need their E8M0 scales", name);
+    return check_device_ptr(w->scales, name);
+  }
   if (w->dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight dtype %d", name, w->dtype);
+  if (w->scales) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: bf16 weights take no scales", name);
   return need_ptr(w->data, name);
+}
+
+const uint8_t* scales_of(const moe_weights* w) {
+  return w->dtype == MOE_DTYPE_MXFP4 ? w->scales : nullptr;
 }
 
 // The GEMMs address each operand through a buffer descriptor with a 32-bit
@@ -114,6 +122,7 @@ int check_weights(const moe_weights* w, const char* name) {
 int check_gemm_extent(int64_t rows, int32_t K, int64_t N_total) {
   const int64_t lim = int64_t(0xFFFFFFFF);
   if (rows * K * 2 > lim) return fail(MOE_ERR_INVALID_ARGUMENT, "permuted rows span more than 4 GiB");
+  // (bf16 weights bound MXFP4 ones, which take a quarter of the bytes)
   if (N_total * K * 2 > lim) return fail(MOE_ERR_INVALID_ARGUMENT, "one expert's weights span more than 4 GiB");
   return MOE_OK;
 }
@@ -264,7 +273,7 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   MOE_CHECK(need_ptr(c, "output rows"));
   if (overlap(a, sizeof(uint16_t) * R_pad * K, c, sizeof(uint16_t) * R_pad * N_out))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
-  moe::GemmArgs g{a, w->data, offsets, E_l, K, N_out, gated, R_pad, c};
+  moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c};
   hipError_t e = moe::launch_grouped_gemm(g, R_pad, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
@@ -355,10 +364,10 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
   if (e != hipSuccess) return hip_fail(e, "permute");
   e = moe::launch_gather_rows(x, map, T, k, H, b.x_perm, s);
   if (e != hipSuccess) return hip_fail(e, "gather");
-  moe::GemmArgs g1{b.x_perm, w1->data, b.offsets, E_l, H, I, 1, b.rows, b.h};
+  moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h};
   e = moe::launch_grouped_gemm(g1, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm1");
-  moe::GemmArgs g2{b.h, w2->data, b.offsets, E_l, I, H, 0, b.rows, y};
+  moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y};
   e = moe::launch_grouped_gemm(g2, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm2");
   return MOE_OK;
@@ -455,10 +464,10 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     uint16_t* s_y = c.take<uint16_t>(T * H);
     hipError_t e = moe::launch_fill_i32(s_off, 2, 0, static_cast<int32_t>(T), s);
     if (e != hipSuccess) return hip_fail(e, "shared offsets");
-    moe::GemmArgs g1{x, ws1, s_off, 1, H, shared_I, 1, T, s_h};
+    moe::GemmArgs g1{x, ws1, nullptr, s_off, 1, H, shared_I, 1, T, s_h};
     e = moe::launch_grouped_gemm(g1, T, s);
     if (e != hipSuccess) return hip_fail(e, "shared gemm1");
-    moe::GemmArgs g2{s_h, ws2, s_off, 1, shared_I, H, 0, T, s_y};
+    moe::GemmArgs g2{s_h, ws2, nullptr, s_off, 1, shared_I, H, 0, T, s_y};
     e = moe::launch_grouped_gemm(g2, T, s);
     if (e != hipSuccess) return hip_fail(e, "shared gemm2");
     shared_out = s_y;

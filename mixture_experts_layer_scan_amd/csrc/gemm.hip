@@ -36,6 +36,16 @@
 //     reads of sub-step ks + 1 and a slice of the loads are issued before the
 //     MFMAs of sub-step ks.
 //
+// MXFP4 weights (e2m1 pairs, low nibble = even k, one E8M0 scale byte per 32
+// k; vLLM flashinfer_moe_ep.py, _E2M1_LUT and _dequant_fp4_ue8m0_gran32): the
+// packed tile (32 bytes per row per k-step) is loaded into LDS the same way;
+// each lane reads its 16 bytes once per k-step and expands 4 of them per
+// sub-step to bf16 with v_cvt_scalef32_pk_bf16_fp4 (value x 2^(s-127), exact
+// in bf16), so the MFMAs and the activations stay bf16.  Inside a k-step,
+// sub-step ks and lane half h cover k = 32h + 8ks .. +7 for A and W alike,
+// which makes a lane's packed bytes of one k-step contiguous and puts all its
+// k in one 32-wide scale block.
+//
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
 // computes gate and up blocks with the same lane layout, so the epilogue
@@ -120,10 +130,11 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_, bool WQ_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr bool GATED = GATED_;
+  static constexpr bool WQ = WQ_;  // weights in MXFP4
   static constexpr int NWAVES = WM * WN;
   static constexpr int kThreads = NWAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -131,25 +142,66 @@ struct TileCfg {
   static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per tile row
   static constexpr int ROWS_PER_LD = kWave / CHUNKS;  // tile rows per 1 KiB load
   static constexpr int A_LD = BM / ROWS_PER_LD / NWAVES;  // loads per wave per k-step
-  static constexpr int B_LD = BN / ROWS_PER_LD / NWAVES;
-  static constexpr int LOADS = A_LD + B_LD;
+  // MXFP4: a packed row of one k-step is 32 bytes, so one load covers 32 rows
+  static constexpr int B_LD = WQ ? BN / 32 / NWAVES : BN / ROWS_PER_LD / NWAVES;
   static constexpr int SUBSTEPS = BK / 16;
   static constexpr int OUT_N = GATED ? BN / 2 : BN;
-  static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
+  static constexpr int A_ELEMS = BM * BK;                  // uint16 units
+  static constexpr int B_ELEMS = WQ ? BN * 16 : BN * BK;   // uint16 units (packed: 32 B/row)
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  // vector-memory loads per wave per k-step: tile loads (+ one scale byte per
+  // weight fragment for MXFP4)
+  static constexpr int LOADS = A_LD + B_LD + (WQ ? FN : 0);
+  // Loads a wave may leave in flight at the end of a k-step so that those of
+  // the next k-step have landed.  In steady state that is (STAGES - 2) * LOADS;
+  // the prologue issues no scale loads between its tile loads, so the first
+  // k-steps need the smaller count below (it also covers the steady state: the
+  // extra scale loads it waits for were consumed a k-step earlier anyway).
+  static constexpr int WAIT = (STAGES - 2) * (A_LD + B_LD) + ((WQ && STAGES > 2) ? FN : 0);
   static_assert(BK == 32 || BK == 64, "k-step");
+  static_assert(!WQ || BK == 64, "MXFP4 tiles use 64-wide k-steps (two scale blocks)");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
-  static_assert((STAGES - 2) * LOADS < 64, "in-flight loads must fit vmcnt");
+  static_assert(WAIT < 64, "in-flight loads must fit vmcnt");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
-  static_assert(BM % (ROWS_PER_LD * NWAVES) == 0 && BN % (ROWS_PER_LD * NWAVES) == 0,
+  static_assert(BM % (ROWS_PER_LD * NWAVES) == 0 && BN % ((WQ ? 32 : ROWS_PER_LD) * NWAVES) == 0,
                 "whole load instructions");
 };
 
+// First virtual weight row of fragment fn of wave column wn.
+template <class Cfg>
+__device__ __forceinline__ int b_row0(int wn, int fn) {
+  constexpr int FN = Cfg::FN;
+  if (Cfg::GATED)
+    return (fn < FN / 2) ? wn * (Cfg::WTN / 2) + fn * 32
+                         : Cfg::BN / 2 + wn * (Cfg::WTN / 2) + (fn - FN / 2) * 32;
+  return wn * Cfg::WTN + fn * 32;
+}
+
+__device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(voff), soff, 0);
+}
+
+// E8M0 scale byte -> the float whose bit pattern is s << 23 (2^(s-127);
+// s = 0 gives 0, s = 255 gives +inf).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 8 e2m1 values (4 bytes, low nibble first) times `scale` -> 8 bf16.
+__device__ __forceinline__ bf16x8 expand_fp4x8(uint32_t w, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int64_t R_pad,
-    uint16_t* __restrict__ C, int n_tiles) {
+    const uint16_t* __restrict__ A, const void* __restrict__ W,
+    const uint8_t* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
+    int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   // LDS stages as distinct objects, so the compiler knows that loads into one
@@ -230,10 +282,12 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         const_cast<uint16_t*>(A + static_cast<int64_t>(row0) * K), 0,
         static_cast<int>(static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * 2u),
         kBufferFlags);
+    // weight bytes per row: K * 2 (bf16) or K / 2 (packed e2m1)
+    const uint32_t w_row_bytes = Cfg::WQ ? static_cast<uint32_t>(K) / 2u : static_cast<uint32_t>(K) * 2u;
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(W + static_cast<int64_t>(e) * N_total * K), 0,
-        static_cast<int>(static_cast<uint32_t>(N_total) * static_cast<uint32_t>(K) * 2u),
-        kBufferFlags);
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(W) +
+                             static_cast<int64_t>(e) * N_total * w_row_bytes),
+        0, static_cast<int>(static_cast<uint32_t>(N_total) * w_row_bytes), kBufferFlags);
     uint32_t a_off[Cfg::A_LD];
 #pragma unroll
     for (int j = 0; j < Cfg::A_LD; ++j) {
@@ -241,16 +295,44 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       const int c = ld_pos ^ swz_key<BK>(r);
       a_off[j] = (static_cast<uint32_t>(r) * K + c * 8) * 2u;
     }
+    // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
+    // I + n0 + v - BN/2; columns past N_out are loaded but never stored
+    auto wrow_of = [&](int v) {
+      return Cfg::GATED ? (v < BN / 2 ? n0 + v : N_out + n0 + v - BN / 2) : n0 + v;
+    };
     uint32_t b_off[Cfg::B_LD];
 #pragma unroll
     for (int j = 0; j < Cfg::B_LD; ++j) {
-      const int v = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
-      const int c = ld_pos ^ swz_key<BK>(v);
-      // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
-      // I + n0 + v - BN/2; columns past N_out are loaded but never stored
-      const int wrow = Cfg::GATED ? (v < BN / 2 ? n0 + v : N_out + n0 + v - BN / 2) : n0 + v;
-      b_off[j] = (static_cast<uint32_t>(wrow) * K + c * 8) * 2u;
+      if constexpr (Cfg::WQ) {
+        // 32 rows per load, lane L -> row L / 2, 16-byte position L % 2
+        const int v = (j * Cfg::NWAVES + wave_u) * 32 + (lane >> 1);
+        const int c = (lane & 1) ^ ((v >> 3) & 1);
+        b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
+      } else {
+        const int v = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
+        const int c = ld_pos ^ swz_key<BK>(v);
+        b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
+      }
     }
+    // MXFP4 scale bytes: lane's weight row per fragment, block 2 kt + half
+    const uint32_t s_row = Cfg::WQ ? static_cast<uint32_t>(K) / 32u : 0u;  // scale bytes per row
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W_scales + static_cast<int64_t>(e) * N_total * s_row), 0,
+        static_cast<int>(static_cast<uint32_t>(N_total) * s_row), kBufferFlags);
+    uint32_t s_off[Cfg::WQ ? FN : 1];
+    uint32_t sc_cur[Cfg::WQ ? FN : 1], sc_nxt[Cfg::WQ ? FN : 1];
+    if constexpr (Cfg::WQ) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        s_off[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn) + (lane & 31))) * s_row +
+                    (lane >> 5);
+    }
+    auto load_scales = [&](uint32_t* dst, int kt) {
+      if constexpr (Cfg::WQ) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) dst[fn] = load_byte(s_rsrc, s_off[fn], kt * 2);
+      }
+    };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -262,6 +344,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // loads of one k-step are spread over its sub-steps.
     auto gload = [&](uint16_t* st, int kt, int part) {
       const int soff = kt * BK * 2;
+      const int soff_b = Cfg::WQ ? kt * BK / 2 : soff;
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
         if (j % SUB == part)
@@ -270,21 +353,25 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < Cfg::B_LD; ++j)
         if ((j + Cfg::A_LD) % SUB == part)
-          lds_dma16(b_rsrc, st + BM * BK + (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD * BK,
-                    b_off[j], soff);
+          lds_dma16(b_rsrc, st + Cfg::A_ELEMS + (j * Cfg::NWAVES + wave_u) * 512, b_off[j],
+                    soff_b);
     };
     auto gload_all = [&](uint16_t* st, int kt) {
 #pragma unroll
       for (int p = 0; p < SUB; ++p) gload(st, kt, p);
     };
 
-    // operand fragments of k sub-step ks (16 k) from stage `as`; `ln` is the
-    // lane id made opaque per k-step so the (swizzled) addresses are rebuilt
-    // there instead of all being kept live
-    auto load_frags = [&](const uint16_t* as, int ln, int ks, bf16x8* af, bf16x8* bfr) {
-      const uint16_t* bs = as + BM * BK;
+    // Operand fragments of k sub-step ks from stage `as`: lane half h holds
+    // k = 32h + 8ks .. +7 of its A row and of its W row.  `ln` is the lane id
+    // made opaque per k-step so the (swizzled) addresses are rebuilt there
+    // instead of all being kept live.  MXFP4: at ks == 0 the lane's 16 packed
+    // bytes of the k-step are read into `bq`; every sub-step expands 4 of them.
+    auto load_frags = [&](const uint16_t* as, int ln, int ks, bf16x8* af, bf16x8* bfr, uint4* bq,
+                          const uint32_t* sc) {
+      const uint16_t* bs = as + Cfg::A_ELEMS;
       const int frag_row = ln & 31;
-      const int chunk = ks * 2 + (ln >> 5);
+      const int half = ln >> 5;
+      const int chunk = half * SUB + ks;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
@@ -292,14 +379,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        int v;
-        if (Cfg::GATED) {
-          v = (fn < FN / 2) ? wn * (Cfg::WTN / 2) + fn * 32
-                            : BN / 2 + wn * (Cfg::WTN / 2) + (fn - FN / 2) * 32;
+        const int v = b_row0<Cfg>(wn, fn) + frag_row;
+        if constexpr (Cfg::WQ) {
+          if (ks == 0) bq[fn] = *reinterpret_cast<const uint4*>(bs + v * 16 + ((half ^ ((v >> 3) & 1)) << 3));
+          const uint32_t word = ks == 0 ? bq[fn].x : ks == 1 ? bq[fn].y : ks == 2 ? bq[fn].z : bq[fn].w;
+          bfr[fn] = expand_fp4x8(word, e8m0_to_f32(sc[fn]));
         } else {
-          v = wn * Cfg::WTN + fn * 32;
+          bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz<BK>(v, chunk));
         }
-        bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz<BK>(v + frag_row, chunk));
       }
     };
 
@@ -308,12 +395,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // the last k-steps reload the final one into stages nobody reads again.
     auto kstep = [&](const uint16_t* cur, uint16_t* ld, int kt) {
       const int kn = min(kt + ST - 1, nk - 1);
+      load_scales(sc_nxt, min(kt + 1, nk - 1));  // before the tile loads: see the vmcnt count
       const int ln = opaque(lane);
       bf16x8 fa[2][FM], fb[2][FN];
-      load_frags(cur, ln, 0, fa[0], fb[0]);
+      uint4 bq[Cfg::WQ ? FN : 1];
+      load_frags(cur, ln, 0, fa[0], fb[0], bq, sc_cur);
 #pragma unroll
       for (int ks = 0; ks < SUB; ++ks) {
-        if (ks + 1 < SUB) load_frags(cur, ln, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        if (ks + 1 < SUB) load_frags(cur, ln, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1], bq, sc_cur);
         gload(ld, kn, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -324,15 +413,21 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
                                                                   acc[fm][fn], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmem<(ST - 2) * Cfg::LOADS>();  // this wave's loads of k-step kt + 1 landed
+      wait_vmem<Cfg::WAIT>();  // this wave's loads of k-step kt + 1 landed
       stage_barrier();
+      if constexpr (Cfg::WQ) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) sc_cur[fn] = sc_nxt[fn];
+      }
     };
 
-    // prologue: k-steps 0 .. ST-2 in flight, then k-step 0 complete
+    // prologue: scales of k-step 0, k-steps 0 .. ST-2 in flight, then k-step 0
+    // complete (the prologue issues no scale loads after the tile loads)
+    load_scales(sc_cur, 0);
     gload_all(lds_s0, 0);
     if constexpr (ST > 2) gload_all(lds_s1, min(1, nk - 1));
     if constexpr (ST > 3) gload_all(lds_s2, min(2, nk - 1));
-    wait_vmem<(ST - 2) * Cfg::LOADS>();
+    wait_vmem<(ST - 2) * (Cfg::A_LD + Cfg::B_LD)>();
     stage_barrier();
 
     // main loop unrolled by ST, so every stage is a compile-time object:
@@ -417,39 +512,47 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
                      dim3(Cfg::kThreads), 0, s,
-                     static_cast<const uint16_t*>(g.a), static_cast<const uint16_t*>(g.w),
-                     g.offsets, g.E_l, g.K, g.N_out, g.R_pad, static_cast<uint16_t*>(g.c),
-                     n_tiles);
+                     static_cast<const uint16_t*>(g.a), g.w, g.w_scales, g.offsets, g.E_l, g.K,
+                     g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles);
   return hipGetLastError();
 }
 
-//                      BM   BN  WM WN  BK ST  gated
-using Big   = TileCfg<128, 256, 2, 2, 64, 3, false>;
-using BigG  = TileCfg<128, 256, 2, 2, 64, 3, true>;
-using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false>;
-using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true>;
-using Slim  = TileCfg<64, 256, 1, 4, 64, 3, false>;
-using SlimG = TileCfg<64, 256, 1, 4, 64, 3, true>;
-using Thin  = TileCfg<32, 256, 1, 4, 64, 4, false>;
-using ThinG = TileCfg<32, 256, 1, 4, 64, 4, true>;
+template <bool WQ>
+struct Configs {
+  //                          BM   BN  WM WN  BK ST  gated
+  using Big   = TileCfg<128, 256, 2, 2, 64, 3, false, WQ>;
+  using BigG  = TileCfg<128, 256, 2, 2, 64, 3, true, WQ>;
+  using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false, WQ>;
+  using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true, WQ>;
+  using Slim  = TileCfg<64, 256, 1, 4, 64, 3, false, WQ>;
+  using SlimG = TileCfg<64, 256, 1, 4, 64, 3, true, WQ>;
+  using Thin  = TileCfg<32, 256, 1, 4, 64, 4, false, WQ>;
+  using ThinG = TileCfg<32, 256, 1, 4, 64, 4, true, WQ>;
+};
+
+// Tile height follows the mean rows per local expert (the host cannot see the
+// real counts without a device round trip).
+template <bool WQ>
+hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
+  using C = Configs<WQ>;
+  const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
+  if (g.gated) {
+    if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
+    if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
+    if (mean_rows >= 48) return launch_cfg<typename C::SlimG>(g, max_rows, s);
+    return launch_cfg<typename C::ThinG>(g, max_rows, s);
+  }
+  if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
+  if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
+  if (mean_rows >= 48) return launch_cfg<typename C::Slim>(g, max_rows, s);
+  return launch_cfg<typename C::Thin>(g, max_rows, s);
+}
 
 }  // namespace
 
 // max_rows: the most local routes the call can see (T * k), from the host.
-// Tile height follows the mean rows per local expert (the host cannot see the
-// real counts without a device round trip).
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
-  if (g.gated) {
-    if (mean_rows >= 512) return launch_cfg<BigG>(g, max_rows, s);
-    if (mean_rows >= 128) return launch_cfg<MidG>(g, max_rows, s);
-    if (mean_rows >= 48) return launch_cfg<SlimG>(g, max_rows, s);
-    return launch_cfg<ThinG>(g, max_rows, s);
-  }
-  if (mean_rows >= 512) return launch_cfg<Big>(g, max_rows, s);
-  if (mean_rows >= 128) return launch_cfg<Mid>(g, max_rows, s);
-  if (mean_rows >= 48) return launch_cfg<Slim>(g, max_rows, s);
-  return launch_cfg<Thin>(g, max_rows, s);
+  return g.w_scales ? launch_fmt<true>(g, max_rows, s) : launch_fmt<false>(g, max_rows, s);
 }
 
 }  // namespace moe

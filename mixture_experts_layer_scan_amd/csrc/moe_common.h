@@ -79,7 +79,8 @@ namespace moe {
 
 struct GemmArgs {
   const void* a;          // bf16 [R_pad, K]
-  const void* w;          // bf16 [E_l, N_total, K]
+  const void* w;          // bf16 [E_l, N_total, K], or packed e2m1 [E_l, N_total, K/2]
+  const uint8_t* w_scales;  // NULL (bf16), or E8M0 [E_l, N_total, K/32] (MXFP4)
   const int32_t* offsets; // [E_l + 1]
   int E_l;
   int K;

@@ -98,6 +98,8 @@ def test_gemm_errors(L):
     assert g1(P, P, 8, 128, 128, 256, _w(), 3, P * 64, None, 0, None) == UNSUPPORTED
     assert g1(P, P, 8, 128, 128, 256, _w(9), 0, P * 64, None, 0, None) == UNSUPPORTED
     assert g1(P, P, 8, 128, 128, 256, None, 0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, 8, 128, 128, 256, _w(2, P, None), 0, P * 64, None, 0, None) == INVALID  # MXFP4, no scales
+    assert g1(P, P, 8, 128, 128, 256, _w(0, P, P), 0, P * 64, None, 0, None) == INVALID  # bf16 with scales
     assert g1(P, P, 8, 128, 128, 256, _w(), 0, P, None, 0, None) == CONFLICT  # h == a_perm
     assert g1(P, P, 0, 128, 128, 256, _w(), 0, P * 64, None, 0, None) == INVALID  # E_l = 0
     g2 = L.moe_grouped_gemm2

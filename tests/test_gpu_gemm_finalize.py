@@ -80,6 +80,29 @@ def test_grouped_gemm2(case):
     assert np.all(host_bf16_bits(y)[R_l:] == NAN_BITS)
 
 
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_gemms_mxfp4_weights(case):
+    """MXFP4 weights (e2m1 + E8M0 per 32 along K): both GEMMs against the
+    oracle's decode of the same packed bytes."""
+    name, counts, H, I = case
+    E_l, offsets, R_l, R_pad, a, w1, w2 = _setup(counts, H, I, seed=sum(counts) + 2)
+    q1, s1 = synth.mxfp4_quantize(w1)
+    q2, s2 = synth.mxfp4_quantize(w2)
+    W1 = moe.Weights(dev(q1), dev(s1))
+    W2 = moe.Weights(dev(q2), dev(s2))
+    h = torch.full((R_pad, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm1_act(dev_bf16(a), dev(offsets), W1, I, h=h)
+    hb = synth.normal_bf16(sum(counts), 8, (R_pad, I))
+    y = moe.moe_grouped_gemm2(dev_bf16(hb), dev(offsets), W2, H)
+    torch.cuda.synchronize()
+    eor = segments_of(offsets, R_l)
+    ref_h = oracle.hidden_rows(a[:R_l], oracle.Weights(q1, s1), eor, I)
+    ref_y = oracle.out_rows(hb[:R_l], oracle.Weights(q2, s2), eor, H)
+    assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
+    assert np.all(host_bf16_bits(h)[R_l:] == NAN_BITS)
+    assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
+
+
 def test_gemm_deterministic():
     E_l, offsets, R_l, R_pad, a, w1, w2 = _setup([300, 1, 420], 256, 448, seed=99)
     outs = []

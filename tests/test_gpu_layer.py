@@ -38,15 +38,26 @@ def _gpu():
 
 
 def _upload(cfg, w):
-    d = {"w1": moe.Weights(dev_bf16(w["w1"])), "w2": moe.Weights(dev_bf16(w["w2"]))}
+    if cfg.mxfp4:
+        d = {"w1": moe.Weights(dev(w["w1_q"]), dev(w["w1_s"])),
+             "w2": moe.Weights(dev(w["w2_q"]), dev(w["w2_s"]))}
+    else:
+        d = {"w1": moe.Weights(dev_bf16(w["w1"])), "w2": moe.Weights(dev_bf16(w["w2"]))}
     if cfg.shared_I:
         d["ws1"], d["ws2"] = dev_bf16(w["ws1"]), dev_bf16(w["ws2"])
     return d
 
 
+def _oracle_weights(cfg, w):
+    if cfg.mxfp4:
+        return oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    return oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
+
+
 def _oracle(cfg, x, logits, w, tokens=None):
+    W1, W2 = _oracle_weights(cfg, w)
     return oracle.moe_tokens(
-        x, logits, oracle.Weights(w["w1"]), oracle.Weights(w["w2"]), cfg.I, cfg.k, cfg.score,
+        x, logits, W1, W2, cfg.I, cfg.k, cfg.score,
         cfg.renormalize, cfg.rsf, expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I,
         ws1=w.get("ws1"), ws2=w.get("ws2"), tokens=tokens)
 
@@ -119,7 +130,7 @@ def test_tiny_edge_cases():
     assert torch.all(z == 0)
 
 
-def _full_size(cfg, n_sample, seed):
+def _full_size(cfg, n_sample, seed, tol=TOL):
     x, logits = configs.make_activations(cfg)
     w = configs.make_weights(cfg)
     W = _upload(cfg, w)
@@ -145,7 +156,7 @@ def _full_size(cfg, n_sample, seed):
     ref = _oracle(cfg, x, logits, w, tokens=toks)
     got = host_f64(out1)[toks]
     assert np.all(np.isfinite(got))
-    assert rel_fro(got, ref["out"]) < TOL
+    assert rel_fro(got, ref["out"]) < tol
 
 
 def test_mixtral_prefill_full_size():
@@ -154,6 +165,30 @@ def test_mixtral_prefill_full_size():
 
 def test_deepseek_routed_shared_full_size():
     _full_size(configs.DEEPSEEK, 24, 3)
+
+
+# MXFP4 weights: bar 3e-2 (the weights are exact in both; the GPU rounds h, Y
+# and out to bf16 like the bf16 path, so the measured gap is the same ~3e-3).
+MXFP4_TOL = 3e-2
+
+
+def test_deepseek_mxfp4_full_size():
+    _full_size(configs.DEEPSEEK_MXFP4, 24, 5, tol=MXFP4_TOL)
+
+
+def test_tiny_mxfp4_deferred_and_fused():
+    cfg = configs.MoeConfig("tiny_mxfp4", T=40, H=256, I=192, E=8, k=2, score=configs.SOFTMAX,
+                            renormalize=True, rsf=1.0, seed=6, mxfp4=True)
+    x, logits = configs.make_activations(cfg)
+    w = configs.make_weights(cfg)
+    W = _upload(cfg, w)
+    ref = _oracle(cfg, x, logits, w)
+    out = moe.moe_fused_experts(dev(logits), dev_bf16(x), W["w1"], W["w2"], cfg.k)
+    y, ew, m = moe.moe_fused_experts_unfinalized(dev(logits), dev_bf16(x), W["w1"], W["w2"], cfg.k)
+    out2 = moe.moe_finalize(y, ew, m)
+    torch.cuda.synchronize()
+    assert rel_fro(host_f64(out), ref["out"]) < MXFP4_TOL
+    assert rel_fro(host_f64(out2), ref["out"]) < MXFP4_TOL
 
 
 @pytest.mark.parametrize("T", configs.EP_DECODE_BATCHES)
