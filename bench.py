@@ -1,18 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the fused MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--tokens T]
 
 One step is the whole hot path on one batch of synthetic input already
 resident in HBM: route -> permute (map, offsets, row gather) -> grouped GEMM1
-with SiLU(gate)*up -> grouped GEMM2 -> finalize.  The default workload is the
-Mixtral-8x7B-shaped prefill layer (4096 tokens, hidden 4096, intermediate
-14336, 8 experts, top-2, Zipf(1.1)-biased routing), random bf16 weights.
+with SiLU(gate)*up -> grouped GEMM2 (-> shared expert) -> finalize.  The
+default workload is the Mixtral-8x7B-shaped prefill layer (4096 tokens, hidden
+4096, intermediate 14336, 8 experts, top-2, Zipf(1.1)-biased routing), random
+bf16 weights.  The other workloads:
+  deepseekv3_routed_shared_2048tok   256 experts, top-8 sigmoid, shared expert
+  deepseekv3_mxfp4_2048tok           the same shape with MXFP4 expert weights
+  ep_rank3of8_decode                 one expert-parallel rank's 32 experts at a
+                                     decode batch (--tokens 1, 8 or 64), deferred
+                                     form followed by the separate finalize; the
+                                     steps cycle through 16 routing draws and a
+                                     512 MiB write evicts L2 and the MALL before
+                                     each step (outside the timed events)
 
 Prints one JSON line: tokens/s (value), algorithmic TFLOP/s, the roofline of
 the dominant kernel (grouped GEMM1) from HIP events recorded around each of its
-launches on the launching stream, and the CPU oracle timed on a bounded sample
-of the same workload on this host's cores.
+launches on the launching stream -- against the bf16 MFMA peak when its
+algorithmic flops take longer there than its algorithmic bytes take at the HBM
+peak, else against the HBM peak -- and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -32,6 +43,7 @@ METRIC = "fused-MoE layer tokens/s and TFLOP/s (% MFMA or HBM peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MiB) + MALL (256 MiB)
 
 
 def parse():
@@ -40,6 +52,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral8x7b_prefill_4096tok")
+    p.add_argument("--tokens", type=int, default=64,
+                   help="decode batch of the expert-parallel decode workload (1, 8 or 64)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -72,31 +86,65 @@ def measured_traffic(workload: str):
     return float(kv["gemm1_hbm_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, x, logits, w, target_s: float):
+def gemm_work(cfg, counts, gemm: int):
+    """Algorithmic flops and HBM bytes of one grouped-GEMM launch: the weights
+    of the experts that received rows (E8M0 scales included), the input rows
+    read once, the output rows written once."""
+    counts = np.asarray(counts, dtype=np.int64)
+    R_l, touched = int(counts.sum()), int((counts > 0).sum())
+    if gemm == 1:
+        N, K, out_cols = 2 * cfg.I, cfg.H, cfg.I
+    else:
+        N, K, out_cols = cfg.H, cfg.I, cfg.H
+    w_bytes_per_expert = N * (K // 2 + K // 32) if cfg.mxfp4 else N * K * 2
+    flops = 2.0 * R_l * N * K
+    nbytes = float(touched * w_bytes_per_expert + R_l * K * 2 + R_l * out_cols * 2)
+    return flops, nbytes
+
+
+def cpu_baseline(cfg, draws, w, target_s: float):
+    """The oracle as it stands, on all host cores, on a bounded sample of the
+    workload's tokens (draw after draw, chunk after chunk) until about
+    target_s seconds of CPU work."""
     import oracle
-    W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
-    kw = dict(expert_map=None, shared_I=cfg.shared_I, ws1=w.get("ws1"), ws2=w.get("ws2"))
-    # warm-up touch of the weight pages with one token
-    oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
-                      tokens=[0], **kw)
-    n = max(oracle.num_threads(), 1)
-    t0 = time.perf_counter()
-    oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
-                      tokens=list(range(n)), **kw)
-    dt = time.perf_counter() - t0
-    total_tok, total_s = n, dt
-    if dt < target_s:
-        m = int(min(cfg.T - n, max(n, (target_s - dt) / dt * n)))
-        m = max(n, m // n * n)
-        t0 = time.perf_counter()
+    if cfg.mxfp4:
+        W1, W2 = oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    else:
+        W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
+    from synth import configs
+    kw = dict(expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I, ws1=w.get("ws1"),
+              ws2=w.get("ws2"))
+
+    def run(x, logits, toks):
         oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
-                          tokens=list(range(n, n + m)), **kw)
-        total_s += time.perf_counter() - t0
-        total_tok += m
+                          tokens=toks, **kw)
+
+    run(draws[0][0], draws[0][1], [0])  # page-touch warm-up
+    n = max(oracle.num_threads(), 1)
+    chunk, total_tok, total_s, n_draws = n, 0, 0.0, 0
+    while total_s < target_s:
+        x, logits = draws[n_draws % len(draws)]
+        T = x.shape[0]
+        n_draws += 1
+        for start in range(0, T, chunk):
+            toks = list(range(start, min(T, start + chunk)))
+            t0 = time.perf_counter()
+            run(x, logits, toks)
+            dt = time.perf_counter() - t0
+            total_tok += len(toks)
+            total_s += dt
+            if total_s >= target_s:
+                break
+            if dt < target_s / 8:
+                chunk *= 2
+        if n_draws > 10000:
+            break
+    where = (f"{total_tok} tokens from {n_draws} routing draws of {cfg.T} tokens"
+             if len(draws) > 1 else f"first {total_tok} of {cfg.T} tokens")
     return {"value": total_tok / total_s, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"first {total_tok} of {cfg.T} tokens of the same workload, float64 "
-                      f"per-token per-expert MLP, {total_s:.1f} s wall"}
+            "sample": f"{where} of the same workload, float64 per-token per-expert MLP, "
+                      f"{total_s:.1f} s wall"}
 
 
 def main():
@@ -114,20 +162,33 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    cfg = configs.ALL[args.workload]
-    if cfg.deferred or cfg.mxfp4:
-        print(f"workload {cfg.name} is a parity-test configuration; bench covers the "
-              f"finalized bf16 layers", file=sys.stderr)
+    if args.workload not in configs.ALL:
+        print(f"unknown workload {args.workload}; one of {sorted(configs.ALL)}", file=sys.stderr)
         sys.exit(2)
-
-    x, logits = configs.make_activations(cfg)
+    cfg = configs.ALL[args.workload]
+    decode = cfg.deferred
+    if decode:
+        if args.tokens not in configs.EP_DECODE_BATCHES:
+            print(f"--tokens must be one of {configs.EP_DECODE_BATCHES}", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.with_T(args.tokens)
+        draws = [configs.make_activations(cfg, seed=configs.EP_DECODE_DRAW_SEED0 + d)
+                 for d in range(configs.EP_DECODE_DRAWS)]
+        label = f"{cfg.name}_T{cfg.T}"
+    else:
+        draws = [configs.make_activations(cfg)]
+        label = cfg.name
     w = configs.make_weights(cfg)
 
     def to_bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
-    xd, ld = to_bf16(x), torch.from_numpy(logits).cuda()
-    W1, W2 = moe.Weights(to_bf16(w["w1"])), moe.Weights(to_bf16(w["w2"]))
+    dev_draws = [(to_bf16(x), torch.from_numpy(lg).cuda()) for x, lg in draws]
+    if cfg.mxfp4:
+        W1 = moe.Weights(torch.from_numpy(w["w1_q"]).cuda(), torch.from_numpy(w["w1_s"]).cuda())
+        W2 = moe.Weights(torch.from_numpy(w["w2_q"]).cuda(), torch.from_numpy(w["w2_s"]).cuda())
+    else:
+        W1, W2 = moe.Weights(to_bf16(w["w1"])), moe.Weights(to_bf16(w["w2"]))
     emap = configs.expert_map(cfg)
     emap_d = None if emap is None else torch.from_numpy(emap).cuda()
     T, H, I, k, E, El = cfg.T, cfg.H, cfg.I, cfg.k, cfg.E, cfg.El
@@ -148,14 +209,26 @@ def main():
         off_s = torch.tensor([0, T], dtype=torch.int32, device=dev)
         hs = torch.empty((T, cfg.shared_I), dtype=torch.bfloat16, device=dev)
         shared = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if decode else None
     stream = torch.cuda.current_stream()
 
     stages = ["route", "permute", "gemm1", "gemm2", "shared", "finalize"]
 
-    def step(ev=None):
-        def mark(i):
+    def route_permute(d):
+        xd, ld = dev_draws[d]
+        moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, stream)
+        moe.moe_permute(ids, E, El, emap_d, xd, R_pad, pmap, offsets, None, x_perm,
+                        want_inv=False, stream=stream)
+
+    def step(i, ev=None):
+        d = i % len(dev_draws)
+        xd, ld = dev_draws[d]
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+
+        def mark(j):
             if ev is not None:
-                ev[i].record(stream)
+                ev[j].record(stream)
         mark(0)
         moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, stream)
         mark(1)
@@ -181,36 +254,65 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(i, events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    stage_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
-                                  for i in range(args.steps)]))
-                for j, s in enumerate(stages)}
+    per_step = [[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
+                for i in range(args.steps)]
+    stage_ms = {s: float(np.mean([p[j] for p in per_step])) for j, s in enumerate(stages)}
     if not cfg.shared_I:
         del stage_ms["shared"]
-    counts = np.diff(offsets.cpu().numpy())
-    R_l = int(counts.sum())
-    flops_gemm1 = 2.0 * R_l * H * (2 * I)
-    flops_gemm2 = 2.0 * R_l * I * H
-    flops_shared = 6.0 * T * H * cfg.shared_I
-    flops_step = flops_gemm1 + flops_gemm2 + flops_shared
-    ms_per_step = elapsed / args.steps * 1e3
-    gemm1_s = stage_ms["gemm1"] * 1e-3
-    achieved = flops_gemm1 / gemm1_s / 1e12
-    traffic = measured_traffic(cfg.name)
 
+    # routed rows per local expert of every draw (untimed re-run of route + permute)
+    draw_counts = []
+    for d in range(len(dev_draws)):
+        route_permute(d)
+        draw_counts.append(np.diff(offsets.cpu().numpy()))
+    step_counts = [draw_counts[i % len(dev_draws)] for i in range(args.steps)]
+
+    flops_step = []
+    g1_flops = g1_bytes = g1_ms = 0.0
+    for i, c in enumerate(step_counts):
+        f1, b1 = gemm_work(cfg, c, 1)
+        f2, _ = gemm_work(cfg, c, 2)
+        flops_step.append(f1 + f2 + 6.0 * T * H * cfg.shared_I)
+        g1_flops += f1
+        g1_bytes += b1
+        g1_ms += per_step[i][2]
+    if decode:
+        # the flush between steps is not part of the layer: time from the events
+        ms_per_step = float(np.mean([sum(p) for p in per_step]))
+    else:
+        ms_per_step = elapsed / args.steps * 1e3
+    tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
+    g1_s = g1_ms * 1e-3
+    t_mfma = g1_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        achieved = g1_flops / g1_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = g1_bytes / g1_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    n_launch = len(step_counts)
+    roof.update({"traffic": measured_traffic(label), "kernel": "grouped_gemm1_act",
+                 "algorithmic_flop_per_launch": g1_flops / n_launch,
+                 "algorithmic_bytes_per_launch": g1_bytes / n_launch})
+
+    counts0 = draw_counts[0]
     result = {
         "metric": METRIC,
-        "value": T * args.steps / elapsed,
+        "value": T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -220,27 +322,29 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights)",
-        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights"
+                + (", MXFP4-quantized" if cfg.mxfp4 else "") + ")",
+        "config": {"workload": label, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "local_experts": El, "top_k": k,
                    "shared_intermediate": cfg.shared_I,
+                   "expert_weights": "mxfp4 (e2m1 + E8M0 per 32)" if cfg.mxfp4 else "bf16",
                    "routing": ("softmax" if cfg.score == 0 else "sigmoid") +
                               (f" top-{k} renormalized") + (f", rsf {cfg.rsf}" if cfg.rsf != 1 else "") +
-                              (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else "")},
-        "tflops": flops_step / (ms_per_step * 1e-3) / 1e12,
-        "mfma_frac_layer": flops_step / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
+                   "form": "deferred + separate finalize, L2/MALL evicted before each step, "
+                           f"{len(draws)} routing draws" if decode else "finalized"},
+        "tflops": tflops,
+        "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
         "stages_ms": stage_ms,
-        "expert_rows": counts.tolist() if len(counts) <= 16 else
-                       {"min": int(counts.min()), "max": int(counts.max()), "mean": float(counts.mean())},
-        "roofline": {"kernel": "grouped_gemm1_act", "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic,
-                     "algorithmic_flop_per_launch": flops_gemm1},
+        "expert_rows": counts0.tolist() if len(counts0) <= 16 else
+                       {"min": int(counts0.min()), "max": int(counts0.max()),
+                        "mean": float(counts0.mean()), "touched": int((counts0 > 0).sum())},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del xd, ld, W1, W2, x_perm, h, y, out
-        result["cpu_baseline"] = cpu_baseline(cfg, x, logits, w, args.cpu_seconds)
+        del dev_draws, W1, W2, x_perm, h, y, out
+        result["cpu_baseline"] = cpu_baseline(cfg, draws, w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
