@@ -15,8 +15,13 @@
 //   - Persistent grid: workgroup b walks tiles slot(b), slot(b) + G, ...  The
 //     slot is chosen so that the G/8 workgroups the hardware puts on one XCD
 //     (round-robin dispatch) take consecutive tiles, and tiles are ordered in
-//     groups of GROUP_M m-tiles per n-tile column, so the tiles one XCD runs
-//     together share A rows and weight rows in that XCD's L2.
+//     groups of GM m-tiles per n-tile column, so the tiles one XCD runs
+//     together share A rows and weight rows in that XCD's L2.  Tiles made for
+//     segments of at most BM rows (one m-tile per expert, nothing to share in
+//     the weights) use GM = 1: all n-tiles of an expert run on one XCD and
+//     read its A rows from HBM once.
+//   - Such tiles (one wave row, several 32-row fragments per wave) skip the
+//     operand reads and MFMAs of fragments that lie wholly past the segment.
 //   - Loads go through buffer descriptors bounded to the expert's row segment
 //     and to the expert's weights: rows of a ragged m-tile past the segment
 //     read as zero (never another expert's rows) and are masked on store.
@@ -57,8 +62,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int GROUP_M = 8;
 
 // Descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-family
 // parts: 32-bit data format, out-of-range offsets read as zero.
@@ -108,6 +111,15 @@ __device__ __forceinline__ void wait_vmem() {
 #endif
 }
 
+// The same, and every LDS read of this wave has returned (lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+#endif
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those would wait for every outstanding load of the wave (vmcnt(0)),
 // including the direct-to-LDS loads of later k-steps.  Each wave instead
@@ -130,15 +142,20 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_, bool WQ_ = false>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_, bool WQ_ = false,
+          int GM_ = 8>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr bool GATED = GATED_;
   static constexpr bool WQ = WQ_;  // weights in MXFP4
+  static constexpr int GM = GM_;   // m-tiles per group of the tile order
   static constexpr int NWAVES = WM * WN;
   static constexpr int kThreads = NWAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
+  // skip row fragments past the segment (one wave row only: otherwise the
+  // waves of the lower rows would idle while the others work)
+  static constexpr bool SKIP = (WM == 1 && FM > 1);
   static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per tile row
   static constexpr int ROWS_PER_LD = kWave / CHUNKS;  // tile rows per 1 KiB load
   static constexpr int A_LD = BM / ROWS_PER_LD / NWAVES;  // loads per wave per k-step
@@ -255,11 +272,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int ld_pos = lane % Cfg::CHUNKS;
 
   for (int tile = slot; tile < total_tiles; tile += G) {
-    // grouped order: GROUP_M m-tiles share each n-tile column
-    const int group = GROUP_M * n_tiles;
+    // grouped order: GM m-tiles share each n-tile column
+    const int group = Cfg::GM * n_tiles;
     const int gid = tile / group;
-    const int first_m = gid * GROUP_M;
-    const int gm = min(total_m - first_m, GROUP_M);
+    const int first_m = gid * Cfg::GM;
+    const int gm = min(total_m - first_m, Cfg::GM);
     const int in_group = tile - gid * group;
     const int m_tile = first_m + in_group % gm;
     const int n_tile = in_group / gm;
@@ -275,6 +292,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const int rows = seg_end - row0;
     if (rows <= 0) continue;
     const int n0 = n_tile * Cfg::OUT_N;
+    // row fragments of this wave that hold rows of the segment (wave-uniform)
+    const int fm_act = Cfg::SKIP ? min(FM, (rows - wm * Cfg::WTM + 31) / 32) : FM;
 
     // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
     // this expert's weights; loads past either range return zero.
@@ -374,6 +393,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       const int chunk = half * SUB + ks;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
+        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
         af[fm] = *reinterpret_cast<const bf16x8*>(as + swz<BK>(r, chunk));
       }
@@ -390,31 +410,44 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       }
     };
 
+    // Operand fragments, double-buffered by sub-step; buffer 0 holds sub-step
+    // 0 of the next k-step when a k-step begins.
+    static_assert(SUB % 2 == 0, "sub-step 0 of the next k-step reuses buffer 0");
+    bf16x8 fa[2][FM], fb[2][FN];
+    uint4 bq[Cfg::WQ ? FN : 1];
+
     // k-step kt from stage `cur` while k-step kt + ST - 1 streams into `ld`
     // (the stage computed in the previous k-step, which the barrier closed);
     // the last k-steps reload the final one into stages nobody reads again.
-    auto kstep = [&](const uint16_t* cur, uint16_t* ld, int kt) {
+    // The barrier that closes `cur` and opens `nxt` (k-step kt + 1) comes
+    // before the last sub-step's MFMAs, and sub-step 0 of `nxt` is read right
+    // after it, so that LDS latency hides behind those MFMAs.
+    auto kstep = [&](const uint16_t* cur, const uint16_t* nxt, uint16_t* ld, int kt) {
       const int kn = min(kt + ST - 1, nk - 1);
       load_scales(sc_nxt, min(kt + 1, nk - 1));  // before the tile loads: see the vmcnt count
       const int ln = opaque(lane);
-      bf16x8 fa[2][FM], fb[2][FN];
-      uint4 bq[Cfg::WQ ? FN : 1];
-      load_frags(cur, ln, 0, fa[0], fb[0], bq, sc_cur);
 #pragma unroll
       for (int ks = 0; ks < SUB; ++ks) {
         if (ks + 1 < SUB) load_frags(cur, ln, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1], bq, sc_cur);
         gload(ld, kn, ks);
+        if (ks + 1 == SUB) {
+          // this wave's loads of k-step kt + 1 landed and its reads of `cur`
+          // returned; after the barrier, every wave's have
+          wait_vmem_lds<Cfg::WAIT>();
+          stage_barrier();
+          load_frags(nxt, ln, 0, fa[0], fb[0], bq, sc_nxt);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+        for (int fm = 0; fm < FM; ++fm) {
+          if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][fm], fb[ks & 1][fn],
                                                                   acc[fm][fn], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmem<Cfg::WAIT>();  // this wave's loads of k-step kt + 1 landed
-      stage_barrier();
       if constexpr (Cfg::WQ) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) sc_cur[fn] = sc_nxt[fn];
@@ -429,34 +462,36 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     if constexpr (ST > 3) gload_all(lds_s2, min(2, nk - 1));
     wait_vmem<(ST - 2) * (Cfg::A_LD + Cfg::B_LD)>();
     stage_barrier();
+    load_frags(lds_s0, opaque(lane), 0, fa[0], fb[0], bq, sc_cur);
 
     // main loop unrolled by ST, so every stage is a compile-time object:
-    // k-step kt reads stage kt % ST and loads into stage (kt - 1) % ST
+    // k-step kt reads stage kt % ST, opens (kt + 1) % ST and loads into
+    // stage (kt - 1) % ST
     int kt = 0;
     if constexpr (ST == 2) {
       for (; kt + 1 < nk; kt += 2) {
-        kstep(lds_s0, lds_s1, kt);
-        kstep(lds_s1, lds_s0, kt + 1);
+        kstep(lds_s0, lds_s1, lds_s1, kt);
+        kstep(lds_s1, lds_s0, lds_s0, kt + 1);
       }
-      if (kt < nk) kstep(lds_s0, lds_s1, kt);
+      if (kt < nk) kstep(lds_s0, lds_s1, lds_s1, kt);
     } else if constexpr (ST == 3) {
       for (; kt + 2 < nk; kt += 3) {
-        kstep(lds_s0, lds_s2, kt);
-        kstep(lds_s1, lds_s0, kt + 1);
-        kstep(lds_s2, lds_s1, kt + 2);
+        kstep(lds_s0, lds_s1, lds_s2, kt);
+        kstep(lds_s1, lds_s2, lds_s0, kt + 1);
+        kstep(lds_s2, lds_s0, lds_s1, kt + 2);
       }
-      if (kt < nk) kstep(lds_s0, lds_s2, kt);
-      if (kt + 1 < nk) kstep(lds_s1, lds_s0, kt + 1);
+      if (kt < nk) kstep(lds_s0, lds_s1, lds_s2, kt);
+      if (kt + 1 < nk) kstep(lds_s1, lds_s2, lds_s0, kt + 1);
     } else {
       for (; kt + 3 < nk; kt += 4) {
-        kstep(lds_s0, lds_s3, kt);
-        kstep(lds_s1, lds_s0, kt + 1);
-        kstep(lds_s2, lds_s1, kt + 2);
-        kstep(lds_s3, lds_s2, kt + 3);
+        kstep(lds_s0, lds_s1, lds_s3, kt);
+        kstep(lds_s1, lds_s2, lds_s0, kt + 1);
+        kstep(lds_s2, lds_s3, lds_s1, kt + 2);
+        kstep(lds_s3, lds_s0, lds_s2, kt + 3);
       }
-      if (kt < nk) kstep(lds_s0, lds_s3, kt);
-      if (kt + 1 < nk) kstep(lds_s1, lds_s0, kt + 1);
-      if (kt + 2 < nk) kstep(lds_s2, lds_s1, kt + 2);
+      if (kt < nk) kstep(lds_s0, lds_s1, lds_s3, kt);
+      if (kt + 1 < nk) kstep(lds_s1, lds_s2, lds_s0, kt + 1);
+      if (kt + 2 < nk) kstep(lds_s2, lds_s3, lds_s1, kt + 2);
     }
     // No load of this tile may land in a stage after the next tile refills
     // it (each wave refills only the rows it loads itself).
@@ -467,6 +502,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // epilogue: lane holds column (lane & 31) and rows 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
+      if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
@@ -519,19 +555,23 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 
 template <bool WQ>
 struct Configs {
-  //                          BM   BN  WM WN  BK ST  gated
+  //                          BM   BN  WM WN  BK ST  gated      GM
   using Big   = TileCfg<128, 256, 2, 2, 64, 3, false, WQ>;
   using BigG  = TileCfg<128, 256, 2, 2, 64, 3, true, WQ>;
   using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false, WQ>;
   using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true, WQ>;
-  using Slim  = TileCfg<64, 256, 1, 4, 64, 3, false, WQ>;
-  using SlimG = TileCfg<64, 256, 1, 4, 64, 3, true, WQ>;
+  using Wide  = TileCfg<128, 256, 1, 4, 64, 3, false, WQ, 1>;
+  using WideG = TileCfg<128, 256, 1, 4, 64, 3, true, WQ, 1>;
   using Thin  = TileCfg<32, 256, 1, 4, 64, 4, false, WQ>;
   using ThinG = TileCfg<32, 256, 1, 4, 64, 4, true, WQ>;
 };
 
-// Tile height follows the mean rows per local expert (the host cannot see the
-// real counts without a device round trip).
+// Tile shape from the mean rows per local expert (the host cannot see the
+// real counts without a device round trip):
+//   >= 128  MFMA-bound: square-ish tiles, weight slices shared by GM m-tiles
+//   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
+//           byte is read once, with the idle fragments skipped
+//   < 16    decode: short tiles.
 template <bool WQ>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ>;
@@ -539,12 +579,12 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (g.gated) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
-    if (mean_rows >= 48) return launch_cfg<typename C::SlimG>(g, max_rows, s);
+    if (mean_rows >= 16) return launch_cfg<typename C::WideG>(g, max_rows, s);
     return launch_cfg<typename C::ThinG>(g, max_rows, s);
   }
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
-  if (mean_rows >= 48) return launch_cfg<typename C::Slim>(g, max_rows, s);
+  if (mean_rows >= 16) return launch_cfg<typename C::Wide>(g, max_rows, s);
   return launch_cfg<typename C::Thin>(g, max_rows, s);
 }
 

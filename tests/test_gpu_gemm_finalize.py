@@ -1,7 +1,9 @@
 """GPU parity of the grouped GEMMs and of finalize against the oracle, each on
 its own, at sizes that span several tiles with ragged tails, for every tile
 shape the library picks (the shape follows the mean rows per local expert:
->= 512, >= 128, >= 48, below).
+>= 512, >= 128, >= 16, below), including segments that end inside each of the
+32-row fragments of the 128-row weight-streaming tile and segments longer
+than one m-tile.
 
 Bar: relative Frobenius error <= 1e-2 for bf16 outputs against the float64
 oracle (the GPU accumulates in fp32 and rounds once to bf16: expected ~3e-3).
@@ -32,7 +34,8 @@ def _gpu():
 GEMM_CASES = [
     # name, counts per local expert, H, I
     ("thin_tiles", [0, 1, 5, 33, 2, 0, 17, 40], 256, 192),
-    ("slim_tiles", [70, 0, 130, 55], 384, 320),
+    ("wide_tiles", [70, 0, 130, 55], 384, 320),
+    ("wide_ragged_fragments", [0, 3, 129, 31, 64, 97], 256, 192),
     ("mid_tiles", [300, 1, 420], 256, 448),
     ("big_tiles", [700, 613], 512, 384),
     ("one_expert_many_rows", [1100], 256, 256),
