@@ -4,8 +4,8 @@
 //   C[r, n] = sum_k A[r, k] * W[e, n, k]     for r in expert e's row segment
 //
 // Both operands are contiguous along k, which is the natural operand layout
-// of the CDNA4 MFMA v_mfma_f32_32x32x16_bf16 (each lane supplies 8 consecutive
-// k of one row of A and of one row of W), so no transposes are needed.
+// of the CDNA4 MFMA v_mfma_f32_32x32x16_bf16 (each lane supplies 8 k of one
+// row of A and of one row of W), so no transposes are needed.
 //
 // Work decomposition
 //   - Each expert's row segment [offsets[e], offsets[e+1]) is cut into m-tiles
@@ -26,30 +26,39 @@
 //     and to the expert's weights: rows of a ragged m-tile past the segment
 //     read as zero (never another expert's rows) and are masked on store.
 //
-// Tile pipeline (per k-step of BK, STAGES LDS stages)
+// Tile pipeline (k-steps of 64; STAGES activation stages, B_STAGES weight
+// stages of 128 bytes per weight row: one k-step of bf16, four of e2m1)
 //   - Operands move global -> LDS with buffer_load ... lds (16 bytes a lane,
 //     straight into LDS, no registers): one wave instruction fills 1 KiB of a
-//     stage.  Rows are stored XOR-swizzled in 16-byte chunks (swz below), the
-//     lane choosing the global chunk the swizzle puts at its LDS position, so
-//     MFMA operand reads are free of bank conflicts.
-//   - k-step kt computes from stage kt % STAGES while the loads of k-step
-//     kt + STAGES - 1 stream into the stage computed one k-step earlier.  A
-//     k-step ends by waiting until this wave's loads of k-step kt + 1 landed
-//     (a partial vmcnt: later k-steps stay in flight) and a barrier, so global
-//     latency is hidden behind STAGES - 1 k-steps of MFMAs.
+//     stage, 8 rows x 128 bytes.  Rows are stored XOR-swizzled in 16-byte
+//     chunks (swz below), the lane choosing the global chunk the swizzle puts
+//     at its LDS position, so MFMA operand reads are free of bank conflicts.
+//   - k-step kt computes from activation stage kt % STAGES while the loads of
+//     k-step kt + STAGES - 1 stream into the stage computed one k-step
+//     earlier; a weight stage streams in while the one before it is used.
+//   - A k-step ends by waiting until this wave's loads that the next k-step
+//     reads have landed (a partial vmcnt: later loads stay in flight; the
+//     count comes from a compile-time model of the issue order) and a
+//     barrier.  The barrier sits before the last sub-step's MFMAs, and the
+//     first operands of the next k-step are read right after it, so LDS read
+//     latency hides behind those MFMAs.
 //   - Inside a k-step, fenced so the compiler keeps the order: the operand
 //     reads of sub-step ks + 1 and a slice of the loads are issued before the
 //     MFMAs of sub-step ks.
 //
 // MXFP4 weights (e2m1 pairs, low nibble = even k, one E8M0 scale byte per 32
-// k; vLLM flashinfer_moe_ep.py, _E2M1_LUT and _dequant_fp4_ue8m0_gran32): the
-// packed tile (32 bytes per row per k-step) is loaded into LDS the same way;
-// each lane reads its 16 bytes once per k-step and expands 4 of them per
-// sub-step to bf16 with v_cvt_scalef32_pk_bf16_fp4 (value x 2^(s-127), exact
-// in bf16), so the MFMAs and the activations stay bf16.  Inside a k-step,
-// sub-step ks and lane half h cover k = 32h + 8ks .. +7 for A and W alike,
-// which makes a lane's packed bytes of one k-step contiguous and puts all its
-// k in one 32-wide scale block.
+// k; vLLM flashinfer_moe_ep.py, _E2M1_LUT and _dequant_fp4_ue8m0_gran32): a
+// weight stage holds 256 k of every row (128 packed bytes, so loads fetch
+// whole 128-byte row segments, as for bf16).  Each lane reads its 16 packed
+// bytes of a k-step once and expands 4 of them per sub-step to bf16 with
+// v_cvt_scalef32_pk_bf16_fp4 (value x 2^(s-127), exact in bf16), so the MFMAs
+// and the activations stay bf16.  Inside a k-step, sub-step ks and lane half h
+// cover k = 32h + 8ks .. +7 for A and W alike, which makes a lane's packed
+// bytes of one k-step contiguous and puts all its k in one 32-wide scale
+// block.  The scale bytes a lane needs for a weight stage (4 per fragment)
+// are loaded into registers one weight stage ahead, right before that
+// stage's weight loads: vmcnt retires in issue order, so a wait for them
+// never waits for younger weight stages.
 //
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
@@ -57,32 +66,44 @@
 // forms silu(g) * u in registers and writes BN/2 columns of h.
 #include "moe_common.h"
 
+#include <utility>
+
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Calls f(ic<0>), ..., f(ic<N-1>) in order: loop bodies with compile-time
+// indices (stage objects, wait counts).
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, J...>) {
+  (f(ic<J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // Descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-family
 // parts: 32-bit data format, out-of-range offsets read as zero.
 constexpr int kBufferFlags = 0x00020000;
 
-// Swizzle of 16-byte chunk positions within a tile row of BK bf16:
-//   BK = 64 (8 chunks, 128-byte rows): chunk c of row r sits at
-//           c ^ (r & 7) ^ ((r >> 3) & 1);
-//   BK = 32 (4 chunks, 64-byte rows):  c ^ ((r >> 2) & 3).
-// Either way 16 consecutive rows read at one logical chunk (a 16-lane group
-// of an MFMA operand read) hit 16 distinct 16-byte bank groups of the 64-bank
-// LDS.
-template <int BK>
-__device__ __forceinline__ int swz_key(int row) {
-  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
-  else return (row >> 2) & 3;
-}
+// Swizzle of the eight 16-byte chunks of a 128-byte tile row: chunk c of row
+// r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), so 16 consecutive rows
+// read at one logical chunk (a 16-lane group of an MFMA operand read) hit 16
+// distinct 16-byte bank groups of the 64-bank LDS.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BK>
+// uint16 offset of chunk `chunk` of tile row `row` (rows of 64 uint16).
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ swz_key<BK>(row)) << 3);
+  return row * 64 + ((chunk ^ swz_key(row)) << 3);
 }
 
 // Device-only instructions sit in helpers whose bodies exist only in the
@@ -142,10 +163,11 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool GATED_, bool WQ_ = false,
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GATED_, bool WQ_ = false,
           int GM_ = 8>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int BK = 64;    // k per k-step (128 bytes of an activation row)
   static constexpr bool GATED = GATED_;
   static constexpr bool WQ = WQ_;  // weights in MXFP4
   static constexpr int GM = GM_;   // m-tiles per group of the tile order
@@ -156,33 +178,81 @@ struct TileCfg {
   // skip row fragments past the segment (one wave row only: otherwise the
   // waves of the lower rows would idle while the others work)
   static constexpr bool SKIP = (WM == 1 && FM > 1);
-  static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per tile row
-  static constexpr int ROWS_PER_LD = kWave / CHUNKS;  // tile rows per 1 KiB load
-  static constexpr int A_LD = BM / ROWS_PER_LD / NWAVES;  // loads per wave per k-step
-  // MXFP4: a packed row of one k-step is 32 bytes, so one load covers 32 rows
-  static constexpr int B_LD = WQ ? BN / 32 / NWAVES : BN / ROWS_PER_LD / NWAVES;
   static constexpr int SUBSTEPS = BK / 16;
   static constexpr int OUT_N = GATED ? BN / 2 : BN;
-  static constexpr int A_ELEMS = BM * BK;                  // uint16 units
-  static constexpr int B_ELEMS = WQ ? BN * 16 : BN * BK;   // uint16 units (packed: 32 B/row)
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  // vector-memory loads per wave per k-step: tile loads (+ one scale byte per
-  // weight fragment for MXFP4)
-  static constexpr int LOADS = A_LD + B_LD + (WQ ? FN : 0);
-  // Loads a wave may leave in flight at the end of a k-step so that those of
-  // the next k-step have landed.  In steady state that is (STAGES - 2) * LOADS;
-  // the prologue issues no scale loads between its tile loads, so the first
-  // k-steps need the smaller count below (it also covers the steady state: the
-  // extra scale loads it waits for were consumed a k-step earlier anyway).
-  static constexpr int WAIT = (STAGES - 2) * (A_LD + B_LD) + ((WQ && STAGES > 2) ? FN : 0);
-  static_assert(BK == 32 || BK == 64, "k-step");
-  static_assert(!WQ || BK == 64, "MXFP4 tiles use 64-wide k-steps (two scale blocks)");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
-  static_assert(WAIT < 64, "in-flight loads must fit vmcnt");
+  // one load instruction: 8 rows x 128 bytes
+  static constexpr int A_LD = BM / 8 / NWAVES;   // activation loads per wave per k-step
+  static constexpr int B_LD = BN / 8 / NWAVES;   // weight loads per wave per weight stage
+  static constexpr int B_KS = WQ ? 4 : 1;        // k-steps per weight stage
+  // MXFP4: three weight stages, so two stream while one is used (a weight
+  // stage lasts four k-steps; with one in flight the stream stalls between)
+  static constexpr int B_STAGES = WQ ? 3 : STAGES;
+  static constexpr int SCQ = WQ ? 4 * FN : 0;    // scale-byte loads per wave per weight stage
+  static constexpr int A_ELEMS = BM * 64;        // uint16 per activation stage
+  static constexpr int B_ELEMS = BN * 64;        // uint16 per weight stage
+  // k-steps per unrolled loop body: every stage object is then compile-time
+  static constexpr int UNROLL = STAGES * (B_KS * B_STAGES) / gcd_c(STAGES, B_KS * B_STAGES);
+
+  // ---- model of the load issue order, for the end-of-k-step vmcnt waits ----
+  // Prologue: the scale bytes of weight stage 0; then, for bf16, the
+  // activation and weight loads of k-steps 0 .. STAGES-2 (stage by stage),
+  // for MXFP4 the weight stages 0 .. B_STAGES-2 and then the activation loads
+  // of k-steps 0 .. STAGES-2.  k-step kt: when it opens a weight stage q, the
+  // scale bytes of stage q + 1; then (spread over its sub-steps) the
+  // activation loads of kt + STAGES - 1 and, when it opens a weight stage,
+  // the weight loads of the stage B_STAGES - 1 ahead.
+  static constexpr int loads_at(int kt) { return A_LD + (kt % B_KS == 0 ? B_LD + SCQ : 0); }
+  static constexpr int sum_loads(int from, int to) {
+    int n = 0;
+    for (int j = from; j <= to; ++j) n += loads_at(j);
+    return n;
+  }
+  // prologue loads issued after the activation loads of k-step s / after the
+  // weight loads of stage q (whole groups only: conservative)
+  static constexpr int pro_after_a(int s) {
+    return B_KS == 1 ? (STAGES - 2 - s) * (A_LD + B_LD) : (STAGES - 2 - s) * A_LD;
+  }
+  static constexpr int pro_after_b(int q) {
+    return B_KS == 1 ? (STAGES - 2 - q) * (A_LD + B_LD)
+                     : (B_STAGES - 2 - q) * B_LD + (STAGES - 1) * A_LD;
+  }
+  // Loads that may stay in flight at the end of k-step kt with the
+  // activation loads of kt + 1 landed, and its weight stage when kt + 1 opens
+  // one: only loads issued in later k-steps (or later in the prologue) count.
+  static constexpr int need(int kt) {
+    const int ia = kt + 2 - STAGES;  // k-step that issued the activations of kt + 1
+    int n = ia >= 0 ? sum_loads(ia + 1, kt) : pro_after_a(kt + 1) + sum_loads(0, kt);
+    if ((kt + 1) % B_KS == 0) {
+      const int q = (kt + 1) / B_KS;
+      const int ib = (q - (B_STAGES - 1)) * B_KS;  // k-step that issued weight stage q
+      const int nb = ib >= 0 ? sum_loads(ib + 1, kt) : pro_after_b(q) + sum_loads(0, kt);
+      n = nb < n ? nb : n;
+    }
+    return n;
+  }
+  // the count for every k-step at position j of the unrolled body (minimum
+  // over the first bodies, which include the prologue transient)
+  static constexpr int wait_at(int j) {
+    int n = 63;
+    for (int kt = j; kt < 4 * UNROLL + 2 * (STAGES + B_KS * B_STAGES); kt += UNROLL) {
+      const int m = need(kt);
+      n = m < n ? m : n;
+    }
+    return n;
+  }
+  static constexpr int WAIT_PRO = pro_after_a(0) < pro_after_b(0) ? pro_after_a(0) : pro_after_b(0);
+
+  static constexpr bool waits_fit() {
+    for (int j = 0; j < UNROLL; ++j)
+      if (wait_at(j) < 0 || wait_at(j) >= 64) return false;
+    return WAIT_PRO >= 0 && WAIT_PRO < 64;
+  }
+  static_assert(waits_fit(), "in-flight loads must fit vmcnt");
+  static_assert(STAGES >= 2 && STAGES <= 4 && B_STAGES >= 2 && B_STAGES <= 4, "stages");
+  static_assert(UNROLL <= 12, "unrolled body");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
-  static_assert(BM % (ROWS_PER_LD * NWAVES) == 0 && BN % ((WQ ? 32 : ROWS_PER_LD) * NWAVES) == 0,
-                "whole load instructions");
+  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "whole load instructions");
 };
 
 // First virtual weight row of fragment fn of wave column wn.
@@ -203,8 +273,6 @@ __device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t
 // s = 0 gives 0, s = 255 gives +inf).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // 8 e2m1 values (4 bytes, low nibble first) times `scale` -> 8 bf16.
 __device__ __forceinline__ bf16x8 expand_fp4x8(uint32_t w, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
@@ -221,14 +289,35 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
+  constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
   // LDS stages as distinct objects, so the compiler knows that loads into one
   // never alias operand reads from another (unused ones are tiny)
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s1[Cfg::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s2[ST > 2 ? Cfg::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s3[ST > 3 ? Cfg::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a0[Cfg::A_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a1[Cfg::A_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a2[ST > 2 ? Cfg::A_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a3[ST > 3 ? Cfg::A_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b0[Cfg::B_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b1[Cfg::B_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b2[SB > 2 ? Cfg::B_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b3[SB > 3 ? Cfg::B_ELEMS : 8];
   __shared__ int32_t s_mt[1025];
   __shared__ int32_t s_scratch[16];
+
+  // stage objects by compile-time index (taken modulo the stage count)
+  auto a_stage = [&](auto i) -> uint16_t* {
+    constexpr int s = decltype(i)::value % ST;
+    if constexpr (s == 0) return lds_a0;
+    else if constexpr (s == 1) return lds_a1;
+    else if constexpr (s == 2) return lds_a2;
+    else return lds_a3;
+  };
+  auto b_stage = [&](auto i) -> uint16_t* {
+    constexpr int s = decltype(i)::value % SB;
+    if constexpr (s == 0) return lds_b0;
+    else if constexpr (s == 1) return lds_b1;
+    else if constexpr (s == 2) return lds_b2;
+    else return lds_b3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -261,15 +350,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int slot = (G % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                                 : static_cast<int>(blockIdx.x);
   const int N_total = Cfg::GATED ? 2 * N_out : N_out;
-  const int nk = K / BK;
+  const int nk = K / BK;                  // k-steps
+  const int nq = (nk + BKS - 1) / BKS;    // weight stages
 
-  // Load j of this wave fills tile rows [R rb, R rb + R) (R = ROWS_PER_LD,
-  // rb = j * NWAVES + wave); lane L writes the 16 bytes at LDS row
-  // R rb + L / CHUNKS, position L % CHUNKS, so it fetches the logical chunk
-  // the swizzle puts there.
+  // Load j of this wave fills tile rows [8 rb, 8 rb + 8) (rb = j * NWAVES +
+  // wave); lane L writes the 16 bytes at LDS row 8 rb + L / 8, position L % 8,
+  // so it fetches the logical chunk the swizzle puts there.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int ld_sub = lane / Cfg::CHUNKS;
-  const int ld_pos = lane % Cfg::CHUNKS;
+  const int ld_sub = lane >> 3;
+  const int ld_pos = lane & 7;
 
   for (int tile = slot; tile < total_tiles; tile += G) {
     // grouped order: GM m-tiles share each n-tile column
@@ -286,14 +375,17 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       const int mid = (lo + hi) >> 1;
       if (s_mt[mid] <= m_tile) lo = mid; else hi = mid;
     }
-    const int e = lo;
+    // the tile's expert and rows are the same in every lane: held in scalar
+    // registers, so the branches on them below are scalar branches
+    const int e = __builtin_amdgcn_readfirstlane(lo);
     const int seg_end = min(static_cast<int64_t>(offsets[e + 1]), R_pad);
-    const int row0 = offsets[e] + (m_tile - s_mt[e]) * BM;
-    const int rows = seg_end - row0;
+    const int row0 = __builtin_amdgcn_readfirstlane(offsets[e] + (m_tile - s_mt[e]) * BM);
+    const int rows = __builtin_amdgcn_readfirstlane(seg_end - row0);
     if (rows <= 0) continue;
     const int n0 = n_tile * Cfg::OUT_N;
     // row fragments of this wave that hold rows of the segment (wave-uniform)
-    const int fm_act = Cfg::SKIP ? min(FM, (rows - wm * Cfg::WTM + 31) / 32) : FM;
+    const int fm_act = __builtin_amdgcn_readfirstlane(
+        Cfg::SKIP ? min(FM, (rows - wm * Cfg::WTM + 31) / 32) : FM);
 
     // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
     // this expert's weights; loads past either range return zero.
@@ -310,8 +402,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     uint32_t a_off[Cfg::A_LD];
 #pragma unroll
     for (int j = 0; j < Cfg::A_LD; ++j) {
-      const int r = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
-      const int c = ld_pos ^ swz_key<BK>(r);
+      const int r = (j * Cfg::NWAVES + wave_u) * 8 + ld_sub;
+      const int c = ld_pos ^ swz_key(r);
       a_off[j] = (static_cast<uint32_t>(r) * K + c * 8) * 2u;
     }
     // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
@@ -322,34 +414,40 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     uint32_t b_off[Cfg::B_LD];
 #pragma unroll
     for (int j = 0; j < Cfg::B_LD; ++j) {
-      if constexpr (Cfg::WQ) {
-        // 32 rows per load, lane L -> row L / 2, 16-byte position L % 2
-        const int v = (j * Cfg::NWAVES + wave_u) * 32 + (lane >> 1);
-        const int c = (lane & 1) ^ ((v >> 3) & 1);
-        b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
-      } else {
-        const int v = (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD + ld_sub;
-        const int c = ld_pos ^ swz_key<BK>(v);
-        b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
-      }
+      const int v = (j * Cfg::NWAVES + wave_u) * 8 + ld_sub;
+      const int c = ld_pos ^ swz_key(v);
+      b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
     }
-    // MXFP4 scale bytes: lane's weight row per fragment, block 2 kt + half
+    // MXFP4 scale bytes: lane's weight row per fragment; k-step kt, half h
+    // uses block 2 kt + h, i.e. byte 2 p + h of the 8 of its weight stage
     const uint32_t s_row = Cfg::WQ ? static_cast<uint32_t>(K) / 32u : 0u;  // scale bytes per row
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(W_scales + static_cast<int64_t>(e) * N_total * s_row), 0,
         static_cast<int>(static_cast<uint32_t>(N_total) * s_row), kBufferFlags);
-    uint32_t s_off[Cfg::WQ ? FN : 1];
-    uint32_t sc_cur[Cfg::WQ ? FN : 1], sc_nxt[Cfg::WQ ? FN : 1];
+    constexpr int NSF = Cfg::WQ ? FN : 1;
+    uint32_t s_off[NSF];
+    uint32_t sc_cur[NSF][4], sc_nxt[NSF][4];
     if constexpr (Cfg::WQ) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
         s_off[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn) + (lane & 31))) * s_row +
                     (lane >> 5);
     }
-    auto load_scales = [&](uint32_t* dst, int kt) {
+    // the scale bytes of weight stage q (blocks 8q + 2p + h, p = 0..3)
+    auto load_scales = [&](int q) {
       if constexpr (Cfg::WQ) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) dst[fn] = load_byte(s_rsrc, s_off[fn], kt * 2);
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) sc_nxt[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p, q * 8);
+      }
+    };
+    auto rotate_scales = [&]() {
+      if constexpr (Cfg::WQ) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) sc_cur[fn][p] = sc_nxt[fn][p];
       }
     };
 
@@ -359,35 +457,32 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    // Slice `part` (of SUB) of k-step kt of A and W into LDS stage `st`: the
-    // loads of one k-step are spread over its sub-steps.
-    auto gload = [&](uint16_t* st, int kt, int part) {
-      const int soff = kt * BK * 2;
-      const int soff_b = Cfg::WQ ? kt * BK / 2 : soff;
+    // Slice `part` (of SUB) of the activation loads of k-step kt into stage
+    // `st`, and of the weight loads of weight stage q into `wst`: the loads
+    // are spread over the sub-steps of the k-step that issues them.
+    auto gload_a = [&](uint16_t* st, int kt, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
         if (j % SUB == part)
-          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * Cfg::ROWS_PER_LD * BK, a_off[j],
-                    soff);
+          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], kt * BK * 2);
+    };
+    auto gload_b = [&](uint16_t* wst, int q, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::B_LD; ++j)
         if ((j + Cfg::A_LD) % SUB == part)
-          lds_dma16(b_rsrc, st + Cfg::A_ELEMS + (j * Cfg::NWAVES + wave_u) * 512, b_off[j],
-                    soff_b);
-    };
-    auto gload_all = [&](uint16_t* st, int kt) {
-#pragma unroll
-      for (int p = 0; p < SUB; ++p) gload(st, kt, p);
+          lds_dma16(b_rsrc, wst + (j * Cfg::NWAVES + wave_u) * 512, b_off[j], q * 128);
     };
 
-    // Operand fragments of k sub-step ks from stage `as`: lane half h holds
-    // k = 32h + 8ks .. +7 of its A row and of its W row.  `ln` is the lane id
-    // made opaque per k-step so the (swizzled) addresses are rebuilt there
-    // instead of all being kept live.  MXFP4: at ks == 0 the lane's 16 packed
-    // bytes of the k-step are read into `bq`; every sub-step expands 4 of them.
-    auto load_frags = [&](const uint16_t* as, int ln, int ks, bf16x8* af, bf16x8* bfr, uint4* bq,
-                          const uint32_t* sc) {
-      const uint16_t* bs = as + Cfg::A_ELEMS;
+    // Operand fragments of sub-step ks of the k-step at position p of its
+    // weight stage, from activation stage `as` and weight stage `bs`: lane
+    // half h holds k = 32h + 8ks .. +7 of its A row and of its W row.  `ln` is
+    // the lane id made opaque per k-step so the (swizzled) addresses are
+    // rebuilt there instead of all being kept live.  MXFP4: at ks == 0 the
+    // lane's 16 packed bytes of the k-step (chunk 2p + h of its row) are read
+    // into `bq`; every sub-step expands 4 of them (sub-step 0's at the top of
+    // the k-step: see expand0).
+    auto load_frags = [&](const uint16_t* as, const uint16_t* bs, int ln, int ks, int p,
+                          bf16x8* af, bf16x8* bfr, uint4* bq) {
       const int frag_row = ln & 31;
       const int half = ln >> 5;
       const int chunk = half * SUB + ks;
@@ -395,17 +490,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       for (int fm = 0; fm < FM; ++fm) {
         if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
-        af[fm] = *reinterpret_cast<const bf16x8*>(as + swz<BK>(r, chunk));
+        af[fm] = *reinterpret_cast<const bf16x8*>(as + swz(r, chunk));
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int v = b_row0<Cfg>(wn, fn) + frag_row;
         if constexpr (Cfg::WQ) {
-          if (ks == 0) bq[fn] = *reinterpret_cast<const uint4*>(bs + v * 16 + ((half ^ ((v >> 3) & 1)) << 3));
-          const uint32_t word = ks == 0 ? bq[fn].x : ks == 1 ? bq[fn].y : ks == 2 ? bq[fn].z : bq[fn].w;
-          bfr[fn] = expand_fp4x8(word, e8m0_to_f32(sc[fn]));
+          if (ks == 0) {
+            bq[fn] = *reinterpret_cast<const uint4*>(bs + swz(v, 2 * p + half));
+          } else {
+            const uint32_t word = ks == 1 ? bq[fn].y : ks == 2 ? bq[fn].z : bq[fn].w;
+            bfr[fn] = expand_fp4x8(word, e8m0_to_f32(sc_cur[fn][p]));
+          }
         } else {
-          bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz<BK>(v, chunk));
+          bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz(v, chunk));
         }
       }
     };
@@ -415,27 +513,55 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     static_assert(SUB % 2 == 0, "sub-step 0 of the next k-step reuses buffer 0");
     bf16x8 fa[2][FM], fb[2][FN];
     uint4 bq[Cfg::WQ ? FN : 1];
+    // MXFP4: sub-step 0's weight fragments from the packed words read after
+    // the previous barrier.  Expanding them there would stall the in-order
+    // issue on that LDS read ahead of the last MFMAs; here those MFMAs are
+    // already in flight.
+    auto expand0 = [&](int p) {
+      if constexpr (Cfg::WQ) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          fb[0][fn] = expand_fp4x8(bq[fn].x, e8m0_to_f32(sc_cur[fn][p]));
+      }
+    };
 
-    // k-step kt from stage `cur` while k-step kt + ST - 1 streams into `ld`
-    // (the stage computed in the previous k-step, which the barrier closed);
-    // the last k-steps reload the final one into stages nobody reads again.
-    // The barrier that closes `cur` and opens `nxt` (k-step kt + 1) comes
-    // before the last sub-step's MFMAs, and sub-step 0 of `nxt` is read right
-    // after it, so that LDS latency hides behind those MFMAs.
-    auto kstep = [&](const uint16_t* cur, const uint16_t* nxt, uint16_t* ld, int kt) {
+    // k-step kt at position J of the unrolled body: computes from activation
+    // stage J and weight stage J / BKS; streams the activations of k-step
+    // kt + ST - 1 into activation stage J - 1 (computed in the previous
+    // k-step, which the barrier closed) and, when J opens a weight stage, the
+    // weight stage SB - 1 ahead into the one the previous weight stage used;
+    // the last k-steps reload the final ones into stages nobody reads again.
+    auto kstep = [&](auto jc, int kt) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int P = J % BKS;  // position inside the weight stage
+      uint16_t* const cur_a = a_stage(ic<J>{});
+      uint16_t* const nxt_a = a_stage(ic<J + 1>{});
+      uint16_t* const ld_a = a_stage(ic<J + ST - 1>{});
+      uint16_t* const cur_b = b_stage(ic<J / BKS>{});
+      uint16_t* const nxt_b = b_stage(ic<(J + 1) / BKS>{});
+      uint16_t* const ld_b = b_stage(ic<J / BKS + SB - 1>{});
       const int kn = min(kt + ST - 1, nk - 1);
-      load_scales(sc_nxt, min(kt + 1, nk - 1));  // before the tile loads: see the vmcnt count
+      const int qn = min(kt / BKS + SB - 1, nq - 1);
+      if constexpr (P == 0) {
+        // scales of this weight stage (loaded a stage ago), then those of the
+        // next one, ahead of this k-step's tile loads as the wait model counts
+        rotate_scales();
+        load_scales(min(kt / BKS + 1, nq - 1));
+      }
+      expand0(P);
       const int ln = opaque(lane);
 #pragma unroll
       for (int ks = 0; ks < SUB; ++ks) {
-        if (ks + 1 < SUB) load_frags(cur, ln, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1], bq, sc_cur);
-        gload(ld, kn, ks);
+        if (ks + 1 < SUB)
+          load_frags(cur_a, cur_b, ln, ks + 1, P, fa[(ks + 1) & 1], fb[(ks + 1) & 1], bq);
+        gload_a(ld_a, kn, ks);
+        if constexpr (P == 0) gload_b(ld_b, qn, ks);
         if (ks + 1 == SUB) {
-          // this wave's loads of k-step kt + 1 landed and its reads of `cur`
-          // returned; after the barrier, every wave's have
-          wait_vmem_lds<Cfg::WAIT>();
+          // this wave's loads that k-step kt + 1 reads landed and its reads
+          // of the current stages returned; after the barrier, every wave's
+          wait_vmem_lds<Cfg::wait_at(J)>();
           stage_barrier();
-          load_frags(nxt, ln, 0, fa[0], fb[0], bq, sc_nxt);
+          load_frags(nxt_a, nxt_b, ln, 0, (J + 1) % BKS, fa[0], fb[0], bq);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -448,51 +574,38 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (Cfg::WQ) {
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) sc_cur[fn] = sc_nxt[fn];
-      }
     };
 
-    // prologue: scales of k-step 0, k-steps 0 .. ST-2 in flight, then k-step 0
-    // complete (the prologue issues no scale loads after the tile loads)
-    load_scales(sc_cur, 0);
-    gload_all(lds_s0, 0);
-    if constexpr (ST > 2) gload_all(lds_s1, min(1, nk - 1));
-    if constexpr (ST > 3) gload_all(lds_s2, min(2, nk - 1));
-    wait_vmem<(ST - 2) * (Cfg::A_LD + Cfg::B_LD)>();
-    stage_barrier();
-    load_frags(lds_s0, opaque(lane), 0, fa[0], fb[0], bq, sc_cur);
-
-    // main loop unrolled by ST, so every stage is a compile-time object:
-    // k-step kt reads stage kt % ST, opens (kt + 1) % ST and loads into
-    // stage (kt - 1) % ST
-    int kt = 0;
-    if constexpr (ST == 2) {
-      for (; kt + 1 < nk; kt += 2) {
-        kstep(lds_s0, lds_s1, lds_s1, kt);
-        kstep(lds_s1, lds_s0, lds_s0, kt + 1);
-      }
-      if (kt < nk) kstep(lds_s0, lds_s1, lds_s1, kt);
-    } else if constexpr (ST == 3) {
-      for (; kt + 2 < nk; kt += 3) {
-        kstep(lds_s0, lds_s1, lds_s2, kt);
-        kstep(lds_s1, lds_s2, lds_s0, kt + 1);
-        kstep(lds_s2, lds_s0, lds_s1, kt + 2);
-      }
-      if (kt < nk) kstep(lds_s0, lds_s1, lds_s2, kt);
-      if (kt + 1 < nk) kstep(lds_s1, lds_s2, lds_s0, kt + 1);
+    // prologue, in the order the wait model assumes
+    load_scales(0);
+    if constexpr (BKS == 1) {
+      static_for<ST - 1>([&](auto s) {
+#pragma unroll
+        for (int p = 0; p < SUB; ++p) {
+          gload_a(a_stage(s), min(static_cast<int>(s), nk - 1), p);
+          gload_b(b_stage(s), min(static_cast<int>(s), nk - 1), p);
+        }
+      });
     } else {
-      for (; kt + 3 < nk; kt += 4) {
-        kstep(lds_s0, lds_s1, lds_s3, kt);
-        kstep(lds_s1, lds_s2, lds_s0, kt + 1);
-        kstep(lds_s2, lds_s3, lds_s1, kt + 2);
-        kstep(lds_s3, lds_s0, lds_s2, kt + 3);
-      }
-      if (kt < nk) kstep(lds_s0, lds_s1, lds_s3, kt);
-      if (kt + 1 < nk) kstep(lds_s1, lds_s2, lds_s0, kt + 1);
-      if (kt + 2 < nk) kstep(lds_s2, lds_s3, lds_s1, kt + 2);
+      static_for<SB - 1>([&](auto q) {
+#pragma unroll
+        for (int p = 0; p < SUB; ++p) gload_b(b_stage(q), min(static_cast<int>(q), nq - 1), p);
+      });
+      static_for<ST - 1>([&](auto s) {
+#pragma unroll
+        for (int p = 0; p < SUB; ++p) gload_a(a_stage(s), min(static_cast<int>(s), nk - 1), p);
+      });
     }
+    wait_vmem<Cfg::WAIT_PRO>();
+    stage_barrier();
+    load_frags(lds_a0, lds_b0, opaque(lane), 0, 0, fa[0], fb[0], bq);
+
+    // main loop, U k-steps per body, then the remaining k-steps
+    int kt = 0;
+    for (; kt + U <= nk; kt += U) static_for<U>([&](auto j) { kstep(j, kt + j); });
+    static_for<U - 1>([&](auto j) {
+      if (kt + j < nk) kstep(j, kt + j);
+    });
     // No load of this tile may land in a stage after the next tile refills
     // it (each wave refills only the rows it loads itself).
     wait_vmem<0>();
@@ -555,15 +668,16 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 
 template <bool WQ>
 struct Configs {
-  //                          BM   BN  WM WN  BK ST  gated      GM
-  using Big   = TileCfg<128, 256, 2, 2, 64, 3, false, WQ>;
-  using BigG  = TileCfg<128, 256, 2, 2, 64, 3, true, WQ>;
-  using Mid   = TileCfg<128, 128, 2, 2, 64, 2, false, WQ>;
-  using MidG  = TileCfg<128, 128, 2, 2, 64, 2, true, WQ>;
-  using Wide  = TileCfg<128, 256, 1, 4, 64, 3, false, WQ, 1>;
-  using WideG = TileCfg<128, 256, 1, 4, 64, 3, true, WQ, 1>;
-  using Thin  = TileCfg<32, 256, 1, 4, 64, 4, false, WQ>;
-  using ThinG = TileCfg<32, 256, 1, 4, 64, 4, true, WQ>;
+  static constexpr int S3 = 3;  // activation stages of the 128-row tiles
+  //                          BM   BN  WM WN ST  gated      GM
+  using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ>;
+  using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ>;
+  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ>;
+  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ>;
+  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1>;
+  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1>;
+  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ>;
+  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ>;
 };
 
 // Tile shape from the mean rows per local expert (the host cannot see the
