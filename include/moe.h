@@ -167,6 +167,12 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
  *   w1      GEMM1 weights, N = 2I, K = H (BF16, or MXFP4: the decoded values
  *           are exact in bf16, so the MFMAs run in bf16 either way)
  *   h       (device) bf16 [R_pad, I] out; rows >= offsets[E_l] not written
+ *   workspace (device) optional scratch, 256-byte aligned, not overlapping
+ *           a_perm or h; NULL with workspace_bytes 0 is valid.  With
+ *           moe_grouped_gemm_workspace_size(R_pad, I, 1) bytes, calls whose
+ *           experts have few rows split the reduction over H into pieces
+ *           summed in a fixed order (results are the same on every run);
+ *           with less, fewer pieces or none.
  * Limits: H and I multiples of 64; R_pad >= offsets[E_l].  MXFP4 weights
  * without scales, or bf16 weights with scales, are MOE_ERR_INVALID_ARGUMENT. */
 int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
@@ -180,10 +186,18 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
  *   h       (device) bf16 [R_pad, I]
  *   w2      GEMM2 weights, N = H, K = I
  *   y       (device) bf16 [R_pad, H] out; rows >= offsets[E_l] not written
+ *   workspace as for moe_grouped_gemm1_act, with
+ *           moe_grouped_gemm_workspace_size(R_pad, H, 0) bytes
  * Limits: H and I multiples of 64. */
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                       int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Scratch bytes with which a grouped GEMM of R_pad permuted rows and N_out
+ * output columns (gated != 0: GEMM1, whose weights have 2 N_out rows) may
+ * split its reduction as far as it ever does; 0 when it never splits (large
+ * R_pad).  Host-only arithmetic.  MOE_ERR_INVALID_ARGUMENT on bad sizes. */
+int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated, size_t* bytes);
 
 /* Finalize (finalize() of page "modular_kernel.py"; MoEOutput of page
  * "moe_output.py": the routed scaling factor multiplies the routed sum before

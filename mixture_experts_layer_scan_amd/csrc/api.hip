@@ -4,6 +4,7 @@
 // follow convert_flashinfer_moe_output of vLLM's MoE output contract
 // (num_tokens >= 0, top_k > 0, int32 map, T * k elements, one device,
 // contiguous buffers, no destination for a deferred output).
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -144,6 +145,11 @@ struct Carve {
   }
 };
 
+// split-reduction scratch shared by the two routed GEMMs (one after the other)
+size_t routed_split_bytes(int64_t R_pad, int32_t H, int32_t I) {
+  return std::max(moe::gemm_split_ws_bytes(R_pad, 2 * I), moe::gemm_split_ws_bytes(R_pad, H));
+}
+
 size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) {
   const int64_t R_pad = moe_permuted_rows(T, k);
   size_t b = 0;
@@ -153,6 +159,7 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) 
   b += align_up(sizeof(int32_t) * (E_l + 1));           // offsets
   b += align_up(sizeof(uint16_t) * R_pad * H);          // x_perm, then GEMM2 output
   b += align_up(sizeof(uint16_t) * R_pad * I);          // h
+  b += align_up(routed_split_bytes(R_pad, H, I));       // GEMM split partials
   return b;
 }
 
@@ -262,7 +269,7 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
 
 static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                        int32_t K, int32_t N_out, int gated, const moe_weights* w, void* c,
-                       void* stream, const char* name) {
+                       void* workspace, size_t workspace_bytes, void* stream, const char* name) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
@@ -273,7 +280,16 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   MOE_CHECK(need_ptr(c, "output rows"));
   if (overlap(a, sizeof(uint16_t) * R_pad * K, c, sizeof(uint16_t) * R_pad * N_out))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
-  moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c};
+  if (workspace_bytes > 0) {
+    MOE_CHECK(need_ptr(workspace, "workspace"));
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return fail(MOE_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", name);
+    const size_t in_bytes = sizeof(uint16_t) * R_pad * K, out_bytes = sizeof(uint16_t) * R_pad * N_out;
+    if (overlap(workspace, workspace_bytes, a, in_bytes) || overlap(workspace, workspace_bytes, c, out_bytes))
+      return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: workspace must not overlap the rows", name);
+  }
+  moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
+                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes};
   hipError_t e = moe::launch_grouped_gemm(g, R_pad, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
@@ -282,21 +298,30 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
                           int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
                           void* h, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  (void)workspace;
-  (void)workspace_bytes;
   MOE_CHECK(check_gemm_dims(H, I));
   if (activation != MOE_ACT_SILU) return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
-  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, w1, h, stream, "moe_grouped_gemm1_act");
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, w1, h, workspace, workspace_bytes,
+                     stream, "moe_grouped_gemm1_act");
 }
 
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                       int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
                       size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  (void)workspace;
-  (void)workspace_bytes;
   MOE_CHECK(check_gemm_dims(H, I));
-  return gemm_common(h, offsets, E_l, R_pad, I, H, 0, w2, y, stream, "moe_grouped_gemm2");
+  return gemm_common(h, offsets, E_l, R_pad, I, H, 0, w2, y, workspace, workspace_bytes, stream,
+                     "moe_grouped_gemm2");
+}
+
+int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  if (R_pad < 0 || R_pad >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "R_pad must be in [0, 2^31)");
+  if (N_out <= 0 || N_out % 64)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "N_out must be a positive multiple of 64 (N_out=%d)", N_out);
+  *bytes = moe::gemm_split_ws_bytes(R_pad, gated ? 2 * N_out : N_out);
+  return MOE_OK;
 }
 
 int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
@@ -333,6 +358,8 @@ struct RoutedWs {
   int32_t* offsets;
   uint16_t* x_perm;  // gathered rows, later reused for the GEMM2 output
   uint16_t* h;
+  void* split;       // split-reduction scratch of both GEMMs
+  size_t split_bytes;
   int64_t rows;
 };
 
@@ -345,6 +372,8 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   b.offsets = c.take<int32_t>(E_l + 1);
   b.x_perm = c.take<uint16_t>(b.rows * H);
   b.h = c.take<uint16_t>(b.rows * I);
+  b.split_bytes = routed_split_bytes(b.rows, H, I);
+  b.split = b.split_bytes ? c.take<char>(b.split_bytes) : nullptr;
   return b;
 }
 
@@ -364,10 +393,12 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
   if (e != hipSuccess) return hip_fail(e, "permute");
   e = moe::launch_gather_rows(x, map, T, k, H, b.x_perm, s);
   if (e != hipSuccess) return hip_fail(e, "gather");
-  moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h};
+  moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
+                   b.split, b.split_bytes};
   e = moe::launch_grouped_gemm(g1, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm1");
-  moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y};
+  moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
+                   b.split_bytes};
   e = moe::launch_grouped_gemm(g2, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm2");
   return MOE_OK;

@@ -60,12 +60,23 @@
 // stage's weight loads: vmcnt retires in issue order, so a wait for them
 // never waits for younger weight stages.
 //
+// Split reduction (tiles for short segments, i.e. decode batches): when the
+// tiles are too few to fill the grid, each tile's k-range is cut into S
+// pieces on weight-stage boundaries and every (tile, piece) is a work unit.
+// S is chosen on the device from the real tile count (a cost model: rounds
+// of the persistent grid times the k-steps of a unit plus a fixed fill and
+// drain cost), up to the number of fp32 partial slices the workspace holds.
+// Pieces write their fp32 sums to slice s of the workspace and
+// split_reduce_kernel adds the S slices in order (deterministic, no atomics)
+// and applies the activation.
+//
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
 // computes gate and up blocks with the same lane layout, so the epilogue
 // forms silu(g) * u in registers and writes BN/2 columns of h.
 #include "moe_common.h"
 
+#include <algorithm>
 #include <utility>
 
 namespace moe {
@@ -94,6 +105,10 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // Descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-family
 // parts: 32-bit data format, out-of-range offsets read as zero.
 constexpr int kBufferFlags = 0x00020000;
+
+// split-reduction workspace: header (the chosen piece count), then slices
+constexpr int64_t kSplitHeader = 256;
+constexpr int64_t kMaxSplit = 8;
 
 // Swizzle of the eight 16-byte chunks of a 128-byte tile row: chunk c of row
 // r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), so 16 consecutive rows
@@ -178,7 +193,12 @@ struct TileCfg {
   // skip row fragments past the segment (one wave row only: otherwise the
   // waves of the lower rows would idle while the others work)
   static constexpr bool SKIP = (WM == 1 && FM > 1);
+  // one wave row: the tiles for short segments, which may split the k-range
+  static constexpr bool SPLIT = (WM == 1);
   static constexpr int SUBSTEPS = BK / 16;
+  // two stages: the next k-step's loads all go out with the first sub-step,
+  // since they must land by the end of this one
+  static constexpr bool EARLY = (STAGES == 2);
   static constexpr int OUT_N = GATED ? BN / 2 : BN;
   // one load instruction: 8 rows x 128 bytes
   static constexpr int A_LD = BM / 8 / NWAVES;   // activation loads per wave per k-step
@@ -286,7 +306,8 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W,
     const uint8_t* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
-    int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles) {
+    int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
+    int s_cap, int* __restrict__ split_out) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
@@ -350,8 +371,23 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int slot = (G % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                                 : static_cast<int>(blockIdx.x);
   const int N_total = Cfg::GATED ? 2 * N_out : N_out;
-  const int nk = K / BK;                  // k-steps
-  const int nq = (nk + BKS - 1) / BKS;    // weight stages
+  const int nk_all = K / BK;                  // k-steps
+  const int nq_all = (nk_all + BKS - 1) / BKS;  // weight stages
+  // pieces per tile: the S <= s_cap (and at least 4 k-steps a piece) that
+  // minimises rounds * (k-steps per piece + fixed cost); 1 without partials
+  int S = 1;
+  if (Cfg::SPLIT && partials != nullptr && total_tiles > 0) {
+    constexpr int kFixed = 8;  // fill, drain and epilogue of a unit, in k-steps
+    const int s_max = min(min(s_cap, nq_all), max(1, nk_all / 4));
+    long best = -1;
+    for (int c = 1; c <= s_max; ++c) {
+      const long rounds = (static_cast<long>(total_tiles) * c + G - 1) / G;
+      const long cost = rounds * ((nk_all + c - 1) / c + kFixed);
+      if (best < 0 || cost < best) { best = cost; S = c; }
+    }
+  }
+  if (split_out != nullptr && blockIdx.x == 0 && tid == 0) split_out[tid] = S;
+  const int total_units = total_tiles * S;
 
   // Load j of this wave fills tile rows [8 rb, 8 rb + 8) (rb = j * NWAVES +
   // wave); lane L writes the 16 bytes at LDS row 8 rb + L / 8, position L % 8,
@@ -360,7 +396,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int ld_sub = lane >> 3;
   const int ld_pos = lane & 7;
 
-  for (int tile = slot; tile < total_tiles; tile += G) {
+  for (int unit = slot; unit < total_units; unit += G) {
+    const int tile = unit / S;
+    const int piece = unit - tile * S;
+    // this piece's weight stages [q0, q0 + nq) and k-steps [kt0, kt0 + nk)
+    const int q0 = piece * nq_all / S;
+    const int nq = (piece + 1) * nq_all / S - q0;
+    const int kt0 = q0 * BKS;
+    const int nk = min(nk_all - kt0, nq * BKS);
     // grouped order: GM m-tiles share each n-tile column
     const int group = Cfg::GM * n_tiles;
     const int gid = tile / group;
@@ -439,7 +482,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) sc_nxt[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p, q * 8);
+          for (int p = 0; p < 4; ++p)
+            sc_nxt[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p, (q0 + q) * 8);
       }
     };
     auto rotate_scales = [&]() {
@@ -463,14 +507,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     auto gload_a = [&](uint16_t* st, int kt, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
-        if (j % SUB == part)
-          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], kt * BK * 2);
+        if (Cfg::EARLY ? part == 0 : j % SUB == part)
+          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + kt) * BK * 2);
     };
     auto gload_b = [&](uint16_t* wst, int q, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::B_LD; ++j)
-        if ((j + Cfg::A_LD) % SUB == part)
-          lds_dma16(b_rsrc, wst + (j * Cfg::NWAVES + wave_u) * 512, b_off[j], q * 128);
+        if (Cfg::EARLY ? part == 0 : (j + Cfg::A_LD) % SUB == part)
+          lds_dma16(b_rsrc, wst + (j * Cfg::NWAVES + wave_u) * 512, b_off[j], (q0 + q) * 128);
     };
 
     // Operand fragments of sub-step ks of the k-step at position p of its
@@ -610,9 +654,34 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // it (each wave refills only the rows it loads itself).
     wait_vmem<0>();
 
-    const int frag_row = lane & 31;
-    const int frag_half = lane >> 5;
     // epilogue: lane holds column (lane & 31) and rows 8*(i/4) + 4*(lane/32) + i%4
+    // (from an opaque lane id: hoisted out of the tile loop, the 16 * FM row
+    // indices would stay live across it)
+    const int eln = opaque(lane);
+    const int frag_row = eln & 31;
+    const int frag_half = eln >> 5;
+    if (Cfg::SPLIT && S > 1) {
+      // fp32 sums of this piece into slice `piece` (weight-row columns: gate
+      // at n, up at N_out + n)
+      float* P = partials + (static_cast<int64_t>(piece) * R_pad + row0) * N_total;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
+          if (r >= rows) continue;
+          float* prow = P + static_cast<int64_t>(r) * N_total;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int v = b_row0<Cfg>(wn, fn) + frag_row;
+            const int col = Cfg::GATED ? (v < BN / 2 ? n0 + v : n0 + v - BN / 2) : n0 + v;
+            if (col < N_out) prow[wrow_of(v)] = acc[fm][fn][i];
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
@@ -642,6 +711,46 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   }
 }
 
+// C[r, n] from the S fp32 slices: y = sum_s P[s, r, n], or for GEMM1
+// h = silu(sum_s P[s, r, n]) * sum_s P[s, r, I + n]; the slices are added in
+// order s = 0, 1, ... (the same result on every run).  Rows at or past the
+// local route count are not written.  One thread per 4 output columns.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials,
+                                                           const int* __restrict__ split,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int E_l, int64_t R_pad, int N_out,
+                                                           int gated, uint16_t* __restrict__ C) {
+  const int S = split[0];
+  if (S <= 1) return;
+  const int64_t r = blockIdx.y;
+  if (r >= offsets[E_l]) return;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= N_out) return;
+  const int N_total = gated ? 2 * N_out : N_out;
+  const int64_t slice = R_pad * N_total;
+  const float* p = partials + r * N_total + n;
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = gated ? *reinterpret_cast<const float4*>(p + N_out) : float4{};
+  for (int s = 1; s < S; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(p + s * slice);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    if (gated) {
+      const float4 u = *reinterpret_cast<const float4*>(p + s * slice + N_out);
+      b.x += u.x; b.y += u.y; b.z += u.z; b.w += u.w;
+    }
+  }
+  if (gated) {
+    a.x = a.x / (1.0f + __expf(-a.x)) * b.x;
+    a.y = a.y / (1.0f + __expf(-a.y)) * b.y;
+    a.z = a.z / (1.0f + __expf(-a.z)) * b.z;
+    a.w = a.w / (1.0f + __expf(-a.w)) * b.w;
+  }
+  uint2 o;
+  o.x = pack_bf16x2(a.x, a.y);
+  o.y = pack_bf16x2(a.z, a.w);
+  *reinterpret_cast<uint2*>(C + r * N_out + n) = o;
+}
+
 template <class Cfg>
 hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   static int occupancy = 0;
@@ -659,10 +768,27 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (grid > max_tiles) grid = max_tiles;
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
+  // split pieces: as many fp32 slices as the workspace holds (after a
+  // 256-byte header that receives the chosen count), at most 8
+  const int64_t N_total = g.gated ? 2 * int64_t(g.N_out) : g.N_out;
+  const int64_t slice_bytes = g.R_pad * N_total * int64_t(sizeof(float));
+  int s_cap = 1;
+  if (Cfg::SPLIT && g.split_ws != nullptr && slice_bytes > 0 && g.split_ws_bytes > kSplitHeader)
+    s_cap = static_cast<int>(std::min<int64_t>(kMaxSplit, (g.split_ws_bytes - kSplitHeader) / slice_bytes));
+  // (the reduce grid has one block row per permuted row: at most 65535)
+  const bool split = s_cap >= 2 && g.N_out % 4 == 0 && g.R_pad <= 65535;
+  int* hdr = split ? static_cast<int*>(g.split_ws) : nullptr;
+  float* partials =
+      split ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kSplitHeader) : nullptr;
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
                      dim3(Cfg::kThreads), 0, s,
                      static_cast<const uint16_t*>(g.a), g.w, g.w_scales, g.offsets, g.E_l, g.K,
-                     g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles);
+                     g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));
+  hipLaunchKernelGGL(split_reduce_kernel, rgrid, dim3(256), 0, s, partials, hdr, g.offsets, g.E_l,
+                     g.R_pad, g.N_out, g.gated, static_cast<uint16_t*>(g.c));
   return hipGetLastError();
 }
 
@@ -670,6 +796,8 @@ template <bool WQ>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
   //                          BM   BN  WM WN ST  gated      GM
+  using Huge  = TileCfg<256, 256, 2, 2, 2, false, WQ>;
+  using HugeG = TileCfg<256, 256, 2, 2, 2, true, WQ>;
   using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ>;
   using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ>;
   using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ>;
@@ -691,11 +819,21 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
   if (g.gated) {
+#ifdef MOE_GEMM1_HUGE
+    if constexpr (!WQ) {
+      if (mean_rows >= 512) return launch_cfg<typename C::HugeG>(g, max_rows, s);
+    }
+#endif
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
     if (mean_rows >= 16) return launch_cfg<typename C::WideG>(g, max_rows, s);
     return launch_cfg<typename C::ThinG>(g, max_rows, s);
   }
+#ifdef MOE_GEMM2_HUGE
+  if constexpr (!WQ) {
+    if (mean_rows >= 512) return launch_cfg<typename C::Huge>(g, max_rows, s);
+  }
+#endif
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
   if (mean_rows >= 16) return launch_cfg<typename C::Wide>(g, max_rows, s);
@@ -703,6 +841,14 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
+  constexpr int64_t kBudget = int64_t(64) << 20;
+  if (R_pad <= 0 || R_pad > 65535 || N_total <= 0) return 0;
+  const int64_t slice = R_pad * N_total * int64_t(sizeof(float));
+  const int64_t n = std::min<int64_t>(kMaxSplit, kBudget / slice);
+  return n < 2 ? 0 : static_cast<size_t>(kSplitHeader + n * slice);
+}
 
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {

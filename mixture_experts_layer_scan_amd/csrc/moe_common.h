@@ -88,7 +88,15 @@ struct GemmArgs {
   int gated;              // 1: GEMM1 with silu(gate) * up, N_total = 2 * N_out
   int64_t R_pad;
   void* c;                // bf16 [R_pad, N_out]
+  // optional scratch for split reductions (256-byte aligned; NULL: no split)
+  void* split_ws = nullptr;
+  size_t split_ws_bytes = 0;
 };
+
+// Scratch bytes with which a grouped GEMM of R_pad rows may split its
+// reduction into the most pieces it uses (0 when it never splits: more than
+// 65535 rows, or a budget of 64 MiB exceeded by two slices).
+size_t gemm_split_ws_bytes(int64_t R_pad, int N_total);
 
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score_fn,
                              int renormalize, float rsf, int32_t* ids, float* w,

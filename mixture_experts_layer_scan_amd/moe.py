@@ -39,6 +39,13 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _hold(t: Optional[torch.Tensor], stream) -> None:
+    """Keep a scratch tensor freed on return alive for work queued on `stream`
+    (a caller's stream other than the current one)."""
+    if t is not None and stream is not None:
+        t.record_stream(stream)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
@@ -170,10 +177,29 @@ def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
     return {"map": map, "offsets": offsets, "inv": inv, "x_perm": x_perm, "R_pad": R_pad}
 
 
+def moe_grouped_gemm_workspace_size(R_pad: int, N_out: int, gated: bool) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_grouped_gemm_workspace_size(R_pad, N_out, int(bool(gated)), ctypes.byref(n)),
+           "moe_grouped_gemm_workspace_size")
+    return int(n.value)
+
+
+def _gemm_workspace(R_pad: int, N_out: int, gated: bool, split: bool, dev, stream):
+    """(pointer, bytes, tensor) of a fresh split-reduction workspace, or (None, 0, None)."""
+    n = moe_grouped_gemm_workspace_size(R_pad, N_out, gated) if split else 0
+    if n == 0:
+        return None, 0, None
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    _hold(buf, stream)
+    return buf.data_ptr(), n, buf
+
+
 def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weights, I: int,
                           h: Optional[torch.Tensor] = None, activation: int = ACT_SILU,
-                          stream=None) -> torch.Tensor:
-    """h[r] = silu(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I]."""
+                          stream=None, split: bool = True) -> torch.Tensor:
+    """h[r] = silu(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I].
+
+    split: pass the workspace that lets few-row calls split the reduction."""
     _need(a_perm, "a_perm", torch.bfloat16)
     R_pad, H = a_perm.shape
     dev = a_perm.device
@@ -183,14 +209,16 @@ def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weigh
     if h is None:
         h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream)
     _check(lib().moe_grouped_gemm1_act(a_perm.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I,
-                                       w1.ref(), activation, h.data_ptr(), None, 0,
+                                       w1.ref(), activation, h.data_ptr(), ws, ws_bytes,
                                        _stream(stream)), "moe_grouped_gemm1_act")
     return h
 
 
 def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: int,
-                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                      y: Optional[torch.Tensor] = None, stream=None,
+                      split: bool = True) -> torch.Tensor:
     """y[r] = h[r] W2[e]^T -> bf16 [R_pad, H] (unweighted gemm2_permuted)."""
     _need(h, "h", torch.bfloat16)
     R_pad, I = h.shape
@@ -201,8 +229,9 @@ def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: in
     if y is None:
         y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, (R_pad, H), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream)
     _check(lib().moe_grouped_gemm2(h.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
-                                   y.data_ptr(), None, 0, _stream(stream)), "moe_grouped_gemm2")
+                                   y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2")
     return y
 
 
@@ -239,9 +268,10 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor, map
     return out
 
 
-def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor], stream=None) -> torch.Tensor:
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        _hold(workspace, stream)
     _need(workspace, "workspace", torch.uint8, device=dev)
     if workspace.numel() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
@@ -276,7 +306,7 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
     if expert_map is not None:
         _need(expert_map, "expert_map", torch.int32, (E,), dev)
     nbytes = moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) if T > 0 else 0
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts_unfinalized(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), R_pad, gemm2_permuted.data_ptr(),
@@ -314,7 +344,7 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
     if T > 0:
         nbytes = (moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) +
                   moe_shared_workspace_size(T, H, shared_I))
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), shared_I, _ptr(ws1), _ptr(ws2),

@@ -135,3 +135,20 @@ def test_fused_errors(L):
     assert call(w1=_w(7, P, P)) == UNSUPPORTED
     assert call(El=4) == INVALID  # no map, E_l != E
     assert call(T=0) == OK
+
+
+def test_grouped_gemm_workspace_size():
+    L = _lib.lib()
+    n = ctypes.c_size_t(0)
+    # decode sizes: fp32 slices of R_pad x N_total, up to 8 within 64 MiB, after a header
+    assert L.moe_grouped_gemm_workspace_size(128, 2048, 1, ctypes.byref(n)) == 0
+    assert n.value == 256 + 8 * 128 * 4096 * 4
+    assert L.moe_grouped_gemm_workspace_size(512, 7168, 0, ctypes.byref(n)) == 0
+    assert n.value == 256 + 4 * 512 * 7168 * 4
+    # prefill sizes never split
+    assert L.moe_grouped_gemm_workspace_size(16384, 2048, 1, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert L.moe_grouped_gemm_workspace_size(70000, 64, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert L.moe_grouped_gemm_workspace_size(128, 100, 0, ctypes.byref(n)) == INVALID
+    assert L.moe_grouped_gemm_workspace_size(128, 64, 0, None) == INVALID

@@ -39,6 +39,10 @@ GEMM_CASES = [
     ("mid_tiles", [300, 1, 420], 256, 448),
     ("big_tiles", [700, 613], 512, 384),
     ("one_expert_many_rows", [1100], 256, 256),
+    # few rows and a long reduction: the k-range splits into pieces (fp32
+    # partial slices in the workspace, then a fixed-order sum)
+    ("split_decode", [1, 0, 2, 1, 0, 3], 1024, 512),
+    ("split_wide", [20, 30, 0, 16], 1024, 512),
 ]
 
 
@@ -104,6 +108,24 @@ def test_grouped_gemms_mxfp4_weights(case):
     assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
     assert np.all(host_bf16_bits(h)[R_l:] == NAN_BITS)
     assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
+
+
+@pytest.mark.parametrize("case", [c for c in GEMM_CASES if c[0].startswith("split")],
+                         ids=lambda c: c[0])
+def test_split_reduction_matches_unsplit(case):
+    """The split path (pieces summed in order) and the unsplit path agree to
+    rounding, and the split path gives the same bits on every run."""
+    name, counts, H, I = case
+    E_l, offsets, R_l, R_pad, a, w1, w2 = _setup(counts, H, I, seed=sum(counts) + 3)
+    assert moe.moe_grouped_gemm_workspace_size(R_pad, I, True) > 0
+    ad, od, W1 = dev_bf16(a), dev(offsets), moe.Weights(dev_bf16(w1))
+    h_split = [host_bf16_bits(moe.moe_grouped_gemm1_act(ad, od, W1, I))[:R_l] for _ in range(2)]
+    h_plain = moe.moe_grouped_gemm1_act(ad, od, W1, I, split=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(h_split[0], h_split[1])
+    ref = oracle.hidden_rows(a[:R_l], oracle.Weights(w1), segments_of(offsets, R_l), I)
+    assert rel_fro(synth.bf16_bits_to_f32(h_split[0]).astype(np.float64), ref) < TOL
+    assert rel_fro(host_f64(h_plain)[:R_l], ref) < TOL
 
 
 def test_gemm_deterministic():
