@@ -279,10 +279,11 @@ def main():
     step_counts = [draw_counts[i % len(dev_draws)] for i in range(args.steps)]
 
     flops_step = []
-    g1_flops = g1_bytes = g1_ms = 0.0
+    g1_flops = g1_bytes = g1_ms = g2_bytes = 0.0
     for i, c in enumerate(step_counts):
         f1, b1 = gemm_work(cfg, c, 1)
-        f2, _ = gemm_work(cfg, c, 2)
+        f2, b2 = gemm_work(cfg, c, 2)
+        g2_bytes += b2
         flops_step.append(f1 + f2 + 6.0 * T * H * cfg.shared_I)
         g1_flops += f1
         g1_bytes += b1
@@ -307,7 +308,8 @@ def main():
     n_launch = len(step_counts)
     roof.update({"traffic": measured_traffic(label), "kernel": "grouped_gemm1_act",
                  "algorithmic_flop_per_launch": g1_flops / n_launch,
-                 "algorithmic_bytes_per_launch": g1_bytes / n_launch})
+                 "algorithmic_bytes_per_launch": g1_bytes / n_launch,
+                 "gemm2_algorithmic_bytes_per_launch": g2_bytes / n_launch})
 
     counts0 = draw_counts[0]
     result = {

@@ -108,7 +108,7 @@ constexpr int kBufferFlags = 0x00020000;
 
 // split-reduction workspace: header (the chosen piece count), then slices
 constexpr int64_t kSplitHeader = 256;
-constexpr int64_t kMaxSplit = 8;
+constexpr int64_t kMaxSplit = 16;
 
 // Swizzle of the eight 16-byte chunks of a 128-byte tile row: chunk c of row
 // r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), so 16 consecutive rows
@@ -769,7 +769,7 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (grid >= 8) grid -= grid % 8;
   if (grid < 1) grid = 1;
   // split pieces: as many fp32 slices as the workspace holds (after a
-  // 256-byte header that receives the chosen count), at most 8
+  // 256-byte header that receives the chosen count), at most kMaxSplit
   const int64_t N_total = g.gated ? 2 * int64_t(g.N_out) : g.N_out;
   const int64_t slice_bytes = g.R_pad * N_total * int64_t(sizeof(float));
   int s_cap = 1;
@@ -796,8 +796,6 @@ template <bool WQ>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
   //                          BM   BN  WM WN ST  gated      GM
-  using Huge  = TileCfg<256, 256, 2, 2, 2, false, WQ>;
-  using HugeG = TileCfg<256, 256, 2, 2, 2, true, WQ>;
   using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ>;
   using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ>;
   using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ>;
@@ -819,21 +817,11 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
   if (g.gated) {
-#ifdef MOE_GEMM1_HUGE
-    if constexpr (!WQ) {
-      if (mean_rows >= 512) return launch_cfg<typename C::HugeG>(g, max_rows, s);
-    }
-#endif
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
     if (mean_rows >= 16) return launch_cfg<typename C::WideG>(g, max_rows, s);
     return launch_cfg<typename C::ThinG>(g, max_rows, s);
   }
-#ifdef MOE_GEMM2_HUGE
-  if constexpr (!WQ) {
-    if (mean_rows >= 512) return launch_cfg<typename C::Huge>(g, max_rows, s);
-  }
-#endif
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
   if (mean_rows >= 16) return launch_cfg<typename C::Wide>(g, max_rows, s);

@@ -140,9 +140,9 @@ def test_fused_errors(L):
 def test_grouped_gemm_workspace_size():
     L = _lib.lib()
     n = ctypes.c_size_t(0)
-    # decode sizes: fp32 slices of R_pad x N_total, up to 8 within 64 MiB, after a header
+    # decode sizes: fp32 slices of R_pad x N_total, up to 16 within 64 MiB, after a header
     assert L.moe_grouped_gemm_workspace_size(128, 2048, 1, ctypes.byref(n)) == 0
-    assert n.value == 256 + 8 * 128 * 4096 * 4
+    assert n.value == 256 + 16 * 128 * 4096 * 4
     assert L.moe_grouped_gemm_workspace_size(512, 7168, 0, ctypes.byref(n)) == 0
     assert n.value == 256 + 4 * 512 * 7168 * 4
     # prefill sizes never split
