@@ -15,7 +15,7 @@ bf16 weights.  The other workloads:
                                      decode batch (--tokens 1, 8 or 64), deferred
                                      form followed by the separate finalize; the
                                      steps cycle through 16 routing draws and a
-                                     512 MiB write evicts L2 and the MALL before
+                                     512 MiB read evicts L2 and the MALL before
                                      each step (outside the timed events)
 
 Prints one JSON line: tokens/s (value), algorithmic TFLOP/s, the roofline of
@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--workload", default="mixtral8x7b_prefill_4096tok")
     p.add_argument("--tokens", type=int, default=64,
                    help="decode batch of the expert-parallel decode workload (1, 8 or 64)")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the layer as a captured HIP graph (one per input batch); "
+                        "the stage breakdown is then not available")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -209,7 +212,17 @@ def main():
         off_s = torch.tensor([0, T], dtype=torch.int32, device=dev)
         hs = torch.empty((T, cfg.shared_I), dtype=torch.bfloat16, device=dev)
         shared = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if decode else None
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if decode else None
+    flush_sum = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict_caches():
+        # read (not write) 512 MiB: evicts L2 and the MALL without leaving
+        # dirty lines whose write-back would compete with the next step
+        torch.sum(flush, dim=0, out=flush_sum)
+    # split-reduction scratch of the two GEMMs (used one after the other)
+    ws_bytes = max(moe.moe_grouped_gemm_workspace_size(R_pad, I, True),
+                   moe.moe_grouped_gemm_workspace_size(R_pad, H, False))
+    split_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
     stages = ["route", "permute", "gemm1", "gemm2", "shared", "finalize"]
@@ -220,31 +233,33 @@ def main():
         moe.moe_permute(ids, E, El, emap_d, xd, R_pad, pmap, offsets, None, x_perm,
                         want_inv=False, stream=stream)
 
-    def step(i, ev=None):
-        d = i % len(dev_draws)
+    def layer(d, st, mark=lambda j: None):
+        """The layer on input batch d, enqueued on stream st; mark(j) records
+        stage boundaries."""
         xd, ld = dev_draws[d]
-        if flush is not None:
-            flush.fill_(i & 0xFF)
-
-        def mark(j):
-            if ev is not None:
-                ev[j].record(stream)
         mark(0)
-        moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, stream)
+        moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, st)
         mark(1)
         moe.moe_permute(ids, E, El, emap_d, xd, R_pad, pmap, offsets, None, x_perm,
-                        want_inv=False, stream=stream)
+                        want_inv=False, stream=st)
         mark(2)
-        moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=stream)
+        moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
+                                  workspace=split_ws)
         mark(3)
-        moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=stream)
+        moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False, workspace=split_ws)
         mark(4)
         if cfg.shared_I:
-            moe.moe_grouped_gemm1_act(xd, off_s, WS1, cfg.shared_I, hs, stream=stream)
-            moe.moe_grouped_gemm2(hs, off_s, WS2, H, shared, stream=stream)
+            moe.moe_grouped_gemm1_act(xd, off_s, WS1, cfg.shared_I, hs, stream=st, split=False)
+            moe.moe_grouped_gemm2(hs, off_s, WS2, H, shared, stream=st, split=False)
         mark(5)
-        moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=stream)
+        moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=st)
         mark(6)
+
+    def step(i, ev=None):
+        if flush is not None:
+            evict_caches()
+        mark = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        layer(i % len(dev_draws), stream, mark)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -257,19 +272,41 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    graphs = []
+    if args.graph:
+        # one graph per input batch; the cache eviction stays outside the graph
+        for d in range(len(dev_draws)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer(d, torch.cuda.current_stream())
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        if graphs:
+            if flush is not None:
+                evict_caches()
+            events[i][0].record()
+            graphs[i % len(graphs)].replay()
+            events[i][6].record()
+        else:
+            step(i, events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per_step = [[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
-                for i in range(args.steps)]
-    stage_ms = {s: float(np.mean([p[j] for p in per_step])) for j, s in enumerate(stages)}
-    if not cfg.shared_I:
-        del stage_ms["shared"]
+    if graphs:
+        per_step = [[0.0] * 5 + [events[i][0].elapsed_time(events[i][6])] for i in range(args.steps)]
+        stage_ms = {"layer_graph": float(np.mean([p[5] for p in per_step]))}
+    else:
+        per_step = [[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
+                    for i in range(args.steps)]
+        stage_ms = {s: float(np.mean([p[j] for p in per_step])) for j, s in enumerate(stages)}
+        if not cfg.shared_I:
+            del stage_ms["shared"]
 
     # routed rows per local expert of every draw (untimed re-run of route + permute)
     draw_counts = []
@@ -294,7 +331,7 @@ def main():
     else:
         ms_per_step = elapsed / args.steps * 1e3
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
-    g1_s = g1_ms * 1e-3
+    g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
     t_mfma = g1_flops / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
@@ -306,6 +343,9 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     n_launch = len(step_counts)
+    if graphs:
+        roof.update({"achieved": None, "frac": None,
+                     "note": "no per-kernel timing under graph replay; run without --graph"})
     roof.update({"traffic": measured_traffic(label), "kernel": "grouped_gemm1_act",
                  "algorithmic_flop_per_launch": g1_flops / n_launch,
                  "algorithmic_bytes_per_launch": g1_bytes / n_launch,
@@ -333,8 +373,9 @@ def main():
                    "routing": ("softmax" if cfg.score == 0 else "sigmoid") +
                               (f" top-{k} renormalized") + (f", rsf {cfg.rsf}" if cfg.rsf != 1 else "") +
                               (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
-                   "form": "deferred + separate finalize, L2/MALL evicted before each step, "
-                           f"{len(draws)} routing draws" if decode else "finalized"},
+                   "form": ("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
+                            f"{len(draws)} routing draws" if decode else "finalized")
+                           + (", replayed as a captured HIP graph" if graphs else "")},
         "tflops": tflops,
         "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
         "stages_ms": stage_ms,

@@ -811,7 +811,7 @@ struct Configs {
 //   >= 128  MFMA-bound: square-ish tiles, weight slices shared by GM m-tiles
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
-//   < 16    decode: short tiles.
+//   < 16    decode: short tiles with split reductions.
 template <bool WQ>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ>;

@@ -184,8 +184,13 @@ def moe_grouped_gemm_workspace_size(R_pad: int, N_out: int, gated: bool) -> int:
     return int(n.value)
 
 
-def _gemm_workspace(R_pad: int, N_out: int, gated: bool, split: bool, dev, stream):
-    """(pointer, bytes, tensor) of a fresh split-reduction workspace, or (None, 0, None)."""
+def _gemm_workspace(R_pad: int, N_out: int, gated: bool, split: bool, dev, stream,
+                    workspace: Optional[torch.Tensor] = None):
+    """(pointer, bytes, tensor) of the split-reduction workspace: the caller's,
+    a fresh one, or (None, 0, None)."""
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, device=dev)
+        return workspace.data_ptr(), workspace.numel(), workspace
     n = moe_grouped_gemm_workspace_size(R_pad, N_out, gated) if split else 0
     if n == 0:
         return None, 0, None
@@ -196,10 +201,12 @@ def _gemm_workspace(R_pad: int, N_out: int, gated: bool, split: bool, dev, strea
 
 def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weights, I: int,
                           h: Optional[torch.Tensor] = None, activation: int = ACT_SILU,
-                          stream=None, split: bool = True) -> torch.Tensor:
+                          stream=None, split: bool = True,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h[r] = silu(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I].
 
-    split: pass the workspace that lets few-row calls split the reduction."""
+    workspace: uint8 scratch (moe_grouped_gemm_workspace_size bytes) that lets
+    few-row calls split the reduction; without one, split=True allocates it."""
     _need(a_perm, "a_perm", torch.bfloat16)
     R_pad, H = a_perm.shape
     dev = a_perm.device
@@ -209,7 +216,7 @@ def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weigh
     if h is None:
         h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", torch.bfloat16, (R_pad, I), dev)
-    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
     _check(lib().moe_grouped_gemm1_act(a_perm.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I,
                                        w1.ref(), activation, h.data_ptr(), ws, ws_bytes,
                                        _stream(stream)), "moe_grouped_gemm1_act")
@@ -218,7 +225,7 @@ def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weigh
 
 def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: int,
                       y: Optional[torch.Tensor] = None, stream=None,
-                      split: bool = True) -> torch.Tensor:
+                      split: bool = True, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[r] = h[r] W2[e]^T -> bf16 [R_pad, H] (unweighted gemm2_permuted)."""
     _need(h, "h", torch.bfloat16)
     R_pad, I = h.shape
@@ -229,7 +236,7 @@ def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: in
     if y is None:
         y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, (R_pad, H), dev)
-    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream, workspace)
     _check(lib().moe_grouped_gemm2(h.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
                                    y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2")
     return y

@@ -1,8 +1,8 @@
 """GPU parity of the grouped GEMMs and of finalize against the oracle, each on
 its own, at sizes that span several tiles with ragged tails, for every tile
 shape the library picks (the shape follows the mean rows per local expert:
->= 512, >= 128, >= 16, below), including segments that end inside each of the
-32-row fragments of the 128-row weight-streaming tile and segments longer
+>= 512, >= 128, >= 16, below), including segments that end inside each of
+the 32-row fragments of the 128-row weight-streaming tile and segments longer
 than one m-tile.
 
 Bar: relative Frobenius error <= 1e-2 for bf16 outputs against the float64
@@ -43,6 +43,8 @@ GEMM_CASES = [
     # partial slices in the workspace, then a fixed-order sum)
     ("split_decode", [1, 0, 2, 1, 0, 3], 1024, 512),
     ("split_wide", [20, 30, 0, 16], 1024, 512),
+    # decode-like segments of 0-9 rows with a reduction of 10 k-steps
+    ("decode_ragged", [9, 0, 1, 5, 4], 640, 320),
 ]
 
 
