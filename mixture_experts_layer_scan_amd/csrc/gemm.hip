@@ -207,7 +207,10 @@ struct TileCfg {
   // MXFP4: three weight stages, so two stream while one is used (a weight
   // stage lasts four k-steps; with one in flight the stream stalls between)
   static constexpr int B_STAGES = WQ ? 3 : STAGES;
-  static constexpr int SCQ = WQ ? 4 * FN : 0;    // scale-byte loads per wave per weight stage
+  // scale loads per wave per weight stage: one 8-byte load per fragment (rows
+  // of K/32 scale bytes 8-byte aligned); the byte-wise fallback for other K
+  // issues more, which only makes the waits stricter
+  static constexpr int SCQ = WQ ? FN : 0;
   static constexpr int A_ELEMS = BM * 64;        // uint16 per activation stage
   static constexpr int B_ELEMS = BN * 64;        // uint16 per weight stage
   // k-steps per unrolled loop body: every stage object is then compile-time
@@ -287,6 +290,12 @@ __device__ __forceinline__ int b_row0(int wn, int fn) {
 
 __device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(voff), soff, 0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 load_u64(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
 }
 
 // E8M0 scale byte -> the float whose bit pattern is s << 23 (2^(s-127);
@@ -462,37 +471,59 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       b_off[j] = static_cast<uint32_t>(wrow_of(v)) * w_row_bytes + c * 16;
     }
     // MXFP4 scale bytes: lane's weight row per fragment; k-step kt, half h
-    // uses block 2 kt + h, i.e. byte 2 p + h of the 8 of its weight stage
+    // uses block 2 kt + h, i.e. byte 2 p + h of the 8 of its weight stage.
+    // A lane holds the stage's 8 bytes of its row (both halves' blocks) in
+    // two dwords, loaded with one 8-byte load when the rows of K/32 bytes
+    // are 8-byte aligned, else byte by byte (its half's 4 bytes) and packed
+    // when the stage opens.
     const uint32_t s_row = Cfg::WQ ? static_cast<uint32_t>(K) / 32u : 0u;  // scale bytes per row
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(W_scales + static_cast<int64_t>(e) * N_total * s_row), 0,
         static_cast<int>(static_cast<uint32_t>(N_total) * s_row), kBufferFlags);
+    const bool s_wide = (s_row % 8u) == 0;  // uniform
     constexpr int NSF = Cfg::WQ ? FN : 1;
     uint32_t s_off[NSF];
-    uint32_t sc_cur[NSF][4], sc_nxt[NSF][4];
+    u32x2 sc_cur[NSF], sc_nxt[NSF];
+    uint32_t sc_byte[NSF][4];
     if constexpr (Cfg::WQ) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        s_off[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn) + (lane & 31))) * s_row +
-                    (lane >> 5);
+        s_off[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn) + (lane & 31))) * s_row;
     }
-    // the scale bytes of weight stage q (blocks 8q + 2p + h, p = 0..3)
+    // the scale bytes of weight stage q (blocks 8q .. 8q + 7 of the lane's row)
     auto load_scales = [&](int q) {
       if constexpr (Cfg::WQ) {
+        if (s_wide) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+          for (int fn = 0; fn < FN; ++fn) sc_nxt[fn] = load_u64(s_rsrc, s_off[fn], (q0 + q) * 8);
+        } else {
 #pragma unroll
-          for (int p = 0; p < 4; ++p)
-            sc_nxt[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p, (q0 + q) * 8);
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              sc_byte[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p + (lane >> 5), (q0 + q) * 8);
+        }
       }
     };
+    // at a weight-stage boundary (the loads were issued a stage earlier)
     auto rotate_scales = [&]() {
       if constexpr (Cfg::WQ) {
+        const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 5);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) sc_cur[fn][p] = sc_nxt[fn][p];
+        for (int fn = 0; fn < FN; ++fn) {
+          if (s_wide) {
+            sc_cur[fn] = sc_nxt[fn];
+          } else {
+            sc_cur[fn] = u32x2{(sc_byte[fn][0] << sh) | (sc_byte[fn][1] << (16u + sh)),
+                               (sc_byte[fn][2] << sh) | (sc_byte[fn][3] << (16u + sh))};
+          }
+        }
       }
+    };
+    // E8M0 scale of fragment fn for the k-step at position p, this lane's half
+    auto scale_of = [&](int fn, int p, int ln) {
+      const uint32_t word = p < 2 ? sc_cur[fn].x : sc_cur[fn].y;
+      return e8m0_to_f32((word >> (8u * static_cast<uint32_t>(2 * (p & 1) + (ln >> 5)))) & 0xFFu);
     };
 
     f32x16 acc[FM][FN];
@@ -544,7 +575,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
             bq[fn] = *reinterpret_cast<const uint4*>(bs + swz(v, 2 * p + half));
           } else {
             const uint32_t word = ks == 1 ? bq[fn].y : ks == 2 ? bq[fn].z : bq[fn].w;
-            bfr[fn] = expand_fp4x8(word, e8m0_to_f32(sc_cur[fn][p]));
+            bfr[fn] = expand_fp4x8(word, scale_of(fn, p, ln));
           }
         } else {
           bfr[fn] = *reinterpret_cast<const bf16x8*>(bs + swz(v, chunk));
@@ -565,7 +596,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       if constexpr (Cfg::WQ) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          fb[0][fn] = expand_fp4x8(bq[fn].x, e8m0_to_f32(sc_cur[fn][p]));
+          fb[0][fn] = expand_fp4x8(bq[fn].x, scale_of(fn, p, lane));
       }
     };
 
