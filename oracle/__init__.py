@@ -64,6 +64,9 @@ def _load():
         L.oracle_out_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_finalize.restype = None
         L.oracle_finalize.argtypes = [vp, vp, vp, i64, i32, i64, dbl, vp, vp]
+        L.oracle_finalize_add_rmsnorm.restype = None
+        L.oracle_finalize_add_rmsnorm.argtypes = [vp, vp, vp, i64, i32, i64, dbl, vp, vp, vp, dbl,
+                                                  vp, vp]
         L.oracle_moe_tokens.restype = None
         L.oracle_moe_tokens.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dbl, vp, Wp, Wp,
                                         i64, vp, vp, dbl, vp, i64, vp, vp, vp, vp]
@@ -190,6 +193,25 @@ def finalize(y_perm_bf16: np.ndarray, weights: np.ndarray, pmap: np.ndarray, rsf
     out = np.empty((T, H), dtype=np.float64)
     _load().oracle_finalize(_p(y), _p(w), _p(pmap), T, k, H, rsf_fin, _p(shared), _p(out))
     return out
+
+
+def finalize_add_rmsnorm(y_perm_bf16: np.ndarray, weights: np.ndarray, pmap: np.ndarray,
+                         residual_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float,
+                         rsf_fin: float = 1.0, shared_bf16: Optional[np.ndarray] = None):
+    """Fused tail: (residual + finalize, RMSNorm of it times gamma), float64 [T, H] each."""
+    y = _c(y_perm_bf16, np.uint16)
+    w = _c(np.asarray(weights, dtype=np.float64), np.float64)
+    pmap = _c(pmap, np.int32)
+    shared = _c(shared_bf16, np.uint16)
+    res = _c(residual_bf16, np.uint16)
+    gamma = _c(gamma_bf16, np.uint16)
+    T, k = pmap.shape
+    H = y.shape[1]
+    res_out = np.empty((T, H), dtype=np.float64)
+    out = np.empty((T, H), dtype=np.float64)
+    _load().oracle_finalize_add_rmsnorm(_p(y), _p(w), _p(pmap), T, k, H, rsf_fin, _p(shared),
+                                        _p(res), _p(gamma), float(eps), _p(res_out), _p(out))
+    return res_out, out
 
 
 def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights, I: int, k: int,

@@ -247,6 +247,33 @@ void oracle_finalize(const uint16_t* y_perm, const double* w, const int32_t* map
   }
 }
 
+/* ---- Fused tail on one GPU ([OUT] MoEOutput: the consumer of the layer's
+ * open reduction is typically the next layer's RMSNorm, which folds the top-k
+ * reduction, the routed scaling factor and the shared add into itself) -------
+ * For each token t, with m[t] the finalize output above:
+ *   residual_out[t] = residual[t] + m[t]
+ *   out[t, n] = residual_out[t, n] / sqrt(mean_n residual_out[t, n]^2 + eps)
+ *               * gamma[n]
+ * (the RMSNorm of the new residual stream, scaled per column by gamma). */
+void oracle_finalize_add_rmsnorm(const uint16_t* y_perm, const double* w, const int32_t* map,
+                                 int64_t T, int32_t k, int64_t H, double rsf_fin,
+                                 const uint16_t* shared, const uint16_t* residual,
+                                 const uint16_t* gamma, double eps, double* residual_out,
+                                 double* out) {
+  oracle_finalize(y_perm, w, map, T, k, H, rsf_fin, shared, residual_out);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* r = residual_out + t * H;
+    double ss = 0.0;
+    for (int64_t n = 0; n < H; ++n) {
+      r[n] += bf16_val(residual[t * H + n]);
+      ss += r[n] * r[n];
+    }
+    const double inv = 1.0 / sqrt(ss / (double)H + eps);
+    for (int64_t n = 0; n < H; ++n) out[t * H + n] = r[n] * inv * bf16_val(gamma[n]);
+  }
+}
+
 /* ---- The whole layer on selected tokens ([MOD] forward: prepare, apply,
  * finalize; [OUT] MoEOutput for the shared add) -------------------------------
  * For each listed token t: route it, localize each route through the expert
