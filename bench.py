@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="replay the layer as a captured HIP graph (one per input batch); "
                         "the stage breakdown is then not available")
+    p.add_argument("--fused-tail", action="store_true",
+                   help="end the step with the fused tail (finalize + shared add + residual add "
+                        "+ the next layer's RMSNorm) instead of the plain finalize")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -205,6 +208,9 @@ def main():
     h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if args.fused_tail:
+        residual = to_bf16(draws[0][0])  # a residual stream of the x distribution
+        gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
     shared = None
     if cfg.shared_I:
         WS1 = moe.Weights(to_bf16(w["ws1"])[None])
@@ -252,7 +258,11 @@ def main():
             moe.moe_grouped_gemm1_act(xd, off_s, WS1, cfg.shared_I, hs, stream=st, split=False)
             moe.moe_grouped_gemm2(hs, off_s, WS2, H, shared, stream=st, split=False)
         mark(5)
-        moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=st)
+        if args.fused_tail:
+            moe.moe_finalize_add_rmsnorm(y, wts, pmap, residual, gamma, 1e-6, 1.0, shared, out,
+                                         stream=st)
+        else:
+            moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=st)
         mark(6)
 
     def step(i, ev=None):
@@ -305,6 +315,8 @@ def main():
         per_step = [[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
                     for i in range(args.steps)]
         stage_ms = {s: float(np.mean([p[j] for p in per_step])) for j, s in enumerate(stages)}
+        if args.fused_tail:
+            stage_ms["finalize_add_rmsnorm"] = stage_ms.pop("finalize")
         if not cfg.shared_I:
             del stage_ms["shared"]
 
@@ -375,7 +387,8 @@ def main():
                               (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
                    "form": ("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
                             f"{len(draws)} routing draws" if decode else "finalized")
-                           + (", replayed as a captured HIP graph" if graphs else "")},
+                           + (", replayed as a captured HIP graph" if graphs else "")
+                           + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")},
         "tflops": tflops,
         "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
         "stages_ms": stage_ms,

@@ -193,6 +193,28 @@ int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_
                       int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Fused tail on one GPU: finalize, the shared-expert add, the residual add
+ * and the next layer's RMSNorm in one pass (page "moe_output.py", MoEOutput:
+ * the consumer of the open reduction is typically the next layer's RMSNorm).
+ * For every token t, with z the fp32 sum
+ *   z[t, :] = rsf_fin * sum_{j: map>=0} w[t,j] * y_perm[map[t,j], :]
+ *             + shared[t, :] + residual[t, :]
+ *   residual[t, :] = bf16(z[t, :])                                  (in place)
+ *   out[t, :] = bf16(z[t, :] / sqrt(mean(z[t, :]^2) + eps) * gamma[:])
+ * (the norm uses z before the residual's rounding).
+ *   y_perm, weights, weights_dtype, map, T, k, H, rsf_fin, shared: as for
+ *              moe_finalize
+ *   residual   (device) bf16 [T, H] in/out (the residual stream)
+ *   gamma      (device) bf16 [H] the norm's per-column scale
+ *   eps        >= 0
+ *   out        (device) bf16 [T, H] out; must not overlap residual, shared
+ *              or y_perm; shared must not overlap residual
+ * Limits: H a multiple of 8, at most 16384. */
+int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t weights_dtype,
+                             const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
+                             const void* shared, void* residual, const void* gamma, float eps,
+                             void* out, void* stream);
+
 /* Scratch bytes with which a grouped GEMM of R_pad permuted rows and N_out
  * output columns (gated != 0: GEMM1, whose weights have 2 N_out rows) may
  * split its reduction as far as it ever does; 0 when it never splits (large

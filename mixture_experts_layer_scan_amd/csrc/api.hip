@@ -349,6 +349,43 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_finalize");
 }
 
+int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t weights_dtype,
+                             const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
+                             const void* shared, void* residual, const void* gamma, float eps,
+                             void* out, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens must be non-negative (T=%lld)", (long long)T);
+  if (k <= 0 || k > 32) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be in [1, 32] (k=%d)", k);
+  if (H <= 0 || H % 8 || H > moe::kTailMaxH)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8, at most %d (H=%d)",
+                moe::kTailMaxH, H);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (weights_dtype != MOE_DTYPE_F32 && weights_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
+  MOE_CHECK(need_ptr(weights, "expert_weights"));
+  MOE_CHECK(need_ptr(map, "map"));
+  MOE_CHECK(opt_ptr(shared, "shared"));
+  MOE_CHECK(need_ptr(residual, "residual"));
+  MOE_CHECK(need_ptr(gamma, "gamma"));
+  MOE_CHECK(need_ptr(out, "out"));
+  const size_t row_bytes = sizeof(uint16_t) * T * H;
+  if (overlap(out, row_bytes, residual, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap residual");
+  if (shared && overlap(shared, row_bytes, residual, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "shared must not overlap residual (written in place)");
+  if (shared && overlap(shared, row_bytes, out, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap shared");
+  const size_t y_bytes = sizeof(uint16_t) * T * k * H;
+  if (overlap(y_perm, y_bytes, out, row_bytes) || overlap(y_perm, y_bytes, residual, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out and residual must not overlap gemm2_permuted");
+  hipError_t e = moe::launch_finalize_add_rmsnorm(y_perm, weights, weights_dtype == MOE_DTYPE_BF16,
+                                                  map, T, k, H, rsf_fin, shared, residual, gamma,
+                                                  eps, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_finalize_add_rmsnorm");
+}
+
 // Workspace of the routed part of the fused entry points (rows sized for
 // moe_permuted_rows(T, k); the GEMMs never touch rows past the local routes).
 struct RoutedWs {

@@ -71,7 +71,135 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__
   }
 }
 
+// Fused tail (MoEOutput of vLLM's MoE output contract: the next layer's
+// RMSNorm is the consumer that folds the open reduction into itself):
+//
+//   z[t, :] = rsf_fin * sum_j w[t,j] * y[map[t,j], :] + shared[t, :] + residual[t, :]
+//   residual[t, :] = bf16(z[t, :])                            (in place)
+//   out[t, :] = bf16(z[t, :] / sqrt(mean(z[t, :]^2) + eps) * gamma)
+//
+// The norm uses the fp32 z, before the residual's rounding.  One workgroup
+// per token: pass 1 forms z (as finalize does), writes the residual, keeps z
+// in LDS and sums its squares; a block reduction gives 1/rms; pass 2 writes
+// out.  H <= kTailMaxH (z of one token in LDS).
+template <bool W_BF16>
+__global__ __launch_bounds__(256) void finalize_norm_kernel(
+    const uint4* __restrict__ y, const void* __restrict__ wts, const int32_t* __restrict__ map,
+    int64_t T, int k, int H8, float rsf_fin, const uint4* shared, uint4* residual,
+    const uint4* __restrict__ gamma, float eps, uint4* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float s_z[];  // [8 * H8]
+  __shared__ int32_t s_row[32];
+  __shared__ float s_w[32];
+  __shared__ float s_part[16];
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    __syncthreads();  // the previous token's routes and sums are no longer read
+    if (threadIdx.x < k) {
+      s_row[threadIdx.x] = map[t * k + threadIdx.x];
+      s_w[threadIdx.x] = W_BF16
+          ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
+          : static_cast<const float*>(wts)[t * k + threadIdx.x];
+    }
+    __syncthreads();
+    float ss = 0.0f;
+    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int32_t r = s_row[j];
+        if (r < 0) continue;
+        const float wj = s_w[j];
+        const uint4 v = y[static_cast<int64_t>(r) * H8 + c];
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] & 0xFFFFu));
+          acc[2 * i + 1] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] >> 16));
+        }
+      }
+      float z[8];
+      const uint4 rv = residual[t * H8 + c];
+      const uint4 sv = shared ? shared[t * H8 + c] : make_uint4(0, 0, 0, 0);
+      const uint32_t rp[4] = {rv.x, rv.y, rv.z, rv.w};
+      const uint32_t sp[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[2 * i] = rsf_fin * acc[2 * i] + bf16_to_f32(static_cast<uint16_t>(sp[i] & 0xFFFFu)) +
+                   bf16_to_f32(static_cast<uint16_t>(rp[i] & 0xFFFFu));
+        z[2 * i + 1] = rsf_fin * acc[2 * i + 1] + bf16_to_f32(static_cast<uint16_t>(sp[i] >> 16)) +
+                       bf16_to_f32(static_cast<uint16_t>(rp[i] >> 16));
+      }
+      uint4 o;
+      o.x = pack_bf16x2(z[0], z[1]);
+      o.y = pack_bf16x2(z[2], z[3]);
+      o.z = pack_bf16x2(z[4], z[5]);
+      o.w = pack_bf16x2(z[6], z[7]);
+      residual[t * H8 + c] = o;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s_z[c * 8 + i] = z[i];
+        ss += z[i] * z[i];
+      }
+    }
+    // block sum of squares: wave butterflies, then the wave totals in order
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+    if (lane_id() == 0) s_part[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    float total = 0.0f;
+    for (int i = 0; i < nw; ++i) total += s_part[i];
+    const float inv = 1.0f / sqrtf(total / static_cast<float>(8 * H8) + eps);
+    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
+      const uint4 gv = gamma[c];
+      const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w};
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = s_z[c * 8 + 2 * i] * inv * bf16_to_f32(static_cast<uint16_t>(gp[i] & 0xFFFFu));
+        v[2 * i + 1] = s_z[c * 8 + 2 * i + 1] * inv * bf16_to_f32(static_cast<uint16_t>(gp[i] >> 16));
+      }
+      uint4 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      o.z = pack_bf16x2(v[4], v[5]);
+      o.w = pack_bf16x2(v[6], v[7]);
+      out[t * H8 + c] = o;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf16,
+                                       const int32_t* map, int64_t T, int k, int H, float rsf_fin,
+                                       const void* shared, void* residual, const void* gamma,
+                                       float eps, void* out, hipStream_t s) {
+  const int H8 = H / 8;
+  const int threads = H8 >= 256 ? 256 : ((H8 + 63) / 64) * 64;
+  const int64_t blocks = T < 16384 ? T : 16384;
+  const size_t lds = sizeof(float) * static_cast<size_t>(H);
+  static bool attr_set[2] = {false, false};
+  const void* fn = w_is_bf16 ? reinterpret_cast<const void*>(finalize_norm_kernel<true>)
+                             : reinterpret_cast<const void*>(finalize_norm_kernel<false>);
+  if (!attr_set[w_is_bf16 ? 1 : 0]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(sizeof(float) * kTailMaxH));
+    if (e != hipSuccess) return e;
+    attr_set[w_is_bf16 ? 1 : 0] = true;
+  }
+  if (w_is_bf16)
+    hipLaunchKernelGGL(finalize_norm_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, T, k, H8,
+                       rsf_fin, static_cast<const uint4*>(shared), static_cast<uint4*>(residual),
+                       static_cast<const uint4*>(gamma), eps, static_cast<uint4*>(out));
+  else
+    hipLaunchKernelGGL(finalize_norm_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, T, k, H8,
+                       rsf_fin, static_cast<const uint4*>(shared), static_cast<uint4*>(residual),
+                       static_cast<const uint4*>(gamma), eps, static_cast<uint4*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
                            int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,

@@ -110,6 +110,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t 
 hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
                            int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,
                            hipStream_t s);
+constexpr int kTailMaxH = 16384;  // the fused tail keeps one token's fp32 row in LDS
+hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf16,
+                                       const int32_t* map, int64_t T, int k, int H, float rsf_fin,
+                                       const void* shared, void* residual, const void* gamma,
+                                       float eps, void* out, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s);
 
 int device_cu_count();

@@ -275,6 +275,44 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor, map
     return out
 
 
+def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
+                             map: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                             eps: float = 1e-6, rsf_fin: float = 1.0,
+                             shared: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, stream=None):
+    """Fused tail: residual += finalize(...) (in place); out = RMSNorm(residual) * gamma.
+    -> (out bf16 [T, H], residual)."""
+    _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16)
+    if gemm2_permuted.dim() != 2:
+        raise ValueError("gemm2_permuted must be rank-2")
+    H = gemm2_permuted.shape[1]
+    dev = gemm2_permuted.device
+    _need(map, "map", torch.int32, device=dev)
+    if map.dim() != 2:
+        raise ValueError("map must be [T, k]")
+    T, k = map.shape
+    if expert_weights.dtype == torch.float32:
+        wdt = DTYPE_F32
+    elif expert_weights.dtype == torch.bfloat16:
+        wdt = DTYPE_BF16
+    else:
+        raise TypeError("expert_weights must be float32 or bfloat16")
+    _need(expert_weights, "expert_weights", expert_weights.dtype, (T, k), dev)
+    _need(residual, "residual", torch.bfloat16, (T, H), dev)
+    _need(gamma, "gamma", torch.bfloat16, (H,), dev)
+    if shared is not None:
+        _need(shared, "shared", torch.bfloat16, (T, H), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _check(lib().moe_finalize_add_rmsnorm(gemm2_permuted.data_ptr(), expert_weights.data_ptr(), wdt,
+                                          map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
+                                          residual.data_ptr(), gamma.data_ptr(), float(eps),
+                                          out.data_ptr(), _stream(stream)),
+           "moe_finalize_add_rmsnorm")
+    return out, residual
+
+
 def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor], stream=None) -> torch.Tensor:
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)

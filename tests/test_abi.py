@@ -119,6 +119,24 @@ def test_finalize_errors(L):
     assert f(P, P, 1, P, 0, 2, 128, 1.0, None, None, None) == OK  # T = 0
 
 
+def test_finalize_add_rmsnorm_errors(L):
+    f = L.moe_finalize_add_rmsnorm
+    # (y, w, wdt, map, T, k, H, rsf, shared, residual, gamma, eps, out, stream)
+    R, G, O = P * 8, P * 16, P * 24
+    assert f(P, P, 1, P, -1, 2, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, P, 1, P, 16, 0, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, P, 1, P, 16, 2, 130, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, P, 1, P, 16, 2, 16392, 1.0, None, R, G, 1e-6, O, None) == INVALID  # H too large
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, -1.0, O, None) == INVALID  # eps < 0
+    assert f(P, P, 3, P, 16, 2, 128, 1.0, None, R, G, 1e-6, O, None) == UNSUPPORTED
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, None, G, 1e-6, O, None) == INVALID  # no residual
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, None, 1e-6, O, None) == INVALID  # no gamma
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, R, None) == CONFLICT  # out == residual
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, R, R, G, 1e-6, O, None) == CONFLICT  # shared == residual
+    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, P + 256, None) == CONFLICT  # out in y
+    assert f(P, P, 1, P, 0, 2, 128, 1.0, None, None, None, 1e-6, None, None) == OK  # T = 0
+
+
 def test_fused_errors(L):
     u = L.moe_fused_experts_unfinalized
     args = dict(logits=P, x=P, T=16, H=128, I=256, E=8, El=8, k=2, score=0, renorm=1, rsf=1.0,
