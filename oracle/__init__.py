@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 SOFTMAX, SIGMOID = 0, 1
 W_BF16, W_MXFP4 = 0, 1
+ACTIVATIONS = {"silu": 0, "gelu": 1}
 
 
 def build(force: bool = True) -> str:
@@ -59,7 +60,7 @@ def _load():
         L.oracle_permute.restype = ctypes.c_int
         L.oracle_permute.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
         L.oracle_hidden_rows.restype = None
-        L.oracle_hidden_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
+        L.oracle_hidden_rows.argtypes = [vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
         L.oracle_out_rows.restype = None
         L.oracle_out_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_finalize.restype = None
@@ -69,7 +70,7 @@ def _load():
                                                   vp, vp]
         L.oracle_moe_tokens.restype = None
         L.oracle_moe_tokens.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dbl, vp, Wp, Wp,
-                                        i64, vp, vp, dbl, vp, i64, vp, vp, vp, vp]
+                                        i64, vp, vp, dbl, i32, dbl, i32, vp, i64, vp, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         _lib = L
@@ -161,13 +162,17 @@ def permute(ids: np.ndarray, E: int, E_l: int, expert_map: Optional[np.ndarray] 
     return m, offsets, counts[:E_l]
 
 
-def hidden_rows(a_bf16: np.ndarray, w1: Weights, expert_of_row: np.ndarray, I: int) -> np.ndarray:
-    """h[r] = silu(W1g[e_r] a_r) * (W1u[e_r] a_r), float64 [rows, I]."""
+def hidden_rows(a_bf16: np.ndarray, w1: Weights, expert_of_row: np.ndarray, I: int,
+                activation: str = "silu", clamp: float = 0.0) -> np.ndarray:
+    """h[r] = act(W1g[e_r] a_r) * (W1u[e_r] a_r), float64 [rows, I]; act is
+    "silu" or "gelu" (erf form); clamp > 0 limits the gate from above and the
+    up value to [-clamp, clamp] first."""
     a = _c(a_bf16, np.uint16)
     eor = _c(expert_of_row.astype(np.int32), np.int32)
     rows, H = a.shape
     h = np.empty((rows, I), dtype=np.float64)
-    _load().oracle_hidden_rows(_p(a), rows, H, I, w1.ref, _p(eor), _p(h))
+    _load().oracle_hidden_rows(_p(a), rows, H, I, w1.ref, _p(eor), ACTIVATIONS[activation],
+                               float(clamp), _p(h))
     return h
 
 
@@ -218,8 +223,12 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
                score: int, renormalize: bool, rsf: float,
                expert_map: Optional[np.ndarray] = None, shared_I: int = 0,
                ws1: Optional[np.ndarray] = None, ws2: Optional[np.ndarray] = None,
-               rsf_fin: float = 1.0, tokens: Optional[Sequence[int]] = None):
-    """The whole layer for the listed tokens (all when None).
+               rsf_fin: float = 1.0, tokens: Optional[Sequence[int]] = None,
+               activation: str = "silu", clamp: float = 0.0, weight_on_input: bool = False):
+    """The whole layer for the listed tokens (all when None).  activation and
+    clamp as for hidden_rows (every expert, the shared one included);
+    weight_on_input: the routing weight scales the token before its expert
+    MLP instead of the MLP's output (top_k = 1).
 
     Returns dict: out float64 [n, H], y_routes float64 [n, k, H] (unweighted
     per-route expert outputs, zero when not local), ids int32 [n, k],
@@ -240,5 +249,7 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
     ws2 = _c(ws2, np.uint16)
     _load().oracle_moe_tokens(_p(x), H, I, _p(logits), E, k, score, int(bool(renormalize)), rsf,
                               _p(expert_map), w1.ref, w2.ref, shared_I, _p(ws1), _p(ws2),
-                              rsf_fin, _p(tok), n, _p(out), _p(y), _p(ids), _p(w))
+                              rsf_fin, ACTIVATIONS[activation], float(clamp),
+                              int(bool(weight_on_input)), _p(tok), n, _p(out), _p(y), _p(ids),
+                              _p(w))
     return {"out": out, "y_routes": y, "ids": ids, "weights": w, "tokens": tok}

@@ -16,7 +16,7 @@
  *          apply / activation; FusedMoEModularKernel.forward.
  *   [EP]   vLLM "flashinfer_moe_ep.py": _E2M1_LUT, _dequant_fp4_ue8m0_gran32.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - w1 is [E, 2I, H]: rows [0, I) are the gate (SiLU'd), rows [I, 2I) the
  *     up projection; w2 is [E, H, I]; both contiguous along the reduction dim.
  *   - top-k is taken on the fp32 logits, ordered by logit descending, ties to
@@ -32,6 +32,7 @@
 
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1 };
+enum { OR_ACT_SILU = 0, OR_ACT_GELU = 1 };
 
 typedef struct {
   int32_t fmt;            /* OR_W_BF16 or OR_W_MXFP4 */
@@ -171,18 +172,38 @@ int oracle_permute(const int32_t* ids, const int32_t* expert_map, int64_t T, int
 }
 
 /* ---- Experts ([MOD] apply: GEMM1, activation, GEMM2, unweighted; activation:
- * the output is half the width of the input and "silu" gives
- * silu(first half) * second half; _moe_problem_size: w1 is [E, N, .], w2 is
- * [E, K, .] with K the hidden size) ------------------------------------------
- * h[i] = silu(g_i) * u_i with g_i = W1[e, i, :] . x, u_i = W1[e, I + i, :] . x,
- * silu(g) = g / (1 + exp(-g)). */
-void oracle_expert_hidden(const double* x, int64_t H, int64_t I, const oracle_weights* w1,
-                          int64_t e, double* h) {
+ * the output is half the width of the input, "silu" gives
+ * silu(first half) * second half and "gelu" gelu(first half) * second half;
+ * _moe_problem_size: w1 is [E, N, .], w2 is [E, K, .] with K the hidden
+ * size) ----------------------------------------------------------------------
+ * h[i] = act(g_i) * u_i with g_i = W1[e, i, :] . x, u_i = W1[e, I + i, :] . x,
+ *   silu(g) = g / (1 + exp(-g)),   gelu(g) = g/2 * (1 + erf(g / sqrt(2)))
+ * (the erf form of GELU).  With clamp > 0 (the activation_clamp of the fused
+ * SwiGLU epilogue in [EP] build_fi_mega_config; the page gives only its name
+ * and type) the gate is limited from above and the up value to [-clamp,
+ * clamp] before the product: g = min(g, clamp), u = min(max(u, -clamp), clamp). */
+static double gated_act(double g, double u, int32_t act, double clamp) {
+  if (clamp > 0.0) {
+    if (g > clamp) g = clamp;
+    if (u > clamp) u = clamp;
+    if (u < -clamp) u = -clamp;
+  }
+  double a = act == OR_ACT_GELU ? 0.5 * g * (1.0 + erf(g / sqrt(2.0))) : g / (1.0 + exp(-g));
+  return a * u;
+}
+
+void oracle_expert_hidden_act(const double* x, int64_t H, int64_t I, const oracle_weights* w1,
+                              int64_t e, int32_t act, double clamp, double* h) {
   for (int64_t i = 0; i < I; ++i) {
     double g = dot_row(w1, e * 2 * I + i, H, x);
     double u = dot_row(w1, e * 2 * I + I + i, H, x);
-    h[i] = g / (1.0 + exp(-g)) * u;
+    h[i] = gated_act(g, u, act, clamp);
   }
+}
+
+void oracle_expert_hidden(const double* x, int64_t H, int64_t I, const oracle_weights* w1,
+                          int64_t e, double* h) {
+  oracle_expert_hidden_act(x, H, I, w1, e, OR_ACT_SILU, 0.0, h);
 }
 
 /* y[n] = W2[e, n, :] . h */
@@ -196,14 +217,15 @@ void oracle_expert_out(const double* h, int64_t H, int64_t I, const oracle_weigh
  *   hidden: rows[r] -> h[r] with expert expert_of_row[r];
  *   out:    h rows (bf16) -> y[r]. */
 void oracle_hidden_rows(const uint16_t* a, int64_t rows, int64_t H, int64_t I,
-                        const oracle_weights* w1, const int32_t* expert_of_row, double* h) {
+                        const oracle_weights* w1, const int32_t* expert_of_row, int32_t act,
+                        double clamp, double* h) {
 #pragma omp parallel
   {
     double* xv = (double*)malloc(sizeof(double) * (size_t)H);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; ++r) {
       for (int64_t c = 0; c < H; ++c) xv[c] = bf16_val(a[r * H + c]);
-      oracle_expert_hidden(xv, H, I, w1, expert_of_row[r], h + r * I);
+      oracle_expert_hidden_act(xv, H, I, w1, expert_of_row[r], act, clamp, h + r * I);
     }
     free(xv);
   }
@@ -279,6 +301,12 @@ void oracle_finalize_add_rmsnorm(const uint16_t* y_perm, const double* w, const 
  * For each listed token t: route it, localize each route through the expert
  * map, run the expert MLP of every local route, and combine:
  *   out[t] = rsf_fin * sum_j w_j * MLP_{L_j}(x_t) + MLP_shared(x_t).
+ * With weight_on_input ([MOD] forward and prepare: apply_router_weight_on_input
+ * puts the weights on the activations before dispatch, and finalize then does
+ * not apply them; only for top_k = 1):
+ *   out[t] = rsf_fin * sum_j MLP_{L_j}(w_j * x_t) + MLP_shared(x_t).
+ * act and clamp select the activation of every expert MLP, the shared one
+ * included (see gated_act).
  * Optional outputs: y_routes [n, k, H] (the unweighted per-route expert output,
  * zero for non-local routes), ids [n, k], weights [n, k].
  * shared_I = 0 disables the shared expert. */
@@ -286,15 +314,16 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
                        int32_t k, int32_t score_fn, int32_t renormalize, double rsf,
                        const int32_t* expert_map, const oracle_weights* w1,
                        const oracle_weights* w2, int64_t shared_I, const uint16_t* ws1,
-                       const uint16_t* ws2, double rsf_fin, const int64_t* tokens,
-                       int64_t n_tokens, double* out, double* y_routes, int32_t* ids_out,
-                       double* w_out) {
+                       const uint16_t* ws2, double rsf_fin, int32_t act, double clamp,
+                       int32_t weight_on_input, const int64_t* tokens, int64_t n_tokens,
+                       double* out, double* y_routes, int32_t* ids_out, double* w_out) {
   oracle_weights s1 = {OR_W_BF16, ws1, NULL};
   oracle_weights s2 = {OR_W_BF16, ws2, NULL};
 #pragma omp parallel
   {
     int64_t Imax = I > shared_I ? I : shared_I;
     double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+    double* xw = (double*)malloc(sizeof(double) * (size_t)H);
     double* hv = (double*)malloc(sizeof(double) * (size_t)Imax);
     double* yv = (double*)malloc(sizeof(double) * (size_t)H);
     int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
@@ -315,18 +344,25 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
           for (int64_t n = 0; n < H; ++n) yr[n] = 0.0;
           continue;
         }
-        oracle_expert_hidden(xv, H, I, w1, L, hv);
+        if (weight_on_input) {
+          for (int64_t c = 0; c < H; ++c) xw[c] = wts[j] * xv[c];
+          oracle_expert_hidden_act(xw, H, I, w1, L, act, clamp, hv);
+        } else {
+          oracle_expert_hidden_act(xv, H, I, w1, L, act, clamp, hv);
+        }
         oracle_expert_out(hv, H, I, w2, L, yr);
-        for (int64_t n = 0; n < H; ++n) o[n] += wts[j] * yr[n];
+        const double wj = weight_on_input ? 1.0 : wts[j];
+        for (int64_t n = 0; n < H; ++n) o[n] += wj * yr[n];
       }
       for (int64_t n = 0; n < H; ++n) o[n] *= rsf_fin;
       if (shared_I > 0) {
-        oracle_expert_hidden(xv, H, shared_I, &s1, 0, hv);
+        oracle_expert_hidden_act(xv, H, shared_I, &s1, 0, act, clamp, hv);
         oracle_expert_out(hv, H, shared_I, &s2, 0, yv);
         for (int64_t n = 0; n < H; ++n) o[n] += yv[n];
       }
     }
     free(xv);
+    free(xw);
     free(hv);
     free(yv);
     free(ids);
