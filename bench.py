@@ -2,6 +2,8 @@
 """Benchmark of the fused MoE layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--tokens T]
+                    [--activation silu|gelu] [--activation-clamp C] [--top-k K]
+                    [--router-weight-on-input] [--chunk-tokens N] [--fused-tail] [--graph]
 
 One step is the whole hot path on one batch of synthetic input already
 resident in HBM: route -> permute (map, offsets, row gather) -> grouped GEMM1
@@ -17,6 +19,12 @@ bf16 weights.  The other workloads:
                                      steps cycle through 16 routing draws and a
                                      512 MiB read evicts L2 and the MALL before
                                      each step (outside the timed events)
+
+Variants of a workload (each named in config.workload): GELU instead of SiLU,
+an activation clamp, another top_k, the routing weight applied to the input
+rows (top_k 1), and activation chunking (the layer over consecutive chunks of
+N tokens with buffers sized for one chunk; every chunk re-streams the weights
+of its experts).
 
 Prints one JSON line: tokens/s (value), algorithmic TFLOP/s, the roofline of
 the dominant kernel (grouped GEMM1) from HIP events recorded around each of its
@@ -60,6 +68,14 @@ def parse():
     p.add_argument("--fused-tail", action="store_true",
                    help="end the step with the fused tail (finalize + shared add + residual add "
                         "+ the next layer's RMSNorm) instead of the plain finalize")
+    p.add_argument("--activation", choices=["silu", "gelu"], default="silu")
+    p.add_argument("--activation-clamp", type=float, default=0.0,
+                   help="> 0: clamp the gate from above and the up value on both sides first")
+    p.add_argument("--top-k", type=int, default=0, help="override the workload's top_k")
+    p.add_argument("--router-weight-on-input", action="store_true",
+                   help="apply the routing weights to the input rows (top_k 1 only)")
+    p.add_argument("--chunk-tokens", type=int, default=0,
+                   help="run the layer over chunks of this many tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -108,7 +124,7 @@ def gemm_work(cfg, counts, gemm: int):
     return flops, nbytes
 
 
-def cpu_baseline(cfg, draws, w, target_s: float):
+def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
     """The oracle as it stands, on all host cores, on a bounded sample of the
     workload's tokens (draw after draw, chunk after chunk) until about
     target_s seconds of CPU work."""
@@ -119,7 +135,7 @@ def cpu_baseline(cfg, draws, w, target_s: float):
         W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
     from synth import configs
     kw = dict(expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I, ws1=w.get("ws1"),
-              ws2=w.get("ws2"))
+              ws2=w.get("ws2"), **(variant or {}))
 
     def run(x, logits, toks):
         oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
@@ -172,6 +188,12 @@ def main():
         print(f"unknown workload {args.workload}; one of {sorted(configs.ALL)}", file=sys.stderr)
         sys.exit(2)
     cfg = configs.ALL[args.workload]
+    if args.top_k:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, k=args.top_k)
+    if args.router_weight_on_input and cfg.k != 1:
+        print("--router-weight-on-input needs top_k 1 (--top-k 1)", file=sys.stderr)
+        sys.exit(2)
     decode = cfg.deferred
     if decode:
         if args.tokens not in configs.EP_DECODE_BATCHES:
@@ -184,6 +206,18 @@ def main():
     else:
         draws = [configs.make_activations(cfg)]
         label = cfg.name
+    if args.top_k:
+        label += f"_top{cfg.k}"
+    if args.activation != "silu":
+        label += f"_{args.activation}"
+    if args.activation_clamp:
+        label += f"_clamp{args.activation_clamp:g}"
+    if args.router_weight_on_input:
+        label += "_weight_on_input"
+    if args.chunk_tokens and args.chunk_tokens < cfg.T:
+        label += f"_chunk{args.chunk_tokens}"
+    variant = {"activation": args.activation, "clamp": args.activation_clamp,
+               "weight_on_input": args.router_weight_on_input}
     w = configs.make_weights(cfg)
 
     def to_bf16(a):
@@ -198,7 +232,9 @@ def main():
     emap = configs.expert_map(cfg)
     emap_d = None if emap is None else torch.from_numpy(emap).cuda()
     T, H, I, k, E, El = cfg.T, cfg.H, cfg.I, cfg.k, cfg.E, cfg.El
-    R_pad = moe.moe_permuted_rows(T, k)
+    P = min(T, args.chunk_tokens) if args.chunk_tokens > 0 else T  # tokens per pass
+    chunks = [(t0, min(P, T - t0)) for t0 in range(0, T, P)]
+    R_pad = moe.moe_permuted_rows(P, k)
     dev = "cuda"
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -215,9 +251,9 @@ def main():
     if cfg.shared_I:
         WS1 = moe.Weights(to_bf16(w["ws1"])[None])
         WS2 = moe.Weights(to_bf16(w["ws2"])[None])
-        off_s = torch.tensor([0, T], dtype=torch.int32, device=dev)
-        hs = torch.empty((T, cfg.shared_I), dtype=torch.bfloat16, device=dev)
-        shared = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        off_s = {n: torch.tensor([0, n], dtype=torch.int32, device=dev) for _, n in chunks}
+        hs = torch.empty((P, cfg.shared_I), dtype=torch.bfloat16, device=dev)
+        shared = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if decode else None
     flush_sum = torch.zeros((), dtype=torch.float32, device=dev)
 
@@ -231,44 +267,69 @@ def main():
     split_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
-    stages = ["route", "permute", "gemm1", "gemm2", "shared", "finalize"]
+    fin_stage = "finalize_add_rmsnorm" if args.fused_tail else "finalize"
+    stages = ["route", "permute", "gemm1", "gemm2"] + (["shared"] if cfg.shared_I else []) \
+        + [fin_stage]
+    act_kw = dict(activation=args.activation, activation_clamp=args.activation_clamp)
+    w_in = args.router_weight_on_input
 
-    def route_permute(d):
+    def route_permute(d, t0, n):
         xd, ld = dev_draws[d]
-        moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, stream)
-        moe.moe_permute(ids, E, El, emap_d, xd, R_pad, pmap, offsets, None, x_perm,
-                        want_inv=False, stream=stream)
+        sl = slice(t0, t0 + n)
+        moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
+                           stream)
+        moe.moe_permute(ids[sl], E, El, emap_d, xd[sl], R_pad, pmap[sl], offsets, None, x_perm,
+                        want_inv=False, x_weights=wts[sl] if w_in else None, stream=stream)
 
-    def layer(d, st, mark=lambda j: None):
-        """The layer on input batch d, enqueued on stream st; mark(j) records
-        stage boundaries."""
+    def layer(d, st, mark=lambda name: None):
+        """The layer on input batch d, enqueued on stream st, one pass per
+        chunk; mark(name) records the start of stage `name` (None: the end)."""
         xd, ld = dev_draws[d]
-        mark(0)
-        moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf, ids, wts, st)
-        mark(1)
-        moe.moe_permute(ids, E, El, emap_d, xd, R_pad, pmap, offsets, None, x_perm,
-                        want_inv=False, stream=st)
-        mark(2)
-        moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
+        for t0, n in chunks:
+            sl = slice(t0, t0 + n)
+            mark("route")
+            moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
+                               st)
+            mark("permute")
+            moe.moe_permute(ids[sl], E, El, emap_d, xd[sl], R_pad, pmap[sl], offsets, None,
+                            x_perm, want_inv=False, x_weights=wts[sl] if w_in else None,
+                            stream=st)
+            mark("gemm1")
+            moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
+                                      workspace=split_ws, **act_kw)
+            mark("gemm2")
+            moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False,
                                   workspace=split_ws)
-        mark(3)
-        moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False, workspace=split_ws)
-        mark(4)
-        if cfg.shared_I:
-            moe.moe_grouped_gemm1_act(xd, off_s, WS1, cfg.shared_I, hs, stream=st, split=False)
-            moe.moe_grouped_gemm2(hs, off_s, WS2, H, shared, stream=st, split=False)
-        mark(5)
-        if args.fused_tail:
-            moe.moe_finalize_add_rmsnorm(y, wts, pmap, residual, gamma, 1e-6, 1.0, shared, out,
-                                         stream=st)
-        else:
-            moe.moe_finalize(y, wts, pmap, 1.0, shared, out, stream=st)
-        mark(6)
+            sh = None
+            if cfg.shared_I:
+                mark("shared")
+                sh = shared[:n]
+                moe.moe_grouped_gemm1_act(xd[sl], off_s[n], WS1, cfg.shared_I, hs[:n], stream=st,
+                                          split=False, **act_kw)
+                moe.moe_grouped_gemm2(hs[:n], off_s[n], WS2, H, sh, stream=st, split=False)
+            mark(fin_stage)
+            wf = None if w_in else wts[sl]
+            if args.fused_tail:
+                moe.moe_finalize_add_rmsnorm(y, wf, pmap[sl], residual[sl], gamma, 1e-6, 1.0, sh,
+                                             out[sl], stream=st)
+            else:
+                moe.moe_finalize(y, wf, pmap[sl], 1.0, sh, out[sl], stream=st)
+        mark(None)
+
+    marks_per_step = len(chunks) * len(stages) + 1
 
     def step(i, ev=None):
         if flush is not None:
             evict_caches()
-        mark = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        if ev is None:
+            layer(i % len(dev_draws), stream)
+            return
+        names, pool = ev
+        it = iter(pool)
+
+        def mark(name):
+            names.append(name)
+            next(it).record(stream)
         layer(i % len(dev_draws), stream, mark)
 
     if args.calibrate_copy_mib:
@@ -293,53 +354,62 @@ def main():
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [([], [torch.cuda.Event(enable_timing=True) for _ in range(marks_per_step)])
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if graphs:
             if flush is not None:
                 evict_caches()
-            events[i][0].record()
+            events[i][1][0].record()
             graphs[i % len(graphs)].replay()
-            events[i][6].record()
+            events[i][1][1].record()
         else:
             step(i, events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    if graphs:
-        per_step = [[0.0] * 5 + [events[i][0].elapsed_time(events[i][6])] for i in range(args.steps)]
-        stage_ms = {"layer_graph": float(np.mean([p[5] for p in per_step]))}
-    else:
-        per_step = [[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
-                    for i in range(args.steps)]
-        stage_ms = {s: float(np.mean([p[j] for p in per_step])) for j, s in enumerate(stages)}
-        if args.fused_tail:
-            stage_ms["finalize_add_rmsnorm"] = stage_ms.pop("finalize")
-        if not cfg.shared_I:
-            del stage_ms["shared"]
+    # per step: milliseconds of each stage, summed over the step's chunks
+    per_step = []
+    for i in range(args.steps):
+        if graphs:
+            per_step.append({"layer_graph": events[i][1][0].elapsed_time(events[i][1][1])})
+            continue
+        names, pool = events[i]
+        ms = dict.fromkeys(stages, 0.0)
+        for j in range(len(names) - 1):
+            ms[names[j]] += pool[j].elapsed_time(pool[j + 1])
+        per_step.append(ms)
+    stage_ms = {s: float(np.mean([p[s] for p in per_step])) for s in per_step[0]}
 
-    # routed rows per local expert of every draw (untimed re-run of route + permute)
+    # routed rows per local expert of every chunk of every draw (untimed
+    # re-run of route + permute)
     draw_counts = []
     for d in range(len(dev_draws)):
-        route_permute(d)
-        draw_counts.append(np.diff(offsets.cpu().numpy()))
+        per_chunk = []
+        for t0, n in chunks:
+            route_permute(d, t0, n)
+            per_chunk.append(np.diff(offsets.cpu().numpy()))
+        draw_counts.append(per_chunk)
     step_counts = [draw_counts[i % len(dev_draws)] for i in range(args.steps)]
 
     flops_step = []
     g1_flops = g1_bytes = g1_ms = g2_bytes = 0.0
-    for i, c in enumerate(step_counts):
-        f1, b1 = gemm_work(cfg, c, 1)
-        f2, b2 = gemm_work(cfg, c, 2)
-        g2_bytes += b2
-        flops_step.append(f1 + f2 + 6.0 * T * H * cfg.shared_I)
-        g1_flops += f1
-        g1_bytes += b1
-        g1_ms += per_step[i][2]
+    for i, per_chunk in enumerate(step_counts):
+        f_step = 6.0 * T * H * cfg.shared_I
+        for c in per_chunk:
+            f1, b1 = gemm_work(cfg, c, 1)
+            f2, b2 = gemm_work(cfg, c, 2)
+            g2_bytes += b2
+            f_step += f1 + f2
+            g1_flops += f1
+            g1_bytes += b1
+        flops_step.append(f_step)
+        g1_ms += per_step[i].get("gemm1", 0.0)
     if decode:
         # the flush between steps is not part of the layer: time from the events
-        ms_per_step = float(np.mean([sum(p) for p in per_step]))
+        ms_per_step = float(np.mean([sum(p.values()) for p in per_step]))
     else:
         ms_per_step = elapsed / args.steps * 1e3
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
@@ -354,7 +424,7 @@ def main():
         achieved = g1_bytes / g1_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-    n_launch = len(step_counts)
+    n_launch = len(step_counts) * len(chunks)
     if graphs:
         roof.update({"achieved": None, "frac": None,
                      "note": "no per-kernel timing under graph replay; run without --graph"})
@@ -363,7 +433,7 @@ def main():
                  "algorithmic_bytes_per_launch": g1_bytes / n_launch,
                  "gemm2_algorithmic_bytes_per_launch": g2_bytes / n_launch})
 
-    counts0 = draw_counts[0]
+    counts0 = np.sum(draw_counts[0], axis=0)
     result = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),
@@ -388,7 +458,11 @@ def main():
                    "form": ("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
                             f"{len(draws)} routing draws" if decode else "finalized")
                            + (", replayed as a captured HIP graph" if graphs else "")
-                           + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")},
+                           + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")
+                           + (f", {len(chunks)} chunks of {P} tokens" if len(chunks) > 1 else ""),
+                   "activation": args.activation
+                                 + (f", clamp {args.activation_clamp:g}" if args.activation_clamp else "")
+                                 + (", routing weight on the input" if w_in else "")},
         "tflops": tflops,
         "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
         "stages_ms": stage_ms,
@@ -400,7 +474,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         del dev_draws, W1, W2, x_perm, h, y, out
-        result["cpu_baseline"] = cpu_baseline(cfg, draws, w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, draws, w, args.cpu_seconds, variant)
     print(json.dumps(result), flush=True)
 
 

@@ -79,8 +79,38 @@ enum {
 };
 
 /* Activations of GEMM1 (page "modular_kernel.py", activation(): the output is
- * half as wide as GEMM1's; "silu" gives silu(first half) * second half). */
-enum { MOE_ACT_SILU = 0 };
+ * half as wide as GEMM1's; "silu" gives silu(first half) * second half and
+ * "gelu" gelu(first half) * second half).  silu(g) = g / (1 + e^-g);
+ * gelu(g) = g/2 * (1 + erf(g / sqrt 2)), the erf form. */
+enum { MOE_ACT_SILU = 0, MOE_ACT_GELU = 1 };
+
+/* Options of the fused entry points; NULL (or all fields 0) gives the
+ * defaults.
+ *   activation        MOE_ACT_SILU or MOE_ACT_GELU, for every expert MLP
+ *                     (the shared expert's included)
+ *   activation_clamp  0: none.  > 0: before the product the gate is limited
+ *                     to <= clamp and the up value to [-clamp, clamp] (the
+ *                     activation_clamp of the fused SwiGLU epilogue, page
+ *                     "flashinfer_moe_ep.py", build_fi_mega_config).  Must be
+ *                     finite and >= 0.
+ *   apply_router_weight_on_input  nonzero: the routing weight scales each
+ *                     token row before GEMM1 (rounded to bf16) and the combine
+ *                     adds the expert rows unweighted (page
+ *                     "modular_kernel.py", forward(), prepare() and
+ *                     finalize()).  top_k must be 1.  The deferred form then
+ *                     returns expert_weights of exactly 1.
+ *   chunk_tokens      0: one pass over all T tokens.  > 0: moe_fused_experts
+ *                     runs the layer over consecutive chunks of at most this
+ *                     many tokens, reusing one workspace sized for a chunk
+ *                     (the activation chunking of forward(), page
+ *                     "modular_kernel.py").  The deferred form takes no
+ *                     chunking: chunk_tokens must be 0 or >= T there. */
+typedef struct moe_layer_options {
+  int32_t activation;
+  float activation_clamp;
+  int32_t apply_router_weight_on_input;
+  int32_t chunk_tokens;
+} moe_layer_options;
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
  *   BF16:  data = bf16 [E_l, N, K],   scales = NULL
@@ -141,6 +171,9 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
  *   inv[r] = t*k+j of the route placed in row r, for r < R_l; -1 for
  *   R_l <= r < R_pad.
  *   x_perm[r, :] = x[inv[r] / k, :] for r < R_l; rows >= R_l are not written.
+ *   With x_weights (apply_router_weight_on_input of prepare(), page
+ *   "modular_kernel.py": the routing weights go on the activations before
+ *   dispatch), x_perm[map[t,j], :] = bf16(x_weights[t,j] * x[t, :]).
  *   topk_ids   (device) int32 [T, k]; an id outside [0, E) is a caller error
  *              and is treated as a non-local route
  *   expert_map (device) int32 [E] with entries in [-1, E_l), or NULL (E_l = E)
@@ -149,19 +182,22 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
  *   offsets    (device) int32 [E_l + 1]   out
  *   inv        (device) int32 [R_pad]     out, may be NULL
  *   x_perm     (device) bf16 [R_pad, H]   out, may be NULL (no gather)
+ *   x_weights  (device) fp32 [T, k] or NULL (rows copied unscaled)
  *   workspace  (device) scratch of moe_workspace_size() bytes, may be NULL
  *              when workspace_bytes is 0 (this version needs none)
  * Limits: E_l <= 1024, H a multiple of 8. */
 int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
                 int32_t E, int32_t E_l, const void* x, int32_t H, int64_t R_pad, int32_t* map,
-                int32_t* offsets, int32_t* inv, void* x_perm, void* workspace,
-                size_t workspace_bytes, void* stream);
+                int32_t* offsets, int32_t* inv, void* x_perm, const float* x_weights,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Grouped GEMM1 + activation (apply() and activation() of page
  * "modular_kernel.py").  For every local expert e and row r in
  * [offsets[e], offsets[e+1]):
  *   g = a_perm[r, :] . W1[e, n, :],  u = a_perm[r, :] . W1[e, I + n, :]
- *   h[r, n] = silu(g) * u   (fp32 accumulation, one rounding to bf16)
+ *   h[r, n] = act(g) * u   (fp32 accumulation, one rounding to bf16)
+ *   activation        MOE_ACT_SILU or MOE_ACT_GELU
+ *   activation_clamp  0, or > 0 to clamp g and u first (moe_layer_options)
  *   a_perm  (device) bf16 [R_pad, H]
  *   offsets (device) int32 [E_l + 1] as written by moe_permute
  *   w1      GEMM1 weights, N = 2I, K = H (BF16, or MXFP4: the decoded values
@@ -177,7 +213,8 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
  * without scales, or bf16 weights with scales, are MOE_ERR_INVALID_ARGUMENT. */
 int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                           int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
-                          void* h, void* workspace, size_t workspace_bytes, void* stream);
+                          float activation_clamp, void* h, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Grouped GEMM2 (apply() of page "modular_kernel.py"; its output is the
  * unweighted, unreduced gemm2_permuted of page "moe_output.py": densely
@@ -203,7 +240,7 @@ int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_
  *   out[t, :] = bf16(z[t, :] / sqrt(mean(z[t, :]^2) + eps) * gamma[:])
  * (the norm uses z before the residual's rounding).
  *   y_perm, weights, weights_dtype, map, T, k, H, rsf_fin, shared: as for
- *              moe_finalize
+ *              moe_finalize (weights may be NULL)
  *   residual   (device) bf16 [T, H] in/out (the residual stream)
  *   gamma      (device) bf16 [H] the norm's per-column scale
  *   eps        >= 0
@@ -230,7 +267,9 @@ int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated,
  * the map never names are never read.  Every row of out is written (a token
  * with no local route gets 0, or its shared row).
  *   y_perm   (device) bf16 [>= R_l, H]
- *   weights  (device) [T, k] of weights_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16)
+ *   weights  (device) [T, k] of weights_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16),
+ *            or NULL: every weight is 1 (finalize() with
+ *            apply_router_weight_on_input, whose weights went on the inputs)
  *   map      (device) int32 [T, k]
  *   shared   (device) bf16 [T, H] or NULL
  *   out      (device) bf16 [T, H] out; may alias shared exactly (in place),
@@ -254,24 +293,29 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
 int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
                                   int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
                                   int32_t renormalize, float rsf, const int32_t* expert_map,
-                                  const moe_weights* w1, const moe_weights* w2, int64_t R_pad,
+                                  const moe_weights* w1, const moe_weights* w2,
+                                  const moe_layer_options* options, int64_t R_pad,
                                   void* gemm2_permuted, void* expert_weights, int32_t* map,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* The whole layer, finalized:
  *   out = rsf_fin * sum_j w_j * MLP_{L_j}(x) + shared MLP(x)
- * with the shared expert (one dense SiLU MLP, intermediate shared_I, weights
+ * (with apply_router_weight_on_input: rsf_fin * sum_j MLP_{L_j}(w_j x) + ...)
+ * with the shared expert (one dense gated MLP, intermediate shared_I, weights
  * ws1 bf16 [2*shared_I, H] and ws2 bf16 [H, shared_I]) present when
  * shared_I > 0.
- *   out       (device) bf16 [T, H]; must not overlap x
- *   workspace (device) >= moe_workspace_size() bytes (with the shared expert:
- *             moe_workspace_size() + moe_shared_workspace_size()) */
+ *   options   moe_layer_options or NULL (SiLU, no clamp, one pass)
+ *   out       (device) bf16 [T, H]; either x itself (in place, forward()'s
+ *             inplace of page "modular_kernel.py") or not overlapping x
+ *   workspace (device) >= moe_workspace_size() + moe_shared_workspace_size()
+ *             bytes (the latter 0 without a shared expert), both taken for
+ *             min(T, chunk_tokens) tokens when chunking */
 int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
                       int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
                       float rsf, const int32_t* expert_map, const moe_weights* w1,
                       const moe_weights* w2, int32_t shared_I, const void* ws1, const void* ws2,
-                      float rsf_fin, void* out, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      float rsf_fin, const moe_layer_options* options, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Extra workspace bytes moe_fused_experts needs for a shared expert of
  * intermediate size shared_I (0 when shared_I = 0). */

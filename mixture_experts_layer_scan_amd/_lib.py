@@ -18,8 +18,15 @@ class MoeWeightsC(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+class MoeLayerOptionsC(ctypes.Structure):
+    _fields_ = [("activation", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
+                ("apply_router_weight_on_input", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32)]
+
+
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _Wp = ctypes.POINTER(MoeWeightsC)
+_Op = ctypes.POINTER(MoeLayerOptionsC)
 
 PROTOTYPES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -30,9 +37,9 @@ PROTOTYPES = {
     "moe_shared_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _vp,
-                                   _vp, _vp, _vp, _sz, _vp]),
-    "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _vp,
-                                             _vp, _sz, _vp]),
+                                   _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _f32,
+                                             _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm2": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _vp, _vp, _sz,
                                          _vp]),
     "moe_finalize_add_rmsnorm": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp,
@@ -40,11 +47,11 @@ PROTOTYPES = {
     "moe_grouped_gemm_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_finalize": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
     "moe_fused_experts_unfinalized": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
-                                                     _i32, _i32, _f32, _vp, _Wp, _Wp, _i64, _vp,
-                                                     _vp, _vp, _vp, _sz, _vp]),
+                                                     _i32, _i32, _f32, _vp, _Wp, _Wp, _Op, _i64,
+                                                     _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_fused_experts": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                         _f32, _vp, _Wp, _Wp, _i32, _vp, _vp, _f32, _vp, _vp, _sz,
-                                         _vp]),
+                                         _f32, _vp, _Wp, _Wp, _i32, _vp, _vp, _f32, _Op, _vp, _vp,
+                                         _sz, _vp]),
 }
 
 _lib = None

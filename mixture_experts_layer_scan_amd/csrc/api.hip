@@ -234,8 +234,8 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
 
 int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
                 int32_t E, int32_t E_l, const void* x, int32_t H, int64_t R_pad, int32_t* map,
-                int32_t* offsets, int32_t* inv, void* x_perm, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                int32_t* offsets, int32_t* inv, void* x_perm, const float* x_weights,
+                void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   (void)workspace;
   (void)workspace_bytes;
@@ -248,6 +248,7 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
   MOE_CHECK(need_ptr(offsets, "offsets"));
   MOE_CHECK(opt_ptr(inv, "inv"));
   MOE_CHECK(opt_ptr(x_perm, "x_perm"));
+  MOE_CHECK(opt_ptr(x_weights, "x_weights"));
   MOE_CHECK(opt_ptr(expert_map, "expert_map"));
   if (T > 0) {
     MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
@@ -261,15 +262,24 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
   hipError_t e = moe::launch_permute(topk_ids, expert_map, T, k, E, E_l, map, offsets, inv, R_pad, s);
   if (e != hipSuccess) return hip_fail(e, "moe_permute");
   if (x_perm && T > 0) {
-    e = moe::launch_gather_rows(x, map, T, k, H, x_perm, s);
+    e = moe::launch_gather_rows(x, map, T, k, H, x_weights, x_perm, s);
     if (e != hipSuccess) return hip_fail(e, "moe_permute gather");
   }
   return MOE_OK;
 }
 
+static int check_activation(int32_t activation, float clamp) {
+  if (activation != MOE_ACT_SILU && activation != MOE_ACT_GELU)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
+  if (!(clamp >= 0.0f) || clamp > 3.0e38f)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "activation_clamp must be finite and >= 0");
+  return MOE_OK;
+}
+
 static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
-                       int32_t K, int32_t N_out, int gated, const moe_weights* w, void* c,
-                       void* workspace, size_t workspace_bytes, void* stream, const char* name) {
+                       int32_t K, int32_t N_out, int gated, int act, float clamp,
+                       const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
+                       void* stream, const char* name) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
@@ -289,19 +299,20 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
       return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: workspace must not overlap the rows", name);
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
-                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes};
+                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp};
   hipError_t e = moe::launch_grouped_gemm(g, R_pad, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
 
 int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                           int32_t H, int32_t I, const moe_weights* w1, int32_t activation,
-                          void* h, void* workspace, size_t workspace_bytes, void* stream) {
+                          float activation_clamp, void* h, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   MOE_CHECK(check_gemm_dims(H, I));
-  if (activation != MOE_ACT_SILU) return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
-  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, w1, h, workspace, workspace_bytes,
-                     stream, "moe_grouped_gemm1_act");
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act");
 }
 
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
@@ -309,8 +320,8 @@ int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_
                       size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   MOE_CHECK(check_gemm_dims(H, I));
-  return gemm_common(h, offsets, E_l, R_pad, I, H, 0, w2, y, workspace, workspace_bytes, stream,
-                     "moe_grouped_gemm2");
+  return gemm_common(h, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
+                     workspace_bytes, stream, "moe_grouped_gemm2");
 }
 
 int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated, size_t* bytes) {
@@ -335,7 +346,7 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
     return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
   if (T == 0) return MOE_OK;
   MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
-  MOE_CHECK(need_ptr(weights, "expert_weights"));
+  MOE_CHECK(opt_ptr(weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(opt_ptr(shared, "shared"));
   MOE_CHECK(need_ptr(out, "out"));
@@ -364,7 +375,7 @@ int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t we
     return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
   if (T == 0) return MOE_OK;
   MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
-  MOE_CHECK(need_ptr(weights, "expert_weights"));
+  MOE_CHECK(opt_ptr(weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(opt_ptr(shared, "shared"));
   MOE_CHECK(need_ptr(residual, "residual"));
@@ -414,24 +425,57 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   return b;
 }
 
-// Route, permute, GEMM1, GEMM2 on one stream.  map_out / y_out default to the
-// workspace copies; w_bf16_out, when given, receives bf16 routing weights.
+// Options of the fused entry points, checked.
+struct LayerOpts {
+  int act = MOE_ACT_SILU;
+  float clamp = 0.0f;
+  bool weight_on_input = false;
+  int64_t chunk = 0;  // 0: one pass
+};
+
+static int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
+  *out = LayerOpts{};
+  if (!o) return MOE_OK;
+  MOE_CHECK(check_activation(o->activation, o->activation_clamp));
+  if (o->apply_router_weight_on_input && k != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "apply_router_weight_on_input needs top_k = 1 (k=%d)", k);
+  if (o->chunk_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "chunk_tokens must be >= 0");
+  out->act = o->activation;
+  out->clamp = o->activation_clamp;
+  out->weight_on_input = o->apply_router_weight_on_input != 0;
+  out->chunk = o->chunk_tokens;
+  return MOE_OK;
+}
+
+// Tokens per pass: all T, or the chunk size when it is smaller.
+static int64_t pass_tokens(int64_t T, const LayerOpts& o) {
+  return (o.chunk > 0 && o.chunk < T) ? o.chunk : T;
+}
+
+// Route, permute, GEMM1, GEMM2 of T tokens on one stream.  map_out / y_out
+// default to the workspace copies; w_bf16_out, when given, receives the bf16
+// routing weights (exactly 1 when they go on the inputs).
 static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
                       int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
                       float rsf, const int32_t* expert_map, const moe_weights* w1,
-                      const moe_weights* w2, const RoutedWs& b, int32_t* map_out, void* y_out,
-                      uint16_t* w_bf16_out, hipStream_t s) {
+                      const moe_weights* w2, const LayerOpts& o, const RoutedWs& b,
+                      int32_t* map_out, void* y_out, uint16_t* w_bf16_out, hipStream_t s) {
   int32_t* map = map_out ? map_out : b.map;
   void* y = y_out ? y_out : b.x_perm;
   hipError_t e = moe::launch_route_topk(logits, T, E, k, score_fn, renormalize, rsf, b.ids, b.wts,
                                         w_bf16_out, s);
   if (e != hipSuccess) return hip_fail(e, "route");
+  if (o.weight_on_input && w_bf16_out) {
+    e = moe::launch_fill_u16(w_bf16_out, T * k, 0x3F80, s);  // bf16 1.0
+    if (e != hipSuccess) return hip_fail(e, "unit weights");
+  }
   e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "permute");
-  e = moe::launch_gather_rows(x, map, T, k, H, b.x_perm, s);
+  e = moe::launch_gather_rows(x, map, T, k, H, o.weight_on_input ? b.wts : nullptr, b.x_perm, s);
   if (e != hipSuccess) return hip_fail(e, "gather");
   moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
-                   b.split, b.split_bytes};
+                   b.split, b.split_bytes, o.act, o.clamp};
   e = moe::launch_grouped_gemm(g1, b.rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm1");
   moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
@@ -444,7 +488,7 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
 static int check_fused_args(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
                             int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
                             const int32_t* expert_map, const moe_weights* w1,
-                            const moe_weights* w2) {
+                            const moe_weights* w2, int64_t pass_T) {
   MOE_CHECK(check_route_sizes(T, E, k));
   MOE_CHECK(check_local(E, E_l));
   MOE_CHECK(check_gemm_dims(H, I));
@@ -454,7 +498,7 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
     return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
   MOE_CHECK(check_weights(w1, "w1"));
   MOE_CHECK(check_weights(w2, "w2"));
-  const int64_t rows = moe_permuted_rows(T, k);
+  const int64_t rows = moe_permuted_rows(pass_T, k);
   MOE_CHECK(check_gemm_extent(rows, H, 2 * int64_t(I)));
   MOE_CHECK(check_gemm_extent(rows, I, H));
   MOE_CHECK(opt_ptr(expert_map, "expert_map"));
@@ -476,11 +520,16 @@ static int check_workspace(void* workspace, size_t have, size_t need) {
 int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
                                   int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
                                   int32_t renormalize, float rsf, const int32_t* expert_map,
-                                  const moe_weights* w1, const moe_weights* w2, int64_t R_pad,
+                                  const moe_weights* w1, const moe_weights* w2,
+                                  const moe_layer_options* options, int64_t R_pad,
                                   void* gemm2_permuted, void* expert_weights, int32_t* map,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2));
+  LayerOpts o;
+  MOE_CHECK(parse_options(options, k, &o));
+  if (o.chunk > 0 && o.chunk < T)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "the deferred form takes no chunking (chunk_tokens < T)");
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, T));
   MOE_CHECK(check_rpad(T, k, R_pad));
   if (T == 0) return MOE_OK;
   MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
@@ -490,7 +539,7 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   Carve c{static_cast<char*>(workspace)};
   const RoutedWs b = carve_routed(c, T, k, E_l, H, I);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
-                    b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
+                    o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
                     static_cast<hipStream_t>(stream));
 }
 
@@ -498,15 +547,18 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
                       int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
                       float rsf, const int32_t* expert_map, const moe_weights* w1,
                       const moe_weights* w2, int32_t shared_I, const void* ws1, const void* ws2,
-                      float rsf_fin, void* out, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      float rsf_fin, const moe_layer_options* options, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2));
+  LayerOpts o;
+  MOE_CHECK(parse_options(options, k, &o));
+  const int64_t P = pass_tokens(T, o);  // tokens per pass
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, P));
   if (shared_I < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "shared_I must be >= 0");
   if (shared_I > 0) {
     MOE_CHECK(check_gemm_dims(H, shared_I));
-    MOE_CHECK(check_gemm_extent(T, H, 2 * int64_t(shared_I)));
-    MOE_CHECK(check_gemm_extent(T, shared_I, H));
+    MOE_CHECK(check_gemm_extent(P, H, 2 * int64_t(shared_I)));
+    MOE_CHECK(check_gemm_extent(P, shared_I, H));
   }
   if (T == 0) return MOE_OK;
   MOE_CHECK(need_ptr(out, "out"));
@@ -515,34 +567,54 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     MOE_CHECK(need_ptr(ws2, "ws2"));
   }
   size_t shared_bytes = 0;
-  MOE_CHECK(moe_shared_workspace_size(T, H, shared_I, &shared_bytes));
-  MOE_CHECK(check_workspace(workspace, workspace_bytes,
-                            routed_ws_bytes(T, k, E_l, H, I) + shared_bytes));
+  MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
+  const size_t need = routed_ws_bytes(P, k, E_l, H, I) + shared_bytes;
+  MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
+  // out is x itself (in place) or apart from it; the workspace is apart from both
+  const size_t row_bytes = sizeof(uint16_t) * T * H;
+  if (out != x && overlap(out, row_bytes, x, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "out must be x itself or not overlap it");
+  if (overlap(workspace, need, out, row_bytes) || overlap(workspace, need, x, row_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "the workspace must not overlap x or out");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I);
-  MOE_CHECK(run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1,
-                       w2, b, nullptr, nullptr, nullptr, s));
-  const uint16_t* shared_out = nullptr;
+  const RoutedWs b = carve_routed(c, P, k, E_l, H, I);
+  int32_t* s_off = nullptr;
+  uint16_t* s_h = nullptr;
+  uint16_t* s_y = nullptr;
   if (shared_I > 0) {
-    // the shared expert is one dense SiLU MLP: a single-expert grouped GEMM
-    // pair over all T rows of x
-    int32_t* s_off = c.take<int32_t>(2);
-    uint16_t* s_h = c.take<uint16_t>(T * shared_I);
-    uint16_t* s_y = c.take<uint16_t>(T * H);
-    hipError_t e = moe::launch_fill_i32(s_off, 2, 0, static_cast<int32_t>(T), s);
-    if (e != hipSuccess) return hip_fail(e, "shared offsets");
-    moe::GemmArgs g1{x, ws1, nullptr, s_off, 1, H, shared_I, 1, T, s_h};
-    e = moe::launch_grouped_gemm(g1, T, s);
-    if (e != hipSuccess) return hip_fail(e, "shared gemm1");
-    moe::GemmArgs g2{s_h, ws2, nullptr, s_off, 1, shared_I, H, 0, T, s_y};
-    e = moe::launch_grouped_gemm(g2, T, s);
-    if (e != hipSuccess) return hip_fail(e, "shared gemm2");
-    shared_out = s_y;
+    s_off = c.take<int32_t>(2);
+    s_h = c.take<uint16_t>(P * shared_I);
+    s_y = c.take<uint16_t>(P * H);
   }
-  hipError_t e = moe::launch_finalize(b.x_perm, b.wts, 0, b.map, T, k, H, rsf_fin, shared_out,
-                                      out, s);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "finalize");
+  // Each pass reads only its own rows of x and writes only its own rows of
+  // out, after its last read of them, so out may be x.
+  for (int64_t t0 = 0; t0 < T; t0 += P) {
+    const int64_t n = std::min(P, T - t0);
+    const uint16_t* xc = static_cast<const uint16_t*>(x) + t0 * H;
+    MOE_CHECK(run_routed(logits + t0 * E, xc, n, H, I, E, E_l, k, score_fn, renormalize, rsf,
+                         expert_map, w1, w2, o, b, nullptr, nullptr, nullptr, s));
+    const uint16_t* shared_out = nullptr;
+    if (shared_I > 0) {
+      // the shared expert is one dense gated MLP: a single-expert grouped
+      // GEMM pair over the pass's rows of x
+      hipError_t e = moe::launch_fill_i32(s_off, 2, 0, static_cast<int32_t>(n), s);
+      if (e != hipSuccess) return hip_fail(e, "shared offsets");
+      moe::GemmArgs g1{xc, ws1, nullptr, s_off, 1, H, shared_I, 1, n, s_h, nullptr, 0, o.act,
+                       o.clamp};
+      e = moe::launch_grouped_gemm(g1, n, s);
+      if (e != hipSuccess) return hip_fail(e, "shared gemm1");
+      moe::GemmArgs g2{s_h, ws2, nullptr, s_off, 1, shared_I, H, 0, n, s_y};
+      e = moe::launch_grouped_gemm(g2, n, s);
+      if (e != hipSuccess) return hip_fail(e, "shared gemm2");
+      shared_out = s_y;
+    }
+    hipError_t e = moe::launch_finalize(b.x_perm, o.weight_on_input ? nullptr : b.wts, 0, b.map,
+                                        n, k, H, rsf_fin, shared_out,
+                                        static_cast<uint16_t*>(out) + t0 * H, s);
+    if (e != hipSuccess) return hip_fail(e, "finalize");
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -10,7 +10,9 @@
 // columns, so every access is a 16-byte load or store.  The routes of the
 // token (map and weights, k <= 32) are staged once in LDS.
 // Entries of -1 are skipped, so rows the map never names are never read.
-// Accumulation is fp32 in j order, rounded once to bf16.
+// Accumulation is fp32 in j order, rounded once to bf16.  Without weights
+// (NULL) every route counts once: finalize() with apply_router_weight_on_input,
+// whose weights were applied to the inputs.
 #include "moe_common.h"
 
 namespace moe {
@@ -28,9 +30,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__
     __syncthreads();  // the previous token's routes are no longer read
     if (threadIdx.x < k) {
       s_row[threadIdx.x] = map[t * k + threadIdx.x];
-      s_w[threadIdx.x] = W_BF16
-          ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
-          : static_cast<const float*>(wts)[t * k + threadIdx.x];
+      s_w[threadIdx.x] = !wts ? 1.0f
+          : W_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
+                   : static_cast<const float*>(wts)[t * k + threadIdx.x];
     }
     __syncthreads();
     for (int c = threadIdx.x; c < H8; c += blockDim.x) {
@@ -96,9 +98,9 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
     __syncthreads();  // the previous token's routes and sums are no longer read
     if (threadIdx.x < k) {
       s_row[threadIdx.x] = map[t * k + threadIdx.x];
-      s_w[threadIdx.x] = W_BF16
-          ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
-          : static_cast<const float*>(wts)[t * k + threadIdx.x];
+      s_w[threadIdx.x] = !wts ? 1.0f
+          : W_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
+                   : static_cast<const float*>(wts)[t * k + threadIdx.x];
     }
     __syncthreads();
     float ss = 0.0f;

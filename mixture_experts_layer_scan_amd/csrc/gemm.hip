@@ -1,5 +1,5 @@
 // Grouped expert GEMMs (apply() of vLLM's modular fused-MoE kernel: GEMM1,
-// the silu-and-mul activation, GEMM2, all unweighted).
+// the silu-and-mul or gelu-and-mul activation, GEMM2, all unweighted).
 //
 //   C[r, n] = sum_k A[r, k] * W[e, n, k]     for r in expert e's row segment
 //
@@ -73,7 +73,7 @@
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
 // computes gate and up blocks with the same lane layout, so the epilogue
-// forms silu(g) * u in registers and writes BN/2 columns of h.
+// forms act(g) * u in registers and writes BN/2 columns of h.
 #include "moe_common.h"
 
 #include <algorithm>
@@ -316,10 +316,12 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W,
     const uint8_t* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
-    int s_cap, int* __restrict__ split_out) {
+    int s_cap, int* __restrict__ split_out, int act, float clamp) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
+  const int kind = act_kind(act, clamp);  // GEMM1 epilogue: 0 silu, 1 clamped silu, 2 gelu
+  const float cl = act_limit(clamp);
   // LDS stages as distinct objects, so the compiler knows that loads into one
   // never alias operand reads from another (unused ones are tiny)
   __shared__ __attribute__((aligned(16))) uint16_t lds_a0[Cfg::A_ELEMS];
@@ -713,44 +715,55 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       }
       continue;
     }
+    // bf16 stores; the activation kind is a compile-time constant inside, so
+    // the unrolled loops carry no branches on it
+    auto store_tile = [&](auto kind) {
+      constexpr int KIND = decltype(kind)::value;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+      for (int fm = 0; fm < FM; ++fm) {
+        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
-        if (r >= rows) continue;
-        uint16_t* crow = C + static_cast<int64_t>(row0 + r) * N_out;
-        if (Cfg::GATED) {
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
+          if (r >= rows) continue;
+          uint16_t* crow = C + static_cast<int64_t>(row0 + r) * N_out;
+          if (Cfg::GATED) {
 #pragma unroll
-          for (int fn = 0; fn < FN / 2; ++fn) {
-            const int col = n0 + wn * (Cfg::WTN / 2) + fn * 32 + frag_row;
-            const float g = acc[fm][fn][i];
-            const float u = acc[fm][fn + FN / 2][i];
-            const float hv = g / (1.0f + __expf(-g)) * u;
-            if (col < N_out) crow[col] = f32_to_bf16(hv);
-          }
-        } else {
+            for (int fn = 0; fn < FN / 2; ++fn) {
+              const int col = n0 + wn * (Cfg::WTN / 2) + fn * 32 + frag_row;
+              const float hv = gated_act_k<KIND>(acc[fm][fn][i], acc[fm][fn + FN / 2][i], cl);
+              if (col < N_out) crow[col] = f32_to_bf16(hv);
+            }
+          } else {
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int col = n0 + wn * Cfg::WTN + fn * 32 + frag_row;
-            if (col < N_out) crow[col] = f32_to_bf16(acc[fm][fn][i]);
+            for (int fn = 0; fn < FN; ++fn) {
+              const int col = n0 + wn * Cfg::WTN + fn * 32 + frag_row;
+              if (col < N_out) crow[col] = f32_to_bf16(acc[fm][fn][i]);
+            }
           }
         }
       }
+    };
+    if constexpr (!Cfg::GATED) {
+      store_tile(ic<0>{});
+    } else {
+      if (kind == 0) store_tile(ic<0>{});
+      else if (kind == 1) store_tile(ic<1>{});
+      else store_tile(ic<2>{});
     }
   }
 }
 
 // C[r, n] from the S fp32 slices: y = sum_s P[s, r, n], or for GEMM1
-// h = silu(sum_s P[s, r, n]) * sum_s P[s, r, I + n]; the slices are added in
+// h = act(sum_s P[s, r, n]) * sum_s P[s, r, I + n]; the slices are added in
 // order s = 0, 1, ... (the same result on every run).  Rows at or past the
 // local route count are not written.  One thread per 4 output columns.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials,
                                                            const int* __restrict__ split,
                                                            const int32_t* __restrict__ offsets,
                                                            int E_l, int64_t R_pad, int N_out,
-                                                           int gated, uint16_t* __restrict__ C) {
+                                                           int gated, int act, float clamp,
+                                                           uint16_t* __restrict__ C) {
   const int S = split[0];
   if (S <= 1) return;
   const int64_t r = blockIdx.y;
@@ -771,10 +784,18 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     }
   }
   if (gated) {
-    a.x = a.x / (1.0f + __expf(-a.x)) * b.x;
-    a.y = a.y / (1.0f + __expf(-a.y)) * b.y;
-    a.z = a.z / (1.0f + __expf(-a.z)) * b.z;
-    a.w = a.w / (1.0f + __expf(-a.w)) * b.w;
+    const int kind = act_kind(act, clamp);
+    const float cl = act_limit(clamp);
+    auto f = [&](auto k) {
+      constexpr int K = decltype(k)::value;
+      a.x = gated_act_k<K>(a.x, b.x, cl);
+      a.y = gated_act_k<K>(a.y, b.y, cl);
+      a.z = gated_act_k<K>(a.z, b.z, cl);
+      a.w = gated_act_k<K>(a.w, b.w, cl);
+    };
+    if (kind == 0) f(ic<0>{});
+    else if (kind == 1) f(ic<1>{});
+    else f(ic<2>{});
   }
   uint2 o;
   o.x = pack_bf16x2(a.x, a.y);
@@ -814,12 +835,13 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
                      dim3(Cfg::kThreads), 0, s,
                      static_cast<const uint16_t*>(g.a), g.w, g.w_scales, g.offsets, g.E_l, g.K,
-                     g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr);
+                     g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
+                     g.act, g.clamp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));
   hipLaunchKernelGGL(split_reduce_kernel, rgrid, dim3(256), 0, s, partials, hdr, g.offsets, g.E_l,
-                     g.R_pad, g.N_out, g.gated, static_cast<uint16_t*>(g.c));
+                     g.R_pad, g.N_out, g.gated, g.act, g.clamp, static_cast<uint16_t*>(g.c));
   return hipGetLastError();
 }
 

@@ -28,6 +28,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & (kWave - 1)); }
 
+// ---- GEMM1 activations: act(gate) * up ---------------------------------------
+// silu(g) = g / (1 + e^-g); gelu(g) = g/2 * (1 + erf(g / sqrt 2)) (erf form).
+// A clamp c > 0 first limits the gate to <= c and the up value to [-c, c].
+// Kinds: 0 silu, 1 silu with clamp, 2 gelu (cl = +inf without a clamp).
+enum : int { kActSilu = 0, kActGelu = 1 };
+
+template <int KIND>
+__device__ __forceinline__ float gated_act_k(float g, float u, float cl) {
+  if constexpr (KIND == 0) {
+    return g / (1.0f + __expf(-g)) * u;
+  } else {
+    g = fminf(g, cl);
+    u = fminf(fmaxf(u, -cl), cl);
+    if constexpr (KIND == 1) return g / (1.0f + __expf(-g)) * u;
+    return 0.5f * g * (1.0f + erff(g * 0.7071067811865476f)) * u;
+  }
+}
+
+__host__ __device__ __forceinline__ int act_kind(int act, float clamp) {
+  return act == kActGelu ? 2 : (clamp > 0.0f ? 1 : 0);
+}
+
+__host__ __device__ __forceinline__ float act_limit(float clamp) {
+  return clamp > 0.0f ? clamp : __builtin_huge_valf();
+}
+
 // Mask of lanes of this wave whose `key` equals this lane's, among lanes with
 // `active` set (0 for an inactive lane).  key must lie in [0, 2^nbits).
 __device__ __forceinline__ uint64_t wave_match(uint32_t key, bool active, int nbits) {
@@ -91,6 +117,8 @@ struct GemmArgs {
   // optional scratch for split reductions (256-byte aligned; NULL: no split)
   void* split_ws = nullptr;
   size_t split_ws_bytes = 0;
+  int act = kActSilu;     // gated only: kActSilu or kActGelu
+  float clamp = 0.0f;     // gated only: > 0 clamps gate and up first
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its
@@ -104,9 +132,11 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
 hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
                           hipStream_t s);
+// x_perm[map[t, j]] = x[t], or bf16(scale[t, j] * x[t]) when scale is given
 hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
-                              void* x_perm, hipStream_t s);
+                              const float* scale, void* x_perm, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s);
+// w == NULL: every weight is 1 (the weights were applied to the inputs)
 hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
                            int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,
                            hipStream_t s);
@@ -116,6 +146,7 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
                                        const void* shared, void* residual, const void* gamma,
                                        float eps, void* out, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s);
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t s);
 
 int device_cu_count();
 

@@ -14,7 +14,9 @@
 //   - the second walk ranks each lane among its peers with a popcount of the
 //     lower-lane mask, so the order within an expert is ascending x.
 // Rows are then gathered token-major: each token row is read once and written
-// to each of its (up to k) local slots with 16-byte accesses.
+// to each of its (up to k) local slots with 16-byte accesses.  With
+// apply_router_weight_on_input (prepare() applies the routing weights to the
+// activations before dispatch) each slot receives bf16(w[t, j] * x[t]).
 #include "moe_common.h"
 
 namespace moe {
@@ -127,10 +129,42 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   }
 }
 
+__global__ __launch_bounds__(256) void gather_scaled_rows_kernel(const uint4* __restrict__ x,
+                                                                 const int32_t* __restrict__ map,
+                                                                 const float* __restrict__ scale,
+                                                                 int64_t T, int k, int H8,
+                                                                 uint4* __restrict__ x_perm) {
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const int32_t* m = map + t * k;
+    const uint4* src = x + t * H8;
+    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
+      const uint4 v = src[c];
+      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+      for (int j = 0; j < k; ++j) {
+        const int32_t r = m[j];
+        if (r < 0) continue;
+        const float w = scale[t * k + j];
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          q[i] = pack_bf16x2(w * bf16_to_f32(static_cast<uint16_t>(p[i] & 0xFFFFu)),
+                             w * bf16_to_f32(static_cast<uint16_t>(p[i] >> 16)));
+        x_perm[static_cast<int64_t>(r) * H8 + c] = uint4{q[0], q[1], q[2], q[3]};
+      }
+    }
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v0, int32_t step) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[i] = v0 + static_cast<int32_t>(i) * step;
+}
+
+__global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
 }
 
 }  // namespace
@@ -152,10 +186,16 @@ hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, in
 }
 
 hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
-                              void* x_perm, hipStream_t s) {
+                              const float* scale, void* x_perm, hipStream_t s) {
   const int64_t blocks = T < 8192 ? T : 8192;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), map, T, k, H / 8, static_cast<uint4*>(x_perm));
+  if (scale)
+    hipLaunchKernelGGL(gather_scaled_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, s, static_cast<const uint4*>(x), map, scale, T, k, H / 8,
+                       static_cast<uint4*>(x_perm));
+  else
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const uint4*>(x), map, T, k, H / 8,
+                       static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 
@@ -163,6 +203,13 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipS
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks > 0 ? blocks : 1)),
                      dim3(256), 0, s, p, n, v0, step);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t s) {
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(fill_u16_kernel, dim3(static_cast<unsigned>(blocks > 0 ? blocks : 1)),
+                     dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

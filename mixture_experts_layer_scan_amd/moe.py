@@ -14,11 +14,12 @@ from typing import Optional
 
 import torch
 
-from ._lib import MoeWeightsC, lib
+from ._lib import MoeLayerOptionsC, MoeWeightsC, lib
 
 SOFTMAX, SIGMOID = 0, 1
 DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4 = 0, 1, 2
-ACT_SILU = 0
+ACT_SILU, ACT_GELU = 0, 1
+_ACT_NAMES = {"silu": ACT_SILU, "gelu": ACT_GELU}
 
 
 class MoeError(RuntimeError):
@@ -48,6 +49,37 @@ def _hold(t: Optional[torch.Tensor], stream) -> None:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
+
+
+def _act(activation) -> int:
+    return _ACT_NAMES[activation] if isinstance(activation, str) else int(activation)
+
+
+def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
+             apply_router_weight_on_input: bool = False, chunk_tokens: int = 0):
+    """moe_layer_options by reference (None when every option is its default)."""
+    act = _act(activation)
+    clamp = 0.0 if activation_clamp is None else float(activation_clamp)
+    if act == ACT_SILU and clamp == 0.0 and not apply_router_weight_on_input and not chunk_tokens:
+        return None
+    return ctypes.byref(MoeLayerOptionsC(act, clamp, int(bool(apply_router_weight_on_input)),
+                                         int(chunk_tokens)))
+
+
+def _weights_arg(expert_weights: Optional[torch.Tensor], T: int, k: int, dev):
+    """(pointer, dtype tag) of finalize's weights; None means unit weights."""
+    if expert_weights is None:
+        return None, DTYPE_F32
+    if expert_weights.dtype == torch.float32:
+        wdt = DTYPE_F32
+    elif expert_weights.dtype == torch.bfloat16:
+        wdt = DTYPE_BF16
+    else:
+        raise TypeError("expert_weights must be float32 or bfloat16")
+    _need(expert_weights, "expert_weights", expert_weights.dtype, device=dev)
+    if expert_weights.numel() != T * k:
+        raise ValueError(f"expert_weights must have T * k = {T * k} elements")
+    return expert_weights.data_ptr(), wdt
 
 
 def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
@@ -142,9 +174,11 @@ def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
                 expert_map: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
                 R_pad: Optional[int] = None, map: Optional[torch.Tensor] = None,
                 offsets: Optional[torch.Tensor] = None, inv: Optional[torch.Tensor] = None,
-                x_perm: Optional[torch.Tensor] = None, want_inv: bool = True, stream=None):
+                x_perm: Optional[torch.Tensor] = None, want_inv: bool = True,
+                x_weights: Optional[torch.Tensor] = None, stream=None):
     """-> dict(map [T,k] int32, offsets [E_l+1] int32, inv [R_pad] int32 or None,
-    x_perm [R_pad, H] bf16 or None, R_pad)."""
+    x_perm [R_pad, H] bf16 or None, R_pad).  x_weights (fp32 [T, k]): each
+    gathered row is scaled by its routing weight (apply_router_weight_on_input)."""
     _need(topk_ids, "topk_ids", torch.int32)
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -171,9 +205,11 @@ def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
     _need(offsets, "offsets", torch.int32, (E_l + 1,), dev)
     if inv is not None:
         _need(inv, "inv", torch.int32, (R_pad,), dev)
+    if x_weights is not None:
+        _need(x_weights, "x_weights", torch.float32, (T, k), dev)
     _check(lib().moe_permute(topk_ids.data_ptr(), _ptr(expert_map), T, k, E, E_l, _ptr(x), H,
                              R_pad, map.data_ptr(), offsets.data_ptr(), _ptr(inv), _ptr(x_perm),
-                             None, 0, _stream(stream)), "moe_permute")
+                             _ptr(x_weights), None, 0, _stream(stream)), "moe_permute")
     return {"map": map, "offsets": offsets, "inv": inv, "x_perm": x_perm, "R_pad": R_pad}
 
 
@@ -200,10 +236,12 @@ def _gemm_workspace(R_pad: int, N_out: int, gated: bool, split: bool, dev, strea
 
 
 def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weights, I: int,
-                          h: Optional[torch.Tensor] = None, activation: int = ACT_SILU,
+                          h: Optional[torch.Tensor] = None, activation=ACT_SILU,
                           stream=None, split: bool = True,
-                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """h[r] = silu(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I].
+                          workspace: Optional[torch.Tensor] = None,
+                          activation_clamp: Optional[float] = None) -> torch.Tensor:
+    """h[r] = act(a_perm[r] W1g[e]^T) * (a_perm[r] W1u[e]^T) -> bf16 [R_pad, I]
+    (act "silu" or "gelu"; activation_clamp > 0 clamps gate and up first).
 
     workspace: uint8 scratch (moe_grouped_gemm_workspace_size bytes) that lets
     few-row calls split the reduction; without one, split=True allocates it."""
@@ -218,8 +256,10 @@ def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weigh
     _need(h, "h", torch.bfloat16, (R_pad, I), dev)
     ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
     _check(lib().moe_grouped_gemm1_act(a_perm.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I,
-                                       w1.ref(), activation, h.data_ptr(), ws, ws_bytes,
-                                       _stream(stream)), "moe_grouped_gemm1_act")
+                                       w1.ref(), _act(activation),
+                                       0.0 if activation_clamp is None else float(activation_clamp),
+                                       h.data_ptr(), ws, ws_bytes, _stream(stream)),
+           "moe_grouped_gemm1_act")
     return h
 
 
@@ -242,10 +282,11 @@ def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: in
     return y
 
 
-def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor, map: torch.Tensor,
-                 rsf_fin: float = 1.0, shared: Optional[torch.Tensor] = None,
+def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: Optional[torch.Tensor],
+                 map: torch.Tensor, rsf_fin: float = 1.0, shared: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out[t] = rsf_fin * sum_{map>=0} w * Y[map] + shared[t] -> bf16 [T, H]."""
+    """out[t] = rsf_fin * sum_{map>=0} w * Y[map] + shared[t] -> bf16 [T, H]
+    (expert_weights None: every weight 1, as after apply_router_weight_on_input)."""
     _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16)
     if gemm2_permuted.dim() != 2:
         raise ValueError("gemm2_permuted must be rank-2")
@@ -255,27 +296,19 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor, map
     if map.dim() != 2:
         raise ValueError("map must be [T, k]")
     T, k = map.shape
-    if expert_weights.dtype == torch.float32:
-        wdt = DTYPE_F32
-    elif expert_weights.dtype == torch.bfloat16:
-        wdt = DTYPE_BF16
-    else:
-        raise ValueError("expert_weights must be float32 or bfloat16")
-    _need(expert_weights, "expert_weights", expert_weights.dtype, device=dev)
-    if expert_weights.numel() != T * k:
-        raise ValueError(f"expert_weights must have T * k = {T * k} elements")
+    w_ptr, wdt = _weights_arg(expert_weights, T, k, dev)
     if shared is not None:
         _need(shared, "shared", torch.bfloat16, (T, H), dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
-    _check(lib().moe_finalize(gemm2_permuted.data_ptr(), expert_weights.data_ptr(), wdt,
+    _check(lib().moe_finalize(gemm2_permuted.data_ptr(), w_ptr, wdt,
                               map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
                               out.data_ptr(), _stream(stream)), "moe_finalize")
     return out
 
 
-def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch.Tensor,
+def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: Optional[torch.Tensor],
                              map: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
                              eps: float = 1e-6, rsf_fin: float = 1.0,
                              shared: Optional[torch.Tensor] = None,
@@ -291,13 +324,7 @@ def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch
     if map.dim() != 2:
         raise ValueError("map must be [T, k]")
     T, k = map.shape
-    if expert_weights.dtype == torch.float32:
-        wdt = DTYPE_F32
-    elif expert_weights.dtype == torch.bfloat16:
-        wdt = DTYPE_BF16
-    else:
-        raise TypeError("expert_weights must be float32 or bfloat16")
-    _need(expert_weights, "expert_weights", expert_weights.dtype, (T, k), dev)
+    w_ptr, wdt = _weights_arg(expert_weights, T, k, dev)
     _need(residual, "residual", torch.bfloat16, (T, H), dev)
     _need(gamma, "gamma", torch.bfloat16, (H,), dev)
     if shared is not None:
@@ -305,7 +332,7 @@ def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: torch
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
-    _check(lib().moe_finalize_add_rmsnorm(gemm2_permuted.data_ptr(), expert_weights.data_ptr(), wdt,
+    _check(lib().moe_finalize_add_rmsnorm(gemm2_permuted.data_ptr(), w_ptr, wdt,
                                           map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
                                           residual.data_ptr(), gamma.data_ptr(), float(eps),
                                           out.data_ptr(), _stream(stream)),
@@ -330,7 +357,9 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
                                   workspace: Optional[torch.Tensor] = None,
                                   gemm2_permuted: Optional[torch.Tensor] = None,
                                   expert_weights: Optional[torch.Tensor] = None,
-                                  map: Optional[torch.Tensor] = None, stream=None):
+                                  map: Optional[torch.Tensor] = None, stream=None,
+                                  activation=ACT_SILU, activation_clamp: Optional[float] = None,
+                                  apply_router_weight_on_input: bool = False):
     """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k])."""
     _need(logits, "logits", torch.float32)
     _need(x, "x", torch.bfloat16, device=logits.device)
@@ -354,7 +383,9 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts_unfinalized(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
-        float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), R_pad, gemm2_permuted.data_ptr(),
+        float(rsf), _ptr(expert_map), w1.ref(), w2.ref(),
+        _options(activation, activation_clamp, apply_router_weight_on_input), R_pad,
+        gemm2_permuted.data_ptr(),
         expert_weights.data_ptr(), map.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts_unfinalized")
     return gemm2_permuted, expert_weights, map
@@ -365,8 +396,14 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
                       expert_map: Optional[torch.Tensor] = None,
                       ws1: Optional[torch.Tensor] = None, ws2: Optional[torch.Tensor] = None,
                       rsf_fin: float = 1.0, out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is])."""
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      activation=ACT_SILU, activation_clamp: Optional[float] = None,
+                      apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
+                      inplace: bool = False) -> torch.Tensor:
+    """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is]).
+
+    chunk_tokens > 0 runs it over chunks of that many tokens with a workspace
+    sized for one chunk; inplace writes the output over x."""
     _need(logits, "logits", torch.float32)
     _need(x, "x", torch.bfloat16, device=logits.device)
     T, E = logits.shape
@@ -382,17 +419,22 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
             raise ValueError("shared weights must be ws1 [2*Is, H] and ws2 [H, Is]")
     if expert_map is not None:
         _need(expert_map, "expert_map", torch.int32, (E,), dev)
-    if out is None:
+    if inplace:
+        out = x
+    elif out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
     nbytes = 0
     if T > 0:
-        nbytes = (moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) +
-                  moe_shared_workspace_size(T, H, shared_I))
+        P = min(T, chunk_tokens) if chunk_tokens > 0 else T
+        nbytes = (moe_workspace_size(P, k, E, w1.E_l, H, I, w1.dtype) +
+                  moe_shared_workspace_size(P, H, shared_I))
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), shared_I, _ptr(ws1), _ptr(ws2),
-        float(rsf_fin), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
+        float(rsf_fin),
+        _options(activation, activation_clamp, apply_router_weight_on_input, chunk_tokens),
+        out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts")
     return out

@@ -79,13 +79,13 @@ def test_route_errors(L):
 def test_permute_errors(L):
     f = L.moe_permute
     # R_pad < T * k
-    assert f(P, None, 16, 2, 8, 8, P, 128, 31, P, P, P, P, None, 0, None) == SIZE
+    assert f(P, None, 16, 2, 8, 8, P, 128, 31, P, P, P, P, None, None, 0, None) == SIZE
     # no expert map but E_l != E
-    assert f(P, None, 16, 2, 8, 4, P, 128, 32, P, P, P, P, None, 0, None) == INVALID
+    assert f(P, None, 16, 2, 8, 4, P, 128, 32, P, P, P, P, None, None, 0, None) == INVALID
     # H not a multiple of 8 with a gather
-    assert f(P, None, 16, 2, 8, 8, P, 100, 32, P, P, P, P, None, 0, None) == INVALID
+    assert f(P, None, 16, 2, 8, 8, P, 100, 32, P, P, P, P, None, None, 0, None) == INVALID
     # x_perm overlapping x
-    assert f(P, None, 16, 2, 8, 8, P, 128, 32, P, P, P, P + 64, None, 0, None) == CONFLICT
+    assert f(P, None, 16, 2, 8, 8, P, 128, 32, P, P, P, P + 64, None, None, 0, None) == CONFLICT
 
 
 def _w(dtype=0, data=P, scales=None):
@@ -94,14 +94,16 @@ def _w(dtype=0, data=P, scales=None):
 
 def test_gemm_errors(L):
     g1 = L.moe_grouped_gemm1_act
-    assert g1(P, P, 8, 128, 100, 256, _w(), 0, P * 64, None, 0, None) == INVALID  # H % 64
-    assert g1(P, P, 8, 128, 128, 256, _w(), 3, P * 64, None, 0, None) == UNSUPPORTED
-    assert g1(P, P, 8, 128, 128, 256, _w(9), 0, P * 64, None, 0, None) == UNSUPPORTED
-    assert g1(P, P, 8, 128, 128, 256, None, 0, P * 64, None, 0, None) == INVALID
-    assert g1(P, P, 8, 128, 128, 256, _w(2, P, None), 0, P * 64, None, 0, None) == INVALID  # MXFP4, no scales
-    assert g1(P, P, 8, 128, 128, 256, _w(0, P, P), 0, P * 64, None, 0, None) == INVALID  # bf16 with scales
-    assert g1(P, P, 8, 128, 128, 256, _w(), 0, P, None, 0, None) == CONFLICT  # h == a_perm
-    assert g1(P, P, 0, 128, 128, 256, _w(), 0, P * 64, None, 0, None) == INVALID  # E_l = 0
+    assert g1(P, P, 8, 128, 100, 256, _w(), 0, 0.0, P * 64, None, 0, None) == INVALID  # H % 64
+    assert g1(P, P, 8, 128, 128, 256, _w(), 3, 0.0, P * 64, None, 0, None) == UNSUPPORTED
+    assert g1(P, P, 8, 128, 128, 256, _w(9), 0, 0.0, P * 64, None, 0, None) == UNSUPPORTED
+    assert g1(P, P, 8, 128, 128, 256, None, 0, 0.0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, 8, 128, 128, 256, _w(2, P, None), 0, 0.0, P * 64, None, 0, None) == INVALID  # MXFP4, no scales
+    assert g1(P, P, 8, 128, 128, 256, _w(0, P, P), 0, 0.0, P * 64, None, 0, None) == INVALID  # bf16 with scales
+    assert g1(P, P, 8, 128, 128, 256, _w(), 0, 0.0, P, None, 0, None) == CONFLICT  # h == a_perm
+    assert g1(P, P, 0, 128, 128, 256, _w(), 0, 0.0, P * 64, None, 0, None) == INVALID  # E_l = 0
+    assert g1(P, P, 8, 128, 128, 256, _w(), 1, -0.5, P * 64, None, 0, None) == INVALID  # clamp < 0
+    assert g1(P, P, 8, 128, 128, 256, _w(), 2, 0.0, P * 64, None, 0, None) == UNSUPPORTED
     g2 = L.moe_grouped_gemm2
     assert g2(P, P, 8, 128, 256, 130, _w(), P * 64, None, 0, None) == INVALID
     # one expert's weights over 4 GiB cannot be addressed
@@ -140,7 +142,8 @@ def test_finalize_add_rmsnorm_errors(L):
 def test_fused_errors(L):
     u = L.moe_fused_experts_unfinalized
     args = dict(logits=P, x=P, T=16, H=128, I=256, E=8, El=8, k=2, score=0, renorm=1, rsf=1.0,
-                emap=None, w1=_w(), w2=_w(), R_pad=32, y=P, w=P, m=P, ws=P, wsb=1 << 30, s=None)
+                emap=None, w1=_w(), w2=_w(), opts=None, R_pad=32, y=P, w=P, m=P, ws=P,
+                wsb=1 << 30, s=None)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -153,6 +156,40 @@ def test_fused_errors(L):
     assert call(w1=_w(7, P, P)) == UNSUPPORTED
     assert call(El=4) == INVALID  # no map, E_l != E
     assert call(T=0) == OK
+    assert call(opts=_opts(activation=2)) == UNSUPPORTED
+    assert call(opts=_opts(clamp=-1.0)) == INVALID
+    assert call(opts=_opts(clamp=float("nan"))) == INVALID
+    assert call(opts=_opts(clamp=float("inf"))) == INVALID
+    assert call(opts=_opts(weight_on_input=1)) == INVALID  # needs top_k = 1
+    assert b"top_k = 1" in L.moe_last_error()
+    assert call(opts=_opts(chunk=-4)) == INVALID
+    assert call(opts=_opts(chunk=8)) == INVALID  # the deferred form takes no chunking
+
+
+def _opts(activation=0, clamp=0.0, weight_on_input=0, chunk=0):
+    return ctypes.byref(_lib.MoeLayerOptionsC(activation, clamp, weight_on_input, chunk))
+
+
+def test_fused_finalized_errors(L):
+    f = L.moe_fused_experts
+    X, OUT = P * 1024, P * 2048
+    args = dict(logits=P, x=X, T=16, H=128, I=256, E=8, El=8, k=2, score=0, renorm=1, rsf=1.0,
+                emap=None, w1=_w(), w2=_w(), sI=0, ws1=None, ws2=None, rsf_fin=1.0, opts=None,
+                out=OUT, ws=P * 4096, wsb=1 << 30, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call(out=X + 256) == CONFLICT          # partly over x
+    assert b"x itself" in L.moe_last_error()
+    assert call(ws=X) == CONFLICT                 # workspace over x
+    assert call(opts=_opts(weight_on_input=1)) == INVALID
+    assert call(k=1, opts=_opts(weight_on_input=1), wsb=16) == SIZE
+    # chunking sizes the workspace for one chunk: 16 tokens in chunks of 4
+    n4 = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(4, 2, 8, 8, 128, 256, 0, ctypes.byref(n4)) == OK
+    assert call(opts=_opts(chunk=4), wsb=n4.value - 256) == SIZE
+    assert call(T=0, opts=_opts(chunk=4)) == OK
 
 
 def test_grouped_gemm_workspace_size():
