@@ -59,6 +59,8 @@ def _load():
         L.oracle_route.argtypes = [vp, i64, i32, i32, i32, i32, dbl, vp, vp]
         L.oracle_permute.restype = ctypes.c_int
         L.oracle_permute.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
+        L.oracle_permute_batched.restype = ctypes.c_int
+        L.oracle_permute_batched.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp]
         L.oracle_hidden_rows.restype = None
         L.oracle_hidden_rows.argtypes = [vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
         L.oracle_out_rows.restype = None
@@ -160,6 +162,22 @@ def permute(ids: np.ndarray, E: int, E_l: int, expert_map: Optional[np.ndarray] 
     if rc != 0:
         raise ValueError("expert id out of range")
     return m, offsets, counts[:E_l]
+
+
+def permute_batched(ids: np.ndarray, E: int, E_l: int, max_tokens: int,
+                    expert_map: Optional[np.ndarray] = None):
+    """Batched experts format -> (map int32 [T, k] into rows [E_l * max_tokens],
+    counts int32 [E_l]).  Routes past an expert's capacity get -1."""
+    ids = _c(ids, np.int32)
+    expert_map = _c(expert_map, np.int32)
+    T, k = ids.shape
+    m = np.empty((T, k), dtype=np.int32)
+    counts = np.empty(max(E_l, 1), dtype=np.int32)
+    rc = _load().oracle_permute_batched(_p(ids), _p(expert_map), T, k, E, E_l, max_tokens, _p(m),
+                                        _p(counts))
+    if rc != 0:
+        raise ValueError("expert id out of range")
+    return m, counts[:E_l]
 
 
 def hidden_rows(a_bf16: np.ndarray, w1: Weights, expert_of_row: np.ndarray, I: int,

@@ -171,6 +171,36 @@ int oracle_permute(const int32_t* ids, const int32_t* expert_map, int64_t T, int
   return 0;
 }
 
+/* ---- Permute into the batched experts format ([MOD] FusedMoEActivationFormat
+ * BatchedExperts: activations laid out as (local experts, max tokens per
+ * expert, hidden); prepare returns the per-local-expert token counts with
+ * them; _moe_problem_size reads M = max_num_tokens from that layout) ---------
+ * Expert L's rows are [L * max_tokens, (L + 1) * max_tokens).  Walking the
+ * expanded index x = t*k + j upward, the n-th route to L (n = 0, 1, ...) goes
+ * to row L * max_tokens + n while n < max_tokens; a route past that capacity,
+ * or to an expert that is not local, gets -1.  counts[L] = all routes to L
+ * (it exceeds max_tokens exactly when routes were dropped).  Returns 0, or -1
+ * on an id outside [0, E) or a local id outside [-1, E_l). */
+int oracle_permute_batched(const int32_t* ids, const int32_t* expert_map, int64_t T, int32_t k,
+                           int32_t E, int32_t E_l, int32_t max_tokens, int32_t* map,
+                           int32_t* counts) {
+  int64_t R = T * k;
+  for (int e = 0; e < E_l; ++e) counts[e] = 0;
+  for (int64_t x = 0; x < R; ++x) {
+    int32_t id = ids[x];
+    if (id < 0 || id >= E) return -1;
+    int32_t L = expert_map ? expert_map[id] : id;
+    if (L < -1 || L >= E_l) return -1;
+    if (L < 0) {
+      map[x] = -1;
+      continue;
+    }
+    map[x] = counts[L] < max_tokens ? L * max_tokens + counts[L] : -1;
+    counts[L] += 1;
+  }
+  return 0;
+}
+
 /* ---- Experts ([MOD] apply: GEMM1, activation, GEMM2, unweighted; activation:
  * the output is half the width of the input, "silu" gives
  * silu(first half) * second half and "gelu" gelu(first half) * second half;
