@@ -3,7 +3,8 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--tokens T]
                     [--activation silu|gelu] [--activation-clamp C] [--top-k K]
-                    [--router-weight-on-input] [--chunk-tokens N] [--fused-tail] [--graph]
+                    [--router-weight-on-input] [--chunk-tokens N] [--batched-max-tokens M]
+                    [--fused-tail] [--graph]
 
 One step is the whole hot path on one batch of synthetic input already
 resident in HBM: route -> permute (map, offsets, row gather) -> grouped GEMM1
@@ -22,9 +23,10 @@ bf16 weights.  The other workloads:
 
 Variants of a workload (each named in config.workload): GELU instead of SiLU,
 an activation clamp, another top_k, the routing weight applied to the input
-rows (top_k 1), and activation chunking (the layer over consecutive chunks of
-N tokens with buffers sized for one chunk; every chunk re-streams the weights
-of its experts).
+rows (top_k 1), activation chunking (the layer over consecutive chunks of N
+tokens with buffers sized for one chunk; every chunk re-streams the weights of
+its experts), and the batched experts format (rows laid out per local expert
+with a capacity of M tokens each).
 
 Prints one JSON line: tokens/s (value), algorithmic TFLOP/s, the roofline of
 the dominant kernel (grouped GEMM1) from HIP events recorded around each of its
@@ -76,6 +78,8 @@ def parse():
                    help="apply the routing weights to the input rows (top_k 1 only)")
     p.add_argument("--chunk-tokens", type=int, default=0,
                    help="run the layer over chunks of this many tokens")
+    p.add_argument("--batched-max-tokens", type=int, default=0,
+                   help="use the batched experts format with this capacity per local expert")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -216,6 +220,8 @@ def main():
         label += "_weight_on_input"
     if args.chunk_tokens and args.chunk_tokens < cfg.T:
         label += f"_chunk{args.chunk_tokens}"
+    if args.batched_max_tokens:
+        label += f"_batched{args.batched_max_tokens}"
     variant = {"activation": args.activation, "clamp": args.activation_clamp,
                "weight_on_input": args.router_weight_on_input}
     w = configs.make_weights(cfg)
@@ -234,7 +240,8 @@ def main():
     T, H, I, k, E, El = cfg.T, cfg.H, cfg.I, cfg.k, cfg.E, cfg.El
     P = min(T, args.chunk_tokens) if args.chunk_tokens > 0 else T  # tokens per pass
     chunks = [(t0, min(P, T - t0)) for t0 in range(0, T, P)]
-    R_pad = moe.moe_permuted_rows(P, k)
+    Mb = args.batched_max_tokens
+    R_pad = El * Mb if Mb else moe.moe_permuted_rows(P, k)
     dev = "cuda"
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -273,33 +280,60 @@ def main():
     act_kw = dict(activation=args.activation, activation_clamp=args.activation_clamp)
     w_in = args.router_weight_on_input
 
+    counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
+
+    def permute(sl, st):
+        if Mb:
+            moe.moe_permute_batched(ids[sl], E, Mb, El, emap_d, xd_cur[0][sl], pmap[sl], counts_b,
+                                    x_perm.view(El, Mb, H), wts[sl] if w_in else None, stream=st)
+        else:
+            moe.moe_permute(ids[sl], E, El, emap_d, xd_cur[0][sl], R_pad, pmap[sl], offsets, None,
+                            x_perm, want_inv=False, x_weights=wts[sl] if w_in else None,
+                            stream=st)
+
+    def gemms(n, st):
+        if Mb:
+            moe.moe_grouped_gemm1_act_batched(x_perm.view(El, Mb, H), counts_b, W1, I,
+                                              h.view(El, Mb, I), max_rows=n * k, stream=st,
+                                              split=False, workspace=split_ws, **act_kw)
+            mark_cur[0]("gemm2")
+            moe.moe_grouped_gemm2_batched(h.view(El, Mb, I), counts_b, W2, H, y.view(El, Mb, H),
+                                          max_rows=n * k, stream=st, split=False,
+                                          workspace=split_ws)
+        else:
+            moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
+                                      workspace=split_ws, **act_kw)
+            mark_cur[0]("gemm2")
+            moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False,
+                                  workspace=split_ws)
+
+    xd_cur, mark_cur = [None], [None]
+
     def route_permute(d, t0, n):
         xd, ld = dev_draws[d]
+        xd_cur[0] = xd
         sl = slice(t0, t0 + n)
         moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                            stream)
-        moe.moe_permute(ids[sl], E, El, emap_d, xd[sl], R_pad, pmap[sl], offsets, None, x_perm,
-                        want_inv=False, x_weights=wts[sl] if w_in else None, stream=stream)
+        permute(sl, stream)
+
+    def chunk_counts():
+        return counts_b.cpu().numpy().clip(0, Mb) if Mb else np.diff(offsets.cpu().numpy())
 
     def layer(d, st, mark=lambda name: None):
         """The layer on input batch d, enqueued on stream st, one pass per
         chunk; mark(name) records the start of stage `name` (None: the end)."""
         xd, ld = dev_draws[d]
+        xd_cur[0], mark_cur[0] = xd, mark
         for t0, n in chunks:
             sl = slice(t0, t0 + n)
             mark("route")
             moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                                st)
             mark("permute")
-            moe.moe_permute(ids[sl], E, El, emap_d, xd[sl], R_pad, pmap[sl], offsets, None,
-                            x_perm, want_inv=False, x_weights=wts[sl] if w_in else None,
-                            stream=st)
+            permute(sl, st)
             mark("gemm1")
-            moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
-                                      workspace=split_ws, **act_kw)
-            mark("gemm2")
-            moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False,
-                                  workspace=split_ws)
+            gemms(n, st)
             sh = None
             if cfg.shared_I:
                 mark("shared")
@@ -390,7 +424,7 @@ def main():
         per_chunk = []
         for t0, n in chunks:
             route_permute(d, t0, n)
-            per_chunk.append(np.diff(offsets.cpu().numpy()))
+            per_chunk.append(chunk_counts())
         draw_counts.append(per_chunk)
     step_counts = [draw_counts[i % len(dev_draws)] for i in range(args.steps)]
 
@@ -459,7 +493,8 @@ def main():
                             f"{len(draws)} routing draws" if decode else "finalized")
                            + (", replayed as a captured HIP graph" if graphs else "")
                            + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")
-                           + (f", {len(chunks)} chunks of {P} tokens" if len(chunks) > 1 else ""),
+                           + (f", {len(chunks)} chunks of {P} tokens" if len(chunks) > 1 else "")
+                           + (f", batched experts format ({Mb} rows per expert)" if Mb else ""),
                    "activation": args.activation
                                  + (f", clamp {args.activation_clamp:g}" if args.activation_clamp else "")
                                  + (", routing weight on the input" if w_in else "")},

@@ -104,12 +104,21 @@ enum { MOE_ACT_SILU = 0, MOE_ACT_GELU = 1 };
  *                     many tokens, reusing one workspace sized for a chunk
  *                     (the activation chunking of forward(), page
  *                     "modular_kernel.py").  The deferred form takes no
- *                     chunking: chunk_tokens must be 0 or >= T there. */
+ *                     chunking: chunk_tokens must be 0 or >= T there.
+ *   batched_max_tokens 0: the standard permuted layout.  > 0: the batched
+ *                     experts format (page "modular_kernel.py",
+ *                     FusedMoEActivationFormat.BatchedExperts) with this many
+ *                     rows per local expert, as moe_permute_batched lays out;
+ *                     the deferred form's gemm2_permuted then has
+ *                     E_l * batched_max_tokens rows (R_pad at least that), and
+ *                     routes past an expert's capacity are dropped (map -1).
+ *                     A capacity of T never drops a route. */
 typedef struct moe_layer_options {
   int32_t activation;
   float activation_clamp;
   int32_t apply_router_weight_on_input;
   int32_t chunk_tokens;
+  int32_t batched_max_tokens;
 } moe_layer_options;
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
@@ -136,13 +145,16 @@ const char* moe_last_error(void);
  * (page "moe_output.py": the padded row count is never referenced). */
 int64_t moe_permuted_rows(int64_t T, int32_t k);
 
-/* Workspace bytes moe_fused_experts and moe_fused_experts_unfinalized need
- * for this problem; the workspace of moe_permute needs no more.  Host-only
- * arithmetic.  Returns MOE_ERR_INVALID_ARGUMENT on bad sizes.  Mirrors
- * FusedMoEPermuteExpertsUnpermute.workspace_shapes (page "modular_kernel.py"):
- * the caller allocates, the library reuses. */
+/* Workspace bytes moe_fused_experts (shared expert of intermediate shared_I,
+ * 0 for none) and moe_fused_experts_unfinalized (shared_I = 0) need for this
+ * problem with these options (NULL: defaults): sized for one chunk when
+ * chunking, for E_l * batched_max_tokens rows in the batched experts format.
+ * Host-only arithmetic.  Returns MOE_ERR_INVALID_ARGUMENT on bad sizes.
+ * Mirrors FusedMoEPermuteExpertsUnpermute.workspace_shapes (page
+ * "modular_kernel.py"): the caller allocates, the library reuses. */
 int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, int32_t I,
-                       int32_t w_dtype, size_t* bytes);
+                       int32_t w_dtype, int32_t shared_I, const moe_layer_options* options,
+                       size_t* bytes);
 
 /* Router ([Router] stage).  For each token t the k experts with the largest
  * logits, ordered by logit descending, ties to the smaller expert id, and
@@ -191,6 +203,28 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
                 int32_t* offsets, int32_t* inv, void* x_perm, const float* x_weights,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Permute into the batched experts format (page "modular_kernel.py":
+ * FusedMoEActivationFormat.BatchedExperts, activations laid out as (local
+ * experts, max tokens per expert, hidden), with the per-local-expert token
+ * counts that prepare() returns as expert_num_tokens).
+ *   Expert L owns rows [L * max_tokens, (L + 1) * max_tokens).  Walking the
+ *   expanded index t*k+j upward, the n-th route to L takes row
+ *   L * max_tokens + n while n < max_tokens; a route past that capacity, or
+ *   to an expert that is not local, gets map -1.
+ *   expert_num_tokens[L] = all routes to L (above max_tokens exactly when
+ *   routes were dropped); the GEMMs use min(expert_num_tokens[L], max_tokens).
+ *   x_batched[map[t,j], :] = x[t, :] (or bf16(x_weights[t,j] * x[t, :])); rows
+ *   past an expert's count are not written.
+ *   topk_ids, expert_map, x, x_weights: as for moe_permute
+ *   map               (device) int32 [T, k] out
+ *   expert_num_tokens (device) int32 [E_l] out (written even for T = 0)
+ *   x_batched         (device) bf16 [E_l, max_tokens, H] out, or NULL
+ * Limits: E_l * max_tokens < 2^31, H a multiple of 8. */
+int moe_permute_batched(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                        int32_t E, int32_t E_l, const void* x, int32_t H, int32_t max_tokens,
+                        int32_t* map, int32_t* expert_num_tokens, void* x_batched,
+                        const float* x_weights, void* stream);
+
 /* Grouped GEMM1 + activation (apply() and activation() of page
  * "modular_kernel.py").  For every local expert e and row r in
  * [offsets[e], offsets[e+1]):
@@ -229,6 +263,28 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                       int32_t I, int32_t H, const moe_weights* w2, void* y, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* The two grouped GEMMs in the batched experts format (apply() of page
+ * "modular_kernel.py" with its expert_num_tokens): the same arithmetic as
+ * moe_grouped_gemm1_act / moe_grouped_gemm2 on expert e's rows
+ * [e * max_tokens, e * max_tokens + min(expert_num_tokens[e], max_tokens)).
+ *   a_batched / h_batched / y_batched  (device) bf16 [E_l, max_tokens, H or I]
+ *   expert_num_tokens  (device) int32 [E_l]
+ *   max_rows   an upper bound on the rows to compute that the caller knows
+ *              (T * top_k), or 0 for E_l * max_tokens; it only picks the tile
+ *              shape
+ *   workspace  as for the standard calls, with
+ *              moe_grouped_gemm_workspace_size(E_l * max_tokens, ...) bytes
+ * Rows past an expert's count are neither read nor written. */
+int moe_grouped_gemm1_act_batched(const void* a_batched, const int32_t* expert_num_tokens,
+                                  int32_t E_l, int32_t max_tokens, int64_t max_rows, int32_t H,
+                                  int32_t I, const moe_weights* w1, int32_t activation,
+                                  float activation_clamp, void* h_batched, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+int moe_grouped_gemm2_batched(const void* h_batched, const int32_t* expert_num_tokens,
+                              int32_t E_l, int32_t max_tokens, int64_t max_rows, int32_t I,
+                              int32_t H, const moe_weights* w2, void* y_batched, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Fused tail on one GPU: finalize, the shared-expert add, the residual add
  * and the next layer's RMSNorm in one pass (page "moe_output.py", MoEOutput:
@@ -287,7 +343,8 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
  *   expert_weights  (device) bf16 [T, k] out (the activation dtype, since this
  *                   call routes itself), rsf already applied
  *   map             (device) int32 [T, k] out (-1 = expert not local)
- *   workspace       (device) >= moe_workspace_size() bytes, 256-byte aligned
+ *   workspace       (device) >= moe_workspace_size(..., 0, options) bytes,
+ *                   256-byte aligned
  * A deferred call takes no destination for the finalized output; pass the
  * three buffers to moe_finalize (weights_dtype MOE_DTYPE_BF16) later. */
 int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
@@ -307,9 +364,7 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
  *   options   moe_layer_options or NULL (SiLU, no clamp, one pass)
  *   out       (device) bf16 [T, H]; either x itself (in place, forward()'s
  *             inplace of page "modular_kernel.py") or not overlapping x
- *   workspace (device) >= moe_workspace_size() + moe_shared_workspace_size()
- *             bytes (the latter 0 without a shared expert), both taken for
- *             min(T, chunk_tokens) tokens when chunking */
+ *   workspace (device) >= moe_workspace_size(..., shared_I, options) bytes */
 int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
                       int32_t E, int32_t E_l, int32_t k, int32_t score_fn, int32_t renormalize,
                       float rsf, const int32_t* expert_map, const moe_weights* w1,

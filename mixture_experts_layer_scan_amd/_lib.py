@@ -21,7 +21,7 @@ class MoeWeightsC(ctypes.Structure):
 class MoeLayerOptionsC(ctypes.Structure):
     _fields_ = [("activation", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("apply_router_weight_on_input", ctypes.c_int32),
-                ("chunk_tokens", ctypes.c_int32)]
+                ("chunk_tokens", ctypes.c_int32), ("batched_max_tokens", ctypes.c_int32)]
 
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -32,7 +32,7 @@ PROTOTYPES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_permuted_rows": (_i64, [_i64, _i32]),
-    "moe_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
+    "moe_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _Op,
                                           ctypes.POINTER(_sz)]),
     "moe_shared_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
@@ -40,6 +40,12 @@ PROTOTYPES = {
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _f32,
                                              _vp, _vp, _sz, _vp]),
+    "moe_permute_batched": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32,
+                                           _vp, _vp, _vp, _vp, _vp]),
+    "moe_grouped_gemm1_act_batched": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64, _i32, _i32, _Wp,
+                                                     _i32, _f32, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm2_batched": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64, _i32, _i32, _Wp,
+                                                 _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm2": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _vp, _vp, _sz,
                                          _vp]),
     "moe_finalize_add_rmsnorm": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp,

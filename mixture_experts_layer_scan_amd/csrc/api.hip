@@ -145,13 +145,59 @@ struct Carve {
   }
 };
 
+int check_activation(int32_t activation, float clamp) {
+  if (activation != MOE_ACT_SILU && activation != MOE_ACT_GELU)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
+  if (!(clamp >= 0.0f) || clamp > 3.0e38f)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "activation_clamp must be finite and >= 0");
+  return MOE_OK;
+}
+
+// Options of the fused entry points, checked.
+struct LayerOpts {
+  int act = MOE_ACT_SILU;
+  float clamp = 0.0f;
+  bool weight_on_input = false;
+  int64_t chunk = 0;  // 0: one pass
+  int batch_m = 0;    // > 0: batched experts format with this capacity
+};
+
+int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
+  *out = LayerOpts{};
+  if (!o) return MOE_OK;
+  MOE_CHECK(check_activation(o->activation, o->activation_clamp));
+  if (o->apply_router_weight_on_input && k != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "apply_router_weight_on_input needs top_k = 1 (k=%d)", k);
+  if (o->chunk_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "chunk_tokens must be >= 0");
+  out->act = o->activation;
+  out->clamp = o->activation_clamp;
+  out->weight_on_input = o->apply_router_weight_on_input != 0;
+  out->chunk = o->chunk_tokens;
+  if (o->batched_max_tokens < 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "batched_max_tokens must be >= 0");
+  out->batch_m = o->batched_max_tokens;
+  return MOE_OK;
+}
+
+// Tokens per pass: all T, or the chunk size when it is smaller.
+int64_t pass_tokens(int64_t T, const LayerOpts& o) {
+  return (o.chunk > 0 && o.chunk < T) ? o.chunk : T;
+}
+
 // split-reduction scratch shared by the two routed GEMMs (one after the other)
 size_t routed_split_bytes(int64_t R_pad, int32_t H, int32_t I) {
   return std::max(moe::gemm_split_ws_bytes(R_pad, 2 * I), moe::gemm_split_ws_bytes(R_pad, H));
 }
 
-size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) {
-  const int64_t R_pad = moe_permuted_rows(T, k);
+// Permuted rows of a pass of T tokens: round_up(T * k, 128), or E_l
+// capacity blocks in the batched experts format.
+int64_t routed_rows(int64_t T, int32_t k, int32_t E_l, int batch_m) {
+  return batch_m > 0 ? int64_t(E_l) * batch_m : moe_permuted_rows(T, k);
+}
+
+size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, int batch_m) {
+  const int64_t R_pad = routed_rows(T, k, E_l, batch_m);
   size_t b = 0;
   b += align_up(sizeof(int32_t) * T * k);               // topk ids
   b += align_up(sizeof(float) * T * k);                 // topk weights
@@ -189,7 +235,8 @@ int64_t moe_permuted_rows(int64_t T, int32_t k) {
 }
 
 int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, int32_t I,
-                       int32_t w_dtype, size_t* bytes) {
+                       int32_t w_dtype, int32_t shared_I, const moe_layer_options* options,
+                       size_t* bytes) {
   g_err[0] = 0;
   MOE_CHECK(check_route_sizes(T, E, k));
   MOE_CHECK(check_local(E, E_l));
@@ -197,7 +244,12 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4)
     return fail(MOE_ERR_UNSUPPORTED, "unknown weight dtype %d", w_dtype);
   if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
-  *bytes = routed_ws_bytes(T, k, E_l, H, I);
+  LayerOpts o;
+  MOE_CHECK(parse_options(options, k, &o));
+  const int64_t P = pass_tokens(T, o);
+  size_t shared_bytes = 0;
+  MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
+  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m) + shared_bytes;
   return MOE_OK;
 }
 
@@ -268,18 +320,52 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
   return MOE_OK;
 }
 
-static int check_activation(int32_t activation, float clamp) {
-  if (activation != MOE_ACT_SILU && activation != MOE_ACT_GELU)
-    return fail(MOE_ERR_UNSUPPORTED, "unknown activation %d", activation);
-  if (!(clamp >= 0.0f) || clamp > 3.0e38f)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "activation_clamp must be finite and >= 0");
+int check_capacity(int32_t E_l, int32_t max_tokens) {
+  if (max_tokens <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_tokens must be positive");
+  if (int64_t(E_l) * max_tokens >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "E_l * max_tokens must fit in int32");
+  return MOE_OK;
+}
+
+int moe_permute_batched(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                        int32_t E, int32_t E_l, const void* x, int32_t H, int32_t max_tokens,
+                        int32_t* map, int32_t* expert_num_tokens, void* x_batched,
+                        const float* x_weights, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  MOE_CHECK(check_capacity(E_l, max_tokens));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  if (x_batched && (H <= 0 || H % 8)) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8 (H=%d)", H);
+  MOE_CHECK(need_ptr(expert_num_tokens, "expert_num_tokens"));
+  MOE_CHECK(opt_ptr(x_batched, "x_batched"));
+  MOE_CHECK(opt_ptr(x_weights, "x_weights"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(map, "map"));
+    if (x_batched) MOE_CHECK(need_ptr(x, "x"));
+  }
+  const int64_t rows = int64_t(E_l) * max_tokens;
+  if (x_batched && overlap(x, sizeof(uint16_t) * T * H, x_batched, sizeof(uint16_t) * rows * H))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "x_batched must not overlap x");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the counts are written even for T = 0
+  hipError_t e = moe::launch_permute(topk_ids, expert_map, T, k, E, E_l, map, expert_num_tokens,
+                                     nullptr, rows, s, max_tokens);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_batched");
+  if (x_batched && T > 0) {
+    e = moe::launch_gather_rows(x, map, T, k, H, x_weights, x_batched, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_batched gather");
+  }
   return MOE_OK;
 }
 
 static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                        int32_t K, int32_t N_out, int gated, int act, float clamp,
                        const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
-                       void* stream, const char* name) {
+                       void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
@@ -299,8 +385,9 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
       return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: workspace must not overlap the rows", name);
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
-                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp};
-  hipError_t e = moe::launch_grouped_gemm(g, R_pad, static_cast<hipStream_t>(stream));
+                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m};
+  const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
+  hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
 }
 
@@ -322,6 +409,36 @@ int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_
   MOE_CHECK(check_gemm_dims(H, I));
   return gemm_common(h, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
                      workspace_bytes, stream, "moe_grouped_gemm2");
+}
+
+int moe_grouped_gemm1_act_batched(const void* a_batched, const int32_t* expert_num_tokens,
+                                  int32_t E_l, int32_t max_tokens, int64_t max_rows, int32_t H,
+                                  int32_t I, const moe_weights* w1, int32_t activation,
+                                  float activation_clamp, void* h_batched, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "E_l must be in [1, 1024]");
+  MOE_CHECK(check_capacity(E_l, max_tokens));
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_rows must be >= 0");
+  return gemm_common(a_batched, expert_num_tokens, E_l, int64_t(E_l) * max_tokens, H, I, 1,
+                     activation, activation_clamp, w1, h_batched, workspace, workspace_bytes,
+                     stream, "moe_grouped_gemm1_act_batched", max_tokens, max_rows);
+}
+
+int moe_grouped_gemm2_batched(const void* h_batched, const int32_t* expert_num_tokens,
+                              int32_t E_l, int32_t max_tokens, int64_t max_rows, int32_t I,
+                              int32_t H, const moe_weights* w2, void* y_batched, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "E_l must be in [1, 1024]");
+  MOE_CHECK(check_capacity(E_l, max_tokens));
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_rows must be >= 0");
+  return gemm_common(h_batched, expert_num_tokens, E_l, int64_t(E_l) * max_tokens, I, H, 0,
+                     MOE_ACT_SILU, 0.0f, w2, y_batched, workspace, workspace_bytes, stream,
+                     "moe_grouped_gemm2_batched", max_tokens, max_rows);
 }
 
 int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated, size_t* bytes) {
@@ -398,7 +515,8 @@ int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t we
 }
 
 // Workspace of the routed part of the fused entry points (rows sized for
-// moe_permuted_rows(T, k); the GEMMs never touch rows past the local routes).
+// moe_permuted_rows(T, k), or E_l capacity blocks in the batched experts
+// format; the GEMMs never touch rows past the local routes).
 struct RoutedWs {
   int32_t* ids;
   float* wts;
@@ -411,46 +529,19 @@ struct RoutedWs {
   int64_t rows;
 };
 
-static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I) {
+static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I,
+                             int batch_m) {
   RoutedWs b;
-  b.rows = moe_permuted_rows(T, k);
+  b.rows = routed_rows(T, k, E_l, batch_m);
   b.ids = c.take<int32_t>(T * k);
   b.wts = c.take<float>(T * k);
   b.map = c.take<int32_t>(T * k);
-  b.offsets = c.take<int32_t>(E_l + 1);
+  b.offsets = c.take<int32_t>(E_l + 1);  // offsets, or per-expert counts when batched
   b.x_perm = c.take<uint16_t>(b.rows * H);
   b.h = c.take<uint16_t>(b.rows * I);
   b.split_bytes = routed_split_bytes(b.rows, H, I);
   b.split = b.split_bytes ? c.take<char>(b.split_bytes) : nullptr;
   return b;
-}
-
-// Options of the fused entry points, checked.
-struct LayerOpts {
-  int act = MOE_ACT_SILU;
-  float clamp = 0.0f;
-  bool weight_on_input = false;
-  int64_t chunk = 0;  // 0: one pass
-};
-
-static int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
-  *out = LayerOpts{};
-  if (!o) return MOE_OK;
-  MOE_CHECK(check_activation(o->activation, o->activation_clamp));
-  if (o->apply_router_weight_on_input && k != 1)
-    return fail(MOE_ERR_INVALID_ARGUMENT,
-                "apply_router_weight_on_input needs top_k = 1 (k=%d)", k);
-  if (o->chunk_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "chunk_tokens must be >= 0");
-  out->act = o->activation;
-  out->clamp = o->activation_clamp;
-  out->weight_on_input = o->apply_router_weight_on_input != 0;
-  out->chunk = o->chunk_tokens;
-  return MOE_OK;
-}
-
-// Tokens per pass: all T, or the chunk size when it is smaller.
-static int64_t pass_tokens(int64_t T, const LayerOpts& o) {
-  return (o.chunk > 0 && o.chunk < T) ? o.chunk : T;
 }
 
 // Route, permute, GEMM1, GEMM2 of T tokens on one stream.  map_out / y_out
@@ -470,17 +561,20 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     e = moe::launch_fill_u16(w_bf16_out, T * k, 0x3F80, s);  // bf16 1.0
     if (e != hipSuccess) return hip_fail(e, "unit weights");
   }
-  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s);
+  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s,
+                          o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");
   e = moe::launch_gather_rows(x, map, T, k, H, o.weight_on_input ? b.wts : nullptr, b.x_perm, s);
   if (e != hipSuccess) return hip_fail(e, "gather");
+  // the tile shape follows the routed rows, the same bound in both formats
+  const int64_t max_rows = std::min(moe_permuted_rows(T, k), b.rows);
   moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
-                   b.split, b.split_bytes, o.act, o.clamp};
-  e = moe::launch_grouped_gemm(g1, b.rows, s);
+                   b.split, b.split_bytes, o.act, o.clamp, o.batch_m};
+  e = moe::launch_grouped_gemm(g1, max_rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm1");
   moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
-                   b.split_bytes};
-  e = moe::launch_grouped_gemm(g2, b.rows, s);
+                   b.split_bytes, moe::kActSilu, 0.0f, o.batch_m};
+  e = moe::launch_grouped_gemm(g2, max_rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm2");
   return MOE_OK;
 }
@@ -488,7 +582,7 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
 static int check_fused_args(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
                             int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
                             const int32_t* expert_map, const moe_weights* w1,
-                            const moe_weights* w2, int64_t pass_T) {
+                            const moe_weights* w2, int64_t pass_T, const LayerOpts& o) {
   MOE_CHECK(check_route_sizes(T, E, k));
   MOE_CHECK(check_local(E, E_l));
   MOE_CHECK(check_gemm_dims(H, I));
@@ -498,7 +592,8 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
     return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
   MOE_CHECK(check_weights(w1, "w1"));
   MOE_CHECK(check_weights(w2, "w2"));
-  const int64_t rows = moe_permuted_rows(pass_T, k);
+  if (o.batch_m > 0) MOE_CHECK(check_capacity(E_l, o.batch_m));
+  const int64_t rows = routed_rows(pass_T, k, E_l, o.batch_m);
   MOE_CHECK(check_gemm_extent(rows, H, 2 * int64_t(I)));
   MOE_CHECK(check_gemm_extent(rows, I, H));
   MOE_CHECK(opt_ptr(expert_map, "expert_map"));
@@ -529,15 +624,21 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   MOE_CHECK(parse_options(options, k, &o));
   if (o.chunk > 0 && o.chunk < T)
     return fail(MOE_ERR_INVALID_ARGUMENT, "the deferred form takes no chunking (chunk_tokens < T)");
-  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, T));
-  MOE_CHECK(check_rpad(T, k, R_pad));
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, T, o));
+  if (o.batch_m > 0) {
+    if (R_pad < int64_t(E_l) * o.batch_m)
+      return fail(MOE_ERR_SIZE_MISMATCH, "R_pad must hold E_l * batched_max_tokens rows");
+  } else {
+    MOE_CHECK(check_rpad(T, k, R_pad));
+  }
   if (T == 0) return MOE_OK;
   MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
   MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
-  MOE_CHECK(check_workspace(workspace, workspace_bytes, routed_ws_bytes(T, k, E_l, H, I)));
+  MOE_CHECK(check_workspace(workspace, workspace_bytes,
+                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m)));
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I);
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
                     o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
                     static_cast<hipStream_t>(stream));
@@ -553,7 +654,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
   LayerOpts o;
   MOE_CHECK(parse_options(options, k, &o));
   const int64_t P = pass_tokens(T, o);  // tokens per pass
-  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, P));
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, P, o));
   if (shared_I < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "shared_I must be >= 0");
   if (shared_I > 0) {
     MOE_CHECK(check_gemm_dims(H, shared_I));
@@ -568,7 +669,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
   }
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  const size_t need = routed_ws_bytes(P, k, E_l, H, I) + shared_bytes;
+  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m) + shared_bytes;
   MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
   // out is x itself (in place) or apart from it; the workspace is apart from both
   const size_t row_bytes = sizeof(uint16_t) * T * H;
@@ -578,7 +679,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     return fail(MOE_ERR_DESTINATION_CONFLICT, "the workspace must not overlap x or out");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, P, k, E_l, H, I);
+  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m);
   int32_t* s_off = nullptr;
   uint16_t* s_h = nullptr;
   uint16_t* s_y = nullptr;

@@ -316,7 +316,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ W,
     const uint8_t* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
-    int s_cap, int* __restrict__ split_out, int act, float clamp) {
+    int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
@@ -356,13 +356,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int wave = tid / kWave;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
+  // Expert e's rows: [offsets[e], offsets[e+1]), or in the batched experts
+  // format [e * batch_m, e * batch_m + min(offsets[e], batch_m)).
+  auto seg_start = [&](int e) -> int { return batch_m > 0 ? e * batch_m : offsets[e]; };
+  auto seg_rows = [&](int e) -> int {
+    return batch_m > 0 ? min(max(offsets[e], 0), batch_m) : offsets[e + 1] - offsets[e];
+  };
+
   // m-tile numbering: s_mt[e] = m-tiles of experts < e.
   {
     const int per = (E_l + NT - 1) / NT;
     int local = 0;
     for (int i = 0; i < per; ++i) {
       const int e = tid * per + i;
-      if (e < E_l) local += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      if (e < E_l) local += (seg_rows(e) + BM - 1) / BM;
     }
     int total_m = 0;
     int run = block_exclusive_sum(local, s_scratch, &total_m);
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       const int e = tid * per + i;
       if (e < E_l) {
         s_mt[e] = run;
-        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+        run += (seg_rows(e) + BM - 1) / BM;
       }
     }
     if (tid == 0) s_mt[E_l] = total_m;
@@ -432,8 +439,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // the tile's expert and rows are the same in every lane: held in scalar
     // registers, so the branches on them below are scalar branches
     const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int seg_end = min(static_cast<int64_t>(offsets[e + 1]), R_pad);
-    const int row0 = __builtin_amdgcn_readfirstlane(offsets[e] + (m_tile - s_mt[e]) * BM);
+    const int s0 = seg_start(e);
+    const int seg_end = min(static_cast<int64_t>(s0) + seg_rows(e), R_pad);
+    const int row0 = __builtin_amdgcn_readfirstlane(s0 + (m_tile - s_mt[e]) * BM);
     const int rows = __builtin_amdgcn_readfirstlane(seg_end - row0);
     if (rows <= 0) continue;
     const int n0 = n_tile * Cfg::OUT_N;
@@ -757,17 +765,25 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 // C[r, n] from the S fp32 slices: y = sum_s P[s, r, n], or for GEMM1
 // h = act(sum_s P[s, r, n]) * sum_s P[s, r, I + n]; the slices are added in
 // order s = 0, 1, ... (the same result on every run).  Rows at or past the
-// local route count are not written.  One thread per 4 output columns.
+// local route count (past an expert's count in the batched experts format)
+// are not written.  One thread per 4 output columns.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials,
                                                            const int* __restrict__ split,
                                                            const int32_t* __restrict__ offsets,
                                                            int E_l, int64_t R_pad, int N_out,
                                                            int gated, int act, float clamp,
+                                                           int batch_m,
                                                            uint16_t* __restrict__ C) {
   const int S = split[0];
   if (S <= 1) return;
   const int64_t r = blockIdx.y;
-  if (r >= offsets[E_l]) return;
+  if (batch_m > 0) {
+    const int e = static_cast<int>(r / batch_m);
+    if (e >= E_l || r - static_cast<int64_t>(e) * batch_m >= min(max(offsets[e], 0), batch_m))
+      return;
+  } else if (r >= offsets[E_l]) {
+    return;
+  }
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= N_out) return;
   const int N_total = gated ? 2 * N_out : N_out;
@@ -836,12 +852,13 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
                      dim3(Cfg::kThreads), 0, s,
                      static_cast<const uint16_t*>(g.a), g.w, g.w_scales, g.offsets, g.E_l, g.K,
                      g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
-                     g.act, g.clamp);
+                     g.act, g.clamp, g.batch_m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));
   hipLaunchKernelGGL(split_reduce_kernel, rgrid, dim3(256), 0, s, partials, hdr, g.offsets, g.E_l,
-                     g.R_pad, g.N_out, g.gated, g.act, g.clamp, static_cast<uint16_t*>(g.c));
+                     g.R_pad, g.N_out, g.gated, g.act, g.clamp, g.batch_m,
+                     static_cast<uint16_t*>(g.c));
   return hipGetLastError();
 }
 

@@ -107,7 +107,7 @@ struct GemmArgs {
   const void* a;          // bf16 [R_pad, K]
   const void* w;          // bf16 [E_l, N_total, K], or packed e2m1 [E_l, N_total, K/2]
   const uint8_t* w_scales;  // NULL (bf16), or E8M0 [E_l, N_total, K/32] (MXFP4)
-  const int32_t* offsets; // [E_l + 1]
+  const int32_t* offsets; // [E_l + 1], or the E_l row counts when batch_m > 0
   int E_l;
   int K;
   int N_out;              // output columns (I when gated, else N)
@@ -119,6 +119,8 @@ struct GemmArgs {
   size_t split_ws_bytes = 0;
   int act = kActSilu;     // gated only: kActSilu or kActGelu
   float clamp = 0.0f;     // gated only: > 0 clamps gate and up first
+  int batch_m = 0;        // > 0: batched experts format, expert e's rows start
+                          // at e * batch_m and number min(offsets[e], batch_m)
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its
@@ -129,9 +131,11 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total);
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score_fn,
                              int renormalize, float rsf, int32_t* ids, float* w,
                              uint16_t* w_bf16, hipStream_t s);
+// batch_m > 0: batched experts format (rows [L * batch_m, ...) per expert,
+// offsets receives the E_l per-expert counts; inv must be NULL)
 hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
-                          hipStream_t s);
+                          hipStream_t s, int batch_m = 0);
 // x_perm[map[t, j]] = x[t], or bf16(scale[t, j] * x[t]) when scale is given
 hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
                               const float* scale, void* x_perm, hipStream_t s);

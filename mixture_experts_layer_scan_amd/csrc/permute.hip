@@ -13,6 +13,9 @@
 //     every (wave, expert) pair its first output row;
 //   - the second walk ranks each lane among its peers with a popcount of the
 //     lower-lane mask, so the order within an expert is ascending x.
+// Batched experts format (batch_m > 0): expert L owns rows [L * batch_m,
+// (L + 1) * batch_m); the same ranks place a route at L * batch_m + rank, or
+// -1 past the capacity, and `offsets` receives the per-expert counts.
 // Rows are then gathered token-major: each token row is read once and written
 // to each of its (up to k) local slots with 16-byte accesses.  With
 // apply_router_weight_on_input (prepare() applies the routing weights to the
@@ -37,7 +40,7 @@ __device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids,
 __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ emap, int64_t R, int E, int E_l,
     int32_t* __restrict__ map, int32_t* __restrict__ offsets, int32_t* __restrict__ inv,
-    int64_t R_pad) {
+    int64_t R_pad, int batch_m) {
   extern __shared__ int32_t smem[];
   int32_t* hist = smem;                                // [waves][E_l]
   int32_t* scratch = smem + kPermuteWaves * E_l;       // 16 ints
@@ -79,11 +82,12 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(
   int total = 0;
   const int start = block_exclusive_sum(e < E_l ? cnt_total : 0, scratch, &total);
   if (e < E_l) {
-    offsets[e] = start;
-    for (int ww = 0; ww < kPermuteWaves; ++ww) hist[ww * E_l + e] += start;
+    const int base = batch_m > 0 ? e * batch_m : start;
+    offsets[e] = batch_m > 0 ? cnt_total : start;
+    for (int ww = 0; ww < kPermuteWaves; ++ww) hist[ww * E_l + e] += base;
   }
   if (threadIdx.x == 0) {
-    offsets[E_l] = total;
+    if (batch_m == 0) offsets[E_l] = total;
     s_total = total;
   }
   __syncthreads();
@@ -97,8 +101,12 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(
     if (valid) {
       if (L >= 0) {
         const int slot = my_hist[L] + __popcll(peers & lt_mask);
-        map[x] = slot;
-        if (inv) inv[slot] = static_cast<int32_t>(x);
+        if (batch_m > 0 && slot - L * batch_m >= batch_m) {
+          map[x] = -1;  // past the expert's capacity
+        } else {
+          map[x] = slot;
+          if (inv) inv[slot] = static_cast<int32_t>(x);
+        }
       } else {
         map[x] = -1;
       }
@@ -171,7 +179,7 @@ __global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
 
 hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
-                          hipStream_t s) {
+                          hipStream_t s, int batch_m) {
   const size_t lds = sizeof(int32_t) * (static_cast<size_t>(kPermuteWaves) * E_l + 16);
   static bool attr_set = false;
   if (!attr_set) {
@@ -181,7 +189,7 @@ hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, in
     attr_set = true;
   }
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermuteThreads), lds, s, ids, emap, T * k, E,
-                     E_l, map, offsets, inv, R_pad);
+                     E_l, map, offsets, inv, R_pad, batch_m);
   return hipGetLastError();
 }
 

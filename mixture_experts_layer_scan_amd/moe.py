@@ -56,14 +56,16 @@ def _act(activation) -> int:
 
 
 def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
-             apply_router_weight_on_input: bool = False, chunk_tokens: int = 0):
+             apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
+             batched_max_tokens: int = 0):
     """moe_layer_options by reference (None when every option is its default)."""
     act = _act(activation)
     clamp = 0.0 if activation_clamp is None else float(activation_clamp)
-    if act == ACT_SILU and clamp == 0.0 and not apply_router_weight_on_input and not chunk_tokens:
+    if (act == ACT_SILU and clamp == 0.0 and not apply_router_weight_on_input
+            and not chunk_tokens and not batched_max_tokens):
         return None
     return ctypes.byref(MoeLayerOptionsC(act, clamp, int(bool(apply_router_weight_on_input)),
-                                         int(chunk_tokens)))
+                                         int(chunk_tokens), int(batched_max_tokens)))
 
 
 def _weights_arg(expert_weights: Optional[torch.Tensor], T: int, k: int, dev):
@@ -135,9 +137,12 @@ def moe_permuted_rows(T: int, k: int) -> int:
 
 
 def moe_workspace_size(T: int, k: int, E: int, E_l: int, H: int, I: int,
-                       w_dtype: int = DTYPE_BF16) -> int:
+                       w_dtype: int = DTYPE_BF16, shared_I: int = 0, chunk_tokens: int = 0,
+                       batched_max_tokens: int = 0) -> int:
+    """Workspace bytes of the fused calls (the shared expert's included)."""
     n = ctypes.c_size_t(0)
-    _check(lib().moe_workspace_size(T, k, E, E_l, H, I, w_dtype, ctypes.byref(n)),
+    opts = _options(chunk_tokens=chunk_tokens, batched_max_tokens=batched_max_tokens)
+    _check(lib().moe_workspace_size(T, k, E, E_l, H, I, w_dtype, shared_I, opts, ctypes.byref(n)),
            "moe_workspace_size")
     return int(n.value)
 
@@ -213,6 +218,93 @@ def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
     return {"map": map, "offsets": offsets, "inv": inv, "x_perm": x_perm, "R_pad": R_pad}
 
 
+def moe_permute_batched(topk_ids: torch.Tensor, E: int, max_tokens: int, E_l: Optional[int] = None,
+                        expert_map: Optional[torch.Tensor] = None,
+                        x: Optional[torch.Tensor] = None, map: Optional[torch.Tensor] = None,
+                        expert_num_tokens: Optional[torch.Tensor] = None,
+                        x_batched: Optional[torch.Tensor] = None,
+                        x_weights: Optional[torch.Tensor] = None, stream=None):
+    """Batched experts format -> dict(map [T,k] int32, expert_num_tokens [E_l]
+    int32, x_batched [E_l, max_tokens, H] bf16 or None)."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    E_l = E if E_l is None else E_l
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    H = 0
+    if x is not None:
+        _need(x, "x", torch.bfloat16, device=dev)
+        if x.dim() != 2 or x.shape[0] != T:
+            raise ValueError("x must be [T, H]")
+        H = x.shape[1]
+        if x_batched is None:
+            x_batched = torch.empty((E_l, max_tokens, H), dtype=torch.bfloat16, device=dev)
+        _need(x_batched, "x_batched", torch.bfloat16, (E_l, max_tokens, H), dev)
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if expert_num_tokens is None:
+        expert_num_tokens = torch.empty((E_l,), dtype=torch.int32, device=dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    _need(expert_num_tokens, "expert_num_tokens", torch.int32, (E_l,), dev)
+    if x_weights is not None:
+        _need(x_weights, "x_weights", torch.float32, (T, k), dev)
+    _check(lib().moe_permute_batched(topk_ids.data_ptr(), _ptr(expert_map), T, k, E, E_l, _ptr(x),
+                                     H, max_tokens, map.data_ptr(), expert_num_tokens.data_ptr(),
+                                     _ptr(x_batched), _ptr(x_weights), _stream(stream)),
+           "moe_permute_batched")
+    return {"map": map, "expert_num_tokens": expert_num_tokens, "x_batched": x_batched}
+
+
+def _batched_in(a: torch.Tensor, name: str):
+    _need(a, name, torch.bfloat16)
+    if a.dim() != 3:
+        raise ValueError(f"{name} must be [E_l, max_tokens, K]")
+    return a.shape
+
+
+def moe_grouped_gemm1_act_batched(a_batched: torch.Tensor, expert_num_tokens: torch.Tensor,
+                                  w1: Weights, I: int, h_batched: Optional[torch.Tensor] = None,
+                                  activation=ACT_SILU, activation_clamp: Optional[float] = None,
+                                  max_rows: int = 0, stream=None, split: bool = True,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM1 + activation in the batched experts format -> bf16 [E_l, max_tokens, I]."""
+    E_l, M, H = _batched_in(a_batched, "a_batched")
+    dev = a_batched.device
+    _need(expert_num_tokens, "expert_num_tokens", torch.int32, (E_l,), dev)
+    if w1.E_l != E_l or w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l={E_l}, 2I={2 * I}, H={H}]")
+    if h_batched is None:
+        h_batched = torch.empty((E_l, M, I), dtype=torch.bfloat16, device=dev)
+    _need(h_batched, "h_batched", torch.bfloat16, (E_l, M, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(E_l * M, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_batched(
+        a_batched.data_ptr(), expert_num_tokens.data_ptr(), E_l, M, max_rows, H, I, w1.ref(),
+        _act(activation), 0.0 if activation_clamp is None else float(activation_clamp),
+        h_batched.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_batched")
+    return h_batched
+
+
+def moe_grouped_gemm2_batched(h_batched: torch.Tensor, expert_num_tokens: torch.Tensor,
+                              w2: Weights, H: int, y_batched: Optional[torch.Tensor] = None,
+                              max_rows: int = 0, stream=None, split: bool = True,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM2 in the batched experts format -> bf16 [E_l, max_tokens, H]."""
+    E_l, M, I = _batched_in(h_batched, "h_batched")
+    dev = h_batched.device
+    _need(expert_num_tokens, "expert_num_tokens", torch.int32, (E_l,), dev)
+    if w2.E_l != E_l or w2.N != H or w2.K != I:
+        raise ValueError(f"w2 must be [E_l={E_l}, H={H}, I={I}]")
+    if y_batched is None:
+        y_batched = torch.empty((E_l, M, H), dtype=torch.bfloat16, device=dev)
+    _need(y_batched, "y_batched", torch.bfloat16, (E_l, M, H), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(E_l * M, H, False, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm2_batched(
+        h_batched.data_ptr(), expert_num_tokens.data_ptr(), E_l, M, max_rows, I, H, w2.ref(),
+        y_batched.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_batched")
+    return y_batched
+
+
 def moe_grouped_gemm_workspace_size(R_pad: int, N_out: int, gated: bool) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().moe_grouped_gemm_workspace_size(R_pad, N_out, int(bool(gated)), ctypes.byref(n)),
@@ -286,8 +378,11 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: Optional[torch.Te
                  map: torch.Tensor, rsf_fin: float = 1.0, shared: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """out[t] = rsf_fin * sum_{map>=0} w * Y[map] + shared[t] -> bf16 [T, H]
-    (expert_weights None: every weight 1, as after apply_router_weight_on_input)."""
+    (expert_weights None: every weight 1, as after apply_router_weight_on_input).
+    gemm2_permuted may be [R, H] or batched [E_l, max_tokens, H]."""
     _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16)
+    if gemm2_permuted.dim() == 3:
+        gemm2_permuted = gemm2_permuted.view(-1, gemm2_permuted.shape[2])
     if gemm2_permuted.dim() != 2:
         raise ValueError("gemm2_permuted must be rank-2")
     H = gemm2_permuted.shape[1]
@@ -359,15 +454,18 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
                                   expert_weights: Optional[torch.Tensor] = None,
                                   map: Optional[torch.Tensor] = None, stream=None,
                                   activation=ACT_SILU, activation_clamp: Optional[float] = None,
-                                  apply_router_weight_on_input: bool = False):
-    """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k])."""
+                                  apply_router_weight_on_input: bool = False,
+                                  batched_max_tokens: int = 0):
+    """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k]).
+    batched_max_tokens > 0: batched experts format, R_pad = E_l * batched_max_tokens."""
     _need(logits, "logits", torch.float32)
     _need(x, "x", torch.bfloat16, device=logits.device)
     T, E = logits.shape
     H = x.shape[1]
     I = w2.K
     dev = x.device
-    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    if R_pad is None:
+        R_pad = w1.E_l * batched_max_tokens if batched_max_tokens else moe_permuted_rows(T, k)
     if gemm2_permuted is None:
         gemm2_permuted = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     if expert_weights is None:
@@ -379,12 +477,14 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
     _need(map, "map", torch.int32, (T, k), dev)
     if expert_map is not None:
         _need(expert_map, "expert_map", torch.int32, (E,), dev)
-    nbytes = moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype) if T > 0 else 0
+    nbytes = (moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype,
+                                 batched_max_tokens=batched_max_tokens) if T > 0 else 0)
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts_unfinalized(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(),
-        _options(activation, activation_clamp, apply_router_weight_on_input), R_pad,
+        _options(activation, activation_clamp, apply_router_weight_on_input, 0,
+                 batched_max_tokens), R_pad,
         gemm2_permuted.data_ptr(),
         expert_weights.data_ptr(), map.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts_unfinalized")
@@ -399,7 +499,7 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
                       workspace: Optional[torch.Tensor] = None, stream=None,
                       activation=ACT_SILU, activation_clamp: Optional[float] = None,
                       apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
-                      inplace: bool = False) -> torch.Tensor:
+                      inplace: bool = False, batched_max_tokens: int = 0) -> torch.Tensor:
     """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is]).
 
     chunk_tokens > 0 runs it over chunks of that many tokens with a workspace
@@ -426,15 +526,15 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
     _need(out, "out", torch.bfloat16, (T, H), dev)
     nbytes = 0
     if T > 0:
-        P = min(T, chunk_tokens) if chunk_tokens > 0 else T
-        nbytes = (moe_workspace_size(P, k, E, w1.E_l, H, I, w1.dtype) +
-                  moe_shared_workspace_size(P, H, shared_I))
+        nbytes = moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype, shared_I, chunk_tokens,
+                                    batched_max_tokens)
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), shared_I, _ptr(ws1), _ptr(ws2),
         float(rsf_fin),
-        _options(activation, activation_clamp, apply_router_weight_on_input, chunk_tokens),
+        _options(activation, activation_clamp, apply_router_weight_on_input, chunk_tokens,
+                 batched_max_tokens),
         out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts")
     return out

@@ -40,9 +40,9 @@ def test_permuted_rows(L):
     assert L.moe_permuted_rows(4096, 2) == 8192
 
 
-def _ws(L, T, k, E, El, H, I, dt=0):
+def _ws(L, T, k, E, El, H, I, dt=0, sI=0, opts=None):
     n = ctypes.c_size_t(0)
-    s = L.moe_workspace_size(T, k, E, El, H, I, dt, ctypes.byref(n))
+    s = L.moe_workspace_size(T, k, E, El, H, I, dt, sI, opts, ctypes.byref(n))
     return s, n.value
 
 
@@ -56,6 +56,18 @@ def test_workspace_size(L):
     assert _ws(L, 16, 2, 8, 8, 100, 256)[0] == INVALID      # H not a multiple of 64
     assert _ws(L, 16, 2, 8, 9, 128, 256)[0] == INVALID      # E_l > E
     assert _ws(L, 16, 2, 8, 8, 128, 256, 7)[0] == UNSUPPORTED
+    # the shared expert's part, chunking and the batched experts format
+    s0, n0 = _ws(L, 2048, 8, 256, 256, 7168, 2048)
+    s1, n1 = _ws(L, 2048, 8, 256, 256, 7168, 2048, sI=2048)
+    ns = ctypes.c_size_t(0)
+    assert L.moe_shared_workspace_size(2048, 7168, 2048, ctypes.byref(ns)) == OK
+    assert s1 == OK and n1 == n0 + ns.value
+    _, n512 = _ws(L, 512, 8, 256, 256, 7168, 2048)
+    assert _ws(L, 2048, 8, 256, 256, 7168, 2048, opts=_opts(chunk=512)) == (OK, n512)
+    assert _ws(L, 2048, 8, 256, 256, 7168, 2048, opts=_opts(chunk=4096)) == (OK, n0)
+    s, nb = _ws(L, 64, 8, 256, 32, 7168, 2048, opts=_opts(batched=64))
+    assert s == OK and nb >= 32 * 64 * (7168 + 2048) * 2
+    assert _ws(L, 64, 8, 256, 32, 7168, 2048, opts=_opts(batched=-1))[0] == INVALID
     n = ctypes.c_size_t(0)
     assert L.moe_shared_workspace_size(2048, 7168, 0, ctypes.byref(n)) == OK and n.value == 0
     assert L.moe_shared_workspace_size(2048, 7168, 2048, ctypes.byref(n)) == OK
@@ -166,8 +178,8 @@ def test_fused_errors(L):
     assert call(opts=_opts(chunk=8)) == INVALID  # the deferred form takes no chunking
 
 
-def _opts(activation=0, clamp=0.0, weight_on_input=0, chunk=0):
-    return ctypes.byref(_lib.MoeLayerOptionsC(activation, clamp, weight_on_input, chunk))
+def _opts(activation=0, clamp=0.0, weight_on_input=0, chunk=0, batched=0):
+    return ctypes.byref(_lib.MoeLayerOptionsC(activation, clamp, weight_on_input, chunk, batched))
 
 
 def test_fused_finalized_errors(L):
@@ -187,9 +199,33 @@ def test_fused_finalized_errors(L):
     assert call(k=1, opts=_opts(weight_on_input=1), wsb=16) == SIZE
     # chunking sizes the workspace for one chunk: 16 tokens in chunks of 4
     n4 = ctypes.c_size_t(0)
-    assert L.moe_workspace_size(4, 2, 8, 8, 128, 256, 0, ctypes.byref(n4)) == OK
+    assert L.moe_workspace_size(4, 2, 8, 8, 128, 256, 0, 0, None, ctypes.byref(n4)) == OK
     assert call(opts=_opts(chunk=4), wsb=n4.value - 256) == SIZE
     assert call(T=0, opts=_opts(chunk=4)) == OK
+
+
+def test_batched_errors(L):
+    pb = L.moe_permute_batched
+    # (ids, emap, T, k, E, E_l, x, H, max_tokens, map, counts, x_batched, x_weights, stream)
+    assert pb(P, None, 16, 2, 8, 8, P, 128, 0, P, P, P * 64, None, None) == INVALID  # capacity 0
+    assert pb(P, None, 16, 2, 8, 8, P, 128, 1 << 28, P, P, P * 64, None, None) == INVALID
+    assert pb(P, None, 16, 2, 8, 4, P, 128, 16, P, P, P * 64, None, None) == INVALID  # no map
+    assert pb(P, None, 16, 2, 8, 8, P, 100, 16, P, P, P * 64, None, None) == INVALID  # H % 8
+    assert pb(P, None, 16, 2, 8, 8, P, 128, 16, P, None, P * 64, None, None) == INVALID
+    assert pb(P, None, 16, 2, 8, 8, P, 128, 16, P, P, P + 64, None, None) == CONFLICT
+    g1 = L.moe_grouped_gemm1_act_batched
+    # (a, counts, E_l, M, max_rows, H, I, w1, act, clamp, h, ws, wsb, stream)
+    assert g1(P, P, 8, 0, 0, 128, 256, _w(), 0, 0.0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, 8, 16, -1, 128, 256, _w(), 0, 0.0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, 8, 16, 0, 128, 256, _w(), 5, 0.0, P * 64, None, 0, None) == UNSUPPORTED
+    assert g1(P, P, 8, 16, 0, 128, 256, _w(), 0, 0.0, P, None, 0, None) == CONFLICT
+    g2 = L.moe_grouped_gemm2_batched
+    assert g2(P, P, 8, 16, 0, 256, 130, _w(), P * 64, None, 0, None) == INVALID
+    assert g2(P, P, 0, 16, 0, 256, 128, _w(), P * 64, None, 0, None) == INVALID
+    u = L.moe_fused_experts_unfinalized
+    # deferred batched: R_pad must hold E_l * capacity rows
+    assert u(P, P, 16, 128, 256, 8, 8, 2, 0, 1, 1.0, None, _w(), _w(), _opts(batched=16), 127,
+             P, P, P, P, 1 << 30, None) == SIZE
 
 
 def test_grouped_gemm_workspace_size():

@@ -180,8 +180,9 @@ def test_chunked_layer(case):
     kw = dict(ws1=W["ws1"], ws2=W["ws2"]) if shared_I else {}
     xd, ld = dev_bf16(x), dev(logits)
     one = moe.moe_fused_experts(ld, xd, W["w1"], W["w2"], k, **kw)
-    ws_chunk = moe.moe_workspace_size(chunk, k, E, E, H, I) + moe.moe_shared_workspace_size(
-        chunk, H, shared_I)
+    ws_chunk = moe.moe_workspace_size(T, k, E, E, H, I, shared_I=shared_I, chunk_tokens=chunk)
+    assert ws_chunk == (moe.moe_workspace_size(chunk, k, E, E, H, I)
+                        + moe.moe_shared_workspace_size(chunk, H, shared_I))
     ws = torch.empty(ws_chunk, dtype=torch.uint8, device="cuda")
     chunked = moe.moe_fused_experts(ld, xd, W["w1"], W["w2"], k, chunk_tokens=chunk,
                                     workspace=ws, **kw)
