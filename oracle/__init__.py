@@ -21,7 +21,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 SOFTMAX, SIGMOID = 0, 1
-W_BF16, W_MXFP4 = 0, 1
+W_BF16, W_MXFP4, W_FP8 = 0, 1, 2
 ACTIVATIONS = {"silu": 0, "gelu": 1}
 
 
@@ -63,6 +63,16 @@ def _load():
         L.oracle_permute_batched.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp]
         L.oracle_hidden_rows.restype = None
         L.oracle_hidden_rows.argtypes = [vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
+        L.oracle_e4m3_decode.restype = dbl
+        L.oracle_e4m3_decode.argtypes = [u8]
+        L.oracle_e4m3_encode.restype = u8
+        L.oracle_e4m3_encode.argtypes = [dbl]
+        L.oracle_quantize_fp8_rows.restype = None
+        L.oracle_quantize_fp8_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.oracle_hidden_rows_fp8.restype = None
+        L.oracle_hidden_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
+        L.oracle_out_rows_fp8.restype = None
+        L.oracle_out_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_out_rows.restype = None
         L.oracle_out_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_finalize.restype = None
@@ -72,7 +82,8 @@ def _load():
                                                   vp, vp]
         L.oracle_moe_tokens.restype = None
         L.oracle_moe_tokens.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dbl, vp, Wp, Wp,
-                                        i64, vp, vp, dbl, i32, dbl, i32, vp, i64, vp, vp, vp, vp]
+                                        i64, vp, vp, dbl, i32, dbl, i32, i32, vp, vp, vp, i64, vp,
+                                        vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         _lib = L
@@ -93,14 +104,19 @@ def _p(a: Optional[np.ndarray]):
 
 
 class Weights:
-    """Expert weights in bf16 bits ([rows, K] uint16) or MXFP4 (packed uint8
-    [rows, K/2] + E8M0 uint8 [rows, K/32]).  Keeps the arrays alive."""
+    """Expert weights in bf16 bits ([rows, K] uint16), MXFP4 (packed uint8
+    [rows, K/2] + E8M0 uint8 [rows, K/32]) or FP8 E4M3 (uint8 [rows, K] + one
+    float32 scale per row).  Keeps the arrays alive."""
 
     def __init__(self, data: np.ndarray, scales: Optional[np.ndarray] = None):
         if scales is None:
             self.data = _c(data, np.uint16)
             self.scales = None
             self.fmt = W_BF16
+        elif scales.dtype == np.float32:
+            self.data = _c(data, np.uint8)
+            self.scales = _c(scales, np.float32)
+            self.fmt = W_FP8
         else:
             self.data = _c(data, np.uint8)
             self.scales = _c(scales, np.uint8)
@@ -180,6 +196,51 @@ def permute_batched(ids: np.ndarray, E: int, E_l: int, max_tokens: int,
     return m, counts[:E_l]
 
 
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def quantize_fp8_rows(x_bf16: np.ndarray, static_scale: Optional[float] = None):
+    """Per-row FP8 E4M3 quantization of bf16 rows -> (codes uint8 [rows, H],
+    scales float32 [rows]); static_scale: one given scale for every row."""
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    q = np.empty((rows, H), dtype=np.uint8)
+    sc = np.empty(rows, dtype=np.float32)
+    st = None if static_scale is None else np.array([static_scale], dtype=np.float32)
+    _load().oracle_quantize_fp8_rows(_p(x), rows, H, _p(st), _p(q), _p(sc))
+    return q, sc
+
+
+def hidden_rows_fp8(aq: np.ndarray, a_scales: np.ndarray, w1: Weights, expert_of_row: np.ndarray,
+                    I: int, activation: str = "silu", clamp: float = 0.0) -> np.ndarray:
+    """hidden_rows on FP8 rows (decoded as code * row scale), float64 [rows, I]."""
+    aq = _c(aq, np.uint8)
+    sc = _c(a_scales, np.float32)
+    eor = _c(expert_of_row.astype(np.int32), np.int32)
+    rows, H = aq.shape
+    h = np.empty((rows, I), dtype=np.float64)
+    _load().oracle_hidden_rows_fp8(_p(aq), _p(sc), rows, H, I, w1.ref, _p(eor),
+                                   ACTIVATIONS[activation], float(clamp), _p(h))
+    return h
+
+
+def out_rows_fp8(hq: np.ndarray, h_scales: np.ndarray, w2: Weights, expert_of_row: np.ndarray,
+                 H: int) -> np.ndarray:
+    """out_rows on FP8 rows, float64 [rows, H]."""
+    hq = _c(hq, np.uint8)
+    sc = _c(h_scales, np.float32)
+    eor = _c(expert_of_row.astype(np.int32), np.int32)
+    rows, I = hq.shape
+    y = np.empty((rows, H), dtype=np.float64)
+    _load().oracle_out_rows_fp8(_p(hq), _p(sc), rows, I, H, w2.ref, _p(eor), _p(y))
+    return y
+
+
 def hidden_rows(a_bf16: np.ndarray, w1: Weights, expert_of_row: np.ndarray, I: int,
                 activation: str = "silu", clamp: float = 0.0) -> np.ndarray:
     """h[r] = act(W1g[e_r] a_r) * (W1u[e_r] a_r), float64 [rows, I]; act is
@@ -242,11 +303,15 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
                expert_map: Optional[np.ndarray] = None, shared_I: int = 0,
                ws1: Optional[np.ndarray] = None, ws2: Optional[np.ndarray] = None,
                rsf_fin: float = 1.0, tokens: Optional[Sequence[int]] = None,
-               activation: str = "silu", clamp: float = 0.0, weight_on_input: bool = False):
+               activation: str = "silu", clamp: float = 0.0, weight_on_input: bool = False,
+               fp8: bool = False, a1_scale: Optional[float] = None,
+               a2_scale: Optional[float] = None):
     """The whole layer for the listed tokens (all when None).  activation and
     clamp as for hidden_rows (every expert, the shared one included);
     weight_on_input: the routing weight scales the token before its expert
-    MLP instead of the MLP's output (top_k = 1).
+    MLP instead of the MLP's output (top_k = 1).  fp8: the routed experts see
+    their input and hidden rows quantized per row to FP8 E4M3 (static
+    a1_scale / a2_scale when given).
 
     Returns dict: out float64 [n, H], y_routes float64 [n, k, H] (unweighted
     per-route expert outputs, zero when not local), ids int32 [n, k],
@@ -265,9 +330,11 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
     expert_map = _c(expert_map, np.int32)
     ws1 = _c(ws1, np.uint16)
     ws2 = _c(ws2, np.uint16)
+    s1 = None if a1_scale is None else np.array([a1_scale], dtype=np.float32)
+    s2 = None if a2_scale is None else np.array([a2_scale], dtype=np.float32)
     _load().oracle_moe_tokens(_p(x), H, I, _p(logits), E, k, score, int(bool(renormalize)), rsf,
                               _p(expert_map), w1.ref, w2.ref, shared_I, _p(ws1), _p(ws2),
                               rsf_fin, ACTIVATIONS[activation], float(clamp),
-                              int(bool(weight_on_input)), _p(tok), n, _p(out), _p(y), _p(ids),
-                              _p(w))
+                              int(bool(weight_on_input)), int(bool(fp8)), _p(s1), _p(s2), _p(tok),
+                              n, _p(out), _p(y), _p(ids), _p(w))
     return {"out": out, "y_routes": y, "ids": ids, "weights": w, "tokens": tok}

@@ -31,13 +31,13 @@
 #include <string.h>
 
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
-enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1 };
+enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1, OR_W_FP8 = 2 };
 enum { OR_ACT_SILU = 0, OR_ACT_GELU = 1 };
 
 typedef struct {
-  int32_t fmt;            /* OR_W_BF16 or OR_W_MXFP4 */
-  const void* data;       /* bf16 [rows, K] or packed e2m1 [rows, K/2] */
-  const uint8_t* scales;  /* E8M0 [rows, K/32] (MXFP4 only) */
+  int32_t fmt;            /* OR_W_BF16, OR_W_MXFP4 or OR_W_FP8 */
+  const void* data;       /* bf16 [rows, K], packed e2m1 [rows, K/2] or e4m3 [rows, K] */
+  const void* scales;     /* E8M0 u8 [rows, K/32] (MXFP4) or fp32 [rows] (FP8, per row) */
 } oracle_weights;
 
 static double bf16_val(uint16_t h) {
@@ -45,6 +45,14 @@ static double bf16_val(uint16_t h) {
   float f;
   memcpy(&f, &u, 4);
   return (double)f;
+}
+
+/* float -> bf16 bits, round to nearest even (finite inputs). */
+static uint16_t bf16_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
 }
 
 /* ---- MXFP4 decode ([EP] _E2M1_LUT and _dequant_fp4_ue8m0_gran32) ----------
@@ -68,10 +76,82 @@ double oracle_mxfp4_value(const uint8_t* packed, const uint8_t* scales, int64_t 
   return kE2M1[code] * oracle_e8m0_scale(scales[row * (K / 32) + kk / 32]);
 }
 
-/* Weight element (row, kk) of a [rows, K] matrix in either storage format. */
+/* ---- FP8 E4M3 (the OCP 8-bit float with 4 exponent bits, bias 7, 3 mantissa
+ * bits, no infinities, S.1111.111 = NaN; largest finite 448): the FP8 type of
+ * the quantized activations of [MOD] prepare / apply (quant_dtype, a1_scale,
+ * a2_scale, w1_scale, w2_scale; the pages name no layout, this one is the
+ * MI355X matrix cores') --------------------------------------------------------
+ * decode: exponent field e, mantissa m: e = 0 -> m * 2^-9; else
+ * (1 + m/8) * 2^(e-7). */
+double oracle_e4m3_decode(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return (c & 0x80) ? -mag : mag;
+}
+
+/* encode: the nearest e4m3 value, ties to the even code; |v| >= 448 gives
+ * +-448 (saturation; the quantizers below never pass more). */
+uint8_t oracle_e4m3_encode(double v) {
+  uint8_t sign = (v < 0.0 || (v == 0.0 && signbit(v))) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  if (a < ldexp(1.0, -6)) {  /* subnormal range: steps of 2^-9, code = steps */
+    double q = nearbyint(a / ldexp(1.0, -9));  /* ties to even */
+    return (uint8_t)(sign | (uint8_t)q);        /* q = 8 is the smallest normal */
+  }
+  int ex;
+  frexp(a, &ex);               /* a = f * 2^ex, f in [0.5, 1) */
+  int e = ex - 1;              /* a in [2^e, 2^(e+1)) */
+  double q = nearbyint(a / ldexp(1.0, e - 3));  /* 8 .. 16, ties to even */
+  if (q == 16.0) { q = 8.0; e += 1; }
+  return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(q - 8.0));
+}
+
+/* Per-row FP8 quantization of bf16 rows (the per-token activation quantization
+ * of prepare, per_act_token_quant; a static a1_scale / a2_scale otherwise).
+ * In float32, as the quantizing kernel decides the codes:
+ *   dynamic: a = max |x| over the row (448 when the row is all zero),
+ *            inv = 448 / a, scale = a / 448;
+ *   static:  scale = *static_scale, inv = 1 / scale;
+ *   q[j] = e4m3(min(max(x[j] * inv, -448), 448)), and x ~ q * scale. */
+void oracle_quantize_fp8_rows(const uint16_t* x, int64_t rows, int64_t H,
+                              const float* static_scale, uint8_t* q, float* scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * H;
+    float inv, sc;
+    if (static_scale) {
+      sc = *static_scale;
+      inv = 1.0f / sc;
+    } else {
+      float amax = 0.0f;
+      for (int64_t j = 0; j < H; ++j) {
+        float a = fabsf((float)bf16_val(xr[j]));
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) amax = 448.0f;
+      inv = 448.0f / amax;
+      sc = amax / 448.0f;
+    }
+    for (int64_t j = 0; j < H; ++j) {
+      float v = (float)bf16_val(xr[j]) * inv;
+      if (v > 448.0f) v = 448.0f;
+      if (v < -448.0f) v = -448.0f;
+      q[r * H + j] = oracle_e4m3_encode((double)v);
+    }
+    scales[r] = sc;
+  }
+}
+
+/* Weight element (row, kk) of a [rows, K] matrix in any storage format (FP8:
+ * the code times the row's scale, per_out_ch_quant). */
 double oracle_weight_at(const oracle_weights* w, int64_t row, int64_t K, int64_t kk) {
   if (w->fmt == OR_W_MXFP4)
-    return oracle_mxfp4_value((const uint8_t*)w->data, w->scales, row, K, kk);
+    return oracle_mxfp4_value((const uint8_t*)w->data, (const uint8_t*)w->scales, row, K, kk);
+  if (w->fmt == OR_W_FP8)
+    return oracle_e4m3_decode(((const uint8_t*)w->data)[row * K + kk]) *
+           (double)((const float*)w->scales)[row];
   return bf16_val(((const uint16_t*)w->data)[row * K + kk]);
 }
 
@@ -80,12 +160,16 @@ static double dot_row(const oracle_weights* w, int64_t row, int64_t K, const dou
   double acc = 0.0;
   if (w->fmt == OR_W_MXFP4) {
     const uint8_t* p = (const uint8_t*)w->data + row * (K / 2);
-    const uint8_t* s = w->scales + row * (K / 32);
+    const uint8_t* s = (const uint8_t*)w->scales + row * (K / 32);
     for (int64_t kk = 0; kk < K; ++kk) {
       uint8_t b = p[kk / 2];
       uint8_t code = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
       acc += kE2M1[code] * oracle_e8m0_scale(s[kk / 32]) * v[kk];
     }
+  } else if (w->fmt == OR_W_FP8) {
+    const uint8_t* p = (const uint8_t*)w->data + row * K;
+    const double sc = (double)((const float*)w->scales)[row];
+    for (int64_t kk = 0; kk < K; ++kk) acc += oracle_e4m3_decode(p[kk]) * sc * v[kk];
   } else {
     const uint16_t* p = (const uint16_t*)w->data + row * K;
     for (int64_t kk = 0; kk < K; ++kk) acc += bf16_val(p[kk]) * v[kk];
@@ -261,6 +345,40 @@ void oracle_hidden_rows(const uint16_t* a, int64_t rows, int64_t H, int64_t I,
   }
 }
 
+/* The same on FP8 rows (codes [rows, K] and one scale per row, as
+ * oracle_quantize_fp8_rows writes them): the rows are decoded to q * scale. */
+void oracle_hidden_rows_fp8(const uint8_t* aq, const float* a_scales, int64_t rows, int64_t H,
+                            int64_t I, const oracle_weights* w1, const int32_t* expert_of_row,
+                            int32_t act, double clamp, double* h) {
+#pragma omp parallel
+  {
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < H; ++c)
+        xv[c] = oracle_e4m3_decode(aq[r * H + c]) * (double)a_scales[r];
+      oracle_expert_hidden_act(xv, H, I, w1, expert_of_row[r], act, clamp, h + r * I);
+    }
+    free(xv);
+  }
+}
+
+void oracle_out_rows_fp8(const uint8_t* hq, const float* h_scales, int64_t rows, int64_t I,
+                         int64_t H, const oracle_weights* w2, const int32_t* expert_of_row,
+                         double* y) {
+#pragma omp parallel
+  {
+    double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < I; ++c)
+        hv[c] = oracle_e4m3_decode(hq[r * I + c]) * (double)h_scales[r];
+      oracle_expert_out(hv, H, I, w2, expert_of_row[r], y + r * H);
+    }
+    free(hv);
+  }
+}
+
 void oracle_out_rows(const uint16_t* hb, int64_t rows, int64_t I, int64_t H,
                      const oracle_weights* w2, const int32_t* expert_of_row, double* y) {
 #pragma omp parallel
@@ -337,6 +455,12 @@ void oracle_finalize_add_rmsnorm(const uint16_t* y_perm, const double* w, const 
  *   out[t] = rsf_fin * sum_j MLP_{L_j}(w_j * x_t) + MLP_shared(x_t).
  * act and clamp select the activation of every expert MLP, the shared one
  * included (see gated_act).
+ * With act_quant (FP8 activations: [MOD] prepare quantizes a1 for the first
+ * GEMM, a2_scale keeps the second GEMM's quantization consistent) each routed
+ * expert sees its input row as bf16 (x, or bf16(w_j * x) with
+ * weight_on_input) quantized per row to FP8 (oracle_quantize_fp8_rows; static
+ * a1_scale when given), and its hidden row h rounded to bf16 and quantized
+ * the same way (static a2_scale when given).  The shared expert stays bf16.
  * Optional outputs: y_routes [n, k, H] (the unweighted per-route expert output,
  * zero for non-local routes), ids [n, k], weights [n, k].
  * shared_I = 0 disables the shared expert. */
@@ -345,7 +469,8 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
                        const int32_t* expert_map, const oracle_weights* w1,
                        const oracle_weights* w2, int64_t shared_I, const uint16_t* ws1,
                        const uint16_t* ws2, double rsf_fin, int32_t act, double clamp,
-                       int32_t weight_on_input, const int64_t* tokens, int64_t n_tokens,
+                       int32_t weight_on_input, int32_t act_quant, const float* a1_scale,
+                       const float* a2_scale, const int64_t* tokens, int64_t n_tokens,
                        double* out, double* y_routes, int32_t* ids_out, double* w_out) {
   oracle_weights s1 = {OR_W_BF16, ws1, NULL};
   oracle_weights s2 = {OR_W_BF16, ws2, NULL};
@@ -358,6 +483,9 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
     double* yv = (double*)malloc(sizeof(double) * (size_t)H);
     int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
     double* wts = (double*)malloc(sizeof(double) * (size_t)k);
+    int64_t Qmax = H > I ? H : I;
+    uint16_t* qin = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Qmax);
+    uint8_t* qout = (uint8_t*)malloc((size_t)Qmax);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t s = 0; s < n_tokens; ++s) {
       int64_t t = tokens[s];
@@ -374,11 +502,25 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
           for (int64_t n = 0; n < H; ++n) yr[n] = 0.0;
           continue;
         }
+        const double* xin = xv;
         if (weight_on_input) {
           for (int64_t c = 0; c < H; ++c) xw[c] = wts[j] * xv[c];
-          oracle_expert_hidden_act(xw, H, I, w1, L, act, clamp, hv);
-        } else {
-          oracle_expert_hidden_act(xv, H, I, w1, L, act, clamp, hv);
+          xin = xw;
+        }
+        if (act_quant) {
+          float sc;
+          for (int64_t c = 0; c < H; ++c)
+            qin[c] = weight_on_input ? bf16_bits((float)wts[j] * (float)xv[c]) : x[t * H + c];
+          oracle_quantize_fp8_rows(qin, 1, H, a1_scale, qout, &sc);
+          for (int64_t c = 0; c < H; ++c) xw[c] = oracle_e4m3_decode(qout[c]) * (double)sc;
+          xin = xw;
+        }
+        oracle_expert_hidden_act(xin, H, I, w1, L, act, clamp, hv);
+        if (act_quant) {
+          float sc;
+          for (int64_t c = 0; c < I; ++c) qin[c] = bf16_bits((float)hv[c]);
+          oracle_quantize_fp8_rows(qin, 1, I, a2_scale, qout, &sc);
+          for (int64_t c = 0; c < I; ++c) hv[c] = oracle_e4m3_decode(qout[c]) * (double)sc;
         }
         oracle_expert_out(hv, H, I, w2, L, yr);
         const double wj = weight_on_input ? 1.0 : wts[j];
@@ -397,6 +539,8 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
     free(yv);
     free(ids);
     free(wts);
+    free(qin);
+    free(qout);
   }
 }
 
