@@ -14,6 +14,10 @@ default workload is the Mixtral-8x7B-shaped prefill layer (4096 tokens, hidden
 bf16 weights.  The other workloads:
   deepseekv3_routed_shared_2048tok   256 experts, top-8 sigmoid, shared expert
   deepseekv3_mxfp4_2048tok           the same shape with MXFP4 expert weights
+  deepseekv3_fp8_2048tok             the same shape (routed experts only) in FP8 E4M3:
+                                     per-channel weight scales, per-token activation
+                                     scales (quantize -> dispatch -> FP8 GEMMs)
+  mixtral8x7b_fp8_prefill_4096tok    the Mixtral shape in FP8 E4M3
   ep_rank3of8_decode                 one expert-parallel rank's 32 experts at a
                                      decode batch (--tokens 1, 8 or 64), deferred
                                      form followed by the separate finalize; the
@@ -51,6 +55,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused-MoE layer tokens/s and TFLOP/s (% MFMA or HBM peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MiB) + MALL (256 MiB)
@@ -122,9 +127,15 @@ def gemm_work(cfg, counts, gemm: int):
         N, K, out_cols = 2 * cfg.I, cfg.H, cfg.I
     else:
         N, K, out_cols = cfg.H, cfg.I, cfg.H
-    w_bytes_per_expert = N * (K // 2 + K // 32) if cfg.mxfp4 else N * K * 2
+    if cfg.mxfp4:
+        w_bytes_per_expert = N * (K // 2 + K // 32)
+    elif cfg.fp8:
+        w_bytes_per_expert = N * (K + 4)     # codes + one fp32 scale per channel
+    else:
+        w_bytes_per_expert = N * K * 2
+    in_bytes = R_l * (K + 4) if cfg.fp8 else R_l * K * 2  # fp8 rows carry a scale
     flops = 2.0 * R_l * N * K
-    nbytes = float(touched * w_bytes_per_expert + R_l * K * 2 + R_l * out_cols * 2)
+    nbytes = float(touched * w_bytes_per_expert + in_bytes + R_l * out_cols * 2)
     return flops, nbytes
 
 
@@ -135,11 +146,14 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
     import oracle
     if cfg.mxfp4:
         W1, W2 = oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    elif cfg.fp8:
+        W1 = oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1))
+        W2 = oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1))
     else:
         W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
     from synth import configs
     kw = dict(expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I, ws1=w.get("ws1"),
-              ws2=w.get("ws2"), **(variant or {}))
+              ws2=w.get("ws2"), fp8=cfg.fp8, **(variant or {}))
 
     def run(x, logits, toks):
         oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
@@ -230,7 +244,7 @@ def main():
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
     dev_draws = [(to_bf16(x), torch.from_numpy(lg).cuda()) for x, lg in draws]
-    if cfg.mxfp4:
+    if cfg.mxfp4 or cfg.fp8:
         W1 = moe.Weights(torch.from_numpy(w["w1_q"]).cuda(), torch.from_numpy(w["w1_s"]).cuda())
         W2 = moe.Weights(torch.from_numpy(w["w2_q"]).cuda(), torch.from_numpy(w["w2_s"]).cuda())
     else:
@@ -251,6 +265,16 @@ def main():
     h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if cfg.fp8:
+        if Mb:
+            print("FP8 workloads take the standard layout", file=sys.stderr)
+            sys.exit(2)
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((T,), dtype=torch.float32, device=dev)
+        xq_perm = torch.empty((R_pad, H), dtype=torch.uint8, device=dev)
+        ps = torch.empty((R_pad,), dtype=torch.float32, device=dev)
+        hq = torch.empty((R_pad, I), dtype=torch.uint8, device=dev)
+        hs = torch.empty((R_pad,), dtype=torch.float32, device=dev)
     if args.fused_tail:
         residual = to_bf16(draws[0][0])  # a residual stream of the x distribution
         gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
@@ -275,14 +299,22 @@ def main():
     stream = torch.cuda.current_stream()
 
     fin_stage = "finalize_add_rmsnorm" if args.fused_tail else "finalize"
-    stages = ["route", "permute", "gemm1", "gemm2"] + (["shared"] if cfg.shared_I else []) \
-        + [fin_stage]
+    stages = (["route", "quantize", "permute", "gemm1", "quantize_h", "gemm2"] if cfg.fp8
+              else ["route", "permute", "gemm1", "gemm2"]) \
+        + (["shared"] if cfg.shared_I else []) + [fin_stage]
     act_kw = dict(activation=args.activation, activation_clamp=args.activation_clamp)
     w_in = args.router_weight_on_input
 
     counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
 
     def permute(sl, st):
+        if cfg.fp8:
+            moe.moe_quantize_fp8(xd_cur[0][sl], None, wts[sl] if w_in else None, xq[sl], xs[sl],
+                                 stream=st)
+            mark_cur[0]("permute")
+            moe.moe_permute_fp8(ids[sl], E, xq[sl], xs[sl], El, emap_d, R_pad, pmap[sl], offsets,
+                                None, xq_perm, ps, want_inv=False, stream=st)
+            return
         if Mb:
             moe.moe_permute_batched(ids[sl], E, Mb, El, emap_d, xd_cur[0][sl], pmap[sl], counts_b,
                                     x_perm.view(El, Mb, H), wts[sl] if w_in else None, stream=st)
@@ -292,6 +324,15 @@ def main():
                             stream=st)
 
     def gemms(n, st):
+        if cfg.fp8:
+            moe.moe_grouped_gemm1_act_fp8(xq_perm, ps, offsets, W1, I, h, stream=st, split=False,
+                                          workspace=split_ws, **act_kw)
+            mark_cur[0]("quantize_h")
+            moe.moe_quantize_fp8(h, None, None, hq, hs, row_count=offsets[El:], stream=st)
+            mark_cur[0]("gemm2")
+            moe.moe_grouped_gemm2_fp8(hq, hs, offsets, W2, H, y, stream=st, split=False,
+                                      workspace=split_ws)
+            return
         if Mb:
             moe.moe_grouped_gemm1_act_batched(x_perm.view(El, Mb, H), counts_b, W1, I,
                                               h.view(El, Mb, I), max_rows=n * k, stream=st,
@@ -311,7 +352,7 @@ def main():
 
     def route_permute(d, t0, n):
         xd, ld = dev_draws[d]
-        xd_cur[0] = xd
+        xd_cur[0], mark_cur[0] = xd, (lambda name: None)
         sl = slice(t0, t0 + n)
         moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                            stream)
@@ -330,7 +371,7 @@ def main():
             mark("route")
             moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                                st)
-            mark("permute")
+            mark("quantize" if cfg.fp8 else "permute")
             permute(sl, st)
             mark("gemm1")
             gemms(n, st)
@@ -448,12 +489,13 @@ def main():
         ms_per_step = elapsed / args.steps * 1e3
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
     g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
-    t_mfma = g1_flops / (PEAK_BF16_TFLOPS * 1e12)
+    peak_mfma = PEAK_FP8_TFLOPS if cfg.fp8 else PEAK_BF16_TFLOPS
+    t_mfma = g1_flops / (peak_mfma * 1e12)
     t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
         achieved = g1_flops / g1_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": achieved / peak_mfma}
     else:
         achieved = g1_bytes / g1_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -479,13 +521,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if cfg.fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights"
-                + (", MXFP4-quantized" if cfg.mxfp4 else "") + ")",
+                + (", MXFP4-quantized" if cfg.mxfp4 else "")
+                + (", FP8 E4M3 weights per channel, activations per token" if cfg.fp8 else "")
+                + ")",
         "config": {"workload": label, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "local_experts": El, "top_k": k,
                    "shared_intermediate": cfg.shared_I,
-                   "expert_weights": "mxfp4 (e2m1 + E8M0 per 32)" if cfg.mxfp4 else "bf16",
+                   "expert_weights": "mxfp4 (e2m1 + E8M0 per 32)" if cfg.mxfp4 else
+                                     ("fp8 e4m3 (fp32 scale per channel)" if cfg.fp8 else "bf16"),
                    "routing": ("softmax" if cfg.score == 0 else "sigmoid") +
                               (f" top-{k} renormalized") + (f", rsf {cfg.rsf}" if cfg.rsf != 1 else "") +
                               (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
@@ -499,7 +544,7 @@ def main():
                                  + (f", clamp {args.activation_clamp:g}" if args.activation_clamp else "")
                                  + (", routing weight on the input" if w_in else "")},
         "tflops": tflops,
-        "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
+        "mfma_frac_layer": tflops / peak_mfma,
         "stages_ms": stage_ms,
         "expert_rows": counts0.tolist() if len(counts0) <= 16 else
                        {"min": int(counts0.min()), "max": int(counts0.max()),

@@ -74,8 +74,10 @@ enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum {
   MOE_DTYPE_BF16 = 0,  /* bfloat16                                              */
   MOE_DTYPE_F32 = 1,   /* float32                                               */
-  MOE_DTYPE_MXFP4 = 2  /* e2m1 pairs (low nibble = even element) + one E8M0 scale
+  MOE_DTYPE_MXFP4 = 2, /* e2m1 pairs (low nibble = even element) + one E8M0 scale
                           byte per 32 elements along the reduction dimension    */
+  MOE_DTYPE_FP8_E4M3 = 3 /* OCP FP8 E4M3 (bias 7, largest 448) codes + one fp32
+                          scale per row (weights: per output channel)           */
 };
 
 /* Activations of GEMM1 (page "modular_kernel.py", activation(): the output is
@@ -119,18 +121,34 @@ typedef struct moe_layer_options {
   int32_t apply_router_weight_on_input;
   int32_t chunk_tokens;
   int32_t batched_max_tokens;
+  int32_t act_quant;        /* MOE_QUANT_NONE, or MOE_QUANT_FP8 (with FP8 weights) */
+  const float* a1_scale;    /* (device) static scale of the GEMM1 input, or NULL */
+  const float* a2_scale;    /* (device) static scale of the GEMM2 input, or NULL */
 } moe_layer_options;
+
+/* Activation quantization of the fused calls (quant_dtype and
+ * per_act_token_quant of page "modular_kernel.py"): MOE_QUANT_FP8 quantizes
+ * each token row to FP8 E4M3 before dispatch (moe_quantize_fp8, one scale per
+ * row, or the static a1_scale) and each bf16 hidden row before GEMM2 (per row,
+ * or a2_scale); both GEMMs then multiply FP8 codes on the matrix cores and
+ * apply the row and channel scales in fp32.  Needs FP8 weights, H and I
+ * multiples of 128, the standard layout (no batched_max_tokens); the shared
+ * expert stays bf16. */
+enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1 };
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
  *   BF16:  data = bf16 [E_l, N, K],   scales = NULL
  *   MXFP4: data = u8 [E_l, N, K/2],   scales = u8 [E_l, N, K/32]
+ *   FP8:   data = e4m3 [E_l, N, K],   scales = fp32 [E_l, N] (per output
+ *          channel, per_out_ch_quant of page "modular_kernel.py"); these
+ *          multiply FP8 activations only (the *_fp8 GEMMs, or MOE_QUANT_FP8)
  * (GEMM1: N = 2I, K = H, rows [0, I) gate and [I, 2I) up; GEMM2: N = H, K = I.)
  * The tag matters: a buffer read as a wider type than it holds is garbage
  * (page "moe_output.py", the comment on expert_weights). */
 typedef struct moe_weights {
   int32_t dtype;
   const void* data;      /* (device) */
-  const uint8_t* scales; /* (device) MXFP4 only */
+  const void* scales;    /* (device) MXFP4 and FP8 only */
 } moe_weights;
 
 /* Text of a status code (static storage). */
@@ -202,6 +220,53 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
                 int32_t E, int32_t E_l, const void* x, int32_t H, int64_t R_pad, int32_t* map,
                 int32_t* offsets, int32_t* inv, void* x_perm, const float* x_weights,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 E4M3 quantization of bf16 rows (the quantize half of [Quantize-Dispatch];
+ * prepare() of page "modular_kernel.py" with per_act_token_quant, or a static
+ * a1_scale / a2_scale).  Per row, in fp32:
+ *   dynamic (static_scale NULL): a = max |x| (448 for an all-zero row),
+ *     inv = 448 / a, scale = a / 448;   static: scale = *static_scale, inv = 1 / scale;
+ *   q[j] = E4M3 code nearest to clamp(x[j] * inv, -448, 448), ties to even.
+ * With row_weights (fp32 [rows], apply_router_weight_on_input) the row is
+ * first bf16(row_weights[r] * x).
+ *   x         (device) bf16 [rows, H];   q (device) u8 [rows, H] out
+ *   row_count (device) int32 scalar or NULL: only rows < *row_count are
+ *             quantized (the local routes of permuted rows: offsets + E_l)
+ *   scales  (device) fp32 [rows] out (the static scale repeated when given)
+ * Limits: H a multiple of 16. */
+int moe_quantize_fp8(const void* x, int64_t rows, int32_t H, const float* static_scale,
+                     const float* row_weights, const int32_t* row_count, uint8_t* q,
+                     float* scales, void* stream);
+
+/* Permute with FP8 rows (the dispatch half of [Quantize-Dispatch]): as
+ * moe_permute, gathering the quantized rows and their scales:
+ *   xq_perm[map[t,j], :] = xq[t, :],  xq_perm_scales[map[t,j]] = x_scales[t].
+ *   xq (device) u8 [T, H], x_scales (device) fp32 [T] (from moe_quantize_fp8)
+ *   xq_perm (device) u8 [R_pad, H] out, xq_perm_scales (device) fp32 [R_pad] out
+ * Limits: H a multiple of 16. */
+int moe_permute_fp8(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                    int32_t E, int32_t E_l, const uint8_t* xq, const float* x_scales, int32_t H,
+                    int64_t R_pad, int32_t* map, int32_t* offsets, int32_t* inv, uint8_t* xq_perm,
+                    float* xq_perm_scales, void* stream);
+
+/* The two grouped GEMMs on FP8 rows with FP8 weights (apply() of page
+ * "modular_kernel.py" with a1q_scale / a2_scale and w1_scale / w2_scale):
+ *   C[r, n] = a_scale[r] * w_scale[e, n] * sum_k a[r, k] * W[e, n, k]
+ * (E4M3 products summed exactly in fp32 by the 32x32x64 MFMA), then, for
+ * GEMM1, act(gate) * up and one rounding to bf16.
+ *   a_perm / h_perm  (device) u8 [R_pad, H or I];  a_scales / h_scales fp32 [R_pad]
+ *   w1 / w2          MOE_DTYPE_FP8_E4M3 weights
+ *   h / y            (device) bf16 [R_pad, I or H] out
+ *   workspace        as for the bf16 calls
+ * Limits: H and I multiples of 128. */
+int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
+                              const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                              int32_t I, const moe_weights* w1, int32_t activation,
+                              float activation_clamp, void* h, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const int32_t* offsets,
+                          int32_t E_l, int64_t R_pad, int32_t I, int32_t H, const moe_weights* w2,
+                          void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Permute into the batched experts format (page "modular_kernel.py":
  * FusedMoEActivationFormat.BatchedExperts, activations laid out as (local

@@ -21,7 +21,9 @@ class MoeWeightsC(ctypes.Structure):
 class MoeLayerOptionsC(ctypes.Structure):
     _fields_ = [("activation", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("apply_router_weight_on_input", ctypes.c_int32),
-                ("chunk_tokens", ctypes.c_int32), ("batched_max_tokens", ctypes.c_int32)]
+                ("chunk_tokens", ctypes.c_int32), ("batched_max_tokens", ctypes.c_int32),
+                ("act_quant", ctypes.c_int32), ("a1_scale", ctypes.c_void_p),
+                ("a2_scale", ctypes.c_void_p)]
 
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -40,6 +42,13 @@ PROTOTYPES = {
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _f32,
                                              _vp, _vp, _sz, _vp]),
+    "moe_quantize_fp8": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_permute_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _i32, _i64,
+                                       _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_grouped_gemm1_act_fp8": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32,
+                                                 _f32, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm2_fp8": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _Wp, _vp, _vp,
+                                             _sz, _vp]),
     "moe_permute_batched": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32,
                                            _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm1_act_batched": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64, _i32, _i32, _Wp,

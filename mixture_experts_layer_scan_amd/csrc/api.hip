@@ -75,6 +75,13 @@ int opt_ptr(const void* p, const char* name) {
   return check_device_ptr(p, name);
 }
 
+// an optional 4-byte aligned device scalar or array
+int opt_ptr4(const void* p, const char* name) {
+  if (!p) return MOE_OK;
+  if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(MOE_ERR_MISALIGNED, "%s must be 4-byte aligned", name);
+  return check_device_ptr(p, name);
+}
+
 bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return a && b && an && bn && x < y + bn && y < x + an;
@@ -103,9 +110,12 @@ int check_gemm_dims(int32_t H, int32_t I) {
 
 int check_weights(const moe_weights* w, const char* name) {
   if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
-  if (w->dtype == MOE_DTYPE_MXFP4) {
+  if (w->dtype == MOE_DTYPE_MXFP4 || w->dtype == MOE_DTYPE_FP8_E4M3) {
     MOE_CHECK(need_ptr(w->data, name));
-    if (!w->scales) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: MXFP4 weights need their E8M0 scales", name);
+    if (!w->scales) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s weights need their scales", name,
+                                w->dtype == MOE_DTYPE_MXFP4 ? "MXFP4" : "FP8");
+    if (w->dtype == MOE_DTYPE_FP8_E4M3 && (reinterpret_cast<uintptr_t>(w->scales) & 3u))
+      return fail(MOE_ERR_MISALIGNED, "%s: FP8 scales must be 4-byte aligned", name);
     return check_device_ptr(w->scales, name);
   }
   if (w->dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight dtype %d", name, w->dtype);
@@ -113,8 +123,18 @@ int check_weights(const moe_weights* w, const char* name) {
   return need_ptr(w->data, name);
 }
 
-const uint8_t* scales_of(const moe_weights* w) {
-  return w->dtype == MOE_DTYPE_MXFP4 ? w->scales : nullptr;
+// The weights' scales as the GEMM takes them (NULL for bf16).
+const void* scales_of(const moe_weights* w) {
+  return w->dtype == MOE_DTYPE_BF16 ? nullptr : w->scales;
+}
+
+// FP8 weights multiply FP8 activations only, and FP8 activations FP8 weights.
+int check_pairing(const moe_weights* w, bool fp8_act, const char* name) {
+  if (fp8_act && w->dtype != MOE_DTYPE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 activations need FP8 weights", name);
+  if (!fp8_act && w->dtype == MOE_DTYPE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 weights need FP8 activations", name);
+  return MOE_OK;
 }
 
 // The GEMMs address each operand through a buffer descriptor with a 32-bit
@@ -160,6 +180,9 @@ struct LayerOpts {
   bool weight_on_input = false;
   int64_t chunk = 0;  // 0: one pass
   int batch_m = 0;    // > 0: batched experts format with this capacity
+  bool fp8 = false;   // FP8 activations (MOE_QUANT_FP8)
+  const float* a1_scale = nullptr;
+  const float* a2_scale = nullptr;
 };
 
 int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
@@ -177,6 +200,17 @@ int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
   if (o->batched_max_tokens < 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "batched_max_tokens must be >= 0");
   out->batch_m = o->batched_max_tokens;
+  if (o->act_quant != MOE_QUANT_NONE && o->act_quant != MOE_QUANT_FP8)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown activation quantization %d", o->act_quant);
+  out->fp8 = o->act_quant == MOE_QUANT_FP8;
+  if (out->fp8 && out->batch_m > 0)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 activations take the standard layout (no batched_max_tokens)");
+  if (!out->fp8 && (o->a1_scale || o->a2_scale))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a1_scale / a2_scale need act_quant = MOE_QUANT_FP8");
+  MOE_CHECK(opt_ptr4(o->a1_scale, "a1_scale"));
+  MOE_CHECK(opt_ptr4(o->a2_scale, "a2_scale"));
+  out->a1_scale = o->a1_scale;
+  out->a2_scale = o->a2_scale;
   return MOE_OK;
 }
 
@@ -196,7 +230,8 @@ int64_t routed_rows(int64_t T, int32_t k, int32_t E_l, int batch_m) {
   return batch_m > 0 ? int64_t(E_l) * batch_m : moe_permuted_rows(T, k);
 }
 
-size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, int batch_m) {
+size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, int batch_m,
+                       bool fp8 = false) {
   const int64_t R_pad = routed_rows(T, k, E_l, batch_m);
   size_t b = 0;
   b += align_up(sizeof(int32_t) * T * k);               // topk ids
@@ -206,6 +241,13 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, 
   b += align_up(sizeof(uint16_t) * R_pad * H);          // x_perm, then GEMM2 output
   b += align_up(sizeof(uint16_t) * R_pad * I);          // h
   b += align_up(routed_split_bytes(R_pad, H, I));       // GEMM split partials
+  if (fp8) {
+    b += align_up(size_t(T) * H);                       // quantized tokens
+    b += align_up(sizeof(float) * T);                   // their scales
+    b += align_up(sizeof(float) * R_pad);               // permuted row scales
+    b += align_up(size_t(R_pad) * I);                   // quantized hidden rows
+    b += align_up(sizeof(float) * R_pad);               // their scales
+  }
   return b;
 }
 
@@ -241,7 +283,7 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   MOE_CHECK(check_route_sizes(T, E, k));
   MOE_CHECK(check_local(E, E_l));
   MOE_CHECK(check_gemm_dims(H, I));
-  if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4)
+  if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4 && w_dtype != MOE_DTYPE_FP8_E4M3)
     return fail(MOE_ERR_UNSUPPORTED, "unknown weight dtype %d", w_dtype);
   if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   LayerOpts o;
@@ -249,7 +291,7 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   const int64_t P = pass_tokens(T, o);
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m) + shared_bytes;
+  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8) + shared_bytes;
   return MOE_OK;
 }
 
@@ -365,27 +407,33 @@ int moe_permute_batched(const int32_t* topk_ids, const int32_t* expert_map, int6
 static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
                        int32_t K, int32_t N_out, int gated, int act, float clamp,
                        const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
-                       void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0) {
+                       void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
+                       bool fp8 = false, const float* a_scales = nullptr) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
+  MOE_CHECK(check_pairing(w, fp8, name));
   MOE_CHECK(check_gemm_extent(R_pad, K, gated ? 2 * int64_t(N_out) : N_out));
   if (R_pad == 0) return MOE_OK;
   MOE_CHECK(need_ptr(a, "input rows"));
   MOE_CHECK(need_ptr(offsets, "offsets"));
   MOE_CHECK(need_ptr(c, "output rows"));
-  if (overlap(a, sizeof(uint16_t) * R_pad * K, c, sizeof(uint16_t) * R_pad * N_out))
+  const size_t in_bytes = (fp8 ? 1 : sizeof(uint16_t)) * R_pad * K;
+  const size_t out_bytes = sizeof(uint16_t) * R_pad * N_out;
+  if (overlap(a, in_bytes, c, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
+  if (a_scales && overlap(a_scales, sizeof(float) * R_pad, c, out_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the row scales", name);
   if (workspace_bytes > 0) {
     MOE_CHECK(need_ptr(workspace, "workspace"));
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
       return fail(MOE_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", name);
-    const size_t in_bytes = sizeof(uint16_t) * R_pad * K, out_bytes = sizeof(uint16_t) * R_pad * N_out;
     if (overlap(workspace, workspace_bytes, a, in_bytes) || overlap(workspace, workspace_bytes, c, out_bytes))
       return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: workspace must not overlap the rows", name);
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
-                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m};
+                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
+                  a_scales};
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -409,6 +457,97 @@ int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_
   MOE_CHECK(check_gemm_dims(H, I));
   return gemm_common(h, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
                      workspace_bytes, stream, "moe_grouped_gemm2");
+}
+
+int moe_quantize_fp8(const void* x, int64_t rows, int32_t H, const float* static_scale,
+                     const float* row_weights, const int32_t* row_count, uint8_t* q,
+                     float* scales, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be non-negative");
+  if (H <= 0 || H % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 16 (H=%d)", H);
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(x, "x"));
+  MOE_CHECK(need_ptr(q, "q"));
+  MOE_CHECK(need_ptr(scales, "scales"));
+  MOE_CHECK(opt_ptr4(static_scale, "static_scale"));
+  MOE_CHECK(opt_ptr4(row_weights, "row_weights"));
+  MOE_CHECK(opt_ptr4(row_count, "row_count"));
+  if (overlap(x, sizeof(uint16_t) * rows * H, q, size_t(rows) * H) ||
+      overlap(x, sizeof(uint16_t) * rows * H, scales, sizeof(float) * rows))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "q and scales must not overlap x");
+  hipError_t e = moe::launch_quantize_fp8(x, rows, H, static_scale, row_weights, row_count, q,
+                                          scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8");
+}
+
+int moe_permute_fp8(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, int32_t k,
+                    int32_t E, int32_t E_l, const uint8_t* xq, const float* x_scales, int32_t H,
+                    int64_t R_pad, int32_t* map, int32_t* offsets, int32_t* inv, uint8_t* xq_perm,
+                    float* xq_perm_scales, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  if (H <= 0 || H % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 16 (H=%d)", H);
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(opt_ptr(inv, "inv"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(map, "map"));
+    MOE_CHECK(need_ptr(xq, "xq"));
+    MOE_CHECK(need_ptr(xq_perm, "xq_perm"));
+    MOE_CHECK(opt_ptr4(x_scales, "x_scales"));
+    MOE_CHECK(opt_ptr4(xq_perm_scales, "xq_perm_scales"));
+    if (!x_scales || !xq_perm_scales)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "x_scales and xq_perm_scales must not be NULL");
+  }
+  if (overlap(xq, size_t(T) * H, xq_perm, size_t(R_pad) * H))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "xq_perm must not overlap xq");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_permute(topk_ids, expert_map, T, k, E, E_l, map, offsets, inv, R_pad, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_fp8");
+  if (T > 0) {
+    e = moe::launch_gather_fp8_rows(xq, x_scales, map, T, k, H, xq_perm, xq_perm_scales, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_fp8 gather");
+  }
+  return MOE_OK;
+}
+
+int check_fp8_dims(int32_t H, int32_t I) {
+  if (H % 128 || I % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "FP8 GEMMs need H and I multiples of 128 (H=%d, I=%d)", H, I);
+  return MOE_OK;
+}
+
+int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
+                              const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                              int32_t I, const moe_weights* w1, int32_t activation,
+                              float activation_clamp, void* h, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(a_scales, "a_scales"));
+  if (R_pad > 0 && !a_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "a_scales must not be NULL");
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_fp8", 0, 0, true,
+                     a_scales);
+}
+
+int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const int32_t* offsets,
+                          int32_t E_l, int64_t R_pad, int32_t I, int32_t H, const moe_weights* w2,
+                          void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(h_scales, "h_scales"));
+  if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
+  return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
+                     workspace_bytes, stream, "moe_grouped_gemm2_fp8", 0, 0, true, h_scales);
 }
 
 int moe_grouped_gemm1_act_batched(const void* a_batched, const int32_t* expert_num_tokens,
@@ -527,10 +666,17 @@ struct RoutedWs {
   void* split;       // split-reduction scratch of both GEMMs
   size_t split_bytes;
   int64_t rows;
+  // FP8 activations: quantized tokens and scales, permuted row scales (the
+  // quantized permuted rows sit in x_perm's slot), quantized hidden rows
+  uint8_t* xq = nullptr;
+  float* xs = nullptr;
+  float* ps = nullptr;
+  uint8_t* hq = nullptr;
+  float* hs = nullptr;
 };
 
 static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I,
-                             int batch_m) {
+                             int batch_m, bool fp8 = false) {
   RoutedWs b;
   b.rows = routed_rows(T, k, E_l, batch_m);
   b.ids = c.take<int32_t>(T * k);
@@ -541,6 +687,13 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   b.h = c.take<uint16_t>(b.rows * I);
   b.split_bytes = routed_split_bytes(b.rows, H, I);
   b.split = b.split_bytes ? c.take<char>(b.split_bytes) : nullptr;
+  if (fp8) {
+    b.xq = c.take<uint8_t>(T * H);
+    b.xs = c.take<float>(T);
+    b.ps = c.take<float>(b.rows);
+    b.hq = c.take<uint8_t>(b.rows * I);
+    b.hs = c.take<float>(b.rows);
+  }
   return b;
 }
 
@@ -561,9 +714,34 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     e = moe::launch_fill_u16(w_bf16_out, T * k, 0x3F80, s);  // bf16 1.0
     if (e != hipSuccess) return hip_fail(e, "unit weights");
   }
+  if (o.fp8) {
+    // Quantize-Dispatch: the tokens (times their weight when it goes on the
+    // input; top_k 1, so one weight per token) to FP8, then their rows
+    e = moe::launch_quantize_fp8(x, T, H, o.a1_scale, o.weight_on_input ? b.wts : nullptr,
+                                 nullptr, b.xq, b.xs, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize");
+  }
   e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s,
                           o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");
+  if (o.fp8) {
+    e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H, b.x_perm, b.ps, s);
+    if (e != hipSuccess) return hip_fail(e, "gather");
+    const int64_t max_rows = moe_permuted_rows(T, k);
+    moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
+                     b.split, b.split_bytes, o.act, o.clamp, 0, b.ps};
+    e = moe::launch_grouped_gemm(g1, max_rows, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm1");
+    // the hidden rows of the local routes (offsets[E_l] of them) to FP8
+    e = moe::launch_quantize_fp8(b.h, b.rows, I, o.a2_scale, nullptr, b.offsets + E_l, b.hq, b.hs,
+                                 s);
+    if (e != hipSuccess) return hip_fail(e, "quantize hidden");
+    moe::GemmArgs g2{b.hq, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
+                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs};
+    e = moe::launch_grouped_gemm(g2, max_rows, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm2");
+    return MOE_OK;
+  }
   e = moe::launch_gather_rows(x, map, T, k, H, o.weight_on_input ? b.wts : nullptr, b.x_perm, s);
   if (e != hipSuccess) return hip_fail(e, "gather");
   // the tile shape follows the routed rows, the same bound in both formats
@@ -592,6 +770,9 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
     return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
   MOE_CHECK(check_weights(w1, "w1"));
   MOE_CHECK(check_weights(w2, "w2"));
+  MOE_CHECK(check_pairing(w1, o.fp8, "w1"));
+  MOE_CHECK(check_pairing(w2, o.fp8, "w2"));
+  if (o.fp8) MOE_CHECK(check_fp8_dims(H, I));
   if (o.batch_m > 0) MOE_CHECK(check_capacity(E_l, o.batch_m));
   const int64_t rows = routed_rows(pass_T, k, E_l, o.batch_m);
   MOE_CHECK(check_gemm_extent(rows, H, 2 * int64_t(I)));
@@ -636,9 +817,9 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(check_workspace(workspace, workspace_bytes,
-                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m)));
+                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8)));
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m);
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
                     o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
                     static_cast<hipStream_t>(stream));
@@ -669,7 +850,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
   }
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m) + shared_bytes;
+  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8) + shared_bytes;
   MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
   // out is x itself (in place) or apart from it; the workspace is apart from both
   const size_t row_bytes = sizeof(uint16_t) * T * H;
@@ -679,7 +860,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     return fail(MOE_ERR_DESTINATION_CONFLICT, "the workspace must not overlap x or out");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m);
+  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m, o.fp8);
   int32_t* s_off = nullptr;
   uint16_t* s_h = nullptr;
   uint16_t* s_y = nullptr;

@@ -77,6 +77,7 @@
 #include "moe_common.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 namespace moe {
@@ -85,6 +86,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int V>
 using ic = std::integral_constant<int, V>;
@@ -179,10 +181,12 @@ __device__ __forceinline__ int opaque(int v) {
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GATED_, bool WQ_ = false,
-          int GM_ = 8>
+          int GM_ = 8, bool F8_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
-  static constexpr int BK = 64;    // k per k-step (128 bytes of an activation row)
+  static constexpr bool F8 = F8_;  // activations and weights in FP8 E4M3
+  // k per k-step: 128 bytes of an activation row (64 bf16 or 128 fp8)
+  static constexpr int BK = F8 ? 128 : 64;
   static constexpr bool GATED = GATED_;
   static constexpr bool WQ = WQ_;  // weights in MXFP4
   static constexpr int GM = GM_;   // m-tiles per group of the tile order
@@ -195,7 +199,8 @@ struct TileCfg {
   static constexpr bool SKIP = (WM == 1 && FM > 1);
   // one wave row: the tiles for short segments, which may split the k-range
   static constexpr bool SPLIT = (WM == 1);
-  static constexpr int SUBSTEPS = BK / 16;
+  // MFMA sub-steps per k-step: 32x32x16 bf16, or 32x32x64 fp8
+  static constexpr int SUBSTEPS = F8 ? BK / 64 : BK / 16;
   // two stages: the next k-step's loads all go out with the first sub-step,
   // since they must land by the end of this one
   static constexpr bool EARLY = (STAGES == 2);
@@ -276,6 +281,7 @@ struct TileCfg {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "whole load instructions");
+  static_assert(!(F8 && WQ), "one weight format");
 };
 
 // First virtual weight row of fragment fn of wave column wn.
@@ -313,13 +319,15 @@ __device__ __forceinline__ bf16x8 expand_fp4x8(uint32_t w, float scale) {
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, const void* __restrict__ W,
-    const uint8_t* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
+    const void* __restrict__ A, const void* __restrict__ W,
+    const void* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
-    int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m) {
+    int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m,
+    const float* __restrict__ A_scales) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
+  using Frag = typename std::conditional<Cfg::F8, i32x8, bf16x8>::type;
   const int kind = act_kind(act, clamp);  // GEMM1 epilogue: 0 silu, 1 clamped silu, 2 gelu
   const float cl = act_limit(clamp);
   // LDS stages as distinct objects, so the compiler knows that loads into one
@@ -451,12 +459,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 
     // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
     // this expert's weights; loads past either range return zero.
+    // activation bytes per row: K * 2 (bf16) or K (fp8)
+    const uint32_t a_row_bytes = Cfg::F8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) * 2u;
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(A + static_cast<int64_t>(row0) * K), 0,
-        static_cast<int>(static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * 2u),
-        kBufferFlags);
-    // weight bytes per row: K * 2 (bf16) or K / 2 (packed e2m1)
-    const uint32_t w_row_bytes = Cfg::WQ ? static_cast<uint32_t>(K) / 2u : static_cast<uint32_t>(K) * 2u;
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(A) + static_cast<int64_t>(row0) * a_row_bytes),
+        0, static_cast<int>(static_cast<uint32_t>(rows) * a_row_bytes), kBufferFlags);
+    // weight bytes per row: K * 2 (bf16), K / 2 (packed e2m1) or K (fp8)
+    const uint32_t w_row_bytes = Cfg::WQ ? static_cast<uint32_t>(K) / 2u
+                                 : Cfg::F8 ? static_cast<uint32_t>(K)
+                                           : static_cast<uint32_t>(K) * 2u;
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(static_cast<const uint8_t*>(W) +
                              static_cast<int64_t>(e) * N_total * w_row_bytes),
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     for (int j = 0; j < Cfg::A_LD; ++j) {
       const int r = (j * Cfg::NWAVES + wave_u) * 8 + ld_sub;
       const int c = ld_pos ^ swz_key(r);
-      a_off[j] = (static_cast<uint32_t>(r) * K + c * 8) * 2u;
+      a_off[j] = static_cast<uint32_t>(r) * a_row_bytes + c * 16u;
     }
     // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
     // I + n0 + v - BN/2; columns past N_out are loaded but never stored
@@ -488,7 +499,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // when the stage opens.
     const uint32_t s_row = Cfg::WQ ? static_cast<uint32_t>(K) / 32u : 0u;  // scale bytes per row
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(W_scales + static_cast<int64_t>(e) * N_total * s_row), 0,
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(W_scales) +
+                             static_cast<int64_t>(e) * N_total * s_row), 0,
         static_cast<int>(static_cast<uint32_t>(N_total) * s_row), kBufferFlags);
     const bool s_wide = (s_row % 8u) == 0;  // uniform
     constexpr int NSF = Cfg::WQ ? FN : 1;
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
         if (Cfg::EARLY ? part == 0 : j % SUB == part)
-          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + kt) * BK * 2);
+          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + kt) * 128);
     };
     auto gload_b = [&](uint16_t* wst, int q, int part) {
 #pragma unroll
@@ -566,21 +578,37 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // lane's 16 packed bytes of the k-step (chunk 2p + h of its row) are read
     // into `bq`; every sub-step expands 4 of them (sub-step 0's at the top of
     // the k-step: see expand0).
+    // FP8: lane half h of sub-step ks holds the 32 bytes of chunks 4h + 2ks
+    // and 4h + 2ks + 1 of its A row and of its W row (k = 64 ks + 32 h ..
+    // + 31 of the k-step); the 32x32x64 MFMA runs unscaled (E8M0 127 = 1),
+    // the per-row and per-channel scales apply in the epilogue.
     auto load_frags = [&](const uint16_t* as, const uint16_t* bs, int ln, int ks, int p,
-                          bf16x8* af, bf16x8* bfr, uint4* bq) {
+                          Frag* af, Frag* bfr, uint4* bq) {
       const int frag_row = ln & 31;
       const int half = ln >> 5;
-      const int chunk = half * SUB + ks;
+      const int chunk = Cfg::F8 ? half * 4 + 2 * ks : half * SUB + ks;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
-        af[fm] = *reinterpret_cast<const bf16x8*>(as + swz(r, chunk));
+        if constexpr (Cfg::F8) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(as + swz(r, chunk));
+          const uint4 hi = *reinterpret_cast<const uint4*>(as + swz(r, chunk + 1));
+          af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+          af[fm] = *reinterpret_cast<const bf16x8*>(as + swz(r, chunk));
+        }
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int v = b_row0<Cfg>(wn, fn) + frag_row;
-        if constexpr (Cfg::WQ) {
+        if constexpr (Cfg::F8) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(bs + swz(v, chunk));
+          const uint4 hi = *reinterpret_cast<const uint4*>(bs + swz(v, chunk + 1));
+          bfr[fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else if constexpr (Cfg::WQ) {
           if (ks == 0) {
             bq[fn] = *reinterpret_cast<const uint4*>(bs + swz(v, 2 * p + half));
           } else {
@@ -596,7 +624,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // Operand fragments, double-buffered by sub-step; buffer 0 holds sub-step
     // 0 of the next k-step when a k-step begins.
     static_assert(SUB % 2 == 0, "sub-step 0 of the next k-step reuses buffer 0");
-    bf16x8 fa[2][FM], fb[2][FN];
+    Frag fa[2][FM], fb[2][FN];
     uint4 bq[Cfg::WQ ? FN : 1];
     // MXFP4: sub-step 0's weight fragments from the packed words read after
     // the previous barrier.  Expanding them there would stall the in-order
@@ -653,9 +681,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         for (int fm = 0; fm < FM; ++fm) {
           if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][fm], fb[ks & 1][fn],
-                                                                  acc[fm][fn], 0, 0, 0);
+          for (int fn = 0; fn < FN; ++fn) {
+            if constexpr (Cfg::F8)
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+            else
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -701,6 +734,26 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const int eln = opaque(lane);
     const int frag_row = eln & 31;
     const int frag_half = eln >> 5;
+    // FP8: the products of codes times the row's activation scale and the
+    // column's weight scale (per output channel; 0 past N_out, never stored)
+    float sw[Cfg::F8 ? FN : 1];
+    if constexpr (Cfg::F8) {
+      const float* wsc = static_cast<const float*>(W_scales) + static_cast<int64_t>(e) * N_total;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int v = b_row0<Cfg>(wn, fn) + frag_row;
+        const int col = Cfg::GATED ? (v < BN / 2 ? n0 + v : n0 + v - BN / 2) : n0 + v;
+        sw[fn] = col < N_out ? wsc[wrow_of(v)] : 0.0f;
+      }
+    }
+    auto scaled = [&](float a, float sa, int fn) -> float {
+      if constexpr (Cfg::F8) return a * sa * sw[fn];
+      return a;
+    };
+    auto row_scale = [&](int r) -> float {
+      if constexpr (Cfg::F8) return A_scales[row0 + r];
+      return 1.0f;
+    };
     if (Cfg::SPLIT && S > 1) {
       // fp32 sums of this piece into slice `piece` (weight-row columns: gate
       // at n, up at N_out + n)
@@ -713,11 +766,12 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
           const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
           if (r >= rows) continue;
           float* prow = P + static_cast<int64_t>(r) * N_total;
+          const float sa = row_scale(r);
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             const int v = b_row0<Cfg>(wn, fn) + frag_row;
             const int col = Cfg::GATED ? (v < BN / 2 ? n0 + v : n0 + v - BN / 2) : n0 + v;
-            if (col < N_out) prow[wrow_of(v)] = acc[fm][fn][i];
+            if (col < N_out) prow[wrow_of(v)] = scaled(acc[fm][fn][i], sa, fn);
           }
         }
       }
@@ -735,18 +789,21 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
           const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
           if (r >= rows) continue;
           uint16_t* crow = C + static_cast<int64_t>(row0 + r) * N_out;
+          const float sa = row_scale(r);
           if (Cfg::GATED) {
 #pragma unroll
             for (int fn = 0; fn < FN / 2; ++fn) {
               const int col = n0 + wn * (Cfg::WTN / 2) + fn * 32 + frag_row;
-              const float hv = gated_act_k<KIND>(acc[fm][fn][i], acc[fm][fn + FN / 2][i], cl);
+              const float hv = gated_act_k<KIND>(scaled(acc[fm][fn][i], sa, fn),
+                                                 scaled(acc[fm][fn + FN / 2][i], sa, fn + FN / 2),
+                                                 cl);
               if (col < N_out) crow[col] = f32_to_bf16(hv);
             }
           } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
               const int col = n0 + wn * Cfg::WTN + fn * 32 + frag_row;
-              if (col < N_out) crow[col] = f32_to_bf16(acc[fm][fn][i]);
+              if (col < N_out) crow[col] = f32_to_bf16(scaled(acc[fm][fn][i], sa, fn));
             }
           }
         }
@@ -850,9 +907,9 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
       split ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kSplitHeader) : nullptr;
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
                      dim3(Cfg::kThreads), 0, s,
-                     static_cast<const uint16_t*>(g.a), g.w, g.w_scales, g.offsets, g.E_l, g.K,
+                     g.a, g.w, g.w_scales, g.offsets, g.E_l, g.K,
                      g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
-                     g.act, g.clamp, g.batch_m);
+                     g.act, g.clamp, g.batch_m, g.a_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));
@@ -862,18 +919,18 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool WQ>
+template <bool WQ, bool F8>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
-  //                          BM   BN  WM WN ST  gated      GM
-  using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ>;
-  using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ>;
-  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ>;
-  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ>;
-  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1>;
-  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1>;
-  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ>;
-  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ>;
+  //                          BM   BN  WM WN ST  gated  WQ  GM  F8
+  using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ, 8, F8>;
+  using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ, 8, F8>;
+  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8>;
+  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8>;
+  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8>;
+  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8>;
+  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ, 8, F8>;
+  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ, 8, F8>;
 };
 
 // Tile shape from the mean rows per local expert (the host cannot see the
@@ -882,9 +939,9 @@ struct Configs {
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
 //   < 16    decode: short tiles with split reductions.
-template <bool WQ>
+template <bool WQ, bool F8>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  using C = Configs<WQ>;
+  using C = Configs<WQ, F8>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
   if (g.gated) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
@@ -910,7 +967,9 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
 
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  return g.w_scales ? launch_fmt<true>(g, max_rows, s) : launch_fmt<false>(g, max_rows, s);
+  if (g.a_scales) return launch_fmt<false, true>(g, max_rows, s);
+  return g.w_scales ? launch_fmt<true, false>(g, max_rows, s)
+                    : launch_fmt<false, false>(g, max_rows, s);
 }
 
 }  // namespace moe

@@ -104,9 +104,11 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int* tot
 namespace moe {
 
 struct GemmArgs {
-  const void* a;          // bf16 [R_pad, K]
-  const void* w;          // bf16 [E_l, N_total, K], or packed e2m1 [E_l, N_total, K/2]
-  const uint8_t* w_scales;  // NULL (bf16), or E8M0 [E_l, N_total, K/32] (MXFP4)
+  const void* a;          // bf16 [R_pad, K], or fp8 e4m3 [R_pad, K] when a_scales is set
+  const void* w;          // bf16 [E_l, N_total, K], packed e2m1 [E_l, N_total, K/2], or
+                          // fp8 e4m3 [E_l, N_total, K]
+  const void* w_scales;   // NULL (bf16), E8M0 u8 [E_l, N_total, K/32] (MXFP4), or fp32
+                          // [E_l, N_total] per output channel (fp8)
   const int32_t* offsets; // [E_l + 1], or the E_l row counts when batch_m > 0
   int E_l;
   int K;
@@ -121,6 +123,7 @@ struct GemmArgs {
   float clamp = 0.0f;     // gated only: > 0 clamps gate and up first
   int batch_m = 0;        // > 0: batched experts format, expert e's rows start
                           // at e * batch_m and number min(offsets[e], batch_m)
+  const float* a_scales = nullptr;  // fp8 activations: fp32 [R_pad], one per row
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its
@@ -149,6 +152,15 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
                                        const int32_t* map, int64_t T, int k, int H, float rsf_fin,
                                        const void* shared, void* residual, const void* gamma,
                                        float eps, void* out, hipStream_t s);
+// FP8 E4M3 rows: q [rows, H] codes and one fp32 scale per row, from bf16 rows
+// (times mult[r] rounded to bf16 when given); static_scale NULL: per-row
+// dynamic scales; row_count (device) NULL: all rows, else rows < *row_count.
+hipError_t launch_quantize_fp8(const void* x, int64_t rows, int H, const float* static_scale,
+                               const float* mult, const int32_t* row_count, void* q,
+                               float* scales, hipStream_t s);
+hipError_t launch_gather_fp8_rows(const void* q, const float* scales, const int32_t* map,
+                                  int64_t T, int k, int H, void* q_perm, float* scales_perm,
+                                  hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s);
 hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t s);
 

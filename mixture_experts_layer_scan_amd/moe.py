@@ -17,7 +17,8 @@ import torch
 from ._lib import MoeLayerOptionsC, MoeWeightsC, lib
 
 SOFTMAX, SIGMOID = 0, 1
-DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4 = 0, 1, 2
+DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4, DTYPE_FP8_E4M3 = 0, 1, 2, 3
+QUANT_NONE, QUANT_FP8 = 0, 1
 ACT_SILU, ACT_GELU = 0, 1
 _ACT_NAMES = {"silu": ACT_SILU, "gelu": ACT_GELU}
 
@@ -57,15 +58,24 @@ def _act(activation) -> int:
 
 def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
              apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
-             batched_max_tokens: int = 0):
+             batched_max_tokens: int = 0, fp8: bool = False,
+             a1_scale: Optional[torch.Tensor] = None, a2_scale: Optional[torch.Tensor] = None):
     """moe_layer_options by reference (None when every option is its default)."""
     act = _act(activation)
     clamp = 0.0 if activation_clamp is None else float(activation_clamp)
     if (act == ACT_SILU and clamp == 0.0 and not apply_router_weight_on_input
-            and not chunk_tokens and not batched_max_tokens):
+            and not chunk_tokens and not batched_max_tokens and not fp8
+            and a1_scale is None and a2_scale is None):
         return None
+    for name, t in (("a1_scale", a1_scale), ("a2_scale", a2_scale)):
+        if t is not None:
+            _need(t, name, torch.float32)
+            if t.numel() != 1:
+                raise ValueError(f"{name} must hold one float32")
     return ctypes.byref(MoeLayerOptionsC(act, clamp, int(bool(apply_router_weight_on_input)),
-                                         int(chunk_tokens), int(batched_max_tokens)))
+                                         int(chunk_tokens), int(batched_max_tokens),
+                                         QUANT_FP8 if fp8 else QUANT_NONE, _ptr(a1_scale),
+                                         _ptr(a2_scale)))
 
 
 def _weights_arg(expert_weights: Optional[torch.Tensor], T: int, k: int, dev):
@@ -99,13 +109,20 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
 
 
 class Weights:
-    """Expert weights of one GEMM: bf16 [E_l, N, K], or MXFP4 packed uint8
-    [E_l, N, K/2] with uint8 E8M0 scales [E_l, N, K/32]."""
+    """Expert weights of one GEMM: bf16 [E_l, N, K]; MXFP4 packed uint8
+    [E_l, N, K/2] with uint8 E8M0 scales [E_l, N, K/32]; or FP8 E4M3 codes
+    (uint8 or float8_e4m3fn) [E_l, N, K] with float32 scales [E_l, N]."""
 
     def __init__(self, data: torch.Tensor, scales: Optional[torch.Tensor] = None):
+        if data.dtype == torch.float8_e4m3fn:
+            data = data.view(torch.uint8)
         if scales is None:
             _need(data, "weights", torch.bfloat16)
             self.dtype = DTYPE_BF16
+        elif scales.dtype == torch.float32:
+            _need(data, "weights", torch.uint8)
+            _need(scales, "scales", torch.float32, tuple(data.shape[:2]), data.device)
+            self.dtype = DTYPE_FP8_E4M3
         else:
             _need(data, "weights", torch.uint8)
             _need(scales, "scales", torch.uint8, device=data.device)
@@ -138,10 +155,10 @@ def moe_permuted_rows(T: int, k: int) -> int:
 
 def moe_workspace_size(T: int, k: int, E: int, E_l: int, H: int, I: int,
                        w_dtype: int = DTYPE_BF16, shared_I: int = 0, chunk_tokens: int = 0,
-                       batched_max_tokens: int = 0) -> int:
+                       batched_max_tokens: int = 0, fp8: bool = False) -> int:
     """Workspace bytes of the fused calls (the shared expert's included)."""
     n = ctypes.c_size_t(0)
-    opts = _options(chunk_tokens=chunk_tokens, batched_max_tokens=batched_max_tokens)
+    opts = _options(chunk_tokens=chunk_tokens, batched_max_tokens=batched_max_tokens, fp8=fp8)
     _check(lib().moe_workspace_size(T, k, E, E_l, H, I, w_dtype, shared_I, opts, ctypes.byref(n)),
            "moe_workspace_size")
     return int(n.value)
@@ -216,6 +233,129 @@ def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
                              R_pad, map.data_ptr(), offsets.data_ptr(), _ptr(inv), _ptr(x_perm),
                              _ptr(x_weights), None, 0, _stream(stream)), "moe_permute")
     return {"map": map, "offsets": offsets, "inv": inv, "x_perm": x_perm, "R_pad": R_pad}
+
+
+def moe_quantize_fp8(x: torch.Tensor, static_scale: Optional[torch.Tensor] = None,
+                     row_weights: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None, row_count: Optional[torch.Tensor] = None,
+                     stream=None):
+    """Per-row FP8 E4M3 quantization of bf16 rows -> (codes uint8 [rows, H],
+    scales float32 [rows]).  row_count: an int32 device scalar (say offsets[E_l:])
+    limiting the rows quantized."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, H]")
+    rows, H = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _need(q, "q", torch.uint8, (rows, H), dev)
+    _need(scales, "scales", torch.float32, (rows,), dev)
+    if static_scale is not None:
+        _need(static_scale, "static_scale", torch.float32, device=dev)
+    if row_weights is not None:
+        _need(row_weights, "row_weights", torch.float32, device=dev)
+        if row_weights.numel() != rows:
+            raise ValueError("row_weights must hold one float32 per row")
+    if row_count is not None:
+        _need(row_count, "row_count", torch.int32, device=dev)
+    _check(lib().moe_quantize_fp8(x.data_ptr(), rows, H, _ptr(static_scale), _ptr(row_weights),
+                                  _ptr(row_count), q.data_ptr(), scales.data_ptr(),
+                                  _stream(stream)),
+           "moe_quantize_fp8")
+    return q, scales
+
+
+def moe_permute_fp8(topk_ids: torch.Tensor, E: int, xq: torch.Tensor, x_scales: torch.Tensor,
+                    E_l: Optional[int] = None, expert_map: Optional[torch.Tensor] = None,
+                    R_pad: Optional[int] = None, map: Optional[torch.Tensor] = None,
+                    offsets: Optional[torch.Tensor] = None, inv: Optional[torch.Tensor] = None,
+                    xq_perm: Optional[torch.Tensor] = None,
+                    xq_perm_scales: Optional[torch.Tensor] = None, want_inv: bool = True,
+                    stream=None):
+    """moe_permute on FP8 rows -> dict(map, offsets, inv, xq_perm uint8 [R_pad, H],
+    xq_perm_scales float32 [R_pad], R_pad)."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    E_l = E if E_l is None else E_l
+    _need(xq, "xq", torch.uint8, device=dev)
+    if xq.dim() != 2 or xq.shape[0] != T:
+        raise ValueError("xq must be [T, H]")
+    H = xq.shape[1]
+    _need(x_scales, "x_scales", torch.float32, (T,), dev)
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty((E_l + 1,), dtype=torch.int32, device=dev)
+    if inv is None and want_inv and R_pad > 0:
+        inv = torch.empty((R_pad,), dtype=torch.int32, device=dev)
+    if xq_perm is None:
+        xq_perm = torch.empty((R_pad, H), dtype=torch.uint8, device=dev)
+    if xq_perm_scales is None:
+        xq_perm_scales = torch.empty((R_pad,), dtype=torch.float32, device=dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    _need(offsets, "offsets", torch.int32, (E_l + 1,), dev)
+    _need(xq_perm, "xq_perm", torch.uint8, (R_pad, H), dev)
+    _need(xq_perm_scales, "xq_perm_scales", torch.float32, (R_pad,), dev)
+    _check(lib().moe_permute_fp8(topk_ids.data_ptr(), _ptr(expert_map), T, k, E, E_l,
+                                 xq.data_ptr(), x_scales.data_ptr(), H, R_pad, map.data_ptr(),
+                                 offsets.data_ptr(), _ptr(inv), xq_perm.data_ptr(),
+                                 xq_perm_scales.data_ptr(), _stream(stream)), "moe_permute_fp8")
+    return {"map": map, "offsets": offsets, "inv": inv, "xq_perm": xq_perm,
+            "xq_perm_scales": xq_perm_scales, "R_pad": R_pad}
+
+
+def moe_grouped_gemm1_act_fp8(a_perm: torch.Tensor, a_scales: torch.Tensor,
+                              offsets: torch.Tensor, w1: Weights, I: int,
+                              h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                              activation_clamp: Optional[float] = None, stream=None,
+                              split: bool = True,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM1 + activation on FP8 rows and FP8 weights -> bf16 [R_pad, I]."""
+    _need(a_perm, "a_perm", torch.uint8)
+    R_pad, H = a_perm.shape
+    dev = a_perm.device
+    _need(a_scales, "a_scales", torch.float32, (R_pad,), dev)
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_fp8(
+        a_perm.data_ptr(), a_scales.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I, w1.ref(),
+        _act(activation), 0.0 if activation_clamp is None else float(activation_clamp),
+        h.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_fp8")
+    return h
+
+
+def moe_grouped_gemm2_fp8(h_perm: torch.Tensor, h_scales: torch.Tensor, offsets: torch.Tensor,
+                          w2: Weights, H: int, y: Optional[torch.Tensor] = None, stream=None,
+                          split: bool = True,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM2 on FP8 rows and FP8 weights -> bf16 [R_pad, H]."""
+    _need(h_perm, "h_perm", torch.uint8)
+    R_pad, I = h_perm.shape
+    dev = h_perm.device
+    _need(h_scales, "h_scales", torch.float32, (R_pad,), dev)
+    _need(offsets, "offsets", torch.int32, (w2.E_l + 1,), dev)
+    if w2.N != H or w2.K != I:
+        raise ValueError(f"w2 must be [E_l, H={H}, I={I}]")
+    if y is None:
+        y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (R_pad, H), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm2_fp8(
+        h_perm.data_ptr(), h_scales.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
+        y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_fp8")
+    return y
 
 
 def moe_permute_batched(topk_ids: torch.Tensor, E: int, max_tokens: int, E_l: Optional[int] = None,
@@ -455,7 +595,9 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
                                   map: Optional[torch.Tensor] = None, stream=None,
                                   activation=ACT_SILU, activation_clamp: Optional[float] = None,
                                   apply_router_weight_on_input: bool = False,
-                                  batched_max_tokens: int = 0):
+                                  batched_max_tokens: int = 0, fp8: bool = False,
+                                  a1_scale: Optional[torch.Tensor] = None,
+                                  a2_scale: Optional[torch.Tensor] = None):
     """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k]).
     batched_max_tokens > 0: batched experts format, R_pad = E_l * batched_max_tokens."""
     _need(logits, "logits", torch.float32)
@@ -478,13 +620,13 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
     if expert_map is not None:
         _need(expert_map, "expert_map", torch.int32, (E,), dev)
     nbytes = (moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype,
-                                 batched_max_tokens=batched_max_tokens) if T > 0 else 0)
+                                 batched_max_tokens=batched_max_tokens, fp8=fp8) if T > 0 else 0)
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts_unfinalized(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(),
         _options(activation, activation_clamp, apply_router_weight_on_input, 0,
-                 batched_max_tokens), R_pad,
+                 batched_max_tokens, fp8, a1_scale, a2_scale), R_pad,
         gemm2_permuted.data_ptr(),
         expert_weights.data_ptr(), map.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts_unfinalized")
@@ -499,7 +641,9 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
                       workspace: Optional[torch.Tensor] = None, stream=None,
                       activation=ACT_SILU, activation_clamp: Optional[float] = None,
                       apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
-                      inplace: bool = False, batched_max_tokens: int = 0) -> torch.Tensor:
+                      inplace: bool = False, batched_max_tokens: int = 0, fp8: bool = False,
+                      a1_scale: Optional[torch.Tensor] = None,
+                      a2_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is]).
 
     chunk_tokens > 0 runs it over chunks of that many tokens with a workspace
@@ -527,14 +671,14 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
     nbytes = 0
     if T > 0:
         nbytes = moe_workspace_size(T, k, E, w1.E_l, H, I, w1.dtype, shared_I, chunk_tokens,
-                                    batched_max_tokens)
+                                    batched_max_tokens, fp8)
     ws = _workspace(nbytes, dev, workspace, stream)
     _check(lib().moe_fused_experts(
         logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
         float(rsf), _ptr(expert_map), w1.ref(), w2.ref(), shared_I, _ptr(ws1), _ptr(ws2),
         float(rsf_fin),
         _options(activation, activation_clamp, apply_router_weight_on_input, chunk_tokens,
-                 batched_max_tokens),
+                 batched_max_tokens, fp8, a1_scale, a2_scale),
         out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
         "moe_fused_experts")
     return out

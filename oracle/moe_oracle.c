@@ -167,9 +167,17 @@ static double dot_row(const oracle_weights* w, int64_t row, int64_t K, const dou
       acc += kE2M1[code] * oracle_e8m0_scale(s[kk / 32]) * v[kk];
     }
   } else if (w->fmt == OR_W_FP8) {
+    /* the 256 decoded values, each from oracle_e4m3_decode */
+    static double table[256];
+    static int ready = 0;
+#pragma omp critical(e4m3_table)
+    if (!ready) {
+      for (int c = 0; c < 256; ++c) table[c] = oracle_e4m3_decode((uint8_t)c);
+      ready = 1;
+    }
     const uint8_t* p = (const uint8_t*)w->data + row * K;
     const double sc = (double)((const float*)w->scales)[row];
-    for (int64_t kk = 0; kk < K; ++kk) acc += oracle_e4m3_decode(p[kk]) * sc * v[kk];
+    for (int64_t kk = 0; kk < K; ++kk) acc += table[p[kk]] * sc * v[kk];
   } else {
     const uint16_t* p = (const uint16_t*)w->data + row * K;
     for (int64_t kk = 0; kk < K; ++kk) acc += bf16_val(p[kk]) * v[kk];

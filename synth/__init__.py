@@ -118,6 +118,20 @@ def mxfp4_quantize(w_bf16: np.ndarray):
     return packed, scales
 
 
+def fp8_quantize_rows(w_bf16: np.ndarray):
+    """Test weights in FP8 E4M3 with one float32 scale per row (per output
+    channel): bf16 bits [..., K] -> (codes uint8 [..., K], scales float32 [...]).
+    scale = amax / 448 of the row (1 for an all-zero row); the codes are torch's
+    round-to-nearest-even cast of w / scale, clamped to +-448 first."""
+    import torch
+    w = bf16_bits_to_f32(np.ascontiguousarray(w_bf16, dtype=np.uint16))
+    amax = np.abs(w).max(axis=-1)
+    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = np.clip(w / scales[..., None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales
+
+
 def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (bit shift, no arithmetic)."""
     return (a.astype(np.uint32) << 16).view(np.float32)

@@ -15,7 +15,7 @@ from typing import Optional
 import numpy as np
 
 from . import (TID_LOGITS, TID_W1, TID_W2, TID_WS1, TID_WS2, TID_X, biased_logits,
-               mxfp4_quantize, normal_bf16, normal_f32, zipf_log_bias)
+               fp8_quantize_rows, mxfp4_quantize, normal_bf16, normal_f32, zipf_log_bias)
 
 SOFTMAX, SIGMOID = 0, 1
 
@@ -36,6 +36,7 @@ class MoeConfig:
     local_first: int = 0            # first global id owned by this rank
     shared_I: int = 0               # shared-expert intermediate (0: none)
     mxfp4: bool = False
+    fp8: bool = False               # FP8 E4M3 weights (per channel) and activations (per token)
     zipf_s: float = 0.0             # Zipf exponent of the logit bias (0: none)
     deferred: bool = False
 
@@ -59,7 +60,15 @@ EP_DECODE = MoeConfig("ep_rank3of8_decode", T=64, H=7168, I=2048, E=256, k=8,
 DEEPSEEK_MXFP4 = MoeConfig("deepseekv3_mxfp4_2048tok", T=2048, H=7168, I=2048, E=256, k=8,
                            score=SIGMOID, renormalize=True, rsf=2.5, seed=5, mxfp4=True)
 
-ALL = {c.name: c for c in (TINY, MIXTRAL, DEEPSEEK, EP_DECODE, DEEPSEEK_MXFP4)}
+# FP8 variants of the two prefill shapes: weights quantized per output channel
+# from the same bf16 draws, activations quantized per token inside the layer
+MIXTRAL_FP8 = MoeConfig("mixtral8x7b_fp8_prefill_4096tok", T=4096, H=4096, I=14336, E=8, k=2,
+                        score=SOFTMAX, renormalize=True, rsf=1.0, seed=2, zipf_s=1.1, fp8=True)
+DEEPSEEK_FP8 = MoeConfig("deepseekv3_fp8_2048tok", T=2048, H=7168, I=2048, E=256, k=8,
+                         score=SIGMOID, renormalize=True, rsf=2.5, seed=3, fp8=True)
+
+ALL = {c.name: c for c in (TINY, MIXTRAL, DEEPSEEK, EP_DECODE, DEEPSEEK_MXFP4, MIXTRAL_FP8,
+                           DEEPSEEK_FP8)}
 
 EP_DECODE_BATCHES = (1, 8, 64)
 EP_DECODE_DRAWS = 16
@@ -103,6 +112,10 @@ def make_weights(cfg: MoeConfig):
     if cfg.mxfp4:
         w["w1_q"], w["w1_s"] = mxfp4_quantize(w["w1"])
         w["w2_q"], w["w2_s"] = mxfp4_quantize(w["w2"])
+        del w["w1"], w["w2"]
+    if cfg.fp8:
+        w["w1_q"], w["w1_s"] = fp8_quantize_rows(w["w1"])
+        w["w2_q"], w["w2_s"] = fp8_quantize_rows(w["w2"])
         del w["w1"], w["w2"]
     return w
 

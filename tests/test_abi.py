@@ -178,8 +178,10 @@ def test_fused_errors(L):
     assert call(opts=_opts(chunk=8)) == INVALID  # the deferred form takes no chunking
 
 
-def _opts(activation=0, clamp=0.0, weight_on_input=0, chunk=0, batched=0):
-    return ctypes.byref(_lib.MoeLayerOptionsC(activation, clamp, weight_on_input, chunk, batched))
+def _opts(activation=0, clamp=0.0, weight_on_input=0, chunk=0, batched=0, quant=0, a1=None,
+          a2=None):
+    return ctypes.byref(_lib.MoeLayerOptionsC(activation, clamp, weight_on_input, chunk, batched,
+                                              quant, a1, a2))
 
 
 def test_fused_finalized_errors(L):
@@ -226,6 +228,52 @@ def test_batched_errors(L):
     # deferred batched: R_pad must hold E_l * capacity rows
     assert u(P, P, 16, 128, 256, 8, 8, 2, 0, 1, 1.0, None, _w(), _w(), _opts(batched=16), 127,
              P, P, P, P, 1 << 30, None) == SIZE
+
+
+def test_fp8_errors(L):
+    q = L.moe_quantize_fp8
+    # (x, rows, H, static, row_weights, row_count, q, scales, stream)
+    assert q(P, 4, 120, None, None, None, P * 64, P * 128, None) == INVALID   # H % 16
+    assert q(P, -1, 128, None, None, None, P * 64, P * 128, None) == INVALID
+    assert q(P, 4, 128, P + 2, None, None, P * 64, P * 128, None) == MISALIGNED
+    assert q(P, 4, 128, None, None, None, P + 256, P * 128, None) == CONFLICT  # q inside x
+    assert q(P, 0, 128, None, None, None, None, None, None) == OK
+    FP8 = 3
+    g1 = L.moe_grouped_gemm1_act_fp8
+    # (a, a_scales, offsets, E_l, R_pad, H, I, w1, act, clamp, h, ws, wsb, stream)
+    assert g1(P, P, P, 8, 128, 128, 256, _w(), 0, 0.0, P * 64, None, 0, None) == INVALID  # bf16 w
+    assert g1(P, P, P, 8, 128, 192, 256, _w(FP8, P, P), 0, 0.0, P * 64, None, 0, None) == INVALID
+    assert g1(P, None, P, 8, 128, 128, 256, _w(FP8, P, P), 0, 0.0, P * 64, None, 0, None) == INVALID
+    assert g1(P, P, P, 8, 128, 128, 256, _w(FP8, P, None), 0, 0.0, P * 64, None, 0, None) == INVALID
+    # FP8 weights with bf16 activations
+    assert L.moe_grouped_gemm1_act(P, P, 8, 128, 128, 256, _w(FP8, P, P), 0, 0.0, P * 64, None,
+                                   0, None) == INVALID
+    assert b"FP8 activations" in L.moe_last_error()
+    g2 = L.moe_grouped_gemm2_fp8
+    assert g2(P, P, P, 8, 128, 256, 128, _w(), P * 64, None, 0, None) == INVALID
+    pf = L.moe_permute_fp8
+    # (ids, emap, T, k, E, E_l, xq, xs, H, R_pad, map, offsets, inv, xq_perm, ps, stream)
+    assert pf(P, None, 16, 2, 8, 8, P, P, 120, 32, P, P, None, P * 64, P * 128, None) == INVALID
+    assert pf(P, None, 16, 2, 8, 8, P, P, 128, 31, P, P, None, P * 64, P * 128, None) == SIZE
+    assert pf(P, None, 16, 2, 8, 8, P, None, 128, 32, P, P, None, P * 64, P * 128, None) == INVALID
+    assert pf(P, None, 16, 2, 8, 8, P, P, 128, 32, P, P, None, P + 1024, P * 128, None) == CONFLICT
+    u = L.moe_fused_experts_unfinalized
+
+    def call(w=_w(FP8, P, P), opts=None, T=16, H=128, I=256):
+        return u(P, P, T, H, I, 8, 8, 2, 0, 1, 1.0, None, w, w, opts, 32, P, P, P, P, 1 << 30, None)
+    assert call(opts=_opts(quant=1, batched=16)) == UNSUPPORTED
+    assert call(opts=_opts(quant=7)) == UNSUPPORTED
+    assert call(w=_w(), opts=_opts(quant=1)) == INVALID          # bf16 weights
+    assert call(opts=None) == INVALID                            # FP8 weights, no quantization
+    assert call(w=_w(), opts=_opts(a1=P)) == INVALID             # a static scale without FP8
+    assert call(opts=_opts(quant=1), H=192) == INVALID           # H % 128
+    assert call(opts=_opts(quant=1, a1=P + 2)) == MISALIGNED
+    assert call(opts=_opts(quant=1), T=0) == OK
+    n0, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.moe_workspace_size(64, 8, 256, 256, 7168, 2048, FP8, 0, None, ctypes.byref(n0)) == OK
+    assert L.moe_workspace_size(64, 8, 256, 256, 7168, 2048, FP8, 0, _opts(quant=1),
+                                ctypes.byref(n1)) == OK
+    assert n1.value >= n0.value + 64 * 7168 + 512 * 2048
 
 
 def test_grouped_gemm_workspace_size():

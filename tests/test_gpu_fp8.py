@@ -1,0 +1,227 @@
+"""GPU parity of the FP8 E4M3 path (quantized activations of vLLM's
+modular_kernel.py prepare/apply with per-token scales, FP8 weights with
+per-channel scales) against the oracle.
+
+- moe_quantize_fp8: codes and scales bit-exact against the oracle's float32
+  quantizer (dynamic, static, with row weights, zero rows, wide rows);
+- moe_permute_fp8: map and offsets as the bf16 permute, gathered codes and
+  scales bit-exact;
+- both FP8 GEMMs on every tile shape and on the split path, against the
+  oracle on the same codes (bar 1e-2, the bf16 bar: both sides multiply the
+  same quantized values, so only the fp32 accumulation and the bf16 output
+  rounding separate them);
+- whole FP8 layers (fused, deferred at the EP decode shape, static scales,
+  router weight on the input, chunked) against the oracle's fp8 mode, and
+  the full-size Mixtral and DeepSeek-V3 FP8 workloads on sampled tokens.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_scan_amd as moe
+import oracle
+import synth
+from synth import configs
+
+from gpu_util import (dev, dev_bf16, host_bf16_bits, host_f64, need_gpu, rel_fro,
+                      sample_tokens, segments_of)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rows,H,mode", [(37, 256, "dynamic"), (5, 7168, "dynamic"),
+                                         (16, 128, "static"), (9, 2048, "weights")])
+def test_quantize_bit_exact(rows, H, mode):
+    x = synth.normal_bf16(rows + H, 0, (rows, H), std=3.0)
+    x[2] = 0                          # an all-zero row
+    x[3, :7] = [0x3C00, 0xBC00, 0x0001, 0x8001, 0x4380, 0xC3E0, 0x7F7F & 0x3FFF]  # odd values
+    static = np.array([0.0123], dtype=np.float32) if mode == "static" else None
+    rw = synth.normal_f32(rows, 3, (rows,)) if mode == "weights" else None
+    q, sc = moe.moe_quantize_fp8(dev_bf16(x), None if static is None else dev(static),
+                                 None if rw is None else dev(rw))
+    torch.cuda.synchronize()
+    if rw is not None:
+        # the oracle quantizes the rows the kernel sees: bf16(w * x) in fp32
+        xf = synth.bf16_bits_to_f32(x) * rw[:, None].astype(np.float32)
+        u = xf.astype(np.float32).view(np.uint32).astype(np.uint64)
+        x_in = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    else:
+        x_in = x
+    ref_q, ref_s = oracle.quantize_fp8_rows(x_in, None if static is None else float(static[0]))
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_permute_fp8_bit_exact():
+    T, k, E, H = 45, 3, 8, 384
+    logits = synth.normal_f32(91, 1, (T, E))
+    ids, _ = moe.moe_route_topk(dev(logits), k)
+    x = synth.normal_bf16(91, 0, (T, H))
+    xq, xs = oracle.quantize_fp8_rows(x)
+    p = moe.moe_permute_fp8(ids, E, dev(xq), dev(xs))
+    std = moe.moe_permute(ids, E)
+    torch.cuda.synchronize()
+    m = p["map"].cpu().numpy()
+    assert np.array_equal(m, std["map"].cpu().numpy())
+    assert np.array_equal(p["offsets"].cpu().numpy(), std["offsets"].cpu().numpy())
+    got_q, got_s = p["xq_perm"].cpu().numpy(), p["xq_perm_scales"].cpu().numpy()
+    for t in range(T):
+        for j in range(k):
+            assert np.array_equal(got_q[m[t, j]], xq[t])
+            assert got_s[m[t, j]] == xs[t]
+
+
+GEMM_CASES = [
+    # name, counts per local expert, H, I
+    ("thin_tiles", [0, 1, 5, 33, 2, 0, 17, 40], 256, 256),
+    ("wide_tiles", [70, 0, 130, 55], 384, 384),
+    ("wide_ragged_fragments", [0, 3, 129, 31, 64, 97], 256, 128),
+    ("mid_tiles", [300, 1, 420], 256, 512),
+    ("big_tiles", [700, 613], 512, 384),
+    ("split_decode", [1, 0, 2, 1, 0, 3], 1024, 512),
+    ("split_wide", [20, 30, 0, 16], 1024, 512),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_fp8_gemms(case):
+    name, counts, H, I = case
+    E_l = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R_l = int(offsets[-1])
+    R_pad = ((R_l + 127) // 128) * 128
+    seed = sum(counts) + 92
+    a = synth.normal_bf16(seed, 0, (R_pad, H))
+    hb = synth.normal_bf16(seed, 7, (R_pad, I))
+    aq, asc = oracle.quantize_fp8_rows(a)
+    hq, hsc = oracle.quantize_fp8_rows(hb)
+    aq[R_l:] = 0x7F   # E4M3 NaN in rows the kernels must not read
+    hq[R_l:] = 0x7F
+    w1q, w1s = synth.fp8_quantize_rows(synth.normal_bf16(seed, 2, (E_l, 2 * I, H),
+                                                         std=1 / np.sqrt(H)))
+    w2q, w2s = synth.fp8_quantize_rows(synth.normal_bf16(seed, 3, (E_l, H, I),
+                                                         std=1 / np.sqrt(I)))
+    off = dev(offsets)
+    h = moe.moe_grouped_gemm1_act_fp8(dev(aq), dev(asc), off, moe.Weights(dev(w1q), dev(w1s)), I)
+    y = moe.moe_grouped_gemm2_fp8(dev(hq), dev(hsc), off, moe.Weights(dev(w2q), dev(w2s)), H)
+    torch.cuda.synchronize()
+    eor = segments_of(offsets, R_l)
+    ref_h = oracle.hidden_rows_fp8(aq[:R_l], asc[:R_l], oracle.Weights(w1q, w1s.reshape(-1)),
+                                   eor, I)
+    ref_y = oracle.out_rows_fp8(hq[:R_l], hsc[:R_l], oracle.Weights(w2q, w2s.reshape(-1)), eor, H)
+    assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
+    assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
+
+
+def _fp8_cfg(name, T, H, I, E, k, seed, score=configs.SOFTMAX, renorm=True, rsf=1.0):
+    return configs.MoeConfig(name, T=T, H=H, I=I, E=E, k=k, score=score, renormalize=renorm,
+                             rsf=rsf, seed=seed, fp8=True)
+
+
+def _upload(w):
+    return (moe.Weights(dev(w["w1_q"]), dev(w["w1_s"])),
+            moe.Weights(dev(w["w2_q"]), dev(w["w2_s"])))
+
+
+def _oracle_w(w):
+    E_l = w["w1_q"].shape[0]
+    return (oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1)),
+            oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1)))
+
+
+def _ref(cfg, x, logits, w, **kw):
+    W1, W2 = _oracle_w(w)
+    # per-expert rows of the flattened [E_l * N] weights: the oracle indexes
+    # expert e's row n as e * N + n, as the packed arrays are laid out
+    return oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize,
+                             cfg.rsf, expert_map=configs.expert_map(cfg), fp8=True, **kw)
+
+
+@pytest.mark.parametrize("chunk", [0, 96])
+def test_fp8_layer_fused_and_deferred(chunk):
+    cfg = _fp8_cfg("f", T=300, H=512, I=384, E=16, k=4, seed=93, score=configs.SIGMOID, rsf=2.5)
+    x, logits = configs.make_activations(cfg)
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    xd, ld = dev_bf16(x), dev(logits)
+    args = (ld, xd, W1, W2, cfg.k, cfg.score, cfg.renormalize, cfg.rsf)
+    out = moe.moe_fused_experts(*args, fp8=True, chunk_tokens=chunk)
+    y, ew, m = moe.moe_fused_experts_unfinalized(*args, fp8=True)
+    fin = moe.moe_finalize(y, ew, m)
+    torch.cuda.synchronize()
+    ref = _ref(cfg, x, logits, w)
+    assert rel_fro(host_f64(out), ref["out"]) < TOL
+    assert rel_fro(host_f64(fin), ref["out"]) < TOL
+    mm = m.cpu().numpy()
+    assert rel_fro(host_f64(y)[mm.reshape(-1)], ref["y_routes"].reshape(-1, cfg.H)) < TOL
+
+
+def test_fp8_layer_static_scales_and_weight_on_input():
+    cfg = _fp8_cfg("s", T=200, H=256, I=256, E=8, k=1, seed=94, score=configs.SIGMOID,
+                   renorm=False)
+    x, logits = configs.make_activations(cfg)
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    xd, ld = dev_bf16(x), dev(logits)
+    a1, a2 = 0.011, 0.0009
+    out = moe.moe_fused_experts(ld, xd, W1, W2, 1, cfg.score, False, 1.0, fp8=True,
+                                a1_scale=torch.tensor([a1], device="cuda"),
+                                a2_scale=torch.tensor([a2], device="cuda"))
+    out_w = moe.moe_fused_experts(ld, xd, W1, W2, 1, cfg.score, False, 1.0, fp8=True,
+                                  apply_router_weight_on_input=True)
+    torch.cuda.synchronize()
+    ref = _ref(cfg, x, logits, w, a1_scale=a1, a2_scale=a2)
+    assert rel_fro(host_f64(out), ref["out"]) < TOL
+    ref_w = _ref(cfg, x, logits, w, weight_on_input=True)
+    assert rel_fro(host_f64(out_w), ref_w["out"]) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_fp8_ep_decode_deferred(T):
+    base = configs.EP_DECODE
+    cfg = configs.MoeConfig("ep_fp8", T=T, H=base.H, I=base.I, E=base.E, k=base.k,
+                            score=base.score, renormalize=True, rsf=base.rsf, seed=base.seed,
+                            E_local=base.E_local, local_first=base.local_first, fp8=True)
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    emap = configs.expert_map(cfg)
+    x, logits = configs.make_activations(cfg, seed=configs.EP_DECODE_DRAW_SEED0 + 1)
+    y, ew, m = moe.moe_fused_experts_unfinalized(dev(logits), dev_bf16(x), W1, W2, cfg.k,
+                                                 cfg.score, True, cfg.rsf,
+                                                 expert_map=dev(emap), fp8=True)
+    out = moe.moe_finalize(y, ew, m)
+    torch.cuda.synchronize()
+    ref = _ref(cfg, x, logits, w)
+    assert rel_fro(host_f64(out), ref["out"]) < TOL
+
+
+@pytest.mark.parametrize("cfg", [configs.MIXTRAL_FP8, configs.DEEPSEEK_FP8],
+                         ids=lambda c: c.name)
+def test_fp8_full_size(cfg):
+    x, logits = configs.make_activations(cfg)
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    xd, ld = dev_bf16(x), dev(logits)
+    out = moe.moe_fused_experts(ld, xd, W1, W2, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
+                                fp8=True)
+    out2 = moe.moe_fused_experts(ld, xd, W1, W2, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
+                                 fp8=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(out), host_bf16_bits(out2))
+    toks = sample_tokens(cfg.T, 16, 9)
+    ref = _ref(cfg, x, logits, w, tokens=toks)
+    got = host_f64(out)[toks]
+    assert np.all(np.isfinite(got))
+    assert rel_fro(got, ref["out"]) < TOL

@@ -112,3 +112,17 @@ def test_config_recipes():
     assert w["w1"].shape == (8, 512, 128) and w["w2"].shape == (8, 128, 256)
     w1f = synth.bf16_bits_to_f32(w["w1"]).astype(np.float64)
     assert abs(w1f.std() - 1 / np.sqrt(128)) < 2e-3
+
+
+def test_fp8_weight_quantizer_per_row():
+    import torch
+    w = synth.normal_bf16(81, 2, (3, 16, 256), std=0.05)
+    w[1, 4] = 0
+    q, s = synth.fp8_quantize_rows(w)
+    assert q.shape == w.shape and s.shape == w.shape[:-1]
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy() * s[..., None]
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    assert np.all(q[1, 4] == 0) and s[1, 4] == 1.0
+    assert np.all(np.abs(dec - wf) <= np.maximum(np.abs(wf) * 2.0 ** -4, 2.0 ** -10 * s[..., None]))
+    top = np.abs(torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy())
+    assert np.all(top.reshape(-1, 256)[np.arange(48) != 20].max(axis=1) == 448.0)
