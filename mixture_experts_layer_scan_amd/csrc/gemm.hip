@@ -922,9 +922,14 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 template <bool WQ, bool F8>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
-  //                          BM   BN  WM WN ST  gated  WQ  GM  F8
-  using Big   = TileCfg<128, 256, 2, 2, S3, false, WQ, 8, F8>;
-  using BigG  = TileCfg<128, 256, 2, 2, S3, true, WQ, 8, F8>;
+  // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
+  // each): with two waves per SIMD one computes while the other waits on its
+  // loads (measured: 5 % faster for bf16, 17 % for fp8 than four waves).
+  // MXFP4 weights keep four (their scale loads and expansion registers).
+  static constexpr int BIG_WM = WQ ? 2 : 4;
+  //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
+  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8>;
+  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8>;
   using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8>;
   using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8>;
   using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8>;
