@@ -95,8 +95,11 @@ GEMM_CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split_ok", "no_split"])
 @pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
-def test_fp8_gemms(case):
+def test_fp8_gemms(case, split):
+    """With split=False (no scratch) the weight-streaming shapes take the
+    eight-wave tile, with a scratch the four-wave one that may split."""
     name, counts, H, I = case
     E_l = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -114,8 +117,10 @@ def test_fp8_gemms(case):
     w2q, w2s = synth.fp8_quantize_rows(synth.normal_bf16(seed, 3, (E_l, H, I),
                                                          std=1 / np.sqrt(I)))
     off = dev(offsets)
-    h = moe.moe_grouped_gemm1_act_fp8(dev(aq), dev(asc), off, moe.Weights(dev(w1q), dev(w1s)), I)
-    y = moe.moe_grouped_gemm2_fp8(dev(hq), dev(hsc), off, moe.Weights(dev(w2q), dev(w2s)), H)
+    h = moe.moe_grouped_gemm1_act_fp8(dev(aq), dev(asc), off, moe.Weights(dev(w1q), dev(w1s)), I,
+                                      split=split)
+    y = moe.moe_grouped_gemm2_fp8(dev(hq), dev(hsc), off, moe.Weights(dev(w2q), dev(w2s)), H,
+                                  split=split)
     torch.cuda.synchronize()
     eor = segments_of(offsets, R_l)
     ref_h = oracle.hidden_rows_fp8(aq[:R_l], asc[:R_l], oracle.Weights(w1q, w1s.reshape(-1)),
@@ -136,15 +141,14 @@ def _upload(w):
 
 
 def _oracle_w(w):
-    E_l = w["w1_q"].shape[0]
+    # one scale per weight row: expert e's row n is row e * N + n of the
+    # flattened [E_l * N] scales, as the codes are laid out
     return (oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1)),
             oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1)))
 
 
 def _ref(cfg, x, logits, w, **kw):
     W1, W2 = _oracle_w(w)
-    # per-expert rows of the flattened [E_l * N] weights: the oracle indexes
-    # expert e's row n as e * N + n, as the packed arrays are laid out
     return oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize,
                              cfg.rsf, expert_map=configs.expert_map(cfg), fp8=True, **kw)
 

@@ -89,10 +89,12 @@ def test_grouped_gemm2(case):
     assert np.all(host_bf16_bits(y)[R_l:] == NAN_BITS)
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split_ok", "no_split"])
 @pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
-def test_grouped_gemms_mxfp4_weights(case):
+def test_grouped_gemms_mxfp4_weights(case, split):
     """MXFP4 weights (e2m1 + E8M0 per 32 along K): both GEMMs against the
-    oracle's decode of the same packed bytes."""
+    oracle's decode of the same packed bytes (without a scratch the
+    weight-streaming shapes take the eight-wave tile)."""
     name, counts, H, I = case
     E_l, offsets, R_l, R_pad, a, w1, w2 = _setup(counts, H, I, seed=sum(counts) + 2)
     q1, s1 = synth.mxfp4_quantize(w1)
@@ -100,9 +102,9 @@ def test_grouped_gemms_mxfp4_weights(case):
     W1 = moe.Weights(dev(q1), dev(s1))
     W2 = moe.Weights(dev(q2), dev(s2))
     h = torch.full((R_pad, I), float("nan"), dtype=torch.bfloat16, device="cuda")
-    moe.moe_grouped_gemm1_act(dev_bf16(a), dev(offsets), W1, I, h=h)
+    moe.moe_grouped_gemm1_act(dev_bf16(a), dev(offsets), W1, I, h=h, split=split)
     hb = synth.normal_bf16(sum(counts), 8, (R_pad, I))
-    y = moe.moe_grouped_gemm2(dev_bf16(hb), dev(offsets), W2, H)
+    y = moe.moe_grouped_gemm2(dev_bf16(hb), dev(offsets), W2, H, split=split)
     torch.cuda.synchronize()
     eor = segments_of(offsets, R_l)
     ref_h = oracle.hidden_rows(a[:R_l], oracle.Weights(q1, s1), eor, I)
