@@ -18,6 +18,8 @@ bf16 weights.  The other workloads:
                                      per-channel weight scales, per-token activation
                                      scales (quantize -> dispatch -> FP8 GEMMs)
   mixtral8x7b_fp8_prefill_4096tok    the Mixtral shape in FP8 E4M3
+  deepseekv3_mxfp4_fp8act_2048tok    MXFP4 weights with FP8 activations per token (FP8 x e2m1
+                                     on the matrix cores, E8M0 block scales applied by them)
   ep_rank3of8_decode                 one expert-parallel rank's 32 experts at a
                                      decode batch (--tokens 1, 8 or 64), deferred
                                      form followed by the separate finalize; the
@@ -524,7 +526,8 @@ def main():
         "dtype": "fp8" if cfg.fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights"
                 + (", MXFP4-quantized" if cfg.mxfp4 else "")
-                + (", FP8 E4M3 weights per channel, activations per token" if cfg.fp8 else "")
+                + ((", FP8 E4M3 activations per token" if cfg.mxfp4 else
+                    ", FP8 E4M3 weights per channel, activations per token") if cfg.fp8 else "")
                 + ")",
         "config": {"workload": label, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "local_experts": El, "top_k": k,

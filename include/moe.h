@@ -131,9 +131,10 @@ typedef struct moe_layer_options {
  * each token row to FP8 E4M3 before dispatch (moe_quantize_fp8, one scale per
  * row, or the static a1_scale) and each bf16 hidden row before GEMM2 (per row,
  * or a2_scale); both GEMMs then multiply FP8 codes on the matrix cores and
- * apply the row and channel scales in fp32.  Needs FP8 weights, H and I
- * multiples of 128, the standard layout (no batched_max_tokens); the shared
- * expert stays bf16. */
+ * apply the row (and FP8 weights' channel) scales in fp32.  Needs FP8 weights
+ * (H and I multiples of 128) or MXFP4 weights (multiples of 256: FP8 x e2m1
+ * on the matrix cores, the E8M0 block scales applied by them), the standard
+ * layout (no batched_max_tokens); the shared expert stays bf16. */
 enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1 };
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
@@ -255,10 +256,12 @@ int moe_permute_fp8(const int32_t* topk_ids, const int32_t* expert_map, int64_t 
  * (E4M3 products summed exactly in fp32 by the 32x32x64 MFMA), then, for
  * GEMM1, act(gate) * up and one rounding to bf16.
  *   a_perm / h_perm  (device) u8 [R_pad, H or I];  a_scales / h_scales fp32 [R_pad]
- *   w1 / w2          MOE_DTYPE_FP8_E4M3 weights
+ *   w1 / w2          MOE_DTYPE_FP8_E4M3 weights, or MOE_DTYPE_MXFP4 (then
+ *                    C[r, n] = a_scale[r] * sum_k a[r, k] * e2m1[n, k] * 2^(e8m0 - 127),
+ *                    the block scales applied by the matrix cores)
  *   h / y            (device) bf16 [R_pad, I or H] out
  *   workspace        as for the bf16 calls
- * Limits: H and I multiples of 128. */
+ * Limits: H and I multiples of 128 (FP8 weights) or 256 (MXFP4 weights). */
 int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
                               const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
                               int32_t I, const moe_weights* w1, int32_t activation,

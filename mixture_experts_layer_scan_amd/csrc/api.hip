@@ -128,10 +128,11 @@ const void* scales_of(const moe_weights* w) {
   return w->dtype == MOE_DTYPE_BF16 ? nullptr : w->scales;
 }
 
-// FP8 weights multiply FP8 activations only, and FP8 activations FP8 weights.
+// FP8 weights multiply FP8 activations only; FP8 activations multiply FP8 or
+// MXFP4 weights.
 int check_pairing(const moe_weights* w, bool fp8_act, const char* name) {
-  if (fp8_act && w->dtype != MOE_DTYPE_FP8_E4M3)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 activations need FP8 weights", name);
+  if (fp8_act && w->dtype != MOE_DTYPE_FP8_E4M3 && w->dtype != MOE_DTYPE_MXFP4)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 activations need FP8 or MXFP4 weights", name);
   if (!fp8_act && w->dtype == MOE_DTYPE_FP8_E4M3)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 weights need FP8 activations", name);
   return MOE_OK;
@@ -433,7 +434,7 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
                   workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
-                  a_scales};
+                  a_scales, w->dtype == MOE_DTYPE_MXFP4};
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -516,9 +517,13 @@ int moe_permute_fp8(const int32_t* topk_ids, const int32_t* expert_map, int64_t 
   return MOE_OK;
 }
 
-int check_fp8_dims(int32_t H, int32_t I) {
-  if (H % 128 || I % 128)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "FP8 GEMMs need H and I multiples of 128 (H=%d, I=%d)", H, I);
+// FP8 activations: k-steps of 128; with MXFP4 weights, weight stages of 256
+// (one 8-byte load of E8M0 scales per row and stage)
+int check_fp8_dims(int32_t H, int32_t I, const moe_weights* w = nullptr) {
+  const int q = (w && w->dtype == MOE_DTYPE_MXFP4) ? 256 : 128;
+  if (H % q || I % q)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "FP8 GEMMs need H and I multiples of %d (H=%d, I=%d)",
+                q, H, I);
   return MOE_OK;
 }
 
@@ -529,7 +534,7 @@ int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
                               size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   MOE_CHECK(check_gemm_dims(H, I));
-  MOE_CHECK(check_fp8_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w1));
   MOE_CHECK(check_activation(activation, activation_clamp));
   if (R_pad > 0) MOE_CHECK(opt_ptr4(a_scales, "a_scales"));
   if (R_pad > 0 && !a_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "a_scales must not be NULL");
@@ -543,7 +548,7 @@ int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const in
                           void* y, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   MOE_CHECK(check_gemm_dims(H, I));
-  MOE_CHECK(check_fp8_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w2));
   if (R_pad > 0) MOE_CHECK(opt_ptr4(h_scales, "h_scales"));
   if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
   return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
@@ -729,7 +734,8 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     if (e != hipSuccess) return hip_fail(e, "gather");
     const int64_t max_rows = moe_permuted_rows(T, k);
     moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
-                     b.split, b.split_bytes, o.act, o.clamp, 0, b.ps};
+                     b.split, b.split_bytes, o.act, o.clamp, 0, b.ps,
+                     w1->dtype == MOE_DTYPE_MXFP4};
     e = moe::launch_grouped_gemm(g1, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm1");
     // the hidden rows of the local routes (offsets[E_l] of them) to FP8
@@ -737,7 +743,7 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
                                  s);
     if (e != hipSuccess) return hip_fail(e, "quantize hidden");
     moe::GemmArgs g2{b.hq, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
-                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs};
+                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs, w2->dtype == MOE_DTYPE_MXFP4};
     e = moe::launch_grouped_gemm(g2, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm2");
     return MOE_OK;
@@ -772,7 +778,7 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
   MOE_CHECK(check_weights(w2, "w2"));
   MOE_CHECK(check_pairing(w1, o.fp8, "w1"));
   MOE_CHECK(check_pairing(w2, o.fp8, "w2"));
-  if (o.fp8) MOE_CHECK(check_fp8_dims(H, I));
+  if (o.fp8) MOE_CHECK(check_fp8_dims(H, I, w1));
   if (o.batch_m > 0) MOE_CHECK(check_capacity(E_l, o.batch_m));
   const int64_t rows = routed_rows(pass_T, k, E_l, o.batch_m);
   MOE_CHECK(check_gemm_extent(rows, H, 2 * int64_t(I)));

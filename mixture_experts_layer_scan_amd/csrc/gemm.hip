@@ -208,7 +208,8 @@ struct TileCfg {
   // one load instruction: 8 rows x 128 bytes
   static constexpr int A_LD = BM / 8 / NWAVES;   // activation loads per wave per k-step
   static constexpr int B_LD = BN / 8 / NWAVES;   // weight loads per wave per weight stage
-  static constexpr int B_KS = WQ ? 4 : 1;        // k-steps per weight stage
+  // k-steps per weight stage (128 bytes of a weight row: 256 k of e2m1)
+  static constexpr int B_KS = WQ ? (F8 ? 2 : 4) : 1;
   // MXFP4: three weight stages, so two stream while one is used (a weight
   // stage lasts four k-steps; with one in flight the stream stalls between)
   static constexpr int B_STAGES = WQ ? 3 : STAGES;
@@ -281,7 +282,6 @@ struct TileCfg {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "whole load instructions");
-  static_assert(!(F8 && WQ), "one weight format");
 };
 
 // First virtual weight row of fragment fn of wave column wn.
@@ -502,7 +502,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         const_cast<uint8_t*>(static_cast<const uint8_t*>(W_scales) +
                              static_cast<int64_t>(e) * N_total * s_row), 0,
         static_cast<int>(static_cast<uint32_t>(N_total) * s_row), kBufferFlags);
-    const bool s_wide = (s_row % 8u) == 0;  // uniform
+    // (FP8 activations with MXFP4 weights need K % 256 == 0: always wide)
+    const bool s_wide = Cfg::F8 || (s_row % 8u) == 0;  // uniform
     constexpr int NSF = Cfg::WQ ? FN : 1;
     uint32_t s_off[NSF];
     u32x2 sc_cur[NSF], sc_nxt[NSF];
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         if (s_wide) {
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) sc_nxt[fn] = load_u64(s_rsrc, s_off[fn], (q0 + q) * 8);
-        } else {
+        } else if constexpr (!Cfg::F8) {
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         const uint32_t sh = 8u * static_cast<uint32_t>(lane >> 5);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          if (s_wide) {
+          if (s_wide || Cfg::F8) {
             sc_cur[fn] = sc_nxt[fn];
           } else {
             sc_cur[fn] = u32x2{(sc_byte[fn][0] << sh) | (sc_byte[fn][1] << (16u + sh)),
@@ -546,6 +547,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     auto scale_of = [&](int fn, int p, int ln) {
       const uint32_t word = p < 2 ? sc_cur[fn].x : sc_cur[fn].y;
       return e8m0_to_f32((word >> (8u * static_cast<uint32_t>(2 * (p & 1) + (ln >> 5)))) & 0xFFu);
+    };
+    // FP8 activations x MXFP4 weights: the E8M0 byte of fragment fn's block
+    // 4p + 2ks + h of the weight stage (k-step position p, sub-step ks, half
+    // h), handed to the MFMA as its B block scale
+    auto scale_byte = [&](int fn, int p, int ks, int ln) -> int {
+      const int block = 4 * p + 2 * ks + (ln >> 5);
+      const uint32_t word = block < 4 ? sc_cur[fn].x : sc_cur[fn].y;
+      return static_cast<int>((word >> (8u * static_cast<uint32_t>(block & 3))) & 0xFFu);
     };
 
     f32x16 acc[FM][FN];
@@ -582,18 +591,26 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // and 4h + 2ks + 1 of its A row and of its W row (k = 64 ks + 32 h ..
     // + 31 of the k-step); the 32x32x64 MFMA runs unscaled (E8M0 127 = 1),
     // the per-row and per-channel scales apply in the epilogue.
+    // FP8 x e2m1: a B lane holds one 32-k block of its weight row (block
+    // 4p + 2ks + h of the weight stage: its 16 bytes and its E8M0 scale);
+    // the MFMA pairs the first 16 values of A half h with B half 0's values
+    // 16h .. 16h + 15 and the last 16 with B half 1's, so A half h reads the
+    // 16-byte halves h of blocks 2ks and 2ks + 1: chunks 4ks + h, 4ks + 2 + h.
     auto load_frags = [&](const uint16_t* as, const uint16_t* bs, int ln, int ks, int p,
                           Frag* af, Frag* bfr, uint4* bq) {
       const int frag_row = ln & 31;
       const int half = ln >> 5;
       const int chunk = Cfg::F8 ? half * 4 + 2 * ks : half * SUB + ks;
+      // FP8 A chunks (see above)
+      const int a_lo = Cfg::WQ ? 4 * ks + half : chunk;
+      const int a_hi = Cfg::WQ ? 4 * ks + 2 + half : chunk + 1;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
         if constexpr (Cfg::F8) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(as + swz(r, chunk));
-          const uint4 hi = *reinterpret_cast<const uint4*>(as + swz(r, chunk + 1));
+          const uint4 lo = *reinterpret_cast<const uint4*>(as + swz(r, a_lo));
+          const uint4 hi = *reinterpret_cast<const uint4*>(as + swz(r, a_hi));
           af[fm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         } else {
@@ -603,7 +620,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int v = b_row0<Cfg>(wn, fn) + frag_row;
-        if constexpr (Cfg::F8) {
+        if constexpr (Cfg::F8 && Cfg::WQ) {
+          // the 32 e2m1 values (low nibble first) of block 4p + 2ks + h
+          const uint4 q = *reinterpret_cast<const uint4*>(bs + swz(v, 4 * p + 2 * ks + half));
+          bfr[fn] = i32x8{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        } else if constexpr (Cfg::F8) {
           const uint4 lo = *reinterpret_cast<const uint4*>(bs + swz(v, chunk));
           const uint4 hi = *reinterpret_cast<const uint4*>(bs + swz(v, chunk + 1));
           bfr[fn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
@@ -631,7 +652,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // issue on that LDS read ahead of the last MFMAs; here those MFMAs are
     // already in flight.
     auto expand0 = [&](int p) {
-      if constexpr (Cfg::WQ) {
+      if constexpr (Cfg::WQ && !Cfg::F8) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
           fb[0][fn] = expand_fp4x8(bq[fn].x, scale_of(fn, p, lane));
@@ -682,7 +703,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
           if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            if constexpr (Cfg::F8)
+            if constexpr (Cfg::F8 && Cfg::WQ)  // B e2m1 (format 4) with its E8M0 block scale
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 4, 0, 127, 0,
+                  scale_byte(fn, P, ks, ln));
+            else if constexpr (Cfg::F8)
               acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
             else
@@ -737,7 +762,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // FP8: the products of codes times the row's activation scale and the
     // column's weight scale (per output channel; 0 past N_out, never stored)
     float sw[Cfg::F8 ? FN : 1];
-    if constexpr (Cfg::F8) {
+    if constexpr (Cfg::F8 && !Cfg::WQ) {
       const float* wsc = static_cast<const float*>(W_scales) + static_cast<int64_t>(e) * N_total;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
@@ -747,6 +772,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       }
     }
     auto scaled = [&](float a, float sa, int fn) -> float {
+      if constexpr (Cfg::F8 && Cfg::WQ) return a * sa;  // block scales applied by the MFMA
       if constexpr (Cfg::F8) return a * sa * sw[fn];
       return a;
     };
@@ -986,7 +1012,8 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
 
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  if (g.a_scales) return launch_fmt<false, true>(g, max_rows, s);
+  if (g.a_scales)
+    return g.w_mxfp4 ? launch_fmt<true, true>(g, max_rows, s) : launch_fmt<false, true>(g, max_rows, s);
   return g.w_scales ? launch_fmt<true, false>(g, max_rows, s)
                     : launch_fmt<false, false>(g, max_rows, s);
 }

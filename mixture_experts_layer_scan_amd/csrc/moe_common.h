@@ -124,6 +124,7 @@ struct GemmArgs {
   int batch_m = 0;        // > 0: batched experts format, expert e's rows start
                           // at e * batch_m and number min(offsets[e], batch_m)
   const float* a_scales = nullptr;  // fp8 activations: fp32 [R_pad], one per row
+  bool w_mxfp4 = false;             // with fp8 activations: MXFP4 weights (else FP8)
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its

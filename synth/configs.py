@@ -36,7 +36,8 @@ class MoeConfig:
     local_first: int = 0            # first global id owned by this rank
     shared_I: int = 0               # shared-expert intermediate (0: none)
     mxfp4: bool = False
-    fp8: bool = False               # FP8 E4M3 weights (per channel) and activations (per token)
+    fp8: bool = False               # FP8 E4M3 activations (per token); weights FP8 per channel
+                                    # unless mxfp4
     zipf_s: float = 0.0             # Zipf exponent of the logit bias (0: none)
     deferred: bool = False
 
@@ -67,8 +68,13 @@ MIXTRAL_FP8 = MoeConfig("mixtral8x7b_fp8_prefill_4096tok", T=4096, H=4096, I=143
 DEEPSEEK_FP8 = MoeConfig("deepseekv3_fp8_2048tok", T=2048, H=7168, I=2048, E=256, k=8,
                          score=SIGMOID, renormalize=True, rsf=2.5, seed=3, fp8=True)
 
+# MXFP4 weights with FP8 activations: FP8 x e2m1 on the matrix cores
+DEEPSEEK_MXFP4_FP8 = MoeConfig("deepseekv3_mxfp4_fp8act_2048tok", T=2048, H=7168, I=2048, E=256,
+                               k=8, score=SIGMOID, renormalize=True, rsf=2.5, seed=5, mxfp4=True,
+                               fp8=True)
+
 ALL = {c.name: c for c in (TINY, MIXTRAL, DEEPSEEK, EP_DECODE, DEEPSEEK_MXFP4, MIXTRAL_FP8,
-                           DEEPSEEK_FP8)}
+                           DEEPSEEK_FP8, DEEPSEEK_MXFP4_FP8)}
 
 EP_DECODE_BATCHES = (1, 8, 64)
 EP_DECODE_DRAWS = 16
@@ -113,7 +119,7 @@ def make_weights(cfg: MoeConfig):
         w["w1_q"], w["w1_s"] = mxfp4_quantize(w["w1"])
         w["w2_q"], w["w2_s"] = mxfp4_quantize(w["w2"])
         del w["w1"], w["w2"]
-    if cfg.fp8:
+    elif cfg.fp8:
         w["w1_q"], w["w1_s"] = fp8_quantize_rows(w["w1"])
         w["w2_q"], w["w2_s"] = fp8_quantize_rows(w["w2"])
         del w["w1"], w["w2"]

@@ -10,9 +10,12 @@ per-channel scales) against the oracle.
   oracle on the same codes (bar 1e-2, the bf16 bar: both sides multiply the
   same quantized values, so only the fp32 accumulation and the bf16 output
   rounding separate them);
+- FP8 rows times MXFP4 weights (E8M0 block scales applied by the matrix
+  cores) on the same shapes, against the oracle on the same codes;
 - whole FP8 layers (fused, deferred at the EP decode shape, static scales,
-  router weight on the input, chunked) against the oracle's fp8 mode, and
-  the full-size Mixtral and DeepSeek-V3 FP8 workloads on sampled tokens.
+  router weight on the input, chunked, MXFP4 weights) against the oracle's
+  fp8 mode, and the full-size Mixtral and DeepSeek-V3 FP8 workloads and the
+  DeepSeek-V3 MXFP4-weight FP8-activation workload on sampled tokens.
 """
 import gc
 
@@ -130,6 +133,48 @@ def test_fp8_gemms(case, split):
     assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
 
 
+W4A8_CASES = [
+    # name, counts per local expert, H, I (multiples of 256: MXFP4 weight stages)
+    ("thin_tiles", [0, 1, 5, 33, 2, 0, 17, 40], 256, 256),
+    ("wide_tiles", [70, 0, 130, 55], 512, 256),
+    ("wide_ragged_fragments", [0, 3, 129, 31, 64, 97], 256, 256),
+    ("mid_tiles", [300, 1, 420], 256, 512),
+    ("big_tiles", [700, 613], 512, 256),
+    ("split_decode", [1, 0, 2, 1, 0, 3], 1024, 512),
+    ("split_wide", [20, 30, 0, 16], 1024, 512),
+]
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split_ok", "no_split"])
+@pytest.mark.parametrize("case", W4A8_CASES, ids=[c[0] for c in W4A8_CASES])
+def test_fp8_activations_mxfp4_weights(case, split):
+    """FP8 rows times MXFP4 weights (e2m1 codes, E8M0 block scales applied by
+    the matrix cores) against the oracle on the same codes."""
+    name, counts, H, I = case
+    E_l = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R_l = int(offsets[-1])
+    R_pad = ((R_l + 127) // 128) * 128
+    seed = sum(counts) + 95
+    aq, asc = oracle.quantize_fp8_rows(synth.normal_bf16(seed, 0, (R_pad, H)))
+    hq, hsc = oracle.quantize_fp8_rows(synth.normal_bf16(seed, 7, (R_pad, I)))
+    aq[R_l:] = 0x7F
+    hq[R_l:] = 0x7F
+    q1, s1 = synth.mxfp4_quantize(synth.normal_bf16(seed, 2, (E_l, 2 * I, H), std=1 / np.sqrt(H)))
+    q2, s2 = synth.mxfp4_quantize(synth.normal_bf16(seed, 3, (E_l, H, I), std=1 / np.sqrt(I)))
+    off = dev(offsets)
+    h = moe.moe_grouped_gemm1_act_fp8(dev(aq), dev(asc), off, moe.Weights(dev(q1), dev(s1)), I,
+                                      split=split)
+    y = moe.moe_grouped_gemm2_fp8(dev(hq), dev(hsc), off, moe.Weights(dev(q2), dev(s2)), H,
+                                  split=split)
+    torch.cuda.synchronize()
+    eor = segments_of(offsets, R_l)
+    ref_h = oracle.hidden_rows_fp8(aq[:R_l], asc[:R_l], oracle.Weights(q1, s1), eor, I)
+    ref_y = oracle.out_rows_fp8(hq[:R_l], hsc[:R_l], oracle.Weights(q2, s2), eor, H)
+    assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
+    assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
+
+
 def _fp8_cfg(name, T, H, I, E, k, seed, score=configs.SOFTMAX, renorm=True, rsf=1.0):
     return configs.MoeConfig(name, T=T, H=H, I=I, E=E, k=k, score=score, renormalize=renorm,
                              rsf=rsf, seed=seed, fp8=True)
@@ -141,8 +186,10 @@ def _upload(w):
 
 
 def _oracle_w(w):
-    # one scale per weight row: expert e's row n is row e * N + n of the
-    # flattened [E_l * N] scales, as the codes are laid out
+    # FP8: one scale per weight row, expert e's row n being row e * N + n of
+    # the flattened [E_l * N] scales, as the codes are laid out; MXFP4: as is
+    if w["w1_s"].dtype == np.uint8:
+        return oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
     return (oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1)),
             oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1)))
 
@@ -211,8 +258,25 @@ def test_fp8_ep_decode_deferred(T):
     assert rel_fro(host_f64(out), ref["out"]) < TOL
 
 
-@pytest.mark.parametrize("cfg", [configs.MIXTRAL_FP8, configs.DEEPSEEK_FP8],
-                         ids=lambda c: c.name)
+def test_fp8_activations_mxfp4_layer():
+    cfg = configs.MoeConfig("w4a8", T=300, H=512, I=256, E=16, k=4, score=configs.SIGMOID,
+                            renormalize=True, rsf=2.5, seed=96, mxfp4=True, fp8=True)
+    x, logits = configs.make_activations(cfg)
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    xd, ld = dev_bf16(x), dev(logits)
+    args = (ld, xd, W1, W2, cfg.k, cfg.score, cfg.renormalize, cfg.rsf)
+    out = moe.moe_fused_experts(*args, fp8=True)
+    y, ew, m = moe.moe_fused_experts_unfinalized(*args, fp8=True)
+    fin = moe.moe_finalize(y, ew, m)
+    torch.cuda.synchronize()
+    ref = _ref(cfg, x, logits, w)
+    assert rel_fro(host_f64(out), ref["out"]) < TOL
+    assert rel_fro(host_f64(fin), ref["out"]) < TOL
+
+
+@pytest.mark.parametrize("cfg", [configs.MIXTRAL_FP8, configs.DEEPSEEK_FP8,
+                                 configs.DEEPSEEK_MXFP4_FP8], ids=lambda c: c.name)
 def test_fp8_full_size(cfg):
     x, logits = configs.make_activations(cfg)
     w = configs.make_weights(cfg)
