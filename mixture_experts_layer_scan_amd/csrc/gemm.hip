@@ -698,6 +698,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
           load_frags(nxt_a, nxt_b, ln, 0, (J + 1) % BKS, fa[0], fb[0], bq);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // the wave issuing MFMAs goes first, so with two waves on a SIMD one
+        // computes while the other waits on its loads
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
@@ -715,6 +718,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
                   fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -983,7 +987,8 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   const int64_t slice = g.R_pad * (g.gated ? 2 * int64_t(g.N_out) : g.N_out) * 4;
   const bool may_split = g.split_ws != nullptr && g.R_pad <= 65535 &&
                          int64_t(g.split_ws_bytes) >= kSplitHeader + 2 * slice;
-  const bool eight = (WQ || F8) && !may_split;
+  // (FP8 x e2m1 GEMM1 streams fastest in four waves with fragment skipping)
+  const bool eight = (WQ || F8) && !may_split && !(WQ && F8 && g.gated);
   if (g.gated) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
