@@ -18,6 +18,9 @@ bf16 weights.  The other workloads:
                                      per-channel weight scales, per-token activation
                                      scales (quantize -> dispatch -> FP8 GEMMs)
   mixtral8x7b_fp8_prefill_4096tok    the Mixtral shape in FP8 E4M3
+  deepseekv3_mxfp4_x2act_2048tok     MXFP4 weights with the bf16 activations carried as two FP8
+                                     terms, scale * (q1 + q2 / 16), through the FP8 x e2m1
+                                     matrix cores (near-bf16 activation precision)
   deepseekv3_mxfp4_fp8act_2048tok    MXFP4 weights with FP8 activations per token (FP8 x e2m1
                                      on the matrix cores, E8M0 block scales applied by them)
   ep_rank3of8_decode                 one expert-parallel rank's 32 experts at a
@@ -135,7 +138,8 @@ def gemm_work(cfg, counts, gemm: int):
         w_bytes_per_expert = N * (K + 4)     # codes + one fp32 scale per channel
     else:
         w_bytes_per_expert = N * K * 2
-    in_bytes = R_l * (K + 4) if cfg.fp8 else R_l * K * 2  # fp8 rows carry a scale
+    # fp8 rows carry a scale; two-term rows hold 2K codes
+    in_bytes = R_l * (K + 4) if cfg.fp8 else R_l * (2 * K + 4) if cfg.fp8x2 else R_l * K * 2
     flops = 2.0 * R_l * N * K
     nbytes = float(touched * w_bytes_per_expert + in_bytes + R_l * out_cols * 2)
     return flops, nbytes
@@ -155,7 +159,7 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
         W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
     from synth import configs
     kw = dict(expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I, ws1=w.get("ws1"),
-              ws2=w.get("ws2"), fp8=cfg.fp8, **(variant or {}))
+              ws2=w.get("ws2"), fp8="x2" if cfg.fp8x2 else cfg.fp8, **(variant or {}))
 
     def run(x, logits, toks):
         oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
@@ -267,15 +271,17 @@ def main():
     h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    if cfg.fp8:
+    quant = cfg.fp8 or cfg.fp8x2        # activations quantized inside the layer
+    terms = 2 if cfg.fp8x2 else 1
+    if quant:
         if Mb:
             print("FP8 workloads take the standard layout", file=sys.stderr)
             sys.exit(2)
-        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xq = torch.empty((T, H * terms), dtype=torch.uint8, device=dev)
         xs = torch.empty((T,), dtype=torch.float32, device=dev)
-        xq_perm = torch.empty((R_pad, H), dtype=torch.uint8, device=dev)
+        xq_perm = torch.empty((R_pad, H * terms), dtype=torch.uint8, device=dev)
         ps = torch.empty((R_pad,), dtype=torch.float32, device=dev)
-        hq = torch.empty((R_pad, I), dtype=torch.uint8, device=dev)
+        hq = torch.empty((R_pad, I * terms), dtype=torch.uint8, device=dev)
         hs = torch.empty((R_pad,), dtype=torch.float32, device=dev)
     if args.fused_tail:
         residual = to_bf16(draws[0][0])  # a residual stream of the x distribution
@@ -301,7 +307,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     fin_stage = "finalize_add_rmsnorm" if args.fused_tail else "finalize"
-    stages = (["route", "quantize", "permute", "gemm1", "quantize_h", "gemm2"] if cfg.fp8
+    stages = (["route", "quantize", "permute", "gemm1", "quantize_h", "gemm2"] if quant
               else ["route", "permute", "gemm1", "gemm2"]) \
         + (["shared"] if cfg.shared_I else []) + [fin_stage]
     act_kw = dict(activation=args.activation, activation_clamp=args.activation_clamp)
@@ -310,9 +316,13 @@ def main():
     counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
 
     def permute(sl, st):
-        if cfg.fp8:
+        if cfg.fp8x2:
+            moe.moe_quantize_fp8x2(xd_cur[0][sl], wts[sl] if w_in else None, xq[sl], xs[sl],
+                                   stream=st)
+        elif cfg.fp8:
             moe.moe_quantize_fp8(xd_cur[0][sl], None, wts[sl] if w_in else None, xq[sl], xs[sl],
                                  stream=st)
+        if quant:
             mark_cur[0]("permute")
             moe.moe_permute_fp8(ids[sl], E, xq[sl], xs[sl], El, emap_d, R_pad, pmap[sl], offsets,
                                 None, xq_perm, ps, want_inv=False, stream=st)
@@ -326,6 +336,15 @@ def main():
                             stream=st)
 
     def gemms(n, st):
+        if cfg.fp8x2:
+            moe.moe_grouped_gemm1_act_fp8x2(xq_perm, ps, offsets, W1, I, h, stream=st,
+                                            split=False, workspace=split_ws, **act_kw)
+            mark_cur[0]("quantize_h")
+            moe.moe_quantize_fp8x2(h, None, hq, hs, row_count=offsets[El:], stream=st)
+            mark_cur[0]("gemm2")
+            moe.moe_grouped_gemm2_fp8x2(hq, hs, offsets, W2, H, y, stream=st, split=False,
+                                        workspace=split_ws)
+            return
         if cfg.fp8:
             moe.moe_grouped_gemm1_act_fp8(xq_perm, ps, offsets, W1, I, h, stream=st, split=False,
                                           workspace=split_ws, **act_kw)
@@ -373,7 +392,7 @@ def main():
             mark("route")
             moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                                st)
-            mark("quantize" if cfg.fp8 else "permute")
+            mark("quantize" if quant else "permute")
             permute(sl, st)
             mark("gemm1")
             gemms(n, st)
@@ -491,6 +510,7 @@ def main():
         ms_per_step = elapsed / args.steps * 1e3
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
     g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
+    # (two-term rows run the fp8 MFMA twice: the bf16 peak is their rate)
     peak_mfma = PEAK_FP8_TFLOPS if cfg.fp8 else PEAK_BF16_TFLOPS
     t_mfma = g1_flops / (peak_mfma * 1e12)
     t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
@@ -523,11 +543,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if cfg.fp8 else "bf16",
+        "dtype": "fp8" if cfg.fp8 else "fp8x2 (two E4M3 terms) x e2m1" if cfg.fp8x2 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights"
                 + (", MXFP4-quantized" if cfg.mxfp4 else "")
                 + ((", FP8 E4M3 activations per token" if cfg.mxfp4 else
                     ", FP8 E4M3 weights per channel, activations per token") if cfg.fp8 else "")
+                + (", bf16 activations as two FP8 E4M3 terms per token" if cfg.fp8x2 else "")
                 + ")",
         "config": {"workload": label, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "local_experts": El, "top_k": k,

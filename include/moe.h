@@ -121,7 +121,8 @@ typedef struct moe_layer_options {
   int32_t apply_router_weight_on_input;
   int32_t chunk_tokens;
   int32_t batched_max_tokens;
-  int32_t act_quant;        /* MOE_QUANT_NONE, or MOE_QUANT_FP8 (with FP8 weights) */
+  int32_t act_quant;        /* MOE_QUANT_NONE, MOE_QUANT_FP8 (FP8 or MXFP4 weights) or
+                               MOE_QUANT_FP8X2 (MXFP4 weights) */
   const float* a1_scale;    /* (device) static scale of the GEMM1 input, or NULL */
   const float* a2_scale;    /* (device) static scale of the GEMM2 input, or NULL */
 } moe_layer_options;
@@ -135,7 +136,13 @@ typedef struct moe_layer_options {
  * (H and I multiples of 128) or MXFP4 weights (multiples of 256: FP8 x e2m1
  * on the matrix cores, the E8M0 block scales applied by them), the standard
  * layout (no batched_max_tokens); the shared expert stays bf16. */
-enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1 };
+/* MOE_QUANT_FP8X2 keeps bf16 activations close to bf16 precision on the
+ * FP8 x e2m1 matrix cores: each row becomes two E4M3 terms with one scale,
+ * x ~ scale * (q1 + q2 / 16) (moe_quantize_fp8x2), before dispatch and before
+ * GEMM2, and both GEMMs multiply both terms by the e2m1 weights.  Needs MXFP4
+ * weights (H and I multiples of 256), dynamic scales (a1_scale and a2_scale
+ * NULL) and the standard layout. */
+enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1, MOE_QUANT_FP8X2 = 2 };
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
  *   BF16:  data = bf16 [E_l, N, K],   scales = NULL
@@ -270,6 +277,44 @@ int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
 int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const int32_t* offsets,
                           int32_t E_l, int64_t R_pad, int32_t I, int32_t H, const moe_weights* w2,
                           void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Two-term FP8 E4M3 quantization of bf16 rows, for bf16 activations on the
+ * FP8 x e2m1 matrix cores with MXFP4 weights (the quantize half of
+ * [Quantize-Dispatch], page "modular_kernel.py", prepare(), per token).  Per
+ * row, in fp32: a = max |x| (448 for an all-zero row), inv = 448 / a,
+ * scale = a / 448; for each element v = clamp(x[j] * inv, -448, 448),
+ *   q1 = E4M3 code nearest to v (ties to even),
+ *   q2 = E4M3 code nearest to 16 * (v - value(q1))   (the residual is exact),
+ * so x[j] ~ scale * (value(q1) + value(q2) / 16).  With row_weights the row is
+ * first bf16(row_weights[r] * x).
+ *   x         (device) bf16 [rows, H]
+ *   q         (device) u8 [rows, 2H] out: per 64 k, the 64 codes q1 of those
+ *             k, then their 64 codes q2
+ *   row_count (device) int32 scalar or NULL, as for moe_quantize_fp8
+ *   scales    (device) fp32 [rows] out
+ * The rows are dispatched with moe_permute_fp8 as rows of 2H bytes.
+ * Limits: H a multiple of 64. */
+int moe_quantize_fp8x2(const void* x, int64_t rows, int32_t H, const float* row_weights,
+                       const int32_t* row_count, uint8_t* q, float* scales, void* stream);
+
+/* The two grouped GEMMs on two-term FP8 rows (moe_quantize_fp8x2) with MXFP4
+ * weights (apply() of page "modular_kernel.py"):
+ *   C[r, n] = a_scale[r] * sum_k (q1[r, k] + q2[r, k] / 16) * e2m1[n, k] * 2^(e8m0 - 127)
+ * (two scaled 32x32x64 MFMAs per 64 k, the second with A scale 2^-4), then,
+ * for GEMM1, act(gate) * up and one rounding to bf16.
+ *   a_perm / h_perm  (device) u8 [R_pad, 2H or 2I];  a_scales / h_scales fp32 [R_pad]
+ *   w1 / w2          MOE_DTYPE_MXFP4 weights
+ *   h / y            (device) bf16 [R_pad, I or H] out;  workspace as for the bf16 calls
+ * Limits: H and I multiples of 256. */
+int moe_grouped_gemm1_act_fp8x2(const uint8_t* a_perm, const float* a_scales,
+                                const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                                int32_t I, const moe_weights* w1, int32_t activation,
+                                float activation_clamp, void* h, void* workspace,
+                                size_t workspace_bytes, void* stream);
+int moe_grouped_gemm2_fp8x2(const uint8_t* h_perm, const float* h_scales,
+                            const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t I,
+                            int32_t H, const moe_weights* w2, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Permute into the batched experts format (page "modular_kernel.py":
  * FusedMoEActivationFormat.BatchedExperts, activations laid out as (local

@@ -181,7 +181,8 @@ struct LayerOpts {
   bool weight_on_input = false;
   int64_t chunk = 0;  // 0: one pass
   int batch_m = 0;    // > 0: batched experts format with this capacity
-  bool fp8 = false;   // FP8 activations (MOE_QUANT_FP8)
+  bool fp8 = false;   // FP8 activations (MOE_QUANT_FP8 or MOE_QUANT_FP8X2)
+  int terms = 1;      // 2: two-term FP8 activations (MOE_QUANT_FP8X2)
   const float* a1_scale = nullptr;
   const float* a2_scale = nullptr;
 };
@@ -201,9 +202,13 @@ int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
   if (o->batched_max_tokens < 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "batched_max_tokens must be >= 0");
   out->batch_m = o->batched_max_tokens;
-  if (o->act_quant != MOE_QUANT_NONE && o->act_quant != MOE_QUANT_FP8)
+  if (o->act_quant != MOE_QUANT_NONE && o->act_quant != MOE_QUANT_FP8 &&
+      o->act_quant != MOE_QUANT_FP8X2)
     return fail(MOE_ERR_UNSUPPORTED, "unknown activation quantization %d", o->act_quant);
-  out->fp8 = o->act_quant == MOE_QUANT_FP8;
+  out->fp8 = o->act_quant != MOE_QUANT_NONE;
+  out->terms = o->act_quant == MOE_QUANT_FP8X2 ? 2 : 1;
+  if (out->terms == 2 && (o->a1_scale || o->a2_scale))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "two-term FP8 activations take dynamic scales only");
   if (out->fp8 && out->batch_m > 0)
     return fail(MOE_ERR_UNSUPPORTED, "FP8 activations take the standard layout (no batched_max_tokens)");
   if (!out->fp8 && (o->a1_scale || o->a2_scale))
@@ -232,7 +237,7 @@ int64_t routed_rows(int64_t T, int32_t k, int32_t E_l, int batch_m) {
 }
 
 size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, int batch_m,
-                       bool fp8 = false) {
+                       bool fp8 = false, int terms = 1) {
   const int64_t R_pad = routed_rows(T, k, E_l, batch_m);
   size_t b = 0;
   b += align_up(sizeof(int32_t) * T * k);               // topk ids
@@ -243,10 +248,10 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, 
   b += align_up(sizeof(uint16_t) * R_pad * I);          // h
   b += align_up(routed_split_bytes(R_pad, H, I));       // GEMM split partials
   if (fp8) {
-    b += align_up(size_t(T) * H);                       // quantized tokens
+    b += align_up(size_t(T) * H * terms);               // quantized tokens
     b += align_up(sizeof(float) * T);                   // their scales
     b += align_up(sizeof(float) * R_pad);               // permuted row scales
-    b += align_up(size_t(R_pad) * I);                   // quantized hidden rows
+    b += align_up(size_t(R_pad) * I * terms);           // quantized hidden rows
     b += align_up(sizeof(float) * R_pad);               // their scales
   }
   return b;
@@ -292,7 +297,7 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   const int64_t P = pass_tokens(T, o);
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8) + shared_bytes;
+  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms) + shared_bytes;
   return MOE_OK;
 }
 
@@ -409,17 +414,20 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
                        int32_t K, int32_t N_out, int gated, int act, float clamp,
                        const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
                        void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
-                       bool fp8 = false, const float* a_scales = nullptr) {
+                       bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
   MOE_CHECK(check_pairing(w, fp8, name));
+  if (a_terms == 2 && w->dtype != MOE_DTYPE_MXFP4)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: two-term FP8 activations need MXFP4 weights", name);
+  // (two-term rows take 2K bytes, as many as bf16 rows)
   MOE_CHECK(check_gemm_extent(R_pad, K, gated ? 2 * int64_t(N_out) : N_out));
   if (R_pad == 0) return MOE_OK;
   MOE_CHECK(need_ptr(a, "input rows"));
   MOE_CHECK(need_ptr(offsets, "offsets"));
   MOE_CHECK(need_ptr(c, "output rows"));
-  const size_t in_bytes = (fp8 ? 1 : sizeof(uint16_t)) * R_pad * K;
+  const size_t in_bytes = (fp8 ? a_terms : sizeof(uint16_t)) * R_pad * K;
   const size_t out_bytes = sizeof(uint16_t) * R_pad * N_out;
   if (overlap(a, in_bytes, c, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
@@ -434,7 +442,7 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
                   workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
-                  a_scales, w->dtype == MOE_DTYPE_MXFP4};
+                  a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms};
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -553,6 +561,54 @@ int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const in
   if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
   return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
                      workspace_bytes, stream, "moe_grouped_gemm2_fp8", 0, 0, true, h_scales);
+}
+
+int moe_quantize_fp8x2(const void* x, int64_t rows, int32_t H, const float* row_weights,
+                       const int32_t* row_count, uint8_t* q, float* scales, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be non-negative");
+  if (H <= 0 || H % 64) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 64 (H=%d)", H);
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(x, "x"));
+  MOE_CHECK(need_ptr(q, "q"));
+  MOE_CHECK(need_ptr(scales, "scales"));
+  MOE_CHECK(opt_ptr4(row_weights, "row_weights"));
+  MOE_CHECK(opt_ptr4(row_count, "row_count"));
+  if (overlap(x, sizeof(uint16_t) * rows * H, q, size_t(rows) * H * 2) ||
+      overlap(x, sizeof(uint16_t) * rows * H, scales, sizeof(float) * rows))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "q and scales must not overlap x");
+  hipError_t e = moe::launch_quantize_fp8(x, rows, H, nullptr, row_weights, row_count, q, scales,
+                                          static_cast<hipStream_t>(stream), 2);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8x2");
+}
+
+int moe_grouped_gemm1_act_fp8x2(const uint8_t* a_perm, const float* a_scales,
+                                const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                                int32_t I, const moe_weights* w1, int32_t activation,
+                                float activation_clamp, void* h, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w1));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(a_scales, "a_scales"));
+  if (R_pad > 0 && !a_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "a_scales must not be NULL");
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_fp8x2", 0, 0,
+                     true, a_scales, 2);
+}
+
+int moe_grouped_gemm2_fp8x2(const uint8_t* h_perm, const float* h_scales,
+                            const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t I,
+                            int32_t H, const moe_weights* w2, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w2));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(h_scales, "h_scales"));
+  if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
+  return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
+                     workspace_bytes, stream, "moe_grouped_gemm2_fp8x2", 0, 0, true, h_scales, 2);
 }
 
 int moe_grouped_gemm1_act_batched(const void* a_batched, const int32_t* expert_num_tokens,
@@ -681,7 +737,7 @@ struct RoutedWs {
 };
 
 static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I,
-                             int batch_m, bool fp8 = false) {
+                             int batch_m, bool fp8 = false, int terms = 1) {
   RoutedWs b;
   b.rows = routed_rows(T, k, E_l, batch_m);
   b.ids = c.take<int32_t>(T * k);
@@ -693,10 +749,11 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   b.split_bytes = routed_split_bytes(b.rows, H, I);
   b.split = b.split_bytes ? c.take<char>(b.split_bytes) : nullptr;
   if (fp8) {
-    b.xq = c.take<uint8_t>(T * H);
+    // (two-term quantized permuted rows, 2H bytes each, fill x_perm's slot)
+    b.xq = c.take<uint8_t>(T * H * terms);
     b.xs = c.take<float>(T);
     b.ps = c.take<float>(b.rows);
-    b.hq = c.take<uint8_t>(b.rows * I);
+    b.hq = c.take<uint8_t>(b.rows * I * terms);
     b.hs = c.take<float>(b.rows);
   }
   return b;
@@ -723,27 +780,28 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     // Quantize-Dispatch: the tokens (times their weight when it goes on the
     // input; top_k 1, so one weight per token) to FP8, then their rows
     e = moe::launch_quantize_fp8(x, T, H, o.a1_scale, o.weight_on_input ? b.wts : nullptr,
-                                 nullptr, b.xq, b.xs, s);
+                                 nullptr, b.xq, b.xs, s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize");
   }
   e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s,
                           o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");
   if (o.fp8) {
-    e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H, b.x_perm, b.ps, s);
+    e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H * o.terms, b.x_perm, b.ps, s);
     if (e != hipSuccess) return hip_fail(e, "gather");
     const int64_t max_rows = moe_permuted_rows(T, k);
     moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
                      b.split, b.split_bytes, o.act, o.clamp, 0, b.ps,
-                     w1->dtype == MOE_DTYPE_MXFP4};
+                     w1->dtype == MOE_DTYPE_MXFP4, o.terms};
     e = moe::launch_grouped_gemm(g1, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm1");
     // the hidden rows of the local routes (offsets[E_l] of them) to FP8
     e = moe::launch_quantize_fp8(b.h, b.rows, I, o.a2_scale, nullptr, b.offsets + E_l, b.hq, b.hs,
-                                 s);
+                                 s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize hidden");
     moe::GemmArgs g2{b.hq, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
-                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs, w2->dtype == MOE_DTYPE_MXFP4};
+                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs, w2->dtype == MOE_DTYPE_MXFP4,
+                     o.terms};
     e = moe::launch_grouped_gemm(g2, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm2");
     return MOE_OK;
@@ -778,6 +836,8 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
   MOE_CHECK(check_weights(w2, "w2"));
   MOE_CHECK(check_pairing(w1, o.fp8, "w1"));
   MOE_CHECK(check_pairing(w2, o.fp8, "w2"));
+  if (o.terms == 2 && (w1->dtype != MOE_DTYPE_MXFP4 || w2->dtype != MOE_DTYPE_MXFP4))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "two-term FP8 activations need MXFP4 weights");
   if (o.fp8) MOE_CHECK(check_fp8_dims(H, I, w1));
   if (o.batch_m > 0) MOE_CHECK(check_capacity(E_l, o.batch_m));
   const int64_t rows = routed_rows(pass_T, k, E_l, o.batch_m);
@@ -823,9 +883,9 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(check_workspace(workspace, workspace_bytes,
-                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8)));
+                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms)));
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8);
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
                     o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
                     static_cast<hipStream_t>(stream));
@@ -856,7 +916,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
   }
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8) + shared_bytes;
+  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms) + shared_bytes;
   MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
   // out is x itself (in place) or apart from it; the workspace is apart from both
   const size_t row_bytes = sizeof(uint16_t) * T * H;
@@ -866,7 +926,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     return fail(MOE_ERR_DESTINATION_CONFLICT, "the workspace must not overlap x or out");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m, o.fp8);
+  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
   int32_t* s_off = nullptr;
   uint16_t* s_h = nullptr;
   uint16_t* s_y = nullptr;

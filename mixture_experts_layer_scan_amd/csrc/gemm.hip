@@ -70,6 +70,13 @@
 // split_reduce_kernel adds the S slices in order (deterministic, no atomics)
 // and applies the activation.
 //
+// Two-term FP8 activations with MXFP4 weights (bf16 activations split as
+// scale * (q1 + q2 / 16), both E4M3): an activation row holds, per 64 k, the
+// 64 codes of q1 and then the 64 of q2, so a 128-byte activation stage row is
+// one k-step of 64.  Sub-step t multiplies term t by the weight block pair of
+// that k-step with the scaled MFMA (A scale 1 or 2^-4, B scale the E8M0 byte),
+// both into the same accumulators; the row scale applies in the epilogue.
+//
 // GEMM1 ("gated"): a tile of BN virtual weight rows holds BN/2 gate rows
 // [n0, n0 + BN/2) and the matching BN/2 up rows [I + n0, ...).  Each wave
 // computes gate and up blocks with the same lane layout, so the epilogue
@@ -107,6 +114,10 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // Descriptor word 3 for raw (untyped, stride 0) buffer access on gfx9-family
 // parts: 32-bit data format, out-of-range offsets read as zero.
 constexpr int kBufferFlags = 0x00020000;
+
+// two-term fp8 activations: the second term holds the first one's residual
+// times 2^kTerm2Shift
+constexpr int kTerm2Shift = 4;
 
 // split-reduction workspace: header (the chosen piece count), then slices
 constexpr int64_t kSplitHeader = 256;
@@ -181,12 +192,17 @@ __device__ __forceinline__ int opaque(int v) {
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GATED_, bool WQ_ = false,
-          int GM_ = 8, bool F8_ = false>
+          int GM_ = 8, bool F8_ = false, bool A2_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr bool F8 = F8_;  // activations and weights in FP8 E4M3
-  // k per k-step: 128 bytes of an activation row (64 bf16 or 128 fp8)
-  static constexpr int BK = F8 ? 128 : 64;
+  // two-term FP8 activations (with MXFP4 weights): 64 codes of the first
+  // term, then the 64 of the second term for the same k, per 128 row bytes
+  static constexpr bool A2 = A2_;
+  static_assert(!A2 || (F8 && WQ_), "two-term activations pair with MXFP4 weights");
+  // k per k-step: 128 bytes of an activation row (64 bf16, 128 fp8, or 64
+  // of each of the two fp8 terms)
+  static constexpr int BK = A2 ? 64 : F8 ? 128 : 64;
   static constexpr bool GATED = GATED_;
   static constexpr bool WQ = WQ_;  // weights in MXFP4
   static constexpr int GM = GM_;   // m-tiles per group of the tile order
@@ -194,13 +210,16 @@ struct TileCfg {
   static constexpr int kThreads = NWAVES * kWave;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  // skip row fragments past the segment (one wave row only: otherwise the
-  // waves of the lower rows would idle while the others work)
-  static constexpr bool SKIP = (WM == 1 && FM > 1);
+  // skip row fragments past the segment: in tiles of one wave row, and in
+  // the eight-wave weight-streaming tile (2 x 4 waves: each SIMD holds one
+  // wave of each wave row, so the skipped work leaves no SIMD idle while
+  // another computes); a wave of the lower row may then have no fragment
+  static constexpr bool SKIP = (WM == 1 && FM > 1) || (GM == 1 && WM > 1);
   // one wave row: the tiles for short segments, which may split the k-range
   static constexpr bool SPLIT = (WM == 1);
-  // MFMA sub-steps per k-step: 32x32x16 bf16, or 32x32x64 fp8
-  static constexpr int SUBSTEPS = F8 ? BK / 64 : BK / 16;
+  // MFMA sub-steps per k-step: 32x32x16 bf16, or 32x32x64 fp8 (two-term:
+  // one per term, both with the same weight fragment)
+  static constexpr int SUBSTEPS = A2 ? 2 : F8 ? BK / 64 : BK / 16;
   // two stages: the next k-step's loads all go out with the first sub-step,
   // since they must land by the end of this one
   static constexpr bool EARLY = (STAGES == 2);
@@ -209,7 +228,7 @@ struct TileCfg {
   static constexpr int A_LD = BM / 8 / NWAVES;   // activation loads per wave per k-step
   static constexpr int B_LD = BN / 8 / NWAVES;   // weight loads per wave per weight stage
   // k-steps per weight stage (128 bytes of a weight row: 256 k of e2m1)
-  static constexpr int B_KS = WQ ? (F8 ? 2 : 4) : 1;
+  static constexpr int B_KS = WQ ? (F8 && !A2 ? 2 : 4) : 1;
   // MXFP4: three weight stages, so two stream while one is used (a weight
   // stage lasts four k-steps; with one in flight the stream stalls between)
   static constexpr int B_STAGES = WQ ? 3 : STAGES;
@@ -453,14 +472,17 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const int rows = __builtin_amdgcn_readfirstlane(seg_end - row0);
     if (rows <= 0) continue;
     const int n0 = n_tile * Cfg::OUT_N;
-    // row fragments of this wave that hold rows of the segment (wave-uniform)
+    // row fragments of this wave that hold rows of the segment (wave-uniform;
+    // at least 1 with one wave row, possibly 0 or less for a lower wave row)
     const int fm_act = __builtin_amdgcn_readfirstlane(
         Cfg::SKIP ? min(FM, (rows - wm * Cfg::WTM + 31) / 32) : FM);
 
     // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
     // this expert's weights; loads past either range return zero.
     // activation bytes per row: K * 2 (bf16) or K (fp8)
-    const uint32_t a_row_bytes = Cfg::F8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) * 2u;
+    // (two-term fp8: K * 2, both terms)
+    const uint32_t a_row_bytes = (Cfg::F8 && !Cfg::A2) ? static_cast<uint32_t>(K)
+                                                       : static_cast<uint32_t>(K) * 2u;
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(static_cast<const uint8_t*>(A) + static_cast<int64_t>(row0) * a_row_bytes),
         0, static_cast<int>(static_cast<uint32_t>(rows) * a_row_bytes), kBufferFlags);
@@ -552,7 +574,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // 4p + 2ks + h of the weight stage (k-step position p, sub-step ks, half
     // h), handed to the MFMA as its B block scale
     auto scale_byte = [&](int fn, int p, int ks, int ln) -> int {
-      const int block = 4 * p + 2 * ks + (ln >> 5);
+      const int block = Cfg::A2 ? 2 * p + (ln >> 5) : 4 * p + 2 * ks + (ln >> 5);
       const uint32_t word = block < 4 ? sc_cur[fn].x : sc_cur[fn].y;
       return static_cast<int>((word >> (8u * static_cast<uint32_t>(block & 3))) & 0xFFu);
     };
@@ -606,7 +628,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       const int a_hi = Cfg::WQ ? 4 * ks + 2 + half : chunk + 1;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+        if (Cfg::SKIP && fm >= fm_act) continue;
         const int r = wm * Cfg::WTM + fm * 32 + frag_row;
         if constexpr (Cfg::F8) {
           const uint4 lo = *reinterpret_cast<const uint4*>(as + swz(r, a_lo));
@@ -622,7 +644,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         const int v = b_row0<Cfg>(wn, fn) + frag_row;
         if constexpr (Cfg::F8 && Cfg::WQ) {
           // the 32 e2m1 values (low nibble first) of block 4p + 2ks + h
-          const uint4 q = *reinterpret_cast<const uint4*>(bs + swz(v, 4 * p + 2 * ks + half));
+          // (two-term: block 2p + h in both sub-steps)
+          const int blk = Cfg::A2 ? 2 * p + half : 4 * p + 2 * ks + half;
+          const uint4 q = *reinterpret_cast<const uint4*>(bs + swz(v, blk));
           bfr[fn] = i32x8{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         } else if constexpr (Cfg::F8) {
           const uint4 lo = *reinterpret_cast<const uint4*>(bs + swz(v, chunk));
@@ -703,13 +727,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-          if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+          if (Cfg::SKIP && fm >= fm_act) continue;
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            if constexpr (Cfg::F8 && Cfg::WQ)  // B e2m1 (format 4) with its E8M0 block scale
+            if constexpr (Cfg::F8 && Cfg::WQ)  // B e2m1 (format 4) with its E8M0 block scale;
+              // A scale 1, or 2^-4 for the second of two terms
               acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 4, 0, 127, 0,
-                  scale_byte(fn, P, ks, ln));
+                  fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 4, 0,
+                  (Cfg::A2 && ks == 1) ? 127 - kTerm2Shift : 127, 0, scale_byte(fn, P, ks, ln));
             else if constexpr (Cfg::F8)
               acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
@@ -790,7 +815,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       float* P = partials + (static_cast<int64_t>(piece) * R_pad + row0) * N_total;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+        if (Cfg::SKIP && fm >= fm_act) continue;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
@@ -813,7 +838,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       constexpr int KIND = decltype(kind)::value;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        if (Cfg::SKIP && fm > 0 && fm >= fm_act) continue;
+        if (Cfg::SKIP && fm >= fm_act) continue;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
@@ -949,7 +974,7 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool WQ, bool F8>
+template <bool WQ, bool F8, bool A2 = false>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
   // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
@@ -958,19 +983,19 @@ struct Configs {
   // MXFP4 weights keep four (their scale loads and expansion registers).
   static constexpr int BIG_WM = WQ ? 2 : 4;
   //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
-  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8>;
-  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8>;
-  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8>;
-  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8>;
-  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8>;
-  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8>;
+  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2>;
+  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2>;
+  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8, A2>;
+  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8, A2>;
+  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8, A2>;
+  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8, A2>;
   // the same tile in eight waves (2 x 4) when no split is possible: the
   // FP8 and MXFP4 weight streams gain from the second wave per SIMD (MXFP4
   // GEMM2 of the DeepSeek shape 12 % faster) what fragment skipping saves
-  using WideP  = TileCfg<128, 256, 2, 4, S3, false, WQ, 1, F8>;
-  using WidePG = TileCfg<128, 256, 2, 4, S3, true, WQ, 1, F8>;
-  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ, 8, F8>;
-  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ, 8, F8>;
+  using WideP  = TileCfg<128, 256, 2, 4, S3, false, WQ, 1, F8, A2>;
+  using WidePG = TileCfg<128, 256, 2, 4, S3, true, WQ, 1, F8, A2>;
+  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ, 8, F8, A2>;
+  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ, 8, F8, A2>;
 };
 
 // Tile shape from the mean rows per local expert (the host cannot see the
@@ -979,9 +1004,9 @@ struct Configs {
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
 //   < 16    decode: short tiles with split reductions.
-template <bool WQ, bool F8>
+template <bool WQ, bool F8, bool A2 = false>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  using C = Configs<WQ, F8>;
+  using C = Configs<WQ, F8, A2>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
   // can this call split its reductions (two fp32 slices in the workspace)?
   const int64_t slice = g.R_pad * (g.gated ? 2 * int64_t(g.N_out) : g.N_out) * 4;
@@ -989,19 +1014,27 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
                          int64_t(g.split_ws_bytes) >= kSplitHeader + 2 * slice;
   // (FP8 x e2m1 GEMM1 streams fastest in four waves with fragment skipping)
   const bool eight = (WQ || F8) && !may_split && !(WQ && F8 && g.gated);
+  // (two-term activations: always the eight-wave tile in that range; with one
+  // wave row their doubled A fragments would not fit in registers)
   if (g.gated) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
-    if (mean_rows >= 16)
-      return eight ? launch_cfg<typename C::WidePG>(g, max_rows, s)
-                   : launch_cfg<typename C::WideG>(g, max_rows, s);
+    if (mean_rows >= 16) {
+      if constexpr (A2) return launch_cfg<typename C::WidePG>(g, max_rows, s);
+      else
+        return eight ? launch_cfg<typename C::WidePG>(g, max_rows, s)
+                     : launch_cfg<typename C::WideG>(g, max_rows, s);
+    }
     return launch_cfg<typename C::ThinG>(g, max_rows, s);
   }
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
-  if (mean_rows >= 16)
-    return eight ? launch_cfg<typename C::WideP>(g, max_rows, s)
-                 : launch_cfg<typename C::Wide>(g, max_rows, s);
+  if (mean_rows >= 16) {
+    if constexpr (A2) return launch_cfg<typename C::WideP>(g, max_rows, s);
+    else
+      return eight ? launch_cfg<typename C::WideP>(g, max_rows, s)
+                   : launch_cfg<typename C::Wide>(g, max_rows, s);
+  }
   return launch_cfg<typename C::Thin>(g, max_rows, s);
 }
 
@@ -1017,6 +1050,7 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
 
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
+  if (g.a_scales && g.a_terms == 2) return launch_fmt<true, true, true>(g, max_rows, s);
   if (g.a_scales)
     return g.w_mxfp4 ? launch_fmt<true, true>(g, max_rows, s) : launch_fmt<false, true>(g, max_rows, s);
   return g.w_scales ? launch_fmt<true, false>(g, max_rows, s)

@@ -125,6 +125,7 @@ struct GemmArgs {
                           // at e * batch_m and number min(offsets[e], batch_m)
   const float* a_scales = nullptr;  // fp8 activations: fp32 [R_pad], one per row
   bool w_mxfp4 = false;             // with fp8 activations: MXFP4 weights (else FP8)
+  int a_terms = 1;                  // 2: two-term fp8 activations [R_pad, 2K] (MXFP4 weights)
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its
@@ -156,9 +157,11 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
 // FP8 E4M3 rows: q [rows, H] codes and one fp32 scale per row, from bf16 rows
 // (times mult[r] rounded to bf16 when given); static_scale NULL: per-row
 // dynamic scales; row_count (device) NULL: all rows, else rows < *row_count.
+// terms 2: two-term codes, [rows, 2H] bytes (per 64 k: the first term's 64
+// codes, then the second's), dynamic scales only
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int H, const float* static_scale,
                                const float* mult, const int32_t* row_count, void* q,
-                               float* scales, hipStream_t s);
+                               float* scales, hipStream_t s, int terms = 1);
 hipError_t launch_gather_fp8_rows(const void* q, const float* scales, const int32_t* map,
                                   int64_t T, int k, int H, void* q_perm, float* scales_perm,
                                   hipStream_t s);

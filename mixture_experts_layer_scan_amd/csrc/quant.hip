@@ -13,6 +13,13 @@
 // multipliers (the routing weight applied to the input, top_k 1) the row is
 // bf16(m * x) before quantization.  The quantized rows are then dispatched
 // like bf16 rows: token-major, 16 bytes at a time, with their scales.
+//
+// Two terms (bf16 activations for the FP8 x e2m1 matrix cores): with
+// v = clamp(x[j] * inv) as above, q1 = e4m3(v), the residual d = v - q1 (exact
+// in fp32: v and q1 are within a factor of two, or d is a multiple of v's
+// ulp below 2^-10) and q2 = e4m3(16 d), so x ~ scale * (q1 + q2 / 16) with
+// about bf16's precision.  The row holds, per 64 k, the 64 codes of q1 and
+// then the 64 codes of q2.
 #include "moe_common.h"
 
 namespace moe {
@@ -37,6 +44,14 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
+// The value of an E4M3 code (exact in fp32).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? static_cast<float>(m) * 0.001953125f  // 2^-9
+                           : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
 // The 8 values of a 16-byte bf16 chunk, times m rounded back to bf16 when
 // a row multiplier is given.
 __device__ __forceinline__ void chunk_values(uint4 c, const float* mult, float m, float* v) {
@@ -55,7 +70,7 @@ __device__ __forceinline__ void chunk_values(uint4 c, const float* mult, float m
 __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_rows_kernel(
     const uint4* __restrict__ x, int64_t rows, int H8, const float* __restrict__ static_scale,
     const float* __restrict__ mult, const int32_t* __restrict__ row_count,
-    uint2* __restrict__ q, float* __restrict__ scales) {
+    uint2* __restrict__ q, float* __restrict__ scales, int terms) {
   __shared__ float s_max[kQuantThreads / kWave];
   const int64_t n = row_count ? static_cast<int64_t>(*row_count) : rows;
   const int lane = lane_id(), w = threadIdx.x / kWave;
@@ -88,6 +103,22 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_rows_kernel(
     for (int c = threadIdx.x; c < H8; c += blockDim.x) {
       float v[8];
       chunk_values(xr[c], mult, m, v);
+      if (terms == 2) {
+        uint32_t c1[2] = {0, 0}, c2[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float a = clamp448(v[i] * inv);
+          const uint32_t q1 = e4m3_rne(a);
+          const uint32_t q2 = e4m3_rne((a - e4m3_value(q1)) * 16.0f);
+          c1[i >> 2] |= q1 << (8 * (i & 3));
+          c2[i >> 2] |= q2 << (8 * (i & 3));
+        }
+        // chunk c (k = 8c .. 8c + 7) of 64-k block c / 8
+        uint2* qr = q + r * 2 * H8 + (c >> 3) * 16 + (c & 7);
+        qr[0] = uint2{c1[0], c1[1]};
+        qr[8] = uint2{c2[0], c2[1]};
+        continue;
+      }
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -129,12 +160,12 @@ __global__ __launch_bounds__(256) void gather_fp8_rows_kernel(const uint4* __res
 
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int H, const float* static_scale,
                                const float* mult, const int32_t* row_count, void* q,
-                               float* scales, hipStream_t s) {
+                               float* scales, hipStream_t s, int terms) {
   if (rows <= 0) return hipSuccess;
   const int64_t blocks = rows < 16384 ? rows : 16384;
   hipLaunchKernelGGL(quantize_fp8_rows_kernel, dim3(static_cast<unsigned>(blocks)),
                      dim3(kQuantThreads), 0, s, static_cast<const uint4*>(x), rows, H / 8,
-                     static_scale, mult, row_count, static_cast<uint2*>(q), scales);
+                     static_scale, mult, row_count, static_cast<uint2*>(q), scales, terms);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ from ._lib import MoeLayerOptionsC, MoeWeightsC, lib
 
 SOFTMAX, SIGMOID = 0, 1
 DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4, DTYPE_FP8_E4M3 = 0, 1, 2, 3
-QUANT_NONE, QUANT_FP8 = 0, 1
+QUANT_NONE, QUANT_FP8, QUANT_FP8X2 = 0, 1, 2
 ACT_SILU, ACT_GELU = 0, 1
 _ACT_NAMES = {"silu": ACT_SILU, "gelu": ACT_GELU}
 
@@ -56,9 +56,19 @@ def _act(activation) -> int:
     return _ACT_NAMES[activation] if isinstance(activation, str) else int(activation)
 
 
+def _quant(fp8) -> int:
+    """act_quant of moe_layer_options: fp8 False (bf16 activations), True (FP8
+    per token) or "x2" (two-term FP8 of the bf16 activations, MXFP4 weights)."""
+    if fp8 == "x2":
+        return QUANT_FP8X2
+    if fp8 in (False, True):
+        return QUANT_FP8 if fp8 else QUANT_NONE
+    raise ValueError(f"fp8 must be False, True or 'x2' (got {fp8!r})")
+
+
 def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
              apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
-             batched_max_tokens: int = 0, fp8: bool = False,
+             batched_max_tokens: int = 0, fp8=False,
              a1_scale: Optional[torch.Tensor] = None, a2_scale: Optional[torch.Tensor] = None):
     """moe_layer_options by reference (None when every option is its default)."""
     act = _act(activation)
@@ -74,7 +84,7 @@ def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
                 raise ValueError(f"{name} must hold one float32")
     return ctypes.byref(MoeLayerOptionsC(act, clamp, int(bool(apply_router_weight_on_input)),
                                          int(chunk_tokens), int(batched_max_tokens),
-                                         QUANT_FP8 if fp8 else QUANT_NONE, _ptr(a1_scale),
+                                         _quant(fp8), _ptr(a1_scale),
                                          _ptr(a2_scale)))
 
 
@@ -155,7 +165,7 @@ def moe_permuted_rows(T: int, k: int) -> int:
 
 def moe_workspace_size(T: int, k: int, E: int, E_l: int, H: int, I: int,
                        w_dtype: int = DTYPE_BF16, shared_I: int = 0, chunk_tokens: int = 0,
-                       batched_max_tokens: int = 0, fp8: bool = False) -> int:
+                       batched_max_tokens: int = 0, fp8=False) -> int:
     """Workspace bytes of the fused calls (the shared expert's included)."""
     n = ctypes.c_size_t(0)
     opts = _options(chunk_tokens=chunk_tokens, batched_max_tokens=batched_max_tokens, fp8=fp8)
@@ -355,6 +365,84 @@ def moe_grouped_gemm2_fp8(h_perm: torch.Tensor, h_scales: torch.Tensor, offsets:
     _check(lib().moe_grouped_gemm2_fp8(
         h_perm.data_ptr(), h_scales.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
         y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_fp8")
+    return y
+
+
+def moe_quantize_fp8x2(x: torch.Tensor, row_weights: Optional[torch.Tensor] = None,
+                       q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                       row_count: Optional[torch.Tensor] = None, stream=None):
+    """Two-term FP8 E4M3 quantization of bf16 rows -> (codes uint8 [rows, 2H]:
+    per 64 k the first term's 64 codes, then the second's; scales float32
+    [rows]), x ~ scale * (q1 + q2 / 16)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, H]")
+    rows, H = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, 2 * H), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _need(q, "q", torch.uint8, (rows, 2 * H), dev)
+    _need(scales, "scales", torch.float32, (rows,), dev)
+    if row_weights is not None:
+        _need(row_weights, "row_weights", torch.float32, device=dev)
+        if row_weights.numel() != rows:
+            raise ValueError("row_weights must hold one float32 per row")
+    if row_count is not None:
+        _need(row_count, "row_count", torch.int32, device=dev)
+    _check(lib().moe_quantize_fp8x2(x.data_ptr(), rows, H, _ptr(row_weights), _ptr(row_count),
+                                    q.data_ptr(), scales.data_ptr(), _stream(stream)),
+           "moe_quantize_fp8x2")
+    return q, scales
+
+
+def moe_grouped_gemm1_act_fp8x2(a_perm: torch.Tensor, a_scales: torch.Tensor,
+                                offsets: torch.Tensor, w1: Weights, I: int,
+                                h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                                activation_clamp: Optional[float] = None, stream=None,
+                                split: bool = True,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM1 + activation on two-term FP8 rows [R_pad, 2H] and MXFP4 weights -> bf16 [R_pad, I]."""
+    _need(a_perm, "a_perm", torch.uint8)
+    R_pad, H2 = a_perm.shape
+    H = H2 // 2
+    dev = a_perm.device
+    _need(a_scales, "a_scales", torch.float32, (R_pad,), dev)
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if H2 % 2 or w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}] for rows of 2H bytes")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_fp8x2(
+        a_perm.data_ptr(), a_scales.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I, w1.ref(),
+        _act(activation), 0.0 if activation_clamp is None else float(activation_clamp),
+        h.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_fp8x2")
+    return h
+
+
+def moe_grouped_gemm2_fp8x2(h_perm: torch.Tensor, h_scales: torch.Tensor, offsets: torch.Tensor,
+                            w2: Weights, H: int, y: Optional[torch.Tensor] = None, stream=None,
+                            split: bool = True,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM2 on two-term FP8 rows [R_pad, 2I] and MXFP4 weights -> bf16 [R_pad, H]."""
+    _need(h_perm, "h_perm", torch.uint8)
+    R_pad, I2 = h_perm.shape
+    I = I2 // 2
+    dev = h_perm.device
+    _need(h_scales, "h_scales", torch.float32, (R_pad,), dev)
+    _need(offsets, "offsets", torch.int32, (w2.E_l + 1,), dev)
+    if I2 % 2 or w2.N != H or w2.K != I:
+        raise ValueError(f"w2 must be [E_l, H={H}, I={I}] for rows of 2I bytes")
+    if y is None:
+        y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (R_pad, H), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm2_fp8x2(
+        h_perm.data_ptr(), h_scales.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
+        y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_fp8x2")
     return y
 
 
@@ -595,7 +683,7 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
                                   map: Optional[torch.Tensor] = None, stream=None,
                                   activation=ACT_SILU, activation_clamp: Optional[float] = None,
                                   apply_router_weight_on_input: bool = False,
-                                  batched_max_tokens: int = 0, fp8: bool = False,
+                                  batched_max_tokens: int = 0, fp8=False,
                                   a1_scale: Optional[torch.Tensor] = None,
                                   a2_scale: Optional[torch.Tensor] = None):
     """-> (gemm2_permuted bf16 [R_pad, H], expert_weights bf16 [T, k], map int32 [T, k]).
@@ -641,7 +729,7 @@ def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: We
                       workspace: Optional[torch.Tensor] = None, stream=None,
                       activation=ACT_SILU, activation_clamp: Optional[float] = None,
                       apply_router_weight_on_input: bool = False, chunk_tokens: int = 0,
-                      inplace: bool = False, batched_max_tokens: int = 0, fp8: bool = False,
+                      inplace: bool = False, batched_max_tokens: int = 0, fp8=False,
                       a1_scale: Optional[torch.Tensor] = None,
                       a2_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer, finalized (optionally with a shared expert ws1 [2Is, H], ws2 [H, Is]).

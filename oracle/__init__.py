@@ -69,10 +69,16 @@ def _load():
         L.oracle_e4m3_encode.argtypes = [dbl]
         L.oracle_quantize_fp8_rows.restype = None
         L.oracle_quantize_fp8_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.oracle_quantize_fp8x2_rows.restype = None
+        L.oracle_quantize_fp8x2_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         L.oracle_hidden_rows_fp8.restype = None
         L.oracle_hidden_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
         L.oracle_out_rows_fp8.restype = None
         L.oracle_out_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, vp]
+        L.oracle_hidden_rows_fp8x2.restype = None
+        L.oracle_hidden_rows_fp8x2.argtypes = [vp, vp, vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
+        L.oracle_out_rows_fp8x2.restype = None
+        L.oracle_out_rows_fp8x2.argtypes = [vp, vp, vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_out_rows.restype = None
         L.oracle_out_rows.argtypes = [vp, i64, i64, i64, Wp, vp, vp]
         L.oracle_finalize.restype = None
@@ -216,6 +222,18 @@ def quantize_fp8_rows(x_bf16: np.ndarray, static_scale: Optional[float] = None):
     return q, sc
 
 
+def quantize_fp8x2_rows(x_bf16: np.ndarray):
+    """Two-term FP8 quantization of bf16 rows -> (q1 uint8 [rows, H], q2 uint8
+    [rows, H], scales float32 [rows]): x ~ scale * (q1 + q2 / 16)."""
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    q1 = np.empty((rows, H), dtype=np.uint8)
+    q2 = np.empty((rows, H), dtype=np.uint8)
+    sc = np.empty((rows,), dtype=np.float32)
+    _load().oracle_quantize_fp8x2_rows(_p(x), rows, H, _p(q1), _p(q2), _p(sc))
+    return q1, q2, sc
+
+
 def hidden_rows_fp8(aq: np.ndarray, a_scales: np.ndarray, w1: Weights, expert_of_row: np.ndarray,
                     I: int, activation: str = "silu", clamp: float = 0.0) -> np.ndarray:
     """hidden_rows on FP8 rows (decoded as code * row scale), float64 [rows, I]."""
@@ -238,6 +256,32 @@ def out_rows_fp8(hq: np.ndarray, h_scales: np.ndarray, w2: Weights, expert_of_ro
     rows, I = hq.shape
     y = np.empty((rows, H), dtype=np.float64)
     _load().oracle_out_rows_fp8(_p(hq), _p(sc), rows, I, H, w2.ref, _p(eor), _p(y))
+    return y
+
+
+def hidden_rows_fp8x2(q1: np.ndarray, q2: np.ndarray, a_scales: np.ndarray, w1: Weights,
+                      expert_of_row: np.ndarray, I: int, activation: str = "silu",
+                      clamp: float = 0.0) -> np.ndarray:
+    """hidden_rows on two-term FP8 rows, decoded to (q1 + q2 / 16) * scale."""
+    a1, a2 = _c(q1, np.uint8), _c(q2, np.uint8)
+    sc = _c(a_scales, np.float32)
+    eor = _c(expert_of_row, np.int32)
+    rows, H = a1.shape
+    h = np.empty((rows, I), dtype=np.float64)
+    _load().oracle_hidden_rows_fp8x2(_p(a1), _p(a2), _p(sc), rows, H, I, w1.ref, _p(eor),
+                                     ACTIVATIONS[activation], float(clamp), _p(h))
+    return h
+
+
+def out_rows_fp8x2(q1: np.ndarray, q2: np.ndarray, h_scales: np.ndarray, w2: Weights,
+                   expert_of_row: np.ndarray, H: int) -> np.ndarray:
+    """out_rows on two-term FP8 rows, decoded to (q1 + q2 / 16) * scale."""
+    a1, a2 = _c(q1, np.uint8), _c(q2, np.uint8)
+    sc = _c(h_scales, np.float32)
+    eor = _c(expert_of_row, np.int32)
+    rows, I = a1.shape
+    y = np.empty((rows, H), dtype=np.float64)
+    _load().oracle_out_rows_fp8x2(_p(a1), _p(a2), _p(sc), rows, I, H, w2.ref, _p(eor), _p(y))
     return y
 
 
@@ -304,14 +348,15 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
                ws1: Optional[np.ndarray] = None, ws2: Optional[np.ndarray] = None,
                rsf_fin: float = 1.0, tokens: Optional[Sequence[int]] = None,
                activation: str = "silu", clamp: float = 0.0, weight_on_input: bool = False,
-               fp8: bool = False, a1_scale: Optional[float] = None,
+               fp8=False, a1_scale: Optional[float] = None,
                a2_scale: Optional[float] = None):
     """The whole layer for the listed tokens (all when None).  activation and
     clamp as for hidden_rows (every expert, the shared one included);
     weight_on_input: the routing weight scales the token before its expert
     MLP instead of the MLP's output (top_k = 1).  fp8: the routed experts see
     their input and hidden rows quantized per row to FP8 E4M3 (static
-    a1_scale / a2_scale when given).
+    a1_scale / a2_scale when given); fp8 "x2": quantized to two FP8 terms
+    (quantize_fp8x2_rows).
 
     Returns dict: out float64 [n, H], y_routes float64 [n, k, H] (unweighted
     per-route expert outputs, zero when not local), ids int32 [n, k],
@@ -335,6 +380,7 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
     _load().oracle_moe_tokens(_p(x), H, I, _p(logits), E, k, score, int(bool(renormalize)), rsf,
                               _p(expert_map), w1.ref, w2.ref, shared_I, _p(ws1), _p(ws2),
                               rsf_fin, ACTIVATIONS[activation], float(clamp),
-                              int(bool(weight_on_input)), int(bool(fp8)), _p(s1), _p(s2), _p(tok),
+                              int(bool(weight_on_input)), 2 if fp8 == "x2" else int(bool(fp8)),
+                              _p(s1), _p(s2), _p(tok),
                               n, _p(out), _p(y), _p(ids), _p(w))
     return {"out": out, "y_routes": y, "ids": ids, "weights": w, "tokens": tok}

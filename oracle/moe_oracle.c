@@ -144,6 +144,54 @@ void oracle_quantize_fp8_rows(const uint16_t* x, int64_t rows, int64_t H,
   }
 }
 
+/* Two-term FP8 quantization of bf16 rows: bf16 activations carried to the
+ * FP8 x e2m1 matrix cores at close to bf16 precision (the quantize step of
+ * prepare for MXFP4 weights).  Per row, with the dynamic scale and inv of
+ * oracle_quantize_fp8_rows, in float32 as the kernel decides the codes:
+ *   v = min(max(x[j] * inv, -448), 448),  q1[j] = e4m3(v),
+ *   d = v - value(q1[j])                  (a difference of two nearby
+ *                                          floats: exact),
+ *   q2[j] = e4m3(16 d),
+ * so x[j] ~ scale * (value(q1) + value(q2) / 16). */
+void oracle_quantize_fp8x2_rows(const uint16_t* x, int64_t rows, int64_t H, uint8_t* q1,
+                                uint8_t* q2, float* scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * H;
+    float amax = 0.0f;
+    for (int64_t j = 0; j < H; ++j) {
+      float a = fabsf((float)bf16_val(xr[j]));
+      if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) amax = 448.0f;
+    const float inv = 448.0f / amax;
+    for (int64_t j = 0; j < H; ++j) {
+      float v = (float)bf16_val(xr[j]) * inv;
+      if (v > 448.0f) v = 448.0f;
+      if (v < -448.0f) v = -448.0f;
+      const uint8_t c1 = oracle_e4m3_encode((double)v);
+      const double d = (double)v - oracle_e4m3_decode(c1);
+      q1[r * H + j] = c1;
+      q2[r * H + j] = oracle_e4m3_encode(16.0 * d);
+    }
+    scales[r] = amax / 448.0f;
+  }
+}
+
+/* A row quantized by oracle_quantize_fp8_rows (terms 1) or
+ * oracle_quantize_fp8x2_rows (terms 2), decoded to doubles. */
+static void quantize_decode(const uint16_t* row, int64_t n, int terms, const float* static_scale,
+                            uint8_t* c1, uint8_t* c2, double* out) {
+  float sc;
+  if (terms == 2) {
+    oracle_quantize_fp8x2_rows(row, 1, n, c1, c2, &sc);
+    for (int64_t c = 0; c < n; ++c)
+      out[c] = (oracle_e4m3_decode(c1[c]) + oracle_e4m3_decode(c2[c]) / 16.0) * (double)sc;
+  } else {
+    oracle_quantize_fp8_rows(row, 1, n, static_scale, c1, &sc);
+    for (int64_t c = 0; c < n; ++c) out[c] = oracle_e4m3_decode(c1[c]) * (double)sc;
+  }
+}
+
 /* Weight element (row, kk) of a [rows, K] matrix in any storage format (FP8:
  * the code times the row's scale, per_out_ch_quant). */
 double oracle_weight_at(const oracle_weights* w, int64_t row, int64_t K, int64_t kk) {
@@ -387,6 +435,44 @@ void oracle_out_rows_fp8(const uint8_t* hq, const float* h_scales, int64_t rows,
   }
 }
 
+/* The same on two-term FP8 rows (codes q1, q2 [rows, K] and one scale per
+ * row, as oracle_quantize_fp8x2_rows writes them): the rows are decoded to
+ * (q1 + q2 / 16) * scale. */
+void oracle_hidden_rows_fp8x2(const uint8_t* q1, const uint8_t* q2, const float* a_scales,
+                              int64_t rows, int64_t H, int64_t I, const oracle_weights* w1,
+                              const int32_t* expert_of_row, int32_t act, double clamp,
+                              double* h) {
+#pragma omp parallel
+  {
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < H; ++c)
+        xv[c] = (oracle_e4m3_decode(q1[r * H + c]) + oracle_e4m3_decode(q2[r * H + c]) / 16.0) *
+                (double)a_scales[r];
+      oracle_expert_hidden_act(xv, H, I, w1, expert_of_row[r], act, clamp, h + r * I);
+    }
+    free(xv);
+  }
+}
+
+void oracle_out_rows_fp8x2(const uint8_t* q1, const uint8_t* q2, const float* h_scales,
+                           int64_t rows, int64_t I, int64_t H, const oracle_weights* w2,
+                           const int32_t* expert_of_row, double* y) {
+#pragma omp parallel
+  {
+    double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < I; ++c)
+        hv[c] = (oracle_e4m3_decode(q1[r * I + c]) + oracle_e4m3_decode(q2[r * I + c]) / 16.0) *
+                (double)h_scales[r];
+      oracle_expert_out(hv, H, I, w2, expert_of_row[r], y + r * H);
+    }
+    free(hv);
+  }
+}
+
 void oracle_out_rows(const uint16_t* hb, int64_t rows, int64_t I, int64_t H,
                      const oracle_weights* w2, const int32_t* expert_of_row, double* y) {
 #pragma omp parallel
@@ -468,7 +554,9 @@ void oracle_finalize_add_rmsnorm(const uint16_t* y_perm, const double* w, const 
  * expert sees its input row as bf16 (x, or bf16(w_j * x) with
  * weight_on_input) quantized per row to FP8 (oracle_quantize_fp8_rows; static
  * a1_scale when given), and its hidden row h rounded to bf16 and quantized
- * the same way (static a2_scale when given).  The shared expert stays bf16.
+ * the same way (static a2_scale when given).  act_quant 2 quantizes both rows
+ * with the two-term rule instead (oracle_quantize_fp8x2_rows, dynamic scales).
+ * The shared expert stays bf16.
  * Optional outputs: y_routes [n, k, H] (the unweighted per-route expert output,
  * zero for non-local routes), ids [n, k], weights [n, k].
  * shared_I = 0 disables the shared expert. */
@@ -494,6 +582,7 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
     int64_t Qmax = H > I ? H : I;
     uint16_t* qin = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Qmax);
     uint8_t* qout = (uint8_t*)malloc((size_t)Qmax);
+    uint8_t* qout2 = (uint8_t*)malloc((size_t)Qmax);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t s = 0; s < n_tokens; ++s) {
       int64_t t = tokens[s];
@@ -516,19 +605,15 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
           xin = xw;
         }
         if (act_quant) {
-          float sc;
           for (int64_t c = 0; c < H; ++c)
             qin[c] = weight_on_input ? bf16_bits((float)wts[j] * (float)xv[c]) : x[t * H + c];
-          oracle_quantize_fp8_rows(qin, 1, H, a1_scale, qout, &sc);
-          for (int64_t c = 0; c < H; ++c) xw[c] = oracle_e4m3_decode(qout[c]) * (double)sc;
+          quantize_decode(qin, H, act_quant, a1_scale, qout, qout2, xw);
           xin = xw;
         }
         oracle_expert_hidden_act(xin, H, I, w1, L, act, clamp, hv);
         if (act_quant) {
-          float sc;
           for (int64_t c = 0; c < I; ++c) qin[c] = bf16_bits((float)hv[c]);
-          oracle_quantize_fp8_rows(qin, 1, I, a2_scale, qout, &sc);
-          for (int64_t c = 0; c < I; ++c) hv[c] = oracle_e4m3_decode(qout[c]) * (double)sc;
+          quantize_decode(qin, I, act_quant, a2_scale, qout, qout2, hv);
         }
         oracle_expert_out(hv, H, I, w2, L, yr);
         const double wj = weight_on_input ? 1.0 : wts[j];
@@ -549,6 +634,7 @@ void oracle_moe_tokens(const uint16_t* x, int64_t H, int64_t I, const float* log
     free(wts);
     free(qin);
     free(qout);
+    free(qout2);
   }
 }
 

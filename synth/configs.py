@@ -38,6 +38,8 @@ class MoeConfig:
     mxfp4: bool = False
     fp8: bool = False               # FP8 E4M3 activations (per token); weights FP8 per channel
                                     # unless mxfp4
+    fp8x2: bool = False             # bf16 activations carried as two FP8 E4M3 terms
+                                    # (MXFP4 weights)
     zipf_s: float = 0.0             # Zipf exponent of the logit bias (0: none)
     deferred: bool = False
 
@@ -73,8 +75,14 @@ DEEPSEEK_MXFP4_FP8 = MoeConfig("deepseekv3_mxfp4_fp8act_2048tok", T=2048, H=7168
                                k=8, score=SIGMOID, renormalize=True, rsf=2.5, seed=5, mxfp4=True,
                                fp8=True)
 
+# the MXFP4 workload with its bf16 activations carried to the FP8 x e2m1
+# matrix cores as two FP8 terms per token (and per hidden row)
+DEEPSEEK_MXFP4_X2 = MoeConfig("deepseekv3_mxfp4_x2act_2048tok", T=2048, H=7168, I=2048, E=256,
+                              k=8, score=SIGMOID, renormalize=True, rsf=2.5, seed=5, mxfp4=True,
+                              fp8x2=True)
+
 ALL = {c.name: c for c in (TINY, MIXTRAL, DEEPSEEK, EP_DECODE, DEEPSEEK_MXFP4, MIXTRAL_FP8,
-                           DEEPSEEK_FP8, DEEPSEEK_MXFP4_FP8)}
+                           DEEPSEEK_FP8, DEEPSEEK_MXFP4_FP8, DEEPSEEK_MXFP4_X2)}
 
 EP_DECODE_BATCHES = (1, 8, 64)
 EP_DECODE_DRAWS = 16
