@@ -7,8 +7,11 @@
 //               + shared[t, :]
 //
 // One workgroup per token (grid-stride); each thread owns 8 consecutive
-// columns, so every access is a 16-byte load or store.  The routes of the
-// token (map and weights, k <= 32) are staged once in LDS.
+// columns, so every access is a 16-byte load or store.  With few tokens the
+// columns of a token are split over gridDim.y workgroups, so a decode batch
+// still spreads over the chip.  The routes of the token (map and weights,
+// k <= 32) are staged once in LDS; a thread issues the loads of up to 8
+// routes before it adds any of them, so their latencies overlap.
 // Entries of -1 are skipped, so rows the map never names are never read.
 // Accumulation is fp32 in j order, rounded once to bf16.  Without weights
 // (NULL) every route counts once: finalize() with apply_router_weight_on_input,
@@ -17,6 +20,35 @@
 
 namespace moe {
 namespace {
+
+constexpr int kRouteBatch = 8;  // route rows loaded before they are added
+
+// acc[0..8) = sum over j ascending with row s_row[j] >= 0 of s_w[j] * y[row, 8c .. 8c+7]
+// (rows of -1 add nothing; the loads of a batch of routes are in flight together)
+__device__ __forceinline__ void sum_routes(const uint4* __restrict__ y, int H8, int c, int k,
+                                           const int32_t* s_row, const float* s_w, float* acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += kRouteBatch) {
+    uint4 v[kRouteBatch];
+#pragma unroll
+    for (int jj = 0; jj < kRouteBatch; ++jj) {
+      const int32_t r = j0 + jj < k ? s_row[j0 + jj] : -1;
+      v[jj] = r >= 0 ? y[static_cast<int64_t>(r) * H8 + c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < kRouteBatch; ++jj) {
+      if (j0 + jj >= k || s_row[j0 + jj] < 0) continue;
+      const float wj = s_w[j0 + jj];
+      const uint32_t p[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] & 0xFFFFu));
+        acc[2 * i + 1] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] >> 16));
+      }
+    }
+  }
+}
 
 template <bool W_BF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__ y,
@@ -35,22 +67,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__
                    : static_cast<const float*>(wts)[t * k + threadIdx.x];
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
+    for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < H8; c += gridDim.y * blockDim.x) {
       float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = s_row[j];
-        if (r < 0) continue;
-        const float wj = s_w[j];
-        const uint4 v = y[static_cast<int64_t>(r) * H8 + c];
-        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] & 0xFFFFu));
-          acc[2 * i + 1] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] >> 16));
-        }
-      }
+      sum_routes(y, H8, c, k, s_row, s_w, acc);
       float add[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) add[i] = 0.0f;
@@ -106,20 +125,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
     float ss = 0.0f;
     for (int c = threadIdx.x; c < H8; c += blockDim.x) {
       float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = s_row[j];
-        if (r < 0) continue;
-        const float wj = s_w[j];
-        const uint4 v = y[static_cast<int64_t>(r) * H8 + c];
-        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] & 0xFFFFu));
-          acc[2 * i + 1] += wj * bf16_to_f32(static_cast<uint16_t>(p[i] >> 16));
-        }
-      }
+      sum_routes(y, H8, c, k, s_row, s_w, acc);
       float z[8];
       const uint4 rv = residual[t * H8 + c];
       const uint4 sv = shared ? shared[t * H8 + c] : make_uint4(0, 0, 0, 0);
@@ -209,12 +215,16 @@ hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const in
   const int H8 = H / 8;
   const int threads = H8 >= 256 ? 256 : ((H8 + 63) / 64) * 64;
   const int64_t blocks = T < 16384 ? T : 16384;
+  // few tokens: each token's columns over several workgroups (one column
+  // chunk per thread), so a decode batch fills more than a few CUs
+  const int split = T < 1024 ? (H8 + threads - 1) / threads : 1;
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(split));
   if (w_is_bf16)
-    hipLaunchKernelGGL(finalize_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(threads),
+    hipLaunchKernelGGL(finalize_kernel<true>, grid, dim3(threads),
                        0, s, static_cast<const uint4*>(y), w, map, T, k, H8, rsf_fin,
                        static_cast<const uint4*>(shared), static_cast<uint4*>(out));
   else
-    hipLaunchKernelGGL(finalize_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(threads),
+    hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(threads),
                        0, s, static_cast<const uint4*>(y), w, map, T, k, H8, rsf_fin,
                        static_cast<const uint4*>(shared), static_cast<uint4*>(out));
   return hipGetLastError();

@@ -4,8 +4,12 @@
 //
 // One wave per token.  Lane l holds logits l, l+64, l+128, ... in registers.
 // Each of the k rounds takes a wave-wide argmax under the order
-// (logit descending, expert id ascending) with an xor butterfly, so every lane
-// ends the round with the same winner; the winning element is marked taken.
+// (logit descending, expert id ascending): four DPP steps give every lane of
+// each 16-lane row its row's best (swap within pairs, within quads, mirror
+// within 8, mirror within 16), and the four rows' bests are read into scalar
+// registers and compared there, so every lane ends the round with the same
+// winner; the winning element is marked taken.  (DPP moves are register
+// operations; a shuffle through the LDS crossbar costs a round trip per step.)
 // Lane j keeps the j-th winner, so the k results end up in lanes 0..k-1 and
 // are stored with one coalesced write.  Selection compares fp32 logits only
 // (no arithmetic), so the chosen ids are exact.
@@ -16,6 +20,40 @@ namespace {
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
+}
+
+// The better of (v, i) and the pair DPP control `ctrl` brings from another
+// lane of the same 16-lane row (every lane of the row takes part).
+template <int CTRL>
+__device__ __forceinline__ void dpp_best(float& v, int& i) {
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide best pair under `better`, returned in every lane.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+  dpp_best<0xB1>(v, i);   // quad_perm [1, 0, 3, 2]
+  dpp_best<0x4E>(v, i);   // quad_perm [2, 3, 0, 1]
+  dpp_best<0x141>(v, i);  // row_half_mirror
+  dpp_best<0x140>(v, i);  // row_mirror
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < kWave / 16; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
 }
 
 template <int EPL>
@@ -52,15 +90,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_best(bv, bi);
     if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == j) {
       my_v = bv;
