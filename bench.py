@@ -64,6 +64,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MiB) + MALL (256 MiB)
+GATHER_IN_GEMM_ROUTES = 1024  # passes of at most this many routes: GEMM1 gathers its rows
 
 
 def parse():
@@ -314,6 +315,10 @@ def main():
     w_in = args.router_weight_on_input
 
     counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
+    # decode-sized bf16 passes: GEMM1 reads its rows from x through the
+    # permute's inverse map, as the library's fused calls do (no gather kernel)
+    gathered = (not quant and not Mb and not w_in and P * k <= GATHER_IN_GEMM_ROUTES)
+    inv_buf = torch.empty((R_pad,), dtype=torch.int32, device=dev) if gathered else None
 
     def permute(sl, st):
         if cfg.fp8x2:
@@ -330,6 +335,9 @@ def main():
         if Mb:
             moe.moe_permute_batched(ids[sl], E, Mb, El, emap_d, xd_cur[0][sl], pmap[sl], counts_b,
                                     x_perm.view(El, Mb, H), wts[sl] if w_in else None, stream=st)
+        elif gathered:
+            moe.moe_permute(ids[sl], E, El, emap_d, None, R_pad, pmap[sl], offsets, inv_buf,
+                            stream=st)
         else:
             moe.moe_permute(ids[sl], E, El, emap_d, xd_cur[0][sl], R_pad, pmap[sl], offsets, None,
                             x_perm, want_inv=False, x_weights=wts[sl] if w_in else None,
@@ -363,13 +371,18 @@ def main():
                                           max_rows=n * k, stream=st, split=False,
                                           workspace=split_ws)
         else:
-            moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
-                                      workspace=split_ws, **act_kw)
+            if gathered:
+                moe.moe_grouped_gemm1_act_gathered(xd_cur[0][gsl[0]], inv_buf, k, offsets, W1, I,
+                                                   h, stream=st, split=False, workspace=split_ws,
+                                                   **act_kw)
+            else:
+                moe.moe_grouped_gemm1_act(x_perm, offsets, W1, I, h, stream=st, split=False,
+                                          workspace=split_ws, **act_kw)
             mark_cur[0]("gemm2")
             moe.moe_grouped_gemm2(h, offsets, W2, H, y, stream=st, split=False,
                                   workspace=split_ws)
 
-    xd_cur, mark_cur = [None], [None]
+    xd_cur, mark_cur, gsl = [None], [None], [None]
 
     def route_permute(d, t0, n):
         xd, ld = dev_draws[d]
@@ -389,6 +402,7 @@ def main():
         xd_cur[0], mark_cur[0] = xd, mark
         for t0, n in chunks:
             sl = slice(t0, t0 + n)
+            gsl[0] = sl
             mark("route")
             moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                                st)

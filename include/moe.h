@@ -363,6 +363,26 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
                           float activation_clamp, void* h, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* GEMM1 + activation reading its rows straight from the token matrix (the
+ * dispatch of [Quantize-Dispatch] folded into the first expert GEMM; apply()
+ * of page "modular_kernel.py"): the same result as moe_permute's gather
+ * followed by moe_grouped_gemm1_act, bit for bit, without the x_perm round
+ * trip.  Permuted row r of expert e reads x[inv[r] / k, :].
+ *   x        (device) bf16 [T, H] token rows (T * H * 2 bytes at most 4 GiB)
+ *   inv      (device) int32 [R_pad] from moe_permute (row -> expanded index
+ *            t*k + j for r < offsets[E_l]; other rows are never read)
+ *   offsets, E_l, R_pad, H, I, w1, activation, h, workspace: as for
+ *            moe_grouped_gemm1_act (bf16 or MXFP4 weights).
+ * The fused calls use it for passes of at most 1024 routes (bf16 activations,
+ * standard layout, weights not on the input), where it saves a kernel; for
+ * larger passes the separate gather is cheaper than the index load that
+ * starts every GEMM tile here. */
+int moe_grouped_gemm1_act_gathered(const void* x, const int32_t* inv, int64_t T, int32_t k,
+                                   const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                                   int32_t I, const moe_weights* w1, int32_t activation,
+                                   float activation_clamp, void* h, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Grouped GEMM2 (apply() of page "modular_kernel.py"; its output is the
  * unweighted, unreduced gemm2_permuted of page "moe_output.py": densely
  * packed at H).  For every local expert e and row r in [offsets[e],

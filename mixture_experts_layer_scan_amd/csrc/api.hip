@@ -174,6 +174,9 @@ int check_activation(int32_t activation, float clamp) {
   return MOE_OK;
 }
 
+// Passes of at most this many routes let GEMM1 gather its rows itself.
+constexpr int64_t kGatherInGemmRoutes = 1024;
+
 // Options of the fused entry points, checked.
 struct LayerOpts {
   int act = MOE_ACT_SILU;
@@ -244,6 +247,7 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, 
   b += align_up(sizeof(float) * T * k);                 // topk weights
   b += align_up(sizeof(int32_t) * T * k);               // permute map (finalized form)
   b += align_up(sizeof(int32_t) * (E_l + 1));           // offsets
+  b += align_up(sizeof(int32_t) * R_pad);               // inverse map (gathered GEMM1 rows)
   b += align_up(sizeof(uint16_t) * R_pad * H);          // x_perm, then GEMM2 output
   b += align_up(sizeof(uint16_t) * R_pad * I);          // h
   b += align_up(routed_split_bytes(R_pad, H, I));       // GEMM split partials
@@ -414,7 +418,8 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
                        int32_t K, int32_t N_out, int gated, int act, float clamp,
                        const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
                        void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
-                       bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1) {
+                       bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1,
+                       const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
@@ -427,7 +432,8 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   MOE_CHECK(need_ptr(a, "input rows"));
   MOE_CHECK(need_ptr(offsets, "offsets"));
   MOE_CHECK(need_ptr(c, "output rows"));
-  const size_t in_bytes = (fp8 ? a_terms : sizeof(uint16_t)) * R_pad * K;
+  // (gathered: the token rows, at most R_pad of them)
+  const size_t in_bytes = (fp8 ? a_terms : sizeof(uint16_t)) * (a_inv ? a_T : R_pad) * K;
   const size_t out_bytes = sizeof(uint16_t) * R_pad * N_out;
   if (overlap(a, in_bytes, c, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
@@ -442,7 +448,7 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   }
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
                   workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
-                  a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms};
+                  a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms, a_inv, a_k, a_T};
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -457,6 +463,31 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
   MOE_CHECK(check_activation(activation, activation_clamp));
   return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
                      workspace, workspace_bytes, stream, "moe_grouped_gemm1_act");
+}
+
+int moe_grouped_gemm1_act_gathered(const void* x, const int32_t* inv, int64_t T, int32_t k,
+                                   const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
+                                   int32_t I, const moe_weights* w1, int32_t activation,
+                                   float activation_clamp, void* h, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (T < 0 || k <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 and k > 0");
+  if (R_pad < T * k) return fail(MOE_ERR_SIZE_MISMATCH, "R_pad (%lld) < T * k (%lld)",
+                                 (long long)R_pad, (long long)(T * k));
+  if (T * int64_t(H) * 2 > int64_t(0xFFFFFFFF))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x spans more than 4 GiB");
+  if (R_pad > 0) MOE_CHECK(need_ptr(inv, "inv"));
+  if (overlap(inv, sizeof(int32_t) * R_pad, h, sizeof(uint16_t) * R_pad * I))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "h must not overlap inv");
+  if (R_pad == 0 || T == 0) {
+    MOE_CHECK(check_weights(w1, "moe_grouped_gemm1_act_gathered"));
+    return MOE_OK;
+  }
+  return gemm_common(x, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_gathered", 0, 0,
+                     false, nullptr, 1, inv, k, T);
 }
 
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
@@ -722,6 +753,7 @@ struct RoutedWs {
   float* wts;
   int32_t* map;
   int32_t* offsets;
+  int32_t* inv;      // permuted row -> expanded index (GEMM1 reading token rows itself)
   uint16_t* x_perm;  // gathered rows, later reused for the GEMM2 output
   uint16_t* h;
   void* split;       // split-reduction scratch of both GEMMs
@@ -744,6 +776,7 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   b.wts = c.take<float>(T * k);
   b.map = c.take<int32_t>(T * k);
   b.offsets = c.take<int32_t>(E_l + 1);  // offsets, or per-expert counts when batched
+  b.inv = c.take<int32_t>(b.rows);
   b.x_perm = c.take<uint16_t>(b.rows * H);
   b.h = c.take<uint16_t>(b.rows * I);
   b.split_bytes = routed_split_bytes(b.rows, H, I);
@@ -783,8 +816,14 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
                                  nullptr, b.xq, b.xs, s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize");
   }
-  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets, nullptr, b.rows, s,
-                          o.batch_m);
+  // Decode-sized passes of bf16 rows: GEMM1 reads each permuted row straight
+  // from x through the inverse map (no gather kernel, no x_perm round trip);
+  // for larger passes the gather kernel's streaming copy costs less than a
+  // dependent index load at the start of every GEMM1 tile.
+  const bool gather_in_gemm = !o.fp8 && o.batch_m == 0 && !o.weight_on_input &&
+                              T * k <= kGatherInGemmRoutes;
+  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets,
+                          gather_in_gemm ? b.inv : nullptr, b.rows, s, o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");
   if (o.fp8) {
     e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H * o.terms, b.x_perm, b.ps, s);
@@ -806,12 +845,20 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     if (e != hipSuccess) return hip_fail(e, "gemm2");
     return MOE_OK;
   }
-  e = moe::launch_gather_rows(x, map, T, k, H, o.weight_on_input ? b.wts : nullptr, b.x_perm, s);
-  if (e != hipSuccess) return hip_fail(e, "gather");
+  if (!gather_in_gemm) {
+    e = moe::launch_gather_rows(x, map, T, k, H, o.weight_on_input ? b.wts : nullptr, b.x_perm,
+                                s);
+    if (e != hipSuccess) return hip_fail(e, "gather");
+  }
   // the tile shape follows the routed rows, the same bound in both formats
   const int64_t max_rows = std::min(moe_permuted_rows(T, k), b.rows);
-  moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
-                   b.split, b.split_bytes, o.act, o.clamp, o.batch_m};
+  moe::GemmArgs g1{gather_in_gemm ? x : b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I,
+                   1, b.rows, b.h, b.split, b.split_bytes, o.act, o.clamp, o.batch_m};
+  if (gather_in_gemm) {
+    g1.a_inv = b.inv;
+    g1.a_k = k;
+    g1.a_T = T;
+  }
   e = moe::launch_grouped_gemm(g1, max_rows, s);
   if (e != hipSuccess) return hip_fail(e, "gemm1");
   moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,

@@ -342,7 +342,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const void* __restrict__ W_scales, const int32_t* __restrict__ offsets, int E_l, int K,
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
     int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m,
-    const float* __restrict__ A_scales) {
+    const float* __restrict__ A_scales, const int32_t* __restrict__ a_inv, int a_k,
+    int64_t a_T) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
@@ -477,15 +478,21 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     const int fm_act = __builtin_amdgcn_readfirstlane(
         Cfg::SKIP ? min(FM, (rows - wm * Cfg::WTM + 31) / 32) : FM);
 
-    // Buffer descriptors: A over rows [row0, seg_end) of this expert, W over
-    // this expert's weights; loads past either range return zero.
+    // Buffer descriptors: A over rows [row0, seg_end) of this expert (or,
+    // gathered, over all token rows, rows past the segment given an offset
+    // past the end), W over this expert's weights; loads past either range
+    // return zero.
     // activation bytes per row: K * 2 (bf16) or K (fp8)
     // (two-term fp8: K * 2, both terms)
     const uint32_t a_row_bytes = (Cfg::F8 && !Cfg::A2) ? static_cast<uint32_t>(K)
                                                        : static_cast<uint32_t>(K) * 2u;
+    const bool gathered = a_inv != nullptr;  // uniform
+    const uint32_t a_span = gathered ? static_cast<uint32_t>(a_T) * a_row_bytes
+                                     : static_cast<uint32_t>(rows) * a_row_bytes;
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(static_cast<const uint8_t*>(A) + static_cast<int64_t>(row0) * a_row_bytes),
-        0, static_cast<int>(static_cast<uint32_t>(rows) * a_row_bytes), kBufferFlags);
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(A) +
+                             (gathered ? 0 : static_cast<int64_t>(row0) * a_row_bytes)),
+        0, static_cast<int>(a_span), kBufferFlags);
     // weight bytes per row: K * 2 (bf16), K / 2 (packed e2m1) or K (fp8)
     const uint32_t w_row_bytes = Cfg::WQ ? static_cast<uint32_t>(K) / 2u
                                  : Cfg::F8 ? static_cast<uint32_t>(K)
@@ -499,7 +506,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     for (int j = 0; j < Cfg::A_LD; ++j) {
       const int r = (j * Cfg::NWAVES + wave_u) * 8 + ld_sub;
       const int c = ld_pos ^ swz_key(r);
-      a_off[j] = static_cast<uint32_t>(r) * a_row_bytes + c * 16u;
+      if (gathered) {
+        // the token of permuted row row0 + r; past the segment, past the end
+        const int32_t x = r < rows ? a_inv[row0 + r] : -1;
+        a_off[j] = x >= 0 ? static_cast<uint32_t>(x / a_k) * a_row_bytes + c * 16u : a_span;
+      } else {
+        a_off[j] = static_cast<uint32_t>(r) * a_row_bytes + c * 16u;
+      }
     }
     // gated: virtual rows [0, BN/2) are gate rows n0 + v, the rest up rows
     // I + n0 + v - BN/2; columns past N_out are loaded but never stored
@@ -964,7 +977,7 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
                      dim3(Cfg::kThreads), 0, s,
                      g.a, g.w, g.w_scales, g.offsets, g.E_l, g.K,
                      g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
-                     g.act, g.clamp, g.batch_m, g.a_scales);
+                     g.act, g.clamp, g.batch_m, g.a_scales, g.a_inv, g.a_k, g.a_T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));

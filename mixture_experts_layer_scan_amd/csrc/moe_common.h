@@ -126,6 +126,11 @@ struct GemmArgs {
   const float* a_scales = nullptr;  // fp8 activations: fp32 [R_pad], one per row
   bool w_mxfp4 = false;             // with fp8 activations: MXFP4 weights (else FP8)
   int a_terms = 1;                  // 2: two-term fp8 activations [R_pad, 2K] (MXFP4 weights)
+  // gathered activations (bf16): a holds a_T token rows [a_T, K] and permuted
+  // row r reads token a_inv[r] / a_k (a_inv: the permute's inverse map)
+  const int32_t* a_inv = nullptr;
+  int a_k = 1;
+  int64_t a_T = 0;
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its

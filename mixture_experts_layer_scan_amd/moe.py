@@ -583,6 +583,35 @@ def moe_grouped_gemm1_act(a_perm: torch.Tensor, offsets: torch.Tensor, w1: Weigh
     return h
 
 
+
+def moe_grouped_gemm1_act_gathered(x: torch.Tensor, inv: torch.Tensor, k: int,
+                                   offsets: torch.Tensor, w1: Weights, I: int,
+                                   h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                                   stream=None, split: bool = True,
+                                   workspace: Optional[torch.Tensor] = None,
+                                   activation_clamp: Optional[float] = None) -> torch.Tensor:
+    """moe_grouped_gemm1_act on rows read straight from the tokens: permuted row
+    r is x[inv[r] // k] (inv from moe_permute) -> bf16 [R_pad, I], R_pad = inv's length."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
+    T, H = x.shape
+    dev = x.device
+    _need(inv, "inv", torch.int32, device=dev)
+    R_pad = inv.numel()
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_gathered(
+        x.data_ptr(), inv.data_ptr(), T, k, offsets.data_ptr(), w1.E_l, R_pad, H, I, w1.ref(),
+        _act(activation), 0.0 if activation_clamp is None else float(activation_clamp),
+        h.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_gathered")
+    return h
+
 def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: int,
                       y: Optional[torch.Tensor] = None, stream=None,
                       split: bool = True, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:

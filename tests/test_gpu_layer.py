@@ -19,6 +19,7 @@ import torch
 
 import mixture_experts_layer_scan_amd as moe
 import oracle
+import synth
 from synth import configs
 
 from gpu_util import (dev, dev_bf16, host_bf16_bits, host_f64, need_gpu, rel_fro,
@@ -218,3 +219,65 @@ def test_ep_rank_decode_deferred(T):
         if sel.any():
             assert rel_fro(yy[mm[sel]], ref["y_routes"][sel]) < TOL
         assert rel_fro(host_f64(out), ref["out"]) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 7, 128, 129])
+def test_decode_rows_gathered_by_gemm1(T):
+    """Passes of at most 1024 routes let GEMM1 read its rows from x through the
+    inverse map (no gather kernel); larger ones gather first.  Both sides of
+    that switch are bit-identical to the individual calls (which always
+    gather) and match the oracle, with a scattered expert map; the first
+    batch has one token whose routes are all non-local."""
+    cfg = configs.MoeConfig("gath", T=T, H=1024, I=512, E=64, k=8, score=configs.SIGMOID,
+                            renormalize=True, rsf=2.5, seed=70 + T, E_local=16)
+    emap = np.full(cfg.E, -1, dtype=np.int32)
+    local = np.arange(3, 64, 4)[:16]          # scattered global ids 3, 7, 11, ...
+    emap[local] = np.arange(16, dtype=np.int32)
+    x, logits = configs.make_activations(cfg)
+    if T == 1:
+        logits[0, local] = -1e9               # no local route at all
+    w = configs.make_weights(cfg)
+    W1, W2 = moe.Weights(dev_bf16(w["w1"])), moe.Weights(dev_bf16(w["w2"]))
+    xd, ld, ed = dev_bf16(x), dev(logits), dev(emap)
+    out = moe.moe_fused_experts(ld, xd, W1, W2, cfg.k, cfg.score, True, cfg.rsf, expert_map=ed)
+    ids, wts = moe.moe_route_topk(ld, cfg.k, cfg.score, True, cfg.rsf)
+    p = moe.moe_permute(ids, cfg.E, 16, ed, xd)
+    h = moe.moe_grouped_gemm1_act(p["x_perm"], p["offsets"], W1, cfg.I)
+    y = moe.moe_grouped_gemm2(h, p["offsets"], W2, cfg.H)
+    out_steps = moe.moe_finalize(y, wts, p["map"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(out), host_bf16_bits(out_steps))
+    ref = oracle.moe_tokens(x, logits, oracle.Weights(w["w1"]), oracle.Weights(w["w2"]), cfg.I,
+                            cfg.k, cfg.score, True, cfg.rsf, expert_map=emap)
+    assert rel_fro(host_f64(out), ref["out"]) < TOL
+    if T == 1:
+        assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("mxfp4", [False, True], ids=["bf16", "mxfp4"])
+@pytest.mark.parametrize("T,split", [(3, True), (40, True), (40, False), (300, False)])
+def test_gemm1_gathered_equals_gather_then_gemm1(T, split, mxfp4):
+    """moe_grouped_gemm1_act_gathered(x, inv) is moe_permute's gather followed by
+    moe_grouped_gemm1_act, bit for bit (decode tiles with and without split
+    reductions, and a wider batch), NaN in the unread padding rows of h's input."""
+    E, E_l, k, H, I = 32, 8, 4, 512, 256
+    x = synth.normal_bf16(80 + T, 0, (T, H))
+    logits = synth.normal_f32(80 + T, 1, (T, E))
+    emap = np.full(E, -1, dtype=np.int32)
+    emap[8:16] = np.arange(8, dtype=np.int32)
+    w1 = synth.normal_bf16(80 + T, 2, (E_l, 2 * I, H), std=1 / np.sqrt(H))
+    if mxfp4:
+        q, sc = synth.mxfp4_quantize(w1)
+        W1 = moe.Weights(dev(q), dev(sc))
+    else:
+        W1 = moe.Weights(dev_bf16(w1))
+    xd = dev_bf16(x)
+    ids, _ = moe.moe_route_topk(dev(logits), k, moe.SIGMOID)
+    p = moe.moe_permute(ids, E, E_l, dev(emap), xd)
+    R_l = int(p["offsets"][-1].item())
+    p["x_perm"][R_l:] = float("nan")
+    h_ref = moe.moe_grouped_gemm1_act(p["x_perm"], p["offsets"], W1, I, split=split)
+    h = moe.moe_grouped_gemm1_act_gathered(xd, p["inv"], k, p["offsets"], W1, I, split=split)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(h)[:R_l], host_bf16_bits(h_ref)[:R_l])
+    assert R_l > 0
