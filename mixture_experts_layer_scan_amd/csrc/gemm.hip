@@ -501,6 +501,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         const_cast<uint8_t*>(static_cast<const uint8_t*>(W) +
                              static_cast<int64_t>(e) * N_total * w_row_bytes),
         0, static_cast<int>(static_cast<uint32_t>(N_total) * w_row_bytes), kBufferFlags);
+    // Weight rows a power of two apart put the 128-byte segments that the
+    // concurrent tiles of an XCD read at one k-step at the same offset in
+    // every row, which bunches them onto few HBM channels.  Such
+    // weight-streaming tiles (one m-tile per expert, all n-tiles of an expert
+    // at once) start their k-range at a tile-dependent weight stage and wrap
+    // around, so concurrent tiles read different offsets (the sum order
+    // changes with the tile, and is the same on every run).
+    const int rq = (Cfg::GM == 1 && nq > 0 && nk == nq * BKS && (w_row_bytes & (w_row_bytes - 1)) == 0)
+                       ? static_cast<int>(tile % nq) : 0;
+    auto qrot = [&](int q) {
+      const int v = q + rq;
+      return v >= nq ? v - nq : v;
+    };
+    auto krot = [&](int kt) { return qrot(kt / BKS) * BKS + kt % BKS; };
     uint32_t a_off[Cfg::A_LD];
 #pragma unroll
     for (int j = 0; j < Cfg::A_LD; ++j) {
@@ -553,13 +567,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       if constexpr (Cfg::WQ) {
         if (s_wide) {
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) sc_nxt[fn] = load_u64(s_rsrc, s_off[fn], (q0 + q) * 8);
+          for (int fn = 0; fn < FN; ++fn) sc_nxt[fn] = load_u64(s_rsrc, s_off[fn], (q0 + qrot(q)) * 8);
         } else if constexpr (!Cfg::F8) {
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-              sc_byte[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p + (lane >> 5), (q0 + q) * 8);
+              sc_byte[fn][p] = load_byte(s_rsrc, s_off[fn] + 2 * p + (lane >> 5), (q0 + qrot(q)) * 8);
         }
       }
     };
@@ -605,13 +619,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
         if (Cfg::EARLY ? part == 0 : j % SUB == part)
-          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + kt) * 128);
+          lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + krot(kt)) * 128);
     };
     auto gload_b = [&](uint16_t* wst, int q, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::B_LD; ++j)
         if (Cfg::EARLY ? part == 0 : (j + Cfg::A_LD) % SUB == part)
-          lds_dma16(b_rsrc, wst + (j * Cfg::NWAVES + wave_u) * 512, b_off[j], (q0 + q) * 128);
+          lds_dma16(b_rsrc, wst + (j * Cfg::NWAVES + wave_u) * 512, b_off[j], (q0 + qrot(q)) * 128);
     };
 
     // Operand fragments of sub-step ks of the k-step at position p of its
