@@ -355,7 +355,9 @@ int moe_permute_batched(const int32_t* topk_ids, const int32_t* expert_map, int6
  *           moe_grouped_gemm_workspace_size(R_pad, I, 1) bytes, calls whose
  *           experts have few rows split the reduction over H into pieces
  *           summed in a fixed order (results are the same on every run);
- *           with less, fewer pieces or none.
+ *           with less, fewer pieces or none.  Calls with many rows use it
+ *           when their tiles leave a last round of a few tiles: those tiles
+ *           are split the same way, so that round fills the GPU.
  * Limits: H and I multiples of 64; R_pad >= offsets[E_l].  MXFP4 weights
  * without scales, or bf16 weights with scales, are MOE_ERR_INVALID_ARGUMENT. */
 int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_l, int64_t R_pad,
@@ -443,8 +445,10 @@ int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t we
 
 /* Scratch bytes with which a grouped GEMM of R_pad permuted rows and N_out
  * output columns (gated != 0: GEMM1, whose weights have 2 N_out rows) may
- * split its reduction as far as it ever does; 0 when it never splits (large
- * R_pad).  Host-only arithmetic.  MOE_ERR_INVALID_ARGUMENT on bad sizes. */
+ * split its reduction as far as it ever does: fp32 slices of all rows for
+ * few-row calls (up to 16 within 64 MiB), or fp32 tiles for the pieces of a
+ * short last round (32 MiB and 1 KiB), whichever is larger.  Host-only
+ * arithmetic.  MOE_ERR_INVALID_ARGUMENT on bad sizes. */
 int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated, size_t* bytes);
 
 /* Finalize (finalize() of page "modular_kernel.py"; MoEOutput of page

@@ -123,6 +123,14 @@ constexpr int kTerm2Shift = 4;
 constexpr int64_t kSplitHeader = 256;
 constexpr int64_t kMaxSplit = 16;
 
+// tail split (tiles of the whole k-range): a header (tail tile count, pieces
+// per tail tile, then row0 / rows / n0 of each tail tile), then one fp32
+// [BM, BN] slab per (tail tile, piece)
+constexpr int kMaxTail = 64;
+constexpr int64_t kTailHeader = 1024;  // >= (2 + 3 * kMaxTail) ints, 256-byte aligned
+constexpr int64_t kTailSlabs = 256;    // slabs of the largest tile the scratch holds
+constexpr int64_t kTailBytes = kTailHeader + kTailSlabs * 128 * 256 * 4;
+
 // Swizzle of the eight 16-byte chunks of a 128-byte tile row: chunk c of row
 // r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), so 16 consecutive rows
 // read at one logical chunk (a 16-lane group of an MFMA operand read) hit 16
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
     int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m,
     const float* __restrict__ A_scales, const int32_t* __restrict__ a_inv, int a_k,
-    int64_t a_T) {
+    int64_t a_T, char* __restrict__ tail_ws, int slab_cap) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
@@ -433,7 +441,29 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     }
   }
   if (split_out != nullptr && blockIdx.x == 0 && tid == 0) split_out[tid] = S;
-  const int total_units = total_tiles * S;
+  // Tail split (tiles of the whole k-range): when the last round of the
+  // persistent grid would hold only a few tiles, each of them is cut along
+  // k into pieces so that round is full; the pieces write fp32 slabs and
+  // tail_reduce_kernel adds them in order.
+  int tail_n = 0, St = 1;
+  if (!Cfg::SPLIT && tail_ws != nullptr) {
+    const int tail = total_tiles % G;
+    if (tail > 0 && tail <= kMaxTail && total_tiles > G) {
+      const int c = min(min(G / tail, static_cast<int>(kMaxSplit)), nq_all);
+      if (c >= 2 && tail * c <= slab_cap) {
+        tail_n = tail;
+        St = c;
+      }
+    }
+  }
+  int* const tail_hdr = reinterpret_cast<int*>(tail_ws);
+  if (tail_ws != nullptr && blockIdx.x == 0 && tid == 0) {
+    tail_hdr[0] = tail_n;
+    tail_hdr[1] = St;
+  }
+  const int head_tiles = total_tiles - tail_n;
+  const int head_units = head_tiles * S;
+  const int total_units = head_units + tail_n * St;
 
   // Load j of this wave fills tile rows [8 rb, 8 rb + 8) (rb = j * NWAVES +
   // wave); lane L writes the 16 bytes at LDS row 8 rb + L / 8, position L % 8,
@@ -443,11 +473,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   const int ld_pos = lane & 7;
 
   for (int unit = slot; unit < total_units; unit += G) {
-    const int tile = unit / S;
-    const int piece = unit - tile * S;
+    const bool in_tail = unit >= head_units;
+    const int tile = in_tail ? head_tiles + (unit - head_units) / St : unit / S;
+    const int piece = in_tail ? (unit - head_units) % St : unit - tile * S;
+    const int S_u = in_tail ? St : S;
     // this piece's weight stages [q0, q0 + nq) and k-steps [kt0, kt0 + nk)
-    const int q0 = piece * nq_all / S;
-    const int nq = (piece + 1) * nq_all / S - q0;
+    const int q0 = piece * nq_all / S_u;
+    const int nq = (piece + 1) * nq_all / S_u - q0;
     const int kt0 = q0 * BKS;
     const int nk = min(nk_all - kt0, nq * BKS);
     // grouped order: GM m-tiles share each n-tile column
@@ -836,6 +868,33 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       if constexpr (Cfg::F8) return A_scales[row0 + r];
       return 1.0f;
     };
+    if (!Cfg::SPLIT && in_tail) {
+      // fp32 sums of this piece into its slab, by virtual weight row (gated:
+      // gate columns [0, BN/2), up columns [BN/2, BN)); piece 0 records the
+      // tile's rows and columns for the reduction
+      const int ti = tile - head_tiles;
+      if (piece == 0 && tid == 0) {
+        tail_hdr[2 + 3 * ti] = row0;
+        tail_hdr[3 + 3 * ti] = min(rows, BM);  // rows of this tile (rows runs to the segment end)
+        tail_hdr[4 + 3 * ti] = n0;
+      }
+      float* slab = reinterpret_cast<float*>(tail_ws + kTailHeader) +
+                    static_cast<int64_t>(ti * St + piece) * (BM * BN);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (Cfg::SKIP && fm >= fm_act) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * Cfg::WTM + fm * 32 + 8 * (i >> 2) + 4 * frag_half + (i & 3);
+          if (r >= rows) continue;
+          const float sa = row_scale(r);
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            slab[r * BN + b_row0<Cfg>(wn, fn) + frag_row] = scaled(acc[fm][fn][i], sa, fn);
+        }
+      }
+      continue;
+    }
     if (Cfg::SPLIT && S > 1) {
       // fp32 sums of this piece into slice `piece` (weight-row columns: gate
       // at n, up at N_out + n)
@@ -958,6 +1017,58 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   *reinterpret_cast<uint2*>(C + r * N_out + n) = o;
 }
 
+// The tail tiles from their slabs: C = sum over pieces s = 0, 1, ... of the
+// slabs (fixed order), or for GEMM1 act(sum of gate) * (sum of up); block
+// (i, y) covers part of tail tile i.  Tiles i >= the header's count exit.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const char* __restrict__ ws, int BM,
+                                                          int BN, int gated, int N_out, int act,
+                                                          float clamp, uint16_t* __restrict__ C) {
+  const int* hdr = reinterpret_cast<const int*>(ws);
+  const int i = blockIdx.x;
+  if (i >= hdr[0]) return;
+  const int St = hdr[1];
+  const int row0 = hdr[2 + 3 * i], rows = hdr[3 + 3 * i], n0 = hdr[4 + 3 * i];
+  const int out_n = gated ? BN / 2 : BN;
+  const int per_row = out_n / 4;
+  const int64_t slab = static_cast<int64_t>(BM) * BN;
+  const float* base = reinterpret_cast<const float*>(ws + kTailHeader) + i * St * slab;
+  const int kind = act_kind(act, clamp);
+  const float cl = act_limit(clamp);
+  for (int idx = blockIdx.y * blockDim.x + threadIdx.x; idx < rows * per_row;
+       idx += gridDim.y * blockDim.x) {
+    const int r = idx / per_row;
+    const int c = (idx - r * per_row) * 4;
+    if (n0 + c >= N_out) continue;
+    const float* p = base + static_cast<int64_t>(r) * BN + c;
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = gated ? *reinterpret_cast<const float4*>(p + out_n) : float4{};
+    for (int sp = 1; sp < St; ++sp) {
+      const float4 x = *reinterpret_cast<const float4*>(p + sp * slab);
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      if (gated) {
+        const float4 u = *reinterpret_cast<const float4*>(p + sp * slab + out_n);
+        b.x += u.x; b.y += u.y; b.z += u.z; b.w += u.w;
+      }
+    }
+    if (gated) {
+      auto f = [&](auto kk) {
+        constexpr int K = decltype(kk)::value;
+        a.x = gated_act_k<K>(a.x, b.x, cl);
+        a.y = gated_act_k<K>(a.y, b.y, cl);
+        a.z = gated_act_k<K>(a.z, b.z, cl);
+        a.w = gated_act_k<K>(a.w, b.w, cl);
+      };
+      if (kind == 0) f(ic<0>{});
+      else if (kind == 1) f(ic<1>{});
+      else f(ic<2>{});
+    }
+    uint2 o;
+    o.x = pack_bf16x2(a.x, a.y);
+    o.y = pack_bf16x2(a.z, a.w);
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row0 + r) * N_out + n0 + c) = o;
+  }
+}
+
 template <class Cfg>
 hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   static int occupancy = 0;
@@ -987,13 +1098,30 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   int* hdr = split ? static_cast<int*>(g.split_ws) : nullptr;
   float* partials =
       split ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kSplitHeader) : nullptr;
+  // tail split (tiles of the whole k-range): slabs of this tile in the scratch
+  const int64_t slab_bytes = int64_t(Cfg::BM) * Cfg::BN * int64_t(sizeof(float));
+  char* tail_ws = nullptr;
+  int slab_cap = 0;
+  if (!Cfg::SPLIT && g.split_ws != nullptr &&
+      int64_t(g.split_ws_bytes) >= kTailHeader + 2 * slab_bytes) {
+    tail_ws = static_cast<char*>(g.split_ws);
+    slab_cap = static_cast<int>(
+        std::min<int64_t>(kMaxTail * kMaxSplit, (int64_t(g.split_ws_bytes) - kTailHeader) / slab_bytes));
+  }
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3(static_cast<unsigned>(grid)),
                      dim3(Cfg::kThreads), 0, s,
                      g.a, g.w, g.w_scales, g.offsets, g.E_l, g.K,
                      g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
-                     g.act, g.clamp, g.batch_m, g.a_scales, g.a_inv, g.a_k, g.a_T);
+                     g.act, g.clamp, g.batch_m, g.a_scales, g.a_inv, g.a_k, g.a_T, tail_ws,
+                     slab_cap);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !split) return e;
+  if (e != hipSuccess) return e;
+  if (tail_ws != nullptr) {
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3(kMaxTail, 8), dim3(256), 0, s, tail_ws, Cfg::BM,
+                       Cfg::BN, g.gated, g.N_out, g.act, g.clamp, static_cast<uint16_t*>(g.c));
+    return hipGetLastError();
+  }
+  if (!split) return e;
   const dim3 rgrid(static_cast<unsigned>((g.N_out / 4 + 255) / 256), static_cast<unsigned>(g.R_pad));
   hipLaunchKernelGGL(split_reduce_kernel, rgrid, dim3(256), 0, s, partials, hdr, g.offsets, g.E_l,
                      g.R_pad, g.N_out, g.gated, g.act, g.clamp, g.batch_m,
@@ -1069,10 +1197,15 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
 
 size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
   constexpr int64_t kBudget = int64_t(64) << 20;
-  if (R_pad <= 0 || R_pad > 65535 || N_total <= 0) return 0;
-  const int64_t slice = R_pad * N_total * int64_t(sizeof(float));
-  const int64_t n = std::min<int64_t>(kMaxSplit, kBudget / slice);
-  return n < 2 ? 0 : static_cast<size_t>(kSplitHeader + n * slice);
+  if (R_pad <= 0 || N_total <= 0) return 0;
+  // split slices (few-row calls), or the tail split's slabs, whichever is larger
+  int64_t split = 0;
+  if (R_pad <= 65535) {
+    const int64_t slice = R_pad * N_total * int64_t(sizeof(float));
+    const int64_t n = std::min<int64_t>(kMaxSplit, kBudget / slice);
+    split = n < 2 ? 0 : kSplitHeader + n * slice;
+  }
+  return static_cast<size_t>(std::max(split, kTailBytes));
 }
 
 // max_rows: the most local routes the call can see (T * k), from the host.

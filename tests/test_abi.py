@@ -279,15 +279,18 @@ def test_fp8_errors(L):
 def test_grouped_gemm_workspace_size():
     L = _lib.lib()
     n = ctypes.c_size_t(0)
-    # decode sizes: fp32 slices of R_pad x N_total, up to 16 within 64 MiB, after a header
+    # the larger of: decode sizes' fp32 slices of R_pad x N_total (up to 16
+    # within 64 MiB, after a 256-byte header), and the tail round's 256 fp32
+    # slabs of a 128 x 256 tile (after a 1 KiB header)
+    tail = 1024 + 256 * 128 * 256 * 4
     assert L.moe_grouped_gemm_workspace_size(128, 2048, 1, ctypes.byref(n)) == 0
-    assert n.value == 256 + 16 * 128 * 4096 * 4
+    assert n.value == max(256 + 16 * 128 * 4096 * 4, tail)
     assert L.moe_grouped_gemm_workspace_size(512, 7168, 0, ctypes.byref(n)) == 0
     assert n.value == 256 + 4 * 512 * 7168 * 4
-    # prefill sizes never split
+    # prefill sizes never split the reduction of every tile: the tail slabs only
     assert L.moe_grouped_gemm_workspace_size(16384, 2048, 1, ctypes.byref(n)) == 0
-    assert n.value == 0
+    assert n.value == tail
     assert L.moe_grouped_gemm_workspace_size(70000, 64, 0, ctypes.byref(n)) == 0
-    assert n.value == 0
+    assert n.value == tail
     assert L.moe_grouped_gemm_workspace_size(128, 100, 0, ctypes.byref(n)) == INVALID
     assert L.moe_grouped_gemm_workspace_size(128, 64, 0, None) == INVALID

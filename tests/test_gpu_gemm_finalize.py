@@ -198,3 +198,51 @@ def test_finalize_in_place_over_shared_and_rsf():
     ref = oracle.finalize(y, host_f64(w_dev), m, 0.5, shared)
     assert out.data_ptr() == s_dev.data_ptr()
     assert rel_fro(host_f64(out), ref) < TOL
+
+
+@pytest.mark.parametrize("mxfp4", [False, True], ids=["bf16", "mxfp4"])
+def test_tail_round_split(mxfp4):
+    """Whole-k tiles (128x256, >= 512 rows per expert) whose count leaves a
+    last round of 32 tiles on a 256-CU part: those tiles are cut along k,
+    summed from fp32 slabs by the reduce kernel (the scratch header records
+    the split).  Both GEMMs against the oracle, bit-identical on a rerun,
+    the same values without the scratch (no split) within rounding."""
+    counts = [2304, 2250]        # 18 m-tiles each: 36 x 8 n-tiles = 288 tiles
+    E_l = len(counts)
+    H, I = (1024, 1024) if mxfp4 else (256, 1024)     # GEMM1: K = H; GEMM2: K = I, N = H
+    H2 = 2048                                         # GEMM2's output width: 8 n-tiles
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R_l = int(offsets[-1])
+    R_pad = ((R_l + 127) // 128) * 128
+    a = synth.normal_bf16(61, 0, (R_pad, H))
+    hb = synth.normal_bf16(61, 7, (R_pad, I))
+    w1 = synth.normal_bf16(61, 2, (E_l, 2 * I, H), std=1 / np.sqrt(H))
+    w2 = synth.normal_bf16(61, 3, (E_l, H2, I), std=1 / np.sqrt(I))
+    if mxfp4:
+        q1, s1 = synth.mxfp4_quantize(w1)
+        q2, s2 = synth.mxfp4_quantize(w2)
+        W1, W2 = moe.Weights(dev(q1), dev(s1)), moe.Weights(dev(q2), dev(s2))
+        O1, O2 = oracle.Weights(q1, s1), oracle.Weights(q2, s2)
+    else:
+        W1, W2 = moe.Weights(dev_bf16(w1)), moe.Weights(dev_bf16(w2))
+        O1, O2 = oracle.Weights(w1), oracle.Weights(w2)
+    off = dev(offsets)
+    ws = torch.empty(moe.moe_grouped_gemm_workspace_size(R_pad, H2, False), dtype=torch.uint8,
+                     device="cuda")
+    ad, hd = dev_bf16(a), dev_bf16(hb)
+    h = moe.moe_grouped_gemm1_act(ad, off, W1, I, workspace=ws)
+    y = moe.moe_grouped_gemm2(hd, off, W2, H2, workspace=ws)
+    hdr = ws[:8].view(torch.int32).cpu().numpy()   # GEMM2's header (the last call)
+    y2 = moe.moe_grouped_gemm2(hd, off, W2, H2, workspace=ws)
+    y_plain = moe.moe_grouped_gemm2(hd, off, W2, H2, split=False)
+    torch.cuda.synchronize()
+    props = torch.cuda.get_device_properties(0)
+    if props.multi_processor_count == 256:
+        assert hdr[0] == 32 and hdr[1] >= 2, hdr
+    assert np.array_equal(host_bf16_bits(y)[:R_l], host_bf16_bits(y2)[:R_l])  # rows past R_l unwritten
+    eor = segments_of(offsets, R_l)
+    ref_h = oracle.hidden_rows(a[:R_l], O1, eor, I)
+    ref_y = oracle.out_rows(hb[:R_l], O2, eor, H2)
+    assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
+    assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
+    assert rel_fro(host_f64(y)[:R_l], host_f64(y_plain)[:R_l]) < 1e-3
