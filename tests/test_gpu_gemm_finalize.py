@@ -246,3 +246,60 @@ def test_tail_round_split(mxfp4):
     assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL
     assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL
     assert rel_fro(host_f64(y)[:R_l], host_f64(y_plain)[:R_l]) < 1e-3
+
+
+@pytest.mark.parametrize("tail", [8, 40, 64])
+@pytest.mark.parametrize("gated", [False, True], ids=["gemm2", "gemm1"])
+def test_tail_split_tiles_against_unsplit(tail, gated):
+    """Tail splits of several sizes on both GEMMs: shapes whose 128x256 tile
+    count is one full round of the persistent grid (one workgroup per CU) plus
+    `tail` tiles.  Every element outside the tail tiles the scratch header
+    records is bit-identical to the call without scratch (no split); the tail
+    tiles agree within fp32 summation-order rounding; sampled rows match the
+    oracle."""
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    n_tiles = 8
+    m_total = (G + tail) // n_tiles
+    if m_total * n_tiles != G + tail:
+        pytest.skip("tail not a multiple of the n-tiles on this part")
+    E_l = 3
+    m_e = [m_total // E_l + (1 if e < m_total % E_l else 0) for e in range(E_l)]
+    counts = [128 * (m - 1) + 1 + (37 * e) % 127 for e, m in enumerate(m_e)]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R_l = int(offsets[-1])
+    R_pad = ((R_l + 127) // 128) * 128
+    K = 512
+    N_out = 128 * n_tiles if gated else 256 * n_tiles
+    a = synth.normal_bf16(90 + tail, 0, (R_pad, K))
+    w = synth.normal_bf16(90 + tail, 2, (E_l, 2 * N_out if gated else N_out, K),
+                          std=1 / np.sqrt(K))
+    W = moe.Weights(dev_bf16(w))
+    off, ad = dev(offsets), dev_bf16(a)
+    ws = torch.empty(moe.moe_grouped_gemm_workspace_size(R_pad, N_out, gated), dtype=torch.uint8,
+                     device="cuda")
+    if gated:
+        c = moe.moe_grouped_gemm1_act(ad, off, W, N_out, workspace=ws)
+        c_plain = moe.moe_grouped_gemm1_act(ad, off, W, N_out, split=False)
+    else:
+        c = moe.moe_grouped_gemm2(ad, off, W, N_out, workspace=ws)
+        c_plain = moe.moe_grouped_gemm2(ad, off, W, N_out, split=False)
+    torch.cuda.synchronize()
+    hdr = ws[:1024].view(torch.int32).cpu().numpy()
+    assert hdr[0] == tail and hdr[1] >= 2, hdr[:2]
+    got, ref = host_bf16_bits(c)[:R_l], host_bf16_bits(c_plain)[:R_l]
+    in_tail = np.zeros((R_l, N_out), dtype=bool)
+    out_n = 128 if gated else 256
+    for i in range(tail):
+        row0, rows, n0 = hdr[2 + 3 * i: 5 + 3 * i]
+        assert 1 <= rows <= 128 and row0 + rows <= R_l and n0 % out_n == 0
+        assert not in_tail[row0:row0 + rows, n0:n0 + out_n].any()   # tail tiles are disjoint
+        in_tail[row0:row0 + rows, n0:n0 + out_n] = True
+    assert np.array_equal(got[~in_tail], ref[~in_tail])
+    assert rel_fro(host_f64(c)[:R_l][in_tail], host_f64(c_plain)[:R_l][in_tail]) < 1e-3
+    rows = np.unique(np.concatenate([np.nonzero(in_tail.any(axis=1))[0][::97], [0, R_l - 1]]))
+    eor = segments_of(offsets, R_l)[rows]
+    if gated:
+        o = oracle.hidden_rows(a[rows], oracle.Weights(w), eor, N_out)
+    else:
+        o = oracle.out_rows(a[rows], oracle.Weights(w), eor, N_out)
+    assert rel_fro(host_f64(c)[rows], o) < TOL
