@@ -64,7 +64,6 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MiB) + MALL (256 MiB)
-GATHER_IN_GEMM_ROUTES = 1024  # passes of at most this many routes: GEMM1 gathers its rows
 
 
 def parse():
@@ -315,9 +314,9 @@ def main():
     w_in = args.router_weight_on_input
 
     counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
-    # decode-sized bf16 passes: GEMM1 reads its rows from x through the
-    # permute's inverse map, as the library's fused calls do (no gather kernel)
-    gathered = (not quant and not Mb and not w_in and P * k <= GATHER_IN_GEMM_ROUTES)
+    # bf16 passes in the standard layout: GEMM1 reads its rows from x through
+    # the permute's inverse map, as the library's fused calls do (no gather kernel)
+    gathered = (not quant and not Mb and not w_in and P * H * 2 <= 0xFFFFFFFF)
     inv_buf = torch.empty((R_pad,), dtype=torch.int32, device=dev) if gathered else None
 
     def permute(sl, st):

@@ -375,10 +375,9 @@ int moe_grouped_gemm1_act(const void* a_perm, const int32_t* offsets, int32_t E_
  *            t*k + j for r < offsets[E_l]; other rows are never read)
  *   offsets, E_l, R_pad, H, I, w1, activation, h, workspace: as for
  *            moe_grouped_gemm1_act (bf16 or MXFP4 weights).
- * The fused calls use it for passes of at most 1024 routes (bf16 activations,
- * standard layout, weights not on the input), where it saves a kernel; for
- * larger passes the separate gather is cheaper than the index load that
- * starts every GEMM tile here. */
+ * The fused calls use it for every pass of bf16 activations in the standard
+ * layout with the weights not on the input (x at most 4 GiB): it saves the
+ * gather kernel and the x_perm write and re-read. */
 int moe_grouped_gemm1_act_gathered(const void* x, const int32_t* inv, int64_t T, int32_t k,
                                    const int32_t* offsets, int32_t E_l, int64_t R_pad, int32_t H,
                                    int32_t I, const moe_weights* w1, int32_t activation,

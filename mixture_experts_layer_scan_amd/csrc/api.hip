@@ -174,9 +174,6 @@ int check_activation(int32_t activation, float clamp) {
   return MOE_OK;
 }
 
-// Passes of at most this many routes let GEMM1 gather its rows itself.
-constexpr int64_t kGatherInGemmRoutes = 1024;
-
 // Options of the fused entry points, checked.
 struct LayerOpts {
   int act = MOE_ACT_SILU;
@@ -816,12 +813,11 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
                                  nullptr, b.xq, b.xs, s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize");
   }
-  // Decode-sized passes of bf16 rows: GEMM1 reads each permuted row straight
-  // from x through the inverse map (no gather kernel, no x_perm round trip);
-  // for larger passes the gather kernel's streaming copy costs less than a
-  // dependent index load at the start of every GEMM1 tile.
+  // bf16 rows in the standard layout: GEMM1 reads each permuted row straight
+  // from x through the inverse map (no gather kernel, no x_perm write and
+  // re-read), while x fits one buffer descriptor's 4 GiB
   const bool gather_in_gemm = !o.fp8 && o.batch_m == 0 && !o.weight_on_input &&
-                              T * k <= kGatherInGemmRoutes;
+                              T * int64_t(H) * 2 <= int64_t(0xFFFFFFFF);
   e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets,
                           gather_in_gemm ? b.inv : nullptr, b.rows, s, o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");

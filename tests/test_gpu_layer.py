@@ -223,11 +223,11 @@ def test_ep_rank_decode_deferred(T):
 
 @pytest.mark.parametrize("T", [1, 7, 128, 129])
 def test_decode_rows_gathered_by_gemm1(T):
-    """Passes of at most 1024 routes let GEMM1 read its rows from x through the
-    inverse map (no gather kernel); larger ones gather first.  Both sides of
-    that switch are bit-identical to the individual calls (which always
-    gather) and match the oracle, with a scattered expert map; the first
-    batch has one token whose routes are all non-local."""
+    """The fused call lets GEMM1 read its rows from x through the inverse map
+    (no gather kernel): bit-identical to the individual calls (which gather
+    first) and equal to the oracle, at decode and wider batches, with a
+    scattered expert map; the first batch has one token whose routes are all
+    non-local."""
     cfg = configs.MoeConfig("gath", T=T, H=1024, I=512, E=64, k=8, score=configs.SIGMOID,
                             renormalize=True, rsf=2.5, seed=70 + T, E_local=16)
     emap = np.full(cfg.E, -1, dtype=np.int32)
