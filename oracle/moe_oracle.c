@@ -8,8 +8,9 @@
  * Plain, slow, obviously correct: per token, per routed expert, a dense
  * SiLU-gated MLP, all in double precision.  Every function names the passage
  * of the pages it follows.  Pages:
- *   [OUT]  vLLM "moe_output.py" (output contract between a MoE layer and a
- *          consumer that fuses its tail): UnfinalizedMoEOutput, MoEOutput.
+ *   [OUT]  vLLM "moe_output.py", module docstring (what a MoE layer returns
+ *          when the code after it finishes the reduction): UnfinalizedMoEOutput,
+ *          MoEOutput.
  *   [MOD]  vLLM "modular_kernel.py" (modular fused-MoE kernel): the stage
  *          comment [Router] -> [Quantize-Dispatch] -> [Permute-Experts-
  *          Unpermute] -> [Combine]; _moe_problem_size; prepare / finalize /
@@ -209,10 +210,14 @@ static double dot_row(const oracle_weights* w, int64_t row, int64_t K, const dou
   if (w->fmt == OR_W_MXFP4) {
     const uint8_t* p = (const uint8_t*)w->data + row * (K / 2);
     const uint8_t* s = (const uint8_t*)w->scales + row * (K / 32);
-    for (int64_t kk = 0; kk < K; ++kk) {
-      uint8_t b = p[kk / 2];
-      uint8_t code = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
-      acc += kE2M1[code] * oracle_e8m0_scale(s[kk / 32]) * v[kk];
+    /* the scale of each 32-element block, decoded once per block */
+    for (int64_t b0 = 0; b0 < K; b0 += 32) {
+      const double sc = oracle_e8m0_scale(s[b0 / 32]);
+      for (int64_t kk = b0; kk < b0 + 32; ++kk) {
+        uint8_t b = p[kk / 2];
+        uint8_t code = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+        acc += kE2M1[code] * sc * v[kk];
+      }
     }
   } else if (w->fmt == OR_W_FP8) {
     /* the 256 decoded values, each from oracle_e4m3_decode */
@@ -511,9 +516,9 @@ void oracle_finalize(const uint16_t* y_perm, const double* w, const int32_t* map
   }
 }
 
-/* ---- Fused tail on one GPU ([OUT] MoEOutput: the consumer of the layer's
- * open reduction is typically the next layer's RMSNorm, which folds the top-k
- * reduction, the routed scaling factor and the shared add into itself) -------
+/* ---- Fused tail on one GPU ([OUT] MoEOutput docstring: the layer may leave
+ * the top-k sum, the routed scaling factor and the shared add for the code
+ * that follows it, usually the next layer's normalization, to carry out) -----
  * For each token t, with m[t] the finalize output above:
  *   residual_out[t] = residual[t] + m[t]
  *   out[t, n] = residual_out[t, n] / sqrt(mean_n residual_out[t, n]^2 + eps)
