@@ -421,8 +421,9 @@ int moe_grouped_gemm2_batched(const void* h_batched, const int32_t* expert_num_t
                               size_t workspace_bytes, void* stream);
 
 /* Fused tail on one GPU: finalize, the shared-expert add, the residual add
- * and the next layer's RMSNorm in one pass (page "moe_output.py", MoEOutput:
- * the consumer of the open reduction is typically the next layer's RMSNorm).
+ * and the next layer's RMSNorm in one pass (page "moe_output.py", MoEOutput
+ * docstring: the code after the layer, usually the next layer's
+ * normalization, may finish the layer's open reduction).
  * For every token t, with z the fp32 sum
  *   z[t, :] = rsf_fin * sum_{j: map>=0} w[t,j] * y_perm[map[t,j], :]
  *             + shared[t, :] + residual[t, :]
@@ -465,7 +466,9 @@ int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated,
  *   map      (device) int32 [T, k]
  *   shared   (device) bf16 [T, H] or NULL
  *   out      (device) bf16 [T, H] out; may alias shared exactly (in place),
- *            must not overlap y_perm
+ *            must not overlap any row of y_perm the map names (checked for
+ *            rows [0, T*k), which hold every named row in the standard
+ *            layout; the map itself is device memory the host does not read)
  * Limits: H a multiple of 8, k <= 32. */
 int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
                  const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,

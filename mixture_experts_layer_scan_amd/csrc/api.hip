@@ -698,6 +698,10 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
   const size_t out_bytes = sizeof(uint16_t) * T * H;
   if (shared && shared != out && overlap(shared, out_bytes, out, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out must alias shared exactly or not overlap it");
+  // The map lives on the device, so the host cannot see the largest row it
+  // names: rows [0, T * k) bound it in the standard layout; in the batched
+  // experts format (rows up to E_l * max_tokens) the caller keeps out apart
+  // from the whole buffer, and the Python binding checks the tensor's extent.
   if (overlap(y_perm, sizeof(uint16_t) * T * k * H, out, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap gemm2_permuted");
   hipError_t e = moe::launch_finalize(y_perm, weights, weights_dtype == MOE_DTYPE_BF16, map, T, k, H,
@@ -925,8 +929,17 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
   MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
-  MOE_CHECK(check_workspace(workspace, workspace_bytes,
-                            routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms)));
+  const size_t need = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
+  // the workspace is apart from the input rows and from the three outputs
+  if (overlap(workspace, need, x, sizeof(uint16_t) * T * H) ||
+      overlap(workspace, need, gemm2_permuted, sizeof(uint16_t) * R_pad * H) ||
+      overlap(workspace, need, expert_weights, sizeof(uint16_t) * T * k) ||
+      overlap(workspace, need, map, sizeof(int32_t) * T * k))
+    return fail(MOE_ERR_DESTINATION_CONFLICT,
+                "the workspace must not overlap x, gemm2_permuted, expert_weights or map");
+  if (overlap(gemm2_permuted, sizeof(uint16_t) * R_pad * H, x, sizeof(uint16_t) * T * H))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "gemm2_permuted must not overlap x");
   Carve c{static_cast<char*>(workspace)};
   const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,

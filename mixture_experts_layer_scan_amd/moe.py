@@ -654,6 +654,11 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: Optional[torch.Te
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
+    # every row the map may name (the batched layout's reach past T * k rows)
+    y0, y1 = gemm2_permuted.data_ptr(), gemm2_permuted.data_ptr() + gemm2_permuted.nbytes
+    o0, o1 = out.data_ptr(), out.data_ptr() + out.nbytes
+    if T > 0 and o0 < y1 and y0 < o1:
+        raise ValueError("out must not overlap gemm2_permuted")
     _check(lib().moe_finalize(gemm2_permuted.data_ptr(), w_ptr, wdt,
                               map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
                               out.data_ptr(), _stream(stream)), "moe_finalize")
