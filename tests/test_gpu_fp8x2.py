@@ -24,8 +24,9 @@ import oracle
 import synth
 from synth import configs
 
-from gpu_util import (dev, dev_bf16, host_bf16_bits, host_f64, need_gpu, rel_fro,
-                      sample_tokens, segments_of)
+from gpu_util import (covering_tokens, dev, dev_bf16, host_bf16_bits, host_f64, need_gpu,
+                      per_row_rel, rel_fro, sample_tokens, segments_of,
+                      expert_sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,8 +141,8 @@ def test_x2_gemms(case, split):
     eor = segments_of(offsets, R_l)
     ref_h = oracle.hidden_rows_fp8x2(a1[:R_l], a2[:R_l], asc[:R_l], oracle.Weights(q1, s1), eor, I)
     ref_y = oracle.out_rows_fp8x2(h1[:R_l], h2[:R_l], hsc[:R_l], oracle.Weights(q2, s2), eor, H)
-    assert rel_fro(host_f64(h)[:R_l], ref_h) < TOL_SAME
-    assert rel_fro(host_f64(y)[:R_l], ref_y) < TOL_SAME
+    assert rel_fro(host_f64(h, slice(None, R_l)), ref_h) < TOL_SAME
+    assert rel_fro(host_f64(y, slice(None, R_l)), ref_y) < TOL_SAME
 
 
 def _upload(w):
@@ -174,7 +175,7 @@ def test_x2_layer_fused_and_deferred(chunk):
     assert rel_fro(host_f64(fin), ref["out"]) < TOL_SAME
     assert rel_fro(host_f64(out), plain["out"]) < TOL_MXFP4
     mm = m.cpu().numpy()
-    assert rel_fro(host_f64(y)[mm.reshape(-1)], ref["y_routes"].reshape(-1, cfg.H)) < TOL_SAME
+    assert rel_fro(host_f64(y, mm.reshape(-1)), ref["y_routes"].reshape(-1, cfg.H)) < TOL_SAME
 
 
 @pytest.mark.parametrize("T", [1, 8, 64])
@@ -217,10 +218,47 @@ def test_x2_full_size_deepseek_mxfp4():
                                 fp8="x2")
     out2 = moe.moe_fused_experts(ld, xd, W1, W2, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
                                  fp8="x2")
+    # the stages one by one, as the benchmark times them
+    k, H, I, E_l = cfg.k, cfg.H, cfg.I, cfg.El
+    ids_d, wts_d = moe.moe_route_topk(ld, k, cfg.score, cfg.renormalize, cfg.rsf)
+    xq, xs = moe.moe_quantize_fp8x2(xd)
+    p = moe.moe_permute_fp8(ids_d, cfg.E, xq, xs)
+    h = moe.moe_grouped_gemm1_act_fp8x2(p["xq_perm"], p["xq_perm_scales"], p["offsets"], W1, I)
+    hq, hs = moe.moe_quantize_fp8x2(h, None, row_count=p["offsets"][E_l:])
+    y = moe.moe_grouped_gemm2_fp8x2(hq, hs, p["offsets"], W2, H)
+    out_s = moe.moe_finalize(y, wts_d, p["map"])
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(out), host_bf16_bits(out2))
-    toks = sample_tokens(cfg.T, 12, 10)
-    got = host_f64(out)[toks]
+    assert np.array_equal(host_bf16_bits(out), host_bf16_bits(out_s))
+    # h and Y rows of every expert against the oracle's row functions on the
+    # kernels' own codes (the codes themselves are pinned bit for bit above)
+    off = p["offsets"].cpu().numpy()
+    R_l = int(off[-1])
+    rows = expert_sample_rows(off, 2, 11)
+    eor = segments_of(off, R_l)[rows]
+    W1o, W2o = oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    a1, a2 = _split_terms(p["xq_perm"].cpu().numpy()[rows])
+    ref_h = oracle.hidden_rows_fp8x2(a1, a2, p["xq_perm_scales"].cpu().numpy()[rows], W1o, eor, I)
+    e_h = per_row_rel(host_f64(h, rows), ref_h)
+    b1, b2 = _split_terms(hq.cpu().numpy()[rows])
+    ref_y = oracle.out_rows_fp8x2(b1, b2, hs.cpu().numpy()[rows], W2o, eor, H)
+    e_y = per_row_rel(host_f64(y, rows), ref_y)
+    print(f"\n{cfg.name}: {len(rows)} h rows of {len(np.unique(eor))} experts, max {e_h.max():.2e}; "
+          f"Y rows max {e_y.max():.2e}")
+    assert len(np.unique(eor)) == E_l
+    assert e_h.max() < TOL_SAME and e_y.max() < TOL_SAME
+    # tokens whose routes reach every expert, per token and pooled, against the
+    # oracle on the same two-term codes and against the bf16-activation layer
+    ids, _ = oracle.route(logits, cfg.k, cfg.score, cfg.renormalize, cfg.rsf)
+    toks = covering_tokens(ids, 256, 10)
+    got = host_f64(out, toks)
     assert np.all(np.isfinite(got))
-    assert rel_fro(got, _ref(cfg, x, logits, w, tokens=toks)["out"]) < TOL_SAME
-    assert rel_fro(got, _ref(cfg, x, logits, w, fp8=False, tokens=toks)["out"]) < TOL_MXFP4
+    same = _ref(cfg, x, logits, w, tokens=toks)["out"]
+    plain = _ref(cfg, x, logits, w, fp8=False, tokens=toks)["out"]
+    e_same, e_plain = per_row_rel(got, same), per_row_rel(got, plain)
+    print(f"\n{cfg.name}: {len(toks)} tokens reaching {len(np.unique(ids[toks]))} experts; "
+          f"same codes per-token max {e_same.max():.2e} pooled {rel_fro(got, same):.2e}; "
+          f"bf16 activations per-token max {e_plain.max():.2e} pooled {rel_fro(got, plain):.2e}")
+    assert len(np.unique(ids[toks])) == cfg.E
+    assert e_same.max() < TOL_SAME and rel_fro(got, same) < TOL_SAME
+    assert e_plain.max() < TOL_MXFP4 and rel_fro(got, plain) < TOL_MXFP4
