@@ -521,6 +521,8 @@ def main():
         ms_per_step = float(np.mean([sum(p.values()) for p in per_step]))
     else:
         ms_per_step = elapsed / args.steps * 1e3
+    # per-step spread from the events (graph replay: one event pair per step)
+    step_ms = np.array([sum(p.values()) for p in per_step])
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
     g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
     # (two-term rows run the fp8 MFMA twice: the bf16 peak is their rate)
@@ -553,6 +555,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_min": float(np.min(step_ms)),
+        "ms_per_step_max": float(np.max(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
