@@ -494,6 +494,34 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
                                   void* gemm2_permuted, void* expert_weights, int32_t* map,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device memory moe_fused_experts_unfinalized_noalloc uses as its
+ * scratch: a static array the library holds on every device it runs on,
+ * from the library's first use there until the process ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* The deferred form without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Arguments, results and errors are those of
+ * moe_fused_experts_unfinalized (less the workspace), except:
+ *   - the scratch is the library's static array of MOE_NOALLOC_SCRATCH_BYTES
+ *     on the current device; the call allocates and frees nothing;
+ *   - a problem whose scratch, not counting the GEMMs' split-reduction
+ *     partials, exceeds that size fails with MOE_ERR_SIZE_MISMATCH (for the
+ *     DeepSeek-V3 rank shape, H 7168, I 2048, top_k 8, that is about 3000
+ *     tokens); the partials get what is left, so a call may split its GEMMs
+ *     into fewer pieces than the workspace form and differ from it in the
+ *     last bits (it gives the same bits on every run);
+ *   - all calls on one device share the one array: calls that may run at the
+ *     same time on one device (other streams, other threads) race.  Each
+ *     call writes every scratch byte it reads; none must start at zero. */
+int moe_fused_experts_unfinalized_noalloc(const float* logits, const void* x, int64_t T,
+                                          int32_t H, int32_t I, int32_t E, int32_t E_l, int32_t k,
+                                          int32_t score_fn, int32_t renormalize, float rsf,
+                                          const int32_t* expert_map, const moe_weights* w1,
+                                          const moe_weights* w2, const moe_layer_options* options,
+                                          int64_t R_pad, void* gemm2_permuted,
+                                          void* expert_weights, int32_t* map, void* stream);
+
 /* The whole layer, finalized:
  *   out = rsf_fin * sum_j w_j * MLP_{L_j}(x) + shared MLP(x)
  * (with apply_router_weight_on_input: rsf_fin * sum_j MLP_{L_j}(w_j x) + ...)

@@ -6,6 +6,7 @@ The compute lives in the HIP library ``libmoe_mi355x.so`` (C ABI in
 from .moe import (ACT_GELU, ACT_SILU, DTYPE_BF16, DTYPE_F32, DTYPE_FP8_E4M3, DTYPE_MXFP4,
                   QUANT_FP8, QUANT_FP8X2, QUANT_NONE, SIGMOID, SOFTMAX, MoeError, Weights, moe_finalize,
                   moe_finalize_add_rmsnorm, moe_fused_experts, moe_fused_experts_unfinalized,
+                  moe_fused_experts_unfinalized_noalloc,
                   moe_grouped_gemm1_act, moe_grouped_gemm1_act_batched,
                   moe_grouped_gemm1_act_gathered,
                   moe_grouped_gemm1_act_fp8, moe_grouped_gemm1_act_fp8x2, moe_grouped_gemm2,
@@ -18,6 +19,7 @@ __all__ = [
     "ACT_GELU", "ACT_SILU", "DTYPE_BF16", "DTYPE_F32", "DTYPE_FP8_E4M3", "DTYPE_MXFP4",
     "QUANT_FP8", "QUANT_FP8X2", "QUANT_NONE", "SIGMOID", "SOFTMAX", "MoeError", "Weights", "moe_finalize",
     "moe_finalize_add_rmsnorm", "moe_fused_experts", "moe_fused_experts_unfinalized",
+    "moe_fused_experts_unfinalized_noalloc",
     "moe_grouped_gemm1_act", "moe_grouped_gemm1_act_batched",
     "moe_grouped_gemm1_act_gathered", "moe_grouped_gemm1_act_fp8",
     "moe_grouped_gemm1_act_fp8x2", "moe_grouped_gemm2", "moe_grouped_gemm2_batched", "moe_grouped_gemm2_fp8",

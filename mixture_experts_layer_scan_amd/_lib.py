@@ -71,6 +71,10 @@ PROTOTYPES = {
     "moe_fused_experts_unfinalized": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
                                                      _i32, _i32, _f32, _vp, _Wp, _Wp, _Op, _i64,
                                                      _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_fused_experts_unfinalized_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32,
+                                                             _i32, _i32, _i32, _i32, _f32, _vp,
+                                                             _Wp, _Wp, _Op, _i64, _vp, _vp, _vp,
+                                                             _vp]),
     "moe_fused_experts": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _f32, _vp, _Wp, _Wp, _i32, _vp, _vp, _f32, _Op, _vp, _vp,
                                          _sz, _vp]),

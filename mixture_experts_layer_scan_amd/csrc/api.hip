@@ -5,6 +5,7 @@
 // (num_tokens >= 0, top_k > 0, int32 map, T * k elements, one device,
 // contiguous buffers, no destination for a deferred output).
 #include <algorithm>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -256,6 +257,42 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, 
     b += align_up(sizeof(float) * R_pad);               // their scales
   }
   return b;
+}
+
+// ---- static scratch of moe_fused_experts_unfinalized_noalloc ---------------
+// Device memory the library holds on every device it runs on, for callers
+// that cannot allocate.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per device
+// (each device has its own copy), and only that address is handed to kernels.
+constexpr size_t kNoallocScratchBytes = size_t(MOE_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (its device address).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_DEVICE, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) % kAlign))
+      return fail(MOE_ERR_HIP, "static scratch has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -770,7 +807,8 @@ struct RoutedWs {
 };
 
 static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I,
-                             int batch_m, bool fp8 = false, int terms = 1) {
+                             int batch_m, bool fp8 = false, int terms = 1,
+                             size_t split_cap = ~size_t(0)) {
   RoutedWs b;
   b.rows = routed_rows(T, k, E_l, batch_m);
   b.ids = c.take<int32_t>(T * k);
@@ -780,7 +818,8 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   b.inv = c.take<int32_t>(b.rows);
   b.x_perm = c.take<uint16_t>(b.rows * H);
   b.h = c.take<uint16_t>(b.rows * I);
-  b.split_bytes = routed_split_bytes(b.rows, H, I);
+  // (a smaller split scratch only lowers the number of pieces the GEMMs use)
+  b.split_bytes = std::min(routed_split_bytes(b.rows, H, I), split_cap);
   b.split = b.split_bytes ? c.take<char>(b.split_bytes) : nullptr;
   if (fp8) {
     // (two-term quantized permuted rows, 2H bytes each, fill x_perm's slot)
@@ -906,31 +945,15 @@ static int check_workspace(void* workspace, size_t have, size_t need) {
   return MOE_OK;
 }
 
-int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
-                                  int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
-                                  int32_t renormalize, float rsf, const int32_t* expert_map,
-                                  const moe_weights* w1, const moe_weights* w2,
-                                  const moe_layer_options* options, int64_t R_pad,
-                                  void* gemm2_permuted, void* expert_weights, int32_t* map,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  LayerOpts o;
-  MOE_CHECK(parse_options(options, k, &o));
-  if (o.chunk > 0 && o.chunk < T)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "the deferred form takes no chunking (chunk_tokens < T)");
-  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, T, o));
-  if (o.batch_m > 0) {
-    if (R_pad < int64_t(E_l) * o.batch_m)
-      return fail(MOE_ERR_SIZE_MISMATCH, "R_pad must hold E_l * batched_max_tokens rows");
-  } else {
-    MOE_CHECK(check_rpad(T, k, R_pad));
-  }
-  if (T == 0) return MOE_OK;
-  MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
-  MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
-  MOE_CHECK(need_ptr(map, "map"));
-  const size_t need = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
-  MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
+// The deferred form on a given scratch: split_cap bounds the GEMMs' split
+// scratch (the rest of the workspace is needed in full).
+static int unfinalized_on(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                          int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                          int32_t renormalize, float rsf, const int32_t* expert_map,
+                          const moe_weights* w1, const moe_weights* w2, const LayerOpts& o,
+                          int64_t R_pad, void* gemm2_permuted, void* expert_weights,
+                          int32_t* map, void* workspace, size_t need, size_t split_cap,
+                          hipStream_t stream) {
   // the workspace is apart from the input rows and from the three outputs
   if (overlap(workspace, need, x, sizeof(uint16_t) * T * H) ||
       overlap(workspace, need, gemm2_permuted, sizeof(uint16_t) * R_pad * H) ||
@@ -941,10 +964,80 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   if (overlap(gemm2_permuted, sizeof(uint16_t) * R_pad * H, x, sizeof(uint16_t) * T * H))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "gemm2_permuted must not overlap x");
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms, split_cap);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
-                    o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights),
-                    static_cast<hipStream_t>(stream));
+                    o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights), stream);
+}
+
+// Argument checks of the deferred form (everything but the workspace).
+static int check_unfinalized(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                             const int32_t* expert_map, const moe_weights* w1,
+                             const moe_weights* w2, const moe_layer_options* options,
+                             int64_t R_pad, void* gemm2_permuted, void* expert_weights,
+                             int32_t* map, LayerOpts* o) {
+  MOE_CHECK(parse_options(options, k, o));
+  if (o->chunk > 0 && o->chunk < T)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "the deferred form takes no chunking (chunk_tokens < T)");
+  MOE_CHECK(check_fused_args(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, T, *o));
+  if (o->batch_m > 0) {
+    if (R_pad < int64_t(E_l) * o->batch_m)
+      return fail(MOE_ERR_SIZE_MISMATCH, "R_pad must hold E_l * batched_max_tokens rows");
+  } else {
+    MOE_CHECK(check_rpad(T, k, R_pad));
+  }
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(gemm2_permuted, "gemm2_permuted"));
+  MOE_CHECK(need_ptr(expert_weights, "expert_weights"));
+  return need_ptr(map, "map");
+}
+
+int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T, int32_t H,
+                                  int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                                  int32_t renormalize, float rsf, const int32_t* expert_map,
+                                  const moe_weights* w1, const moe_weights* w2,
+                                  const moe_layer_options* options, int64_t R_pad,
+                                  void* gemm2_permuted, void* expert_weights, int32_t* map,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  LayerOpts o;
+  MOE_CHECK(check_unfinalized(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, options,
+                              R_pad, gemm2_permuted, expert_weights, map, &o));
+  if (T == 0) return MOE_OK;
+  const size_t need = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
+  return unfinalized_on(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1,
+                        w2, o, R_pad, gemm2_permuted, expert_weights, map, workspace, need,
+                        ~size_t(0), static_cast<hipStream_t>(stream));
+}
+
+int moe_fused_experts_unfinalized_noalloc(const float* logits, const void* x, int64_t T,
+                                          int32_t H, int32_t I, int32_t E, int32_t E_l, int32_t k,
+                                          int32_t score_fn, int32_t renormalize, float rsf,
+                                          const int32_t* expert_map, const moe_weights* w1,
+                                          const moe_weights* w2, const moe_layer_options* options,
+                                          int64_t R_pad, void* gemm2_permuted,
+                                          void* expert_weights, int32_t* map, void* stream) {
+  g_err[0] = 0;
+  LayerOpts o;
+  MOE_CHECK(check_unfinalized(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, options,
+                              R_pad, gemm2_permuted, expert_weights, map, &o));
+  if (T == 0) return MOE_OK;
+  // everything but the GEMMs' split scratch must fit; the split scratch takes
+  // what is left (fewer split pieces, or none, when little is)
+  const int64_t rows = routed_rows(T, k, E_l, o.batch_m);
+  const size_t full = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  const size_t base = full - align_up(routed_split_bytes(rows, H, I));
+  if (base > kNoallocScratchBytes)
+    return fail(MOE_ERR_SIZE_MISMATCH,
+                "problem needs %zu bytes of scratch, more than the %zu-byte static scratch",
+                base, size_t(kNoallocScratchBytes));
+  const size_t split_cap = (kNoallocScratchBytes - base) / kAlign * kAlign;
+  void* ws = nullptr;
+  MOE_CHECK(noalloc_scratch(&ws));
+  return unfinalized_on(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1,
+                        w2, o, R_pad, gemm2_permuted, expert_weights, map, ws,
+                        kNoallocScratchBytes, split_cap, static_cast<hipStream_t>(stream));
 }
 
 int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, int32_t I,

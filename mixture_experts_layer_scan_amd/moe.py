@@ -755,6 +755,53 @@ def moe_fused_experts_unfinalized(logits: torch.Tensor, x: torch.Tensor, w1: Wei
     return gemm2_permuted, expert_weights, map
 
 
+def moe_fused_experts_unfinalized_noalloc(logits: torch.Tensor, x: torch.Tensor, w1: Weights,
+                                          w2: Weights, k: int, score_fn: int = SOFTMAX,
+                                          renormalize: bool = True, rsf: float = 1.0,
+                                          expert_map: Optional[torch.Tensor] = None,
+                                          R_pad: Optional[int] = None,
+                                          gemm2_permuted: Optional[torch.Tensor] = None,
+                                          expert_weights: Optional[torch.Tensor] = None,
+                                          map: Optional[torch.Tensor] = None, stream=None,
+                                          activation=ACT_SILU,
+                                          activation_clamp: Optional[float] = None,
+                                          apply_router_weight_on_input: bool = False,
+                                          batched_max_tokens: int = 0, fp8=False,
+                                          a1_scale: Optional[torch.Tensor] = None,
+                                          a2_scale: Optional[torch.Tensor] = None):
+    """moe_fused_experts_unfinalized on the library's static device scratch (no
+    workspace): the library allocates nothing.  Outputs the caller does not
+    pass are allocated here by torch; pass all three to allocate nothing at
+    all.  -> (gemm2_permuted, expert_weights, map)."""
+    _need(logits, "logits", torch.float32)
+    _need(x, "x", torch.bfloat16, device=logits.device)
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w2.K
+    dev = x.device
+    if R_pad is None:
+        R_pad = w1.E_l * batched_max_tokens if batched_max_tokens else moe_permuted_rows(T, k)
+    if gemm2_permuted is None:
+        gemm2_permuted = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    if expert_weights is None:
+        expert_weights = torch.empty((T, k), dtype=torch.bfloat16, device=dev)
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16, (R_pad, H), dev)
+    _need(expert_weights, "expert_weights", torch.bfloat16, (T, k), dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    _check(lib().moe_fused_experts_unfinalized_noalloc(
+        logits.data_ptr(), x.data_ptr(), T, H, I, E, w1.E_l, k, score_fn, int(bool(renormalize)),
+        float(rsf), _ptr(expert_map), w1.ref(), w2.ref(),
+        _options(activation, activation_clamp, apply_router_weight_on_input, 0,
+                 batched_max_tokens, fp8, a1_scale, a2_scale), R_pad,
+        gemm2_permuted.data_ptr(), expert_weights.data_ptr(), map.data_ptr(), _stream(stream)),
+        "moe_fused_experts_unfinalized_noalloc")
+    return gemm2_permuted, expert_weights, map
+
+
 def moe_fused_experts(logits: torch.Tensor, x: torch.Tensor, w1: Weights, w2: Weights, k: int,
                       score_fn: int = SOFTMAX, renormalize: bool = True, rsf: float = 1.0,
                       expert_map: Optional[torch.Tensor] = None,

@@ -294,3 +294,22 @@ def test_grouped_gemm_workspace_size():
     assert n.value == tail
     assert L.moe_grouped_gemm_workspace_size(128, 100, 0, ctypes.byref(n)) == INVALID
     assert L.moe_grouped_gemm_workspace_size(128, 64, 0, None) == INVALID
+
+
+def test_noalloc_host_checks(L):
+    """The entry point on the static scratch checks on the host: a problem
+    whose scratch exceeds the static array is rejected before any HIP call."""
+    u = L.moe_fused_experts_unfinalized_noalloc
+    args = dict(logits=P, x=P, T=8192, H=7168, I=2048, E=8, El=8, k=8, score=1, renorm=1,
+                rsf=1.0, emap=None, w1=_w(), w2=_w(), opts=None, R_pad=65536, y=P, w=P, m=P,
+                s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return u(*a.values())
+    assert call() == SIZE
+    assert b"static scratch" in L.moe_last_error()
+    assert call(T=-1) == INVALID
+    assert call(R_pad=100) == SIZE           # R_pad < T * k
+    assert call(T=0, R_pad=0) == OK
+    assert call(w1=_w(7, P, P)) == UNSUPPORTED
