@@ -21,7 +21,8 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 SOFTMAX, SIGMOID = 0, 1
-W_BF16, W_MXFP4, W_FP8 = 0, 1, 2
+W_BF16, W_MXFP4, W_FP8, W_FP8_BLOCK = 0, 1, 2, 3
+BLOCK = 128  # rows and columns of a weight block, elements of an activation group
 ACTIVATIONS = {"silu": 0, "gelu": 1}
 
 
@@ -72,9 +73,11 @@ def _load():
         L.oracle_quantize_fp8x2_rows.restype = None
         L.oracle_quantize_fp8x2_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         L.oracle_hidden_rows_fp8.restype = None
-        L.oracle_hidden_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
+        L.oracle_hidden_rows_fp8.argtypes = [vp, vp, i64, i64, i64, i64, Wp, vp, i32, dbl, vp]
         L.oracle_out_rows_fp8.restype = None
-        L.oracle_out_rows_fp8.argtypes = [vp, vp, i64, i64, i64, Wp, vp, vp]
+        L.oracle_out_rows_fp8.argtypes = [vp, vp, i64, i64, i64, i64, Wp, vp, vp]
+        L.oracle_quantize_fp8_groups.restype = None
+        L.oracle_quantize_fp8_groups.argtypes = [vp, i64, i64, i64, vp, vp]
         L.oracle_hidden_rows_fp8x2.restype = None
         L.oracle_hidden_rows_fp8x2.argtypes = [vp, vp, vp, i64, i64, i64, Wp, vp, i32, dbl, vp]
         L.oracle_out_rows_fp8x2.restype = None
@@ -111,14 +114,25 @@ def _p(a: Optional[np.ndarray]):
 
 class Weights:
     """Expert weights in bf16 bits ([rows, K] uint16), MXFP4 (packed uint8
-    [rows, K/2] + E8M0 uint8 [rows, K/32]) or FP8 E4M3 (uint8 [rows, K] + one
-    float32 scale per row).  Keeps the arrays alive."""
+    [rows, K/2] + E8M0 uint8 [rows, K/32]), FP8 E4M3 (uint8 [rows, K] + one
+    float32 scale per row) or, with block=True, block-scaled FP8 E4M3 (uint8
+    [rows, K] + float32 [rows/128, K/128], one scale per 128 x 128 block).
+    Keeps the arrays alive."""
 
-    def __init__(self, data: np.ndarray, scales: Optional[np.ndarray] = None):
+    def __init__(self, data: np.ndarray, scales: Optional[np.ndarray] = None,
+                 block: bool = False):
         if scales is None:
             self.data = _c(data, np.uint16)
             self.scales = None
             self.fmt = W_BF16
+        elif block:
+            self.data = _c(data, np.uint8)
+            self.scales = _c(scales, np.float32)
+            K = self.data.shape[-1]
+            rows = self.data.size // K
+            if rows % BLOCK or K % BLOCK or self.scales.size != (rows // BLOCK) * (K // BLOCK):
+                raise ValueError("block FP8 weights need [rows/128, K/128] scales")
+            self.fmt = W_FP8_BLOCK
         elif scales.dtype == np.float32:
             self.data = _c(data, np.uint8)
             self.scales = _c(scales, np.float32)
@@ -234,28 +248,54 @@ def quantize_fp8x2_rows(x_bf16: np.ndarray):
     return q1, q2, sc
 
 
+def _group(codes: np.ndarray, scales: np.ndarray) -> int:
+    """Elements per scale of FP8 rows: one scale per row ([rows] scales) or per
+    group of 128 ([rows, K/128] scales)."""
+    rows, K = codes.shape
+    if scales.size == rows:
+        return K
+    if scales.size == rows * (K // BLOCK) and K % BLOCK == 0:
+        return BLOCK
+    raise ValueError("scales must be [rows] or [rows, K/128]")
+
+
+def quantize_fp8_groups(x_bf16: np.ndarray, group: int = BLOCK):
+    """Block-scaled FP8 E4M3 quantization of bf16 rows, one scale per `group`
+    consecutive elements -> (codes uint8 [rows, H], scales float32 [rows, H/group])."""
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    if H % group:
+        raise ValueError("H must be a multiple of the group")
+    q = np.empty((rows, H), dtype=np.uint8)
+    sc = np.empty((rows, H // group), dtype=np.float32)
+    _load().oracle_quantize_fp8_groups(_p(x), rows, H, group, _p(q), _p(sc))
+    return q, sc
+
+
 def hidden_rows_fp8(aq: np.ndarray, a_scales: np.ndarray, w1: Weights, expert_of_row: np.ndarray,
                     I: int, activation: str = "silu", clamp: float = 0.0) -> np.ndarray:
-    """hidden_rows on FP8 rows (decoded as code * row scale), float64 [rows, I]."""
+    """hidden_rows on FP8 rows (decoded as code * the scale of its row, or of its
+    group of 128 with [rows, H/128] scales), float64 [rows, I]."""
     aq = _c(aq, np.uint8)
     sc = _c(a_scales, np.float32)
     eor = _c(expert_of_row.astype(np.int32), np.int32)
     rows, H = aq.shape
     h = np.empty((rows, I), dtype=np.float64)
-    _load().oracle_hidden_rows_fp8(_p(aq), _p(sc), rows, H, I, w1.ref, _p(eor),
+    _load().oracle_hidden_rows_fp8(_p(aq), _p(sc), _group(aq, sc), rows, H, I, w1.ref, _p(eor),
                                    ACTIVATIONS[activation], float(clamp), _p(h))
     return h
 
 
 def out_rows_fp8(hq: np.ndarray, h_scales: np.ndarray, w2: Weights, expert_of_row: np.ndarray,
                  H: int) -> np.ndarray:
-    """out_rows on FP8 rows, float64 [rows, H]."""
+    """out_rows on FP8 rows (per-row or per-128-group scales), float64 [rows, H]."""
     hq = _c(hq, np.uint8)
     sc = _c(h_scales, np.float32)
     eor = _c(expert_of_row.astype(np.int32), np.int32)
     rows, I = hq.shape
     y = np.empty((rows, H), dtype=np.float64)
-    _load().oracle_out_rows_fp8(_p(hq), _p(sc), rows, I, H, w2.ref, _p(eor), _p(y))
+    _load().oracle_out_rows_fp8(_p(hq), _p(sc), _group(hq, sc), rows, I, H, w2.ref, _p(eor),
+                                _p(y))
     return y
 
 
@@ -356,7 +396,8 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
     MLP instead of the MLP's output (top_k = 1).  fp8: the routed experts see
     their input and hidden rows quantized per row to FP8 E4M3 (static
     a1_scale / a2_scale when given); fp8 "x2": quantized to two FP8 terms
-    (quantize_fp8x2_rows).
+    (quantize_fp8x2_rows); fp8 "block": quantized per group of 128 elements
+    (quantize_fp8_groups), for block-scaled FP8 weights.
 
     Returns dict: out float64 [n, H], y_routes float64 [n, k, H] (unweighted
     per-route expert outputs, zero when not local), ids int32 [n, k],
@@ -380,7 +421,9 @@ def moe_tokens(x_bf16: np.ndarray, logits: np.ndarray, w1: Weights, w2: Weights,
     _load().oracle_moe_tokens(_p(x), H, I, _p(logits), E, k, score, int(bool(renormalize)), rsf,
                               _p(expert_map), w1.ref, w2.ref, shared_I, _p(ws1), _p(ws2),
                               rsf_fin, ACTIVATIONS[activation], float(clamp),
-                              int(bool(weight_on_input)), 2 if fp8 == "x2" else int(bool(fp8)),
+                              int(bool(weight_on_input)),
+                              {"x2": 2, "block": 3}.get(fp8, int(bool(fp8))) if isinstance(fp8, str)
+                              else int(bool(fp8)),
                               _p(s1), _p(s2), _p(tok),
                               n, _p(out), _p(y), _p(ids), _p(w))
     return {"out": out, "y_routes": y, "ids": ids, "weights": w, "tokens": tok}

@@ -32,13 +32,16 @@
 #include <string.h>
 
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
-enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1, OR_W_FP8 = 2 };
+enum { OR_W_BF16 = 0, OR_W_MXFP4 = 1, OR_W_FP8 = 2, OR_W_FP8_BLOCK = 3 };
+/* rows and columns of a weight block, elements of an activation group (block FP8) */
+enum { OR_BLOCK = 128 };
 enum { OR_ACT_SILU = 0, OR_ACT_GELU = 1 };
 
 typedef struct {
-  int32_t fmt;            /* OR_W_BF16, OR_W_MXFP4 or OR_W_FP8 */
+  int32_t fmt;            /* OR_W_BF16, OR_W_MXFP4, OR_W_FP8 or OR_W_FP8_BLOCK */
   const void* data;       /* bf16 [rows, K], packed e2m1 [rows, K/2] or e4m3 [rows, K] */
-  const void* scales;     /* E8M0 u8 [rows, K/32] (MXFP4) or fp32 [rows] (FP8, per row) */
+  const void* scales;     /* E8M0 u8 [rows, K/32] (MXFP4), fp32 [rows] (FP8, per row) or
+                             fp32 [rows/128, K/128] (FP8_BLOCK, per 128 x 128 block) */
 } oracle_weights;
 
 static double bf16_val(uint16_t h) {
@@ -178,11 +181,32 @@ void oracle_quantize_fp8x2_rows(const uint16_t* x, int64_t rows, int64_t H, uint
   }
 }
 
+/* Block-scaled FP8 activations ([MOD] FusedMoEPermuteExpertsUnpermute quant
+ * properties: block_shape, with per_act_token_quant the activations scaled
+ * per token; the page names the knobs, not the rule): every group of G
+ * consecutive elements of a row gets its own scale, by the per-row rule of
+ * oracle_quantize_fp8_rows applied to the group alone.  scales is
+ * [rows, H / G]. */
+void oracle_quantize_fp8_groups(const uint16_t* x, int64_t rows, int64_t H, int64_t G, uint8_t* q,
+                                float* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < H / G; ++g)
+      oracle_quantize_fp8_rows(x + r * H + g * G, 1, G, NULL, q + r * H + g * G,
+                               scales + r * (H / G) + g);
+}
+
 /* A row quantized by oracle_quantize_fp8_rows (terms 1) or
  * oracle_quantize_fp8x2_rows (terms 2), decoded to doubles. */
 static void quantize_decode(const uint16_t* row, int64_t n, int terms, const float* static_scale,
                             uint8_t* c1, uint8_t* c2, double* out) {
   float sc;
+  if (terms == 3) {  /* block FP8: one scale per 128 elements */
+    float gs[1024];
+    oracle_quantize_fp8_groups(row, 1, n, OR_BLOCK, c1, gs);
+    for (int64_t c = 0; c < n; ++c)
+      out[c] = oracle_e4m3_decode(c1[c]) * (double)gs[c / OR_BLOCK];
+    return;
+  }
   if (terms == 2) {
     oracle_quantize_fp8x2_rows(row, 1, n, c1, c2, &sc);
     for (int64_t c = 0; c < n; ++c)
@@ -201,6 +225,9 @@ double oracle_weight_at(const oracle_weights* w, int64_t row, int64_t K, int64_t
   if (w->fmt == OR_W_FP8)
     return oracle_e4m3_decode(((const uint8_t*)w->data)[row * K + kk]) *
            (double)((const float*)w->scales)[row];
+  if (w->fmt == OR_W_FP8_BLOCK)
+    return oracle_e4m3_decode(((const uint8_t*)w->data)[row * K + kk]) *
+           (double)((const float*)w->scales)[(row / OR_BLOCK) * (K / OR_BLOCK) + kk / OR_BLOCK];
   return bf16_val(((const uint16_t*)w->data)[row * K + kk]);
 }
 
@@ -231,6 +258,12 @@ static double dot_row(const oracle_weights* w, int64_t row, int64_t K, const dou
     const uint8_t* p = (const uint8_t*)w->data + row * K;
     const double sc = (double)((const float*)w->scales)[row];
     for (int64_t kk = 0; kk < K; ++kk) acc += table[p[kk]] * sc * v[kk];
+  } else if (w->fmt == OR_W_FP8_BLOCK) {
+    /* element (row, kk) = code * the scale of its 128 x 128 block */
+    const uint8_t* p = (const uint8_t*)w->data + row * K;
+    const float* s = (const float*)w->scales + (row / OR_BLOCK) * (K / OR_BLOCK);
+    for (int64_t kk = 0; kk < K; ++kk)
+      acc += oracle_e4m3_decode(p[kk]) * (double)s[kk / OR_BLOCK] * v[kk];
   } else {
     const uint16_t* p = (const uint16_t*)w->data + row * K;
     for (int64_t kk = 0; kk < K; ++kk) acc += bf16_val(p[kk]) * v[kk];
@@ -406,34 +439,37 @@ void oracle_hidden_rows(const uint16_t* a, int64_t rows, int64_t H, int64_t I,
   }
 }
 
-/* The same on FP8 rows (codes [rows, K] and one scale per row, as
- * oracle_quantize_fp8_rows writes them): the rows are decoded to q * scale. */
-void oracle_hidden_rows_fp8(const uint8_t* aq, const float* a_scales, int64_t rows, int64_t H,
-                            int64_t I, const oracle_weights* w1, const int32_t* expert_of_row,
-                            int32_t act, double clamp, double* h) {
+/* The same on FP8 rows (codes [rows, K] and one scale per group of `group`
+ * consecutive elements of a row: group = K for one scale per row, as
+ * oracle_quantize_fp8_rows writes them, 128 for block-scaled rows as
+ * oracle_quantize_fp8_groups writes them): the rows are decoded to
+ * q * the scale of q's group. */
+void oracle_hidden_rows_fp8(const uint8_t* aq, const float* a_scales, int64_t group, int64_t rows,
+                            int64_t H, int64_t I, const oracle_weights* w1,
+                            const int32_t* expert_of_row, int32_t act, double clamp, double* h) {
 #pragma omp parallel
   {
     double* xv = (double*)malloc(sizeof(double) * (size_t)H);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; ++r) {
       for (int64_t c = 0; c < H; ++c)
-        xv[c] = oracle_e4m3_decode(aq[r * H + c]) * (double)a_scales[r];
+        xv[c] = oracle_e4m3_decode(aq[r * H + c]) * (double)a_scales[r * (H / group) + c / group];
       oracle_expert_hidden_act(xv, H, I, w1, expert_of_row[r], act, clamp, h + r * I);
     }
     free(xv);
   }
 }
 
-void oracle_out_rows_fp8(const uint8_t* hq, const float* h_scales, int64_t rows, int64_t I,
-                         int64_t H, const oracle_weights* w2, const int32_t* expert_of_row,
-                         double* y) {
+void oracle_out_rows_fp8(const uint8_t* hq, const float* h_scales, int64_t group, int64_t rows,
+                         int64_t I, int64_t H, const oracle_weights* w2,
+                         const int32_t* expert_of_row, double* y) {
 #pragma omp parallel
   {
     double* hv = (double*)malloc(sizeof(double) * (size_t)I);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; ++r) {
       for (int64_t c = 0; c < I; ++c)
-        hv[c] = oracle_e4m3_decode(hq[r * I + c]) * (double)h_scales[r];
+        hv[c] = oracle_e4m3_decode(hq[r * I + c]) * (double)h_scales[r * (I / group) + c / group];
       oracle_expert_out(hv, H, I, w2, expert_of_row[r], y + r * H);
     }
     free(hv);
@@ -560,7 +596,9 @@ void oracle_finalize_add_rmsnorm(const uint16_t* y_perm, const double* w, const 
  * weight_on_input) quantized per row to FP8 (oracle_quantize_fp8_rows; static
  * a1_scale when given), and its hidden row h rounded to bf16 and quantized
  * the same way (static a2_scale when given).  act_quant 2 quantizes both rows
- * with the two-term rule instead (oracle_quantize_fp8x2_rows, dynamic scales).
+ * with the two-term rule instead (oracle_quantize_fp8x2_rows, dynamic scales);
+ * act_quant 3 (block-scaled FP8) quantizes them per group of 128 elements
+ * (oracle_quantize_fp8_groups, dynamic scales).
  * The shared expert stays bf16.
  * Optional outputs: y_routes [n, k, H] (the unweighted per-route expert output,
  * zero for non-local routes), ids [n, k], weights [n, k].

@@ -132,6 +132,24 @@ def fp8_quantize_rows(w_bf16: np.ndarray):
     return codes, scales
 
 
+def fp8_quantize_blocks(w_bf16: np.ndarray, block: int = 128):
+    """Test weights in block-scaled FP8 E4M3: bf16 bits [..., N, K] -> (codes
+    uint8 [..., N, K], scales float32 [..., N/block, K/block]), one scale per
+    block x block tile: amax / 448 of the tile (1 for an all-zero tile); the
+    codes are torch's round-to-nearest-even cast of w / scale, clamped first."""
+    import torch
+    w = bf16_bits_to_f32(np.ascontiguousarray(w_bf16, dtype=np.uint16))
+    *lead, N, K = w.shape
+    if N % block or K % block:
+        raise ValueError("N and K must be multiples of the block")
+    t = w.reshape(*lead, N // block, block, K // block, block)
+    amax = np.abs(t).max(axis=(-3, -1))
+    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = np.clip(t / scales[..., :, None, :, None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.numpy().reshape(w.shape), scales
+
+
 def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (bit shift, no arithmetic)."""
     return (a.astype(np.uint32) << 16).view(np.float32)
