@@ -23,6 +23,9 @@ bf16 weights.  The other workloads:
                                      matrix cores (near-bf16 activation precision)
   deepseekv3_mxfp4_fp8act_2048tok    MXFP4 weights with FP8 activations per token (FP8 x e2m1
                                      on the matrix cores, E8M0 block scales applied by them)
+  deepseekv3_fp8block_2048tok        the DeepSeek-V3 routed shape in blockwise FP8: one weight
+                                     scale per 128 x 128 block, one activation scale per token
+                                     and 128-element group
   ep_rank3of8_decode                 one expert-parallel rank's 32 experts at a
                                      decode batch (--tokens 1, 8 or 64), deferred
                                      form followed by the separate finalize; the
@@ -64,6 +67,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MiB) + MALL (256 MiB)
+HOST_AHEAD_CYCLES = 2_000_000  # GPU spin before each decode step (outside the events)
 
 
 def parse():
@@ -90,6 +94,9 @@ def parse():
                    help="run the layer over chunks of this many tokens")
     p.add_argument("--batched-max-tokens", type=int, default=0,
                    help="use the batched experts format with this capacity per local expert")
+    p.add_argument("--gather-kernel", action="store_true",
+                   help="gather the permuted rows with the permute's own kernel instead of "
+                        "reading them through the inverse map inside GEMM1")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -134,12 +141,15 @@ def gemm_work(cfg, counts, gemm: int):
         N, K, out_cols = cfg.H, cfg.I, cfg.H
     if cfg.mxfp4:
         w_bytes_per_expert = N * (K // 2 + K // 32)
+    elif cfg.fp8_block:
+        w_bytes_per_expert = N * K + (N // 128) * (K // 128) * 4   # codes + one scale per block
     elif cfg.fp8:
         w_bytes_per_expert = N * (K + 4)     # codes + one fp32 scale per channel
     else:
         w_bytes_per_expert = N * K * 2
     # fp8 rows carry a scale; two-term rows hold 2K codes
-    in_bytes = R_l * (K + 4) if cfg.fp8 else R_l * (2 * K + 4) if cfg.fp8x2 else R_l * K * 2
+    in_bytes = (R_l * (K + 4 * (K // 128)) if cfg.fp8_block else R_l * (K + 4) if cfg.fp8
+                else R_l * (2 * K + 4) if cfg.fp8x2 else R_l * K * 2)
     flops = 2.0 * R_l * N * K
     nbytes = float(touched * w_bytes_per_expert + in_bytes + R_l * out_cols * 2)
     return flops, nbytes
@@ -152,6 +162,9 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
     import oracle
     if cfg.mxfp4:
         W1, W2 = oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    elif cfg.fp8_block:
+        W1 = oracle.Weights(w["w1_q"], w["w1_s"], block=True)
+        W2 = oracle.Weights(w["w2_q"], w["w2_s"], block=True)
     elif cfg.fp8:
         W1 = oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1))
         W2 = oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1))
@@ -159,7 +172,9 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
         W1, W2 = oracle.Weights(w["w1"]), oracle.Weights(w["w2"])
     from synth import configs
     kw = dict(expert_map=configs.expert_map(cfg), shared_I=cfg.shared_I, ws1=w.get("ws1"),
-              ws2=w.get("ws2"), fp8="x2" if cfg.fp8x2 else cfg.fp8, **(variant or {}))
+              ws2=w.get("ws2"),
+              fp8="x2" if cfg.fp8x2 else "block" if cfg.fp8_block else cfg.fp8,
+              **(variant or {}))
 
     def run(x, logits, toks):
         oracle.moe_tokens(x, logits, W1, W2, cfg.I, cfg.k, cfg.score, cfg.renormalize, cfg.rsf,
@@ -250,7 +265,7 @@ def main():
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
     dev_draws = [(to_bf16(x), torch.from_numpy(lg).cuda()) for x, lg in draws]
-    if cfg.mxfp4 or cfg.fp8:
+    if cfg.mxfp4 or cfg.fp8 or cfg.fp8_block:
         W1 = moe.Weights(torch.from_numpy(w["w1_q"]).cuda(), torch.from_numpy(w["w1_s"]).cuda())
         W2 = moe.Weights(torch.from_numpy(w["w2_q"]).cuda(), torch.from_numpy(w["w2_s"]).cuda())
     else:
@@ -271,18 +286,23 @@ def main():
     h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    quant = cfg.fp8 or cfg.fp8x2        # activations quantized inside the layer
+    quant = cfg.fp8 or cfg.fp8x2 or cfg.fp8_block   # activations quantized inside the layer
     terms = 2 if cfg.fp8x2 else 1
     if quant:
         if Mb:
             print("FP8 workloads take the standard layout", file=sys.stderr)
             sys.exit(2)
         xq = torch.empty((T, H * terms), dtype=torch.uint8, device=dev)
-        xs = torch.empty((T,), dtype=torch.float32, device=dev)
         xq_perm = torch.empty((R_pad, H * terms), dtype=torch.uint8, device=dev)
-        ps = torch.empty((R_pad,), dtype=torch.float32, device=dev)
         hq = torch.empty((R_pad, I * terms), dtype=torch.uint8, device=dev)
-        hs = torch.empty((R_pad,), dtype=torch.float32, device=dev)
+        if cfg.fp8_block:   # group-major scales, one per row and 128 elements
+            xs = torch.empty((H // 128, T), dtype=torch.float32, device=dev)
+            ps = torch.empty((H // 128, R_pad), dtype=torch.float32, device=dev)
+            hs = torch.empty((I // 128, R_pad), dtype=torch.float32, device=dev)
+        else:
+            xs = torch.empty((T,), dtype=torch.float32, device=dev)
+            ps = torch.empty((R_pad,), dtype=torch.float32, device=dev)
+            hs = torch.empty((R_pad,), dtype=torch.float32, device=dev)
     if args.fused_tail:
         residual = to_bf16(draws[0][0])  # a residual stream of the x distribution
         gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
@@ -316,10 +336,23 @@ def main():
     counts_b = torch.empty((El,), dtype=torch.int32, device=dev)
     # bf16 passes in the standard layout: GEMM1 reads its rows from x through
     # the permute's inverse map, as the library's fused calls do (no gather kernel)
-    gathered = (not quant and not Mb and not w_in and P * H * 2 <= 0xFFFFFFFF)
-    inv_buf = torch.empty((R_pad,), dtype=torch.int32, device=dev) if gathered else None
+    gathered = (not quant and not Mb and not w_in and P * H * 2 <= 0xFFFFFFFF
+                and not args.gather_kernel)
+    # FP8 and two-term rows: GEMM1 reads the quantized token rows through the
+    # inverse map too (the library's fused calls do the same)
+    gathered_q = (quant and not cfg.fp8_block and P * H * terms <= 0xFFFFFFFF
+                  and not args.gather_kernel)
+    inv_buf = (torch.empty((R_pad,), dtype=torch.int32, device=dev)
+               if gathered or gathered_q else None)
 
     def permute(sl, st):
+        if cfg.fp8_block:
+            moe.moe_quantize_fp8_blockwise(xd_cur[0][sl], None, xq[sl], xs[:, sl], stream=st)
+            mark_cur[0]("permute")
+            moe.moe_permute_fp8_blockwise(ids[sl], E, xq[sl], xs[:, sl], El, emap_d, R_pad,
+                                          pmap[sl], offsets, None, xq_perm, ps, want_inv=False,
+                                          stream=st)
+            return
         if cfg.fp8x2:
             moe.moe_quantize_fp8x2(xd_cur[0][sl], wts[sl] if w_in else None, xq[sl], xs[sl],
                                    stream=st)
@@ -328,8 +361,12 @@ def main():
                                  stream=st)
         if quant:
             mark_cur[0]("permute")
-            moe.moe_permute_fp8(ids[sl], E, xq[sl], xs[sl], El, emap_d, R_pad, pmap[sl], offsets,
-                                None, xq_perm, ps, want_inv=False, stream=st)
+            if gathered_q:
+                moe.moe_permute(ids[sl], E, El, emap_d, None, R_pad, pmap[sl], offsets, inv_buf,
+                                stream=st)
+            else:
+                moe.moe_permute_fp8(ids[sl], E, xq[sl], xs[sl], El, emap_d, R_pad, pmap[sl],
+                                    offsets, None, xq_perm, ps, want_inv=False, stream=st)
             return
         if Mb:
             moe.moe_permute_batched(ids[sl], E, Mb, El, emap_d, xd_cur[0][sl], pmap[sl], counts_b,
@@ -343,9 +380,23 @@ def main():
                             stream=st)
 
     def gemms(n, st):
-        if cfg.fp8x2:
+        if cfg.fp8_block:
+            moe.moe_grouped_gemm1_act_fp8_blockwise(xq_perm, ps, offsets, W1, I, h, stream=st,
+                                                    split=False, workspace=split_ws, **act_kw)
+            mark_cur[0]("quantize_h")
+            moe.moe_quantize_fp8_blockwise(h, offsets[El:], hq, hs, stream=st)
+            mark_cur[0]("gemm2")
+            moe.moe_grouped_gemm2_fp8_blockwise(hq, hs, offsets, W2, H, y, stream=st, split=False,
+                                                workspace=split_ws)
+            return
+        if quant and gathered_q:
+            moe.moe_grouped_gemm1_act_fp8_gathered(xq[gsl[0]], xs[gsl[0]], inv_buf, k, offsets,
+                                                   W1, I, terms=terms, h=h, stream=st,
+                                                   split=False, workspace=split_ws, **act_kw)
+        elif cfg.fp8x2:
             moe.moe_grouped_gemm1_act_fp8x2(xq_perm, ps, offsets, W1, I, h, stream=st,
                                             split=False, workspace=split_ws, **act_kw)
+        if cfg.fp8x2:
             mark_cur[0]("quantize_h")
             moe.moe_quantize_fp8x2(h, None, hq, hs, row_count=offsets[El:], stream=st)
             mark_cur[0]("gemm2")
@@ -353,8 +404,9 @@ def main():
                                         workspace=split_ws)
             return
         if cfg.fp8:
-            moe.moe_grouped_gemm1_act_fp8(xq_perm, ps, offsets, W1, I, h, stream=st, split=False,
-                                          workspace=split_ws, **act_kw)
+            if not gathered_q:
+                moe.moe_grouped_gemm1_act_fp8(xq_perm, ps, offsets, W1, I, h, stream=st,
+                                              split=False, workspace=split_ws, **act_kw)
             mark_cur[0]("quantize_h")
             moe.moe_quantize_fp8(h, None, None, hq, hs, row_count=offsets[El:], stream=st)
             mark_cur[0]("gemm2")
@@ -430,6 +482,10 @@ def main():
     def step(i, ev=None):
         if flush is not None:
             evict_caches()
+            # keep the GPU busy (outside the events) while the host enqueues the
+            # step, so the events time the kernels, not the Python call overhead
+            # between them (a decode step's kernels take a few microseconds each)
+            torch.cuda._sleep(HOST_AHEAD_CYCLES)
         if ev is None:
             layer(i % len(dev_draws), stream)
             return
@@ -526,7 +582,7 @@ def main():
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
     g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
     # (two-term rows run the fp8 MFMA twice: the bf16 peak is their rate)
-    peak_mfma = PEAK_FP8_TFLOPS if cfg.fp8 else PEAK_BF16_TFLOPS
+    peak_mfma = PEAK_FP8_TFLOPS if (cfg.fp8 or cfg.fp8_block) else PEAK_BF16_TFLOPS
     t_mfma = g1_flops / (peak_mfma * 1e12)
     t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm:
@@ -561,27 +617,37 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if cfg.fp8 else "fp8x2 (two E4M3 terms) x e2m1" if cfg.fp8x2 else "bf16",
+        "dtype": ("fp8 (blockwise: 128-element activation groups, 128 x 128 weight blocks)"
+                  if cfg.fp8_block else "fp8" if cfg.fp8
+                  else "fp8x2 (two E4M3 terms) x e2m1" if cfg.fp8x2 else "bf16"),
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random weights"
                 + (", MXFP4-quantized" if cfg.mxfp4 else "")
                 + ((", FP8 E4M3 activations per token" if cfg.mxfp4 else
                     ", FP8 E4M3 weights per channel, activations per token") if cfg.fp8 else "")
                 + (", bf16 activations as two FP8 E4M3 terms per token" if cfg.fp8x2 else "")
+                + (", FP8 E4M3 weights per 128 x 128 block, activations per token and 128-element"
+                   " group" if cfg.fp8_block else "")
                 + ")",
         "config": {"workload": label, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "local_experts": El, "top_k": k,
                    "shared_intermediate": cfg.shared_I,
                    "expert_weights": "mxfp4 (e2m1 + E8M0 per 32)" if cfg.mxfp4 else
-                                     ("fp8 e4m3 (fp32 scale per channel)" if cfg.fp8 else "bf16"),
+                                     ("fp8 e4m3 (fp32 scale per 128 x 128 block)" if cfg.fp8_block
+                                      else "fp8 e4m3 (fp32 scale per channel)" if cfg.fp8
+                                      else "bf16"),
                    "routing": ("softmax" if cfg.score == 0 else "sigmoid") +
                               (f" top-{k} renormalized") + (f", rsf {cfg.rsf}" if cfg.rsf != 1 else "") +
                               (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
                    "form": ("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
-                            f"{len(draws)} routing draws" if decode else "finalized")
+                            f"{len(draws)} routing draws, the host enqueues each step while a GPU spin "
+                            "runs ahead of it (events time the kernels, not the Python call overhead)"
+                            if decode else "finalized")
                            + (", replayed as a captured HIP graph" if graphs else "")
                            + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")
                            + (f", {len(chunks)} chunks of {P} tokens" if len(chunks) > 1 else "")
-                           + (f", batched experts format ({Mb} rows per expert)" if Mb else ""),
+                           + (f", batched experts format ({Mb} rows per expert)" if Mb else "")
+                           + (", rows gathered through the inverse map inside GEMM1"
+                              if gathered or gathered_q else ""),
                    "activation": args.activation
                                  + (f", clamp {args.activation_clamp:g}" if args.activation_clamp else "")
                                  + (", routing weight on the input" if w_in else "")},

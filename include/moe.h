@@ -76,8 +76,10 @@ enum {
   MOE_DTYPE_F32 = 1,   /* float32                                               */
   MOE_DTYPE_MXFP4 = 2, /* e2m1 pairs (low nibble = even element) + one E8M0 scale
                           byte per 32 elements along the reduction dimension    */
-  MOE_DTYPE_FP8_E4M3 = 3 /* OCP FP8 E4M3 (bias 7, largest 448) codes + one fp32
+  MOE_DTYPE_FP8_E4M3 = 3, /* OCP FP8 E4M3 (bias 7, largest 448) codes + one fp32
                           scale per row (weights: per output channel)           */
+  MOE_DTYPE_FP8_BLOCK = 4 /* E4M3 weight codes + one fp32 scale per 128 x 128 block
+                          (block_shape [128, 128])                              */
 };
 
 /* Activations of GEMM1 (page "modular_kernel.py", activation(): the output is
@@ -121,8 +123,9 @@ typedef struct moe_layer_options {
   int32_t apply_router_weight_on_input;
   int32_t chunk_tokens;
   int32_t batched_max_tokens;
-  int32_t act_quant;        /* MOE_QUANT_NONE, MOE_QUANT_FP8 (FP8 or MXFP4 weights) or
-                               MOE_QUANT_FP8X2 (MXFP4 weights) */
+  int32_t act_quant;        /* MOE_QUANT_NONE, MOE_QUANT_FP8 (FP8 or MXFP4 weights),
+                               MOE_QUANT_FP8X2 (MXFP4 weights) or MOE_QUANT_FP8_BLOCK
+                               (FP8_BLOCK weights) */
   const float* a1_scale;    /* (device) static scale of the GEMM1 input, or NULL */
   const float* a2_scale;    /* (device) static scale of the GEMM2 input, or NULL */
 } moe_layer_options;
@@ -134,15 +137,25 @@ typedef struct moe_layer_options {
  * or a2_scale); both GEMMs then multiply FP8 codes on the matrix cores and
  * apply the row (and FP8 weights' channel) scales in fp32.  Needs FP8 weights
  * (H and I multiples of 128) or MXFP4 weights (multiples of 256: FP8 x e2m1
- * on the matrix cores, the E8M0 block scales applied by them), the standard
- * layout (no batched_max_tokens); the shared expert stays bf16. */
+ * on the matrix cores, the E8M0 block scales applied by them); the shared
+ * expert stays bf16.  In the standard layout GEMM1 reads the quantized token
+ * rows through the permute's inverse map (no gather); in the batched experts
+ * format the quantized rows are gathered into the capacity blocks. */
 /* MOE_QUANT_FP8X2 keeps bf16 activations close to bf16 precision on the
  * FP8 x e2m1 matrix cores: each row becomes two E4M3 terms with one scale,
  * x ~ scale * (q1 + q2 / 16) (moe_quantize_fp8x2), before dispatch and before
  * GEMM2, and both GEMMs multiply both terms by the e2m1 weights.  Needs MXFP4
- * weights (H and I multiples of 256), dynamic scales (a1_scale and a2_scale
- * NULL) and the standard layout. */
-enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1, MOE_QUANT_FP8X2 = 2 };
+ * weights (H and I multiples of 256) and dynamic scales (a1_scale and a2_scale
+ * NULL); either layout. */
+/* MOE_QUANT_FP8_BLOCK: blockwise FP8 (block_shape [128, 128] with
+ * per_act_token_quant, page "modular_kernel.py", FusedMoEPermuteExpertsUnpermute
+ * quant properties): each token row, and each bf16 hidden row before GEMM2,
+ * is quantized per group of 128 consecutive elements (moe_quantize_fp8_blockwise),
+ * and both GEMMs apply one activation scale per row and 128 k and one weight
+ * scale per 128 x 128 block to each k-block's sum.  Needs MOE_DTYPE_FP8_BLOCK
+ * weights, H and I multiples of 128, dynamic scales and no router weight on
+ * the input; either layout (the quantized rows are always gathered). */
+enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1, MOE_QUANT_FP8X2 = 2, MOE_QUANT_FP8_BLOCK = 3 };
 
 /* Expert weights of one GEMM, all local experts, reduction dimension last:
  *   BF16:  data = bf16 [E_l, N, K],   scales = NULL
@@ -150,6 +163,10 @@ enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8 = 1, MOE_QUANT_FP8X2 = 2 };
  *   FP8:   data = e4m3 [E_l, N, K],   scales = fp32 [E_l, N] (per output
  *          channel, per_out_ch_quant of page "modular_kernel.py"); these
  *          multiply FP8 activations only (the *_fp8 GEMMs, or MOE_QUANT_FP8)
+ *   FP8_BLOCK: data = e4m3 [E_l, N, K], scales = fp32 [E_l, N/128, K/128]
+ *          (block_shape [128, 128]; element (n, k) is code * scale[n/128][k/128]);
+ *          these multiply blockwise FP8 activations only (the *_fp8_blockwise
+ *          GEMMs, or MOE_QUANT_FP8_BLOCK); N and K multiples of 128
  * (GEMM1: N = 2I, K = H, rows [0, I) gate and [I, 2I) up; GEMM2: N = H, K = I.)
  * The tag matters: a buffer read as a wider type than it holds is garbage
  * (page "moe_output.py", the comment on expert_weights). */
@@ -277,6 +294,78 @@ int moe_grouped_gemm1_act_fp8(const uint8_t* a_perm, const float* a_scales,
 int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const int32_t* offsets,
                           int32_t E_l, int64_t R_pad, int32_t I, int32_t H, const moe_weights* w2,
                           void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Blockwise FP8 E4M3 quantization of bf16 rows (the quantize half of
+ * [Quantize-Dispatch] with block_shape [128, 128] and per_act_token_quant,
+ * page "modular_kernel.py"): every group of 128 consecutive elements of a row
+ * gets its own scale by the rule of moe_quantize_fp8 (dynamic: a = max |x|
+ * over the group, 448 for an all-zero group; inv = 448 / a; scale = a / 448;
+ * q = E4M3 nearest to clamp(x * inv, -448, 448), ties to even).
+ *   x          (device) bf16 [rows, H]
+ *   row_count  (device) int32 scalar or NULL: only rows < *row_count
+ *   q          (device) u8 [rows, H] out
+ *   scales     (device) fp32 [H / 128, scales_ld] out, group-major: the scale
+ *              of row r, group g at scales[g * scales_ld + r]; scales_ld >= rows
+ * Limits: H a multiple of 128. */
+int moe_quantize_fp8_blockwise(const void* x, int64_t rows, int32_t H, const int32_t* row_count,
+                               uint8_t* q, float* scales, int64_t scales_ld, void* stream);
+
+/* moe_permute on blockwise FP8 rows: as moe_permute_fp8, the group scales
+ * gathered along with the codes:
+ *   xq_perm[map[t,j], :] = xq[t, :],
+ *   xq_perm_scales[g * R_pad + map[t,j]] = x_scales[g * T + t]   (g < H / 128)
+ *   xq        (device) u8 [T, H];  x_scales (device) fp32 [H / 128, T]
+ *   xq_perm   (device) u8 [R_pad, H] out;  xq_perm_scales (device) fp32 [H / 128, R_pad] out
+ * Limits: H a multiple of 128. */
+int moe_permute_fp8_blockwise(const int32_t* topk_ids, const int32_t* expert_map, int64_t T,
+                              int32_t k, int32_t E, int32_t E_l, const uint8_t* xq,
+                              const float* x_scales, int32_t H, int64_t R_pad, int32_t* map,
+                              int32_t* offsets, int32_t* inv, uint8_t* xq_perm,
+                              float* xq_perm_scales, void* stream);
+
+/* The two grouped GEMMs on blockwise FP8 rows with MOE_DTYPE_FP8_BLOCK weights
+ * (apply() of page "modular_kernel.py" with block_shape [128, 128]):
+ *   C[r, n] = sum over k-blocks b of a_scale[b][r] * w_scale[e][n/128][b] *
+ *             sum_{k in block b} a[r, k] * W[e, n, k]
+ * (each block's E4M3 products summed in fp32 by the 32x32x64 MFMA, scaled and
+ * added in fp32), then, for GEMM1, act(gate) * up and one rounding to bf16.
+ *   a_perm / h_perm    (device) u8 [R_pad, H or I]
+ *   a_scales / h_scales (device) fp32 [H/128 or I/128, R_pad], group-major
+ *                      (as moe_permute_fp8_blockwise / moe_quantize_fp8_blockwise
+ *                      with scales_ld = R_pad write them)
+ *   h / y              (device) bf16 [R_pad, I or H] out;  workspace as for
+ *                      the bf16 calls
+ * Limits: H and I multiples of 128. */
+int moe_grouped_gemm1_act_fp8_blockwise(const uint8_t* a_perm, const float* a_scales,
+                                        const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                        int32_t H, int32_t I, const moe_weights* w1,
+                                        int32_t activation, float activation_clamp, void* h,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+int moe_grouped_gemm2_fp8_blockwise(const uint8_t* h_perm, const float* h_scales,
+                                    const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                    int32_t I, int32_t H, const moe_weights* w2, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 GEMM1 + activation reading its rows straight from the quantized token
+ * rows (the dispatch of [Quantize-Dispatch] folded into the first expert GEMM;
+ * apply() of page "modular_kernel.py"): the same result as moe_permute_fp8 (or
+ * the two-term rows dispatched by it) followed by moe_grouped_gemm1_act_fp8 or
+ * moe_grouped_gemm1_act_fp8x2, bit for bit, without the gather.  Permuted row
+ * r of expert e reads token row inv[r] / k and that token's scale.
+ *   xq        (device) u8 [T, H * terms]: FP8 codes (terms 1) or two-term codes
+ *             (terms 2, moe_quantize_fp8x2) of the tokens
+ *   x_scales  (device) fp32 [T], one per token
+ *   inv       (device) int32 [R_pad] from moe_permute (rows < offsets[E_l] read)
+ *   offsets, E_l, R_pad, H, I, activation, h, workspace: as for
+ *             moe_grouped_gemm1_act_fp8; w1 FP8 or MXFP4 weights (terms 1),
+ *             MXFP4 (terms 2)
+ * Limits: as for moe_grouped_gemm1_act_fp8; xq at most 4 GiB. */
+int moe_grouped_gemm1_act_fp8_gathered(const uint8_t* xq, const float* x_scales,
+                                       int32_t terms, const int32_t* inv, int64_t T, int32_t k,
+                                       const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                       int32_t H, int32_t I, const moe_weights* w1,
+                                       int32_t activation, float activation_clamp, void* h,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Two-term FP8 E4M3 quantization of bf16 rows, for bf16 activations on the
  * FP8 x e2m1 matrix cores with MXFP4 weights (the quantize half of

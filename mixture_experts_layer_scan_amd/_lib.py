@@ -49,6 +49,16 @@ PROTOTYPES = {
                                                  _f32, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm2_fp8": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _Wp, _vp, _vp,
                                              _sz, _vp]),
+    "moe_quantize_fp8_blockwise": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp]),
+    "moe_permute_fp8_blockwise": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _i32,
+                                                 _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_grouped_gemm1_act_fp8_blockwise": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32,
+                                                           _Wp, _i32, _f32, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm2_fp8_blockwise": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _Wp,
+                                                       _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm1_act_fp8_gathered": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _vp,
+                                                          _i32, _i64, _i32, _i32, _Wp, _i32, _f32,
+                                                          _vp, _vp, _sz, _vp]),
     "moe_quantize_fp8x2": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm1_act_fp8x2": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _Wp,
                                                    _i32, _f32, _vp, _vp, _sz, _vp]),

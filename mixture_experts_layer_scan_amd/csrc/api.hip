@@ -111,11 +111,12 @@ int check_gemm_dims(int32_t H, int32_t I) {
 
 int check_weights(const moe_weights* w, const char* name) {
   if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must not be NULL", name);
-  if (w->dtype == MOE_DTYPE_MXFP4 || w->dtype == MOE_DTYPE_FP8_E4M3) {
+  if (w->dtype == MOE_DTYPE_MXFP4 || w->dtype == MOE_DTYPE_FP8_E4M3 ||
+      w->dtype == MOE_DTYPE_FP8_BLOCK) {
     MOE_CHECK(need_ptr(w->data, name));
     if (!w->scales) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s weights need their scales", name,
                                 w->dtype == MOE_DTYPE_MXFP4 ? "MXFP4" : "FP8");
-    if (w->dtype == MOE_DTYPE_FP8_E4M3 && (reinterpret_cast<uintptr_t>(w->scales) & 3u))
+    if (w->dtype != MOE_DTYPE_MXFP4 && (reinterpret_cast<uintptr_t>(w->scales) & 3u))
       return fail(MOE_ERR_MISALIGNED, "%s: FP8 scales must be 4-byte aligned", name);
     return check_device_ptr(w->scales, name);
   }
@@ -130,8 +131,13 @@ const void* scales_of(const moe_weights* w) {
 }
 
 // FP8 weights multiply FP8 activations only; FP8 activations multiply FP8 or
-// MXFP4 weights.
-int check_pairing(const moe_weights* w, bool fp8_act, const char* name) {
+// MXFP4 weights; block-scaled FP8 weights and blockwise activations pair
+// with each other only.
+int check_pairing(const moe_weights* w, bool fp8_act, const char* name, bool block = false) {
+  if (block != (w->dtype == MOE_DTYPE_FP8_BLOCK))
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: block-scaled FP8 weights and blockwise FP8 activations go together", name);
+  if (block) return MOE_OK;
   if (fp8_act && w->dtype != MOE_DTYPE_FP8_E4M3 && w->dtype != MOE_DTYPE_MXFP4)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: FP8 activations need FP8 or MXFP4 weights", name);
   if (!fp8_act && w->dtype == MOE_DTYPE_FP8_E4M3)
@@ -184,6 +190,7 @@ struct LayerOpts {
   int batch_m = 0;    // > 0: batched experts format with this capacity
   bool fp8 = false;   // FP8 activations (MOE_QUANT_FP8 or MOE_QUANT_FP8X2)
   int terms = 1;      // 2: two-term FP8 activations (MOE_QUANT_FP8X2)
+  bool block = false; // blockwise FP8 activations and weights (MOE_QUANT_FP8_BLOCK)
   const float* a1_scale = nullptr;
   const float* a2_scale = nullptr;
 };
@@ -204,14 +211,17 @@ int parse_options(const moe_layer_options* o, int32_t k, LayerOpts* out) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "batched_max_tokens must be >= 0");
   out->batch_m = o->batched_max_tokens;
   if (o->act_quant != MOE_QUANT_NONE && o->act_quant != MOE_QUANT_FP8 &&
-      o->act_quant != MOE_QUANT_FP8X2)
+      o->act_quant != MOE_QUANT_FP8X2 && o->act_quant != MOE_QUANT_FP8_BLOCK)
     return fail(MOE_ERR_UNSUPPORTED, "unknown activation quantization %d", o->act_quant);
   out->fp8 = o->act_quant != MOE_QUANT_NONE;
   out->terms = o->act_quant == MOE_QUANT_FP8X2 ? 2 : 1;
+  out->block = o->act_quant == MOE_QUANT_FP8_BLOCK;
+  if (out->block && (o->a1_scale || o->a2_scale))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "blockwise FP8 activations take dynamic scales only");
+  if (out->block && out->weight_on_input)
+    return fail(MOE_ERR_UNSUPPORTED, "blockwise FP8 activations take no router weight on the input");
   if (out->terms == 2 && (o->a1_scale || o->a2_scale))
     return fail(MOE_ERR_INVALID_ARGUMENT, "two-term FP8 activations take dynamic scales only");
-  if (out->fp8 && out->batch_m > 0)
-    return fail(MOE_ERR_UNSUPPORTED, "FP8 activations take the standard layout (no batched_max_tokens)");
   if (!out->fp8 && (o->a1_scale || o->a2_scale))
     return fail(MOE_ERR_INVALID_ARGUMENT, "a1_scale / a2_scale need act_quant = MOE_QUANT_FP8");
   MOE_CHECK(opt_ptr4(o->a1_scale, "a1_scale"));
@@ -238,7 +248,9 @@ int64_t routed_rows(int64_t T, int32_t k, int32_t E_l, int batch_m) {
 }
 
 size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, int batch_m,
-                       bool fp8 = false, int terms = 1) {
+                       bool fp8 = false, int terms = 1, bool block = false) {
+  // scales per row: one, or one per 128 elements (blockwise)
+  const int64_t gh = block ? H / 128 : 1, gi = block ? I / 128 : 1;
   const int64_t R_pad = routed_rows(T, k, E_l, batch_m);
   size_t b = 0;
   b += align_up(sizeof(int32_t) * T * k);               // topk ids
@@ -251,10 +263,10 @@ size_t routed_ws_bytes(int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I, 
   b += align_up(routed_split_bytes(R_pad, H, I));       // GEMM split partials
   if (fp8) {
     b += align_up(size_t(T) * H * terms);               // quantized tokens
-    b += align_up(sizeof(float) * T);                   // their scales
-    b += align_up(sizeof(float) * R_pad);               // permuted row scales
+    b += align_up(sizeof(float) * T * gh);              // their scales
+    b += align_up(sizeof(float) * R_pad * gh);          // permuted row scales
     b += align_up(size_t(R_pad) * I * terms);           // quantized hidden rows
-    b += align_up(sizeof(float) * R_pad);               // their scales
+    b += align_up(sizeof(float) * R_pad * gi);          // their scales
   }
   return b;
 }
@@ -327,7 +339,8 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   MOE_CHECK(check_route_sizes(T, E, k));
   MOE_CHECK(check_local(E, E_l));
   MOE_CHECK(check_gemm_dims(H, I));
-  if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4 && w_dtype != MOE_DTYPE_FP8_E4M3)
+  if (w_dtype != MOE_DTYPE_BF16 && w_dtype != MOE_DTYPE_MXFP4 && w_dtype != MOE_DTYPE_FP8_E4M3 &&
+      w_dtype != MOE_DTYPE_FP8_BLOCK)
     return fail(MOE_ERR_UNSUPPORTED, "unknown weight dtype %d", w_dtype);
   if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
   LayerOpts o;
@@ -335,7 +348,7 @@ int moe_workspace_size(int64_t T, int32_t k, int32_t E, int32_t E_l, int32_t H, 
   const int64_t P = pass_tokens(T, o);
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms) + shared_bytes;
+  *bytes = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms, o.block) + shared_bytes;
   return MOE_OK;
 }
 
@@ -453,11 +466,12 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
                        const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
                        void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
                        bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1,
-                       const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0) {
+                       const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0,
+                       bool block = false) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
-  MOE_CHECK(check_pairing(w, fp8, name));
+  MOE_CHECK(check_pairing(w, fp8, name, block));
   if (a_terms == 2 && w->dtype != MOE_DTYPE_MXFP4)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: two-term FP8 activations need MXFP4 weights", name);
   // (two-term rows take 2K bytes, as many as bf16 rows)
@@ -471,7 +485,8 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   const size_t out_bytes = sizeof(uint16_t) * R_pad * N_out;
   if (overlap(a, in_bytes, c, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the input rows", name);
-  if (a_scales && overlap(a_scales, sizeof(float) * R_pad, c, out_bytes))
+  const size_t scale_bytes = sizeof(float) * R_pad * (block ? K / 128 : 1);
+  if (a_scales && overlap(a_scales, scale_bytes, c, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: output must not overlap the row scales", name);
   if (workspace_bytes > 0) {
     MOE_CHECK(need_ptr(workspace, "workspace"));
@@ -483,6 +498,7 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
   moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
                   workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
                   a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms, a_inv, a_k, a_T};
+  if (block) g.a_ld = R_pad;
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -626,6 +642,129 @@ int moe_grouped_gemm2_fp8(const uint8_t* h_perm, const float* h_scales, const in
   if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
   return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
                      workspace_bytes, stream, "moe_grouped_gemm2_fp8", 0, 0, true, h_scales);
+}
+
+int moe_grouped_gemm1_act_fp8_gathered(const uint8_t* xq, const float* x_scales,
+                                       int32_t terms, const int32_t* inv, int64_t T, int32_t k,
+                                       const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                       int32_t H, int32_t I, const moe_weights* w1,
+                                       int32_t activation, float activation_clamp, void* h,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w1));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (terms != 1 && terms != 2) return fail(MOE_ERR_INVALID_ARGUMENT, "terms must be 1 or 2");
+  if (T < 0 || k <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 and k > 0");
+  if (R_pad < T * k) return fail(MOE_ERR_SIZE_MISMATCH, "R_pad (%lld) < T * k (%lld)",
+                                 (long long)R_pad, (long long)(T * k));
+  if (T * int64_t(H) * terms > int64_t(0xFFFFFFFF))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "xq spans more than 4 GiB");
+  if (R_pad > 0) MOE_CHECK(need_ptr(inv, "inv"));
+  if (overlap(inv, sizeof(int32_t) * R_pad, h, sizeof(uint16_t) * R_pad * I))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "h must not overlap inv");
+  if (R_pad == 0 || T == 0) {
+    MOE_CHECK(check_weights(w1, "moe_grouped_gemm1_act_fp8_gathered"));
+    return MOE_OK;
+  }
+  MOE_CHECK(opt_ptr4(x_scales, "x_scales"));
+  if (!x_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "x_scales must not be NULL");
+  return gemm_common(xq, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_fp8_gathered", 0,
+                     0, true, x_scales, terms, inv, k, T);
+}
+
+int moe_quantize_fp8_blockwise(const void* x, int64_t rows, int32_t H, const int32_t* row_count,
+                               uint8_t* q, float* scales, int64_t scales_ld, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be non-negative");
+  if (H <= 0 || H % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (H=%d)", H);
+  if (scales_ld < rows) return fail(MOE_ERR_SIZE_MISMATCH, "scales_ld must be >= rows");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(x, "x"));
+  MOE_CHECK(need_ptr(q, "q"));
+  MOE_CHECK(need_ptr(scales, "scales"));
+  MOE_CHECK(opt_ptr4(row_count, "row_count"));
+  const size_t sc_bytes = sizeof(float) * size_t(scales_ld) * (H / 128);
+  if (overlap(x, sizeof(uint16_t) * rows * H, q, size_t(rows) * H) ||
+      overlap(x, sizeof(uint16_t) * rows * H, scales, sc_bytes) ||
+      overlap(q, size_t(rows) * H, scales, sc_bytes))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "x, q and scales must not overlap");
+  hipError_t e = moe::launch_quantize_fp8_groups(x, rows, H, row_count, q, scales, scales_ld,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_fp8_blockwise");
+}
+
+int moe_permute_fp8_blockwise(const int32_t* topk_ids, const int32_t* expert_map, int64_t T,
+                              int32_t k, int32_t E, int32_t E_l, const uint8_t* xq,
+                              const float* x_scales, int32_t H, int64_t R_pad, int32_t* map,
+                              int32_t* offsets, int32_t* inv, uint8_t* xq_perm,
+                              float* xq_perm_scales, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  MOE_CHECK(check_local(E, E_l));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  if (H <= 0 || H % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (H=%d)", H);
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(opt_ptr(inv, "inv"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(map, "map"));
+    MOE_CHECK(need_ptr(xq, "xq"));
+    MOE_CHECK(need_ptr(xq_perm, "xq_perm"));
+    MOE_CHECK(opt_ptr4(x_scales, "x_scales"));
+    MOE_CHECK(opt_ptr4(xq_perm_scales, "xq_perm_scales"));
+    if (!x_scales || !xq_perm_scales)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "x_scales and xq_perm_scales must not be NULL");
+  }
+  if (overlap(xq, size_t(T) * H, xq_perm, size_t(R_pad) * H) ||
+      overlap(x_scales, sizeof(float) * T * (H / 128), xq_perm_scales,
+              sizeof(float) * R_pad * (H / 128)))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "xq_perm and its scales must not overlap xq and its scales");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_permute(topk_ids, expert_map, T, k, E, E_l, map, offsets, inv, R_pad, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_fp8_blockwise");
+  if (T > 0) {
+    e = moe::launch_gather_fp8_rows(xq, x_scales, map, T, k, H, xq_perm, xq_perm_scales, s,
+                                    H / 128, R_pad);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_fp8_blockwise gather");
+  }
+  return MOE_OK;
+}
+
+int moe_grouped_gemm1_act_fp8_blockwise(const uint8_t* a_perm, const float* a_scales,
+                                        const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                        int32_t H, int32_t I, const moe_weights* w1,
+                                        int32_t activation, float activation_clamp, void* h,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w1));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(a_scales, "a_scales"));
+  if (R_pad > 0 && !a_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "a_scales must not be NULL");
+  return gemm_common(a_perm, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                     workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_fp8_blockwise", 0,
+                     0, true, a_scales, 1, nullptr, 1, 0, true);
+}
+
+int moe_grouped_gemm2_fp8_blockwise(const uint8_t* h_perm, const float* h_scales,
+                                    const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                                    int32_t I, int32_t H, const moe_weights* w2, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_fp8_dims(H, I, w2));
+  if (R_pad > 0) MOE_CHECK(opt_ptr4(h_scales, "h_scales"));
+  if (R_pad > 0 && !h_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "h_scales must not be NULL");
+  return gemm_common(h_perm, offsets, E_l, R_pad, I, H, 0, MOE_ACT_SILU, 0.0f, w2, y, workspace,
+                     workspace_bytes, stream, "moe_grouped_gemm2_fp8_blockwise", 0, 0, true,
+                     h_scales, 1, nullptr, 1, 0, true);
 }
 
 int moe_quantize_fp8x2(const void* x, int64_t rows, int32_t H, const float* row_weights,
@@ -808,7 +947,8 @@ struct RoutedWs {
 
 static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_t H, int32_t I,
                              int batch_m, bool fp8 = false, int terms = 1,
-                             size_t split_cap = ~size_t(0)) {
+                             size_t split_cap = ~size_t(0), bool block = false) {
+  const int64_t gh = block ? H / 128 : 1, gi = block ? I / 128 : 1;  // scales per row
   RoutedWs b;
   b.rows = routed_rows(T, k, E_l, batch_m);
   b.ids = c.take<int32_t>(T * k);
@@ -824,10 +964,10 @@ static RoutedWs carve_routed(Carve& c, int64_t T, int32_t k, int32_t E_l, int32_
   if (fp8) {
     // (two-term quantized permuted rows, 2H bytes each, fill x_perm's slot)
     b.xq = c.take<uint8_t>(T * H * terms);
-    b.xs = c.take<float>(T);
-    b.ps = c.take<float>(b.rows);
+    b.xs = c.take<float>(T * gh);
+    b.ps = c.take<float>(b.rows * gh);
     b.hq = c.take<uint8_t>(b.rows * I * terms);
-    b.hs = c.take<float>(b.rows);
+    b.hs = c.take<float>(b.rows * gi);
   }
   return b;
 }
@@ -849,36 +989,77 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
     e = moe::launch_fill_u16(w_bf16_out, T * k, 0x3F80, s);  // bf16 1.0
     if (e != hipSuccess) return hip_fail(e, "unit weights");
   }
-  if (o.fp8) {
+  if (o.block) {
+    // Quantize-Dispatch, blockwise: the tokens per 128-element group
+    e = moe::launch_quantize_fp8_groups(x, T, H, nullptr, b.xq, b.xs, T, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize");
+  } else if (o.fp8) {
     // Quantize-Dispatch: the tokens (times their weight when it goes on the
     // input; top_k 1, so one weight per token) to FP8, then their rows
     e = moe::launch_quantize_fp8(x, T, H, o.a1_scale, o.weight_on_input ? b.wts : nullptr,
                                  nullptr, b.xq, b.xs, s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize");
   }
-  // bf16 rows in the standard layout: GEMM1 reads each permuted row straight
-  // from x through the inverse map (no gather kernel, no x_perm write and
-  // re-read), while x fits one buffer descriptor's 4 GiB
-  const bool gather_in_gemm = !o.fp8 && o.batch_m == 0 && !o.weight_on_input &&
-                              T * int64_t(H) * 2 <= int64_t(0xFFFFFFFF);
+  // Rows in the standard layout: GEMM1 reads each permuted row straight from
+  // the token rows through the inverse map (no gather kernel, no x_perm write
+  // and re-read), while they fit one buffer descriptor's 4 GiB: bf16 rows
+  // unless the routing weight goes on them (the gather applies it); FP8 and
+  // two-term rows with their token's scale (the weight, top-1, was applied
+  // before quantizing); blockwise FP8 keeps the gather (its group scales are
+  // read per k-block by rows of the permuted order).
+  const int64_t token_row_bytes = o.fp8 ? int64_t(H) * o.terms : int64_t(H) * 2;
+  const bool gather_in_gemm = (o.fp8 ? !o.block : !o.weight_on_input) && o.batch_m == 0 &&
+                              T * token_row_bytes <= int64_t(0xFFFFFFFF);
   e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets,
                           gather_in_gemm ? b.inv : nullptr, b.rows, s, o.batch_m);
   if (e != hipSuccess) return hip_fail(e, "permute");
-  if (o.fp8) {
-    e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H * o.terms, b.x_perm, b.ps, s);
+  // (batched experts format: the quantized hidden rows are all E_l * capacity
+  // rows, those past an expert's count never read; the standard layout
+  // quantizes the offsets[E_l] local routes)
+  const int32_t* h_rows = o.batch_m > 0 ? nullptr : b.offsets + E_l;
+  if (o.block) {
+    e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H, b.x_perm, b.ps, s, H / 128, b.rows);
     if (e != hipSuccess) return hip_fail(e, "gather");
-    const int64_t max_rows = moe_permuted_rows(T, k);
+    const int64_t max_rows = std::min(moe_permuted_rows(T, k), b.rows);
     moe::GemmArgs g1{b.x_perm, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h,
-                     b.split, b.split_bytes, o.act, o.clamp, 0, b.ps,
+                     b.split, b.split_bytes, o.act, o.clamp, o.batch_m, b.ps};
+    g1.a_ld = b.rows;
+    e = moe::launch_grouped_gemm(g1, max_rows, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm1");
+    // the hidden rows of the local routes, per 128-element group
+    e = moe::launch_quantize_fp8_groups(b.h, b.rows, I, h_rows, b.hq, b.hs, b.rows, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize hidden");
+    moe::GemmArgs g2{b.hq, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
+                     b.split_bytes, moe::kActSilu, 0.0f, o.batch_m, b.hs};
+    g2.a_ld = b.rows;
+    e = moe::launch_grouped_gemm(g2, max_rows, s);
+    if (e != hipSuccess) return hip_fail(e, "gemm2");
+    return MOE_OK;
+  }
+  if (o.fp8) {
+    if (!gather_in_gemm) {
+      e = moe::launch_gather_fp8_rows(b.xq, b.xs, map, T, k, H * o.terms, b.x_perm, b.ps, s);
+      if (e != hipSuccess) return hip_fail(e, "gather");
+    }
+    const int64_t max_rows = std::min(moe_permuted_rows(T, k), b.rows);
+    moe::GemmArgs g1{gather_in_gemm ? static_cast<const void*>(b.xq) : b.x_perm, w1->data,
+                     scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h, b.split,
+                     b.split_bytes, o.act, o.clamp, o.batch_m, gather_in_gemm ? b.xs : b.ps,
                      w1->dtype == MOE_DTYPE_MXFP4, o.terms};
+    if (gather_in_gemm) {
+      g1.a_inv = b.inv;
+      g1.a_k = k;
+      g1.a_T = T;
+    }
     e = moe::launch_grouped_gemm(g1, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm1");
     // the hidden rows of the local routes (offsets[E_l] of them) to FP8
-    e = moe::launch_quantize_fp8(b.h, b.rows, I, o.a2_scale, nullptr, b.offsets + E_l, b.hq, b.hs,
-                                 s, o.terms);
+    e = moe::launch_quantize_fp8(b.h, b.rows, I, o.a2_scale, nullptr, h_rows, b.hq, b.hs, s,
+                                 o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize hidden");
     moe::GemmArgs g2{b.hq, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
-                     b.split_bytes, moe::kActSilu, 0.0f, 0, b.hs, w2->dtype == MOE_DTYPE_MXFP4,
+                     b.split_bytes, moe::kActSilu, 0.0f, o.batch_m, b.hs,
+                     w2->dtype == MOE_DTYPE_MXFP4,
                      o.terms};
     e = moe::launch_grouped_gemm(g2, max_rows, s);
     if (e != hipSuccess) return hip_fail(e, "gemm2");
@@ -920,8 +1101,8 @@ static int check_fused_args(const float* logits, const void* x, int64_t T, int32
     return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
   MOE_CHECK(check_weights(w1, "w1"));
   MOE_CHECK(check_weights(w2, "w2"));
-  MOE_CHECK(check_pairing(w1, o.fp8, "w1"));
-  MOE_CHECK(check_pairing(w2, o.fp8, "w2"));
+  MOE_CHECK(check_pairing(w1, o.fp8, "w1", o.block));
+  MOE_CHECK(check_pairing(w2, o.fp8, "w2", o.block));
   if (o.terms == 2 && (w1->dtype != MOE_DTYPE_MXFP4 || w2->dtype != MOE_DTYPE_MXFP4))
     return fail(MOE_ERR_INVALID_ARGUMENT, "two-term FP8 activations need MXFP4 weights");
   if (o.fp8) MOE_CHECK(check_fp8_dims(H, I, w1));
@@ -964,7 +1145,7 @@ static int unfinalized_on(const float* logits, const void* x, int64_t T, int32_t
   if (overlap(gemm2_permuted, sizeof(uint16_t) * R_pad * H, x, sizeof(uint16_t) * T * H))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "gemm2_permuted must not overlap x");
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms, split_cap);
+  const RoutedWs b = carve_routed(c, T, k, E_l, H, I, o.batch_m, o.fp8, o.terms, split_cap, o.block);
   return run_routed(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1, w2,
                     o, b, map, gemm2_permuted, static_cast<uint16_t*>(expert_weights), stream);
 }
@@ -1004,7 +1185,7 @@ int moe_fused_experts_unfinalized(const float* logits, const void* x, int64_t T,
   MOE_CHECK(check_unfinalized(logits, x, T, H, I, E, E_l, k, score_fn, expert_map, w1, w2, options,
                               R_pad, gemm2_permuted, expert_weights, map, &o));
   if (T == 0) return MOE_OK;
-  const size_t need = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  const size_t need = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms, o.block);
   MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
   return unfinalized_on(logits, x, T, H, I, E, E_l, k, score_fn, renormalize, rsf, expert_map, w1,
                         w2, o, R_pad, gemm2_permuted, expert_weights, map, workspace, need,
@@ -1026,7 +1207,7 @@ int moe_fused_experts_unfinalized_noalloc(const float* logits, const void* x, in
   // everything but the GEMMs' split scratch must fit; the split scratch takes
   // what is left (fewer split pieces, or none, when little is)
   const int64_t rows = routed_rows(T, k, E_l, o.batch_m);
-  const size_t full = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  const size_t full = routed_ws_bytes(T, k, E_l, H, I, o.batch_m, o.fp8, o.terms, o.block);
   const size_t base = full - align_up(routed_split_bytes(rows, H, I));
   if (base > kNoallocScratchBytes)
     return fail(MOE_ERR_SIZE_MISMATCH,
@@ -1065,7 +1246,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
   }
   size_t shared_bytes = 0;
   MOE_CHECK(moe_shared_workspace_size(P, H, shared_I, &shared_bytes));
-  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms) + shared_bytes;
+  const size_t need = routed_ws_bytes(P, k, E_l, H, I, o.batch_m, o.fp8, o.terms, o.block) + shared_bytes;
   MOE_CHECK(check_workspace(workspace, workspace_bytes, need));
   // out is x itself (in place) or apart from it; the workspace is apart from both
   const size_t row_bytes = sizeof(uint16_t) * T * H;
@@ -1075,7 +1256,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
     return fail(MOE_ERR_DESTINATION_CONFLICT, "the workspace must not overlap x or out");
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c{static_cast<char*>(workspace)};
-  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m, o.fp8, o.terms);
+  const RoutedWs b = carve_routed(c, P, k, E_l, H, I, o.batch_m, o.fp8, o.terms, ~size_t(0), o.block);
   int32_t* s_off = nullptr;
   uint16_t* s_h = nullptr;
   uint16_t* s_y = nullptr;

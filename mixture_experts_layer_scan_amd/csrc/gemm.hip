@@ -200,7 +200,7 @@ __device__ __forceinline__ int opaque(int v) {
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool GATED_, bool WQ_ = false,
-          int GM_ = 8, bool F8_ = false, bool A2_ = false>
+          int GM_ = 8, bool F8_ = false, bool A2_ = false, bool BS_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr bool F8 = F8_;  // activations and weights in FP8 E4M3
@@ -208,6 +208,10 @@ struct TileCfg {
   // term, then the 64 of the second term for the same k, per 128 row bytes
   static constexpr bool A2 = A2_;
   static_assert(!A2 || (F8 && WQ_), "two-term activations pair with MXFP4 weights");
+  // blockwise FP8: one activation scale per row and 128 k, one weight scale
+  // per 128 x 128 block; a k-step (128 k of FP8) is exactly one k-block
+  static constexpr bool BS = BS_;
+  static_assert(!BS || (F8_ && !WQ_ && !A2_), "block scales pair FP8 activations and weights");
   // k per k-step: 128 bytes of an activation row (64 bf16, 128 fp8, or 64
   // of each of the two fp8 terms)
   static constexpr int BK = A2 ? 64 : F8 ? 128 : 64;
@@ -244,6 +248,10 @@ struct TileCfg {
   // of K/32 scale bytes 8-byte aligned); the byte-wise fallback for other K
   // issues more, which only makes the waits stricter
   static constexpr int SCQ = WQ ? FN : 0;
+  // blockwise FP8: per k-step, its k-block's scales of this lane's 16 rows
+  // per row fragment (four 16-byte loads) and of each weight fragment (one
+  // 4-byte load), issued at the top of the k-step before its tile loads
+  static constexpr int SAQ = BS ? FM * 4 + FN : 0;
   static constexpr int A_ELEMS = BM * 64;        // uint16 per activation stage
   static constexpr int B_ELEMS = BN * 64;        // uint16 per weight stage
   // k-steps per unrolled loop body: every stage object is then compile-time
@@ -257,7 +265,9 @@ struct TileCfg {
   // scale bytes of stage q + 1; then (spread over its sub-steps) the
   // activation loads of kt + STAGES - 1 and, when it opens a weight stage,
   // the weight loads of the stage B_STAGES - 1 ahead.
-  static constexpr int loads_at(int kt) { return A_LD + (kt % B_KS == 0 ? B_LD + SCQ : 0); }
+  static constexpr int loads_at(int kt) {
+    return A_LD + SAQ + (kt % B_KS == 0 ? B_LD + SCQ : 0);
+  }
   static constexpr int sum_loads(int from, int to) {
     int n = 0;
     for (int j = from; j <= to; ++j) n += loads_at(j);
@@ -326,6 +336,15 @@ __device__ __forceinline__ uint32_t load_byte(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load_u128(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
+}
+
+__device__ __forceinline__ uint32_t load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), soff, 0);
+}
 
 __device__ __forceinline__ u32x2 load_u64(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     int N_out, int64_t R_pad, uint16_t* __restrict__ C, int n_tiles, float* __restrict__ partials,
     int s_cap, int* __restrict__ split_out, int act, float clamp, int batch_m,
     const float* __restrict__ A_scales, const int32_t* __restrict__ a_inv, int a_k,
-    int64_t a_T, char* __restrict__ tail_ws, int slab_cap) {
+    int64_t a_T, char* __restrict__ tail_ws, int slab_cap, int64_t a_ld) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int NT = Cfg::kThreads, ST = Cfg::STAGES, SUB = Cfg::SUBSTEPS;
   constexpr int SB = Cfg::B_STAGES, BKS = Cfg::B_KS, U = Cfg::UNROLL;
@@ -638,7 +657,56 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       return static_cast<int>((word >> (8u * static_cast<uint32_t>(block & 3))) & 0xFFu);
     };
 
+    // Blockwise FP8: the scales of k-block kb for this lane's rows (A scales
+    // stored k-block-major, [K / 128][a_ld]) and for its weight fragments'
+    // 128-row blocks ([E_l][N_total / 128][K / 128]); a k-step's scales are
+    // loaded at the top of the k-step, before its tile loads, and applied
+    // after its MFMAs: acc += sum_k * a_scale[row] * w_scale.  (Waiting for
+    // them there retires only loads issued before them, which the stage
+    // pipeline has waited for already.)  Reads past either array return zero
+    // (rows past the segment, virtual weight rows past N_out): their results
+    // are never stored.
+    constexpr int BSM = Cfg::BS ? FM : 1, BSN = Cfg::BS ? FN : 1;
+    u32x4 bs_a[BSM][4];
+    uint32_t bs_w[BSN];
+    uint32_t bs_aoff[BSM][4], bs_woff[BSN];
+    const int nkb = K / BK;
+    const int nb_rows = N_total / 128;
+    const __amdgpu_buffer_rsrc_t bs_arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(A_scales), 0,
+        Cfg::BS ? static_cast<int>(static_cast<int64_t>(nkb) * a_ld * 4) : 0, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t bs_wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(W_scales) +
+                             (Cfg::BS ? static_cast<int64_t>(e) * nb_rows * nkb * 4 : 0)),
+        0, Cfg::BS ? nb_rows * nkb * 4 : 0, kBufferFlags);
+    if constexpr (Cfg::BS) {
+      const int half = lane >> 5;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bs_aoff[fm][g] = static_cast<uint32_t>(row0 + wm * Cfg::WTM + fm * 32 + 8 * g + 4 * half) * 4u;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bs_woff[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn)) / 128) * nkb * 4u;
+    }
+    // k-block of k-step kt (the k-order may start at a tile-dependent stage)
+    auto kblock = [&](int kt) { return kt0 + krot(kt); };
+    auto load_bscales = [&](int kt) {
+      if constexpr (Cfg::BS) {
+        const int kb = kblock(kt);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bs_a[fm][g] = load_u128(bs_arsrc, bs_aoff[fm][g], static_cast<int>(kb * a_ld * 4));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) bs_w[fn] = load_u32(bs_wrsrc, bs_woff[fn], kb * 4);
+      }
+    };
+
     f32x16 acc[FM][FN];
+    f32x16 tmp[Cfg::BS ? FM : 1][Cfg::BS ? FN : 1];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -765,6 +833,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         rotate_scales();
         load_scales(min(kt / BKS + 1, nq - 1));
       }
+      // blockwise FP8: this k-step's block scales, before its tile loads
+      load_bscales(kt);
       expand0(P);
       const int ln = opaque(lane);
 #pragma unroll
@@ -794,6 +864,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
               acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 4, 0,
                   (Cfg::A2 && ks == 1) ? 127 - kTerm2Shift : 127, 0, scale_byte(fn, P, ks, ln));
+            else if constexpr (Cfg::BS)  // this k-block's sums, scaled below
+              tmp[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  fa[ks & 1][fm], fb[ks & 1][fn], ks == 0 ? f32x16{} : tmp[fm][fn], 0, 0, 0,
+                  127, 0, 127);
             else if constexpr (Cfg::F8)
               acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   fa[ks & 1][fm], fb[ks & 1][fn], acc[fm][fn], 0, 0, 0, 127, 0, 127);
@@ -804,6 +878,23 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (Cfg::BS) {
+        // the k-block's sums times their row and block scales (lane element i
+        // is row 8 (i / 4) + 4 (lane / 32) + i % 4 of its fragment)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          if (Cfg::SKIP && fm >= fm_act) continue;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            // (whole-vector updates keep the accumulators in registers)
+            const float sw = __uint_as_float(bs_w[fn]);
+            f32x16 s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = __uint_as_float(bs_a[fm][i >> 2][i & 3]) * sw;
+            acc[fm][fn] = acc[fm][fn] + tmp[fm][fn] * s;
+          }
+        }
       }
     };
 
@@ -850,7 +941,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // FP8: the products of codes times the row's activation scale and the
     // column's weight scale (per output channel; 0 past N_out, never stored)
     float sw[Cfg::F8 ? FN : 1];
-    if constexpr (Cfg::F8 && !Cfg::WQ) {
+    if constexpr (Cfg::F8 && !Cfg::WQ && !Cfg::BS) {
       const float* wsc = static_cast<const float*>(W_scales) + static_cast<int64_t>(e) * N_total;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
@@ -860,12 +951,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       }
     }
     auto scaled = [&](float a, float sa, int fn) -> float {
+      if constexpr (Cfg::BS) return a;                  // scaled per k-block already
       if constexpr (Cfg::F8 && Cfg::WQ) return a * sa;  // block scales applied by the MFMA
       if constexpr (Cfg::F8) return a * sa * sw[fn];
       return a;
     };
     auto row_scale = [&](int r) -> float {
-      if constexpr (Cfg::F8) return A_scales[row0 + r];
+      if constexpr (Cfg::BS) return 1.0f;
+      // (rows read from the tokens take their token's scale)
+      if constexpr (Cfg::F8) return A_scales[gathered ? a_inv[row0 + r] / a_k : row0 + r];
       return 1.0f;
     };
     if (!Cfg::SPLIT && in_tail) {
@@ -1113,7 +1207,7 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
                      g.a, g.w, g.w_scales, g.offsets, g.E_l, g.K,
                      g.N_out, g.R_pad, static_cast<uint16_t*>(g.c), n_tiles, partials, s_cap, hdr,
                      g.act, g.clamp, g.batch_m, g.a_scales, g.a_inv, g.a_k, g.a_T, tail_ws,
-                     slab_cap);
+                     slab_cap, g.a_ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tail_ws != nullptr) {
@@ -1129,28 +1223,29 @@ hipError_t launch_cfg(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool WQ, bool F8, bool A2 = false>
+template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
   // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
   // each): with two waves per SIMD one computes while the other waits on its
   // loads (measured: 5 % faster for bf16, 17 % for fp8 than four waves).
-  // MXFP4 weights keep four (their scale loads and expansion registers).
-  static constexpr int BIG_WM = WQ ? 2 : 4;
+  // MXFP4 weights and blockwise FP8 keep four (their scale loads, expansion
+  // registers, k-block sums).
+  static constexpr int BIG_WM = (WQ || BS) ? 2 : 4;
   //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
-  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2>;
-  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2>;
-  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8, A2>;
-  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8, A2>;
-  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8, A2>;
-  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8, A2>;
+  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2, BS>;
+  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2, BS>;
+  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8, A2, BS>;
+  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8, A2, BS>;
+  using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8, A2, BS>;
+  using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8, A2, BS>;
   // the same tile in eight waves (2 x 4) when no split is possible: the
   // FP8 and MXFP4 weight streams gain from the second wave per SIMD (MXFP4
   // GEMM2 of the DeepSeek shape 12 % faster) what fragment skipping saves
-  using WideP  = TileCfg<128, 256, 2, 4, S3, false, WQ, 1, F8, A2>;
-  using WidePG = TileCfg<128, 256, 2, 4, S3, true, WQ, 1, F8, A2>;
-  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ, 8, F8, A2>;
-  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ, 8, F8, A2>;
+  using WideP  = TileCfg<128, 256, 2, 4, S3, false, WQ, 1, F8, A2, BS>;
+  using WidePG = TileCfg<128, 256, 2, 4, S3, true, WQ, 1, F8, A2, BS>;
+  using Thin  = TileCfg<32, 256, 1, 4, 4, false, WQ, 8, F8, A2, BS>;
+  using ThinG = TileCfg<32, 256, 1, 4, 4, true, WQ, 8, F8, A2, BS>;
 };
 
 // Tile shape from the mean rows per local expert (the host cannot see the
@@ -1159,16 +1254,19 @@ struct Configs {
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
 //   < 16    decode: short tiles with split reductions.
-template <bool WQ, bool F8, bool A2 = false>
+template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
-  using C = Configs<WQ, F8, A2>;
+  using C = Configs<WQ, F8, A2, BS>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
   // can this call split its reductions (two fp32 slices in the workspace)?
   const int64_t slice = g.R_pad * (g.gated ? 2 * int64_t(g.N_out) : g.N_out) * 4;
   const bool may_split = g.split_ws != nullptr && g.R_pad <= 65535 &&
                          int64_t(g.split_ws_bytes) >= kSplitHeader + 2 * slice;
   // (FP8 x e2m1 GEMM1 streams fastest in four waves with fragment skipping)
-  const bool eight = (WQ || F8) && !may_split && !(WQ && F8 && g.gated);
+  // (blockwise FP8 always: in the one-wave-row tile its four row fragments'
+  // k-block sums and block scales beside the accumulators do not fit in
+  // registers)
+  const bool eight = BS || ((WQ || F8) && !may_split && !(WQ && F8 && g.gated));
   // (two-term activations: always the eight-wave tile in that range; with one
   // wave row their doubled A fragments would not fit in registers)
   if (g.gated) {
@@ -1210,6 +1308,7 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
 
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
+  if (g.a_scales && g.a_ld > 0) return launch_fmt<false, true, false, true>(g, max_rows, s);
   if (g.a_scales && g.a_terms == 2) return launch_fmt<true, true, true>(g, max_rows, s);
   if (g.a_scales)
     return g.w_mxfp4 ? launch_fmt<true, true>(g, max_rows, s) : launch_fmt<false, true>(g, max_rows, s);

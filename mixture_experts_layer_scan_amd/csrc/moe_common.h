@@ -126,11 +126,16 @@ struct GemmArgs {
   const float* a_scales = nullptr;  // fp8 activations: fp32 [R_pad], one per row
   bool w_mxfp4 = false;             // with fp8 activations: MXFP4 weights (else FP8)
   int a_terms = 1;                  // 2: two-term fp8 activations [R_pad, 2K] (MXFP4 weights)
-  // gathered activations (bf16): a holds a_T token rows [a_T, K] and permuted
-  // row r reads token a_inv[r] / a_k (a_inv: the permute's inverse map)
+  // gathered activations (bf16, FP8 or two-term FP8 with one scale per row):
+  // a holds a_T token rows [a_T, K] and permuted row r reads token
+  // a_inv[r] / a_k (a_inv: the permute's inverse map), with that token's scale
   const int32_t* a_inv = nullptr;
   int a_k = 1;
   int64_t a_T = 0;
+  // > 0: blockwise FP8 (FP8 weights): a_scales holds one scale per row and
+  // 128 k, k-block-major [K / 128][a_ld]; w_scales one per 128 x 128 weight
+  // block, [E_l][N_total / 128][K / 128]
+  int64_t a_ld = 0;
 };
 
 // Scratch bytes with which a grouped GEMM of R_pad rows may split its
@@ -167,9 +172,15 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int H, const float* static_scale,
                                const float* mult, const int32_t* row_count, void* q,
                                float* scales, hipStream_t s, int terms = 1);
+// groups > 0: blockwise scales, group-major [groups, T] in and [groups, R_pad] out
 hipError_t launch_gather_fp8_rows(const void* q, const float* scales, const int32_t* map,
                                   int64_t T, int k, int H, void* q_perm, float* scales_perm,
-                                  hipStream_t s);
+                                  hipStream_t s, int groups = 0, int64_t R_pad = 0);
+// Blockwise FP8 rows: codes [rows, H] and one scale per row and group of 128
+// elements, stored group-major: scales[g * ld + r] (ld >= rows).
+hipError_t launch_quantize_fp8_groups(const void* x, int64_t rows, int H,
+                                      const int32_t* row_count, void* q, float* scales,
+                                      int64_t ld, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v0, int32_t step, hipStream_t s);
 hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t s);
 

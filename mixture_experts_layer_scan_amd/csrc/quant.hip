@@ -22,6 +22,8 @@
 // then the 64 codes of q2.
 #include "moe_common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -131,6 +133,53 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_rows_kernel(
   }
 }
 
+// Blockwise FP8 (one scale per row and group of 128 consecutive elements,
+// the per-token activation groups of block-scaled FP8): the per-row rule
+// above applied to each group alone.  16 lanes take a group, 8 elements
+// (one 16-byte chunk) each, so a wave quantizes 4 groups at once; the group
+// maximum is a 16-lane reduction.  Scales are stored group-major,
+// scales[g * ld + r] (the GEMM reads the scales of consecutive rows of one
+// group together); rows at or past *row_count (when given) are skipped.
+constexpr int kGroup = 128;
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_fp8_groups_kernel(
+    const uint4* __restrict__ x, int64_t rows, int H8, const int32_t* __restrict__ row_count,
+    uint2* __restrict__ q, float* __restrict__ scales, int64_t ld) {
+  const int64_t n = row_count ? min(static_cast<int64_t>(*row_count), rows) : rows;
+  const int groups = H8 / (kGroup / 8);
+  const int lane = lane_id();
+  const int sub = lane & 15;              // chunk of the group
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  // group index gi = wave * 4 + lane / 16 (row-major over (row, group))
+  for (int64_t gi0 = wave * 4; gi0 < n * groups; gi0 += waves * 4) {
+    const int64_t gi = gi0 + (lane >> 4);
+    const bool on = gi < n * groups;     // uniform per 16 lanes
+    const int64_t r = on ? gi / groups : 0;
+    const int g = on ? static_cast<int>(gi - r * groups) : 0;
+    const int64_t c = r * H8 + g * (kGroup / 8) + sub;
+    float v[8];
+    chunk_values(on ? x[c] : uint4{0, 0, 0, 0}, nullptr, 1.0f, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    if (amax == 0.0f) amax = 448.0f;
+    const float inv = 448.0f / amax;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_rne(clamp448(v[i] * inv)) << (8 * i);
+      hi |= e4m3_rne(clamp448(v[4 + i] * inv)) << (8 * i);
+    }
+    if (on) {
+      q[c] = uint2{lo, hi};
+      if (sub == 0) scales[g * ld + r] = amax / 448.0f;
+    }
+  }
+}
+
 // Dispatch of quantized rows: q_perm[map[t, j]] = q[t] (16 bytes at a time),
 // scales_perm[map[t, j]] = scales[t].
 __global__ __launch_bounds__(256) void gather_fp8_rows_kernel(const uint4* __restrict__ q,
@@ -138,7 +187,9 @@ __global__ __launch_bounds__(256) void gather_fp8_rows_kernel(const uint4* __res
                                                               const int32_t* __restrict__ map,
                                                               int64_t T, int k, int H16,
                                                               uint4* __restrict__ q_perm,
-                                                              float* __restrict__ scales_perm) {
+                                                              float* __restrict__ scales_perm,
+                                                              int groups, int64_t ld_src,
+                                                              int64_t ld_dst) {
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     const int32_t* mt = map + t * k;
     const uint4* src = q + t * H16;
@@ -149,9 +200,18 @@ __global__ __launch_bounds__(256) void gather_fp8_rows_kernel(const uint4* __res
         if (r >= 0) q_perm[static_cast<int64_t>(r) * H16 + c] = v;
       }
     }
-    if (threadIdx.x < k) {
-      const int32_t r = mt[threadIdx.x];
-      if (r >= 0) scales_perm[r] = scales[t];
+    if (groups == 0) {
+      if (threadIdx.x < k) {
+        const int32_t r = mt[threadIdx.x];
+        if (r >= 0) scales_perm[r] = scales[t];
+      }
+    } else {
+      // group-major scales: scales_perm[g * ld_dst + r] = scales[g * ld_src + t]
+      for (int i = threadIdx.x; i < k * groups; i += blockDim.x) {
+        const int j = i / groups, g = i - j * groups;
+        const int32_t r = mt[j];
+        if (r >= 0) scales_perm[g * ld_dst + r] = scales[g * ld_src + t];
+      }
     }
   }
 }
@@ -171,12 +231,25 @@ hipError_t launch_quantize_fp8(const void* x, int64_t rows, int H, const float* 
 
 hipError_t launch_gather_fp8_rows(const void* q, const float* scales, const int32_t* map,
                                   int64_t T, int k, int H, void* q_perm, float* scales_perm,
-                                  hipStream_t s) {
+                                  hipStream_t s, int groups, int64_t R_pad) {
   if (T <= 0) return hipSuccess;
   const int64_t blocks = T < 8192 ? T : 8192;
   hipLaunchKernelGGL(gather_fp8_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      s, static_cast<const uint4*>(q), scales, map, T, k, H / 16,
-                     static_cast<uint4*>(q_perm), scales_perm);
+                     static_cast<uint4*>(q_perm), scales_perm, groups, T, R_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_groups(const void* x, int64_t rows, int H,
+                                      const int32_t* row_count, void* q, float* scales,
+                                      int64_t ld, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t groups = rows * (H / kGroup);
+  const int64_t waves = (groups + 3) / 4;
+  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 8192);
+  hipLaunchKernelGGL(quantize_fp8_groups_kernel, dim3(static_cast<unsigned>(blocks)),
+                     dim3(kQuantThreads), 0, s, static_cast<const uint4*>(x), rows, H / 8,
+                     row_count, static_cast<uint2*>(q), scales, ld);
   return hipGetLastError();
 }
 

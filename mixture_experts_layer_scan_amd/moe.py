@@ -17,8 +17,8 @@ import torch
 from ._lib import MoeLayerOptionsC, MoeWeightsC, lib
 
 SOFTMAX, SIGMOID = 0, 1
-DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4, DTYPE_FP8_E4M3 = 0, 1, 2, 3
-QUANT_NONE, QUANT_FP8, QUANT_FP8X2 = 0, 1, 2
+DTYPE_BF16, DTYPE_F32, DTYPE_MXFP4, DTYPE_FP8_E4M3, DTYPE_FP8_BLOCK = 0, 1, 2, 3, 4
+QUANT_NONE, QUANT_FP8, QUANT_FP8X2, QUANT_FP8_BLOCK = 0, 1, 2, 3
 ACT_SILU, ACT_GELU = 0, 1
 _ACT_NAMES = {"silu": ACT_SILU, "gelu": ACT_GELU}
 
@@ -58,12 +58,15 @@ def _act(activation) -> int:
 
 def _quant(fp8) -> int:
     """act_quant of moe_layer_options: fp8 False (bf16 activations), True (FP8
-    per token) or "x2" (two-term FP8 of the bf16 activations, MXFP4 weights)."""
+    per token), "x2" (two-term FP8 of the bf16 activations, MXFP4 weights) or
+    "block" (blockwise FP8 per 128-element group, block-scaled FP8 weights)."""
     if fp8 == "x2":
         return QUANT_FP8X2
+    if fp8 == "block":
+        return QUANT_FP8_BLOCK
     if fp8 in (False, True):
         return QUANT_FP8 if fp8 else QUANT_NONE
-    raise ValueError(f"fp8 must be False, True or 'x2' (got {fp8!r})")
+    raise ValueError(f"fp8 must be False, True, 'x2' or 'block' (got {fp8!r})")
 
 
 def _options(activation=ACT_SILU, activation_clamp: Optional[float] = None,
@@ -120,8 +123,10 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
 
 class Weights:
     """Expert weights of one GEMM: bf16 [E_l, N, K]; MXFP4 packed uint8
-    [E_l, N, K/2] with uint8 E8M0 scales [E_l, N, K/32]; or FP8 E4M3 codes
-    (uint8 or float8_e4m3fn) [E_l, N, K] with float32 scales [E_l, N]."""
+    [E_l, N, K/2] with uint8 E8M0 scales [E_l, N, K/32]; FP8 E4M3 codes
+    (uint8 or float8_e4m3fn) [E_l, N, K] with float32 scales [E_l, N]; or
+    block-scaled FP8 codes [E_l, N, K] with float32 scales [E_l, N/128, K/128]
+    (one per 128 x 128 block)."""
 
     def __init__(self, data: torch.Tensor, scales: Optional[torch.Tensor] = None):
         if data.dtype == torch.float8_e4m3fn:
@@ -129,6 +134,13 @@ class Weights:
         if scales is None:
             _need(data, "weights", torch.bfloat16)
             self.dtype = DTYPE_BF16
+        elif scales.dtype == torch.float32 and scales.dim() == 3:
+            _need(data, "weights", torch.uint8)
+            if data.dim() != 3 or data.shape[1] % 128 or data.shape[2] % 128:
+                raise ValueError("block-scaled FP8 weights need N and K multiples of 128")
+            _need(scales, "scales", torch.float32,
+                  (data.shape[0], data.shape[1] // 128, data.shape[2] // 128), data.device)
+            self.dtype = DTYPE_FP8_BLOCK
         elif scales.dtype == torch.float32:
             _need(data, "weights", torch.uint8)
             _need(scales, "scales", torch.float32, tuple(data.shape[:2]), data.device)
@@ -365,6 +377,163 @@ def moe_grouped_gemm2_fp8(h_perm: torch.Tensor, h_scales: torch.Tensor, offsets:
     _check(lib().moe_grouped_gemm2_fp8(
         h_perm.data_ptr(), h_scales.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
         y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_fp8")
+    return y
+
+
+def moe_grouped_gemm1_act_fp8_gathered(xq: torch.Tensor, x_scales: torch.Tensor,
+                                       inv: torch.Tensor, k: int, offsets: torch.Tensor,
+                                       w1: Weights, I: int, terms: int = 1,
+                                       h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                                       activation_clamp: Optional[float] = None, stream=None,
+                                       split: bool = True,
+                                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP8 GEMM1 on rows read from the quantized tokens: permuted row r is
+    xq[inv[r] // k] with scale x_scales[inv[r] // k] (xq [T, H * terms]) -> bf16
+    [R_pad, I], R_pad = inv's length."""
+    _need(xq, "xq", torch.uint8)
+    if xq.dim() != 2 or terms not in (1, 2):
+        raise ValueError("xq must be [T, H * terms], terms 1 or 2")
+    T = xq.shape[0]
+    H = xq.shape[1] // terms
+    dev = xq.device
+    _need(x_scales, "x_scales", torch.float32, (T,), dev)
+    _need(inv, "inv", torch.int32, device=dev)
+    R_pad = inv.numel()
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_fp8_gathered(
+        xq.data_ptr(), x_scales.data_ptr(), terms, inv.data_ptr(), T, k, offsets.data_ptr(),
+        w1.E_l, R_pad, H, I, w1.ref(), _act(activation),
+        0.0 if activation_clamp is None else float(activation_clamp), h.data_ptr(), ws, ws_bytes,
+        _stream(stream)), "moe_grouped_gemm1_act_fp8_gathered")
+    return h
+
+
+def moe_quantize_fp8_blockwise(x: torch.Tensor, row_count: Optional[torch.Tensor] = None,
+                               q: Optional[torch.Tensor] = None,
+                               scales: Optional[torch.Tensor] = None, stream=None):
+    """Blockwise FP8 E4M3 quantization of bf16 rows, one scale per row and group
+    of 128 elements -> (codes uint8 [rows, H], scales float32 [H/128, ld]
+    group-major, ld = rows unless `scales` gives a wider one)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, H]")
+    rows, H = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((H // 128, rows), dtype=torch.float32, device=dev)
+    _need(q, "q", torch.uint8, (rows, H), dev)
+    _need(scales, "scales", torch.float32, device=dev)
+    if scales.dim() != 2 or scales.shape[0] != H // 128 or scales.shape[1] < rows:
+        raise ValueError("scales must be [H/128, ld >= rows]")
+    if row_count is not None:
+        _need(row_count, "row_count", torch.int32, device=dev)
+    _check(lib().moe_quantize_fp8_blockwise(x.data_ptr(), rows, H, _ptr(row_count), q.data_ptr(),
+                                            scales.data_ptr(), scales.shape[1], _stream(stream)),
+           "moe_quantize_fp8_blockwise")
+    return q, scales
+
+
+def moe_permute_fp8_blockwise(topk_ids: torch.Tensor, E: int, xq: torch.Tensor,
+                              x_scales: torch.Tensor, E_l: Optional[int] = None,
+                              expert_map: Optional[torch.Tensor] = None,
+                              R_pad: Optional[int] = None, map: Optional[torch.Tensor] = None,
+                              offsets: Optional[torch.Tensor] = None,
+                              inv: Optional[torch.Tensor] = None,
+                              xq_perm: Optional[torch.Tensor] = None,
+                              xq_perm_scales: Optional[torch.Tensor] = None,
+                              want_inv: bool = True, stream=None):
+    """moe_permute on blockwise FP8 rows -> dict(map, offsets, inv, xq_perm uint8
+    [R_pad, H], xq_perm_scales float32 [H/128, R_pad], R_pad)."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    E_l = E if E_l is None else E_l
+    _need(xq, "xq", torch.uint8, device=dev)
+    if xq.dim() != 2 or xq.shape[0] != T:
+        raise ValueError("xq must be [T, H]")
+    H = xq.shape[1]
+    _need(x_scales, "x_scales", torch.float32, (H // 128, T), dev)
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty((E_l + 1,), dtype=torch.int32, device=dev)
+    if inv is None and want_inv and R_pad > 0:
+        inv = torch.empty((R_pad,), dtype=torch.int32, device=dev)
+    if xq_perm is None:
+        xq_perm = torch.empty((R_pad, H), dtype=torch.uint8, device=dev)
+    if xq_perm_scales is None:
+        xq_perm_scales = torch.empty((H // 128, R_pad), dtype=torch.float32, device=dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    _need(offsets, "offsets", torch.int32, (E_l + 1,), dev)
+    _need(xq_perm, "xq_perm", torch.uint8, (R_pad, H), dev)
+    _need(xq_perm_scales, "xq_perm_scales", torch.float32, (H // 128, R_pad), dev)
+    _check(lib().moe_permute_fp8_blockwise(topk_ids.data_ptr(), _ptr(expert_map), T, k, E, E_l,
+                                           xq.data_ptr(), x_scales.data_ptr(), H, R_pad,
+                                           map.data_ptr(), offsets.data_ptr(), _ptr(inv),
+                                           xq_perm.data_ptr(), xq_perm_scales.data_ptr(),
+                                           _stream(stream)), "moe_permute_fp8_blockwise")
+    return {"map": map, "offsets": offsets, "inv": inv, "xq_perm": xq_perm,
+            "xq_perm_scales": xq_perm_scales, "R_pad": R_pad}
+
+
+def moe_grouped_gemm1_act_fp8_blockwise(a_perm: torch.Tensor, a_scales: torch.Tensor,
+                                        offsets: torch.Tensor, w1: Weights, I: int,
+                                        h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                                        activation_clamp: Optional[float] = None, stream=None,
+                                        split: bool = True,
+                                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM1 + activation on blockwise FP8 rows (scales [H/128, R_pad]) and
+    block-scaled FP8 weights -> bf16 [R_pad, I]."""
+    _need(a_perm, "a_perm", torch.uint8)
+    R_pad, H = a_perm.shape
+    dev = a_perm.device
+    _need(a_scales, "a_scales", torch.float32, (H // 128, R_pad), dev)
+    _need(offsets, "offsets", torch.int32, (w1.E_l + 1,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    if h is None:
+        h = torch.empty((R_pad, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (R_pad, I), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm1_act_fp8_blockwise(
+        a_perm.data_ptr(), a_scales.data_ptr(), offsets.data_ptr(), w1.E_l, R_pad, H, I, w1.ref(),
+        _act(activation), 0.0 if activation_clamp is None else float(activation_clamp),
+        h.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_fp8_blockwise")
+    return h
+
+
+def moe_grouped_gemm2_fp8_blockwise(h_perm: torch.Tensor, h_scales: torch.Tensor,
+                                    offsets: torch.Tensor, w2: Weights, H: int,
+                                    y: Optional[torch.Tensor] = None, stream=None,
+                                    split: bool = True,
+                                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM2 on blockwise FP8 rows (scales [I/128, R_pad]) and block-scaled FP8
+    weights -> bf16 [R_pad, H]."""
+    _need(h_perm, "h_perm", torch.uint8)
+    R_pad, I = h_perm.shape
+    dev = h_perm.device
+    _need(h_scales, "h_scales", torch.float32, (I // 128, R_pad), dev)
+    _need(offsets, "offsets", torch.int32, (w2.E_l + 1,), dev)
+    if w2.N != H or w2.K != I:
+        raise ValueError(f"w2 must be [E_l, H={H}, I={I}]")
+    if y is None:
+        y = torch.empty((R_pad, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (R_pad, H), dev)
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, H, False, split, dev, stream, workspace)
+    _check(lib().moe_grouped_gemm2_fp8_blockwise(
+        h_perm.data_ptr(), h_scales.data_ptr(), offsets.data_ptr(), w2.E_l, R_pad, I, H, w2.ref(),
+        y.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm2_fp8_blockwise")
     return y
 
 

@@ -15,7 +15,8 @@ from typing import Optional
 import numpy as np
 
 from . import (TID_LOGITS, TID_W1, TID_W2, TID_WS1, TID_WS2, TID_X, biased_logits,
-               fp8_quantize_rows, mxfp4_quantize, normal_bf16, normal_f32, zipf_log_bias)
+               fp8_quantize_blocks, fp8_quantize_rows, mxfp4_quantize, normal_bf16, normal_f32,
+               zipf_log_bias)
 
 SOFTMAX, SIGMOID = 0, 1
 
@@ -40,6 +41,8 @@ class MoeConfig:
                                     # unless mxfp4
     fp8x2: bool = False             # bf16 activations carried as two FP8 E4M3 terms
                                     # (MXFP4 weights)
+    fp8_block: bool = False         # blockwise FP8: activations per 128-element group,
+                                    # weights per 128 x 128 block
     zipf_s: float = 0.0             # Zipf exponent of the logit bias (0: none)
     deferred: bool = False
 
@@ -81,8 +84,14 @@ DEEPSEEK_MXFP4_X2 = MoeConfig("deepseekv3_mxfp4_x2act_2048tok", T=2048, H=7168, 
                               k=8, score=SIGMOID, renormalize=True, rsf=2.5, seed=5, mxfp4=True,
                               fp8x2=True)
 
+# blockwise FP8 (128 x 128 weight blocks, 128-element activation groups, as
+# DeepSeek-V3 stores its weights) on the DeepSeek-V3 routed shape
+DEEPSEEK_FP8_BLOCK = MoeConfig("deepseekv3_fp8block_2048tok", T=2048, H=7168, I=2048, E=256, k=8,
+                               score=SIGMOID, renormalize=True, rsf=2.5, seed=3, fp8_block=True)
+
 ALL = {c.name: c for c in (TINY, MIXTRAL, DEEPSEEK, EP_DECODE, DEEPSEEK_MXFP4, MIXTRAL_FP8,
-                           DEEPSEEK_FP8, DEEPSEEK_MXFP4_FP8, DEEPSEEK_MXFP4_X2)}
+                           DEEPSEEK_FP8, DEEPSEEK_MXFP4_FP8, DEEPSEEK_MXFP4_X2,
+                           DEEPSEEK_FP8_BLOCK)}
 
 EP_DECODE_BATCHES = (1, 8, 64)
 EP_DECODE_DRAWS = 16
@@ -126,6 +135,10 @@ def make_weights(cfg: MoeConfig):
     if cfg.mxfp4:
         w["w1_q"], w["w1_s"] = mxfp4_quantize(w["w1"])
         w["w2_q"], w["w2_s"] = mxfp4_quantize(w["w2"])
+        del w["w1"], w["w2"]
+    elif cfg.fp8_block:
+        w["w1_q"], w["w1_s"] = fp8_quantize_blocks(w["w1"])
+        w["w2_q"], w["w2_s"] = fp8_quantize_blocks(w["w2"])
         del w["w1"], w["w2"]
     elif cfg.fp8:
         w["w1_q"], w["w1_s"] = fp8_quantize_rows(w["w1"])

@@ -261,7 +261,12 @@ def test_fp8_errors(L):
 
     def call(w=_w(FP8, P, P), opts=None, T=16, H=128, I=256):
         return u(P, P, T, H, I, 8, 8, 2, 0, 1, 1.0, None, w, w, opts, 32, P, P, P, P, 1 << 30, None)
-    assert call(opts=_opts(quant=1, batched=16)) == UNSUPPORTED
+    # FP8 in the batched layout: R_pad must hold E_l * capacity rows
+    assert call(opts=_opts(quant=1, batched=16)) == SIZE
+    # blockwise FP8: block-scaled weights only, both ways
+    assert call(opts=_opts(quant=3)) == INVALID                     # per-channel FP8 weights
+    assert call(w=_w(4, P, P), opts=_opts(quant=1)) == INVALID       # block weights, per-row acts
+    assert call(w=_w(4, P, P), opts=_opts(quant=3), H=192) == INVALID  # H not a multiple of 128
     assert call(opts=_opts(quant=7)) == UNSUPPORTED
     assert call(w=_w(), opts=_opts(quant=1)) == INVALID          # bf16 weights
     assert call(opts=None) == INVALID                            # FP8 weights, no quantization

@@ -299,3 +299,92 @@ def test_fp8_full_size(cfg):
     assert len(np.unique(ids[toks])) == cfg.E
     assert e_t.max() < TOL
     assert rel_fro(got, ref["out"]) < TOL
+
+
+@pytest.mark.parametrize("wfmt", ["fp8", "mxfp4", "x2"])
+@pytest.mark.parametrize("T,split", [(3, True), (40, True), (40, False), (300, False)])
+def test_fp8_gemm1_gathered_equals_gather_then_gemm1(T, split, wfmt):
+    """moe_grouped_gemm1_act_fp8_gathered(xq, scales, inv) is moe_permute_fp8's
+    gather followed by the FP8 GEMM1, bit for bit: per-row FP8 with FP8 and
+    with MXFP4 weights, two-term rows with MXFP4 weights; decode tiles with and
+    without split reductions and a wider batch; NaN codes in the unread padding
+    rows of the gathered input."""
+    E, E_l, k, H, I = 32, 8, 4, 512, 256
+    x = synth.normal_bf16(160 + T, 0, (T, H))
+    logits = synth.normal_f32(160 + T, 1, (T, E))
+    logits[np.arange(T), 8 + np.arange(T) % 8] += 5.0   # every token has a local route
+    emap = np.full(E, -1, dtype=np.int32)
+    emap[8:16] = np.arange(8, dtype=np.int32)
+    w1 = synth.normal_bf16(160 + T, 2, (E_l, 2 * I, H), std=1 / np.sqrt(H))
+    if wfmt == "fp8":
+        q, s = synth.fp8_quantize_rows(w1)
+    else:
+        q, s = synth.mxfp4_quantize(w1)
+    W1 = moe.Weights(dev(q), dev(s))
+    terms = 2 if wfmt == "x2" else 1
+    xd = dev_bf16(x)
+    xq, xs = moe.moe_quantize_fp8x2(xd) if terms == 2 else moe.moe_quantize_fp8(xd)
+    ids, _ = moe.moe_route_topk(dev(logits), k, moe.SIGMOID)
+    p = moe.moe_permute_fp8(ids, E, xq, xs, E_l, dev(emap))
+    R_l = int(p["offsets"][-1].item())
+    p["xq_perm"][R_l:] = 0x7F
+    if terms == 2:
+        h_ref = moe.moe_grouped_gemm1_act_fp8x2(p["xq_perm"], p["xq_perm_scales"], p["offsets"],
+                                                W1, I, split=split)
+    else:
+        h_ref = moe.moe_grouped_gemm1_act_fp8(p["xq_perm"], p["xq_perm_scales"], p["offsets"],
+                                              W1, I, split=split)
+    h = moe.moe_grouped_gemm1_act_fp8_gathered(xq, xs, p["inv"], k, p["offsets"], W1, I,
+                                               terms=terms, split=split)
+    torch.cuda.synchronize()
+    assert R_l > 0
+    assert np.array_equal(host_bf16_bits(h)[:R_l], host_bf16_bits(h_ref)[:R_l])
+
+
+@pytest.mark.parametrize("mode", ["fp8", "x2", "block"])
+def test_fp8_batched_layout(mode):
+    """FP8, two-term and blockwise FP8 activations in the batched experts
+    format: with a capacity of T, the fused layer equals the oracle's per token
+    and the standard layout's to rounding, and the deferred form's map is the
+    oracle's batched map; with a smaller capacity the dropped routes are
+    missing from the output exactly as in the oracle's kept-route sum."""
+    T, H, I, E, k = 96, 512, 256, 8, 2
+    kw = {"fp8": {"fp8": True}, "x2": {"mxfp4": True, "fp8x2": True},
+          "block": {"fp8_block": True}}[mode]
+    cfg = configs.MoeConfig("fb_" + mode, T=T, H=H, I=I, E=E, k=k, score=configs.SOFTMAX,
+                            renormalize=True, rsf=1.0, seed=170, **kw)
+    x, logits = configs.make_activations(cfg)
+    logits[:, 1] += 2.5       # expert 1 takes most tokens
+    w = configs.make_weights(cfg)
+    W1, W2 = _upload(w)
+    fp8 = {"fp8": True, "x2": "x2", "block": "block"}[mode]
+    args = (dev(logits), dev_bf16(x), W1, W2, k)
+    std = moe.moe_fused_experts(*args, fp8=fp8)
+    bat = moe.moe_fused_experts(*args, fp8=fp8, batched_max_tokens=T)
+    y, ew, m = moe.moe_fused_experts_unfinalized(*args, fp8=fp8, batched_max_tokens=T)
+    M = 24
+    dropped = moe.moe_fused_experts(*args, fp8=fp8, batched_max_tokens=M)
+    torch.cuda.synchronize()
+    if mode == "block":
+        Wo1 = oracle.Weights(w["w1_q"], w["w1_s"], block=True)
+        Wo2 = oracle.Weights(w["w2_q"], w["w2_s"], block=True)
+    elif mode == "x2":
+        Wo1, Wo2 = oracle.Weights(w["w1_q"], w["w1_s"]), oracle.Weights(w["w2_q"], w["w2_s"])
+    else:
+        Wo1 = oracle.Weights(w["w1_q"], w["w1_s"].reshape(-1))
+        Wo2 = oracle.Weights(w["w2_q"], w["w2_s"].reshape(-1))
+    ref = oracle.moe_tokens(x, logits, Wo1, Wo2, I, k, cfg.score, True, 1.0, fp8=fp8)
+    got = host_f64(bat)
+    # (per token: a code flip where the kernel's and the oracle's bf16 h
+    # differ in one ulp moves that row by 1-2 %; pooled the bar is 1e-2)
+    assert per_row_rel(got, ref["out"]).max() < 3e-2
+    assert rel_fro(got, ref["out"]) < TOL
+    assert rel_fro(got, host_f64(std)) < TOL
+    bmap, cnt = oracle.permute_batched(ref["ids"], E, E, T)
+    assert np.array_equal(m.cpu().numpy(), bmap)
+    dmap, dcnt = oracle.permute_batched(ref["ids"], E, E, M)
+    assert dcnt.max() > M
+    kept = (dmap >= 0)[:, :, None]
+    want = np.sum(np.where(kept, ref["weights"][:, :, None] * ref["y_routes"], 0.0), axis=1)
+    assert rel_fro(host_f64(dropped), want) < TOL
+    assert rel_fro(want, ref["out"]) > 5 * TOL
