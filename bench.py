@@ -327,9 +327,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     fin_stage = "finalize_add_rmsnorm" if args.fused_tail else "finalize"
-    stages = (["route", "quantize", "permute", "gemm1", "quantize_h", "gemm2"] if quant
-              else ["route", "permute", "gemm1", "gemm2"]) \
-        + (["shared"] if cfg.shared_I else []) + [fin_stage]
+    stages = None  # set below, once the dispatch form is known
     act_kw = dict(activation=args.activation, activation_clamp=args.activation_clamp)
     w_in = args.router_weight_on_input
 
@@ -344,6 +342,26 @@ def main():
                   and not args.gather_kernel)
     inv_buf = (torch.empty((R_pad,), dtype=torch.int32, device=dev)
                if gathered or gathered_q else None)
+    # a batch of at most 16 tokens routes and permutes in one launch
+    merged = (gathered or gathered_q) and P <= 16
+    first = ["route_permute"] if merged else ["route"]
+    stages = (first + ["quantize"] + ([] if merged else ["permute"])
+              + ["gemm1", "quantize_h", "gemm2"] if quant
+              else first + ([] if merged else ["permute"]) + ["gemm1", "gemm2"]) \
+        + (["shared"] if cfg.shared_I else []) + [fin_stage]
+
+    def route_and_map(ld, sl, st):
+        """Router and permute map of a small batch in one call (gathered GEMM1)."""
+        moe.moe_route_permute(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, El, emap_d, R_pad,
+                              ids[sl], wts[sl], pmap[sl], offsets, inv_buf, stream=st)
+
+    def quantize_tokens(sl, st):
+        if cfg.fp8x2:
+            moe.moe_quantize_fp8x2(xd_cur[0][sl], wts[sl] if w_in else None, xq[sl], xs[sl],
+                                   stream=st)
+        else:
+            moe.moe_quantize_fp8(xd_cur[0][sl], None, wts[sl] if w_in else None, xq[sl], xs[sl],
+                                 stream=st)
 
     def permute(sl, st):
         if cfg.fp8_block:
@@ -353,13 +371,8 @@ def main():
                                           pmap[sl], offsets, None, xq_perm, ps, want_inv=False,
                                           stream=st)
             return
-        if cfg.fp8x2:
-            moe.moe_quantize_fp8x2(xd_cur[0][sl], wts[sl] if w_in else None, xq[sl], xs[sl],
-                                   stream=st)
-        elif cfg.fp8:
-            moe.moe_quantize_fp8(xd_cur[0][sl], None, wts[sl] if w_in else None, xq[sl], xs[sl],
-                                 stream=st)
         if quant:
+            quantize_tokens(sl, st)
             mark_cur[0]("permute")
             if gathered_q:
                 moe.moe_permute(ids[sl], E, El, emap_d, None, R_pad, pmap[sl], offsets, inv_buf,
@@ -439,6 +452,9 @@ def main():
         xd, ld = dev_draws[d]
         xd_cur[0], mark_cur[0] = xd, (lambda name: None)
         sl = slice(t0, t0 + n)
+        if merged:
+            route_and_map(ld, sl, stream)
+            return
         moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
                            stream)
         permute(sl, stream)
@@ -454,11 +470,18 @@ def main():
         for t0, n in chunks:
             sl = slice(t0, t0 + n)
             gsl[0] = sl
-            mark("route")
-            moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl], wts[sl],
-                               st)
-            mark("quantize" if quant else "permute")
-            permute(sl, st)
+            if merged:
+                mark("route_permute")
+                route_and_map(ld, sl, st)
+                if quant:
+                    mark("quantize")
+                    quantize_tokens(sl, st)
+            else:
+                mark("route")
+                moe.moe_route_topk(ld[sl], k, cfg.score, cfg.renormalize, cfg.rsf, ids[sl],
+                                   wts[sl], st)
+                mark("quantize" if quant else "permute")
+                permute(sl, st)
             mark("gemm1")
             gemms(n, st)
             sh = None
@@ -527,6 +550,7 @@ def main():
         if graphs:
             if flush is not None:
                 evict_caches()
+                torch.cuda._sleep(HOST_AHEAD_CYCLES)  # the replay is submitted meanwhile
             events[i][1][0].record()
             graphs[i % len(graphs)].replay()
             events[i][1][1].record()

@@ -246,6 +246,23 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
                 int32_t* offsets, int32_t* inv, void* x_perm, const float* x_weights,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Router and Permute map in one call ([Router] followed by the permute of
+ * [Quantize-Dispatch], prepare() of page "modular_kernel.py"): the topk ids
+ * and weights of moe_route_topk, then the map, offsets and inverse map of
+ * moe_permute with x_perm = NULL (no rows are gathered: the gathered form of
+ * GEMM1 reads them through inv).  The results are those of the two calls.
+ * For T <= 16 both steps run in one kernel of one workgroup (each wave
+ * routes one token and keeps its local experts in on-chip memory, then the
+ * workgroup sorts them), which saves a launch on decode batches; larger
+ * batches launch the two kernels.
+ *   logits, topk_ids, topk_weights   as for moe_route_topk
+ *   expert_map, map, offsets, inv    as for moe_permute
+ * Limits: those of both calls. */
+int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score_fn,
+                      int32_t renormalize, float rsf, const int32_t* expert_map, int32_t E_l,
+                      int64_t R_pad, int32_t* topk_ids, float* topk_weights, int32_t* map,
+                      int32_t* offsets, int32_t* inv, void* stream);
+
 /* FP8 E4M3 quantization of bf16 rows (the quantize half of [Quantize-Dispatch];
  * prepare() of page "modular_kernel.py" with per_act_token_quant, or a static
  * a1_scale / a2_scale).  Per row, in fp32:

@@ -38,6 +38,8 @@ PROTOTYPES = {
                                           ctypes.POINTER(_sz)]),
     "moe_shared_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "moe_route_permute": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _i32, _i64,
+                                         _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _f32,

@@ -21,7 +21,8 @@ OUT = os.path.join(PKG, "libmoe_mi355x.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "finalize.hip", "quant.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "decode_gemm.hip", "finalize.hip",
+           "quant.hip"]
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -419,6 +419,34 @@ int moe_permute(const int32_t* topk_ids, const int32_t* expert_map, int64_t T, i
   return MOE_OK;
 }
 
+int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score_fn,
+                      int32_t renormalize, float rsf, const int32_t* expert_map, int32_t E_l,
+                      int64_t R_pad, int32_t* topk_ids, float* topk_weights, int32_t* map,
+                      int32_t* offsets, int32_t* inv, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown score function %d", score_fn);
+  MOE_CHECK(check_local(E, E_l));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(opt_ptr(inv, "inv"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(logits, "logits"));
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(topk_weights, "topk_weights"));
+    MOE_CHECK(need_ptr(map, "map"));
+  }
+  // offsets (and the inverse map's padding) are written even for T = 0
+  hipError_t e = moe::launch_route_permute(logits, T, E, k, score_fn, renormalize, rsf, topk_ids,
+                                           topk_weights, nullptr, expert_map, E_l, map, offsets,
+                                           inv, R_pad, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_permute");
+}
+
 int check_capacity(int32_t E_l, int32_t max_tokens) {
   if (max_tokens <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_tokens must be positive");
   if (int64_t(E_l) * max_tokens >= (int64_t(1) << 31))
@@ -982,9 +1010,21 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
                       int32_t* map_out, void* y_out, uint16_t* w_bf16_out, hipStream_t s) {
   int32_t* map = map_out ? map_out : b.map;
   void* y = y_out ? y_out : b.x_perm;
-  hipError_t e = moe::launch_route_topk(logits, T, E, k, score_fn, renormalize, rsf, b.ids, b.wts,
-                                        w_bf16_out, s);
-  if (e != hipSuccess) return hip_fail(e, "route");
+  // Rows in the standard layout: GEMM1 reads each permuted row straight from
+  // the token rows through the inverse map (no gather kernel, no x_perm write
+  // and re-read), while they fit one buffer descriptor's 4 GiB: bf16 rows
+  // unless the routing weight goes on them (the gather applies it); FP8 and
+  // two-term rows with their token's scale (the weight, top-1, was applied
+  // before quantizing); blockwise FP8 keeps the gather (its group scales are
+  // read per k-block by rows of the permuted order).
+  const int64_t token_row_bytes = o.fp8 ? int64_t(H) * o.terms : int64_t(H) * 2;
+  const bool gather_in_gemm = (o.fp8 ? !o.block : !o.weight_on_input) && o.batch_m == 0 &&
+                              T * token_row_bytes <= int64_t(0xFFFFFFFF);
+  // Router and permute map (one launch for a small batch)
+  hipError_t e = moe::launch_route_permute(logits, T, E, k, score_fn, renormalize, rsf, b.ids,
+                                           b.wts, w_bf16_out, expert_map, E_l, map, b.offsets,
+                                           gather_in_gemm ? b.inv : nullptr, b.rows, o.batch_m, s);
+  if (e != hipSuccess) return hip_fail(e, "route and permute");
   if (o.weight_on_input && w_bf16_out) {
     e = moe::launch_fill_u16(w_bf16_out, T * k, 0x3F80, s);  // bf16 1.0
     if (e != hipSuccess) return hip_fail(e, "unit weights");
@@ -1000,19 +1040,6 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
                                  nullptr, b.xq, b.xs, s, o.terms);
     if (e != hipSuccess) return hip_fail(e, "quantize");
   }
-  // Rows in the standard layout: GEMM1 reads each permuted row straight from
-  // the token rows through the inverse map (no gather kernel, no x_perm write
-  // and re-read), while they fit one buffer descriptor's 4 GiB: bf16 rows
-  // unless the routing weight goes on them (the gather applies it); FP8 and
-  // two-term rows with their token's scale (the weight, top-1, was applied
-  // before quantizing); blockwise FP8 keeps the gather (its group scales are
-  // read per k-block by rows of the permuted order).
-  const int64_t token_row_bytes = o.fp8 ? int64_t(H) * o.terms : int64_t(H) * 2;
-  const bool gather_in_gemm = (o.fp8 ? !o.block : !o.weight_on_input) && o.batch_m == 0 &&
-                              T * token_row_bytes <= int64_t(0xFFFFFFFF);
-  e = moe::launch_permute(b.ids, expert_map, T, k, E, E_l, map, b.offsets,
-                          gather_in_gemm ? b.inv : nullptr, b.rows, s, o.batch_m);
-  if (e != hipSuccess) return hip_fail(e, "permute");
   // (batched experts format: the quantized hidden rows are all E_l * capacity
   // rows, those past an expert's count never read; the standard layout
   // quantizes the offsets[E_l] local routes)

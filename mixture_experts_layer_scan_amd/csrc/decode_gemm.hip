@@ -1,0 +1,216 @@
+// Grouped GEMM for decode batches (bf16): the [Experts] GEMMs of vLLM's
+// modular fused-MoE kernel (apply(): GEMM1 with act(gate) * up, GEMM2) when
+// each local expert receives only a few rows.
+//
+// With a handful of rows per expert the GEMMs are weight streams: every
+// weight byte is read once and each feeds a few multiply-adds.  The tiled
+// kernel then needs a split reduction to give every compute unit a share of
+// one expert's weights, and each share is too short to fill its load
+// pipeline.  Here a work item is a slice of 16 weight rows of one expert over
+// the whole k-range (for GEMM1: 8 gate rows and the 8 matching up rows), so a
+// workgroup streams one long run of each row and no reduction kernel follows:
+//   - 8 waves split the k-range; lane l streams 16 contiguous bytes of weight
+//     row l % 16 per 32-k step (four lanes cover a row's 64-byte run), with
+//     5 steps of loads in flight (one for a k-range under 5 steps), and two
+//     workgroups share a compute unit;
+//   - the 16 x 16 x 32 bf16 MFMA takes the expert's rows (up to 16 per pass)
+//     as A and the 16 weight rows as B, so the sum over k happens in the
+//     matrix core and each lane keeps four fp32 sums;
+//   - the 8 waves' sums add up in LDS; GEMM1 pairs gate column j with up
+//     column j + 8 through a lane shuffle and applies the activation.
+// Rows come from the permuted activations, or (gathered form) from the token
+// rows through the permute's inverse map.  An expert with more than 16 rows
+// takes one pass per 16 (each pass re-reads the slice), so the host picks
+// this kernel only for batches whose experts see a few rows each.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kDecRows = 16;  // weight rows per slice, expert rows per pass
+constexpr int kDecMaxExperts = 1024;
+constexpr int kDecDeep = 5;   // 32-k steps of loads in flight per wave
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8_t*>(p);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int gated,
+    uint16_t* __restrict__ C, int act, float clamp, int batch_m, const int32_t* __restrict__ a_inv,
+    int a_k) {
+  __shared__ f32x4_t red[kDecWaves][kWave];
+  __shared__ int32_t s_exp[kDecMaxExperts];   // experts with rows, in order
+  __shared__ int32_t s_row0[kDecMaxExperts];  // their first row
+  __shared__ int32_t s_rows[kDecMaxExperts];  // their row count
+  __shared__ int32_t s_n;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int j = lane & 15;       // weight row in the slice (MFMA column)
+  const int kq = lane >> 4;      // 8-element k group of the 32-k step
+  const int N_total = gated ? 2 * N_out : N_out;
+  const int slices = gated ? N_out / 8 : N_out / kDecRows;
+  const int kw = K / kDecWaves;  // this wave's k-range: [w * kw, (w + 1) * kw)
+  const int nsteps = kw / 32;    // >= D
+  const int kind = act_kind(act, clamp);
+  const float cl = act_limit(clamp);
+
+  // The experts that have rows, compacted in order by wave 0 (every
+  // workgroup builds the same list), so the work items are only theirs.
+  if (w == 0) {
+    int n = 0;
+    for (int e0 = 0; e0 < E_l; e0 += kWave) {
+      const int e = e0 + lane;
+      int row0 = 0, rows = 0;
+      if (e < E_l) {
+        if (batch_m > 0) {
+          row0 = e * batch_m;
+          rows = min(offsets[e], batch_m);
+        } else {
+          row0 = offsets[e];
+          rows = offsets[e + 1] - row0;
+        }
+      }
+      const uint64_t has = __ballot(rows > 0);
+      if (rows > 0) {
+        const int at = n + __popcll(has & ((1ull << lane) - 1ull));
+        s_exp[at] = e;
+        s_row0[at] = row0;
+        s_rows[at] = rows;
+      }
+      n += __popcll(has);
+    }
+    if (lane == 0) s_n = n;
+  }
+  __syncthreads();
+  const int64_t items = static_cast<int64_t>(s_n) * slices;
+
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int xi = static_cast<int>(it / slices);
+    const int s = static_cast<int>(it - static_cast<int64_t>(xi) * slices);
+    const int e = s_exp[xi], row0 = s_row0[xi], rows = s_rows[xi];
+
+    const int wrow = gated ? (j < 8 ? 8 * s + j : N_out + 8 * s + (j - 8)) : kDecRows * s + j;
+    const uint16_t* wp =
+        W + (static_cast<int64_t>(e) * N_total + wrow) * K + w * kw + kq * 8;
+
+    for (int rg = 0; rg < rows; rg += kDecRows) {
+      // MFMA row j takes expert row rg + j; past the count it repeats the
+      // last row, whose products land only in output rows that are not stored
+      const int64_t pr = row0 + min(rg + j, rows - 1);
+      const int64_t src = a_inv ? a_inv[pr] / a_k : pr;
+      const uint16_t* ap = A + src * K + w * kw + kq * 8;
+
+      bf16x8_t bq[D], aq[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        bq[d] = load_bf16x8(wp + d * 32);
+        aq[d] = load_bf16x8(ap + d * 32);
+      }
+      f32x4_t acc = {};
+      int st = 0;
+      // steady state: consume D steps, load the D after them
+      for (; st + 2 * D <= nsteps; st += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
+          bq[d] = load_bf16x8(wp + (st + D + d) * 32);
+          aq[d] = load_bf16x8(ap + (st + D + d) * 32);
+        }
+      }
+      // the last D loaded steps and the rem < D after them
+      const int rem = nsteps - st - D;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
+        if (d < rem) {
+          bq[d] = load_bf16x8(wp + (st + D + d) * 32);
+          aq[d] = load_bf16x8(ap + (st + D + d) * 32);
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (d < rem) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
+
+      // the waves' sums over their k-ranges
+      red[w][lane] = acc;
+      __syncthreads();
+      if (w == 0) {
+        f32x4_t sum = red[0][lane];
+#pragma unroll
+        for (int ww = 1; ww < kDecWaves; ++ww) sum += red[ww][lane];
+        // lane holds rows 4 * kq + i (i < 4) of column j
+        if (gated) {
+          f32x4_t up;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) up[i] = __shfl(sum[i], lane + 8, kWave);
+          if (j < 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = rg + 4 * kq + i;
+              if (r >= rows) break;
+              float v;
+              if (kind == 0) v = gated_act_k<0>(sum[i], up[i], cl);
+              else if (kind == 1) v = gated_act_k<1>(sum[i], up[i], cl);
+              else v = gated_act_k<2>(sum[i], up[i], cl);
+              C[static_cast<int64_t>(row0 + r) * N_out + 8 * s + j] = f32_to_bf16(v);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = rg + 4 * kq + i;
+            if (r >= rows) break;
+            C[static_cast<int64_t>(row0 + r) * N_out + kDecRows * s + j] = f32_to_bf16(sum[i]);
+          }
+        }
+      }
+      __syncthreads();  // red is rewritten by the next pass
+    }
+  }
+}
+
+}  // namespace
+
+bool decode_gemm_fits(const GemmArgs& g) {
+  return g.a_scales == nullptr && g.w_scales == nullptr && g.K % (kDecWaves * 32) == 0 &&
+         (g.gated ? g.N_out % 8 == 0 : g.N_out % kDecRows == 0) && g.E_l > 0 &&
+         g.E_l <= kDecMaxExperts;
+}
+
+hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s) {
+  const int slices = g.gated ? g.N_out / 8 : g.N_out / kDecRows;
+  const int64_t items = static_cast<int64_t>(g.E_l) * slices;  // at most
+  // five 32-k steps in flight per wave when each wave's k-range has them
+  // (then two workgroups fit a compute unit: at most 128 registers a lane)
+  const bool deep = g.K / kDecWaves / 32 >= kDecDeep;
+  auto kern = deep ? decode_gemm_kernel<kDecDeep> : decode_gemm_kernel<1>;
+  // one resident wave of workgroups; work item i (slice i mod slices of the
+  // (i / slices)-th expert with rows) goes to workgroup i mod grid
+  static int occ[2] = {0, 0};
+  int& o = occ[deep ? 1 : 0];
+  if (o == 0) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(kern), kDecThreads, 0);
+    if (e != hipSuccess) return e;
+    o = n > 0 ? n : 1;
+  }
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * o;
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kDecThreads), 0, s,
+                     static_cast<const uint16_t*>(g.a), static_cast<const uint16_t*>(g.w),
+                     g.offsets, g.E_l, g.K, g.N_out, g.gated, static_cast<uint16_t*>(g.c), g.act,
+                     g.clamp, g.batch_m, g.a_inv, g.a_k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1254,10 +1254,15 @@ struct Configs {
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
 //   < 16    decode: short tiles with split reductions.
+constexpr int64_t kDecodeMeanRows = 16;
+
 template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ, F8, A2, BS>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
+  // bf16 decode batches: whole-k weight slices per workgroup, no split
+  if constexpr (!WQ && !F8)
+    if (mean_rows < kDecodeMeanRows && decode_gemm_fits(g)) return launch_decode_gemm(g, s);
   // can this call split its reductions (two fp32 slices in the workspace)?
   const int64_t slice = g.R_pad * (g.gated ? 2 * int64_t(g.N_out) : g.N_out) * 4;
   const bool may_split = g.split_ws != nullptr && g.R_pad <= 65535 &&

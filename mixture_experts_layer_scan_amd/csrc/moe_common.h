@@ -151,10 +151,26 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
 hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
                           hipStream_t s, int batch_m = 0);
+// Router and the permute map in one launch for T <= kRoutePermuteMaxT (one
+// workgroup, one token per wave); larger batches launch the router and the
+// permute kernels (the router then spreads its tokens over many compute
+// units: in one workgroup every further token per wave costs about 6 us).
+// Results equal launch_route_topk followed by launch_permute.
+constexpr int64_t kRoutePermuteMaxT = 16;
+hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int score_fn,
+                                int renormalize, float rsf, int32_t* ids, float* w,
+                                uint16_t* w_bf16, const int32_t* emap, int E_l, int32_t* map,
+                                int32_t* offsets, int32_t* inv, int64_t R_pad, int batch_m,
+                                hipStream_t s);
 // x_perm[map[t, j]] = x[t], or bf16(scale[t, j] * x[t]) when scale is given
 hipError_t launch_gather_rows(const void* x, const int32_t* map, int64_t T, int k, int H,
                               const float* scale, void* x_perm, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s);
+// Grouped GEMM for experts with a few rows each (bf16 weights and rows): one
+// workgroup per slice of 16 weight rows over the whole k-range, no split
+// reduction.  decode_gemm_fits: K a multiple of 256, N_out of 8 (gated) or 16.
+bool decode_gemm_fits(const GemmArgs& g);
+hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s);
 // w == NULL: every weight is 1 (the weights were applied to the inputs)
 hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
                            int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,

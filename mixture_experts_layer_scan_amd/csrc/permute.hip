@@ -3,16 +3,21 @@
 // producing the expanded_idx_to_permuted_idx map of vLLM's MoE output contract
 // (int32, -1 for an expert that is not local).
 //
-// Deterministic stable counting sort in one workgroup of 16 waves:
-//   - wave w owns a contiguous run of the expanded index x = t*k + j and walks
-//     it 64 routes at a time;
+// Deterministic stable counting sort (permute_core.h), one workgroup of 16
+// waves per 1024 routes (at most 256 workgroups), each placing the routes of
+// its own contiguous range of the expanded index x = t*k + j:
+//   - every workgroup first counts all routes per local expert with integer
+//     LDS atomics (their sums do not depend on the order), in total and
+//     before its range, so the workgroups never wait for one another;
+//   - wave w owns a contiguous run of the range and walks it 64 routes at a
+//     time, loading the expert ids (and their expert-map entries) of 16 such
+//     steps ahead with independent loads;
+//   - per-wave counts, a column scan over the 16 waves and a block scan over
+//     experts give every (wave, expert) pair its first output row;
 //   - inside a step, lanes with equal local expert find each other with a
-//     ballot per key bit (wave_match); the lowest such lane adds the group
-//     size to the wave's LDS histogram row, so no atomics are needed;
-//   - a column scan over the 16 wave rows and a block scan over experts give
-//     every (wave, expert) pair its first output row;
-//   - the second walk ranks each lane among its peers with a popcount of the
-//     lower-lane mask, so the order within an expert is ascending x.
+//     ballot per key bit (wave_match) and each takes the popcount of its
+//     lower-lane peers as its rank, so the order within an expert is
+//     ascending x.
 // Batched experts format (batch_m > 0): expert L owns rows [L * batch_m,
 // (L + 1) * batch_m); the same ranks place a route at L * batch_m + rank, or
 // -1 past the capacity, and `offsets` receives the per-expert counts.
@@ -20,103 +25,18 @@
 // to each of its (up to k) local slots with 16-byte accesses.  With
 // apply_router_weight_on_input (prepare() applies the routing weights to the
 // activations before dispatch) each slot receives bf16(w[t, j] * x[t]).
-#include "moe_common.h"
+#include "permute_core.h"
 
 namespace moe {
 namespace {
-
-constexpr int kPermuteThreads = 1024;
-constexpr int kPermuteWaves = kPermuteThreads / kWave;
-
-__device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids,
-                                            const int32_t* __restrict__ emap, int64_t x, int E,
-                                            int E_l) {
-  const int id = ids[x];
-  if (id < 0 || id >= E) return -1;
-  const int L = emap ? emap[id] : id;
-  return (L >= 0 && L < E_l) ? L : -1;
-}
 
 __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ emap, int64_t R, int E, int E_l,
     int32_t* __restrict__ map, int32_t* __restrict__ offsets, int32_t* __restrict__ inv,
     int64_t R_pad, int batch_m) {
   extern __shared__ int32_t smem[];
-  int32_t* hist = smem;                                // [waves][E_l]
-  int32_t* scratch = smem + kPermuteWaves * E_l;       // 16 ints
-  __shared__ int32_t s_total;
-  const int w = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-  for (int i = threadIdx.x; i < kPermuteWaves * E_l; i += kPermuteThreads) hist[i] = 0;
-  __syncthreads();
-
-  const int64_t per_wave = ((R + kPermuteWaves * kWave - 1) / (kPermuteWaves * kWave)) * kWave;
-  const int64_t beg = w * per_wave;
-  const int64_t end = (beg + per_wave < R) ? beg + per_wave : R;
-  const int nbits = 32 - __clz(E_l);  // keys L + 1 lie in [0, E_l]
-  int32_t* my_hist = hist + w * E_l;
-
-  // Walk 1: per-wave histogram.
-  for (int64_t base = beg; base < end; base += kWave) {
-    const int64_t x = base + lane;
-    const bool valid = x < end;
-    const int L = valid ? local_expert(ids, emap, x, E, E_l) : -1;
-    const uint64_t peers = wave_match(static_cast<uint32_t>(L + 1), valid, nbits);
-    if (valid && L >= 0 && (peers & lt_mask) == 0ull) my_hist[L] += __popcll(peers);
-  }
-  __syncthreads();
-
-  // Column scan over waves: hist[w][e] becomes the count of routes to e in
-  // waves before w; the per-expert totals go through a block scan.
-  int cnt_total = 0;
-  const int e = threadIdx.x;  // E_l <= kPermuteThreads
-  if (e < E_l) {
-    for (int ww = 0; ww < kPermuteWaves; ++ww) {
-      const int c = hist[ww * E_l + e];
-      hist[ww * E_l + e] = cnt_total;
-      cnt_total += c;
-    }
-  }
-  int total = 0;
-  const int start = block_exclusive_sum(e < E_l ? cnt_total : 0, scratch, &total);
-  if (e < E_l) {
-    const int base = batch_m > 0 ? e * batch_m : start;
-    offsets[e] = batch_m > 0 ? cnt_total : start;
-    for (int ww = 0; ww < kPermuteWaves; ++ww) hist[ww * E_l + e] += base;
-  }
-  if (threadIdx.x == 0) {
-    if (batch_m == 0) offsets[E_l] = total;
-    s_total = total;
-  }
-  __syncthreads();
-
-  // Walk 2: ranks, map and inverse map.
-  for (int64_t base = beg; base < end; base += kWave) {
-    const int64_t x = base + lane;
-    const bool valid = x < end;
-    const int L = valid ? local_expert(ids, emap, x, E, E_l) : -1;
-    const uint64_t peers = wave_match(static_cast<uint32_t>(L + 1), valid, nbits);
-    if (valid) {
-      if (L >= 0) {
-        const int slot = my_hist[L] + __popcll(peers & lt_mask);
-        if (batch_m > 0 && slot - L * batch_m >= batch_m) {
-          map[x] = -1;  // past the expert's capacity
-        } else {
-          map[x] = slot;
-          if (inv) inv[slot] = static_cast<int32_t>(x);
-        }
-      } else {
-        map[x] = -1;
-      }
-    }
-    // every lane has read its row of my_hist above before the leader adds
-    if (valid && L >= 0 && (peers & lt_mask) == 0ull) my_hist[L] += __popcll(peers);
-  }
-  if (inv) {
-    for (int64_t r = s_total + threadIdx.x; r < R_pad; r += kPermuteThreads) inv[r] = -1;
-  }
+  counting_sort(GlobalRoutes{ids, emap, E, E_l}, R, E_l, map, offsets, inv, R_pad, batch_m, smem,
+                static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
 }
 
 // x_perm[map[t, j], :] = x[t, :] for every local route of token t.
@@ -180,7 +100,7 @@ __global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
 hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, int k, int E,
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
                           hipStream_t s, int batch_m) {
-  const size_t lds = sizeof(int32_t) * (static_cast<size_t>(kPermuteWaves) * E_l + 16);
+  const size_t lds = sort_lds_bytes(E_l);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
@@ -188,8 +108,8 @@ hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, in
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermuteThreads), lds, s, ids, emap, T * k, E,
-                     E_l, map, offsets, inv, R_pad, batch_m);
+  hipLaunchKernelGGL(permute_kernel, dim3(sort_blocks(T * k)), dim3(kPermuteThreads), lds, s, ids,
+                     emap, T * k, E, E_l, map, offsets, inv, R_pad, batch_m);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@
 // Lane j keeps the j-th winner, so the k results end up in lanes 0..k-1 and
 // are stored with one coalesced write.  Selection compares fp32 logits only
 // (no arithmetic), so the chosen ids are exact.
-#include "moe_common.h"
+#include "permute_core.h"
 
 namespace moe {
 namespace {
@@ -56,16 +56,14 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   i = bi;
 }
 
+// Routes token t with the whole wave; returns the selected expert id in lanes
+// 0..k-1 (-1 in the other lanes).
 template <int EPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
-                                                         int64_t T, int E, int k, int score_fn,
-                                                         int renormalize, float rsf,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ w,
-                                                         uint16_t* __restrict__ w_bf16) {
+__device__ __forceinline__ int route_token(const float* __restrict__ logits, int64_t t, int E,
+                                           int k, int score_fn, int renormalize, float rsf,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           uint16_t* __restrict__ w_bf16) {
   const int lane = lane_id();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;  // whole wave leaves together
   const float* row = logits + t * E;
 
   float v[EPL];
@@ -130,6 +128,40 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     w[t * k + lane] = wt;
     if (w_bf16) w_bf16[t * k + lane] = f32_to_bf16(wt);
   }
+  return sel ? my_id : -1;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t T, int E, int k, int score_fn,
+                                                         int renormalize, float rsf,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w,
+                                                         uint16_t* __restrict__ w_bf16) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // whole wave leaves together
+  route_token<EPL>(logits, t, E, k, score_fn, renormalize, rsf, ids, w, w_bf16);
+}
+
+// Router and Permute of a small batch in one workgroup: wave w routes tokens
+// w, w + 16, ... and keeps their local experts in LDS, then the workgroup
+// runs the same counting sort as the permute kernel on them.  The map,
+// offsets and inverse map equal those of the two separate kernels.
+template <int EPL>
+__global__ __launch_bounds__(kPermuteThreads) void route_permute_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int score_fn, int renormalize,
+    float rsf, int32_t* __restrict__ ids, float* __restrict__ w, uint16_t* __restrict__ w_bf16,
+    const int32_t* __restrict__ emap, int E_l, int32_t* __restrict__ map,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ inv, int64_t R_pad, int batch_m) {
+  extern __shared__ int32_t smem[];
+  int32_t* s_local = smem + sort_lds_bytes(E_l) / sizeof(int32_t);  // [T * k]
+  const int lane = lane_id();
+  for (int64_t t = threadIdx.x / kWave; t < T; t += kPermuteWaves) {
+    const int id = route_token<EPL>(logits, t, E, k, score_fn, renormalize, rsf, ids, w, w_bf16);
+    if (lane < k) s_local[t * k + lane] = local_of(id, emap, E, E_l);
+  }
+  __syncthreads();
+  counting_sort(LdsRoutes{s_local}, T * k, E_l, map, offsets, inv, R_pad, batch_m, smem, 0, 1);
 }
 
 template <int EPL>
@@ -154,6 +186,50 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
   if (epl <= 4) return launch_epl<4>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
   if (epl <= 8) return launch_epl<8>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
   return launch_epl<16>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+}
+
+namespace {
+template <int EPL>
+hipError_t launch_merged(const float* logits, int64_t T, int E, int k, int score_fn, int renorm,
+                         float rsf, int32_t* ids, float* w, uint16_t* w_bf16, const int32_t* emap,
+                         int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
+                         int batch_m, hipStream_t s) {
+  const size_t lds = sort_lds_bytes(E_l) + sizeof(int32_t) * T * k;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_permute_kernel<EPL>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(route_permute_kernel<EPL>, dim3(1), dim3(kPermuteThreads), lds, s, logits, T,
+                     E, k, score_fn, renorm, rsf, ids, w, w_bf16, emap, E_l, map, offsets, inv,
+                     R_pad, batch_m);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int score_fn,
+                                int renormalize, float rsf, int32_t* ids, float* w,
+                                uint16_t* w_bf16, const int32_t* emap, int E_l, int32_t* map,
+                                int32_t* offsets, int32_t* inv, int64_t R_pad, int batch_m,
+                                hipStream_t s) {
+  if (T > kRoutePermuteMaxT || T == 0) {
+    hipError_t e = hipSuccess;
+    if (T > 0) e = launch_route_topk(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, s);
+    if (e != hipSuccess) return e;
+    return launch_permute(ids, emap, T, k, E, E_l, map, offsets, inv, R_pad, s, batch_m);
+  }
+  const int epl = (E + kWave - 1) / kWave;
+#define MOE_MERGED(N)                                                                          \
+  return launch_merged<N>(logits, T, E, k, score_fn, renormalize, rsf, ids, w, w_bf16, emap, E_l, \
+                          map, offsets, inv, R_pad, batch_m, s)
+  if (epl <= 1) MOE_MERGED(1);
+  if (epl <= 2) MOE_MERGED(2);
+  if (epl <= 4) MOE_MERGED(4);
+  if (epl <= 8) MOE_MERGED(8);
+  MOE_MERGED(16);
+#undef MOE_MERGED
 }
 
 }  // namespace moe

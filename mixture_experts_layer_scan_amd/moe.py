@@ -214,6 +214,48 @@ def moe_route_topk(logits: torch.Tensor, k: int, score_fn: int = SOFTMAX, renorm
     return topk_ids, topk_weights
 
 
+def moe_route_permute(logits: torch.Tensor, k: int, score_fn: int = SOFTMAX,
+                      renormalize: bool = True, rsf: float = 1.0, E_l: Optional[int] = None,
+                      expert_map: Optional[torch.Tensor] = None, R_pad: Optional[int] = None,
+                      topk_ids: Optional[torch.Tensor] = None,
+                      topk_weights: Optional[torch.Tensor] = None,
+                      map: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
+                      inv: Optional[torch.Tensor] = None, want_inv: bool = True, stream=None):
+    """Router and permute map in one call (one kernel for T <= 16).
+    -> dict(topk_ids, topk_weights, map, offsets, inv or None, R_pad)."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be rank-2 [T, E]")
+    T, E = logits.shape
+    dev = logits.device
+    E_l = E if E_l is None else E_l
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if map is None:
+        map = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty((E_l + 1,), dtype=torch.int32, device=dev)
+    if inv is None and want_inv and R_pad > 0:
+        inv = torch.empty((R_pad,), dtype=torch.int32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, (T, k), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, k), dev)
+    _need(map, "map", torch.int32, (T, k), dev)
+    _need(offsets, "offsets", torch.int32, (E_l + 1,), dev)
+    if inv is not None:
+        _need(inv, "inv", torch.int32, (R_pad,), dev)
+    _check(lib().moe_route_permute(logits.data_ptr(), T, E, k, score_fn, int(bool(renormalize)),
+                                   float(rsf), _ptr(expert_map), E_l, R_pad, topk_ids.data_ptr(),
+                                   topk_weights.data_ptr(), map.data_ptr(), offsets.data_ptr(),
+                                   _ptr(inv), _stream(stream)), "moe_route_permute")
+    return {"topk_ids": topk_ids, "topk_weights": topk_weights, "map": map, "offsets": offsets,
+            "inv": inv, "R_pad": R_pad}
+
+
 def moe_permute(topk_ids: torch.Tensor, E: int, E_l: Optional[int] = None,
                 expert_map: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
                 R_pad: Optional[int] = None, map: Optional[torch.Tensor] = None,

@@ -88,6 +88,19 @@ def test_route_errors(L):
     assert r(None, 0, 8, 2, 0, 1, 1.0, None, None, None) == OK  # T = 0: nothing to do
 
 
+def test_route_permute_errors(L):
+    f = L.moe_route_permute
+    # (logits, T, E, k, score, renorm, rsf, emap, E_l, R_pad, ids, w, map, offsets, inv, stream)
+    assert f(P, -1, 8, 2, 0, 1, 1.0, None, 8, 0, P, P, P, P, None, None) == INVALID
+    assert f(P, 4, 8, 9, 0, 1, 1.0, None, 8, 36, P, P, P, P, None, None) == INVALID  # k > E
+    assert f(P, 4, 8, 2, 5, 1, 1.0, None, 8, 8, P, P, P, P, None, None) == UNSUPPORTED
+    assert f(P, 4, 8, 2, 0, 1, 1.0, None, 4, 8, P, P, P, P, None, None) == INVALID  # E_l != E, no map
+    assert f(P, 4, 8, 2, 0, 1, 1.0, None, 8, 7, P, P, P, P, None, None) == SIZE     # R_pad < T * k
+    assert f(P, 4, 8, 2, 0, 1, 1.0, None, 8, 8, P, P, P, None, None, None) == INVALID  # no offsets
+    assert f(None, 4, 8, 2, 0, 1, 1.0, None, 8, 8, P, P, P, P, None, None) == INVALID
+    assert f(P, 4, 8, 2, 0, 1, 1.0, None, 8, 8, P + 4, P, P, P, None, None) == MISALIGNED
+
+
 def test_permute_errors(L):
     f = L.moe_permute
     # R_pad < T * k

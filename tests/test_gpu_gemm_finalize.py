@@ -45,6 +45,13 @@ GEMM_CASES = [
     ("split_wide", [20, 30, 0, 16], 1024, 512),
     # decode-like segments of 0-9 rows with a reduction of 10 k-steps
     ("decode_ragged", [9, 0, 1, 5, 4], 640, 320),
+    # under 16 rows per expert on average (128 rows over 16 experts): the
+    # whole-k decode kernel, with five 32-k steps in flight per wave (GEMM1,
+    # k = 2048) and with one (GEMM2, k = 256; k = 768 below)
+    ("decode_kernel", [1, 0, 2, 1, 0, 3, 0, 0, 1, 0, 0, 0, 4, 0, 0, 2], 2048, 256),
+    # an expert past 16 rows takes two passes
+    ("decode_kernel_two_passes", [0, 20, 1, 0, 0, 0, 0, 0, 3, 0, 0, 0, 0, 0, 0, 0], 2048, 512),
+    ("decode_kernel_short_k", [2, 1, 0, 0, 0, 5, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1], 768, 768),
 ]
 
 

@@ -151,3 +151,67 @@ def test_permute_out_of_range_ids_are_dropped():
 def test_permute_empty():
     r = moe.moe_permute(torch.zeros((0, 8), dtype=torch.int32, device="cuda"), 256, 256)
     assert np.all(r["offsets"].cpu().numpy() == 0)
+
+
+ROUTE_PERMUTE_CASES = [
+    # name, T, E, E_l (None: all local), k, score, renormalize, rsf, seed
+    ("decode_1_ep_rank", 1, 256, "ep", 8, 1, True, 2.5, 500),
+    ("decode_8_ep_rank", 8, 256, "ep", 8, 1, True, 2.5, 501),
+    ("decode_16_ep_rank", 16, 256, "ep", 8, 1, True, 2.5, 502),
+    ("ragged_13x100_top5", 13, 100, None, 5, 0, True, 1.0, 503),
+    ("max_16x1024_top32", 16, 1024, None, 32, 1, True, 2.5, 504),
+    ("mixtral_16x8_top2_no_renorm", 16, 8, None, 2, 0, False, 1.0, 505),
+    # past one workgroup's batch: the two kernels
+    ("two_kernels_17", 17, 256, "ep", 8, 1, True, 2.5, 506),
+    ("two_kernels_64", 64, 256, "ep", 8, 1, True, 2.5, 508),
+    ("two_kernels_2048", 2048, 256, None, 8, 1, True, 2.5, 507),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_PERMUTE_CASES, ids=[c[0] for c in ROUTE_PERMUTE_CASES])
+def test_route_permute(case):
+    """moe_route_permute equals the router and the permute of the oracle:
+    ids, map, offsets and inverse map bit-exact, weights to W_TOL; the R_pad
+    tail of inv is -1."""
+    name, T, E, El, k, score, renorm, rsf, seed = case
+    emap = None
+    E_l = E
+    if El == "ep":
+        cfg = configs.EP_DECODE
+        emap, E_l = configs.expert_map(cfg), cfg.El
+    logits = synth.normal_f32(seed, synth.TID_LOGITS, (T, E))
+    R_pad = configs.permuted_rows(T, k) + 37
+    inv = torch.full((R_pad,), 12345, dtype=torch.int32, device="cuda")
+    r = moe.moe_route_permute(dev(logits), k, score, renorm, rsf, E_l,
+                              None if emap is None else dev(emap), R_pad, inv=inv)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route(logits, k, score, renorm, rsf)
+    assert np.array_equal(r["topk_ids"].cpu().numpy(), ref_ids)
+    assert rel_fro(r["topk_weights"].cpu().numpy(), ref_w) < W_TOL
+    ref_map, ref_off, _ = oracle.permute(ref_ids, E, E_l, emap)
+    assert np.array_equal(r["map"].cpu().numpy(), ref_map)
+    assert np.array_equal(r["offsets"].cpu().numpy(), ref_off)
+    want_inv = np.full(R_pad, -1, dtype=np.int64)
+    flat = ref_map.reshape(-1)
+    want_inv[flat[flat >= 0]] = np.nonzero(flat >= 0)[0]
+    assert np.array_equal(r["inv"].cpu().numpy(), want_inv)
+
+
+def test_route_permute_matches_separate_calls_with_ties():
+    # coarse logits (exact ties at the top-k boundary) on a decode batch: the
+    # merged kernel gives the bits of the two separate calls
+    T, E, k = 12, 64, 8
+    logits = dev((np.floor(synth.normal_f32(13, 1, (T, E)) * 2.0) / 2.0).astype(np.float32))
+    r = moe.moe_route_permute(logits, k, 1, True, 2.5)
+    ids, w = moe.moe_route_topk(logits, k, 1, True, 2.5)
+    p = moe.moe_permute(ids, E)
+    torch.cuda.synchronize()
+    for a, b in [(r["topk_ids"], ids), (r["topk_weights"], w), (r["map"], p["map"]),
+                 (r["offsets"], p["offsets"]), (r["inv"], p["inv"])]:
+        assert torch.equal(a, b)
+
+
+def test_route_permute_empty():
+    r = moe.moe_route_permute(torch.zeros((0, 32), dtype=torch.float32, device="cuda"), 4)
+    torch.cuda.synchronize()
+    assert np.all(r["offsets"].cpu().numpy() == 0)
