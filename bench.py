@@ -95,8 +95,8 @@ def parse():
     p.add_argument("--batched-max-tokens", type=int, default=0,
                    help="use the batched experts format with this capacity per local expert")
     p.add_argument("--gather-kernel", action="store_true",
-                   help="gather the permuted rows with the permute's own kernel instead of "
-                        "reading them through the inverse map inside GEMM1")
+                   help="gather the permuted rows with the permute's own kernel wherever GEMM1 "
+                        "would read them through the inverse map")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -107,16 +107,18 @@ def parse():
 
 
 def gemm_source_hash() -> str:
+    """Hash of the GEMM kernels' sources (the tiled kernels and the decode kernel)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "mixture_experts_layer_scan_amd", "csrc", "gemm.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("gemm.hip", "decode_gemm.hip"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_scan_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel), or None when it is
-    missing or was taken on a different gemm.hip."""
+    missing or was taken on different GEMM sources."""
     path = os.path.join(TRAFFIC_DIR, f"gemm_hbm_traffic_{workload}.txt")
     try:
         with open(path) as f:
@@ -336,10 +338,11 @@ def main():
     # the permute's inverse map, as the library's fused calls do (no gather kernel)
     gathered = (not quant and not Mb and not w_in and P * H * 2 <= 0xFFFFFFFF
                 and not args.gather_kernel)
-    # FP8 and two-term rows: GEMM1 reads the quantized token rows through the
-    # inverse map too (the library's fused calls do the same)
-    gathered_q = (quant and not cfg.fp8_block and P * H * terms <= 0xFFFFFFFF
-                  and not args.gather_kernel)
+    # two-term rows, and one-term FP8 rows of batches up to 64 tokens: GEMM1
+    # reads the quantized token rows through the inverse map too (as the
+    # library's fused calls do)
+    gathered_q = (quant and not cfg.fp8_block and (cfg.fp8x2 or P <= 64)
+                  and P * H * terms <= 0xFFFFFFFF and not args.gather_kernel)
     inv_buf = (torch.empty((R_pad,), dtype=torch.int32, device=dev)
                if gathered or gathered_q else None)
     # a batch of at most 16 tokens routes and permutes in one launch

@@ -11,8 +11,11 @@
 // workgroup streams one long run of each row and no reduction kernel follows:
 //   - 8 waves split the k-range; lane l streams 16 contiguous bytes of weight
 //     row l % 16 per 32-k step (four lanes cover a row's 64-byte run), with
-//     5 steps of loads in flight (one for a k-range under 5 steps), and two
-//     workgroups share a compute unit;
+//     4 steps of loads in flight (one when the range is not a multiple of 4
+//     steps), and two workgroups share a compute unit;
+//   - a workgroup's work units (item, pass of 16 rows) follow one another
+//     without a pipeline drain: the next unit's first loads are issued
+//     before the current unit's last MFMAs, reduction and stores;
 //   - the 16 x 16 x 32 bf16 MFMA takes the expert's rows (up to 16 per pass)
 //     as A and the 16 weight rows as B, so the sum over k happens in the
 //     matrix core and each lane keeps four fp32 sums;
@@ -34,7 +37,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kDecRows = 16;  // weight rows per slice, expert rows per pass
 constexpr int kDecMaxExperts = 1024;
-constexpr int kDecDeep = 5;   // 32-k steps of loads in flight per wave
+constexpr int kDecDeep = 4;   // 32-k steps of loads in flight per wave
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
     const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int gated,
     uint16_t* __restrict__ C, int act, float clamp, int batch_m, const int32_t* __restrict__ a_inv,
     int a_k) {
-  __shared__ f32x4_t red[kDecWaves][kWave];
+  __shared__ f32x4_t red[2][kDecWaves][kWave];
   __shared__ int32_t s_exp[kDecMaxExperts];   // experts with rows, in order
   __shared__ int32_t s_row0[kDecMaxExperts];  // their first row
   __shared__ int32_t s_rows[kDecMaxExperts];  // their row count
@@ -92,95 +95,123 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
   __syncthreads();
   const int64_t items = static_cast<int64_t>(s_n) * slices;
 
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int xi = static_cast<int>(it / slices);
-    const int s = static_cast<int>(it - static_cast<int64_t>(xi) * slices);
-    const int e = s_exp[xi], row0 = s_row0[xi], rows = s_rows[xi];
+  // Work units: (item, pass of 16 expert rows), items blockIdx.x, +grid, ...
+  int64_t it = blockIdx.x;
+  if (it >= items) return;  // the whole workgroup
+  int rg = 0, s = 0, row0 = 0, rows = 0;
+  const uint16_t* wp = W;
+  const uint16_t* ap = A;
+  // pointers of unit (it_, rg_): weight row of this lane's MFMA column and
+  // activation row of its MFMA row (past the expert's count the last row
+  // repeats; its products land only in output rows that are not stored)
+  auto unit = [&](int64_t it_, int rg_, int& s_, int& row0_, int& rows_, const uint16_t*& wp_,
+                  const uint16_t*& ap_) {
+    const int xi = static_cast<int>(it_ / slices);
+    s_ = static_cast<int>(it_ - static_cast<int64_t>(xi) * slices);
+    const int e = s_exp[xi];
+    row0_ = s_row0[xi];
+    rows_ = s_rows[xi];
+    const int wrow =
+        gated ? (j < 8 ? 8 * s_ + j : N_out + 8 * s_ + (j - 8)) : kDecRows * s_ + j;
+    wp_ = W + (static_cast<int64_t>(e) * N_total + wrow) * K + w * kw + kq * 8;
+    const int64_t pr = row0_ + min(rg_ + j, rows_ - 1);
+    const int64_t src = a_inv ? a_inv[pr] / a_k : pr;
+    ap_ = A + src * K + w * kw + kq * 8;
+  };
+  unit(it, rg, s, row0, rows, wp, ap);
 
-    const int wrow = gated ? (j < 8 ? 8 * s + j : N_out + 8 * s + (j - 8)) : kDecRows * s + j;
-    const uint16_t* wp =
-        W + (static_cast<int64_t>(e) * N_total + wrow) * K + w * kw + kq * 8;
-
-    for (int rg = 0; rg < rows; rg += kDecRows) {
-      // MFMA row j takes expert row rg + j; past the count it repeats the
-      // last row, whose products land only in output rows that are not stored
-      const int64_t pr = row0 + min(rg + j, rows - 1);
-      const int64_t src = a_inv ? a_inv[pr] / a_k : pr;
-      const uint16_t* ap = A + src * K + w * kw + kq * 8;
-
-      bf16x8_t bq[D], aq[D];
+  bf16x8_t bq[D], aq[D];
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        bq[d] = load_bf16x8(wp + d * 32);
-        aq[d] = load_bf16x8(ap + d * 32);
-      }
-      f32x4_t acc = {};
-      int st = 0;
-      // steady state: consume D steps, load the D after them
-      for (; st + 2 * D <= nsteps; st += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
-          bq[d] = load_bf16x8(wp + (st + D + d) * 32);
-          aq[d] = load_bf16x8(ap + (st + D + d) * 32);
-        }
-      }
-      // the last D loaded steps and the rem < D after them
-      const int rem = nsteps - st - D;
+  for (int d = 0; d < D; ++d) {
+    bq[d] = load_bf16x8(wp + d * 32);
+    aq[d] = load_bf16x8(ap + d * 32);
+  }
+  int buf = 0;
+  while (true) {
+    f32x4_t acc = {};
+    // consume D steps, load the D after them (nsteps is a multiple of D)
+    for (int st = 0; st + D < nsteps; st += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
-        if (d < rem) {
-          bq[d] = load_bf16x8(wp + (st + D + d) * 32);
-          aq[d] = load_bf16x8(ap + (st + D + d) * 32);
-        }
+        bq[d] = load_bf16x8(wp + (st + D + d) * 32);
+        aq[d] = load_bf16x8(ap + (st + D + d) * 32);
       }
+    }
+    // the next unit's first D steps go out while this one's last D are used
+    // and its sums are reduced and stored
+    int64_t it2 = it;
+    int rg2 = rg + kDecRows;
+    if (rg2 >= rows) {
+      it2 = it + gridDim.x;
+      rg2 = 0;
+    }
+    const bool more = it2 < items;
+    int s2 = s, row02 = row0, rows2 = rows;
+    const uint16_t* wp2 = wp;
+    const uint16_t* ap2 = ap;
+    if (more) unit(it2, rg2, s2, row02, rows2, wp2, ap2);
 #pragma unroll
-      for (int d = 0; d < D; ++d)
-        if (d < rem) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
+    for (int d = 0; d < D; ++d) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
+      if (more) {
+        bq[d] = load_bf16x8(wp2 + d * 32);
+        aq[d] = load_bf16x8(ap2 + d * 32);
+      }
+    }
 
-      // the waves' sums over their k-ranges
-      red[w][lane] = acc;
-      __syncthreads();
-      if (w == 0) {
-        f32x4_t sum = red[0][lane];
+    // the waves' sums over their k-ranges (two buffers: the next unit writes
+    // the other one, and this one is rewritten only after the next barrier,
+    // which wave 0 reaches once it has read it)
+    red[buf][w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+      f32x4_t sum = red[buf][0][lane];
 #pragma unroll
-        for (int ww = 1; ww < kDecWaves; ++ww) sum += red[ww][lane];
-        // lane holds rows 4 * kq + i (i < 4) of column j
-        if (gated) {
-          f32x4_t up;
+      for (int ww = 1; ww < kDecWaves; ++ww) sum += red[buf][ww][lane];
+      // lane holds rows 4 * kq + i (i < 4) of column j
+      if (gated) {
+        f32x4_t up;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) up[i] = __shfl(sum[i], lane + 8, kWave);
-          if (j < 8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = rg + 4 * kq + i;
-              if (r >= rows) break;
-              float v;
-              if (kind == 0) v = gated_act_k<0>(sum[i], up[i], cl);
-              else if (kind == 1) v = gated_act_k<1>(sum[i], up[i], cl);
-              else v = gated_act_k<2>(sum[i], up[i], cl);
-              C[static_cast<int64_t>(row0 + r) * N_out + 8 * s + j] = f32_to_bf16(v);
-            }
-          }
-        } else {
+        for (int i = 0; i < 4; ++i) up[i] = __shfl(sum[i], lane + 8, kWave);
+        if (j < 8) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = rg + 4 * kq + i;
             if (r >= rows) break;
-            C[static_cast<int64_t>(row0 + r) * N_out + kDecRows * s + j] = f32_to_bf16(sum[i]);
+            float v;
+            if (kind == 0) v = gated_act_k<0>(sum[i], up[i], cl);
+            else if (kind == 1) v = gated_act_k<1>(sum[i], up[i], cl);
+            else v = gated_act_k<2>(sum[i], up[i], cl);
+            C[static_cast<int64_t>(row0 + r) * N_out + 8 * s + j] = f32_to_bf16(v);
           }
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rg + 4 * kq + i;
+          if (r >= rows) break;
+          C[static_cast<int64_t>(row0 + r) * N_out + kDecRows * s + j] = f32_to_bf16(sum[i]);
+        }
       }
-      __syncthreads();  // red is rewritten by the next pass
     }
+    if (!more) break;
+    it = it2;
+    rg = rg2;
+    s = s2;
+    row0 = row02;
+    rows = rows2;
+    wp = wp2;
+    ap = ap2;
+    buf ^= 1;
   }
 }
 
 }  // namespace
 
 bool decode_gemm_fits(const GemmArgs& g) {
-  return g.a_scales == nullptr && g.w_scales == nullptr && g.K % (kDecWaves * 32) == 0 &&
+  return g.a_scales == nullptr && g.w_scales == nullptr && g.K >= kDecWaves * 32 &&
+         g.K % (kDecWaves * 32) == 0 &&
          (g.gated ? g.N_out % 8 == 0 : g.N_out % kDecRows == 0) && g.E_l > 0 &&
          g.E_l <= kDecMaxExperts;
 }
@@ -188,9 +219,9 @@ bool decode_gemm_fits(const GemmArgs& g) {
 hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s) {
   const int slices = g.gated ? g.N_out / 8 : g.N_out / kDecRows;
   const int64_t items = static_cast<int64_t>(g.E_l) * slices;  // at most
-  // five 32-k steps in flight per wave when each wave's k-range has them
-  // (then two workgroups fit a compute unit: at most 128 registers a lane)
-  const bool deep = g.K / kDecWaves / 32 >= kDecDeep;
+  // four 32-k steps in flight per wave when each wave's k-range is a
+  // multiple of four steps (two workgroups fit a compute unit)
+  const bool deep = (g.K / kDecWaves / 32) % kDecDeep == 0;
   auto kern = deep ? decode_gemm_kernel<kDecDeep> : decode_gemm_kernel<1>;
   // one resident wave of workgroups; work item i (slice i mod slices of the
   // (i / slices)-th expert with rows) goes to workgroup i mod grid
