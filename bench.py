@@ -545,28 +545,42 @@ def main():
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-    events = [([], [torch.cuda.Event(enable_timing=True) for _ in range(marks_per_step)])
-              for _ in range(args.steps)]
+    # Timed pass 1, the throughput: whole steps, one event pair around each
+    # (an event between two kernels of one stream costs ~5.5 us of idle GPU on
+    # this runtime, so the stage events of pass 2 would inflate short steps)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            evict_caches()
+            torch.cuda._sleep(HOST_AHEAD_CYCLES)  # the step is enqueued meanwhile
+        step_ev[i][0].record()
         if graphs:
-            if flush is not None:
-                evict_caches()
-                torch.cuda._sleep(HOST_AHEAD_CYCLES)  # the replay is submitted meanwhile
-            events[i][1][0].record()
             graphs[i % len(graphs)].replay()
-            events[i][1][1].record()
         else:
-            step(i, events[i])
+            layer(i % len(dev_draws), stream)
+        step_ev[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+
+    # Timed pass 2, the breakdown: the same steps with an event before every
+    # stage (not under graph replay)
+    events = [([], [torch.cuda.Event(enable_timing=True) for _ in range(marks_per_step)])
+              for _ in range(args.steps)]
+    if not graphs:
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(i, events[i])
+        torch.cuda.synchronize()
 
     # per step: milliseconds of each stage, summed over the step's chunks
     per_step = []
     for i in range(args.steps):
         if graphs:
-            per_step.append({"layer_graph": events[i][1][0].elapsed_time(events[i][1][1])})
+            per_step.append({"layer_graph": float(step_ms[i])})
             continue
         names, pool = events[i]
         ms = dict.fromkeys(stages, 0.0)
@@ -600,12 +614,13 @@ def main():
         flops_step.append(f_step)
         g1_ms += per_step[i].get("gemm1", 0.0)
     if decode:
-        # the flush between steps is not part of the layer: time from the events
-        ms_per_step = float(np.mean([sum(p.values()) for p in per_step]))
+        # the flush between steps is not part of the layer: time from the
+        # events around each step
+        ms_per_step = float(np.mean(step_ms))
     else:
         ms_per_step = elapsed / args.steps * 1e3
-    # per-step spread from the events (graph replay: one event pair per step)
-    step_ms = np.array([sum(p.values()) for p in per_step])
+    # the same steps with an event before every stage
+    ms_per_step_staged = float(np.mean([sum(p.values()) for p in per_step]))
     tflops = float(np.mean(flops_step)) / (ms_per_step * 1e-3) / 1e12
     g1_s = g1_ms * 1e-3 if g1_ms > 0 else float("nan")  # no per-kernel events under graph replay
     # (two-term rows run the fp8 MFMA twice: the bf16 peak is their rate)
@@ -638,6 +653,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_staged": ms_per_step_staged,
         "ms_per_step_median": float(np.median(step_ms)),
         "ms_per_step_min": float(np.min(step_ms)),
         "ms_per_step_max": float(np.max(step_ms)),
