@@ -263,6 +263,29 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int3
                       int64_t R_pad, int32_t* topk_ids, float* topk_weights, int32_t* map,
                       int32_t* offsets, int32_t* inv, void* stream);
 
+/* Router, permute map and GEMM1 in one call ([Router], the permute of
+ * [Quantize-Dispatch] and the first expert GEMM with its activation; page
+ * "modular_kernel.py", prepare() and apply()): moe_route_permute followed by
+ * moe_grouped_gemm1_act_gathered(x, inv, T, k, offsets, ..., h).  The results
+ * are those of the two calls.  With bf16 weights, at most 8 tokens and 64
+ * routes, and few rows per local expert (R_pad / E_l under 16), the three
+ * steps run in one kernel: every workgroup routes the tokens and sorts the
+ * routes in on-chip memory itself, then runs its share of GEMM1 on the token
+ * rows through that inverse map (one launch instead of two on decode
+ * batches); otherwise the router-permute and GEMM1 kernels are launched.
+ *   logits, topk_ids, topk_weights          as for moe_route_topk
+ *   expert_map, R_pad, map, offsets, inv    as for moe_permute (inv required)
+ *   x, H, I, w1, activation, activation_clamp, h, workspace
+ *                                           as for moe_grouped_gemm1_act_gathered
+ * Limits: those of the calls it stands for. */
+int moe_route_permute_gemm1_act(const float* logits, const void* x, int64_t T, int32_t H,
+                                int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                                int32_t renormalize, float rsf, const int32_t* expert_map,
+                                int64_t R_pad, const moe_weights* w1, int32_t activation,
+                                float activation_clamp, int32_t* topk_ids, float* topk_weights,
+                                int32_t* map, int32_t* offsets, int32_t* inv, void* h,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* FP8 E4M3 quantization of bf16 rows (the quantize half of [Quantize-Dispatch];
  * prepare() of page "modular_kernel.py" with per_act_token_quant, or a static
  * a1_scale / a2_scale).  Per row, in fp32:

@@ -16,7 +16,8 @@ from .moe import (ACT_GELU, ACT_SILU, DTYPE_BF16, DTYPE_F32, DTYPE_FP8_BLOCK, DT
                   moe_grouped_gemm2_batched, moe_grouped_gemm2_fp8, moe_grouped_gemm2_fp8x2,
                   moe_grouped_gemm_workspace_size, moe_permute,
                   moe_permute_batched, moe_permute_fp8, moe_permuted_rows, moe_quantize_fp8,
-                  moe_quantize_fp8x2, moe_route_permute, moe_route_topk, moe_shared_workspace_size,
+                  moe_quantize_fp8x2, moe_route_permute, moe_route_permute_gemm1_act, moe_route_topk,
+                  moe_shared_workspace_size,
                   moe_workspace_size)
 
 __all__ = [
@@ -31,6 +32,6 @@ __all__ = [
     "moe_grouped_gemm1_act_gathered", "moe_grouped_gemm1_act_fp8",
     "moe_grouped_gemm1_act_fp8x2", "moe_grouped_gemm2", "moe_grouped_gemm2_batched", "moe_grouped_gemm2_fp8",
     "moe_grouped_gemm2_fp8x2", "moe_grouped_gemm_workspace_size", "moe_permute", "moe_permute_batched", "moe_permute_fp8",
-    "moe_permuted_rows", "moe_quantize_fp8", "moe_quantize_fp8x2", "moe_route_permute", "moe_route_topk", "moe_shared_workspace_size",
+    "moe_permuted_rows", "moe_quantize_fp8", "moe_quantize_fp8x2", "moe_route_permute", "moe_route_permute_gemm1_act", "moe_route_topk", "moe_shared_workspace_size",
     "moe_workspace_size",
 ]

@@ -40,6 +40,9 @@ PROTOTYPES = {
     "moe_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "moe_route_permute": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _i32, _i64,
                                          _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_permute_gemm1_act": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _f32, _vp, _i64, _vp, _i32, _f32,
+                                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm1_act": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32, _i32, _Wp, _i32, _f32,

@@ -489,13 +489,15 @@ int moe_permute_batched(const int32_t* topk_ids, const int32_t* expert_map, int6
   return MOE_OK;
 }
 
-static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
-                       int32_t K, int32_t N_out, int gated, int act, float clamp,
-                       const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
-                       void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
-                       bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1,
-                       const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0,
-                       bool block = false) {
+// Checks the arguments of one grouped GEMM call and fills *g (R_pad = 0:
+// nothing to launch, *g untouched).
+static int gemm_check(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                      int32_t K, int32_t N_out, int gated, int act, float clamp,
+                      const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
+                      const char* name, moe::GemmArgs* g, int batch_m = 0, bool fp8 = false,
+                      const float* a_scales = nullptr, int a_terms = 1,
+                      const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0,
+                      bool block = false) {
   if (E_l <= 0 || E_l > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: E_l must be in [1, 1024]", name);
   if (R_pad < 0 || R_pad >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: R_pad must be in [0, 2^31)", name);
   MOE_CHECK(check_weights(w, name));
@@ -523,10 +525,25 @@ static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64
     if (overlap(workspace, workspace_bytes, a, in_bytes) || overlap(workspace, workspace_bytes, c, out_bytes))
       return fail(MOE_ERR_DESTINATION_CONFLICT, "%s: workspace must not overlap the rows", name);
   }
-  moe::GemmArgs g{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
-                  workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp, batch_m,
-                  a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms, a_inv, a_k, a_T};
-  if (block) g.a_ld = R_pad;
+  *g = moe::GemmArgs{a, w->data, scales_of(w), offsets, E_l, K, N_out, gated, R_pad, c,
+                     workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, act, clamp,
+                     batch_m, a_scales, w->dtype == MOE_DTYPE_MXFP4, a_terms, a_inv, a_k, a_T};
+  if (block) g->a_ld = R_pad;
+  return MOE_OK;
+}
+
+static int gemm_common(const void* a, const int32_t* offsets, int32_t E_l, int64_t R_pad,
+                       int32_t K, int32_t N_out, int gated, int act, float clamp,
+                       const moe_weights* w, void* c, void* workspace, size_t workspace_bytes,
+                       void* stream, const char* name, int batch_m = 0, int64_t max_rows = 0,
+                       bool fp8 = false, const float* a_scales = nullptr, int a_terms = 1,
+                       const int32_t* a_inv = nullptr, int a_k = 1, int64_t a_T = 0,
+                       bool block = false) {
+  moe::GemmArgs g{};
+  MOE_CHECK(gemm_check(a, offsets, E_l, R_pad, K, N_out, gated, act, clamp, w, c, workspace,
+                       workspace_bytes, name, &g, batch_m, fp8, a_scales, a_terms, a_inv, a_k,
+                       a_T, block));
+  if (R_pad == 0) return MOE_OK;
   const int64_t rows_bound = (max_rows > 0 && max_rows < R_pad) ? max_rows : R_pad;
   hipError_t e = moe::launch_grouped_gemm(g, rows_bound, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, name);
@@ -566,6 +583,58 @@ int moe_grouped_gemm1_act_gathered(const void* x, const int32_t* inv, int64_t T,
   return gemm_common(x, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
                      workspace, workspace_bytes, stream, "moe_grouped_gemm1_act_gathered", 0, 0,
                      false, nullptr, 1, inv, k, T);
+}
+
+int moe_route_permute_gemm1_act(const float* logits, const void* x, int64_t T, int32_t H,
+                                int32_t I, int32_t E, int32_t E_l, int32_t k, int32_t score_fn,
+                                int32_t renormalize, float rsf, const int32_t* expert_map,
+                                int64_t R_pad, const moe_weights* w1, int32_t activation,
+                                float activation_clamp, int32_t* topk_ids, float* topk_weights,
+                                int32_t* map, int32_t* offsets, int32_t* inv, void* h,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MOE_CHECK(check_route_sizes(T, E, k));
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown score function %d", score_fn);
+  MOE_CHECK(check_local(E, E_l));
+  if (!expert_map && E_l != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "without an expert map every expert is local (E_l=%d, E=%d)", E_l, E);
+  MOE_CHECK(check_rpad(T, k, R_pad));
+  MOE_CHECK(check_gemm_dims(H, I));
+  MOE_CHECK(check_activation(activation, activation_clamp));
+  if (T * int64_t(H) * 2 > int64_t(0xFFFFFFFF))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x spans more than 4 GiB");
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(opt_ptr(expert_map, "expert_map"));
+  if (R_pad > 0) MOE_CHECK(need_ptr(inv, "inv"));
+  if (T > 0) {
+    MOE_CHECK(need_ptr(logits, "logits"));
+    MOE_CHECK(need_ptr(topk_ids, "topk_ids"));
+    MOE_CHECK(need_ptr(topk_weights, "topk_weights"));
+    MOE_CHECK(need_ptr(map, "map"));
+  }
+  if (overlap(inv, sizeof(int32_t) * R_pad, h, sizeof(uint16_t) * R_pad * I))
+    return fail(MOE_ERR_DESTINATION_CONFLICT, "h must not overlap inv");
+  moe::GemmArgs g{};
+  MOE_CHECK(gemm_check(x, offsets, E_l, R_pad, H, I, 1, activation, activation_clamp, w1, h,
+                       workspace, workspace_bytes, "moe_route_permute_gemm1_act", &g, 0, false,
+                       nullptr, 1, inv, k, T));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 0 && R_pad > 0 && moe::gemm_picks_decode(g, R_pad) &&
+      moe::decode_route_gemm1_fits(g, T, E, k)) {
+    hipError_t e = moe::launch_decode_route_gemm1(logits, T, E, k, score_fn, renormalize, rsf,
+                                                  topk_ids, topk_weights, nullptr, expert_map,
+                                                  map, offsets, inv, R_pad, g, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_permute_gemm1_act");
+  }
+  // offsets (and the inverse map's padding) are written even for T = 0
+  hipError_t e = moe::launch_route_permute(logits, T, E, k, score_fn, renormalize, rsf, topk_ids,
+                                           topk_weights, nullptr, expert_map, E_l, map, offsets,
+                                           inv, R_pad, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_permute_gemm1_act route");
+  if (T == 0 || R_pad == 0) return MOE_OK;
+  e = moe::launch_grouped_gemm(g, R_pad, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_permute_gemm1_act gemm1");
 }
 
 int moe_grouped_gemm2(const void* h, const int32_t* offsets, int32_t E_l, int64_t R_pad,
@@ -1027,6 +1096,26 @@ static int run_routed(const float* logits, const void* x, int64_t T, int32_t H, 
   const bool gather_in_gemm =
       (o.fp8 ? !o.block && (o.terms == 2 || T <= kGatherFp8MaxT) : !o.weight_on_input) &&
       o.batch_m == 0 && T * token_row_bytes <= int64_t(0xFFFFFFFF);
+  // A small bf16 batch whose GEMM1 takes the decode kernel: router, permute
+  // map and GEMM1 in one launch, then GEMM2
+  if (!o.fp8 && gather_in_gemm && o.batch_m == 0) {
+    const int64_t max_rows = std::min(moe_permuted_rows(T, k), b.rows);
+    moe::GemmArgs g1{x, w1->data, scales_of(w1), b.offsets, E_l, H, I, 1, b.rows, b.h, b.split,
+                     b.split_bytes, o.act, o.clamp, 0};
+    g1.a_inv = b.inv;
+    g1.a_k = k;
+    g1.a_T = T;
+    if (moe::gemm_picks_decode(g1, max_rows) && moe::decode_route_gemm1_fits(g1, T, E, k)) {
+      hipError_t e = moe::launch_decode_route_gemm1(logits, T, E, k, score_fn, renormalize, rsf,
+                                                    b.ids, b.wts, w_bf16_out, expert_map, map,
+                                                    b.offsets, b.inv, b.rows, g1, s);
+      if (e != hipSuccess) return hip_fail(e, "route, permute and gemm1");
+      moe::GemmArgs g2{b.h, w2->data, scales_of(w2), b.offsets, E_l, I, H, 0, b.rows, y, b.split,
+                       b.split_bytes, moe::kActSilu, 0.0f, 0};
+      e = moe::launch_grouped_gemm(g2, max_rows, s);
+      return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm2");
+    }
+  }
   // Router and permute map (one launch for a small batch)
   hipError_t e = moe::launch_route_permute(logits, T, E, k, score_fn, renormalize, rsf, b.ids,
                                            b.wts, w_bf16_out, expert_map, E_l, map, b.offsets,

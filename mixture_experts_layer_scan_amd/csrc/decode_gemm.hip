@@ -25,7 +25,7 @@
 // rows through the permute's inverse map.  An expert with more than 16 rows
 // takes one pass per 16 (each pass re-reads the slice), so the host picks
 // this kernel only for batches whose experts see a few rows each.
-#include "moe_common.h"
+#include "route_core.h"
 
 namespace moe {
 namespace {
@@ -43,12 +43,13 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
 }
 
+// The work of one workgroup: offsets and a_inv may point to global memory or
+// to LDS (the fused kernel below computes them in LDS).
 template <int D>
-__global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int gated,
-    uint16_t* __restrict__ C, int act, float clamp, int batch_m, const int32_t* __restrict__ a_inv,
-    int a_k) {
+__device__ __forceinline__ void decode_units(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const int32_t* offsets,
+    int E_l, int K, int N_out, int gated, uint16_t* __restrict__ C, int act, float clamp,
+    int batch_m, const int32_t* a_inv, int a_k) {
   __shared__ f32x4_t red[2][kDecWaves][kWave];
   __shared__ int32_t s_exp[kDecMaxExperts];   // experts with rows, in order
   __shared__ int32_t s_row0[kDecMaxExperts];  // their first row
@@ -120,14 +121,29 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
   };
   unit(it, rg, s, row0, rows, wp, ap);
 
+  // (the weight loads go out first: the activation pointer waits on the
+  // inverse-map load)
   bf16x8_t bq[D], aq[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    bq[d] = load_bf16x8(wp + d * 32);
-    aq[d] = load_bf16x8(ap + d * 32);
-  }
+  for (int d = 0; d < D; ++d) bq[d] = load_bf16x8(wp + d * 32);
+#pragma unroll
+  for (int d = 0; d < D; ++d) aq[d] = load_bf16x8(ap + d * 32);
   int buf = 0;
   while (true) {
+    // the next unit, resolved now so that its inverse-map load lands while
+    // this unit streams
+    int64_t it2 = it;
+    int rg2 = rg + kDecRows;
+    if (rg2 >= rows) {
+      it2 = it + gridDim.x;
+      rg2 = 0;
+    }
+    const bool more = it2 < items;
+    int s2 = s, row02 = row0, rows2 = rows;
+    const uint16_t* wp2 = wp;
+    const uint16_t* ap2 = ap;
+    if (more) unit(it2, rg2, s2, row02, rows2, wp2, ap2);
+
     f32x4_t acc = {};
     // consume D steps, load the D after them (nsteps is a multiple of D)
     for (int st = 0; st + D < nsteps; st += D) {
@@ -140,17 +156,6 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
     }
     // the next unit's first D steps go out while this one's last D are used
     // and its sums are reduced and stored
-    int64_t it2 = it;
-    int rg2 = rg + kDecRows;
-    if (rg2 >= rows) {
-      it2 = it + gridDim.x;
-      rg2 = 0;
-    }
-    const bool more = it2 < items;
-    int s2 = s, row02 = row0, rows2 = rows;
-    const uint16_t* wp2 = wp;
-    const uint16_t* ap2 = ap;
-    if (more) unit(it2, rg2, s2, row02, rows2, wp2, ap2);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d], bq[d], acc, 0, 0, 0);
@@ -207,6 +212,87 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ offsets, int E_l, int K, int N_out, int gated,
+    uint16_t* __restrict__ C, int act, float clamp, int batch_m, const int32_t* __restrict__ a_inv,
+    int a_k) {
+  decode_units<D>(A, W, offsets, E_l, K, N_out, gated, C, act, clamp, batch_m, a_inv, a_k);
+}
+
+// Router, permute map and GEMM1 of a batch of at most 64 routes in one
+// launch.  Every workgroup routes the tokens itself (wave t takes token t;
+// the same code on the same logits gives the same picks everywhere), sorts
+// the routes by local expert in LDS with one wave (wave_match ranks, counts,
+// a scan over the experts) and then runs its GEMM1 work units on the token
+// rows through that LDS inverse map; workgroup 0 alone writes the ids,
+// weights, map, offsets and inverse map that GEMM2 and finalize read.  The
+// results equal those of the router, permute and gathered GEMM1 calls.
+template <int EPL, int D>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_route_gemm1_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score_fn, int renormalize,
+    float rsf, int32_t* __restrict__ ids, float* __restrict__ wts, uint16_t* __restrict__ w_bf16,
+    const int32_t* __restrict__ emap, int E_l, int32_t* __restrict__ map,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ inv, int64_t R_pad,
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int K, int N_out,
+    uint16_t* __restrict__ C, int act, float clamp) {
+  __shared__ int32_t s_loc[kWave];                 // local expert of each route
+  __shared__ int32_t s_cnt[kDecMaxExperts];        // routes per local expert
+  __shared__ int32_t s_off[kDecMaxExperts + 1];    // their first rows
+  __shared__ int32_t s_inv[kWave];                 // route of each row
+  const bool lead = blockIdx.x == 0;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int R = T * k;  // <= 64
+  for (int e = threadIdx.x; e < E_l; e += kDecThreads) s_cnt[e] = 0;
+  if (w < T) {
+    int em[EPL];
+    load_local_map<EPL>(emap, E, E_l, em);
+    const int id = route_token<EPL>(logits, w, E, k, score_fn, renormalize, rsf, ids, wts,
+                                    w_bf16, lead);
+    const int l = local_of_pick<EPL>(em, id, E);
+    if (lane < k) s_loc[w * k + lane] = l;
+  }
+  __syncthreads();
+  if (w == 0) {
+    // rank of each route among equal experts (ascending route index), the
+    // counts, then offsets by a scan over the experts
+    const bool valid = lane < R;
+    const int L = valid ? s_loc[lane] : -1;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const uint64_t peers = wave_match(static_cast<uint32_t>(L + 1), valid, 32 - __clz(E_l));
+    if (valid && L >= 0 && (peers & lt) == 0ull) s_cnt[L] = __popcll(peers);
+    int run = 0;
+    for (int e0 = 0; e0 < E_l; e0 += kWave) {
+      const int e = e0 + lane;
+      const int c = e < E_l ? s_cnt[e] : 0;
+      const int incl = wave_inclusive_sum(c);
+      if (e < E_l) {
+        s_off[e] = run + incl - c;
+        if (lead) offsets[e] = run + incl - c;
+      }
+      run += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      s_off[E_l] = run;
+      if (lead) offsets[E_l] = run;
+    }
+    if (valid) {
+      const int slot = L >= 0 ? s_off[L] + __popcll(peers & lt) : -1;
+      if (L >= 0) s_inv[slot] = lane;
+      if (lead) {
+        map[lane] = slot;
+        if (L >= 0 && inv) inv[slot] = lane;
+      }
+    }
+    if (lead && inv)
+      for (int64_t r = run + lane; r < R_pad; r += kWave) inv[r] = -1;
+  }
+  __syncthreads();
+  decode_units<D>(X, W, s_off, E_l, K, N_out, 1, C, act, clamp, 0, s_inv, k);
+}
+
 }  // namespace
 
 bool decode_gemm_fits(const GemmArgs& g) {
@@ -242,6 +328,59 @@ hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s) {
                      g.offsets, g.E_l, g.K, g.N_out, g.gated, static_cast<uint16_t*>(g.c), g.act,
                      g.clamp, g.batch_m, g.a_inv, g.a_k);
   return hipGetLastError();
+}
+
+namespace {
+template <int EPL>
+hipError_t launch_fused_epl(const float* logits, int T, int E, int k, int score_fn, int renorm,
+                            float rsf, int32_t* ids, float* wts, uint16_t* w_bf16,
+                            const int32_t* emap, int E_l, int32_t* map, int32_t* offsets,
+                            int32_t* inv, int64_t R_pad, const GemmArgs& g, hipStream_t s) {
+  const bool deep = (g.K / kDecWaves / 32) % kDecDeep == 0;
+  auto kern = deep ? decode_route_gemm1_kernel<EPL, kDecDeep> : decode_route_gemm1_kernel<EPL, 1>;
+  static int occ[2] = {0, 0};
+  int& o = occ[deep ? 1 : 0];
+  if (o == 0) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(kern), kDecThreads, 0);
+    if (e != hipSuccess) return e;
+    o = n > 0 ? n : 1;
+  }
+  const int slices = g.N_out / 8;
+  const int64_t items = static_cast<int64_t>(g.E_l) * slices;  // at most
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * o;
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kDecThreads), 0, s, logits, T,
+                     E, k, score_fn, renorm, rsf, ids, wts, w_bf16, emap, E_l, map, offsets, inv,
+                     R_pad, static_cast<const uint16_t*>(g.a), static_cast<const uint16_t*>(g.w),
+                     g.K, g.N_out, static_cast<uint16_t*>(g.c), g.act, g.clamp);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool decode_route_gemm1_fits(const GemmArgs& g, int64_t T, int E, int k) {
+  return g.gated && decode_gemm_fits(g) && g.batch_m == 0 && T >= 1 && T * k <= kWave &&
+         T <= kDecWaves && E <= 1024;
+}
+
+hipError_t launch_decode_route_gemm1(const float* logits, int64_t T, int E, int k, int score_fn,
+                                     int renormalize, float rsf, int32_t* ids, float* wts,
+                                     uint16_t* w_bf16, const int32_t* emap, int32_t* map,
+                                     int32_t* offsets, int32_t* inv, int64_t R_pad,
+                                     const GemmArgs& g, hipStream_t s) {
+  const int epl = (E + kWave - 1) / kWave;
+  const int Ti = static_cast<int>(T);
+#define MOE_FUSED(N)                                                                          \
+  return launch_fused_epl<N>(logits, Ti, E, k, score_fn, renormalize, rsf, ids, wts, w_bf16, \
+                             emap, g.E_l, map, offsets, inv, R_pad, g, s)
+  if (epl <= 1) MOE_FUSED(1);
+  if (epl <= 2) MOE_FUSED(2);
+  if (epl <= 4) MOE_FUSED(4);
+  if (epl <= 8) MOE_FUSED(8);
+  MOE_FUSED(16);
+#undef MOE_FUSED
 }
 
 }  // namespace moe

@@ -1311,6 +1311,12 @@ size_t gemm_split_ws_bytes(int64_t R_pad, int N_total) {
   return static_cast<size_t>(std::max(split, kTailBytes));
 }
 
+bool gemm_picks_decode(const GemmArgs& g, int64_t max_rows) {
+  const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
+  return g.a_scales == nullptr && g.w_scales == nullptr && mean_rows < kDecodeMeanRows &&
+         decode_gemm_fits(g);
+}
+
 // max_rows: the most local routes the call can see (T * k), from the host.
 hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (g.a_scales && g.a_ld > 0) return launch_fmt<false, true, false, true>(g, max_rows, s);

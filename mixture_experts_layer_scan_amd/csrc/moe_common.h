@@ -171,6 +171,17 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t 
 // reduction.  decode_gemm_fits: K a multiple of 256, N_out of 8 (gated) or 16.
 bool decode_gemm_fits(const GemmArgs& g);
 hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s);
+// launch_grouped_gemm(g, max_rows) runs the decode kernel
+bool gemm_picks_decode(const GemmArgs& g, int64_t max_rows);
+// Router, permute map (inverse map included) and gathered GEMM1 in one launch
+// (g: the gathered bf16 GEMM1 of the decode kernel, its a_inv and offsets
+// the buffers to fill).  Fits: T <= 8 tokens, T * k <= 64 routes, E <= 1024.
+bool decode_route_gemm1_fits(const GemmArgs& g, int64_t T, int E, int k);
+hipError_t launch_decode_route_gemm1(const float* logits, int64_t T, int E, int k, int score_fn,
+                                     int renormalize, float rsf, int32_t* ids, float* wts,
+                                     uint16_t* w_bf16, const int32_t* emap, int32_t* map,
+                                     int32_t* offsets, int32_t* inv, int64_t R_pad,
+                                     const GemmArgs& g, hipStream_t s);
 // w == NULL: every weight is 1 (the weights were applied to the inputs)
 hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
                            int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,

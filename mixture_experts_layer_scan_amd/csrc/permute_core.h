@@ -165,6 +165,11 @@ __device__ __forceinline__ void counting_sort(const Src& src, int64_t R, int E_l
   // registers for the ranking walk below.
   const int64_t span = end_b - beg_b;
   const int64_t per_wave = ((span + kStep - 1) / kStep) * kWave;
+  // waves whose run is not empty (all 16 but for small ranges)
+  const int nwa =
+      per_wave > 0 ? static_cast<int>(min(static_cast<int64_t>(kPermuteWaves),
+                                          (span + per_wave - 1) / per_wave))
+                   : 0;
   const int64_t beg = beg_b + (w * per_wave < span ? w * per_wave : span);
   const int64_t end = beg + per_wave < end_b ? beg + per_wave : end_b;
   const bool one_chunk = end - beg <= kChunk * kWave;
@@ -202,7 +207,7 @@ __device__ __forceinline__ void counting_sort(const Src& src, int64_t R, int E_l
   int cnt_total = 0;
   if (e < E_l) {
     int run = 0;
-    for (int ww = 0; ww < kPermuteWaves; ++ww) {
+    for (int ww = 0; ww < nwa; ++ww) {
       const int c = hist[ww * E_l + e];
       hist[ww * E_l + e] = run;
       run += c;
@@ -214,7 +219,7 @@ __device__ __forceinline__ void counting_sort(const Src& src, int64_t R, int E_l
   if (e < E_l) {
     const int base = (batch_m > 0 ? e * batch_m : start) + pre[e];
     if (blk == 0) offsets[e] = batch_m > 0 ? cnt_total : start;
-    for (int ww = 0; ww < kPermuteWaves; ++ww) hist[ww * E_l + e] += base;
+    for (int ww = 0; ww < nwa; ++ww) hist[ww * E_l + e] += base;
   }
   if (threadIdx.x == 0) {
     if (blk == 0 && batch_m == 0) offsets[E_l] = total;

@@ -823,6 +823,57 @@ def moe_grouped_gemm1_act_gathered(x: torch.Tensor, inv: torch.Tensor, k: int,
         h.data_ptr(), ws, ws_bytes, _stream(stream)), "moe_grouped_gemm1_act_gathered")
     return h
 
+def moe_route_permute_gemm1_act(logits: torch.Tensor, x: torch.Tensor, k: int, w1: Weights,
+                                I: int, score_fn: int = SOFTMAX, renormalize: bool = True,
+                                rsf: float = 1.0, expert_map: Optional[torch.Tensor] = None,
+                                R_pad: Optional[int] = None,
+                                topk_ids: Optional[torch.Tensor] = None,
+                                topk_weights: Optional[torch.Tensor] = None,
+                                map: Optional[torch.Tensor] = None,
+                                offsets: Optional[torch.Tensor] = None,
+                                inv: Optional[torch.Tensor] = None,
+                                h: Optional[torch.Tensor] = None, activation=ACT_SILU,
+                                activation_clamp: Optional[float] = None, stream=None,
+                                split: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Router, permute map and GEMM1 on the token rows in one call (one kernel
+    for small bf16 decode batches).  -> dict(topk_ids, topk_weights, map,
+    offsets, inv, h, R_pad)."""
+    _need(logits, "logits", torch.float32)
+    _need(x, "x", torch.bfloat16)
+    if logits.dim() != 2 or x.dim() != 2 or x.shape[0] != logits.shape[0]:
+        raise ValueError("logits must be [T, E] and x [T, H]")
+    T, E = logits.shape
+    H = x.shape[1]
+    dev = x.device
+    E_l = w1.E_l
+    if expert_map is not None:
+        _need(expert_map, "expert_map", torch.int32, (E,), dev)
+    if w1.N != 2 * I or w1.K != H:
+        raise ValueError(f"w1 must be [E_l, 2I={2 * I}, H={H}]")
+    R_pad = moe_permuted_rows(T, k) if R_pad is None else R_pad
+    out = {}
+    for name, t, dt, shape in [("topk_ids", topk_ids, torch.int32, (T, k)),
+                               ("topk_weights", topk_weights, torch.float32, (T, k)),
+                               ("map", map, torch.int32, (T, k)),
+                               ("offsets", offsets, torch.int32, (E_l + 1,)),
+                               ("inv", inv, torch.int32, (R_pad,)),
+                               ("h", h, torch.bfloat16, (R_pad, I))]:
+        if t is None:
+            t = torch.empty(shape, dtype=dt, device=dev)
+        _need(t, name, dt, shape, dev)
+        out[name] = t
+    ws, ws_bytes, _keep = _gemm_workspace(R_pad, I, True, split, dev, stream, workspace)
+    _check(lib().moe_route_permute_gemm1_act(
+        logits.data_ptr(), x.data_ptr(), T, H, I, E, E_l, k, score_fn, int(bool(renormalize)),
+        float(rsf), _ptr(expert_map), R_pad, w1.ref(), _act(activation),
+        0.0 if activation_clamp is None else float(activation_clamp),
+        out["topk_ids"].data_ptr(), out["topk_weights"].data_ptr(), out["map"].data_ptr(),
+        out["offsets"].data_ptr(), out["inv"].data_ptr(), out["h"].data_ptr(), ws, ws_bytes,
+        _stream(stream)), "moe_route_permute_gemm1_act")
+    out["R_pad"] = R_pad
+    return out
+
+
 def moe_grouped_gemm2(h: torch.Tensor, offsets: torch.Tensor, w2: Weights, H: int,
                       y: Optional[torch.Tensor] = None, stream=None,
                       split: bool = True, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
