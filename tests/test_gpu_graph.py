@@ -22,7 +22,7 @@ def _gpu():
     need_gpu()
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.parametrize("T", [1, 8, 64])
 def test_decode_layer_graph_replays_match_eager(T):
     base = configs.EP_DECODE
     cfg = base.with_T(T)
