@@ -669,7 +669,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     constexpr int BSM = Cfg::BS ? FM : 1, BSN = Cfg::BS ? FN : 1;
     u32x4 bs_a[BSM][4];
     uint32_t bs_w[BSN];
-    uint32_t bs_aoff[BSM][4], bs_woff[BSN];
+    // byte offsets: this lane's first row scale (the others at constant
+    // distances, folded into the load instructions) and, wave-uniform, each
+    // weight fragment's block row
+    uint32_t bs_abase = 0;
+    uint32_t bs_woff[BSN];
     const int nkb = K / BK;
     const int nb_rows = N_total / 128;
     const __amdgpu_buffer_rsrc_t bs_arsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -681,14 +685,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         0, Cfg::BS ? nb_rows * nkb * 4 : 0, kBufferFlags);
     if constexpr (Cfg::BS) {
       const int half = lane >> 5;
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          bs_aoff[fm][g] = static_cast<uint32_t>(row0 + wm * Cfg::WTM + fm * 32 + 8 * g + 4 * half) * 4u;
+      bs_abase = static_cast<uint32_t>(row0 + wm * Cfg::WTM + 4 * half) * 4u;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bs_woff[fn] = static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn)) / 128) * nkb * 4u;
+        bs_woff[fn] = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn)) / 128) * nkb * 4u);
     }
     // k-block of k-step kt (the k-order may start at a tile-dependent stage)
     auto kblock = [&](int kt) { return kt0 + krot(kt); };
@@ -699,7 +700,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            bs_a[fm][g] = load_u128(bs_arsrc, bs_aoff[fm][g], static_cast<int>(kb * a_ld * 4));
+            bs_a[fm][g] = load_u128(bs_arsrc, bs_abase + static_cast<uint32_t>(fm * 32 + 8 * g) * 4u,
+                                    static_cast<int>(kb * a_ld * 4));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) bs_w[fn] = load_u32(bs_wrsrc, bs_woff[fn], kb * 4);
       }
