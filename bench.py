@@ -73,7 +73,9 @@ HOST_AHEAD_CYCLES = 2_000_000  # GPU spin before each decode step (outside the e
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=3000,
+                   help="timed steps of the throughput pass (the default keeps the GPU busy for "
+                        "several seconds); the per-stage pass runs the first min(steps, 100)")
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral8x7b_prefill_4096tok")
     p.add_argument("--tokens", type=int, default=64,
@@ -592,17 +594,18 @@ def main():
 
     # Timed pass 2, the breakdown: the same steps with an event before every
     # stage (not under graph replay)
+    stage_steps = args.steps if graphs else min(args.steps, 100)
     events = [([], [torch.cuda.Event(enable_timing=True) for _ in range(marks_per_step)])
-              for _ in range(args.steps)]
+              for _ in range(stage_steps)]
     if not graphs:
         torch.cuda.synchronize()
-        for i in range(args.steps):
+        for i in range(stage_steps):
             step(i, events[i])
         torch.cuda.synchronize()
 
     # per step: milliseconds of each stage, summed over the step's chunks
     per_step = []
-    for i in range(args.steps):
+    for i in range(stage_steps):
         if graphs:
             per_step.append({"layer_graph": float(step_ms[i])})
             continue
@@ -622,20 +625,20 @@ def main():
             route_permute(d, t0, n)
             per_chunk.append(chunk_counts())
         draw_counts.append(per_chunk)
-    step_counts = [draw_counts[i % len(dev_draws)] for i in range(args.steps)]
 
-    flops_step = []
+    # algorithmic work of every timed step (throughput) and of the per-stage
+    # pass's steps (the GEMM1 roofline)
+    work = [[(gemm_work(cfg, c, 1), gemm_work(cfg, c, 2)) for c in per_chunk]
+            for per_chunk in draw_counts]
+    flops_step = [6.0 * T * H * cfg.shared_I
+                  + sum(f1 + f2 for (f1, _), (f2, _) in work[i % len(dev_draws)])
+                  for i in range(args.steps)]
     g1_flops = g1_bytes = g1_ms = g2_bytes = 0.0
-    for i, per_chunk in enumerate(step_counts):
-        f_step = 6.0 * T * H * cfg.shared_I
-        for c in per_chunk:
-            f1, b1 = gemm_work(cfg, c, 1)
-            f2, b2 = gemm_work(cfg, c, 2)
-            g2_bytes += b2
-            f_step += f1 + f2
+    for i in range(stage_steps):
+        for (f1, b1), (f2, b2) in work[i % len(dev_draws)]:
             g1_flops += f1
             g1_bytes += b1
-        flops_step.append(f_step)
+            g2_bytes += b2
         # (with the fused first stage its time, routing included, stands for GEMM1)
         g1_ms += per_step[i].get("gemm1", per_step[i].get("route_permute_gemm1", 0.0))
     if decode:
@@ -660,7 +663,7 @@ def main():
         achieved = g1_bytes / g1_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-    n_launch = len(step_counts) * len(chunks)
+    n_launch = stage_steps * len(chunks)
     if graphs:
         roof.update({"achieved": None, "frac": None,
                      "note": "no per-kernel timing under graph replay; run without --graph"})
@@ -681,6 +684,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "ms_per_step_staged": ms_per_step_staged,
+        "stage_steps": stage_steps,
         "ms_per_step_median": float(np.median(step_ms)),
         "ms_per_step_min": float(np.min(step_ms)),
         "ms_per_step_max": float(np.max(step_ms)),
