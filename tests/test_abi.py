@@ -101,6 +101,32 @@ def test_route_permute_errors(L):
     assert f(P, 4, 8, 2, 0, 1, 1.0, None, 8, 8, P + 4, P, P, P, None, None) == MISALIGNED
 
 
+def test_route_permute_gemm1_errors(L):
+    f = L.moe_route_permute_gemm1_act
+    # (logits, x, T, H, I, E, E_l, k, score, renorm, rsf, emap, R_pad, w1, act, clamp,
+    #  ids, w, map, offsets, inv, h, workspace, workspace_bytes, stream)
+    w = _w()
+    ok = dict(T=4, H=128, I=256, E=8, E_l=8, k=2, R_pad=128)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(P, P * 2, a["T"], a["H"], a["I"], a["E"], a["E_l"], a["k"], kw.get("score", 0), 1,
+                 1.0, None, a["R_pad"], kw.get("w1", w), kw.get("act", 0), kw.get("clamp", 0.0),
+                 P * 3, P * 4, P * 5, kw.get("offsets", P * 6), kw.get("inv", P * 7),
+                 kw.get("h", P * 64), None, 0, None)
+    assert call(T=-1) == INVALID
+    assert call(k=9) == INVALID                  # k > E
+    assert call(score=5) == UNSUPPORTED
+    assert call(E_l=4) == INVALID                # no expert map, E_l != E
+    assert call(R_pad=7) == SIZE                 # R_pad < T * k
+    assert call(H=100) == INVALID                # H not a multiple of 64
+    assert call(act=3) == UNSUPPORTED
+    assert call(offsets=None) == INVALID
+    assert call(inv=None) == INVALID
+    assert call(h=P * 7) == CONFLICT             # h over the inverse map
+    assert call(w1=None) == INVALID
+
+
 def test_permute_errors(L):
     f = L.moe_permute
     # R_pad < T * k
