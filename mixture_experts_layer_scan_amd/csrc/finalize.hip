@@ -187,15 +187,12 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
   const int threads = H8 >= 256 ? 256 : ((H8 + 63) / 64) * 64;
   const int64_t blocks = T < 16384 ? T : 16384;
   const size_t lds = sizeof(float) * static_cast<size_t>(H);
-  static bool attr_set[2] = {false, false};
+  static bool attr_set[2][kMaxDevices] = {};
   const void* fn = w_is_bf16 ? reinterpret_cast<const void*>(finalize_norm_kernel<true>)
                              : reinterpret_cast<const void*>(finalize_norm_kernel<false>);
-  if (!attr_set[w_is_bf16 ? 1 : 0]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(sizeof(float) * kTailMaxH));
-    if (e != hipSuccess) return e;
-    attr_set[w_is_bf16 ? 1 : 0] = true;
-  }
+  hipError_t e = ensure_dynamic_lds(fn, static_cast<int>(sizeof(float) * kTailMaxH),
+                                    attr_set[w_is_bf16 ? 1 : 0]);
+  if (e != hipSuccess) return e;
   if (w_is_bf16)
     hipLaunchKernelGGL(finalize_norm_kernel<true>, dim3(static_cast<unsigned>(blocks)),
                        dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, T, k, H8,

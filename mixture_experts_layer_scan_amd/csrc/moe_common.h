@@ -213,4 +213,19 @@ hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t s);
 
 int device_cu_count();
 
+// Raises func's dynamic-LDS limit to `bytes` once per device; `done` holds
+// the caller's per-device flags (a race between threads only repeats the
+// call).
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_dynamic_lds(const void* func, int bytes, bool (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && tracked) done[dev] = true;
+  return e;
+}
+
 }  // namespace moe

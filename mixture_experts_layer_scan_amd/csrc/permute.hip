@@ -101,13 +101,10 @@ hipError_t launch_permute(const int32_t* ids, const int32_t* emap, int64_t T, in
                           int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
                           hipStream_t s, int batch_m) {
   const size_t lds = sort_lds_bytes(E_l);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool attr_set[kMaxDevices] = {};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(permute_kernel), 80 * 1024,
+                                    attr_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(permute_kernel, dim3(sort_blocks(T * k)), dim3(kPermuteThreads), lds, s, ids,
                      emap, T * k, E, E_l, map, offsets, inv, R_pad, batch_m);
   return hipGetLastError();

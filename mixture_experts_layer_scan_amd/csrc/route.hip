@@ -88,13 +88,10 @@ hipError_t launch_merged(const float* logits, int64_t T, int E, int k, int score
                          int E_l, int32_t* map, int32_t* offsets, int32_t* inv, int64_t R_pad,
                          int batch_m, hipStream_t s) {
   const size_t lds = sort_lds_bytes(E_l) + sizeof(int32_t) * T * k;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_permute_kernel<EPL>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool attr_set[kMaxDevices] = {};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(route_permute_kernel<EPL>),
+                                    80 * 1024, attr_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_permute_kernel<EPL>, dim3(1), dim3(kPermuteThreads), lds, s, logits, T,
                      E, k, score_fn, renorm, rsf, ids, w, w_bf16, emap, E_l, map, offsets, inv,
                      R_pad, batch_m);
