@@ -50,6 +50,9 @@ def _route(T, E, k, seed, hot=None):
     (64, 8, 8, 4, 20, False),     # expert 3 overflows its 20 slots
     (33, 16, 4, 3, 8, True),      # expert-parallel map, 4 local experts
     (1, 8, 8, 2, 1, False),       # one token
+    # several permute workgroups (one per 1024 routes), with drops
+    (1500, 8, 8, 2, 300, False),  # 3000 routes, expert 3 overflows
+    (1200, 16, 4, 3, 600, True),  # 3600 routes, expert-parallel map
 ])
 def test_permute_batched_bit_exact(T, E, E_l, k, M, use_map):
     H = 136

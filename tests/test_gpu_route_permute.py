@@ -129,20 +129,23 @@ def test_permute_scattered_map_and_all_nonlocal():
     _check_permute(ids2, E, 1, none, 64, seed=4)
 
 
-def test_permute_out_of_range_ids_are_dropped():
+@pytest.mark.parametrize("T", [50, 3000])  # one workgroup; 12 of them
+def test_permute_out_of_range_ids_are_dropped(T):
     E = 16
-    ids = _ids(50, E, 4, 61)
+    ids = _ids(T, E, 4, 61)
     bad = ids.copy()
     bad[3, 1] = 99
     bad[10, 0] = -5
+    bad[T - 1, 3] = 1 << 30
     r = moe.moe_permute(dev(bad), E, E)
     m = r["map"].cpu().numpy()
-    assert m[3, 1] == -1 and m[10, 0] == -1
+    assert m[3, 1] == -1 and m[10, 0] == -1 and m[T - 1, 3] == -1
     # the rest equals the oracle with those routes sent to a non-local expert
     emap = np.concatenate([np.arange(E, dtype=np.int32), np.array([-1], dtype=np.int32)])
     fixed = bad.copy()
     fixed[3, 1] = E
     fixed[10, 0] = E
+    fixed[T - 1, 3] = E
     ref_map, ref_off, _ = oracle.permute(fixed, E + 1, E, emap)
     assert np.array_equal(m, ref_map)
     assert np.array_equal(r["offsets"].cpu().numpy(), ref_off)
