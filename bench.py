@@ -204,8 +204,12 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
                 chunk *= 2
         if n_draws > 10000:
             break
-    where = (f"{total_tok} tokens from {n_draws} routing draws of {cfg.T} tokens"
-             if len(draws) > 1 else f"first {total_tok} of {cfg.T} tokens")
+    if len(draws) > 1:
+        where = f"{total_tok} tokens from {n_draws} routing draws of {cfg.T} tokens"
+    elif n_draws > 1:
+        where = f"{total_tok} tokens ({n_draws} passes over the {cfg.T} tokens)"
+    else:
+        where = f"first {total_tok} of {cfg.T} tokens"
     return {"value": total_tok / total_s, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{where} of the same workload, float64 per-token per-expert MLP, "
@@ -531,12 +535,16 @@ def main():
 
     marks_per_step = len(chunks) * len(stages) + 1
 
+    # Steps of a few dozen microseconds (decode batches, the tiny layer) are
+    # timed from their events with a GPU spin before each (outside the
+    # events) that keeps the GPU busy while the host enqueues the step, so
+    # the events time the kernels, not the Python call overhead between them.
+    host_ahead = decode or T * k <= 256
+
     def step(i, ev=None):
         if flush is not None:
             evict_caches()
-            # keep the GPU busy (outside the events) while the host enqueues the
-            # step, so the events time the kernels, not the Python call overhead
-            # between them (a decode step's kernels take a few microseconds each)
+        if host_ahead:
             torch.cuda._sleep(HOST_AHEAD_CYCLES)
         if ev is None:
             layer(i % len(dev_draws), stream)
@@ -581,6 +589,7 @@ def main():
     for i in range(args.steps):
         if flush is not None:
             evict_caches()
+        if host_ahead:
             torch.cuda._sleep(HOST_AHEAD_CYCLES)  # the step is enqueued meanwhile
         step_ev[i][0].record()
         if graphs:
@@ -641,9 +650,9 @@ def main():
             g2_bytes += b2
         # (with the fused first stage its time, routing included, stands for GEMM1)
         g1_ms += per_step[i].get("gemm1", per_step[i].get("route_permute_gemm1", 0.0))
-    if decode:
-        # the flush between steps is not part of the layer: time from the
-        # events around each step
+    if host_ahead:
+        # the flush and the spin between steps are not part of the layer:
+        # time from the events around each step
         ms_per_step = float(np.mean(step_ms))
     else:
         ms_per_step = elapsed / args.steps * 1e3
@@ -712,10 +721,11 @@ def main():
                    "routing": ("softmax" if cfg.score == 0 else "sigmoid") +
                               (f" top-{k} renormalized") + (f", rsf {cfg.rsf}" if cfg.rsf != 1 else "") +
                               (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else ""),
-                   "form": ("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
-                            f"{len(draws)} routing draws, the host enqueues each step while a GPU spin "
-                            "runs ahead of it (events time the kernels, not the Python call overhead)"
-                            if decode else "finalized")
+                   "form": (("deferred + separate finalize, L2/MALL evicted (512 MiB read) before each step, "
+                             f"{len(draws)} routing draws" if decode else "finalized")
+                            + (", the host enqueues each step while a GPU spin runs ahead of it "
+                               "(events time the kernels, not the Python call overhead)"
+                               if host_ahead else ""))
                            + (", replayed as a captured HIP graph" if graphs else "")
                            + (", fused tail (finalize + residual add + RMSNorm)" if args.fused_tail else "")
                            + (f", {len(chunks)} chunks of {P} tokens" if len(chunks) > 1 else "")
