@@ -157,6 +157,16 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* ds
 #endif
 }
 
+// 4 bytes per lane, written into LDS at dst + 4 * lane.
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t voff,
+                                         int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, static_cast<int>(voff), soff, 0,
+                                           0);
+#endif
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
 // left open).
@@ -248,10 +258,12 @@ struct TileCfg {
   // of K/32 scale bytes 8-byte aligned); the byte-wise fallback for other K
   // issues more, which only makes the waits stricter
   static constexpr int SCQ = WQ ? FN : 0;
-  // blockwise FP8: per k-step, its k-block's scales of this lane's 16 rows
-  // per row fragment (four 16-byte loads) and of each weight fragment (one
-  // 4-byte load), issued at the top of the k-step before its tile loads
-  static constexpr int SAQ = BS ? FM * 4 + FN : 0;
+  // blockwise FP8: the activation scales of a k-step's rows travel with its
+  // activation loads, one 4-byte direct-to-LDS load per wave (its wave row's
+  // rows, 64 lanes: wave tiles of at most 64 rows), into a scale stage of
+  // SC_N floats per activation stage
+  static constexpr int SAQ = BS ? 1 : 0;
+  static constexpr int SC_N = BS ? WM * 64 : 4;
   static constexpr int A_ELEMS = BM * 64;        // uint16 per activation stage
   static constexpr int B_ELEMS = BN * 64;        // uint16 per weight stage
   // k-steps per unrolled loop body: every stage object is then compile-time
@@ -276,10 +288,10 @@ struct TileCfg {
   // prologue loads issued after the activation loads of k-step s / after the
   // weight loads of stage q (whole groups only: conservative)
   static constexpr int pro_after_a(int s) {
-    return B_KS == 1 ? (STAGES - 2 - s) * (A_LD + B_LD) : (STAGES - 2 - s) * A_LD;
+    return B_KS == 1 ? (STAGES - 2 - s) * (A_LD + SAQ + B_LD) : (STAGES - 2 - s) * A_LD;
   }
   static constexpr int pro_after_b(int q) {
-    return B_KS == 1 ? (STAGES - 2 - q) * (A_LD + B_LD)
+    return B_KS == 1 ? (STAGES - 2 - q) * (A_LD + SAQ + B_LD)
                      : (B_STAGES - 2 - q) * B_LD + (STAGES - 1) * A_LD;
   }
   // Loads that may stay in flight at the end of k-step kt with the
@@ -318,6 +330,7 @@ struct TileCfg {
   static_assert(UNROLL <= 12, "unrolled body");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!GATED || (FN % 2 == 0), "gated tiles pair gate and up blocks");
+  static_assert(!BS || WTM <= 64, "one scale load covers a wave row of at most 64 rows");
   static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "whole load instructions");
 };
 
@@ -387,6 +400,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds_b1[Cfg::B_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b2[SB > 2 ? Cfg::B_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b3[SB > 3 ? Cfg::B_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) float lds_c0[Cfg::SC_N];
+  __shared__ __attribute__((aligned(16))) float lds_c1[Cfg::SC_N];
+  __shared__ __attribute__((aligned(16))) float lds_c2[ST > 2 ? Cfg::SC_N : 4];
+  __shared__ __attribute__((aligned(16))) float lds_c3[ST > 3 ? Cfg::SC_N : 4];
   __shared__ int32_t s_mt[1025];
   __shared__ int32_t s_scratch[16];
 
@@ -404,6 +421,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     else if constexpr (s == 1) return lds_b1;
     else if constexpr (s == 2) return lds_b2;
     else return lds_b3;
+  };
+  // blockwise FP8: the activation scale stage beside each activation stage
+  auto c_stage = [&](auto i) -> float* {
+    constexpr int s = decltype(i)::value % ST;
+    if constexpr (s == 0) return lds_c0;
+    else if constexpr (s == 1) return lds_c1;
+    else if constexpr (s == 2) return lds_c2;
+    else return lds_c3;
   };
 
   const int tid = threadIdx.x;
@@ -657,53 +682,52 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       return static_cast<int>((word >> (8u * static_cast<uint32_t>(block & 3))) & 0xFFu);
     };
 
-    // Blockwise FP8: the scales of k-block kb for this lane's rows (A scales
-    // stored k-block-major, [K / 128][a_ld]) and for its weight fragments'
-    // 128-row blocks ([E_l][N_total / 128][K / 128]); a k-step's scales are
-    // loaded at the top of the k-step, before its tile loads, and applied
-    // after its MFMAs: acc += sum_k * a_scale[row] * w_scale.  (Waiting for
-    // them there retires only loads issued before them, which the stage
-    // pipeline has waited for already.)  Reads past either array return zero
-    // (rows past the segment, virtual weight rows past N_out): their results
-    // are never stored.
+    // Blockwise FP8: the scales of k-block kb for the tile's rows (A scales
+    // stored k-block-major, [K / 128][a_ld]) and for the weight fragments'
+    // 128-row blocks ([E_l][N_total / 128][K / 128]), applied after a
+    // k-step's MFMAs: acc += sum_k * a_scale[row] * w_scale.  The row scales
+    // of a k-step ride with its activation loads into the scale stage beside
+    // its activation stage (each wave loads its wave row's 64 rows; reads
+    // past the array return zero, and rows past the segment are never
+    // stored); at the top of the k-step each lane reads its 16 rows' scales
+    // per row fragment from there, before the barrier that frees the stage.
+    // The weight scales are wave-uniform: read through the scalar cache.
     constexpr int BSM = Cfg::BS ? FM : 1, BSN = Cfg::BS ? FN : 1;
     u32x4 bs_a[BSM][4];
     uint32_t bs_w[BSN];
-    // byte offsets: this lane's first row scale (the others at constant
-    // distances, folded into the load instructions) and, wave-uniform, each
-    // weight fragment's block row
-    uint32_t bs_abase = 0;
-    uint32_t bs_woff[BSN];
+    // the uniform index of each weight fragment's scale row (the last block
+    // row for virtual weight rows past N_total, whose results are never
+    // stored)
+    int bs_wblk[BSN];
     const int nkb = K / BK;
     const int nb_rows = N_total / 128;
+    const int wm_u = wave_u / Cfg::WN;
     const __amdgpu_buffer_rsrc_t bs_arsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(A_scales), 0,
         Cfg::BS ? static_cast<int>(static_cast<int64_t>(nkb) * a_ld * 4) : 0, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t bs_wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(static_cast<const uint8_t*>(W_scales) +
-                             (Cfg::BS ? static_cast<int64_t>(e) * nb_rows * nkb * 4 : 0)),
-        0, Cfg::BS ? nb_rows * nkb * 4 : 0, kBufferFlags);
+    const uint32_t* const bs_wsc =
+        static_cast<const uint32_t*>(W_scales) + (Cfg::BS ? static_cast<int64_t>(e) * nb_rows * nkb : 0);
     if constexpr (Cfg::BS) {
-      const int half = lane >> 5;
-      bs_abase = static_cast<uint32_t>(row0 + wm * Cfg::WTM + 4 * half) * 4u;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bs_woff[fn] = __builtin_amdgcn_readfirstlane(
-            static_cast<uint32_t>(wrow_of(b_row0<Cfg>(wn, fn)) / 128) * nkb * 4u);
+        bs_wblk[fn] = __builtin_amdgcn_readfirstlane(
+            min(wrow_of(b_row0<Cfg>(wn, fn)) / 128, nb_rows - 1) * nkb);
     }
     // k-block of k-step kt (the k-order may start at a tile-dependent stage)
     auto kblock = [&](int kt) { return kt0 + krot(kt); };
-    auto load_bscales = [&](int kt) {
+    // this k-step's scales: the rows' from scale stage `cs`, the weights'
+    auto load_bscales = [&](int kt, const float* cs) {
       if constexpr (Cfg::BS) {
         const int kb = kblock(kt);
+        const int half = lane >> 5;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            bs_a[fm][g] = load_u128(bs_arsrc, bs_abase + static_cast<uint32_t>(fm * 32 + 8 * g) * 4u,
-                                    static_cast<int>(kb * a_ld * 4));
+            bs_a[fm][g] = *reinterpret_cast<const u32x4*>(
+                cs + wm * 64 + fm * 32 + 8 * g + 4 * half);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bs_w[fn] = load_u32(bs_wrsrc, bs_woff[fn], kb * 4);
+        for (int fn = 0; fn < FN; ++fn) bs_w[fn] = bs_wsc[bs_wblk[fn] + kb];
       }
     };
 
@@ -717,11 +741,17 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
     // Slice `part` (of SUB) of the activation loads of k-step kt into stage
     // `st`, and of the weight loads of weight stage q into `wst`: the loads
     // are spread over the sub-steps of the k-step that issues them.
-    auto gload_a = [&](uint16_t* st, int kt, int part) {
+    // (blockwise FP8: with the first slice, the k-step's row scales of this
+    // wave's wave row into scale stage `cst`)
+    auto gload_a = [&](uint16_t* st, float* cst, int kt, int part) {
 #pragma unroll
       for (int j = 0; j < Cfg::A_LD; ++j)
         if (Cfg::EARLY ? part == 0 : j % SUB == part)
           lds_dma16(a_rsrc, st + (j * Cfg::NWAVES + wave_u) * 512, a_off[j], (kt0 + krot(kt)) * 128);
+      if constexpr (Cfg::BS)
+        if (part == 0)
+          lds_dma4(bs_arsrc, cst + wm_u * 64,
+                   static_cast<uint32_t>(kblock(kt) * a_ld + row0 + wm_u * Cfg::WTM + lane) * 4u, 0);
     };
     auto gload_b = [&](uint16_t* wst, int q, int part) {
 #pragma unroll
@@ -824,6 +854,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       uint16_t* const cur_a = a_stage(ic<J>{});
       uint16_t* const nxt_a = a_stage(ic<J + 1>{});
       uint16_t* const ld_a = a_stage(ic<J + ST - 1>{});
+      float* const ld_c = c_stage(ic<J + ST - 1>{});
       uint16_t* const cur_b = b_stage(ic<J / BKS>{});
       uint16_t* const nxt_b = b_stage(ic<(J + 1) / BKS>{});
       uint16_t* const ld_b = b_stage(ic<J / BKS + SB - 1>{});
@@ -835,15 +866,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
         rotate_scales();
         load_scales(min(kt / BKS + 1, nq - 1));
       }
-      // blockwise FP8: this k-step's block scales, before its tile loads
-      load_bscales(kt);
+      // blockwise FP8: this k-step's block scales
+      load_bscales(kt, c_stage(ic<J>{}));
       expand0(P);
       const int ln = opaque(lane);
 #pragma unroll
       for (int ks = 0; ks < SUB; ++ks) {
         if (ks + 1 < SUB)
           load_frags(cur_a, cur_b, ln, ks + 1, P, fa[(ks + 1) & 1], fb[(ks + 1) & 1], bq);
-        gload_a(ld_a, kn, ks);
+        gload_a(ld_a, ld_c, kn, ks);
         if constexpr (P == 0) gload_b(ld_b, qn, ks);
         if (ks + 1 == SUB) {
           // this wave's loads that k-step kt + 1 reads landed and its reads
@@ -906,7 +937,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       static_for<ST - 1>([&](auto s) {
 #pragma unroll
         for (int p = 0; p < SUB; ++p) {
-          gload_a(a_stage(s), min(static_cast<int>(s), nk - 1), p);
+          gload_a(a_stage(s), c_stage(s), min(static_cast<int>(s), nk - 1), p);
           gload_b(b_stage(s), min(static_cast<int>(s), nk - 1), p);
         }
       });
@@ -917,7 +948,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_gemm_kernel(
       });
       static_for<ST - 1>([&](auto s) {
 #pragma unroll
-        for (int p = 0; p < SUB; ++p) gload_a(a_stage(s), min(static_cast<int>(s), nk - 1), p);
+        for (int p = 0; p < SUB; ++p)
+          gload_a(a_stage(s), c_stage(s), min(static_cast<int>(s), nk - 1), p);
       });
     }
     wait_vmem<Cfg::WAIT_PRO>();
@@ -1280,7 +1312,7 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
     if (mean_rows >= 16) {
-      if constexpr (A2) return launch_cfg<typename C::WidePG>(g, max_rows, s);
+      if constexpr (A2 || BS) return launch_cfg<typename C::WidePG>(g, max_rows, s);
       else
         return eight ? launch_cfg<typename C::WidePG>(g, max_rows, s)
                      : launch_cfg<typename C::WideG>(g, max_rows, s);
@@ -1290,7 +1322,7 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
   if (mean_rows >= 16) {
-    if constexpr (A2) return launch_cfg<typename C::WideP>(g, max_rows, s);
+    if constexpr (A2 || BS) return launch_cfg<typename C::WideP>(g, max_rows, s);
     else
       return eight ? launch_cfg<typename C::WideP>(g, max_rows, s)
                    : launch_cfg<typename C::Wide>(g, max_rows, s);
