@@ -202,7 +202,7 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
                 break
             if dt < target_s / 8:
                 chunk *= 2
-        if n_draws > 10000:
+        if n_draws > 200000:  # (a bound on the loop; the time target ends it first)
             break
     if len(draws) > 1:
         where = f"{total_tok} tokens from {n_draws} routing draws of {cfg.T} tokens"
