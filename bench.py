@@ -50,6 +50,7 @@ sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -214,6 +215,43 @@ def cpu_baseline(cfg, draws, w, target_s: float, variant=None):
             "kind": "oracle",
             "sample": f"{where} of the same workload, float64 per-token per-expert MLP, "
                       f"{total_s:.1f} s wall"}
+
+
+class TimingEvent:
+    """A HIP event used only to time GPU work: created with
+    hipEventDisableSystemFence, so recording it skips the system-scope fence
+    (a cache write-back and invalidation) that the default event performs,
+    which idles the GPU before the next kernel and leaves it cold caches.  The
+    interface is torch.cuda.Event's record / elapsed_time; the host
+    synchronizes with torch.cuda.synchronize() before reading it."""
+
+    _hip = None
+    _FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._e = ctypes.c_void_p()
+        self._call("hipEventCreateWithFlags", ctypes.byref(self._e), ctypes.c_uint(self._FLAGS))
+
+    def _call(self, fn, *a):
+        rc = getattr(TimingEvent._hip, fn)(*a)
+        if rc != 0:
+            raise RuntimeError(f"{fn} failed ({rc})")
+
+    def record(self, stream=None):
+        import torch
+        s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        self._call("hipEventRecord", self._e, ctypes.c_void_p(s))
+
+    def elapsed_time(self, end) -> float:
+        ms = ctypes.c_float()
+        self._call("hipEventElapsedTime", ctypes.byref(ms), self._e, end._e)
+        return ms.value
+
+    def __del__(self):
+        if self._e:
+            TimingEvent._hip.hipEventDestroy(self._e)
 
 
 def main():
@@ -580,10 +618,10 @@ def main():
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
     # Timed pass 1, the throughput: whole steps, one event pair around each
-    # (an event between two kernels of one stream costs ~5.5 us of idle GPU on
-    # this runtime, so the stage events of pass 2 would inflate short steps)
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    # (an event between two kernels of one stream still leaves the GPU idle a
+    # few microseconds on this runtime, so the stage events of pass 2 would
+    # inflate short steps)
+    step_ev = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -604,8 +642,7 @@ def main():
     # Timed pass 2, the breakdown: the same steps with an event before every
     # stage (not under graph replay)
     stage_steps = args.steps if graphs else min(args.steps, 100)
-    events = [([], [torch.cuda.Event(enable_timing=True) for _ in range(marks_per_step)])
-              for _ in range(stage_steps)]
+    events = [([], [TimingEvent() for _ in range(marks_per_step)]) for _ in range(stage_steps)]
     if not graphs:
         torch.cuda.synchronize()
         for i in range(stage_steps):
