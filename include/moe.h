@@ -559,15 +559,16 @@ int moe_grouped_gemm2_batched(const void* h_batched, const int32_t* expert_num_t
  *   residual[t, :] = bf16(z[t, :])                                  (in place)
  *   out[t, :] = bf16(z[t, :] / sqrt(mean(z[t, :]^2) + eps) * gamma[:])
  * (the norm uses z before the residual's rounding).
- *   y_perm, weights, weights_dtype, map, T, k, H, rsf_fin, shared: as for
- *              moe_finalize (weights may be NULL)
+ *   y_perm, y_rows, weights, weights_dtype, map, T, k, H, rsf_fin, shared:
+ *              as for moe_finalize (weights may be NULL)
  *   residual   (device) bf16 [T, H] in/out (the residual stream)
  *   gamma      (device) bf16 [H] the norm's per-column scale
  *   eps        >= 0
  *   out        (device) bf16 [T, H] out; must not overlap residual, shared
  *              or y_perm; shared must not overlap residual
  * Limits: H a multiple of 8, at most 16384. */
-int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t weights_dtype,
+int moe_finalize_add_rmsnorm(const void* y_perm, int64_t y_rows, const void* weights,
+                             int32_t weights_dtype,
                              const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
                              const void* shared, void* residual, const void* gamma, float eps,
                              void* out, void* stream);
@@ -585,21 +586,22 @@ int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated,
  * the shared-expert add).
  *   out[t, :] = rsf_fin * sum_{j ascending, map[t,j] >= 0} w[t,j] * y[map[t,j], :]
  *               + shared[t, :]
- * fp32 accumulation, one rounding to bf16.  -1 entries are skipped, so rows
- * the map never names are never read.  Every row of out is written (a token
- * with no local route gets 0, or its shared row).
- *   y_perm   (device) bf16 [>= R_l, H]
+ * fp32 accumulation, one rounding to bf16.  -1 entries, and entries at or
+ * past y_rows, are skipped, so no row outside y_perm is read.  Every row of
+ * out is written (a token with no local route gets 0, or its shared row).
+ *   y_perm   (device) bf16 [y_rows, H]: R_pad rows in the standard layout,
+ *            E_l * max_tokens in the batched experts format; may be NULL when
+ *            y_rows is 0
+ *   y_rows   its row count (>= 0)
  *   weights  (device) [T, k] of weights_dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16),
  *            or NULL: every weight is 1 (finalize() with
  *            apply_router_weight_on_input, whose weights went on the inputs)
  *   map      (device) int32 [T, k]
  *   shared   (device) bf16 [T, H] or NULL
  *   out      (device) bf16 [T, H] out; may alias shared exactly (in place),
- *            must not overlap any row of y_perm the map names (checked for
- *            rows [0, T*k), which hold every named row in the standard
- *            layout; the map itself is device memory the host does not read)
+ *            must not overlap y_perm's y_rows rows
  * Limits: H a multiple of 8, k <= 32. */
-int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
+int moe_finalize(const void* y_perm, int64_t y_rows, const void* weights, int32_t weights_dtype,
                  const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
                  const void* shared, void* out, void* stream);
 

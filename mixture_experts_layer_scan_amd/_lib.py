@@ -79,10 +79,11 @@ PROTOTYPES = {
                                          _vp]),
     "moe_grouped_gemm1_act_gathered": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i32, _i64, _i32,
                                                       _i32, _Wp, _i32, _f32, _vp, _vp, _sz, _vp]),
-    "moe_finalize_add_rmsnorm": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp,
+    "moe_finalize_add_rmsnorm": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp,
                                                 _vp, _vp, _f32, _vp, _vp]),
     "moe_grouped_gemm_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
-    "moe_finalize": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "moe_finalize": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp, _i64, _i32, _i32, _f32, _vp, _vp,
+                                    _vp]),
     "moe_fused_experts_unfinalized": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
                                                      _i32, _i32, _f32, _vp, _Wp, _Wp, _Op, _i64,
                                                      _vp, _vp, _vp, _vp, _sz, _vp]),

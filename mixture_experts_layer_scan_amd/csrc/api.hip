@@ -953,17 +953,26 @@ int moe_grouped_gemm_workspace_size(int64_t R_pad, int32_t N_out, int32_t gated,
   return MOE_OK;
 }
 
-int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
+// The rows of gemm2_permuted: non-negative, and their bytes within int64.
+int check_y_rows(int64_t y_rows, int32_t H) {
+  if (y_rows < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "y_rows must be non-negative (y_rows=%lld)", (long long)y_rows);
+  if (y_rows > (int64_t(1) << 62) / (2 * int64_t(H)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "gemm2_permuted is too large (y_rows=%lld)", (long long)y_rows);
+  return MOE_OK;
+}
+
+int moe_finalize(const void* y_perm, int64_t y_rows, const void* weights, int32_t weights_dtype,
                  const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
                  const void* shared, void* out, void* stream) {
   g_err[0] = 0;
   if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens must be non-negative (T=%lld)", (long long)T);
   if (k <= 0 || k > 32) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be in [1, 32] (k=%d)", k);
   if (H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8 (H=%d)", H);
+  MOE_CHECK(check_y_rows(y_rows, H));
   if (weights_dtype != MOE_DTYPE_F32 && weights_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
   if (T == 0) return MOE_OK;
-  MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
+  if (y_rows > 0) MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
   MOE_CHECK(opt_ptr(weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(opt_ptr(shared, "shared"));
@@ -971,18 +980,17 @@ int moe_finalize(const void* y_perm, const void* weights, int32_t weights_dtype,
   const size_t out_bytes = sizeof(uint16_t) * T * H;
   if (shared && shared != out && overlap(shared, out_bytes, out, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out must alias shared exactly or not overlap it");
-  // The map lives on the device, so the host cannot see the largest row it
-  // names: rows [0, T * k) bound it in the standard layout; in the batched
-  // experts format (rows up to E_l * max_tokens) the caller keeps out apart
-  // from the whole buffer, and the Python binding checks the tensor's extent.
-  if (overlap(y_perm, sizeof(uint16_t) * T * k * H, out, out_bytes))
+  // every row the kernel may read: map entries past y_rows count as -1
+  if (overlap(y_perm, sizeof(uint16_t) * y_rows * H, out, out_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap gemm2_permuted");
-  hipError_t e = moe::launch_finalize(y_perm, weights, weights_dtype == MOE_DTYPE_BF16, map, T, k, H,
-                                      rsf_fin, shared, out, static_cast<hipStream_t>(stream));
+  hipError_t e = moe::launch_finalize(y_perm, y_rows, weights, weights_dtype == MOE_DTYPE_BF16, map,
+                                      T, k, H, rsf_fin, shared, out,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_finalize");
 }
 
-int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t weights_dtype,
+int moe_finalize_add_rmsnorm(const void* y_perm, int64_t y_rows, const void* weights,
+                             int32_t weights_dtype,
                              const int32_t* map, int64_t T, int32_t k, int32_t H, float rsf_fin,
                              const void* shared, void* residual, const void* gamma, float eps,
                              void* out, void* stream) {
@@ -993,10 +1001,11 @@ int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t we
     return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 8, at most %d (H=%d)",
                 moe::kTailMaxH, H);
   if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  MOE_CHECK(check_y_rows(y_rows, H));
   if (weights_dtype != MOE_DTYPE_F32 && weights_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "weights must be float32 or bfloat16 (dtype %d)", weights_dtype);
   if (T == 0) return MOE_OK;
-  MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
+  if (y_rows > 0) MOE_CHECK(need_ptr(y_perm, "gemm2_permuted"));
   MOE_CHECK(opt_ptr(weights, "expert_weights"));
   MOE_CHECK(need_ptr(map, "map"));
   MOE_CHECK(opt_ptr(shared, "shared"));
@@ -1010,10 +1019,11 @@ int moe_finalize_add_rmsnorm(const void* y_perm, const void* weights, int32_t we
     return fail(MOE_ERR_DESTINATION_CONFLICT, "shared must not overlap residual (written in place)");
   if (shared && overlap(shared, row_bytes, out, row_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out must not overlap shared");
-  const size_t y_bytes = sizeof(uint16_t) * T * k * H;
+  const size_t y_bytes = sizeof(uint16_t) * y_rows * H;
   if (overlap(y_perm, y_bytes, out, row_bytes) || overlap(y_perm, y_bytes, residual, row_bytes))
     return fail(MOE_ERR_DESTINATION_CONFLICT, "out and residual must not overlap gemm2_permuted");
-  hipError_t e = moe::launch_finalize_add_rmsnorm(y_perm, weights, weights_dtype == MOE_DTYPE_BF16,
+  hipError_t e = moe::launch_finalize_add_rmsnorm(y_perm, y_rows, weights,
+                                                  weights_dtype == MOE_DTYPE_BF16,
                                                   map, T, k, H, rsf_fin, shared, residual, gamma,
                                                   eps, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_finalize_add_rmsnorm");
@@ -1410,7 +1420,7 @@ int moe_fused_experts(const float* logits, const void* x, int64_t T, int32_t H, 
       if (e != hipSuccess) return hip_fail(e, "shared gemm2");
       shared_out = s_y;
     }
-    hipError_t e = moe::launch_finalize(b.x_perm, o.weight_on_input ? nullptr : b.wts, 0, b.map,
+    hipError_t e = moe::launch_finalize(b.x_perm, b.rows, o.weight_on_input ? nullptr : b.wts, 0, b.map,
                                         n, k, H, rsf_fin, shared_out,
                                         static_cast<uint16_t*>(out) + t0 * H, s);
     if (e != hipSuccess) return hip_fail(e, "finalize");

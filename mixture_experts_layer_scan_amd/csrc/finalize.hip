@@ -12,7 +12,8 @@
 // still spreads over the chip.  The routes of the token (map and weights,
 // k <= 32) are staged once in LDS; a thread issues the loads of up to 8
 // routes before it adds any of them, so their latencies overlap.
-// Entries of -1 are skipped, so rows the map never names are never read.
+// Entries of -1, and entries at or past the caller's row count of y, are
+// skipped, so no row outside y is ever read.
 // Accumulation is fp32 in j order, rounded once to bf16.  Without weights
 // (NULL) every route counts once: finalize() with apply_router_weight_on_input,
 // whose weights were applied to the inputs.
@@ -54,14 +55,16 @@ template <bool W_BF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__ y,
                                                        const void* __restrict__ wts,
                                                        const int32_t* __restrict__ map,
-                                                       int64_t T, int k, int H8, float rsf_fin,
-                                                       const uint4* shared, uint4* out) {
+                                                       int64_t y_rows, int64_t T, int k, int H8,
+                                                       float rsf_fin, const uint4* shared,
+                                                       uint4* out) {
   __shared__ int32_t s_row[32];
   __shared__ float s_w[32];
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     __syncthreads();  // the previous token's routes are no longer read
     if (threadIdx.x < k) {
-      s_row[threadIdx.x] = map[t * k + threadIdx.x];
+      const int32_t r = map[t * k + threadIdx.x];
+      s_row[threadIdx.x] = r < y_rows ? r : -1;
       s_w[threadIdx.x] = !wts ? 1.0f
           : W_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
                    : static_cast<const float*>(wts)[t * k + threadIdx.x];
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint4* __restrict__
 template <bool W_BF16>
 __global__ __launch_bounds__(256) void finalize_norm_kernel(
     const uint4* __restrict__ y, const void* __restrict__ wts, const int32_t* __restrict__ map,
-    int64_t T, int k, int H8, float rsf_fin, const uint4* shared, uint4* residual,
+    int64_t y_rows, int64_t T, int k, int H8, float rsf_fin, const uint4* shared, uint4* residual,
     const uint4* __restrict__ gamma, float eps, uint4* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) float s_z[];  // [8 * H8]
   __shared__ int32_t s_row[32];
@@ -116,7 +119,8 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     __syncthreads();  // the previous token's routes and sums are no longer read
     if (threadIdx.x < k) {
-      s_row[threadIdx.x] = map[t * k + threadIdx.x];
+      const int32_t r = map[t * k + threadIdx.x];
+      s_row[threadIdx.x] = r < y_rows ? r : -1;
       s_w[threadIdx.x] = !wts ? 1.0f
           : W_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wts)[t * k + threadIdx.x])
                    : static_cast<const float*>(wts)[t * k + threadIdx.x];
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
 
 }  // namespace
 
-hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf16,
+hipError_t launch_finalize_add_rmsnorm(const void* y, int64_t y_rows, const void* w, int w_is_bf16,
                                        const int32_t* map, int64_t T, int k, int H, float rsf_fin,
                                        const void* shared, void* residual, const void* gamma,
                                        float eps, void* out, hipStream_t s) {
@@ -195,20 +199,20 @@ hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf
   if (e != hipSuccess) return e;
   if (w_is_bf16)
     hipLaunchKernelGGL(finalize_norm_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, T, k, H8,
+                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, y_rows, T, k, H8,
                        rsf_fin, static_cast<const uint4*>(shared), static_cast<uint4*>(residual),
                        static_cast<const uint4*>(gamma), eps, static_cast<uint4*>(out));
   else
     hipLaunchKernelGGL(finalize_norm_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, T, k, H8,
+                       dim3(threads), lds, s, static_cast<const uint4*>(y), w, map, y_rows, T, k, H8,
                        rsf_fin, static_cast<const uint4*>(shared), static_cast<uint4*>(residual),
                        static_cast<const uint4*>(gamma), eps, static_cast<uint4*>(out));
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
-                           int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,
-                           hipStream_t s) {
+hipError_t launch_finalize(const void* y, int64_t y_rows, const void* w, int w_is_bf16,
+                           const int32_t* map, int64_t T, int k, int H, float rsf_fin,
+                           const void* shared, void* out, hipStream_t s) {
   const int H8 = H / 8;
   const int threads = H8 >= 256 ? 256 : ((H8 + 63) / 64) * 64;
   const int64_t blocks = T < 16384 ? T : 16384;
@@ -218,11 +222,11 @@ hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const in
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(split));
   if (w_is_bf16)
     hipLaunchKernelGGL(finalize_kernel<true>, grid, dim3(threads),
-                       0, s, static_cast<const uint4*>(y), w, map, T, k, H8, rsf_fin,
+                       0, s, static_cast<const uint4*>(y), w, map, y_rows, T, k, H8, rsf_fin,
                        static_cast<const uint4*>(shared), static_cast<uint4*>(out));
   else
     hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(threads),
-                       0, s, static_cast<const uint4*>(y), w, map, T, k, H8, rsf_fin,
+                       0, s, static_cast<const uint4*>(y), w, map, y_rows, T, k, H8, rsf_fin,
                        static_cast<const uint4*>(shared), static_cast<uint4*>(out));
   return hipGetLastError();
 }

@@ -182,12 +182,13 @@ hipError_t launch_decode_route_gemm1(const float* logits, int64_t T, int E, int 
                                      uint16_t* w_bf16, const int32_t* emap, int32_t* map,
                                      int32_t* offsets, int32_t* inv, int64_t R_pad,
                                      const GemmArgs& g, hipStream_t s);
-// w == NULL: every weight is 1 (the weights were applied to the inputs)
-hipError_t launch_finalize(const void* y, const void* w, int w_is_bf16, const int32_t* map,
-                           int64_t T, int k, int H, float rsf_fin, const void* shared, void* out,
-                           hipStream_t s);
+// w == NULL: every weight is 1 (the weights were applied to the inputs);
+// y has y_rows rows, map entries at or past them count as -1
+hipError_t launch_finalize(const void* y, int64_t y_rows, const void* w, int w_is_bf16,
+                           const int32_t* map, int64_t T, int k, int H, float rsf_fin,
+                           const void* shared, void* out, hipStream_t s);
 constexpr int kTailMaxH = 16384;  // the fused tail keeps one token's fp32 row in LDS
-hipError_t launch_finalize_add_rmsnorm(const void* y, const void* w, int w_is_bf16,
+hipError_t launch_finalize_add_rmsnorm(const void* y, int64_t y_rows, const void* w, int w_is_bf16,
                                        const int32_t* map, int64_t T, int k, int H, float rsf_fin,
                                        const void* shared, void* residual, const void* gamma,
                                        float eps, void* out, hipStream_t s);

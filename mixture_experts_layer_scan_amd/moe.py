@@ -916,12 +916,7 @@ def moe_finalize(gemm2_permuted: torch.Tensor, expert_weights: Optional[torch.Te
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
-    # every row the map may name (the batched layout's reach past T * k rows)
-    y0, y1 = gemm2_permuted.data_ptr(), gemm2_permuted.data_ptr() + gemm2_permuted.nbytes
-    o0, o1 = out.data_ptr(), out.data_ptr() + out.nbytes
-    if T > 0 and o0 < y1 and y0 < o1:
-        raise ValueError("out must not overlap gemm2_permuted")
-    _check(lib().moe_finalize(gemm2_permuted.data_ptr(), w_ptr, wdt,
+    _check(lib().moe_finalize(gemm2_permuted.data_ptr(), gemm2_permuted.shape[0], w_ptr, wdt,
                               map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
                               out.data_ptr(), _stream(stream)), "moe_finalize")
     return out
@@ -933,8 +928,10 @@ def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: Optio
                              shared: Optional[torch.Tensor] = None,
                              out: Optional[torch.Tensor] = None, stream=None):
     """Fused tail: residual += finalize(...) (in place); out = RMSNorm(residual) * gamma.
-    -> (out bf16 [T, H], residual)."""
+    -> (out bf16 [T, H], residual).  gemm2_permuted as for moe_finalize."""
     _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16)
+    if gemm2_permuted.dim() == 3:
+        gemm2_permuted = gemm2_permuted.view(-1, gemm2_permuted.shape[2])
     if gemm2_permuted.dim() != 2:
         raise ValueError("gemm2_permuted must be rank-2")
     H = gemm2_permuted.shape[1]
@@ -951,7 +948,8 @@ def moe_finalize_add_rmsnorm(gemm2_permuted: torch.Tensor, expert_weights: Optio
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
-    _check(lib().moe_finalize_add_rmsnorm(gemm2_permuted.data_ptr(), w_ptr, wdt,
+    _check(lib().moe_finalize_add_rmsnorm(gemm2_permuted.data_ptr(), gemm2_permuted.shape[0],
+                                          w_ptr, wdt,
                                           map.data_ptr(), T, k, H, float(rsf_fin), _ptr(shared),
                                           residual.data_ptr(), gamma.data_ptr(), float(eps),
                                           out.data_ptr(), _stream(stream)),

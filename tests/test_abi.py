@@ -163,31 +163,36 @@ def test_gemm_errors(L):
 
 def test_finalize_errors(L):
     f = L.moe_finalize
-    assert f(P, P, 1, P, -1, 2, 128, 1.0, None, P * 8, None) == INVALID
-    assert f(P, P, 1, P, 16, 0, 128, 1.0, None, P * 8, None) == INVALID
-    assert f(P, P, 3, P, 16, 2, 128, 1.0, None, P * 8, None) == UNSUPPORTED  # int32 weights
-    assert f(P, P, 1, P, 16, 2, 130, 1.0, None, P * 8, None) == INVALID
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, P + 256, None) == CONFLICT  # out inside y
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, P * 4 + 16, P * 4, None) == CONFLICT  # partial alias
-    assert f(P, P, 1, P, 0, 2, 128, 1.0, None, None, None) == OK  # T = 0
+    assert f(P, 32, P, 1, P, -1, 2, 128, 1.0, None, P * 8, None) == INVALID
+    assert f(P, 32, P, 1, P, 16, 0, 128, 1.0, None, P * 8, None) == INVALID
+    assert f(P, 32, P, 3, P, 16, 2, 128, 1.0, None, P * 8, None) == UNSUPPORTED  # int32 weights
+    assert f(P, 32, P, 1, P, 16, 2, 130, 1.0, None, P * 8, None) == INVALID
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, P + 256, None) == CONFLICT  # out inside y
+    # the check spans y_rows rows of y (here 33 x 256 bytes), not T * k
+    assert f(P, 33, P, 1, P, 16, 2, 128, 1.0, None, P + 32 * 256, None) == CONFLICT
+    assert f(P, -1, P, 1, P, 16, 2, 128, 1.0, None, P * 8, None) == INVALID  # y_rows < 0
+    assert f(P, 1 << 60, P, 1, P, 16, 2, 128, 1.0, None, P * 8, None) == INVALID  # y too large
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, P * 4 + 16, P * 4, None) == CONFLICT  # partial alias
+    assert f(P, 32, P, 1, P, 0, 2, 128, 1.0, None, None, None) == OK  # T = 0
 
 
 def test_finalize_add_rmsnorm_errors(L):
     f = L.moe_finalize_add_rmsnorm
-    # (y, w, wdt, map, T, k, H, rsf, shared, residual, gamma, eps, out, stream)
+    # (y, y_rows, w, wdt, map, T, k, H, rsf, shared, residual, gamma, eps, out, stream)
     R, G, O = P * 8, P * 16, P * 24
-    assert f(P, P, 1, P, -1, 2, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
-    assert f(P, P, 1, P, 16, 0, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
-    assert f(P, P, 1, P, 16, 2, 130, 1.0, None, R, G, 1e-6, O, None) == INVALID
-    assert f(P, P, 1, P, 16, 2, 16392, 1.0, None, R, G, 1e-6, O, None) == INVALID  # H too large
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, -1.0, O, None) == INVALID  # eps < 0
-    assert f(P, P, 3, P, 16, 2, 128, 1.0, None, R, G, 1e-6, O, None) == UNSUPPORTED
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, None, G, 1e-6, O, None) == INVALID  # no residual
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, None, 1e-6, O, None) == INVALID  # no gamma
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, R, None) == CONFLICT  # out == residual
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, R, R, G, 1e-6, O, None) == CONFLICT  # shared == residual
-    assert f(P, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, P + 256, None) == CONFLICT  # out in y
-    assert f(P, P, 1, P, 0, 2, 128, 1.0, None, None, None, 1e-6, None, None) == OK  # T = 0
+    assert f(P, 32, P, 1, P, -1, 2, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, 32, P, 1, P, 16, 0, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, 32, P, 1, P, 16, 2, 130, 1.0, None, R, G, 1e-6, O, None) == INVALID
+    assert f(P, 32, P, 1, P, 16, 2, 16392, 1.0, None, R, G, 1e-6, O, None) == INVALID  # H too large
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, R, G, -1.0, O, None) == INVALID  # eps < 0
+    assert f(P, 32, P, 3, P, 16, 2, 128, 1.0, None, R, G, 1e-6, O, None) == UNSUPPORTED
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, None, G, 1e-6, O, None) == INVALID  # no residual
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, R, None, 1e-6, O, None) == INVALID  # no gamma
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, R, None) == CONFLICT  # out == residual
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, R, R, G, 1e-6, O, None) == CONFLICT  # shared == residual
+    assert f(P, 32, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, P + 256, None) == CONFLICT  # out in y
+    assert f(P, -1, P, 1, P, 16, 2, 128, 1.0, None, R, G, 1e-6, O, None) == INVALID  # y_rows < 0
+    assert f(P, 32, P, 1, P, 0, 2, 128, 1.0, None, None, None, 1e-6, None, None) == OK  # T = 0
 
 
 def test_fused_errors(L):

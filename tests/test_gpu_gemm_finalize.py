@@ -206,6 +206,46 @@ def test_finalize_in_place_over_shared_and_rsf():
     assert rel_fro(host_f64(out), ref) < TOL
 
 
+def test_finalize_reads_only_y_rows():
+    # y_perm holds R rows of a larger buffer whose rows past R are NaN bits;
+    # map entries naming those rows count as -1 (nothing read), and an out
+    # placed right after y's R rows is accepted although T * k > R (the
+    # batched experts format's shape: E_l * max_tokens rows below T * k)
+    T, k, H, R = 40, 4, 256, 96
+    logits = synth.normal_f32(17, 1, (T, 8))
+    _, w = oracle.route(logits, k, 0, True, 1.0)
+    rng = np.random.default_rng(17)
+    m = rng.integers(-1, R + 32, size=(T, k)).astype(np.int32)   # some entries >= R
+    assert (m >= R).any() and T * k > R
+    buf = torch.empty((R + 32 + T) * H, dtype=torch.bfloat16, device="cuda")
+    y = synth.normal_bf16(17, 2, (R, H))
+    bits = np.full((R + 32, H), NAN_BITS, dtype=np.uint16)
+    bits[:R] = y
+    buf[:(R + 32) * H].copy_(dev_bf16(bits).view(-1))
+    y_dev = buf[:R * H].view(R, H)
+    out = buf[R * H:(R + T) * H].view(T, H)        # overlaps the NaN rows, not y
+    w_dev = dev(w.astype(np.float32))
+    m_dev = dev(m)
+    moe.moe_finalize(y_dev, w_dev, m_dev, 1.0, None, out=out)
+    torch.cuda.synchronize()
+    m_ref = np.where(m < R, m, -1).astype(np.int32)
+    ref = oracle.finalize(y, host_f64(w_dev), m_ref, 1.0, None)
+    got = host_f64(out)
+    assert np.all(np.isfinite(got)) and rel_fro(got, ref) < TOL
+    # the fused tail the same way
+    res = synth.normal_bf16(17, 6, (T, H))
+    gamma = synth.normal_bf16(17, 7, (H,), mean=1.0, std=0.2)
+    res_dev = dev_bf16(res)
+    out2 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_finalize_add_rmsnorm(y_dev, w_dev, m_dev, res_dev, dev_bf16(gamma), 1e-6, 1.0,
+                                 None, out=out2)
+    torch.cuda.synchronize()
+    ref_res, ref_out = oracle.finalize_add_rmsnorm(y, host_f64(w_dev), m_ref, res, gamma, 1e-6,
+                                                   1.0, None)
+    assert rel_fro(host_f64(res_dev), ref_res) < TOL
+    assert np.all(np.isfinite(host_f64(out2))) and rel_fro(host_f64(out2), ref_out) < TOL
+
+
 @pytest.mark.parametrize("mxfp4", [False, True], ids=["bf16", "mxfp4"])
 def test_tail_round_split(mxfp4):
     """Whole-k tiles (128x256, >= 512 rows per expert) whose count leaves a
