@@ -24,6 +24,11 @@ two bf16 roundings fall on either side of a rounding midpoint.  One step is
 few percent of the token (seen: an element near 4.55 with a static scale of
 0.03, one step = 3.2 % of its token).  So the per-token bar for FP8
 activations is 6e-2, and the pooled bar stays 1e-2 (3e-2 with MXFP4 weights).
+
+Ten fixed layers add the limits and the degenerate shapes: 1024 experts with
+top-32 (decode- and prefill-sized, all local or a scattered subset, bf16,
+MXFP4, FP8, blockwise FP8, two-term, batched), k = E, a single expert, and a
+single local expert of 256, whose tokens mostly have nothing to add.
 """
 import gc
 
@@ -86,7 +91,30 @@ def _name(c: dict) -> str:
             f"{'_sh' + str(c['shared_I']) if c['shared_I'] else ''}")
 
 
-CASES = [_draw(i) for i in range(N_LAYERS)]
+def _fixed(seed, T, E, k, H, I, El=None, mxfp4=False, score=0, shared_I=0):
+    c = {"seed": seed, "E": E, "k": k, "T": T, "H": H, "I": I, "mxfp4": mxfp4, "score": score,
+         "renormalize": True, "rsf": 2.5 if score else 1.0, "ties": False, "shared_I": shared_I,
+         "El": E, "emap": None}
+    if El is not None:
+        emap = np.full(E, -1, dtype=np.int32)
+        emap[np.random.default_rng(seed).choice(E, size=El, replace=False)] = np.arange(El)
+        c["El"], c["emap"] = El, emap
+    return c
+
+
+# the limits and degenerate shapes: 1024 experts with top-32 (decode-sized
+# and prefill-sized, all local and a scattered tenth), k = E, one expert, one
+# local expert of many
+EXTREME = [
+    _fixed(9900, 2, 1024, 32, 128, 64),
+    _fixed(9901, 300, 1024, 32, 256, 128, El=100, score=1),
+    _fixed(9902, 64, 1024, 32, 128, 64, mxfp4=True),
+    _fixed(9903, 37, 4, 4, 256, 128),
+    _fixed(9904, 33, 1, 1, 128, 64, shared_I=64),
+    _fixed(9905, 200, 256, 8, 256, 128, El=1, score=1),
+]
+
+CASES = [_draw(i) for i in range(N_LAYERS)] + EXTREME
 
 
 @pytest.mark.parametrize("c", CASES, ids=[_name(c) for c in CASES])
@@ -182,7 +210,24 @@ def _vname(c: dict) -> str:
             f"{'_oninput' if c['on_input'] else ''}{'_static' if c['static'] else ''}")
 
 
-VCASES = [_draw_variant(i) for i in range(N_LAYERS)]
+def _vfixed(seed, fmt, T, E, k, H, I, El=None, **opt):
+    c = _fixed(seed, T, E, k, H, I, El=El, score=1)
+    c.update(fmt=fmt, act="silu", clamp=0.0, chunk=0, batched=False, on_input=False,
+             static=False)
+    c.update(opt)
+    return c
+
+
+# the quantized formats at the routing limits, and the batched layout with
+# top-32 over a scattered map
+VEXTREME = [
+    _vfixed(9950, "fp8", 64, 1024, 32, 256, 128),
+    _vfixed(9951, "block", 300, 512, 16, 256, 256, El=64),
+    _vfixed(9952, "x2", 2, 1024, 32, 256, 256),
+    _vfixed(9953, "bf16", 100, 1024, 32, 128, 64, El=200, batched=True, act="gelu"),
+]
+
+VCASES = [_draw_variant(i) for i in range(N_LAYERS)] + VEXTREME
 # the oracle checks a spread of tokens (first and last included) of the large layers
 ORACLE_TOKENS = 192
 
