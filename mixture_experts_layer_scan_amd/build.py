@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -26,6 +27,11 @@ SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "decode_gemm.hip",
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# A kernel whose registers spill beyond this many bytes of scratch per lane
+# fails the build: a spill that size inside a k-loop costs tens of times the
+# kernel's time (the tiles that keep a few spilled registers stay below it).
+MAX_SCRATCH_BYTES = 128
+
 
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -34,15 +40,41 @@ def hipcc() -> str:
     return path
 
 
+def _scratch_use(lines) -> dict:
+    """Scratch bytes per lane of each kernel, from the compiler's resource
+    usage remarks (a "Function Name" line, then its "ScratchSize" line)."""
+    use, fn = {}, None
+    for l in lines:
+        if "Function Name:" in l:
+            fn = l.split("Function Name:", 1)[1].split("[-Rpass")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in l and fn is not None:
+            use[fn] = int(l.split("ScratchSize [bytes/lane]:", 1)[1].split("[-Rpass")[0])
+    return use
+
+
 def _compile(src: str, obj: str, extra) -> None:
     cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-I", INCLUDE, "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *extra, "-c", src,
-           "-o", obj]
+           "-I", INCLUDE, "-Wall", "-Wno-unused-function", *DEVICE_FLAGS,
+           "-Rpass-analysis=kernel-resource-usage", *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [l for l in (r.stderr or "").splitlines() if noise not in l]
+    lines = (r.stderr or "").splitlines()
+    spills = {f: b for f, b in _scratch_use(lines).items() if b > MAX_SCRATCH_BYTES}
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill more than {MAX_SCRATCH_BYTES} bytes of scratch "
+                           f"per lane: " + ", ".join(f"{f} ({b})" for f, b in sorted(spills.items())))
+    # drop the remarks with their source excerpts, and the host pass's note
+    # on the device-only feature flag
+    msgs, in_remark = [], False
+    for l in lines:
+        if "-Rpass-analysis=kernel-resource-usage" in l:
+            in_remark = True
+        elif in_remark and re.match(r"^\s*(\d+\s*)?\|", l):
+            pass
+        elif "'-packed-fp32-ops' is not a recognized feature" not in l:
+            in_remark = False
+            msgs.append(l)
     if msgs:
         sys.stderr.write("\n".join(msgs) + "\n")
 

@@ -1263,9 +1263,11 @@ struct Configs {
   // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
   // each): with two waves per SIMD one computes while the other waits on its
   // loads (measured: 5 % faster for bf16, 17 % for fp8 than four waves).
-  // MXFP4 weights and blockwise FP8 keep four (their scale loads, expansion
-  // registers, k-block sums).
-  static constexpr int BIG_WM = (WQ || BS) ? 2 : 4;
+  // MXFP4 weights with FP8 activations and blockwise FP8 keep four (their
+  // scale loads, k-block sums).  MXFP4 weights with bf16 activations take
+  // eight: in four waves the 128 accumulators per lane beside the e2m1
+  // expansion went to scratch, 50 times slower.
+  static constexpr int BIG_WM = (BS || (WQ && F8)) ? 2 : 4;
   //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
   using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2, BS>;
   using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2, BS>;
@@ -1306,13 +1308,16 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   // k-block sums and block scales beside the accumulators do not fit in
   // registers)
   const bool eight = BS || ((WQ || F8) && !may_split && !(WQ && F8 && g.gated));
-  // (two-term activations: always the eight-wave tile in that range; with one
-  // wave row their doubled A fragments would not fit in registers)
+  // (two-term activations, and MXFP4 weights with bf16 activations: always
+  // the eight-wave tile in that range; with one wave row the doubled A
+  // fragments, or the four row fragments beside the e2m1 expansion, do not
+  // fit in registers, and the latter went to scratch, 30 times slower)
+  constexpr bool always_eight = A2 || BS || (WQ && !F8);
   if (g.gated) {
     if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
     if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
     if (mean_rows >= 16) {
-      if constexpr (A2 || BS) return launch_cfg<typename C::WidePG>(g, max_rows, s);
+      if constexpr (always_eight) return launch_cfg<typename C::WidePG>(g, max_rows, s);
       else
         return eight ? launch_cfg<typename C::WidePG>(g, max_rows, s)
                      : launch_cfg<typename C::WideG>(g, max_rows, s);
@@ -1322,7 +1327,7 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
   if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
   if (mean_rows >= 16) {
-    if constexpr (A2 || BS) return launch_cfg<typename C::WideP>(g, max_rows, s);
+    if constexpr (always_eight) return launch_cfg<typename C::WideP>(g, max_rows, s);
     else
       return eight ? launch_cfg<typename C::WideP>(g, max_rows, s)
                    : launch_cfg<typename C::Wide>(g, max_rows, s);
