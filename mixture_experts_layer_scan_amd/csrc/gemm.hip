@@ -1263,11 +1263,12 @@ struct Configs {
   // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
   // each): with two waves per SIMD one computes while the other waits on its
   // loads (measured: 5 % faster for bf16, 17 % for fp8 than four waves).
-  // MXFP4 weights with FP8 activations and blockwise FP8 keep four (their
-  // scale loads, k-block sums).  MXFP4 weights with bf16 activations take
-  // eight: in four waves the 128 accumulators per lane beside the e2m1
-  // expansion went to scratch, 50 times slower.
-  static constexpr int BIG_WM = (BS || (WQ && F8)) ? 2 : 4;
+  // MXFP4 weights with FP8 activations keep four (their scale loads).
+  // MXFP4 weights with bf16 activations take eight: in four waves the 128
+  // accumulators per lane beside the e2m1 expansion went to scratch, 50
+  // times slower.  Blockwise FP8 takes eight as well (20 % faster than four,
+  // its k-block sums spilling a few registers a lane).
+  static constexpr int BIG_WM = (WQ && F8) ? 2 : 4;
   //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
   using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2, BS>;
   using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2, BS>;
