@@ -1272,8 +1272,6 @@ struct Configs {
   //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
   using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2, BS>;
   using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2, BS>;
-  using Mid   = TileCfg<128, 128, 2, 2, 2, false, WQ, 8, F8, A2, BS>;
-  using MidG  = TileCfg<128, 128, 2, 2, 2, true, WQ, 8, F8, A2, BS>;
   using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8, A2, BS>;
   using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8, A2, BS>;
   // the same tile in eight waves (2 x 4) when no split is possible: the
@@ -1287,11 +1285,15 @@ struct Configs {
 
 // Tile shape from the mean rows per local expert (the host cannot see the
 // real counts without a device round trip):
-//   >= 128  MFMA-bound: square-ish tiles, weight slices shared by GM m-tiles
+//   >= 128  MFMA-bound: the 128x256 tile, weight slices shared by GM m-tiles
+//           (from 128 rows on it is 4-29 % faster than a 128x128 tile)
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
-//   < 16    decode: short tiles with split reductions.
-constexpr int64_t kDecodeMeanRows = 16;
+//   < 16    short tiles with split reductions; bf16 under 8 rows the whole-k
+//           decode kernel (from 8 to 15 rows the split tiles are up to 28 %
+//           faster; at 8 the two tie).
+constexpr int64_t kDecodeMeanRows = 8;
+constexpr int64_t kThinMeanRows = 16;
 
 template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
@@ -1315,9 +1317,8 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   // fit in registers, and the latter went to scratch, 30 times slower)
   constexpr bool always_eight = A2 || BS || (WQ && !F8);
   if (g.gated) {
-    if (mean_rows >= 512) return launch_cfg<typename C::BigG>(g, max_rows, s);
-    if (mean_rows >= 128) return launch_cfg<typename C::MidG>(g, max_rows, s);
-    if (mean_rows >= 16) {
+    if (mean_rows >= 128) return launch_cfg<typename C::BigG>(g, max_rows, s);
+    if (mean_rows >= kThinMeanRows) {
       if constexpr (always_eight) return launch_cfg<typename C::WidePG>(g, max_rows, s);
       else
         return eight ? launch_cfg<typename C::WidePG>(g, max_rows, s)
@@ -1325,9 +1326,8 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
     }
     return launch_cfg<typename C::ThinG>(g, max_rows, s);
   }
-  if (mean_rows >= 512) return launch_cfg<typename C::Big>(g, max_rows, s);
-  if (mean_rows >= 128) return launch_cfg<typename C::Mid>(g, max_rows, s);
-  if (mean_rows >= 16) {
+  if (mean_rows >= 128) return launch_cfg<typename C::Big>(g, max_rows, s);
+  if (mean_rows >= kThinMeanRows) {
     if constexpr (always_eight) return launch_cfg<typename C::WideP>(g, max_rows, s);
     else
       return eight ? launch_cfg<typename C::WideP>(g, max_rows, s)
