@@ -1261,17 +1261,15 @@ template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 struct Configs {
   static constexpr int S3 = 3;  // activation stages of the 128-row tiles
   // The MFMA-bound 128x256 tile runs eight waves (4 x 2, a 32 x 128 block
-  // each): with two waves per SIMD one computes while the other waits on its
-  // loads (measured: 5 % faster for bf16, 17 % for fp8 than four waves).
-  // MXFP4 weights with FP8 activations keep four (their scale loads).
-  // MXFP4 weights with bf16 activations take eight: in four waves the 128
-  // accumulators per lane beside the e2m1 expansion went to scratch, 50
-  // times slower.  Blockwise FP8 takes eight as well (20 % faster than four,
-  // its k-block sums spilling a few registers a lane).
-  static constexpr int BIG_WM = (WQ && F8) ? 2 : 4;
-  //                          BM   BN  WM      WN ST  gated  WQ  GM  F8
-  using Big   = TileCfg<128, 256, BIG_WM, 2, S3, false, WQ, 8, F8, A2, BS>;
-  using BigG  = TileCfg<128, 256, BIG_WM, 2, S3, true, WQ, 8, F8, A2, BS>;
+  // each) in every format: with two waves per SIMD one computes while the
+  // other waits on its loads.  Against four waves (2 x 2): bf16 5 % faster,
+  // FP8 17 %, blockwise FP8 20 % (its k-block sums spill a few registers a
+  // lane), FP8 or two-term activations with MXFP4 weights 4-22 %; MXFP4
+  // weights with bf16 activations 50 times, since in four waves their 128
+  // accumulators per lane beside the e2m1 expansion went to scratch.
+  //                          BM   BN  WM WN ST  gated  WQ  GM  F8
+  using Big   = TileCfg<128, 256, 4, 2, S3, false, WQ, 8, F8, A2, BS>;
+  using BigG  = TileCfg<128, 256, 4, 2, S3, true, WQ, 8, F8, A2, BS>;
   using Wide  = TileCfg<128, 256, 1, 4, S3, false, WQ, 1, F8, A2, BS>;
   using WideG = TileCfg<128, 256, 1, 4, S3, true, WQ, 1, F8, A2, BS>;
   // the same tile in eight waves (2 x 4) when no split is possible: the
