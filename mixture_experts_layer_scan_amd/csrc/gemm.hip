@@ -1300,6 +1300,10 @@ hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   // bf16 decode batches: whole-k weight slices per workgroup, no split
   if constexpr (!WQ && !F8)
     if (mean_rows < kDecodeMeanRows && decode_gemm_fits(g)) return launch_decode_gemm(g, s);
+  // FP8 decode batches (per-row and per-channel scales): the same, on FP8
+  if constexpr (!WQ && F8 && !A2 && !BS)
+    if (mean_rows < kDecodeMeanRows && decode_gemm_fp8_fits(g))
+      return launch_decode_gemm_fp8(g, s);
   // can this call split its reductions (two fp32 slices in the workspace)?
   const int64_t slice = g.R_pad * (g.gated ? 2 * int64_t(g.N_out) : g.N_out) * 4;
   const bool may_split = g.split_ws != nullptr && g.R_pad <= 65535 &&

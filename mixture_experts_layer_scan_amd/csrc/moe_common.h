@@ -171,6 +171,10 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int64_t max_rows, hipStream_t 
 // reduction.  decode_gemm_fits: K a multiple of 256, N_out of 8 (gated) or 16.
 bool decode_gemm_fits(const GemmArgs& g);
 hipError_t launch_decode_gemm(const GemmArgs& g, hipStream_t s);
+// The same for FP8 E4M3 rows and weights with per-row and per-weight-row
+// scales (no MXFP4, two-term or blockwise): K a multiple of 512.
+bool decode_gemm_fp8_fits(const GemmArgs& g);
+hipError_t launch_decode_gemm_fp8(const GemmArgs& g, hipStream_t s);
 // launch_grouped_gemm(g, max_rows) runs the decode kernel
 bool gemm_picks_decode(const GemmArgs& g, int64_t max_rows);
 // Router, permute map (inverse map included) and gathered GEMM1 in one launch

@@ -95,6 +95,12 @@ GEMM_CASES = [
     ("big_tiles", [700, 613], 512, 384),
     ("split_decode", [1, 0, 2, 1, 0, 3], 1024, 512),
     ("split_wide", [20, 30, 0, 16], 1024, 512),
+    # under 8 rows per expert over the padded rows: the whole-k FP8 decode
+    # kernel (four 64-k steps in flight for k = 2048, one for 512), and an
+    # expert of 20 rows that takes two 16-row passes
+    ("decode_kernel", [(7 * e) % 6 for e in range(32)], 2048, 512),
+    ("decode_kernel_ragged", [20, 0, 1, 3, 0, 0, 2, 5, 0, 1, 0, 0, 4, 0, 1, 2] + [0] * 16, 1024,
+     512),
 ]
 
 
