@@ -25,10 +25,12 @@ few percent of the token (seen: an element near 4.55 with a static scale of
 0.03, one step = 3.2 % of its token).  So the per-token bar for FP8
 activations is 6e-2, and the pooled bar stays 1e-2 (3e-2 with MXFP4 weights).
 
-Ten fixed layers add the limits and the degenerate shapes: 1024 experts with
-top-32 (decode- and prefill-sized, all local or a scattered subset, bf16,
-MXFP4, FP8, blockwise FP8, two-term, batched), k = E, a single expert, and a
-single local expert of 256, whose tokens mostly have nothing to add.
+Thirteen fixed layers add the limits and the degenerate shapes: 1024 experts
+with top-32 (decode- and prefill-sized, all local or a scattered subset, bf16,
+MXFP4, FP8, blockwise FP8, two-term, batched), k = E, a single expert, a
+single local expert of 256, whose tokens mostly have nothing to add, and FP8
+decode batches with static scales, the router weight on the input and the
+batched layout.
 """
 import gc
 
@@ -225,6 +227,11 @@ VEXTREME = [
     _vfixed(9951, "block", 300, 512, 16, 256, 256, El=64),
     _vfixed(9952, "x2", 2, 1024, 32, 256, 256),
     _vfixed(9953, "bf16", 100, 1024, 32, 128, 64, El=200, batched=True, act="gelu"),
+    # the whole-k FP8 decode GEMMs under the layer options: static scales
+    # with GELU and a clamp, the router weight on the input, the batched layout
+    _vfixed(9954, "fp8", 3, 64, 4, 1024, 512, El=40, static=True, act="gelu", clamp=7.0),
+    _vfixed(9955, "fp8", 5, 16, 1, 1024, 512, on_input=True),
+    _vfixed(9956, "fp8", 6, 32, 8, 2048, 1024, batched=True),
 ]
 
 VCASES = [_draw_variant(i) for i in range(N_LAYERS)] + VEXTREME
