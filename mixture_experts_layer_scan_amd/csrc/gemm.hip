@@ -1287,16 +1287,18 @@ struct Configs {
 //           (from 128 rows on it is 4-29 % faster than a 128x128 tile)
 //   16-127  weight-streaming: one 128-row m-tile per expert, so every weight
 //           byte is read once, with the idle fragments skipped
-//   < 16    short tiles with split reductions; bf16 under 8 rows the whole-k
-//           decode kernel (from 8 to 15 rows the split tiles are up to 28 %
-//           faster; at 8 the two tie).
+//   < 16    short tiles with split reductions (bf16: from 8 rows on the
+//           weight-streaming tile, GEMM2 10-17 % faster than the short tile
+//           there, GEMM1 level; FP8 and MXFP4 were level or slower); under 8
+//           rows the whole-k decode kernels (bf16, per-channel FP8), which
+//           from 8 to 15 rows the split tiles beat by up to 28 %.
 constexpr int64_t kDecodeMeanRows = 8;
-constexpr int64_t kThinMeanRows = 16;
 
 template <bool WQ, bool F8, bool A2 = false, bool BS = false>
 hipError_t launch_fmt(const GemmArgs& g, int64_t max_rows, hipStream_t s) {
   using C = Configs<WQ, F8, A2, BS>;
   const int64_t mean_rows = g.E_l > 0 ? max_rows / g.E_l : max_rows;
+  constexpr int64_t kThinMeanRows = (WQ || F8) ? 16 : 8;
   // bf16 decode batches: whole-k weight slices per workgroup, no split
   if constexpr (!WQ && !F8)
     if (mean_rows < kDecodeMeanRows && decode_gemm_fits(g)) return launch_decode_gemm(g, s);
